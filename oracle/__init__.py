@@ -1,0 +1,215 @@
+"""CPU oracle for the batched causal long convolution -- TEST INFRASTRUCTURE ONLY.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of ``bench.py``
+may import this package.  The product path (``fft_causal_long_amd`` / libspecconv) never
+imports, links or calls it, and the two share no code: this package does its own
+storage decoding (bf16 bits -> float), its own modular lift and its own builds.
+
+Every function is a plain definition or the pages' recipe written out without any
+blocking or fusion (see ``oracle.c`` for the C side):
+
+* :func:`causal_conv_f64` -- r[t] = sum_{j<=t} v[j] g[t-j] and the error scale
+  S[t] = sum_{j<=t} |v[j]| |g[t-j]|, float64.  This is the causal convolution that
+  "Caracal: Causal Architecture via Spectral Mixing" (key design 1, the multi-head
+  Fourier module) equates with the frequency-domain product, and that key design 2
+  (the frequency-domain causal mask) says pad-to-2L / truncate-to-L reduces to.
+* :func:`causal_conv_i64` -- the same sum in exact int64.
+* :func:`lift_mod_p` -- residue of an exact integer, mapped to the symmetric range
+  [-(p-1)/2, (p-1)/2]: what an exact number-theoretic transform returns ("Catastrophic
+  Token Leakage in Convolutional Sequence Modeling and How to Mitigate It", abstract:
+  FFTs done on integers only).
+* :func:`causal_conv_f64_at` -- the float64 sum for sampled (channel, t) outputs.
+* :func:`circular_conv_dft` / :func:`circular_conv_ntt` -- the pages' recipe (zero-pad on
+  the right to n, transform, multiply, inverse, keep all n values) with O(n^2) DFT / NTT,
+  used only to pin key design 2 against the direct sum.
+
+NTT modulus: p = 998244353 = 119 * 2^23 + 1 with primitive root 3.  The pages fix only
+"32-bit integers"; this prime is the reading used on both sides of the parity tests.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+import threading
+
+import numpy as np
+
+P_NTT = 998244353
+ROOT_NTT = 3
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.c")
+_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+_lock = threading.Lock()
+_lib = None
+
+
+def build(force: bool = False) -> str:
+    """Compile oracle.c with gcc into oracle/liboracle.so (host code only)."""
+    if force or not os.path.exists(_LIB_PATH) or (
+        os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC)
+    ):
+        tmp = _LIB_PATH + ".tmp%d" % os.getpid()
+        cmd = [
+            "gcc", "-O2", "-ffp-contract=off", "-fPIC", "-shared", "-std=c99",
+            "-Wall", "-o", tmp, _SRC, "-lm", "-lpthread",
+        ]
+        subprocess.run(cmd, check=True)
+        os.replace(tmp, _LIB_PATH)
+    return _LIB_PATH
+
+
+def _load():
+    global _lib
+    with _lock:
+        if _lib is not None:
+            return _lib
+        if not os.path.exists(_LIB_PATH) or (
+            os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC)
+        ):
+            build()
+        lib = ctypes.CDLL(_LIB_PATH)
+        i64, dp, lp = ctypes.c_int64, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int64)
+        lib.oracle_conv_f64.argtypes = [dp, dp, dp, dp, i64, i64, ctypes.c_int]
+        lib.oracle_conv_f64.restype = ctypes.c_int
+        lib.oracle_conv_i64.argtypes = [lp, lp, lp, i64, i64, ctypes.c_int]
+        lib.oracle_conv_i64.restype = ctypes.c_int
+        lib.oracle_conv_f64_at.argtypes = [dp, dp, i64, lp, lp, i64, dp, dp]
+        lib.oracle_conv_f64_at.restype = ctypes.c_int
+        lib.oracle_circular_dft_f64.argtypes = [dp, dp, i64, i64, dp]
+        lib.oracle_circular_dft_f64.restype = ctypes.c_int
+        lib.oracle_circular_ntt.argtypes = [lp, lp, i64, i64, ctypes.c_uint32, ctypes.c_uint32, lp]
+        lib.oracle_circular_ntt.restype = ctypes.c_int
+        _lib = lib
+        return lib
+
+
+def _dptr(a):
+    return a.ctypes.data_as(ctypes.POINTER(ctypes.c_double))
+
+
+def _lptr(a):
+    return a.ctypes.data_as(ctypes.POINTER(ctypes.c_int64))
+
+
+def default_threads() -> int:
+    try:
+        return max(1, len(os.sched_getaffinity(0)))
+    except AttributeError:  # pragma: no cover
+        return max(1, os.cpu_count() or 1)
+
+
+def bf16_bits_to_f64(bits: np.ndarray) -> np.ndarray:
+    """Decode stored bfloat16 bit patterns (uint16) exactly: bf16 is the top half of an
+    IEEE binary32, so shifting the bits up gives the float32 with the same value."""
+    b = np.ascontiguousarray(bits, dtype=np.uint16)
+    return (b.astype(np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64)
+
+
+def as_f64(x: np.ndarray) -> np.ndarray:
+    """Widen stored values exactly to float64 (uint16 arrays are read as bf16 bits)."""
+    x = np.asarray(x)
+    if x.dtype == np.uint16:
+        return bf16_bits_to_f64(x)
+    if x.dtype not in (np.float16, np.float32, np.float64):
+        raise TypeError("oracle: unsupported float storage dtype %s" % x.dtype)
+    return np.ascontiguousarray(x, dtype=np.float64)
+
+
+def causal_conv_f64(v, g, nthreads: int | None = None, with_scale: bool = True):
+    """Direct float64 causal convolution along the last axis.
+
+    Returns ``(r, S)`` (``S`` is None when ``with_scale`` is False); both have the
+    shape of ``v``.  Inputs are widened exactly from their stored dtype."""
+    v64, g64 = as_f64(v), as_f64(g)
+    if v64.shape != g64.shape:
+        raise ValueError("v and g must have the same shape")
+    shape = v64.shape
+    L = shape[-1] if len(shape) else 0
+    nch = int(np.prod(shape[:-1])) if len(shape) > 1 else 1
+    r = np.zeros(shape, dtype=np.float64)
+    S = np.zeros(shape, dtype=np.float64) if with_scale else None
+    if v64.size == 0:
+        return r, S
+    rc = _load().oracle_conv_f64(
+        _dptr(v64), _dptr(g64), _dptr(r), _dptr(S) if S is not None else None,
+        nch, L, nthreads or default_threads(),
+    )
+    if rc != 0:
+        raise RuntimeError("oracle_conv_f64 failed")
+    return r, S
+
+
+def causal_conv_i64(v, g, nthreads: int | None = None) -> np.ndarray:
+    """Exact int64 causal convolution along the last axis."""
+    v64 = np.ascontiguousarray(v, dtype=np.int64)
+    g64 = np.ascontiguousarray(g, dtype=np.int64)
+    if v64.shape != g64.shape:
+        raise ValueError("v and g must have the same shape")
+    shape = v64.shape
+    L = shape[-1] if len(shape) else 0
+    nch = int(np.prod(shape[:-1])) if len(shape) > 1 else 1
+    r = np.zeros(shape, dtype=np.int64)
+    if v64.size == 0:
+        return r
+    rc = _load().oracle_conv_i64(_lptr(v64), _lptr(g64), _lptr(r), nch, L,
+                                 nthreads or default_threads())
+    if rc != 0:
+        raise RuntimeError("oracle_conv_i64 failed")
+    return r
+
+
+def lift_mod_p(r, p: int = P_NTT) -> np.ndarray:
+    """(r mod p) mapped into [-(p-1)/2, (p-1)/2] (p odd, so there is no tie)."""
+    r = np.asarray(r, dtype=np.int64)
+    m = np.mod(r, p)
+    return np.where(m > (p - 1) // 2, m - p, m).astype(np.int64)
+
+
+def causal_conv_f64_at(v, g, ch, t):
+    """float64 r and S at sampled outputs: v, g of shape (nch, L); ch, t index arrays."""
+    v64, g64 = as_f64(v), as_f64(g)
+    L = v64.shape[-1]
+    v64 = v64.reshape(-1, L)
+    g64 = g64.reshape(-1, L)
+    ch = np.ascontiguousarray(ch, dtype=np.int64)
+    t = np.ascontiguousarray(t, dtype=np.int64)
+    if ch.shape != t.shape:
+        raise ValueError("ch and t must have the same shape")
+    if ch.size and (ch.min() < 0 or ch.max() >= v64.shape[0]):
+        raise IndexError("channel index out of range")
+    r = np.zeros(ch.shape, dtype=np.float64)
+    S = np.zeros(ch.shape, dtype=np.float64)
+    rc = _load().oracle_conv_f64_at(_dptr(v64), _dptr(g64), L, _lptr(ch), _lptr(t), ch.size,
+                                    _dptr(r), _dptr(S))
+    if rc != 0:
+        raise RuntimeError("oracle_conv_f64_at failed")
+    return r, S
+
+
+def circular_conv_dft(v, g, n: int) -> np.ndarray:
+    """Naive O(n^2) float64 DFT circular convolution of v, g zero-padded to n (1-D)."""
+    v64 = np.ascontiguousarray(v, dtype=np.float64).ravel()
+    g64 = np.ascontiguousarray(g, dtype=np.float64).ravel()
+    if v64.size != g64.size:
+        raise ValueError("v and g must have the same length")
+    out = np.zeros(n, dtype=np.float64)
+    rc = _load().oracle_circular_dft_f64(_dptr(v64), _dptr(g64), v64.size, n, _dptr(out))
+    if rc != 0:
+        raise RuntimeError("oracle_circular_dft_f64 failed")
+    return out
+
+
+def circular_conv_ntt(v, g, n: int, p: int = P_NTT, root: int = ROOT_NTT) -> np.ndarray:
+    """Naive O(n^2) NTT circular convolution mod p of v, g zero-padded to n (1-D).
+    Returns residues in [0, p)."""
+    v64 = np.ascontiguousarray(v, dtype=np.int64).ravel()
+    g64 = np.ascontiguousarray(g, dtype=np.int64).ravel()
+    if v64.size != g64.size:
+        raise ValueError("v and g must have the same length")
+    out = np.zeros(n, dtype=np.int64)
+    rc = _load().oracle_circular_ntt(_lptr(v64), _lptr(g64), v64.size, n, p, root, _lptr(out))
+    if rc != 0:
+        raise RuntimeError("oracle_circular_ntt failed")
+    return out

@@ -1,0 +1,68 @@
+"""Seeded input generator checks (CPU only)."""
+import numpy as np
+
+from workloads import (WORKLOADS, bf16_bits_to_f32, f32_to_bf16_bits, make_inputs,
+                       perturbation_positions)
+
+
+def test_presets_match_shapes():
+    w = WORKLOADS
+    assert (w[1].B, w[1].C, w[1].L, w[1].storage) == (1, 64, 256, "f32")
+    assert (w[2].B, w[2].C, w[2].L, w[2].groups) == (8, 768, 1024, 12)
+    assert (w[3].B, w[3].C, w[3].L, w[3].storage, w[3].groups) == (8, 1024, 4096, "bf16", 16)
+    assert (w[4].B, w[4].C, w[4].L) == (1, 1536, 65536)
+    assert (w[5].B, w[5].C, w[5].L, w[5].storage) == (4, 768, 4096, "i32")
+
+
+def test_deterministic_and_seed_families_differ():
+    for cid in (1, 2, 5):
+        a = make_inputs(WORKLOADS[cid], B=1, C=64, L=128)
+        b = make_inputs(WORKLOADS[cid], B=1, C=64, L=128)
+        assert all(np.array_equal(x, y) for x, y in zip(a, b))
+        c = make_inputs(WORKLOADS[cid], B=1, C=64, L=128, seed_offset=1)
+        assert not np.array_equal(a[0], c[0])
+
+
+def test_distributions():
+    v, g = make_inputs(WORKLOADS[1])
+    assert v.dtype == np.float32 and v.shape == (1, 64, 256)
+    assert abs(v.mean()) < 0.05 and abs(v.std() - 1) < 0.05
+    assert g.min() > 0 and g.max() < 1 and abs(g.mean() - 0.5) < 0.02
+    v, g = make_inputs(WORKLOADS[5], B=1, C=8, L=512)
+    assert v.dtype == np.int32 and v.min() >= -127 and v.max() <= 127
+    assert v.min() == -127 and v.max() == 127
+    v, g = make_inputs(WORKLOADS[4], B=1, C=4, L=65536)
+    gf = g.astype(np.float64)
+    assert gf[..., :1024].mean() > 2 * gf[..., -1024:].mean()   # decay envelope
+
+
+def test_gate_conv_is_causal_and_grouped():
+    w = WORKLOADS[2]
+    v, g = make_inputs(w, B=2, C=24, L=64)
+    # groups = 12 does not divide 24 channels into 64-wide heads, but the recipe still
+    # only looks back: g[..., 0] depends on s[..., 0] alone, so it is finite and the
+    # tensors have the requested shape
+    assert g.shape == (2, 24, 64) and np.isfinite(g).all()
+    v, g = make_inputs(WORKLOADS[3], B=1, C=1024, L=16)
+    assert g.dtype == np.uint16
+
+
+def test_bf16_rounding_is_nearest_even():
+    x = np.array([1.0, 1.0 + 2.0**-8, 1.0 + 3 * 2.0**-8, 1.0 + 2.0**-7 + 2.0**-9,
+                  -2.5, 3.0e38, 1e-30], dtype=np.float32)
+    bits = f32_to_bf16_bits(x)
+    back = bf16_bits_to_f32(bits)
+    # ties go to even mantissa
+    assert back[0] == 1.0
+    assert back[1] == 1.0
+    assert back[2] == 1.0 + 2.0**-6
+    assert back[3] == 1.0 + 2.0**-7        # below the midpoint: rounds down
+    assert back[4] == -2.5
+    assert np.isfinite(back[5])
+    # everything within half an ulp of bf16 (relative 2^-8)
+    assert np.all(np.abs(back - x) <= np.abs(x) * 2.0**-8)
+
+
+def test_perturbation_positions():
+    p = perturbation_positions(5, 4096)
+    assert 1 in p and 4095 in p and len(p) == 8 and p.max() < 4096
