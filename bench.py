@@ -1,0 +1,210 @@
+"""Benchmark of the batched causal long convolution on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--config 3] [--no-cpu-baseline]
+
+One step = one call of the library's hot path over one batch of synthetic input (for the
+default workload, sc_causal_conv_bf16 at B=8, C=1024, L=4096: load v and g, pad-to-2L FFT,
+spectral product, inverse FFT, truncation, direct head, store r -- a single kernel).
+Inputs are resident in HBM before the timed region.  Several copies of the buffers are
+rotated so that the 256 MB last-level cache cannot hold a step's working set.
+
+Prints ONE JSON line.  `value` is causal-conv outputs (B*C*L) per second.  The
+`roofline` object refers to the dominant kernel, timed with HIP events recorded on the
+stream the kernel runs on; `cpu_baseline` is the float64 CPU oracle timed on a bounded
+sample of the same workload on this host's cores.
+"""
+from __future__ import annotations
+
+import argparse
+import glob
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E, AMD published
+FP32_VECTOR_PEAK_TFLOPS = 157.3  # MI355X fp32 vector, AMD published
+CACHE_BYTES = 256 << 20          # MI355X last-level (Infinity) cache
+
+
+def algorithmic_flops_per_output(L: int) -> float:
+    """Real flops per output of the pad-2L FFT method with real-pair packing, the pruned
+    first forward stage and the half-length real inverse: (12.75 log2 L + 28)."""
+    return 12.75 * np.log2(L) + 28.0
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for p in sorted(glob.glob(os.path.join(ROOT, "fft_causal_long_amd", "csrc", "*"))):
+        with open(p, "rb") as f:
+            h.update(os.path.basename(p).encode())
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per launch from committed rocprofv3 counter runs, if they were taken on
+    the current kernel sources; else None."""
+    path = os.path.join(ROOT, "profiles", "traffic_%s.json" % workload)
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("source_hash") != kernel_source_hash():
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def cpu_baseline(w, v, g, budget_s: float = 10.0):
+    """Time the float64 oracle on growing channel samples until one takes >= budget_s/2."""
+    import oracle
+    nthreads = oracle.default_threads()
+    nch = w.B * w.C
+    vv = v.reshape(nch, w.L)
+    gg = g.reshape(nch, w.L)
+    n = 8
+    while True:
+        t0 = time.perf_counter()
+        oracle.causal_conv_f64(vv[:n], gg[:n], nthreads=nthreads, with_scale=False)
+        dt = time.perf_counter() - t0
+        if dt >= budget_s / 2 or n >= nch:
+            break
+        n = min(nch, max(2 * n, int(n * (budget_s / 2) / max(dt, 1e-3))))
+    return {
+        "value": n * w.L / dt,
+        "unit": "outputs/s",
+        "cores": nthreads,
+        "kind": "oracle",
+        "sample": "%d of %d channels (L=%d), float64 direct O(L^2) sum on the stored inputs, "
+                  "%.2f s wall" % (n, nch, w.L, dt),
+    }
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calib-copy", action="store_true",
+                    help="also run a plain device copy of known size (profiler calibration)")
+    args = ap.parse_args(argv)
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(channels shard across GPUs with no communication; run one process per GPU)",
+              file=sys.stderr)
+        return 2
+
+    import torch
+    import fft_causal_long_amd as sc
+    from workloads import WORKLOADS, make_inputs
+
+    w = WORKLOADS[args.config]
+    if w.storage == "i32":
+        fn_name, esz = "sc_causal_conv_ntt_i32", 4
+    elif w.storage == "bf16":
+        fn_name, esz = "sc_causal_conv_bf16", 2
+    else:
+        fn_name, esz = "sc_causal_conv_f32", 4
+    fn = getattr(sc.lib(), fn_name)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    v, g = make_inputs(w)
+    tdtype = {"f32": torch.float32, "bf16": torch.int16, "i32": torch.int32}[w.storage]
+    hv = torch.from_numpy(v.view(np.int16) if w.storage == "bf16" else v)
+    hg = torch.from_numpy(g.view(np.int16) if w.storage == "bf16" else g)
+    set_bytes = 3 * w.outputs * esz
+    nsets = max(1, -(-2 * CACHE_BYTES // set_bytes))
+    bufs = []
+    for _ in range(nsets):
+        bufs.append((hv.to(dev), hg.to(dev), torch.empty(w.outputs, dtype=tdtype, device=dev)))
+    stream = torch.cuda.current_stream(dev)
+    sptr = stream.cuda_stream
+
+    def step(i):
+        a, b, c = bufs[i % nsets]
+        st = fn(a.data_ptr(), b.data_ptr(), c.data_ptr(), w.B, w.C, w.L, sptr)
+        if st != 0:
+            raise RuntimeError("%s failed: %s" % (fn_name, sc.sc_status_string(st)))
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    # per-launch events on the launch stream, plus one pair around the whole region
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
+    t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start.record(stream)
+    for i in range(args.steps):
+        ev[i][0].record(stream)
+        step(i)
+        ev[i][1].record(stream)
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    total_ms = t_start.elapsed_time(t_end)
+    launch_ms = [a.elapsed_time(b) for a, b in ev]
+    ms_per_step = total_ms / args.steps
+    kernel_ms = float(np.mean(launch_ms))
+
+    if args.calib_copy:
+        # 1 GiB device-to-device copy: a known-size reference for the profiler's byte counters
+        src = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+
+    outputs = w.outputs
+    value = outputs * args.steps / (total_ms * 1e-3)
+    alg_bytes = outputs * 3 * esz
+    hbm_gbps = alg_bytes / (kernel_ms * 1e-3) / 1e9
+    traffic = measured_traffic(w.name)
+    if w.storage == "i32":
+        roof = {"bound": "hbm", "achieved": round(hbm_gbps, 1), "peak": HBM_PEAK_GBPS,
+                "unit": "GB/s", "frac": round(hbm_gbps / HBM_PEAK_GBPS, 4), "traffic": traffic}
+    else:
+        flops = algorithmic_flops_per_output(w.L) * outputs
+        tf = flops / (kernel_ms * 1e-3) / 1e12
+        roof = {"bound": "alu", "achieved": round(tf, 2), "peak": FP32_VECTOR_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(tf / FP32_VECTOR_PEAK_TFLOPS, 4),
+                "traffic": traffic}
+    rec = {
+        "metric": "causal-conv outputs/sec (B*C*L) at L=%d + %% HBM roofline" % w.L,
+        "value": round(value, 1),
+        "unit": "outputs/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32" if w.storage != "i32" else "int32-mod-p",
+        "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "C": w.C, "L": w.L, "storage": w.storage,
+                   "entry": fn_name, "buffer_sets": nsets},
+        "roofline": roof,
+        "hbm": {"algorithmic_bytes_per_launch": alg_bytes, "achieved_GBps": round(hbm_gbps, 1),
+                "peak_GBps": HBM_PEAK_GBPS, "frac": round(hbm_gbps / HBM_PEAK_GBPS, 4)},
+        "kernel_ms": {"mean": round(kernel_ms, 5), "min": round(float(np.min(launch_ms)), 5),
+                      "p50": round(float(np.median(launch_ms)), 5),
+                      "max": round(float(np.max(launch_ms)), 5)},
+    }
+    if not args.no_cpu_baseline:
+        rec["cpu_baseline"] = cpu_baseline(w, v, g)
+    print(json.dumps(rec), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

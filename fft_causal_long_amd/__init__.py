@@ -1,0 +1,196 @@
+"""fft_causal_long_amd -- Python binding of libspecconv (argument marshalling only).
+
+The batched per-channel causal long convolution
+
+    r[b, c, t] = sum_{j <= t} v[b, c, j] * g[b, c, t - j]
+
+runs entirely in the HIP kernels of ``libspecconv.so`` (built in-tree from ``csrc/`` by
+``python -m fft_causal_long_amd.build``).  PyTorch only provides device memory and the
+stream: tensors are passed by ``data_ptr()`` together with the current HIP stream.
+There is no CPU fallback: if the library is missing, importing this package fails.
+
+Public names mirror the C ABI of ``include/specconv.h``:
+``sc_causal_conv_f32``, ``sc_causal_conv_bf16``, ``sc_causal_conv_ntt_i32``, their
+``_ws`` variants, ``sc_causal_conv_ex``, ``sc_workspace_bytes``, ``sc_ntt_range_ok``,
+``sc_status_string``, ``sc_version``; plus :func:`causal_conv`, which dispatches on dtype.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch  # noqa: F401  -- load torch's HIP runtime first; libspecconv binds to it by soname
+
+__all__ = [
+    "SpecConvError", "lib", "causal_conv", "sc_causal_conv_f32", "sc_causal_conv_bf16",
+    "sc_causal_conv_ntt_i32", "sc_causal_conv_f32_ws", "sc_causal_conv_bf16_ws",
+    "sc_causal_conv_ntt_i32_ws", "sc_causal_conv_ex", "sc_workspace_bytes", "sc_ntt_range_ok",
+    "sc_status_string", "sc_version", "KIND_F32", "KIND_BF16", "KIND_NTT_I32", "PATH_AUTO",
+    "PATH_FUSED", "PATH_FOUR_STEP", "PATH_DIRECT", "LIB_PATH",
+]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libspecconv.so")
+
+SC_OK, SC_ERR_INVALID_ARGUMENT, SC_ERR_UNSUPPORTED, SC_ERR_HIP, SC_ERR_WORKSPACE = range(5)
+KIND_F32, KIND_BF16, KIND_NTT_I32 = 0, 1, 2
+PATH_AUTO, PATH_FUSED, PATH_FOUR_STEP, PATH_DIRECT = 0, 1, 2, 3
+
+
+class SpecConvError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        super().__init__("%s: %s" % (what, sc_status_string(status)))
+        self.status = status
+
+
+class sc_options(ctypes.Structure):
+    _fields_ = [("path", ctypes.c_int32), ("head", ctypes.c_int32),
+                ("reserved", ctypes.c_int32 * 6)]
+
+
+def _open():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError("libspecconv.so is not built (run: python -m fft_causal_long_amd.build)")
+    h = ctypes.CDLL(LIB_PATH)
+    vp, i64, sz, st = ctypes.c_void_p, ctypes.c_int64, ctypes.c_size_t, ctypes.c_int
+    for name in ("sc_causal_conv_f32", "sc_causal_conv_bf16", "sc_causal_conv_ntt_i32"):
+        f = getattr(h, name)
+        f.argtypes = [vp, vp, vp, i64, i64, i64, vp]
+        f.restype = st
+    for name in ("sc_causal_conv_f32_ws", "sc_causal_conv_bf16_ws", "sc_causal_conv_ntt_i32_ws"):
+        f = getattr(h, name)
+        f.argtypes = [vp, vp, vp, i64, i64, i64, vp, sz, vp]
+        f.restype = st
+    h.sc_causal_conv_ex.argtypes = [st, vp, vp, vp, i64, i64, i64,
+                                    ctypes.POINTER(sc_options), vp, sz, vp]
+    h.sc_causal_conv_ex.restype = st
+    h.sc_workspace_bytes.argtypes = [st, i64, i64, i64]
+    h.sc_workspace_bytes.restype = sz
+    h.sc_ntt_range_ok.argtypes = [i64, i64, i64]
+    h.sc_ntt_range_ok.restype = ctypes.c_int
+    h.sc_status_string.argtypes = [st]
+    h.sc_status_string.restype = ctypes.c_char_p
+    h.sc_version.argtypes = []
+    h.sc_version.restype = ctypes.c_int
+    return h
+
+
+_lib = _open()
+
+
+def lib():
+    """The ctypes handle of libspecconv.so (argtypes set)."""
+    return _lib
+
+
+# ---------------------------------------------------------------- raw C-ABI mirrors
+
+def sc_causal_conv_f32(v, g, r, B, C, L, stream):
+    return _lib.sc_causal_conv_f32(v, g, r, B, C, L, stream)
+
+
+def sc_causal_conv_bf16(v, g, r, B, C, L, stream):
+    return _lib.sc_causal_conv_bf16(v, g, r, B, C, L, stream)
+
+
+def sc_causal_conv_ntt_i32(v, g, r, B, C, L, stream):
+    return _lib.sc_causal_conv_ntt_i32(v, g, r, B, C, L, stream)
+
+
+def sc_causal_conv_f32_ws(v, g, r, B, C, L, ws, ws_bytes, stream):
+    return _lib.sc_causal_conv_f32_ws(v, g, r, B, C, L, ws, ws_bytes, stream)
+
+
+def sc_causal_conv_bf16_ws(v, g, r, B, C, L, ws, ws_bytes, stream):
+    return _lib.sc_causal_conv_bf16_ws(v, g, r, B, C, L, ws, ws_bytes, stream)
+
+
+def sc_causal_conv_ntt_i32_ws(v, g, r, B, C, L, ws, ws_bytes, stream):
+    return _lib.sc_causal_conv_ntt_i32_ws(v, g, r, B, C, L, ws, ws_bytes, stream)
+
+
+def sc_causal_conv_ex(kind, v, g, r, B, C, L, opt, ws, ws_bytes, stream):
+    return _lib.sc_causal_conv_ex(kind, v, g, r, B, C, L, opt, ws, ws_bytes, stream)
+
+
+def sc_workspace_bytes(kind, B, C, L) -> int:
+    return int(_lib.sc_workspace_bytes(kind, B, C, L))
+
+
+def sc_ntt_range_ok(max_abs_v, max_abs_g, L) -> bool:
+    return bool(_lib.sc_ntt_range_ok(max_abs_v, max_abs_g, L))
+
+
+def sc_status_string(status: int) -> str:
+    return _lib.sc_status_string(int(status)).decode()
+
+
+def sc_version() -> int:
+    return int(_lib.sc_version())
+
+
+# ---------------------------------------------------------------- tensor front end
+
+_KIND_OF_DTYPE = {torch.float32: KIND_F32, torch.bfloat16: KIND_BF16, torch.int32: KIND_NTT_I32}
+
+
+def _shape3(t: torch.Tensor):
+    if t.dim() == 3:
+        return tuple(int(x) for x in t.shape)
+    if t.dim() == 0:
+        raise ValueError("causal_conv needs at least 1 dimension")
+    L = int(t.shape[-1])
+    lead = 1
+    for s in t.shape[:-1]:
+        lead *= int(s)
+    return lead, 1, L
+
+
+def causal_conv(v: torch.Tensor, g: torch.Tensor, out: torch.Tensor | None = None, *,
+                path: int | None = None, head: int | None = None,
+                workspace: torch.Tensor | None = None) -> torch.Tensor:
+    """r = causal_conv(v, g) along the last axis, on v's device and torch's current stream.
+
+    dtype selects the kind: float32 -> sc_causal_conv_f32, bfloat16 -> sc_causal_conv_bf16,
+    int32 -> sc_causal_conv_ntt_i32 (exact mod p).  v, g (and out) must be contiguous
+    device tensors of one shape and dtype.  ``path``/``head`` go through
+    sc_causal_conv_ex; ``workspace`` is an optional caller-owned uint8 device tensor."""
+    if v.shape != g.shape or v.dtype != g.dtype:
+        raise ValueError("v and g must have the same shape and dtype")
+    if v.dtype not in _KIND_OF_DTYPE:
+        raise TypeError("unsupported dtype %s" % v.dtype)
+    if not (v.is_cuda and g.is_cuda) or v.device != g.device:
+        raise ValueError("v and g must be on the same GPU")
+    if not (v.is_contiguous() and g.is_contiguous()):
+        raise ValueError("v and g must be contiguous")
+    if out is None:
+        out = torch.empty_like(v)
+    elif out.shape != v.shape or out.dtype != v.dtype or out.device != v.device \
+            or not out.is_contiguous():
+        raise ValueError("out must match v in shape, dtype, device and be contiguous")
+    B, C, L = _shape3(v)
+    kind = _KIND_OF_DTYPE[v.dtype]
+    ws_ptr, ws_bytes = None, 0
+    if workspace is not None:
+        if not workspace.is_cuda or workspace.device != v.device or not workspace.is_contiguous():
+            raise ValueError("workspace must be a contiguous tensor on v's device")
+        ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
+    with torch.cuda.device(v.device):
+        stream = torch.cuda.current_stream(v.device).cuda_stream
+        if path is None and head is None:
+            if ws_ptr is None:
+                fn = (_lib.sc_causal_conv_f32, _lib.sc_causal_conv_bf16,
+                      _lib.sc_causal_conv_ntt_i32)[kind]
+                st = fn(v.data_ptr(), g.data_ptr(), out.data_ptr(), B, C, L, stream)
+            else:
+                fn = (_lib.sc_causal_conv_f32_ws, _lib.sc_causal_conv_bf16_ws,
+                      _lib.sc_causal_conv_ntt_i32_ws)[kind]
+                st = fn(v.data_ptr(), g.data_ptr(), out.data_ptr(), B, C, L, ws_ptr, ws_bytes,
+                        stream)
+        else:
+            opt = sc_options(PATH_AUTO if path is None else int(path),
+                             -1 if head is None else int(head))
+            st = _lib.sc_causal_conv_ex(kind, v.data_ptr(), g.data_ptr(), out.data_ptr(),
+                                        B, C, L, ctypes.byref(opt), ws_ptr, ws_bytes, stream)
+    if st != SC_OK:
+        raise SpecConvError(st, "causal_conv")
+    return out

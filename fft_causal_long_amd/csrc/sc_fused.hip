@@ -1,0 +1,386 @@
+// Fused in-LDS causal long convolution for L <= 4096 (gfx950).
+//
+// Method ("Caracal: Causal Architecture via Spectral Mixing", key designs 1 and 2):
+// zero-pad v and g on the right to N = 2M (M = next power of two >= L), FFT, multiply the
+// spectra bin by bin, inverse FFT, keep the first L values.  That equals the causal
+// convolution r_t = sum_{j<=t} v_j g_{t-j}.  The improvement direction the notes list
+// under limitations (a real FFT to halve the work) is taken here in three places:
+//
+//  1. v and g are real, so one complex transform of z = v + i g carries both spectra:
+//     V_k = (Z_k + conj Z_{N-k}) / 2,  G_k = (Z_k - conj Z_{N-k}) / (2i).
+//  2. The upper half of z is the zero padding, so the first decimation-in-frequency stage
+//     of the length-N transform is only a twiddle: with u^b_n = z_n W_N^{b n} (n < M),
+//     Z_{2j+b} = DFT_M(u^b)_j for b = 0, 1.  The two length-M transforms ("branches")
+//     run side by side in one workgroup.
+//  3. The result x = IDFT_N(V G) is real, so it is obtained from one length-M complex
+//     inverse transform:  Y_k = [(X_k + X_{k+M}) + i W_N^{-k} (X_k - X_{k+M})] / 2,
+//     y = IDFT_M(Y) / M gives y_m = x_{2m} + i x_{2m+1}.  With X_{k+M} = conj X_{M-k},
+//     the four bins {k, N-k, M-k, M+k} of Z give Y_k and Y_{M-k} together.
+//
+// The first `head` outputs (default 32) are recomputed by direct fp32 summation: their
+// error scale sum_j |v_j||g_{t-j}| holds only t+1 products, far below the global round-off
+// of any float FFT.
+//
+// Workgroup = 512 threads.  A length-M transform is held by TB = M/16 threads with 16
+// values each (element tau + TB*r sits in register r of thread tau, at the input and the
+// output of every transform); between radix passes the values go through LDS.  A
+// workgroup serves CPW = 4096/M channels (two branch units per channel) and uses
+// 2*CPW*(M + M/16) complex values = 68 KB of LDS for every M, so two workgroups fit a CU.
+// HBM traffic is read v, read g, write r: nothing else leaves the chip.
+
+#include "sc_device.h"
+#include "sc_internal.h"
+
+namespace sc {
+
+constexpr int FUSED_THREADS = 512;
+constexpr int HEAD_MAX = 64;   // largest direct head (the host clamps to this)
+
+// one float2 of padding after every 16 keeps stride-16 LDS accesses conflict free
+__device__ __forceinline__ int lds_pad(int a) { return a + (a >> 4); }
+
+// Float twiddle bank (device constant table built by the host):
+//   [0, 8192)                        W_8192^i
+//   [8192 + (Q - 32) + k*(Q/16) + n] W_Q^{n k}, for each pass length Q = 32 .. 4096,
+//                                    k < 16, n < Q/16  (row k contiguous in n)
+// The pass tables make every twiddle load of a radix-16 pass a contiguous wave access.
+constexpr int PASS_TW_BASE = FUSED_TW_N;
+constexpr int BANK_FLOAT2 = FUSED_BANK_FLOAT2;
+
+struct Bank {
+    __amdgpu_buffer_rsrc_t rs;   // raw buffer over the whole bank, bounds-checked
+    __device__ __forceinline__ float2 at(int voff_elems, int soff_elems) const
+    {
+        const auto w = __builtin_amdgcn_raw_buffer_load_b64(rs, voff_elems * 8, soff_elems * 8, 0);
+        return __builtin_bit_cast(float2, w);
+    }
+};
+
+__device__ __forceinline__ Bank make_bank(const float2* tw)
+{
+    return Bank{__builtin_amdgcn_make_buffer_rsrc((void*)tw, (short)0, BANK_FLOAT2 * 8, 0x00020000)};
+}
+
+// W_n^e for a power of two n dividing 8192 (conj when INV)
+template <bool INV>
+__device__ __forceinline__ float2 tw_get(const Bank& b, int n, int e)
+{
+    const float2 w = b.at((e & (n - 1)) * (FUSED_TW_N / n), 0);
+    return INV ? conjf2(w) : w;
+}
+
+// LDS offset of flat element tau + TB*q (register q of thread tau)
+template <int TB>
+__device__ __forceinline__ int reg_off(int tau, int q)
+{
+    if constexpr (TB % 16 == 0) return tau + (tau >> 4) + q * (TB + TB / 16);
+    else return lds_pad(tau + TB * q);
+}
+
+// One Stockham decimation-in-frequency pass of radix R over a length-M transform held by
+// TB = M/16 threads.  Stage data: S sub-transforms of length Q = M/S, element (s, n) of
+// sub-transform s at flat index s + S*n; thread tau holds flat index tau + TB*r in x[r].
+// Butterfly "item" (s, n1), n1 < Q/R, combines elements (s, n1 + (Q/R) n2), n2 < R:
+//   out[s + S*k2, n1] = W_Q^{n1 k2} * sum_{n2} in[s, n1 + (Q/R) n2] W_R^{n2 k2}
+// which is written to flat index s + S*(k2 + R*n1).  Radix 16 is used while Q > 16, so a
+// pass with twiddles has one item per thread (item = tau).  The last pass (Q == R) leaves
+// the result in registers: x[r] = X[tau + TB*r], natural order.
+template <int M, int R, int S, bool INV>
+__device__ __forceinline__ void stockham_pass(float2 (&x)[16], float2* __restrict__ buf, int tau,
+                                              const Bank& bank)
+{
+    constexpr int NB = 16 / R, Q = M / S, QN = Q / R;
+    if constexpr (QN > 1) {
+        static_assert(R == 16, "passes with twiddles are radix 16");
+        const int s = tau & (S - 1), n1 = tau / S;
+        float2 w[16];
+#pragma unroll
+        for (int k2 = 1; k2 < 16; ++k2) w[k2] = bank.at(n1, PASS_TW_BASE + (Q - 32) + k2 * (Q / 16));
+        dft<16, INV>(x);
+#pragma unroll
+        for (int k2 = 1; k2 < 16; ++k2) x[k2] = cmul_dir<INV>(x[k2], w[k2]);
+        // flat s + S*(k2 + 16 n1), padded: base + k2*STEP
+        constexpr int STEP = S == 1 ? 1 : S + S / 16;
+        const int base = S == 1 ? 17 * n1 : (s + (s >> 4)) + 16 * n1 * STEP;
+#pragma unroll
+        for (int k2 = 0; k2 < 16; ++k2) buf[base + k2 * STEP] = x[k2];
+    } else {
+#pragma unroll
+        for (int q = 0; q < NB; ++q) {
+            float2 b[R];
+#pragma unroll
+            for (int n2 = 0; n2 < R; ++n2) b[n2] = x[q + NB * n2];
+            dft<R, INV>(b);
+#pragma unroll
+            for (int k2 = 0; k2 < R; ++k2) x[q + NB * k2] = b[k2];
+        }
+    }
+}
+
+// All passes of a length-M DFT (radix 16 while possible, then the remainder).  Inactive
+// threads only join the barriers.  On return every thread has passed a barrier that
+// follows its last read of buf.
+template <int M, bool INV, int S = 1>
+__device__ __forceinline__ void fft_passes(float2 (&x)[16], float2* __restrict__ buf, int tau,
+                                           const Bank& bank, bool active)
+{
+    constexpr int TB = M / 16, Q = M / S, R = Q >= 16 ? 16 : Q;
+    if constexpr (Q / R > 1) {
+        if (active) stockham_pass<M, R, S, INV>(x, buf, tau, bank);
+        __syncthreads();
+        if (active) {
+#pragma unroll
+            for (int q = 0; q < 16; ++q) x[q] = buf[reg_off<TB>(tau, q)];
+        }
+        __syncthreads();
+        fft_passes<M, INV, S * R>(x, buf, tau, bank, active);
+    } else {
+        if (active) stockham_pass<M, R, S, INV>(x, buf, tau, bank);
+    }
+}
+
+// From the branch spectra u0[j] = Z_{2j}, u1[j] = Z_{2j+1} (natural order, padded) form
+// Y_k and Y_{M-k} of the real-output inverse, both scaled by 8 (constants folded later).
+template <int M>
+__device__ __forceinline__ void unpack_pair(int k, const float2* __restrict__ u0,
+                                            const float2* __restrict__ u1, const Bank& bank,
+                                            float2& yk, float2& ymk)
+{
+    constexpr int N = 2 * M;
+    const int b = k & 1, j = k >> 1;
+    const float2* u = b ? u1 : u0;
+    // bins k, N-k, M-k, M+k of Z
+    const float2 p1 = u[lds_pad(j)];
+    const float2 q1 = conjf2(u[lds_pad((M - j - b) & (M - 1))]);
+    const float2 p2 = u[lds_pad((M / 2 - j - b) & (M - 1))];
+    const float2 q2 = conjf2(u[lds_pad(M / 2 + j)]);
+    // 4 X = 4 V G = -i (P + Q)(P - Q)
+    const float2 s1 = cadd(p1, q1), d1 = csub(p1, q1);
+    const float2 s2 = cadd(p2, q2), d2 = csub(p2, q2);
+    const float2 x1 = make_float2(__builtin_fmaf(s1.x, d1.y, s1.y * d1.x),
+                                  __builtin_fmaf(s1.y, d1.y, -s1.x * d1.x));   // 4 X_k
+    const float2 x2 = make_float2(__builtin_fmaf(s2.x, d2.y, s2.y * d2.x),
+                                  __builtin_fmaf(s2.y, d2.y, -s2.x * d2.x));   // 4 X_{M-k}
+    // S = X_k + X_{k+M}, D = X_k - X_{k+M} with X_{k+M} = conj X_{M-k}
+    const float2 sm = make_float2(x1.x + x2.x, x1.y - x2.y);
+    const float2 df = make_float2(x1.x - x2.x, x1.y + x2.y);
+    const float2 t = cmulc(df, tw_get<false>(bank, N, k));        // W_N^{-k} D
+    // Y_k = S + i T,  Y_{M-k} = conj(S - i T)
+    yk = make_float2(sm.x - t.y, sm.y + t.x);
+    ymk = make_float2(sm.x + t.y, t.x - sm.y);
+}
+
+template <int M, class IO>
+__global__ __launch_bounds__(FUSED_THREADS) void fused_conv_kernel(
+    const typename IO::T* __restrict__ v, const typename IO::T* __restrict__ g,
+    typename IO::T* __restrict__ r, int64_t nch, int L, int head, int pair_store,
+    const float2* __restrict__ tw)
+{
+    static_assert(M >= 64 && M <= 4096, "fused path handles 64 <= M <= 4096");
+    constexpr int N = 2 * M, TB = M / 16, UNITS = FUSED_THREADS / TB, CPW = UNITS / 2;
+    constexpr int REG = M + M / 16;
+    __shared__ float2 lds[UNITS * REG];
+    // first HEAD_MAX inputs of each local channel (v then g) for the direct head
+    __shared__ float hbuf[CPW * 2 * HEAD_MAX];
+
+    const Bank bank = make_bank(tw);
+    const int tid = threadIdx.x;
+    const int unit = tid / TB, tau = tid % TB;
+    const int cl = unit >> 1, beta = unit & 1;
+    const int64_t ch0 = (int64_t)blockIdx.x * CPW;
+    const int64_t ch = ch0 + cl;
+    // every channel of this workgroup present and no padding inside M: no guards needed
+    const bool full = L == M && ch0 + CPW <= nch;
+    float2* ubuf = lds + unit * REG;
+
+    // 1. u^beta_n = z_n W_N^{beta n},  z_n = v_n + i g_n for n < L, 0 otherwise
+    float2 x[16];
+    {
+        const int64_t base = ch * (int64_t)L;
+        if (full) {
+#pragma unroll
+            for (int q = 0; q < 16; ++q) {
+                const int n = tau + TB * q;
+                x[q] = make_float2(IO::load(v, base + n), IO::load(g, base + n));
+            }
+        } else {
+            const bool valid = ch < nch;
+#pragma unroll
+            for (int q = 0; q < 16; ++q) {
+                const int n = tau + TB * q;
+                x[q] = make_float2(0.f, 0.f);
+                if (valid && n < L) x[q] = make_float2(IO::load(v, base + n), IO::load(g, base + n));
+            }
+        }
+        if (!beta) {
+#pragma unroll
+            for (int q = 0; q < (TB >= HEAD_MAX ? 1 : HEAD_MAX / TB); ++q) {
+                const int n = tau + TB * q;
+                if (n < head) {
+                    hbuf[cl * 2 * HEAD_MAX + n] = x[q].x;
+                    hbuf[cl * 2 * HEAD_MAX + HEAD_MAX + n] = x[q].y;
+                }
+            }
+        } else {
+#pragma unroll
+            for (int q = 0; q < 16; ++q) x[q] = cmul(x[q], tw_get<false>(bank, N, tau + TB * q));
+        }
+    }
+
+    // 2. U^beta = DFT_M(u^beta); x[q] = U^beta_{tau + TB q}
+    fft_passes<M, false>(x, ubuf, tau, bank, true);
+#pragma unroll
+    for (int q = 0; q < 16; ++q) ubuf[reg_off<TB>(tau, q)] = x[q];
+    __syncthreads();
+
+    // 3. unpack + spectral product: channel-local thread lt takes k = lt + 2TB i, i < 4,
+    //    covering k in [0, M/2); k = 0 also yields Y_{M/2} in place of the absent Y_M.
+    const int lt = tid - cl * 2 * TB;
+    float2* u0 = lds + (2 * cl) * REG;
+    const float2* u1 = u0 + REG;
+    float2 yk[4], ymk[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int k = lt + 2 * TB * i;
+        unpack_pair<M>(k, u0, u1, bank, yk[i], ymk[i]);
+        if (k == 0) {
+            float2 unused;
+            unpack_pair<M>(M / 2, u0, u1, bank, ymk[i], unused);
+        }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int k = lt + 2 * TB * i;
+        u0[lds_pad(k)] = yk[i];
+        u0[lds_pad(k == 0 ? M / 2 : M - k)] = ymk[i];
+    }
+    __syncthreads();
+
+    // 4. y = IDFT_M(Y): threads [c*TB, (c+1)*TB) serve local channel c; the rest idle
+    const bool iact = tid < CPW * TB;
+    const int icl = iact ? tid / TB : 0, itau = tid % TB;
+    float2* ybuf = lds + (2 * icl) * REG;
+    if (iact) {
+#pragma unroll
+        for (int q = 0; q < 16; ++q) x[q] = ybuf[reg_off<TB>(itau, q)];
+    }
+    __syncthreads();
+    fft_passes<M, true>(x, ybuf, itau, bank, iact);
+
+    // 5. store: x[q] = 8 M y_m with m = itau + TB q; r_{2m} = Re y_m, r_{2m+1} = Im y_m
+    if (iact) {
+        const int64_t och = ch0 + icl;
+        const float scale = 1.0f / (8.0f * (float)M);
+        const int64_t base = och * (int64_t)L;
+        if (full && pair_store) {
+#pragma unroll
+            for (int q = 0; q < 8; ++q) {
+                const int t = 2 * (itau + TB * q);
+                if (2 * TB * q >= HEAD_MAX || t >= head)
+                    IO::store2(r, base + t, x[q].x * scale, x[q].y * scale);
+            }
+        } else if (och < nch) {
+#pragma unroll
+            for (int q = 0; q < 8; ++q) {
+                const int t = 2 * (itau + TB * q);
+                if (t >= head && t < L) {
+                    const float a = x[q].x * scale, b = x[q].y * scale;
+                    if (t + 1 < L) {
+                        if (pair_store) {
+                            IO::store2(r, base + t, a, b);
+                        } else {
+                            IO::store(r, base + t, a);
+                            IO::store(r, base + t + 1, b);
+                        }
+                    } else {
+                        IO::store(r, base + t, a);
+                    }
+                }
+            }
+        }
+    } else {
+        // 6. direct head from the staged inputs: r_t = sum_{j<=t} v_j g_{t-j}, fp32, t < head
+        const int nidle = FUSED_THREADS - CPW * TB;
+        for (int idx = tid - CPW * TB; idx < CPW * head; idx += nidle) {
+            const int c2 = idx / head, t = idx - c2 * head;
+            const int64_t hch = ch0 + c2;
+            if (hch < nch && t < L) {
+                const float* hv = hbuf + c2 * 2 * HEAD_MAX;
+                const float* hg = hv + HEAD_MAX;
+                float acc = 0.f;
+                for (int j = 0; j <= t; ++j) acc = __builtin_fmaf(hv[j], hg[t - j], acc);
+                IO::store(r, hch * (int64_t)L + t, acc);
+            }
+        }
+    }
+}
+
+template <class IO>
+__global__ void direct_conv_kernel(const typename IO::T* __restrict__ v,
+                                   const typename IO::T* __restrict__ g,
+                                   typename IO::T* __restrict__ r, int64_t nch, int L)
+{
+    const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (idx >= nch * (int64_t)L) return;
+    const int64_t c = idx / L;
+    const int t = (int)(idx - c * L);
+    const int64_t base = c * (int64_t)L;
+    float acc = 0.f;
+    for (int j = 0; j <= t; ++j)
+        acc = __builtin_fmaf(IO::load(v, base + j), IO::load(g, base + t - j), acc);
+    IO::store(r, base + t, acc);
+}
+
+template <int M, class IO>
+static hipError_t launch_fused_m(const void* v, const void* g, void* r, int64_t nch, int L,
+                                 int head, bool pair, const float2* tw, hipStream_t stream)
+{
+    constexpr int CPW = (FUSED_THREADS / (M / 16)) / 2;
+    const int64_t blocks = (nch + CPW - 1) / CPW;
+    hipLaunchKernelGGL((fused_conv_kernel<M, IO>), dim3((unsigned)blocks), dim3(FUSED_THREADS), 0,
+                       stream, (const typename IO::T*)v, (const typename IO::T*)g,
+                       (typename IO::T*)r, nch, L, head, pair ? 1 : 0, tw);
+    return hipGetLastError();
+}
+
+template <class IO>
+static hipError_t launch_fused_io(const void* v, const void* g, void* r, int64_t nch, int L, int M,
+                                  int head, bool pair, const float2* tw, hipStream_t s)
+{
+    switch (M) {
+    case 64: return launch_fused_m<64, IO>(v, g, r, nch, L, head, pair, tw, s);
+    case 128: return launch_fused_m<128, IO>(v, g, r, nch, L, head, pair, tw, s);
+    case 256: return launch_fused_m<256, IO>(v, g, r, nch, L, head, pair, tw, s);
+    case 512: return launch_fused_m<512, IO>(v, g, r, nch, L, head, pair, tw, s);
+    case 1024: return launch_fused_m<1024, IO>(v, g, r, nch, L, head, pair, tw, s);
+    case 2048: return launch_fused_m<2048, IO>(v, g, r, nch, L, head, pair, tw, s);
+    case 4096: return launch_fused_m<4096, IO>(v, g, r, nch, L, head, pair, tw, s);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+hipError_t launch_fused(Store st, const void* v, const void* g, void* r, int64_t nch, int L, int M,
+                        int head, bool pair_store, const float2* tw, hipStream_t stream)
+{
+    if (st == Store::F32)
+        return launch_fused_io<f32_io>(v, g, r, nch, L, M, head, pair_store, tw, stream);
+    return launch_fused_io<bf16_io>(v, g, r, nch, L, M, head, pair_store, tw, stream);
+}
+
+hipError_t launch_direct(Store st, const void* v, const void* g, void* r, int64_t nch, int L,
+                         hipStream_t stream)
+{
+    const int64_t total = nch * (int64_t)L;
+    const int threads = 256;
+    const int64_t blocks = (total + threads - 1) / threads;
+    if (st == Store::F32)
+        hipLaunchKernelGGL(direct_conv_kernel<f32_io>, dim3((unsigned)blocks), dim3(threads), 0,
+                           stream, (const float*)v, (const float*)g, (float*)r, nch, L);
+    else
+        hipLaunchKernelGGL(direct_conv_kernel<bf16_io>, dim3((unsigned)blocks), dim3(threads), 0,
+                           stream, (const uint16_t*)v, (const uint16_t*)g, (uint16_t*)r, nch, L);
+    return hipGetLastError();
+}
+
+}  // namespace sc

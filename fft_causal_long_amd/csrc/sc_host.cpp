@@ -1,0 +1,324 @@
+// libspecconv host layer: argument checks, per-device constant tables, path choice and
+// kernel launches behind the C ABI declared in include/specconv.h.
+#include "specconv.h"
+
+#include <climits>
+#include <cmath>
+#include <mutex>
+#include <new>
+#include <vector>
+
+#include "sc_internal.h"
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+constexpr int kDefaultHead = 32;
+constexpr int kMaxHead = 64;
+constexpr int64_t kMaxLFloat = 4096;     // fused path; longer sequences need the four-step path
+constexpr int64_t kMaxLNtt = 4096;
+constexpr int64_t kNttP = 998244353;
+
+sc_status upload(const void* host, size_t bytes, void** dev)
+{
+    void* p = nullptr;
+    if (hipMalloc(&p, bytes) != hipSuccess) return SC_ERR_HIP;
+    if (hipMemcpy(p, host, bytes, hipMemcpyHostToDevice) != hipSuccess) {
+        (void)hipFree(p);
+        return SC_ERR_HIP;
+    }
+    *dev = p;
+    return SC_OK;
+}
+
+struct DeviceState {
+    float2* fused_tw = nullptr;   // the float twiddle bank (sc_internal.h)
+    sc::NttTables ntt{};
+    bool ntt_ready = false;
+};
+
+uint64_t powmod(uint64_t b, uint64_t e, uint64_t m)
+{
+    uint64_t r = 1;
+    b %= m;
+    while (e) {
+        if (e & 1) r = (uint64_t)((unsigned __int128)r * b % m);
+        b = (uint64_t)((unsigned __int128)b * b % m);
+        e >>= 1;
+    }
+    return r;
+}
+
+// {w, floor(w * 2^32 / p)}
+uint2 shoup_pair(uint64_t w)
+{
+    return make_uint2((uint32_t)w, (uint32_t)((w << 32) / (uint64_t)kNttP));
+}
+
+sc_status build_ntt_tables(sc::NttTables* t)
+{
+    const uint64_t p = (uint64_t)kNttP;
+    const uint64_t w = powmod(3, (p - 1) / sc::FUSED_TW_N, p);
+    std::vector<uint2> h(sc::FUSED_TW_N);
+    uint64_t x = 1;
+    for (int i = 0; i < sc::FUSED_TW_N; ++i) {
+        h[i] = shoup_pair(x);
+        x = x * w % p;
+    }
+    void* d = nullptr;
+    sc_status st = upload(h.data(), h.size() * sizeof(uint2), &d);
+    if (st != SC_OK) return st;
+    t->tw = (const uint2*)d;
+    for (int k = 0; k < 24; ++k) {
+        const uint64_t ninv = powmod(powmod(2, (uint64_t)k, p), p - 2, p);
+        t->ninv_r[k] = shoup_pair((uint64_t)((unsigned __int128)ninv * ((uint64_t)1 << 32) % p));
+    }
+    return SC_OK;
+}
+
+std::mutex g_mu;
+DeviceState g_dev[kMaxDevices];
+
+// exp(-2 pi i k / n) in float64, rounded once to float32; exact zeros and ones on the axes
+float2 unit_root(int64_t k, int64_t n)
+{
+    k %= n;
+    if (k < 0) k += n;
+    if (4 * k == 0) return make_float2(1.f, 0.f);
+    if (4 * k == n) return make_float2(0.f, -1.f);
+    if (4 * k == 2 * n) return make_float2(-1.f, 0.f);
+    if (4 * k == 3 * n) return make_float2(0.f, 1.f);
+    const double a = 6.283185307179586476925286766559 * (double)k / (double)n;
+    return make_float2((float)std::cos(a), (float)-std::sin(a));
+}
+
+sc_status device_state(DeviceState** out, bool need_ntt)
+{
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return SC_ERR_HIP;
+    std::lock_guard<std::mutex> lk(g_mu);
+    DeviceState& d = g_dev[dev];
+    if (!d.fused_tw) {
+        std::vector<float2> h(sc::FUSED_BANK_FLOAT2);
+        for (int i = 0; i < sc::FUSED_TW_N; ++i) h[i] = unit_root(i, sc::FUSED_TW_N);
+        for (int Q = 32; Q <= 4096; Q *= 2)
+            for (int k = 0; k < 16; ++k)
+                for (int n = 0; n < Q / 16; ++n)
+                    h[sc::FUSED_TW_N + (Q - 32) + k * (Q / 16) + n] = unit_root((int64_t)n * k, Q);
+        void* p = nullptr;
+        sc_status st = upload(h.data(), h.size() * sizeof(float2), &p);
+        if (st != SC_OK) return st;
+        d.fused_tw = (float2*)p;
+    }
+    if (need_ntt && !d.ntt_ready) {
+        sc_status st = build_ntt_tables(&d.ntt);
+        if (st != SC_OK) return st;
+        d.ntt_ready = true;
+    }
+    *out = &d;
+    return SC_OK;
+}
+
+size_t elt_size(sc_kind k) { return k == SC_KIND_BF16 ? 2 : 4; }
+
+int64_t next_pow2(int64_t x)
+{
+    int64_t p = 1;
+    while (p < x) p <<= 1;
+    return p;
+}
+
+bool overlaps(const void* a, const void* b, uint64_t bytes)
+{
+    const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
+    return x < y + bytes && y < x + bytes;
+}
+
+// Host-side checks common to every entry point.  *n receives B*C*L.
+sc_status check_args(sc_kind kind, const void* v, const void* g, const void* r, int64_t B,
+                     int64_t C, int64_t L, int64_t* n)
+{
+    if (kind != SC_KIND_F32 && kind != SC_KIND_BF16 && kind != SC_KIND_NTT_I32)
+        return SC_ERR_INVALID_ARGUMENT;
+    if (B < 0 || C < 0 || L < 0) return SC_ERR_INVALID_ARGUMENT;
+    const size_t es = elt_size(kind);
+    const __int128 total = (__int128)B * (__int128)C * (__int128)L;
+    if (total * (__int128)es > (__int128)INT64_MAX) return SC_ERR_INVALID_ARGUMENT;
+    *n = (int64_t)total;
+    if (total == 0) return SC_OK;
+    if (!v || !g || !r) return SC_ERR_INVALID_ARGUMENT;
+    if (((uintptr_t)v | (uintptr_t)g | (uintptr_t)r) % es) return SC_ERR_INVALID_ARGUMENT;
+    const uint64_t bytes = (uint64_t)total * es;
+    if (overlaps(r, v, bytes) || overlaps(r, g, bytes)) return SC_ERR_INVALID_ARGUMENT;
+    return SC_OK;
+}
+
+sc_status resolve_path(sc_kind kind, int64_t L, int32_t requested, sc_path* out)
+{
+    const bool fl = kind != SC_KIND_NTT_I32;
+    switch (requested) {
+    case SC_PATH_AUTO:
+        if (!fl) {
+            if (L > kMaxLNtt) return SC_ERR_UNSUPPORTED;
+            *out = SC_PATH_FUSED;
+        } else if (L <= sc::DIRECT_MAX_L) {
+            *out = SC_PATH_DIRECT;
+        } else if (L <= kMaxLFloat) {
+            *out = SC_PATH_FUSED;
+        } else {
+            return SC_ERR_UNSUPPORTED;
+        }
+        return SC_OK;
+    case SC_PATH_FUSED:
+        if (L > (fl ? kMaxLFloat : kMaxLNtt)) return SC_ERR_UNSUPPORTED;
+        *out = SC_PATH_FUSED;
+        return SC_OK;
+    case SC_PATH_DIRECT:
+        if (!fl || L > kMaxLFloat) return SC_ERR_UNSUPPORTED;
+        *out = SC_PATH_DIRECT;
+        return SC_OK;
+    case SC_PATH_FOUR_STEP:
+        return SC_ERR_UNSUPPORTED;
+    default:
+        return SC_ERR_INVALID_ARGUMENT;
+    }
+}
+
+sc_status run(sc_kind kind, const void* v, const void* g, void* r, int64_t B, int64_t C,
+              int64_t L, const sc_options* opt, void* ws, size_t ws_bytes, hipStream_t stream)
+{
+    (void)ws;
+    (void)ws_bytes;
+    int64_t n = 0;
+    sc_status st = check_args(kind, v, g, r, B, C, L, &n);
+    if (st != SC_OK) return st;
+    int32_t req = SC_PATH_AUTO, head = kDefaultHead;
+    if (opt) {
+        for (int i = 0; i < 6; ++i)
+            if (opt->reserved[i]) return SC_ERR_INVALID_ARGUMENT;
+        req = opt->path;
+        if (opt->head != -1) {
+            if (opt->head < 0 || opt->head > kMaxHead) return SC_ERR_INVALID_ARGUMENT;
+            head = (opt->head + 1) & ~1;
+        }
+    }
+    sc_path path;
+    st = resolve_path(kind, L, req, &path);
+    if (st != SC_OK) return st;
+    if (n == 0) return SC_OK;
+    const int64_t nch = B * C;
+
+    DeviceState* d = nullptr;
+    st = device_state(&d, kind == SC_KIND_NTT_I32);
+    if (st != SC_OK) return st;
+
+    hipError_t e = hipSuccess;
+    if (kind == SC_KIND_NTT_I32) {
+        const int M = (int)std::max<int64_t>(64, next_pow2(L));
+        e = sc::launch_ntt((const int32_t*)v, (const int32_t*)g, (int32_t*)r, nch, (int)L, M,
+                           d->ntt, stream);
+    } else {
+        const sc::Store s = kind == SC_KIND_F32 ? sc::Store::F32 : sc::Store::BF16;
+        if (path == SC_PATH_DIRECT) {
+            e = sc::launch_direct(s, v, g, r, nch, (int)L, stream);
+        } else {
+            const int M = (int)std::max<int64_t>(64, next_pow2(L));
+            const bool pair = (L % 2 == 0) && ((uintptr_t)r % (2 * elt_size(kind)) == 0);
+            e = sc::launch_fused(s, v, g, r, nch, (int)L, M, head, pair, d->fused_tw, stream);
+        }
+    }
+    return e == hipSuccess ? SC_OK : SC_ERR_HIP;
+}
+
+template <class F>
+sc_status guarded(F&& f)
+{
+    try {
+        return f();
+    } catch (...) {
+        return SC_ERR_HIP;
+    }
+}
+
+}  // namespace
+
+extern "C" {
+
+sc_status sc_causal_conv_f32(const float* v, const float* g, float* r, int64_t B, int64_t C,
+                             int64_t L, hipStream_t stream)
+{
+    return guarded([&] { return run(SC_KIND_F32, v, g, r, B, C, L, nullptr, nullptr, 0, stream); });
+}
+
+sc_status sc_causal_conv_bf16(const uint16_t* v, const uint16_t* g, uint16_t* r, int64_t B,
+                              int64_t C, int64_t L, hipStream_t stream)
+{
+    return guarded([&] { return run(SC_KIND_BF16, v, g, r, B, C, L, nullptr, nullptr, 0, stream); });
+}
+
+sc_status sc_causal_conv_ntt_i32(const int32_t* v, const int32_t* g, int32_t* r, int64_t B,
+                                 int64_t C, int64_t L, hipStream_t stream)
+{
+    return guarded(
+        [&] { return run(SC_KIND_NTT_I32, v, g, r, B, C, L, nullptr, nullptr, 0, stream); });
+}
+
+size_t sc_workspace_bytes(sc_kind kind, int64_t B, int64_t C, int64_t L)
+{
+    (void)kind;
+    (void)B;
+    (void)C;
+    (void)L;
+    return 0;
+}
+
+sc_status sc_causal_conv_f32_ws(const float* v, const float* g, float* r, int64_t B, int64_t C,
+                                int64_t L, void* ws, size_t ws_bytes, hipStream_t stream)
+{
+    return guarded([&] { return run(SC_KIND_F32, v, g, r, B, C, L, nullptr, ws, ws_bytes, stream); });
+}
+
+sc_status sc_causal_conv_bf16_ws(const uint16_t* v, const uint16_t* g, uint16_t* r, int64_t B,
+                                 int64_t C, int64_t L, void* ws, size_t ws_bytes,
+                                 hipStream_t stream)
+{
+    return guarded([&] { return run(SC_KIND_BF16, v, g, r, B, C, L, nullptr, ws, ws_bytes, stream); });
+}
+
+sc_status sc_causal_conv_ntt_i32_ws(const int32_t* v, const int32_t* g, int32_t* r, int64_t B,
+                                    int64_t C, int64_t L, void* ws, size_t ws_bytes,
+                                    hipStream_t stream)
+{
+    return guarded(
+        [&] { return run(SC_KIND_NTT_I32, v, g, r, B, C, L, nullptr, ws, ws_bytes, stream); });
+}
+
+sc_status sc_causal_conv_ex(sc_kind kind, const void* v, const void* g, void* r, int64_t B,
+                            int64_t C, int64_t L, const sc_options* opt, void* ws,
+                            size_t ws_bytes, hipStream_t stream)
+{
+    return guarded([&] { return run(kind, v, g, r, B, C, L, opt, ws, ws_bytes, stream); });
+}
+
+int sc_ntt_range_ok(int64_t max_abs_v, int64_t max_abs_g, int64_t L)
+{
+    if (max_abs_v < 0 || max_abs_g < 0 || L < 0) return 0;
+    const __int128 worst = (__int128)L * (__int128)max_abs_v * (__int128)max_abs_g;
+    return worst <= (__int128)((kNttP - 1) / 2) ? 1 : 0;
+}
+
+const char* sc_status_string(sc_status s)
+{
+    switch (s) {
+    case SC_OK: return "SC_OK";
+    case SC_ERR_INVALID_ARGUMENT: return "SC_ERR_INVALID_ARGUMENT";
+    case SC_ERR_UNSUPPORTED: return "SC_ERR_UNSUPPORTED";
+    case SC_ERR_HIP: return "SC_ERR_HIP";
+    case SC_ERR_WORKSPACE: return "SC_ERR_WORKSPACE";
+    default: return "SC_STATUS_UNKNOWN";
+    }
+}
+
+int sc_version(void) { return 100; }
+
+}  // extern "C"

@@ -1,0 +1,43 @@
+// Internal (non-exported) interface between the host ABI layer and the kernel files.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace sc {
+
+// Length of the shared float twiddle table used by the fused path: tw[i] = W_8192^i.
+constexpr int FUSED_TW_N = 8192;
+// The float twiddle bank: W_8192^i (i < 8192), then for each pass length Q = 32..4096 a
+// table of W_Q^{n k} stored row k (k < 16), column n (n < Q/16): Q entries per Q.
+constexpr int FUSED_BANK_FLOAT2 = FUSED_TW_N + (4096 * 2 - 32);
+// Largest sequence length handled by the one-workgroup-per-channel (fused) kernels.
+constexpr int FUSED_MAX_L = 4096;
+// Sequences up to this length are computed entirely by direct summation.
+constexpr int DIRECT_MAX_L = 32;
+
+enum class Store { F32, BF16 };
+
+// Fused in-LDS causal convolution for DIRECT_MAX_L < L <= FUSED_MAX_L.
+// M = next power of two >= L.  head = number of leading outputs computed directly (even).
+hipError_t launch_fused(Store st, const void* v, const void* g, void* r, int64_t nch, int L,
+                        int M, int head, bool pair_store, const float2* tw, hipStream_t stream);
+
+// Constants of the exact path modulo p = 998244353.  tw[i] = {w, floor(w 2^32 / p)} with
+// w = omega_8192^i (omega_8192 = 3^((p-1)/8192)); ninv_r[k] = {c, floor(c 2^32 / p)} with
+// c = (2^k)^{-1} * 2^32 mod p.
+struct NttTables {
+    const uint2* tw = nullptr;
+    uint2 ninv_r[24];
+};
+
+// Exact NTT causal convolution for L <= FUSED_MAX_L, M = max(64, next power of two >= L).
+hipError_t launch_ntt(const int32_t* v, const int32_t* g, int32_t* r, int64_t nch, int L, int M,
+                      const NttTables& tables, hipStream_t stream);
+
+// Direct summation r_t = sum_{j<=t} v_j g_{t-j} in fp32, one thread per output.
+hipError_t launch_direct(Store st, const void* v, const void* g, void* r, int64_t nch, int L,
+                         hipStream_t stream);
+
+}  // namespace sc

@@ -1,0 +1,175 @@
+/*
+ * libspecconv -- batched per-channel causal long convolution on AMD Instinct MI355X (gfx950).
+ *
+ * The operation (one "channel" = one (b, c) pair, sequences of length L):
+ *
+ *     r[b][c][t] = sum_{j=0..t} v[b][c][j] * g[b][c][t-j],      t = 0 .. L-1
+ *
+ * "Caracal: Causal Architecture via Spectral Mixing" (key design 1, the multi-head Fourier
+ * module) computes it as: zero-pad v and the data-dependent gate stream g on the right to
+ * 2L, FFT both, multiply the spectra bin by bin, inverse FFT, keep the first L values; key
+ * design 2 (the frequency-domain causal mask) explains why the truncated 2L circular
+ * convolution equals this causal sum.  Every channel has its own g (the gate stream is
+ * produced from the input), so nothing is shared between channels.
+ *
+ * "Catastrophic Token Leakage in Convolutional Sequence Modeling and How to Mitigate It"
+ * (abstract) shows that float FFT convolutions leak future tokens through round-off and
+ * proposes number-theoretic transforms on integers, which cannot: sc_causal_conv_ntt_i32
+ * is that exact path, modulo the prime p = 998244353 (primitive root 3).
+ *
+ * Conventions shared by every entry point below
+ * --------------------------------------------
+ *  - Layout: v, g, r are dense row-major [B][C][L] arrays, t contiguous (stride 1), channel
+ *    (b, c) at offset (b*C + c)*L.  B, C, L are element counts, not bytes.
+ *  - Memory: v, g, r (and ws) are DEVICE pointers on the current HIP device, owned by the
+ *    caller.  The library keeps no pointer after a call returns.
+ *  - Asynchrony: work is enqueued on `stream` (0 = the null stream) and the call returns
+ *    without waiting.  The caller keeps every buffer alive, and does not touch r, until the
+ *    stream has passed the work.  Faults during execution surface at the caller's sync.
+ *  - Determinism: for the same inputs and arguments the output is bitwise identical from
+ *    run to run (fixed reduction order, no atomics).
+ *  - Errors: status codes only; nothing is printed, no call aborts, no C++ exception crosses
+ *    the boundary.  Arguments are checked on the host before any HIP call:
+ *      B, C or L negative, a null pointer with B*C*L > 0, a pointer not aligned to its
+ *      element size, r overlapping v or g, byte sizes overflowing int64
+ *                                              -> SC_ERR_INVALID_ARGUMENT
+ *      B*C*L == 0                              -> SC_OK, nothing enqueued
+ *      L above the path's maximum               -> SC_ERR_UNSUPPORTED
+ *      a workspace smaller than required        -> SC_ERR_WORKSPACE
+ *      a failed HIP call or kernel launch       -> SC_ERR_HIP
+ *  - Library-owned state: per-device constant tables (twiddles, modular constants), built on
+ *    the first call on a device (a blocking host-to-device copy) and kept until the process
+ *    ends.  Calls from several host threads are safe.
+ *  - Any L >= 1 is accepted; internally N = 2M with M the next power of two >= L.
+ *    Throughput is best for powers of two.
+ *  - Inputs of the float paths must be finite.  (A NaN or Inf at v_s reaches every output of
+ *    its channel through the transform, including t < s, whereas the causal sum would only
+ *    reach t >= s.)
+ */
+#ifndef SPECCONV_H
+#define SPECCONV_H
+
+#include <hip/hip_runtime_api.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum sc_status {
+    SC_OK = 0,
+    SC_ERR_INVALID_ARGUMENT = 1,
+    SC_ERR_UNSUPPORTED = 2,
+    SC_ERR_HIP = 3,
+    SC_ERR_WORKSPACE = 4
+} sc_status;
+
+typedef enum sc_kind {
+    SC_KIND_F32 = 0,     /* float32 storage, float32 arithmetic                    */
+    SC_KIND_BF16 = 1,    /* bfloat16 storage, float32 arithmetic                   */
+    SC_KIND_NTT_I32 = 2  /* int32 storage, exact arithmetic in Z_p, p = 998244353   */
+} sc_kind;
+
+typedef enum sc_path {
+    SC_PATH_AUTO = 0,      /* the library's choice (below)                         */
+    SC_PATH_FUSED = 1,     /* one workgroup per channel, transform held in LDS     */
+    SC_PATH_FOUR_STEP = 2, /* column / twiddle / row transforms staged through HBM  */
+    SC_PATH_DIRECT = 3     /* direct fp32 summation (float kinds, small L only)     */
+} sc_path;
+
+/* Optional controls for sc_causal_conv_ex (testing and experiments). */
+typedef struct sc_options {
+    int32_t path;      /* sc_path; SC_PATH_AUTO picks: L <= 32 direct, L <= 4096 fused,
+                          larger L four-step                                          */
+    int32_t head;      /* float kinds: outputs t < head are computed by direct fp32
+                          summation instead of the transform.  -1 = default (32);
+                          0 disables; odd values are rounded up to even; at most 64.  */
+    int32_t reserved[6]; /* must be zero */
+} sc_options;
+
+/*
+ * sc_causal_conv_f32 -- r = causal_conv(v, g), float32 in and out.
+ *   Pad-to-2L FFT method of the Caracal notes (key designs 1-2) in fp32 arithmetic.
+ *   Accuracy: |r_t - exact_t| <= 1e-4 * sum_{j<=t} |v_j||g_{t-j}| for the inputs this
+ *   library is tested on (the first 32 outputs use direct summation).
+ *   L <= 4096 runs fused in LDS and allocates nothing.  L > 4096 uses the four-step path,
+ *   which needs sc_workspace_bytes(SC_KIND_F32, B, C, L) bytes of device scratch; this call
+ *   allocates it stream-ordered on `stream` (hipMallocAsync/hipFreeAsync).  Use
+ *   sc_causal_conv_f32_ws to supply it instead.  Largest L: 4,194,304.
+ */
+sc_status sc_causal_conv_f32(const float* v, const float* g, float* r, int64_t B, int64_t C,
+                             int64_t L, hipStream_t stream);
+
+/*
+ * sc_causal_conv_bf16 -- as sc_causal_conv_f32 with bfloat16 storage.
+ *   v, g, r hold bfloat16 bit patterns (uint16_t).  Inputs are widened exactly to fp32,
+ *   all arithmetic is fp32, and each output is rounded once to bfloat16 (nearest, ties to
+ *   even).  Accuracy: the fp32 bound plus one bf16 rounding, 2^-8 |r_t|.
+ */
+sc_status sc_causal_conv_bf16(const uint16_t* v, const uint16_t* g, uint16_t* r, int64_t B,
+                              int64_t C, int64_t L, hipStream_t stream);
+
+/*
+ * sc_causal_conv_ntt_i32 -- exact causal convolution of int32 sequences through a
+ *   number-theoretic transform modulo p = 998244353 ("Catastrophic Token Leakage ...",
+ *   abstract: an FFT executed on integers only, which provably leaks no future token).
+ *   Inputs are reduced into Z_p (x < 0 -> x + p after reduction).  Output:
+ *       r_t = the residue of sum_{j<=t} v_j g_{t-j} mod p, in [-(p-1)/2, (p-1)/2].
+ *   It equals the integer sum whenever |sum| <= (p-1)/2 = 499,122,176: a caller
+ *   precondition (see sc_ntt_range_ok).  Output t depends on v_0..v_t, g_0..g_t only, bit
+ *   for bit.  Largest L: 4096 (the transform is held in LDS); no allocation.
+ */
+sc_status sc_causal_conv_ntt_i32(const int32_t* v, const int32_t* g, int32_t* r, int64_t B,
+                                 int64_t C, int64_t L, hipStream_t stream);
+
+/*
+ * sc_workspace_bytes -- device scratch bytes a call of this kind and shape needs
+ *   (0 when the chosen path needs none, e.g. the fused path).  Returns 0 for invalid
+ *   arguments as well.
+ */
+size_t sc_workspace_bytes(sc_kind kind, int64_t B, int64_t C, int64_t L);
+
+/*
+ * sc_causal_conv_*_ws -- as above, with caller-owned scratch: ws (device pointer, 256-byte
+ *   aligned) of ws_bytes bytes.  ws_bytes below sc_workspace_bytes(...) -> SC_ERR_WORKSPACE.
+ *   ws may be null when the requirement is 0.  The library never allocates in these calls.
+ *   The caller keeps ws alive and unshared until the stream has passed the work.
+ */
+sc_status sc_causal_conv_f32_ws(const float* v, const float* g, float* r, int64_t B, int64_t C,
+                                int64_t L, void* ws, size_t ws_bytes, hipStream_t stream);
+sc_status sc_causal_conv_bf16_ws(const uint16_t* v, const uint16_t* g, uint16_t* r, int64_t B,
+                                 int64_t C, int64_t L, void* ws, size_t ws_bytes,
+                                 hipStream_t stream);
+sc_status sc_causal_conv_ntt_i32_ws(const int32_t* v, const int32_t* g, int32_t* r, int64_t B,
+                                    int64_t C, int64_t L, void* ws, size_t ws_bytes,
+                                    hipStream_t stream);
+
+/*
+ * sc_causal_conv_ex -- any kind, with options (opt may be null = defaults) and an optional
+ *   caller workspace (ws null and ws_bytes 0: allocate stream-ordered when needed).
+ *   v, g, r point to elements of the kind's storage type.  A path that cannot serve the
+ *   kind and L -> SC_ERR_UNSUPPORTED; nonzero reserved fields -> SC_ERR_INVALID_ARGUMENT.
+ */
+sc_status sc_causal_conv_ex(sc_kind kind, const void* v, const void* g, void* r, int64_t B,
+                            int64_t C, int64_t L, const sc_options* opt, void* ws,
+                            size_t ws_bytes, hipStream_t stream);
+
+/*
+ * sc_ntt_range_ok -- 1 if every |v_j| <= max_abs_v and |g_j| <= max_abs_g guarantee that
+ *   the exact sums fit the symmetric residue range, i.e. L * max_abs_v * max_abs_g <=
+ *   (p-1)/2; 0 otherwise (or on negative arguments).  Host only.
+ */
+int sc_ntt_range_ok(int64_t max_abs_v, int64_t max_abs_g, int64_t L);
+
+/* Human-readable name of a status code (static storage).  Host only. */
+const char* sc_status_string(sc_status s);
+
+/* Library version: major * 10000 + minor * 100 + patch.  Host only. */
+int sc_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SPECCONV_H */

@@ -1,0 +1,115 @@
+"""The C ABI without a GPU: the library loads, exports every symbol include/specconv.h
+declares, and rejects bad arguments on the host before any HIP call (CPU only; no call
+here reaches a kernel launch)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "specconv.h")
+LIB = os.path.join(ROOT, "fft_causal_long_amd", "libspecconv.so")
+
+
+@pytest.fixture(scope="module")
+def sc():
+    if not os.path.exists(LIB):
+        from fft_causal_long_amd import build as b  # noqa: F401  (package import needs the .so)
+    import importlib.util
+    if not os.path.exists(LIB):
+        spec = importlib.util.spec_from_file_location(
+            "sc_build", os.path.join(ROOT, "fft_causal_long_amd", "build.py"))
+        mod = importlib.util.module_from_spec(spec)
+        spec.loader.exec_module(mod)
+        mod.build()
+    import fft_causal_long_amd as m
+    return m
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(sc_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for n in ("sc_causal_conv_f32", "sc_causal_conv_bf16", "sc_causal_conv_ntt_i32",
+              "sc_workspace_bytes", "sc_causal_conv_ex", "sc_status_string", "sc_version",
+              "sc_ntt_range_ok"):
+        assert n in names
+
+
+def test_every_declared_symbol_is_exported(sc):
+    h = sc.lib()
+    for n in declared_functions():
+        assert hasattr(h, n), n
+    out = subprocess.run(["nm", "-D", "--defined-only", LIB], capture_output=True, text=True).stdout
+    exported = set(re.findall(r" T (sc_\w+)", out))
+    assert set(declared_functions()) <= exported
+    # nothing but the C ABI leaks out under the sc_ prefix
+    assert exported <= set(declared_functions())
+
+
+def test_links_hip_runtime_by_soname():
+    out = subprocess.run(["readelf", "-d", LIB], capture_output=True, text=True).stdout
+    assert "libamdhip64.so.7" in out
+
+
+A, B_, C_ = 0x100000, 0x200000, 0x300000   # fake, never dereferenced
+
+
+@pytest.mark.parametrize("fn", ["sc_causal_conv_f32", "sc_causal_conv_bf16", "sc_causal_conv_ntt_i32"])
+def test_host_validation(sc, fn):
+    f = getattr(sc.lib(), fn)
+    INVALID, OK = sc.SC_ERR_INVALID_ARGUMENT, sc.SC_OK
+    assert f(A, B_, C_, -1, 1, 1, None) == INVALID
+    assert f(A, B_, C_, 1, -1, 1, None) == INVALID
+    assert f(A, B_, C_, 1, 1, -5, None) == INVALID
+    assert f(None, B_, C_, 1, 1, 4, None) == INVALID
+    assert f(A, None, C_, 1, 1, 4, None) == INVALID
+    assert f(A, B_, None, 1, 1, 4, None) == INVALID
+    assert f(A + 1, B_, C_, 1, 1, 4, None) == INVALID          # misaligned
+    assert f(A, B_, A, 1, 1, 4, None) == INVALID               # r aliases v
+    assert f(A, B_, B_ + 4, 1, 1, 4, None) == INVALID           # r overlaps g
+    assert f(A, B_, C_, 2**40, 2**40, 2**40, None) == INVALID  # size overflow
+    # empty problems are a successful no-op, even with null pointers
+    assert f(None, None, None, 0, 7, 9, None) == OK
+    assert f(None, None, None, 3, 7, 0, None) == OK
+
+
+def test_unsupported_lengths_rejected_before_launch(sc):
+    h = sc.lib()
+    UNSUP = sc.SC_ERR_UNSUPPORTED
+    assert h.sc_causal_conv_ntt_i32(A, B_, C_, 1, 1, 5000, None) == UNSUP
+
+
+def test_options_validation(sc):
+    h = sc.lib()
+    INVALID = sc.SC_ERR_INVALID_ARGUMENT
+    opt = sc.sc_options(0, -1)
+    opt.reserved[2] = 1
+    assert h.sc_causal_conv_ex(0, A, B_, C_, 1, 1, 64, ctypes.byref(opt), None, 0, None) == INVALID
+    opt = sc.sc_options(0, 65)
+    assert h.sc_causal_conv_ex(0, A, B_, C_, 1, 1, 64, ctypes.byref(opt), None, 0, None) == INVALID
+    opt = sc.sc_options(9, -1)
+    assert h.sc_causal_conv_ex(0, A, B_, C_, 1, 1, 64, ctypes.byref(opt), None, 0, None) == INVALID
+    opt = sc.sc_options(sc.PATH_DIRECT, -1)    # direct summation is float only
+    assert h.sc_causal_conv_ex(2, A, B_, C_, 1, 1, 64, ctypes.byref(opt), None, 0, None) == \
+        sc.SC_ERR_UNSUPPORTED
+    assert h.sc_causal_conv_ex(7, A, B_, C_, 1, 1, 64, None, None, 0, None) == INVALID
+
+
+def test_host_helpers(sc):
+    assert sc.sc_ntt_range_ok(127, 127, 4096)                  # 66,064,384
+    assert sc.sc_ntt_range_ok(1, 499122176, 1)
+    assert not sc.sc_ntt_range_ok(1, 499122177, 1)
+    assert not sc.sc_ntt_range_ok(2**40, 2**40, 2**40)        # no overflow
+    assert not sc.sc_ntt_range_ok(-1, 1, 1)
+    assert sc.sc_status_string(0) == "SC_OK"
+    assert sc.sc_status_string(4) == "SC_ERR_WORKSPACE"
+    assert sc.sc_status_string(99) == "SC_STATUS_UNKNOWN"
+    assert sc.sc_version() >= 100
+    assert sc.sc_workspace_bytes(sc.KIND_F32, 8, 1024, 4096) == 0

@@ -1,0 +1,175 @@
+"""GPU parity of the float paths (fp32 and bf16 storage) against the float64 oracle.
+
+Every case calls libspecconv through its C ABI (via the ctypes binding) on seeded
+synthetic inputs and compares element by element with the oracle on the same stored
+inputs, within the per-output bound of tests/gpu_util.py.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from tests.gpu_util import assert_within_bound, decode, to_device, to_host
+from workloads import WORKLOADS, make_inputs
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def sc():
+    import fft_causal_long_amd as m
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    return m
+
+
+def run(sc, v, g, **kw):
+    tv, tg = to_device(v), to_device(g)
+    out = sc.causal_conv(tv, tg, **kw)
+    torch.cuda.synchronize()
+    return to_host(out)
+
+
+def check(sc, v, g, what, **kw):
+    r = run(sc, v, g, **kw)
+    r_ref, S = oracle.causal_conv_f64(v, g)
+    worst = assert_within_bound(r, r_ref, S, v.dtype == np.uint16, what)
+    print("%s: worst err/bound = %.3g" % (what, worst), flush=True)
+    return r, worst
+
+
+def test_config1_tiny_full(sc):
+    v, g = make_inputs(WORKLOADS[1])
+    check(sc, v, g, "config1")
+
+
+def test_config2_small_full(sc):
+    v, g = make_inputs(WORKLOADS[2])
+    check(sc, v, g, "config2")
+
+
+LS = [1, 2, 3, 5, 16, 31, 32, 33, 47, 63, 64, 65, 100, 127, 128, 129, 255, 256, 257, 300,
+      511, 512, 513, 1000, 1023, 1024, 1025, 2047, 2048, 2049, 3001, 4095, 4096]
+
+
+@pytest.mark.parametrize("L", LS)
+def test_length_sweep_f32(sc, L):
+    # 15 channels: not a multiple of the channels-per-workgroup of any small M
+    v, g = make_inputs(WORKLOADS[1], B=3, C=5, L=L, seed_offset=L)
+    check(sc, v, g, "f32 L=%d" % L)
+
+
+@pytest.mark.parametrize("L", [33, 64, 257, 1024, 2049, 4096])
+def test_length_sweep_bf16_conv_gate(sc, L):
+    v, g = make_inputs(WORKLOADS[3], B=2, C=16, L=L, seed_offset=L)
+    check(sc, v, g, "bf16 L=%d" % L)
+
+
+@pytest.mark.parametrize("L", [256, 1024, 4096])
+def test_fp32_conv_gate_shapes(sc, L):
+    v, g = make_inputs(WORKLOADS[2], B=2, C=64, L=L, seed_offset=7 + L)
+    check(sc, v, g, "f32 conv-gate L=%d" % L)
+
+
+def test_config3_full_size_sampled(sc):
+    # full Caracal-Medium shape in the launch configuration the benchmark times; the
+    # oracle checks 96 whole channels spread over the batch
+    w = WORKLOADS[3]
+    v, g = make_inputs(w)
+    r = run(sc, v, g)
+    nch = w.B * w.C
+    chans = np.unique(np.concatenate([[0, nch - 1], np.random.default_rng(3).integers(0, nch, 94)]))
+    vs = v.reshape(nch, w.L)[chans]
+    gs = g.reshape(nch, w.L)[chans]
+    r_ref, S = oracle.causal_conv_f64(vs, gs)
+    worst = assert_within_bound(r.reshape(nch, w.L)[chans], r_ref, S, True, "config3 sampled")
+    print("config3 sampled: worst err/bound = %.3g" % worst, flush=True)
+
+
+def test_config3_shape_as_fp32_sampled(sc):
+    w = WORKLOADS[3]
+    v, g = make_inputs(w, B=2)
+    v32, g32 = decode(v).astype(np.float32), decode(g).astype(np.float32)
+    r = run(sc, v32, g32)
+    chans = np.arange(0, 2 * w.C, 37)
+    r_ref, S = oracle.causal_conv_f64(v32.reshape(-1, w.L)[chans], g32.reshape(-1, w.L)[chans])
+    assert_within_bound(r.reshape(-1, w.L)[chans], r_ref, S, False, "config3 fp32 sampled")
+
+
+def test_bitwise_deterministic(sc):
+    v, g = make_inputs(WORKLOADS[2], B=1, C=128, L=1024)
+    a = run(sc, v, g)
+    b = run(sc, v, g)
+    assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+    v, g = make_inputs(WORKLOADS[3], B=1, C=64, L=4096)
+    a = run(sc, v, g)
+    b = run(sc, v, g)
+    assert np.array_equal(a, b)
+
+
+def test_side_stream_and_offsets(sc):
+    v, g = make_inputs(WORKLOADS[1], B=1, C=9, L=500)
+    r_ref, S = oracle.causal_conv_f64(v, g)
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        tv, tg = to_device(v), to_device(g)
+        # an output that is 4-byte but not 8-byte aligned (paired stores must be avoided)
+        buf = torch.empty(v.size + 1, dtype=torch.float32, device="cuda:0")
+        out = buf[1:].view(v.shape)
+        sc.causal_conv(tv, tg, out=out)
+    s.synchronize()
+    assert_within_bound(to_host(out), r_ref, S, False, "side stream, offset output")
+
+
+def test_paths_agree_with_oracle(sc):
+    v, g = make_inputs(WORKLOADS[1], B=1, C=6, L=200, seed_offset=3)
+    for path in (sc.PATH_DIRECT, sc.PATH_FUSED):
+        check(sc, v, g, "path %d" % path, path=path)
+    # fused path for a length the automatic choice sends to direct summation
+    v, g = make_inputs(WORKLOADS[1], B=1, C=6, L=20, seed_offset=4)
+    check(sc, v, g, "forced fused L=20", path=sc.PATH_FUSED)
+
+
+@pytest.mark.parametrize("L", [256, 1024])
+def test_head_length_option(sc, L):
+    v, g = make_inputs(WORKLOADS[1], B=1, C=64, L=L, seed_offset=5)
+    r_ref, S = oracle.causal_conv_f64(v, g)
+    r0 = run(sc, v, g, head=0)        # every output from the transform
+    r64 = run(sc, v, g, head=64)
+    assert_within_bound(r64, r_ref, S, False, "head=64")
+    # outputs from t = 64 on are the same computation in both runs
+    assert np.array_equal(r0[..., 64:], r64[..., 64:])
+    # with head = 0 the transform's global round-off is visible at t = 0
+    assert np.abs(r0[..., 0] - r_ref[..., 0]).max() > 0.0
+
+
+def test_empty_is_noop(sc):
+    for shape in ((0, 4, 16), (2, 0, 16), (2, 4, 0)):
+        t = torch.zeros(shape, dtype=torch.float32, device="cuda:0")
+        out = sc.causal_conv(t, t.clone())
+        assert out.shape == shape
+
+
+def test_fp32_leakage_is_small_but_reported(sc):
+    # "Catastrophic Token Leakage ..." (abstract): a float FFT convolution lets a change at
+    # position s move outputs t < s through round-off.  Measure max_{t<s} |dr_t| with the
+    # original and perturbed rows in one launch.
+    from workloads import perturbation_positions
+    w = WORKLOADS[3]
+    L = w.L
+    v, g = make_inputs(w, B=1, C=16)
+    v32, g32 = decode(v).astype(np.float32), decode(g).astype(np.float32)
+    pos = perturbation_positions(w.cid, L)
+    vv = np.concatenate([v32] + [v32.copy() for _ in pos], axis=0)
+    gg = np.concatenate([g32] * (len(pos) + 1), axis=0)
+    for i, s in enumerate(pos):
+        vv[i + 1, :, s] += 1.0
+    r = run(sc, vv, gg)
+    leak = 0.0
+    for i, s in enumerate(pos):
+        d = np.abs(r[i + 1, :, :s].astype(np.float64) - r[0, :, :s].astype(np.float64))
+        if d.size:
+            leak = max(leak, float(d.max()))
+    rms = float(np.sqrt(np.mean(r[0].astype(np.float64) ** 2)))
+    print("fp32 leakage max_{t<s}|dr_t| = %.3g (rms r = %.3g)" % (leak, rms), flush=True)
+    assert np.isfinite(leak)
+    assert leak < 1e-3 * rms     # round-off sized, not a structural leak

@@ -91,16 +91,19 @@ def _grouped_causal_conv3(s: np.ndarray, w: np.ndarray, groups: int) -> np.ndarr
     with s[..., tau < 0] = 0 (causal left padding of 2, PyTorch tap order)."""
     B, C, L = s.shape
     cg = C // groups
-    sg = s.reshape(B, groups, cg, L)
     wg = w.reshape(groups, cg, cg, 3)
-    out = np.zeros((B, groups, cg, L), dtype=np.float64)
-    for k in range(3):
-        shift = 2 - k
-        sh = np.zeros_like(sg)
-        if shift < L:
-            sh[..., shift:] = sg[..., : L - shift]
-        out += np.matmul(wg[None, :, :, :, k], sh)
-    return out.reshape(B, C, L)
+    taps = [np.ascontiguousarray(wg[:, :, :, k]) for k in range(3)]
+    out = np.empty((B, C, L), dtype=np.float64)
+    for b in range(B):
+        for gi in range(groups):
+            blk = s[b, gi * cg:(gi + 1) * cg]          # (cg, L) inputs of this group
+            acc = taps[2][gi] @ blk                     # tap k=2 reads s[t]
+            if L > 1:
+                acc[:, 1:] += taps[1][gi] @ blk[:, :-1]  # tap k=1 reads s[t-1]
+            if L > 2:
+                acc[:, 2:] += taps[0][gi] @ blk[:, :-2]  # tap k=0 reads s[t-2]
+            out[b, gi * cg:(gi + 1) * cg] = acc
+    return out
 
 
 def make_inputs(w: Workload, B: int | None = None, C: int | None = None,
