@@ -1,0 +1,389 @@
+// Four-step (HBM-staged) causal long convolution for 4096 < L (gfx950).
+//
+// Same method as the fused kernel ("Caracal: Causal Architecture via Spectral Mixing", key
+// designs 1 and 2: pad to N = 2M, FFT, multiply, inverse FFT, truncate), with the same
+// reductions: z = v + i g packed into one complex sequence, the zero upper half turned
+// into two length-M branch transforms U^b = DFT_M(z_n W_N^{b n}), the spectral product
+// and the real-output inverse formed from bin quadruples.  When 2M complex values no
+// longer fit the LDS of one CU, each length-M transform is split as M = M1 * M2:
+//
+//   U_{M1 k1 + k2} = sum_{n1<M2} W_M2^{n1 k1} [ W_M^{n1 k2} sum_{n2<M1} u_{n1 + M2 n2} W_M1^{n2 k2} ]
+//
+//  kernel A (columns): for every column n1 the length-M1 DFT over n2, times W_M^{n1 k2},
+//     stored as T^b[k2][n1] (both branches, z read once).
+//  kernel B (rows): the length-M2 DFT of rows k2 and of the mirror row M1 - k2 - b, which
+//     hold every bin of the quadruples {j, M-j-b, M/2-j-b, M/2+j}; the product and the
+//     real-output inverse spectrum Y^b_i = Y_{2i+b} (i = M1 i1 + i2, row i2 of length
+//     M2/2); the length-M2/2 inverse DFT of each Y row and the twiddle W_{M/2}^{-m1 i2},
+//     stored as S^b[i2][m1].
+//  kernel C (columns): the length-M1 inverse DFT over i2 gives e (b = 0) and o (b = 1) at
+//     m = m1 + (M2/2) m2; y_m = (e_m + W_M^{-m} o_m) / (8M) = x_{2m} + i x_{2m+1}.
+//  A small kernel recomputes the first `head` outputs by direct fp32 summation.
+//
+// HBM traffic per channel: read v, g; write and read T (2M complex) and S (M complex);
+// write r.  Channels are processed in chunks so T and S can stay in the last-level cache.
+
+#include "sc_device.h"
+#include "sc_fft_lds.h"
+#include "sc_internal.h"
+
+namespace sc {
+
+// W_N^e from the two-level table: W_N^{(e >> fbits) << fbits} * W_N^{e & (F-1)}
+__device__ __forceinline__ float2 big_tw(const BigTw& t, int e)
+{
+    e &= t.n - 1;
+    return cmul(t.coarse[e >> t.fbits], t.fine[e & ((1 << t.fbits) - 1)]);
+}
+
+// ---------------------------------------------------------------- kernel A: columns, forward
+
+template <int M1, class IO>
+__global__ __launch_bounds__(512) void fs_columns_fwd(const typename IO::T* __restrict__ v,
+                                                      const typename IO::T* __restrict__ g,
+                                                      float2* __restrict__ T, int64_t ch_begin,
+                                                      int L, int M2, const float2* __restrict__ bankp,
+                                                      BigTw tw)
+{
+    constexpr int TQ = M1 / 16, NCOL = 256 / TQ, CREG = M1 + M1 / 16 + 1;
+    __shared__ float2 lds[2 * NCOL * CREG];
+    const Bank bank = make_bank(bankp);
+    const int tid = threadIdx.x, beta = tid >> 8, t = tid & 255;
+    const int c = t % NCOL, tau = t / NCOL;
+    const int tiles = M2 / NCOL;
+    const int chl = blockIdx.x / tiles;
+    const int n1 = (blockIdx.x - chl * tiles) * NCOL + c;
+    const int64_t base = (ch_begin + chl) * (int64_t)L;
+
+    float2 x[16];
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+        const int n = n1 + M2 * (tau + TQ * q);
+        float2 z = make_float2(0.f, 0.f);
+        if (n < L) z = make_float2(IO::load(v, base + n), IO::load(g, base + n));
+        if (beta) z = cmul(z, big_tw(tw, n));
+        x[q] = z;
+    }
+    fft_passes<M1, false>(x, lds + (beta * NCOL + c) * CREG, tau, bank, true);
+    // x[q] = column output k2 = tau + TQ q; times W_M^{n1 k2} = W_N^{2 n1 k2}
+    float2* out = T + (int64_t)(chl * 2 + beta) * M1 * M2;
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+        const int k2 = tau + TQ * q;
+        out[(int64_t)k2 * M2 + n1] = cmul(x[q], big_tw(tw, 2 * n1 * k2));
+    }
+}
+
+// ---------------------------------------------------------------- kernel B: rows
+
+// Bins of the quadruple of item (row rho, column k1): U[row][col] through `at`.
+// Returns Y_j and Y_{partner}, both scaled by 8 like the fused kernel.
+template <class At>
+__device__ __forceinline__ void fs_unpack(int rho, int k1, int beta, int M1, int M2, int M,
+                                          const At& at, const BigTw& tw, float2& yj, float2& yp)
+{
+    const int j = M1 * k1 + rho;
+    const bool zero = rho + beta == 0;
+    const int prow = zero ? 0 : M1 - rho - beta;
+    const float2 p1 = at(rho, k1);
+    const float2 q1 = conjf2(at(prow, zero ? (M2 - k1) & (M2 - 1) : M2 - 1 - k1));
+    const float2 p2 = at(prow, zero ? M2 / 2 - k1 : M2 / 2 - 1 - k1);
+    const float2 q2 = conjf2(at(rho, M2 / 2 + k1));
+    const float2 s1 = cadd(p1, q1), d1 = csub(p1, q1);
+    const float2 s2 = cadd(p2, q2), d2 = csub(p2, q2);
+    const float2 x1 = make_float2(__builtin_fmaf(s1.x, d1.y, s1.y * d1.x),
+                                  __builtin_fmaf(s1.y, d1.y, -s1.x * d1.x));
+    const float2 x2 = make_float2(__builtin_fmaf(s2.x, d2.y, s2.y * d2.x),
+                                  __builtin_fmaf(s2.y, d2.y, -s2.x * d2.x));
+    const float2 sm = make_float2(x1.x + x2.x, x1.y - x2.y);
+    const float2 df = make_float2(x1.x - x2.x, x1.y + x2.y);
+    const float2 t = cmulc(df, big_tw(tw, 2 * j + beta));       // W_N^{-k} D, k = 2j + b
+    yj = make_float2(sm.x - t.y, sm.y + t.x);
+    yp = make_float2(sm.x + t.y, t.x - sm.y);
+    (void)M;
+}
+
+template <int M2>
+__global__ __launch_bounds__(512) void fs_rows(const float2* __restrict__ T, float2* __restrict__ S,
+                                               int M1, const float2* __restrict__ bankp, BigTw tw)
+{
+    constexpr int TR = M2 / 16, PAIRS = (2048 / M2) > 1 ? 2048 / M2 : 1;
+    constexpr int RREG = M2 + M2 / 16 + 1, H = M2 / 2, TH = H / 16;
+    __shared__ float2 lds[PAIRS * 2 * RREG];
+    const Bank bank = make_bank(bankp);
+    const int M = M1 * M2;
+    const int groups = (M1 / 2) / PAIRS;                 // slot groups per branch
+    const int chl = blockIdx.x / (2 * groups);
+    const int rem = blockIdx.x - chl * 2 * groups;
+    const int beta = rem / groups;
+    const int tid = threadIdx.x;
+    const int pl = tid / (2 * TR), side = (tid / TR) & 1, tau = tid % TR;
+    const int slot = (rem - beta * groups) * PAIRS + pl;
+    const int ra = slot, rb = (beta == 0 && slot == 0) ? M1 / 2 : M1 - slot - beta;
+    const int row = side ? rb : ra;
+    float2* bufa = lds + (pl * 2) * RREG;
+    float2* bufb = bufa + RREG;
+    float2* mybuf = side ? bufb : bufa;
+
+    // row DFT of length M2: x[q] = U_{M1 k1 + row}, k1 = tau + TR q
+    const float2* in = T + ((int64_t)(chl * 2 + beta) * M1 + row) * M2;
+    float2 x[16];
+#pragma unroll
+    for (int q = 0; q < 16; ++q) x[q] = in[tau + TR * q];
+    fft_passes<M2, false>(x, mybuf, tau, bank, true);
+#pragma unroll
+    for (int q = 0; q < 16; ++q) mybuf[reg_off<TR>(tau, q)] = x[q];
+    __syncthreads();
+
+    // quadruple unpack: items (row, k1 < M2/4) of both rows of the slot, 4 per thread
+    auto at = [&](int r_, int c_) { return (r_ == ra ? bufa : bufb)[lds_pad(c_)]; };
+    const int lt = tid - pl * 2 * TR;
+    float2 yj[4], yp[4];
+    int rowj[4], colj[4], rowp[4], colp[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int item = lt + 2 * TR * i;
+        const int rsel = item / (M2 / 4), k1 = item - rsel * (M2 / 4);
+        const int rho = rsel ? rb : ra;
+        fs_unpack(rho, k1, beta, M1, M2, M, at, tw, yj[i], yp[i]);
+        rowj[i] = rho;
+        colj[i] = k1;
+        if (rho + beta == 0) {
+            rowp[i] = 0;
+            colp[i] = H - k1;
+            if (k1 == 0) {            // Y_M is absent: take Y_{M/2} (j = M/4, row 0)
+                float2 unused;
+                fs_unpack(0, M2 / 4, 0, M1, M2, M, at, tw, yp[i], unused);
+                colp[i] = H / 2;
+            }
+        } else {
+            rowp[i] = M1 - rho - beta;
+            colp[i] = H - 1 - k1;
+        }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        (rowj[i] == ra ? bufa : bufb)[lds_pad(colj[i])] = yj[i];
+        (rowp[i] == ra ? bufa : bufb)[lds_pad(colp[i])] = yp[i];
+    }
+    __syncthreads();
+
+    // row inverse DFT of length H (first TH threads of each row)
+    const bool iact = tau < TH;
+    if (iact) {
+#pragma unroll
+        for (int q = 0; q < 16; ++q) x[q] = mybuf[reg_off<TH>(tau, q)];
+    }
+    __syncthreads();
+    fft_passes<H, true>(x, mybuf, tau, bank, iact);
+    if (iact) {
+        float2* out = S + ((int64_t)(chl * 2 + beta) * M1 + row) * H;
+#pragma unroll
+        for (int q = 0; q < 16; ++q) {
+            const int m1 = tau + TH * q;
+            // W_{M/2}^{-m1 row} = W_N^{-4 m1 row}
+            out[m1] = cmulc(x[q], big_tw(tw, 4 * m1 * row));
+        }
+    }
+}
+
+// ---------------------------------------------------------------- kernel C: columns, inverse
+
+template <int M1, class IO>
+__global__ __launch_bounds__(512) void fs_columns_inv(const float2* __restrict__ S,
+                                                      typename IO::T* __restrict__ r,
+                                                      int64_t ch_begin, int L, int M2, int head,
+                                                      int pair_store,
+                                                      const float2* __restrict__ bankp, BigTw tw)
+{
+    constexpr int TQ = M1 / 16, NCOL = 256 / TQ, CREG = M1 + M1 / 16 + 1;
+    __shared__ float2 lds[2 * NCOL * CREG];
+    const Bank bank = make_bank(bankp);
+    const int H = M2 / 2, M = M1 * M2;
+    const int tid = threadIdx.x, beta = tid >> 8, t = tid & 255;
+    const int c = t % NCOL, tau = t / NCOL;
+    const int tiles = (H + NCOL - 1) / NCOL;
+    const int chl = blockIdx.x / tiles;
+    const int m1 = (blockIdx.x - chl * tiles) * NCOL + c;
+    const bool col_ok = m1 < H;
+    const float2* in = S + (int64_t)(chl * 2 + beta) * M1 * H;
+
+    float2 x[16];
+#pragma unroll
+    for (int q = 0; q < 16; ++q)
+        x[q] = col_ok ? in[(int64_t)(tau + TQ * q) * H + m1] : make_float2(0.f, 0.f);
+    float2* mybuf = lds + (beta * NCOL + c) * CREG;
+    fft_passes<M1, true>(x, mybuf, tau, bank, true);
+    // x[q] = e (beta 0) or o (beta 1) at m = m1 + H m2, m2 = tau + TQ q
+    if (beta) {
+#pragma unroll
+        for (int q = 0; q < 16; ++q) {
+            const int m = m1 + H * (tau + TQ * q);
+            mybuf[reg_off<TQ>(tau, q)] = cmulc(x[q], big_tw(tw, 2 * m));   // W_M^{-m} o_m
+        }
+    }
+    __syncthreads();
+    if (!beta && col_ok) {
+        const float2* obuf = lds + (NCOL + c) * CREG;
+        const float scale = 1.0f / (8.0f * (float)M);
+        const int64_t base = (ch_begin + chl) * (int64_t)L;
+#pragma unroll
+        for (int q = 0; q < 16; ++q) {
+            const int m = m1 + H * (tau + TQ * q);
+            const int tt = 2 * m;
+            if (tt < head || tt >= L) continue;
+            const float2 o = obuf[reg_off<TQ>(tau, q)];
+            const float a = (x[q].x + o.x) * scale, b = (x[q].y + o.y) * scale;
+            if (tt + 1 < L) {
+                if (pair_store) {
+                    IO::store2(r, base + tt, a, b);
+                } else {
+                    IO::store(r, base + tt, a);
+                    IO::store(r, base + tt + 1, b);
+                }
+            } else {
+                IO::store(r, base + tt, a);
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------- direct head
+
+template <class IO>
+__global__ void head_kernel(const typename IO::T* __restrict__ v, const typename IO::T* __restrict__ g,
+                            typename IO::T* __restrict__ r, int64_t nch, int L, int head)
+{
+    const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const int64_t c = idx / head;
+    const int t = (int)(idx - c * head);
+    if (c >= nch || t >= L) return;
+    const int64_t base = c * (int64_t)L;
+    float acc = 0.f;
+    for (int j = 0; j <= t; ++j)
+        acc = __builtin_fmaf(IO::load(v, base + j), IO::load(g, base + t - j), acc);
+    IO::store(r, base + t, acc);
+}
+
+// ---------------------------------------------------------------- launch
+
+template <class IO, int M1>
+static hipError_t launch_cols(bool fwd, const void* v, const void* g, void* r, float2* T,
+                              const float2* S, int64_t c0, int nc, int L, int M2, int head,
+                              bool pair, const float2* bank, const BigTw& tw, hipStream_t s)
+{
+    constexpr int NCOL = 256 / (M1 / 16);
+    if (fwd) {
+        const int64_t blocks = (int64_t)nc * (M2 / NCOL);
+        hipLaunchKernelGGL((fs_columns_fwd<M1, IO>), dim3((unsigned)blocks), dim3(512), 0, s,
+                           (const typename IO::T*)v, (const typename IO::T*)g, T, c0, L, M2, bank,
+                           tw);
+    } else {
+        const int H = M2 / 2;
+        const int64_t blocks = (int64_t)nc * ((H + NCOL - 1) / NCOL);
+        hipLaunchKernelGGL((fs_columns_inv<M1, IO>), dim3((unsigned)blocks), dim3(512), 0, s, S,
+                           (typename IO::T*)r, c0, L, M2, head, pair ? 1 : 0, bank, tw);
+    }
+    return hipGetLastError();
+}
+
+template <class IO>
+static hipError_t dispatch_cols(bool fwd, int M1, const void* v, const void* g, void* r, float2* T,
+                                const float2* S, int64_t c0, int nc, int L, int M2, int head,
+                                bool pair, const float2* bank, const BigTw& tw, hipStream_t s)
+{
+    switch (M1) {
+    case 64: return launch_cols<IO, 64>(fwd, v, g, r, T, S, c0, nc, L, M2, head, pair, bank, tw, s);
+    case 128: return launch_cols<IO, 128>(fwd, v, g, r, T, S, c0, nc, L, M2, head, pair, bank, tw, s);
+    case 256: return launch_cols<IO, 256>(fwd, v, g, r, T, S, c0, nc, L, M2, head, pair, bank, tw, s);
+    case 512: return launch_cols<IO, 512>(fwd, v, g, r, T, S, c0, nc, L, M2, head, pair, bank, tw, s);
+    case 1024: return launch_cols<IO, 1024>(fwd, v, g, r, T, S, c0, nc, L, M2, head, pair, bank, tw, s);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+template <int M2>
+static hipError_t launch_rows(const float2* T, float2* S, int nc, int M1, const float2* bank,
+                              const BigTw& tw, hipStream_t s)
+{
+    constexpr int TR = M2 / 16, PAIRS = (2048 / M2) > 1 ? 2048 / M2 : 1;
+    const int64_t blocks = (int64_t)nc * 2 * ((M1 / 2) / PAIRS);
+    hipLaunchKernelGGL((fs_rows<M2>), dim3((unsigned)blocks), dim3(PAIRS * 2 * TR), 0, s, T, S, M1,
+                       bank, tw);
+    return hipGetLastError();
+}
+
+static hipError_t dispatch_rows(int M2, const float2* T, float2* S, int nc, int M1,
+                                const float2* bank, const BigTw& tw, hipStream_t s)
+{
+    switch (M2) {
+    case 64: return launch_rows<64>(T, S, nc, M1, bank, tw, s);
+    case 128: return launch_rows<128>(T, S, nc, M1, bank, tw, s);
+    case 256: return launch_rows<256>(T, S, nc, M1, bank, tw, s);
+    case 512: return launch_rows<512>(T, S, nc, M1, bank, tw, s);
+    case 1024: return launch_rows<1024>(T, S, nc, M1, bank, tw, s);
+    case 2048: return launch_rows<2048>(T, S, nc, M1, bank, tw, s);
+    case 4096: return launch_rows<4096>(T, S, nc, M1, bank, tw, s);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+void fourstep_split(int M, int* M1, int* M2)
+{
+    int m1 = M / FOURSTEP_MAX_ROW;
+    if (m1 < 64) m1 = 64;
+    *M1 = m1;
+    *M2 = M / m1;
+}
+
+size_t fourstep_bytes_per_channel(int M)
+{
+    // T: 2 branches x M complex; S: 2 branches x M/2 complex
+    return (size_t)3 * (size_t)M * sizeof(float2);
+}
+
+hipError_t launch_fourstep(Store st, const void* v, const void* g, void* r, int64_t nch, int L,
+                           int M, int head, bool pair_store, const float2* bank, const BigTw& tw,
+                           void* ws, int64_t chunk, hipStream_t stream)
+{
+    int M1, M2;
+    fourstep_split(M, &M1, &M2);
+    float2* T = (float2*)ws;
+    float2* S = T + (size_t)chunk * 2 * M;
+    for (int64_t c0 = 0; c0 < nch; c0 += chunk) {
+        const int nc = (int)((nch - c0) < chunk ? (nch - c0) : chunk);
+        hipError_t e;
+        if (st == Store::F32)
+            e = dispatch_cols<f32_io>(true, M1, v, g, r, T, S, c0, nc, L, M2, head, pair_store,
+                                      bank, tw, stream);
+        else
+            e = dispatch_cols<bf16_io>(true, M1, v, g, r, T, S, c0, nc, L, M2, head, pair_store,
+                                       bank, tw, stream);
+        if (e != hipSuccess) return e;
+        e = dispatch_rows(M2, T, S, nc, M1, bank, tw, stream);
+        if (e != hipSuccess) return e;
+        if (st == Store::F32)
+            e = dispatch_cols<f32_io>(false, M1, v, g, r, T, S, c0, nc, L, M2, head, pair_store,
+                                      bank, tw, stream);
+        else
+            e = dispatch_cols<bf16_io>(false, M1, v, g, r, T, S, c0, nc, L, M2, head, pair_store,
+                                       bank, tw, stream);
+        if (e != hipSuccess) return e;
+    }
+    if (head > 0) {
+        const int64_t total = nch * (int64_t)head;
+        const int threads = 256;
+        const int64_t blocks = (total + threads - 1) / threads;
+        if (st == Store::F32)
+            hipLaunchKernelGGL(head_kernel<f32_io>, dim3((unsigned)blocks), dim3(threads), 0, stream,
+                               (const float*)v, (const float*)g, (float*)r, nch, L, head);
+        else
+            hipLaunchKernelGGL(head_kernel<bf16_io>, dim3((unsigned)blocks), dim3(threads), 0, stream,
+                               (const uint16_t*)v, (const uint16_t*)g, (uint16_t*)r, nch, L, head);
+        return hipGetLastError();
+    }
+    return hipSuccess;
+}
+
+}  // namespace sc

@@ -4,6 +4,7 @@
 
 #include <climits>
 #include <cmath>
+#include <map>
 #include <mutex>
 #include <new>
 #include <vector>
@@ -15,7 +16,10 @@ namespace {
 constexpr int kMaxDevices = 64;
 constexpr int kDefaultHead = 32;
 constexpr int kMaxHead = 64;
-constexpr int64_t kMaxLFloat = 4096;     // fused path; longer sequences need the four-step path
+constexpr int64_t kMaxLFused = 4096;     // fused path; longer sequences use the four-step path
+constexpr int64_t kMinLFourStep = 2049;  // the four-step split needs M >= 4096
+// channels per four-step chunk: as many as fit this much scratch (last-level cache sized)
+constexpr int64_t kFourStepChunkBytes = (int64_t)96 << 20;
 constexpr int64_t kMaxLNtt = 4096;
 constexpr int64_t kNttP = 998244353;
 
@@ -35,6 +39,7 @@ struct DeviceState {
     float2* fused_tw = nullptr;   // the float twiddle bank (sc_internal.h)
     sc::NttTables ntt{};
     bool ntt_ready = false;
+    std::map<int, sc::BigTw> big;   // four-step tables by N
 };
 
 uint64_t powmod(uint64_t b, uint64_t e, uint64_t m)
@@ -119,6 +124,29 @@ sc_status device_state(DeviceState** out, bool need_ntt)
     return SC_OK;
 }
 
+// two-level W_N table for the four-step path (built once per device and N)
+sc_status big_tables(DeviceState& d, int N, sc::BigTw* out)
+{
+    auto it = d.big.find(N);
+    if (it != d.big.end()) {
+        *out = it->second;
+        return SC_OK;
+    }
+    int lg = 0;
+    while ((1 << lg) < N) ++lg;
+    const int fbits = (lg + 1) / 2, F = 1 << fbits, NC = N / F;
+    std::vector<float2> h((size_t)NC + F);
+    for (int i = 0; i < NC; ++i) h[i] = unit_root((int64_t)i * F, N);
+    for (int i = 0; i < F; ++i) h[(size_t)NC + i] = unit_root(i, N);
+    void* p = nullptr;
+    sc_status st = upload(h.data(), h.size() * sizeof(float2), &p);
+    if (st != SC_OK) return st;
+    sc::BigTw t{(const float2*)p, (const float2*)p + NC, fbits, N};
+    d.big[N] = t;
+    *out = t;
+    return SC_OK;
+}
+
 size_t elt_size(sc_kind k) { return k == SC_KIND_BF16 ? 2 : 4; }
 
 int64_t next_pow2(int64_t x)
@@ -134,17 +162,26 @@ bool overlaps(const void* a, const void* b, uint64_t bytes)
     return x < y + bytes && y < x + bytes;
 }
 
-// Host-side checks common to every entry point.  *n receives B*C*L.
-sc_status check_args(sc_kind kind, const void* v, const void* g, const void* r, int64_t B,
-                     int64_t C, int64_t L, int64_t* n)
+// Kind and shape checks.  *n receives B*C*L.
+sc_status check_shape(sc_kind kind, int64_t B, int64_t C, int64_t L, int64_t* n)
 {
     if (kind != SC_KIND_F32 && kind != SC_KIND_BF16 && kind != SC_KIND_NTT_I32)
         return SC_ERR_INVALID_ARGUMENT;
     if (B < 0 || C < 0 || L < 0) return SC_ERR_INVALID_ARGUMENT;
-    const size_t es = elt_size(kind);
     const __int128 total = (__int128)B * (__int128)C * (__int128)L;
-    if (total * (__int128)es > (__int128)INT64_MAX) return SC_ERR_INVALID_ARGUMENT;
+    if (total * (__int128)elt_size(kind) > (__int128)INT64_MAX) return SC_ERR_INVALID_ARGUMENT;
     *n = (int64_t)total;
+    return SC_OK;
+}
+
+// Host-side checks common to every entry point.  *n receives B*C*L.
+sc_status check_args(sc_kind kind, const void* v, const void* g, const void* r, int64_t B,
+                     int64_t C, int64_t L, int64_t* n)
+{
+    const sc_status st = check_shape(kind, B, C, L, n);
+    if (st != SC_OK) return st;
+    const size_t es = elt_size(kind);
+    const int64_t total = *n;
     if (total == 0) return SC_OK;
     if (!v || !g || !r) return SC_ERR_INVALID_ARGUMENT;
     if (((uintptr_t)v | (uintptr_t)g | (uintptr_t)r) % es) return SC_ERR_INVALID_ARGUMENT;
@@ -163,32 +200,46 @@ sc_status resolve_path(sc_kind kind, int64_t L, int32_t requested, sc_path* out)
             *out = SC_PATH_FUSED;
         } else if (L <= sc::DIRECT_MAX_L) {
             *out = SC_PATH_DIRECT;
-        } else if (L <= kMaxLFloat) {
+        } else if (L <= kMaxLFused) {
             *out = SC_PATH_FUSED;
+        } else if (L <= sc::FOURSTEP_MAX_L) {
+            *out = SC_PATH_FOUR_STEP;
         } else {
             return SC_ERR_UNSUPPORTED;
         }
         return SC_OK;
     case SC_PATH_FUSED:
-        if (L > (fl ? kMaxLFloat : kMaxLNtt)) return SC_ERR_UNSUPPORTED;
+        if (L > (fl ? kMaxLFused : kMaxLNtt)) return SC_ERR_UNSUPPORTED;
         *out = SC_PATH_FUSED;
         return SC_OK;
     case SC_PATH_DIRECT:
-        if (!fl || L > kMaxLFloat) return SC_ERR_UNSUPPORTED;
+        if (!fl || L > kMaxLFused) return SC_ERR_UNSUPPORTED;
         *out = SC_PATH_DIRECT;
         return SC_OK;
     case SC_PATH_FOUR_STEP:
-        return SC_ERR_UNSUPPORTED;
+        if (!fl || L < kMinLFourStep || L > sc::FOURSTEP_MAX_L) return SC_ERR_UNSUPPORTED;
+        *out = SC_PATH_FOUR_STEP;
+        return SC_OK;
     default:
         return SC_ERR_INVALID_ARGUMENT;
     }
 }
 
+// four-step scratch: channels per chunk and bytes needed
+void fourstep_plan(int64_t nch, int64_t L, int64_t* chunk, size_t* bytes)
+{
+    const int M = (int)next_pow2(L);
+    const int64_t per = (int64_t)sc::fourstep_bytes_per_channel(M);
+    int64_t c = kFourStepChunkBytes / per;
+    if (c < 1) c = 1;
+    if (c > nch) c = nch;
+    *chunk = c;
+    *bytes = (size_t)(c * per);
+}
+
 sc_status run(sc_kind kind, const void* v, const void* g, void* r, int64_t B, int64_t C,
               int64_t L, const sc_options* opt, void* ws, size_t ws_bytes, hipStream_t stream)
 {
-    (void)ws;
-    (void)ws_bytes;
     int64_t n = 0;
     sc_status st = check_args(kind, v, g, r, B, C, L, &n);
     if (st != SC_OK) return st;
@@ -219,12 +270,37 @@ sc_status run(sc_kind kind, const void* v, const void* g, void* r, int64_t B, in
                            d->ntt, stream);
     } else {
         const sc::Store s = kind == SC_KIND_F32 ? sc::Store::F32 : sc::Store::BF16;
+        const bool pair = (L % 2 == 0) && ((uintptr_t)r % (2 * elt_size(kind)) == 0);
         if (path == SC_PATH_DIRECT) {
             e = sc::launch_direct(s, v, g, r, nch, (int)L, stream);
-        } else {
+        } else if (path == SC_PATH_FUSED) {
             const int M = (int)std::max<int64_t>(64, next_pow2(L));
-            const bool pair = (L % 2 == 0) && ((uintptr_t)r % (2 * elt_size(kind)) == 0);
             e = sc::launch_fused(s, v, g, r, nch, (int)L, M, head, pair, d->fused_tw, stream);
+        } else {
+            const int M = (int)next_pow2(L);
+            sc::BigTw tw;
+            {
+                std::lock_guard<std::mutex> lk(g_mu);
+                st = big_tables(*d, 2 * M, &tw);
+            }
+            if (st != SC_OK) return st;
+            int64_t chunk;
+            size_t need;
+            fourstep_plan(nch, L, &chunk, &need);
+            void* scratch = ws;
+            bool own = false;
+            if (ws) {
+                if (ws_bytes < need) return SC_ERR_WORKSPACE;
+                if ((uintptr_t)ws % 256) return SC_ERR_INVALID_ARGUMENT;
+            } else {
+                if (ws_bytes) return SC_ERR_INVALID_ARGUMENT;
+                if (hipMallocAsync(&scratch, need, stream) != hipSuccess) return SC_ERR_HIP;
+                own = true;
+            }
+            e = sc::launch_fourstep(s, v, g, r, nch, (int)L, M, head, pair, d->fused_tw, tw,
+                                    scratch, chunk, stream);
+            if (own && hipFreeAsync(scratch, stream) != hipSuccess && e == hipSuccess)
+                e = hipErrorUnknown;
         }
     }
     return e == hipSuccess ? SC_OK : SC_ERR_HIP;
@@ -265,11 +341,19 @@ sc_status sc_causal_conv_ntt_i32(const int32_t* v, const int32_t* g, int32_t* r,
 
 size_t sc_workspace_bytes(sc_kind kind, int64_t B, int64_t C, int64_t L)
 {
-    (void)kind;
-    (void)B;
-    (void)C;
-    (void)L;
-    return 0;
+    try {
+        int64_t n = 0;
+        if (check_shape(kind, B, C, L, &n) != SC_OK || n == 0) return 0;
+        sc_path path;
+        if (resolve_path(kind, L, SC_PATH_AUTO, &path) != SC_OK) return 0;
+        if (path != SC_PATH_FOUR_STEP) return 0;
+        int64_t chunk;
+        size_t need;
+        fourstep_plan(B * C, L, &chunk, &need);
+        return need;
+    } catch (...) {
+        return 0;
+    }
 }
 
 sc_status sc_causal_conv_f32_ws(const float* v, const float* g, float* r, int64_t B, int64_t C,

@@ -36,6 +36,27 @@ struct NttTables {
 hipError_t launch_ntt(const int32_t* v, const int32_t* g, int32_t* r, int64_t nch, int L, int M,
                       const NttTables& tables, hipStream_t stream);
 
+// ---- four-step path (L > FUSED_MAX_L)
+// Longest row transform of the four-step split M = M1 * M2 (M2 <= this, M1 >= 64).
+constexpr int FOURSTEP_MAX_ROW = 4096;
+// Largest sequence length of the four-step path (N = 2M <= 2^23 divides p - 1 as well).
+constexpr int64_t FOURSTEP_MAX_L = (int64_t)1 << 22;
+
+// Two-level table of W_N^e for one N: coarse[h] = W_N^{h F}, fine[l] = W_N^l, F = 2^fbits.
+struct BigTw {
+    const float2* coarse;
+    const float2* fine;
+    int fbits;
+    int n;
+};
+
+void fourstep_split(int M, int* M1, int* M2);
+size_t fourstep_bytes_per_channel(int M);
+// ws holds chunk channels of scratch (chunk * fourstep_bytes_per_channel(M) bytes).
+hipError_t launch_fourstep(Store st, const void* v, const void* g, void* r, int64_t nch, int L,
+                           int M, int head, bool pair_store, const float2* bank, const BigTw& tw,
+                           void* ws, int64_t chunk, hipStream_t stream);
+
 // Direct summation r_t = sum_{j<=t} v_j g_{t-j} in fp32, one thread per output.
 hipError_t launch_direct(Store st, const void* v, const void* g, void* r, int64_t nch, int L,
                          hipStream_t stream);

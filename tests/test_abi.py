@@ -84,6 +84,12 @@ def test_unsupported_lengths_rejected_before_launch(sc):
     h = sc.lib()
     UNSUP = sc.SC_ERR_UNSUPPORTED
     assert h.sc_causal_conv_ntt_i32(A, B_, C_, 1, 1, 5000, None) == UNSUP
+    far = (1 << 32, 2 << 32, 3 << 32)                  # fake, far enough apart not to overlap
+    assert h.sc_causal_conv_f32(*far, 1, 1, 2**22 + 1, None) == UNSUP
+    opt = sc.sc_options(sc.PATH_FOUR_STEP, -1)         # the split needs L > 2048
+    assert h.sc_causal_conv_ex(0, A, B_, C_, 1, 1, 2048, ctypes.byref(opt), None, 0, None) == UNSUP
+    opt = sc.sc_options(sc.PATH_FUSED, -1)             # one workgroup holds at most L = 4096
+    assert h.sc_causal_conv_ex(0, A, B_, C_, 1, 1, 4097, ctypes.byref(opt), None, 0, None) == UNSUP
 
 
 def test_options_validation(sc):
@@ -113,3 +119,9 @@ def test_host_helpers(sc):
     assert sc.sc_status_string(99) == "SC_STATUS_UNKNOWN"
     assert sc.sc_version() >= 100
     assert sc.sc_workspace_bytes(sc.KIND_F32, 8, 1024, 4096) == 0
+    # four-step lengths need scratch; the exact path and bad shapes need none
+    assert sc.sc_workspace_bytes(sc.KIND_F32, 1, 1536, 65536) > 0
+    assert sc.sc_workspace_bytes(sc.KIND_BF16, 1, 1, 5000) > 0
+    assert sc.sc_workspace_bytes(sc.KIND_NTT_I32, 1, 1, 4096) == 0
+    assert sc.sc_workspace_bytes(sc.KIND_F32, -1, 1, 65536) == 0
+    assert sc.sc_workspace_bytes(sc.KIND_F32, 1, 1, 2**23) == 0      # above the maximum

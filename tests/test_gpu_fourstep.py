@@ -1,0 +1,102 @@
+"""GPU parity of the four-step (HBM-staged) path against the float64 oracle."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from tests.gpu_util import assert_within_bound, to_device, to_host
+from workloads import WORKLOADS, make_inputs
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def sc():
+    import fft_causal_long_amd as m
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    return m
+
+
+def run(sc, v, g, **kw):
+    out = sc.causal_conv(to_device(v), to_device(g), **kw)
+    torch.cuda.synchronize()
+    return to_host(out)
+
+
+def check(sc, v, g, what, chans=None, **kw):
+    r = run(sc, v, g, **kw)
+    L = v.shape[-1]
+    if chans is not None:
+        v = v.reshape(-1, L)[chans]
+        g = g.reshape(-1, L)[chans]
+        r = r.reshape(-1, L)[chans]
+    r_ref, S = oracle.causal_conv_f64(v, g)
+    worst = assert_within_bound(r, r_ref, S, v.dtype == np.uint16, what)
+    print("%s: worst err/bound = %.3g" % (what, worst), flush=True)
+    return worst
+
+
+@pytest.mark.parametrize("L", [2049, 3000, 4096])
+def test_forced_four_step_small(sc, L):
+    v, g = make_inputs(WORKLOADS[4], B=2, C=8, L=L, seed_offset=L)
+    check(sc, v, g, "four-step forced L=%d" % L, path=sc.PATH_FOUR_STEP)
+
+
+@pytest.mark.parametrize("L", [4097, 5000, 8192, 16384])
+def test_auto_four_step(sc, L):
+    v, g = make_inputs(WORKLOADS[4], B=1, C=8, L=L, seed_offset=L)
+    check(sc, v, g, "four-step L=%d" % L)
+
+
+def test_four_step_conv_gate_and_bf16(sc):
+    v, g = make_inputs(WORKLOADS[2], B=1, C=8, L=8192, seed_offset=11)
+    check(sc, v, g, "four-step conv gate f32 L=8192")
+    v, g = make_inputs(WORKLOADS[3], B=1, C=8, L=8192, seed_offset=12)
+    check(sc, v, g, "four-step bf16 L=8192")
+
+
+def test_four_step_L65536_few_channels(sc):
+    v, g = make_inputs(WORKLOADS[4], B=1, C=4)
+    check(sc, v, g, "four-step L=65536")
+
+
+def test_four_step_several_chunks(sc):
+    # 600 channels at L = 8192 span two scratch chunks
+    L, C = 8192, 600
+    per = sc.sc_workspace_bytes(sc.KIND_F32, 1, 1, L)
+    assert sc.sc_workspace_bytes(sc.KIND_F32, 1, C, L) < per * C
+    v, g = make_inputs(WORKLOADS[4], B=1, C=C, L=L, seed_offset=13)
+    check(sc, v, g, "four-step 600 channels", chans=np.array([0, 1, 255, 511, 512, 513, 598, 599]))
+
+
+def test_config4_full_size_sampled(sc):
+    w = WORKLOADS[4]
+    v, g = make_inputs(w)
+    chans = np.array([0, 517, 1024, w.C - 1])
+    check(sc, v, g, "config4 sampled", chans=chans)
+
+
+def test_caller_workspace_and_errors(sc):
+    L = 8192
+    v, g = make_inputs(WORKLOADS[4], B=1, C=16, L=L, seed_offset=14)
+    tv, tg = to_device(v), to_device(g)
+    need = sc.sc_workspace_bytes(sc.KIND_F32, 1, 16, L)
+    assert need > 0
+    ws = torch.empty(need, dtype=torch.uint8, device="cuda:0")
+    a = sc.causal_conv(tv, tg, workspace=ws)
+    b = sc.causal_conv(tv, tg)
+    torch.cuda.synchronize()
+    assert torch.equal(a.view(torch.int32), b.view(torch.int32))      # bitwise, same plan
+    small = torch.empty(need - 256, dtype=torch.uint8, device="cuda:0")
+    with pytest.raises(sc.SpecConvError) as ei:
+        sc.causal_conv(tv, tg, workspace=small)
+    assert ei.value.status == sc.SC_ERR_WORKSPACE
+    # the fused path needs no workspace
+    assert sc.sc_workspace_bytes(sc.KIND_F32, 8, 1024, 4096) == 0
+
+
+def test_four_step_deterministic(sc):
+    v, g = make_inputs(WORKLOADS[4], B=1, C=32, L=16384, seed_offset=15)
+    a = run(sc, v, g)
+    b = run(sc, v, g)
+    assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
