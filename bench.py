@@ -61,6 +61,56 @@ def measured_traffic(workload: str):
     return rec.get("bytes_per_launch")
 
 
+COPY_BYTES = 1 << 30   # the --calib-copy transfer: 2^28 float32 read and written
+
+
+def kernel_matches(name: str, storage: str, L: int) -> bool:
+    """Is this profiled kernel part of the timed hot path of the workload?"""
+    if storage == "i32":
+        return "ntt_conv_kernel" in name
+    if L > 4096:
+        return "fs_" in name or "head_kernel" in name
+    return "fused_conv_kernel" in name
+
+
+def record_traffic(w, fetch_dir: str, write_dir: str) -> dict:
+    """Turn two rocprofv3 counter runs (FETCH_SIZE, WRITE_SIZE, KiB per dispatch, both run
+    with --calib-copy) into HBM bytes per launch of the hot path.  Each counter is scaled
+    by (known copy bytes) / (what it reads for the 1 GiB copy)."""
+    import csv
+
+    if w.L > 4096:
+        raise SystemExit("--record-traffic handles the single-kernel paths (L <= 4096) only")
+
+    def per_dispatch(d, counter):
+        rows = list(csv.DictReader(open(os.path.join(d, "run_counter_collection.csv"))))
+        hot, copy = {}, []
+        for r in rows:
+            if r["Counter_Name"] != counter:
+                continue
+            val = float(r["Counter_Value"])
+            if "copyBuffer" in r["Kernel_Name"]:
+                copy.append(val)
+            elif kernel_matches(r["Kernel_Name"], w.storage, w.L):
+                hot[r["Dispatch_Id"]] = hot.get(r["Dispatch_Id"], 0.0) + val
+        if not hot or len(copy) != 1:
+            raise RuntimeError("%s: expected hot-path dispatches and one calibration copy" % d)
+        scale = COPY_BYTES / (copy[0] * 1024.0)
+        return float(np.mean(list(hot.values()))) * 1024.0 * scale, scale
+
+    fetch, fs = per_dispatch(fetch_dir, "FETCH_SIZE")
+    write, ws = per_dispatch(write_dir, "WRITE_SIZE")
+    rec = {"workload": w.name, "source_hash": kernel_source_hash(),
+           "fetch_bytes_per_launch": round(fetch), "write_bytes_per_launch": round(write),
+           "bytes_per_launch": round(fetch + write), "fetch_scale": fs, "write_scale": ws,
+           "algorithmic_bytes_per_launch": 3 * w.outputs * (2 if w.storage == "bf16" else 4)}
+    path = os.path.join(ROOT, "profiles", "traffic_%s.json" % w.name)
+    with open(path, "w") as f:
+        json.dump(rec, f, indent=1)
+        f.write("\n")
+    return rec
+
+
 def cpu_baseline(w, v, g, budget_s: float = 10.0):
     """Time the float64 oracle on growing channel samples until one takes >= budget_s/2."""
     import oracle
@@ -95,7 +145,15 @@ def main(argv=None):
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run a plain device copy of known size (profiler calibration)")
+    ap.add_argument("--record-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="write profiles/traffic_<workload>.json from two rocprofv3 --pmc "
+                         "runs (FETCH_SIZE, WRITE_SIZE) of this script with --calib-copy")
     args = ap.parse_args(argv)
+
+    if args.record_traffic:
+        from workloads import WORKLOADS
+        print(json.dumps(record_traffic(WORKLOADS[args.config], *args.record_traffic)))
+        return 0
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "

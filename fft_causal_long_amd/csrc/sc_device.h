@@ -148,36 +148,75 @@ __device__ __forceinline__ void dft(float2* a)
 
 // ------------------------------------------------------------------ storage types
 
+// A raw buffer descriptor over `count` elements starting at p[first].  Loads outside it
+// return 0 and stores outside it are dropped by the hardware; offsets are 32-bit.
+struct Span {
+    __amdgpu_buffer_rsrc_t rs;
+};
+template <class T>
+__device__ __forceinline__ Span make_span(const T* p, int64_t first, int64_t count)
+{
+    int64_t bytes = count * (int64_t)sizeof(T);
+    if (bytes > 0x7fffffff) bytes = 0x7fffffff;
+    if (bytes < 0) bytes = 0;
+    return Span{__builtin_amdgcn_make_buffer_rsrc((void*)(p + first), (short)0, (int)bytes, 0x00020000)};
+}
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
+
+// round two floats to bfloat16 (nearest, ties to even) and pack them, a in the low half
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b)
+{
+    const f32x2_t f = {a, b};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2_t));
+}
+
 struct f32_io {
     typedef float T;
+    static constexpr int SIZE = 4;
     __device__ __forceinline__ static float load(const float* p, int64_t i) { return p[i]; }
     __device__ __forceinline__ static void store(float* p, int64_t i, float x) { p[i] = x; }
-    // two consecutive outputs at an even offset of an 8-byte aligned row
-    __device__ __forceinline__ static void store2(float* p, int64_t i, float a, float b)
+    __device__ __forceinline__ static float load(const Span& s, int i)
     {
-        *reinterpret_cast<float2*>(p + i) = make_float2(a, b);
+        return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(s.rs, i * 4, 0, 0));
+    }
+    __device__ __forceinline__ static void store(const Span& s, int i, float x)
+    {
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(x), s.rs, i * 4, 0, 0);
+    }
+    // two consecutive outputs at element i (8-byte aligned)
+    __device__ __forceinline__ static void store2(const Span& s, int i, float a, float b)
+    {
+        const u32x2_t w = {__float_as_uint(a), __float_as_uint(b)};
+        __builtin_amdgcn_raw_buffer_store_b64(w, s.rs, i * 4, 0, 0);
     }
 };
 
 // bfloat16 storage: widen exactly on load, round to nearest even on store
 struct bf16_io {
     typedef uint16_t T;
+    static constexpr int SIZE = 2;
     __device__ __forceinline__ static float load(const uint16_t* p, int64_t i)
     {
         return __uint_as_float(((uint32_t)p[i]) << 16);
     }
-    __device__ __forceinline__ static uint16_t round(float x)
+    __device__ __forceinline__ static void store(uint16_t* p, int64_t i, float x)
     {
-        uint32_t b = __float_as_uint(x);
-        if ((b & 0x7f800000u) == 0x7f800000u)             // inf / nan: keep, quiet nan
-            return (uint16_t)((b >> 16) | ((b & 0x007fffffu) ? 0x40u : 0u));
-        b += 0x7fffu + ((b >> 16) & 1u);
-        return (uint16_t)(b >> 16);
+        p[i] = (uint16_t)pack_bf16x2(x, 0.f);
     }
-    __device__ __forceinline__ static void store(uint16_t* p, int64_t i, float x) { p[i] = round(x); }
-    __device__ __forceinline__ static void store2(uint16_t* p, int64_t i, float a, float b)
+    __device__ __forceinline__ static float load(const Span& s, int i)
     {
-        *reinterpret_cast<uint32_t*>(p + i) = (uint32_t)round(a) | ((uint32_t)round(b) << 16);
+        return __uint_as_float(((uint32_t)__builtin_amdgcn_raw_buffer_load_b16(s.rs, i * 2, 0, 0)) << 16);
+    }
+    __device__ __forceinline__ static void store(const Span& s, int i, float x)
+    {
+        __builtin_amdgcn_raw_buffer_store_b16((unsigned short)pack_bf16x2(x, 0.f), s.rs, i * 2, 0, 0);
+    }
+    __device__ __forceinline__ static void store2(const Span& s, int i, float a, float b)
+    {
+        __builtin_amdgcn_raw_buffer_store_b32(pack_bf16x2(a, b), s.rs, i * 2, 0, 0);
     }
 };
 

@@ -53,14 +53,15 @@ __global__ __launch_bounds__(512) void fs_columns_fwd(const typename IO::T* __re
     const int tiles = M2 / NCOL;
     const int chl = blockIdx.x / tiles;
     const int n1 = (blockIdx.x - chl * tiles) * NCOL + c;
-    const int64_t base = (ch_begin + chl) * (int64_t)L;
+    // this channel's inputs; positions n >= L (the padding inside M) read as 0
+    const Span vs = make_span(v, (ch_begin + chl) * (int64_t)L, L);
+    const Span gs = make_span(g, (ch_begin + chl) * (int64_t)L, L);
 
     float2 x[16];
 #pragma unroll
     for (int q = 0; q < 16; ++q) {
         const int n = n1 + M2 * (tau + TQ * q);
-        float2 z = make_float2(0.f, 0.f);
-        if (n < L) z = make_float2(IO::load(v, base + n), IO::load(g, base + n));
+        float2 z = make_float2(IO::load(vs, n), IO::load(gs, n));
         if (beta) z = cmul(z, big_tw(tw, n));
         x[q] = z;
     }
@@ -227,7 +228,7 @@ __global__ __launch_bounds__(512) void fs_columns_inv(const float2* __restrict__
     if (!beta && col_ok) {
         const float2* obuf = lds + (NCOL + c) * CREG;
         const float scale = 1.0f / (8.0f * (float)M);
-        const int64_t base = (ch_begin + chl) * (int64_t)L;
+        const Span rs = make_span(r, (ch_begin + chl) * (int64_t)L, L);
 #pragma unroll
         for (int q = 0; q < 16; ++q) {
             const int m = m1 + H * (tau + TQ * q);
@@ -237,13 +238,13 @@ __global__ __launch_bounds__(512) void fs_columns_inv(const float2* __restrict__
             const float a = (x[q].x + o.x) * scale, b = (x[q].y + o.y) * scale;
             if (tt + 1 < L) {
                 if (pair_store) {
-                    IO::store2(r, base + tt, a, b);
+                    IO::store2(rs, tt, a, b);
                 } else {
-                    IO::store(r, base + tt, a);
-                    IO::store(r, base + tt + 1, b);
+                    IO::store(rs, tt, a);
+                    IO::store(rs, tt + 1, b);
                 }
             } else {
-                IO::store(r, base + tt, a);
+                IO::store(rs, tt, a);
             }
         }
     }

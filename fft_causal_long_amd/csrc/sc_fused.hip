@@ -36,6 +36,12 @@ namespace sc {
 
 constexpr int FUSED_THREADS = 512;
 constexpr int HEAD_MAX = 64;   // largest direct head (the host clamps to this)
+#ifndef SC_LDS_EXTRA
+#define SC_LDS_EXTRA 24
+#endif
+// extra float2 between the LDS regions of the two branches of a channel: with it the
+// unpack's alternating reads of u0[j] and u1[j] land in different banks
+constexpr int LDS_EXTRA = SC_LDS_EXTRA;
 
 // From the branch spectra u0[j] = Z_{2j}, u1[j] = Z_{2j+1} (natural order, padded) form
 // Y_k and Y_{M-k} of the real-output inverse, both scaled by 8 (constants folded later).
@@ -76,7 +82,7 @@ __global__ __launch_bounds__(FUSED_THREADS) void fused_conv_kernel(
 {
     static_assert(M >= 64 && M <= 4096, "fused path handles 64 <= M <= 4096");
     constexpr int N = 2 * M, TB = M / 16, UNITS = FUSED_THREADS / TB, CPW = UNITS / 2;
-    constexpr int REG = M + M / 16;
+    constexpr int REG = M + M / 16 + (M >= 256 ? LDS_EXTRA : 0);
     __shared__ float2 lds[UNITS * REG];
     // first HEAD_MAX inputs of each local channel (v then g) for the direct head
     __shared__ float hbuf[CPW * 2 * HEAD_MAX];
@@ -86,28 +92,28 @@ __global__ __launch_bounds__(FUSED_THREADS) void fused_conv_kernel(
     const int unit = tid / TB, tau = tid % TB;
     const int cl = unit >> 1, beta = unit & 1;
     const int64_t ch0 = (int64_t)blockIdx.x * CPW;
-    const int64_t ch = ch0 + cl;
-    // every channel of this workgroup present and no padding inside M: no guards needed
-    const bool full = L == M && ch0 + CPW <= nch;
+    const int nvalid = (int)((nch - ch0) < CPW ? (nch - ch0) : CPW);
+    // descriptors over this workgroup's channels: loads past them read 0, stores are dropped
+    const Span vs = make_span(v, ch0 * L, (int64_t)nvalid * L);
+    const Span gs = make_span(g, ch0 * L, (int64_t)nvalid * L);
     float2* ubuf = lds + unit * REG;
 
     // 1. u^beta_n = z_n W_N^{beta n},  z_n = v_n + i g_n for n < L, 0 otherwise
     float2 x[16];
     {
-        const int64_t base = ch * (int64_t)L;
-        if (full) {
+        const int cbase = cl * L;
+        if (L == M) {
 #pragma unroll
             for (int q = 0; q < 16; ++q) {
                 const int n = tau + TB * q;
-                x[q] = make_float2(IO::load(v, base + n), IO::load(g, base + n));
+                x[q] = make_float2(IO::load(vs, cbase + n), IO::load(gs, cbase + n));
             }
         } else {
-            const bool valid = ch < nch;
 #pragma unroll
             for (int q = 0; q < 16; ++q) {
                 const int n = tau + TB * q;
                 x[q] = make_float2(0.f, 0.f);
-                if (valid && n < L) x[q] = make_float2(IO::load(v, base + n), IO::load(g, base + n));
+                if (n < L) x[q] = make_float2(IO::load(vs, cbase + n), IO::load(gs, cbase + n));
             }
         }
         if (!beta) {
@@ -167,18 +173,18 @@ __global__ __launch_bounds__(FUSED_THREADS) void fused_conv_kernel(
     fft_passes<M, true>(x, ybuf, itau, bank, iact);
 
     // 5. store: x[q] = 8 M y_m with m = itau + TB q; r_{2m} = Re y_m, r_{2m+1} = Im y_m
+    const Span rs = make_span(r, ch0 * L, (int64_t)nvalid * L);
     if (iact) {
-        const int64_t och = ch0 + icl;
         const float scale = 1.0f / (8.0f * (float)M);
-        const int64_t base = och * (int64_t)L;
-        if (full && pair_store) {
+        const int cbase = icl * L;
+        if (L == M && pair_store) {
 #pragma unroll
             for (int q = 0; q < 8; ++q) {
                 const int t = 2 * (itau + TB * q);
                 if (2 * TB * q >= HEAD_MAX || t >= head)
-                    IO::store2(r, base + t, x[q].x * scale, x[q].y * scale);
+                    IO::store2(rs, cbase + t, x[q].x * scale, x[q].y * scale);
             }
-        } else if (och < nch) {
+        } else {
 #pragma unroll
             for (int q = 0; q < 8; ++q) {
                 const int t = 2 * (itau + TB * q);
@@ -186,13 +192,13 @@ __global__ __launch_bounds__(FUSED_THREADS) void fused_conv_kernel(
                     const float a = x[q].x * scale, b = x[q].y * scale;
                     if (t + 1 < L) {
                         if (pair_store) {
-                            IO::store2(r, base + t, a, b);
+                            IO::store2(rs, cbase + t, a, b);
                         } else {
-                            IO::store(r, base + t, a);
-                            IO::store(r, base + t + 1, b);
+                            IO::store(rs, cbase + t, a);
+                            IO::store(rs, cbase + t + 1, b);
                         }
                     } else {
-                        IO::store(r, base + t, a);
+                        IO::store(rs, cbase + t, a);
                     }
                 }
             }
@@ -202,13 +208,12 @@ __global__ __launch_bounds__(FUSED_THREADS) void fused_conv_kernel(
         const int nidle = FUSED_THREADS - CPW * TB;
         for (int idx = tid - CPW * TB; idx < CPW * head; idx += nidle) {
             const int c2 = idx / head, t = idx - c2 * head;
-            const int64_t hch = ch0 + c2;
-            if (hch < nch && t < L) {
+            if (c2 < nvalid && t < L) {
                 const float* hv = hbuf + c2 * 2 * HEAD_MAX;
                 const float* hg = hv + HEAD_MAX;
                 float acc = 0.f;
                 for (int j = 0; j <= t; ++j) acc = __builtin_fmaf(hv[j], hg[t - j], acc);
-                IO::store(r, hch * (int64_t)L + t, acc);
+                IO::store(rs, c2 * L + t, acc);
             }
         }
     }
