@@ -1,10 +1,11 @@
-// Length-Q DFTs held in registers and LDS by Q/16 threads of a workgroup (gfx950).
+// Length-Q DFTs held in registers and LDS by the threads of a workgroup (gfx950).
 //
-// Thread tau of a transform holds element tau + (Q/16)*r in register r (r < 16) at the
-// input and the output of the transform.  Between radix-16 passes (Stockham, decimation in
-// frequency) the values go through a padded LDS region of Q + Q/16 complex values.
-// Twiddles come from the float twiddle bank (see sc_internal.h) through a raw buffer
-// descriptor, so a load costs no vector ALU work for its address.
+// A transform is held by TB = Q/P threads with P = 16 (or 8) values each: thread tau holds
+// element tau + TB*r in register r (r < P) at the input and the output of the transform.
+// Between radix-P passes (Stockham, decimation in frequency) the values go through a padded
+// LDS region of Q + Q/16 complex values.  Twiddles come from the float twiddle bank (see
+// sc_internal.h) through a raw buffer descriptor, so a load costs no vector ALU work for
+// its address, and every twiddle load of a pass is one contiguous wave access.
 #pragma once
 
 #include "sc_device.h"
@@ -16,25 +17,36 @@ namespace sc {
 __device__ __forceinline__ int lds_pad(int a) { return a + (a >> 4); }
 
 // Float twiddle bank (device constant table built by the host):
-//   [0, 8192)                        W_8192^i
-//   [8192 + (Q - 32) + k*(Q/16) + n] W_Q^{n k}, for each pass length Q = 32 .. 4096,
-//                                    k < 16, n < Q/16  (row k contiguous in n)
-// The pass tables make every twiddle load of a radix-16 pass a contiguous wave access.
-constexpr int PASS_TW_BASE = FUSED_TW_N;
+//   [0, 8192)                              W_8192^i
+//   [PASS16_TW_BASE + (Q - 32) + k*(Q/16) + n]   W_Q^{n k}, Q = 32 .. 4096, k < 16, n < Q/16
+//   [PASS8_TW_BASE  + (Q - 16) + k*(Q/8)  + n]   W_Q^{n k}, Q = 16 .. 4096, k < 8,  n < Q/8
+constexpr int PASS16_TW_BASE = FUSED_TW_N;
+constexpr int PASS8_TW_BASE = FUSED_TW_N + (2 * 4096 - 32);
 
 struct Bank {
     __amdgpu_buffer_rsrc_t rs;   // raw buffer over the whole bank, bounds-checked
+    int salt = 0;                // 0, but opaque to the compiler after reseed()
     __device__ __forceinline__ float2 at(int voff_elems, int soff_elems) const
     {
-        const auto w = __builtin_amdgcn_raw_buffer_load_b64(rs, voff_elems * 8, soff_elems * 8, 0);
+        const auto w = __builtin_amdgcn_raw_buffer_load_b64(rs, voff_elems * 8,
+                                                            soff_elems * 8 + salt, 0);
         return __builtin_bit_cast(float2, w);
+    }
+    // Loads issued after this cannot be merged with, or hoisted above, earlier identical
+    // loads: a loop that repeats a transform reloads its twiddles instead of keeping every
+    // twiddle of every pass live in registers across iterations.
+    __device__ __forceinline__ void reseed()
+    {
+        int z = 0;
+        asm volatile("" : "+s"(z));
+        salt = z;
     }
 };
 
 __device__ __forceinline__ Bank make_bank(const float2* tw)
 {
     return Bank{__builtin_amdgcn_make_buffer_rsrc((void*)tw, (short)0, FUSED_BANK_FLOAT2 * 8,
-                                                0x00020000)};
+                                                0x00020000), 0};
 }
 
 // W_n^e for a power of two n dividing 8192 (conj when INV)
@@ -53,33 +65,47 @@ __device__ __forceinline__ int reg_off(int tau, int q)
     else return lds_pad(tau + TB * q);
 }
 
-// One Stockham decimation-in-frequency pass of radix R over a length-M transform held by
-// TB = M/16 threads.  Stage data: S sub-transforms of length Q = M/S, element (s, n) of
+// One Stockham decimation-in-frequency pass of radix R over a length-Q transform held by
+// TB = Q/P threads.  Stage data: S sub-transforms of length Qs = Q/S, element (s, n) of
 // sub-transform s at flat index s + S*n; thread tau holds flat index tau + TB*r in x[r].
-// Butterfly "item" (s, n1), n1 < Q/R, combines elements (s, n1 + (Q/R) n2), n2 < R:
-//   out[s + S*k2, n1] = W_Q^{n1 k2} * sum_{n2} in[s, n1 + (Q/R) n2] W_R^{n2 k2}
-// which is written to flat index s + S*(k2 + R*n1).  Radix 16 is used while Q > 16, so a
-// pass with twiddles has one item per thread (item = tau).  The last pass (Q == R) leaves
+// Butterfly "item" (s, n1), n1 < Qs/R, combines elements (s, n1 + (Qs/R) n2), n2 < R:
+//   out[s + S*k2, n1] = W_Qs^{n1 k2} * sum_{n2} in[s, n1 + (Qs/R) n2] W_R^{n2 k2}
+// which is written to flat index s + S*(k2 + R*n1).  Radix P is used while Qs > P, so a
+// pass with twiddles has one item per thread (item = tau).  The last pass (Qs == R) leaves
 // the result in registers: x[r] = X[tau + TB*r], natural order.
-template <int M, int R, int S, bool INV>
-__device__ __forceinline__ void stockham_pass(float2 (&x)[16], float2* __restrict__ buf, int tau,
+template <int Q, int R, int S, bool INV, int P>
+__device__ __forceinline__ void stockham_pass(float2 (&x)[P], float2* __restrict__ buf, int tau,
                                               const Bank& bank)
 {
-    constexpr int NB = 16 / R, Q = M / S, QN = Q / R;
+    constexpr int NB = P / R, Qs = Q / S, QN = Qs / R;
     if constexpr (QN > 1) {
-        static_assert(R == 16, "passes with twiddles are radix 16");
+        static_assert(R == P, "passes with twiddles use the full radix");
         const int s = tau & (S - 1), n1 = tau / S;
-        float2 w[16];
+        constexpr int TBASE = P == 16 ? PASS16_TW_BASE + (Qs - 32) : PASS8_TW_BASE + (Qs - 16);
+        float2 w[P];
 #pragma unroll
-        for (int k2 = 1; k2 < 16; ++k2) w[k2] = bank.at(n1, PASS_TW_BASE + (Q - 32) + k2 * (Q / 16));
-        dft<16, INV>(x);
+        for (int k2 = 1; k2 < P; ++k2) w[k2] = bank.at(n1, TBASE + k2 * (Qs / P));
+        dft<P, INV>(x);
 #pragma unroll
-        for (int k2 = 1; k2 < 16; ++k2) x[k2] = cmul_dir<INV>(x[k2], w[k2]);
-        // flat s + S*(k2 + 16 n1), padded: base + k2*STEP
-        constexpr int STEP = S == 1 ? 1 : S + S / 16;
-        const int base = S == 1 ? 17 * n1 : (s + (s >> 4)) + 16 * n1 * STEP;
+        for (int k2 = 1; k2 < P; ++k2) x[k2] = cmul_dir<INV>(x[k2], w[k2]);
+        // padded flat index s + S*(k2 + P*n1) = base + off(k2)
+        if constexpr (S == 1) {
+            // (k2 + P n1) >> 4 == (P n1) >> 4 because k2 < P <= 16 and P n1 is a multiple of P
+            const int base = P * n1 + ((P * n1) >> 4);
 #pragma unroll
-        for (int k2 = 0; k2 < 16; ++k2) buf[base + k2 * STEP] = x[k2];
+            for (int k2 = 0; k2 < P; ++k2) buf[base + k2] = x[k2];
+        } else if constexpr (S % 16 == 0) {
+            constexpr int STEP = S + S / 16;
+            const int base = (s + (s >> 4)) + P * n1 * STEP;
+#pragma unroll
+            for (int k2 = 0; k2 < P; ++k2) buf[base + k2 * STEP] = x[k2];
+        } else {
+            static_assert(S == 8 && P == 8, "S = 8 occurs only for radix 8");
+            // s < 8: (s + 8 k2 + 64 n1) >> 4 == (k2 >> 1) + 4 n1
+            const int base = s + 68 * n1;
+#pragma unroll
+            for (int k2 = 0; k2 < P; ++k2) buf[base + 8 * k2 + (k2 >> 1)] = x[k2];
+        }
     } else {
 #pragma unroll
         for (int q = 0; q < NB; ++q) {
@@ -93,25 +119,25 @@ __device__ __forceinline__ void stockham_pass(float2 (&x)[16], float2* __restric
     }
 }
 
-// All passes of a length-M DFT (radix 16 while possible, then the remainder).  Inactive
-// threads only join the barriers.  On return every thread has passed a barrier that
-// follows its last read of buf.
-template <int M, bool INV, int S = 1>
-__device__ __forceinline__ void fft_passes(float2 (&x)[16], float2* __restrict__ buf, int tau,
+// All passes of a length-Q DFT held with P values per thread (radix P while possible,
+// then the remainder).  Inactive threads only join the barriers.  On return every thread
+// has passed a barrier that follows its last read of buf.
+template <int Q, bool INV, int S = 1, int P = 16>
+__device__ __forceinline__ void fft_passes(float2 (&x)[P], float2* __restrict__ buf, int tau,
                                            const Bank& bank, bool active)
 {
-    constexpr int TB = M / 16, Q = M / S, R = Q >= 16 ? 16 : Q;
-    if constexpr (Q / R > 1) {
-        if (active) stockham_pass<M, R, S, INV>(x, buf, tau, bank);
+    constexpr int TB = Q / P, Qs = Q / S, R = Qs >= P ? P : Qs;
+    if constexpr (Qs / R > 1) {
+        if (active) stockham_pass<Q, R, S, INV, P>(x, buf, tau, bank);
         __syncthreads();
         if (active) {
 #pragma unroll
-            for (int q = 0; q < 16; ++q) x[q] = buf[reg_off<TB>(tau, q)];
+            for (int q = 0; q < P; ++q) x[q] = buf[reg_off<TB>(tau, q)];
         }
         __syncthreads();
-        fft_passes<M, INV, S * R>(x, buf, tau, bank, active);
+        fft_passes<Q, INV, S * R, P>(x, buf, tau, bank, active);
     } else {
-        if (active) stockham_pass<M, R, S, INV>(x, buf, tau, bank);
+        if (active) stockham_pass<Q, R, S, INV, P>(x, buf, tau, bank);
     }
 }
 

@@ -54,29 +54,35 @@ uint64_t powmod(uint64_t b, uint64_t e, uint64_t m)
     return r;
 }
 
-// {w, floor(w * 2^32 / p)}
-uint2 shoup_pair(uint64_t w)
-{
-    return make_uint2((uint32_t)w, (uint32_t)((w << 32) / (uint64_t)kNttP));
-}
-
 sc_status build_ntt_tables(sc::NttTables* t)
 {
     const uint64_t p = (uint64_t)kNttP;
-    const uint64_t w = powmod(3, (p - 1) / sc::FUSED_TW_N, p);
-    std::vector<uint2> h(sc::FUSED_TW_N);
+    std::vector<double> h(2 * (size_t)sc::NTT_BANK_ENTRIES);
+    auto put = [&](size_t i, uint64_t w) {
+        h[2 * i] = (double)w;
+        h[2 * i + 1] = (double)w / (double)p;
+    };
+    const uint64_t w8192 = powmod(3, (p - 1) / sc::NTT_TW_N, p);
     uint64_t x = 1;
-    for (int i = 0; i < sc::FUSED_TW_N; ++i) {
-        h[i] = shoup_pair(x);
-        x = x * w % p;
+    for (int i = 0; i < sc::NTT_TW_N; ++i) {
+        put((size_t)i, x);
+        x = x * w8192 % p;
+    }
+    for (int Q = 32; Q <= 4096; Q *= 2) {
+        const uint64_t wq = powmod(3, (p - 1) / (uint64_t)Q, p);
+        for (int k = 0; k < 16; ++k)
+            for (int n = 0; n < Q / 16; ++n)
+                put((size_t)(sc::NTT_PASS_BASE + (Q - 32) + k * (Q / 16) + n),
+                    powmod(wq, (uint64_t)n * (uint64_t)k, p));
     }
     void* d = nullptr;
-    sc_status st = upload(h.data(), h.size() * sizeof(uint2), &d);
+    sc_status st = upload(h.data(), h.size() * sizeof(double), &d);
     if (st != SC_OK) return st;
-    t->tw = (const uint2*)d;
+    t->bank = (const double*)d;
     for (int k = 0; k < 24; ++k) {
         const uint64_t ninv = powmod(powmod(2, (uint64_t)k, p), p - 2, p);
-        t->ninv_r[k] = shoup_pair((uint64_t)((unsigned __int128)ninv * ((uint64_t)1 << 32) % p));
+        t->ninv[k] = (double)ninv;
+        t->ninv_q[k] = (double)ninv / (double)p;
     }
     return SC_OK;
 }
@@ -110,6 +116,11 @@ sc_status device_state(DeviceState** out, bool need_ntt)
             for (int k = 0; k < 16; ++k)
                 for (int n = 0; n < Q / 16; ++n)
                     h[sc::FUSED_TW_N + (Q - 32) + k * (Q / 16) + n] = unit_root((int64_t)n * k, Q);
+        for (int Q = 16; Q <= 4096; Q *= 2)
+            for (int k = 0; k < 8; ++k)
+                for (int n = 0; n < Q / 8; ++n)
+                    h[sc::FUSED_TW_N + (2 * 4096 - 32) + (Q - 16) + k * (Q / 8) + n] =
+                        unit_root((int64_t)n * k, Q);
         void* p = nullptr;
         sc_status st = upload(h.data(), h.size() * sizeof(float2), &p);
         if (st != SC_OK) return st;

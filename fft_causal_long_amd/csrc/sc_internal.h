@@ -9,9 +9,10 @@ namespace sc {
 
 // Length of the shared float twiddle table used by the fused path: tw[i] = W_8192^i.
 constexpr int FUSED_TW_N = 8192;
-// The float twiddle bank: W_8192^i (i < 8192), then for each pass length Q = 32..4096 a
-// table of W_Q^{n k} stored row k (k < 16), column n (n < Q/16): Q entries per Q.
-constexpr int FUSED_BANK_FLOAT2 = FUSED_TW_N + (4096 * 2 - 32);
+// The float twiddle bank: W_8192^i (i < 8192); then for each radix-16 pass length
+// Q = 32..4096 a table of W_Q^{n k} stored row k (k < 16), column n (n < Q/16); then for
+// each radix-8 pass length Q = 16..4096 the same with k < 8, n < Q/8.  Q entries per Q.
+constexpr int FUSED_BANK_FLOAT2 = FUSED_TW_N + (4096 * 2 - 32) + (4096 * 2 - 16);
 // Largest sequence length handled by the one-workgroup-per-channel (fused) kernels.
 constexpr int FUSED_MAX_L = 4096;
 // Sequences up to this length are computed entirely by direct summation.
@@ -24,12 +25,18 @@ enum class Store { F32, BF16 };
 hipError_t launch_fused(Store st, const void* v, const void* g, void* r, int64_t nch, int L,
                         int M, int head, bool pair_store, const float2* tw, hipStream_t stream);
 
-// Constants of the exact path modulo p = 998244353.  tw[i] = {w, floor(w 2^32 / p)} with
-// w = omega_8192^i (omega_8192 = 3^((p-1)/8192)); ninv_r[k] = {c, floor(c 2^32 / p)} with
-// c = (2^k)^{-1} * 2^32 mod p.
+// Constants of the exact path modulo p = 998244353 (omega_n = 3^((p-1)/n)).  The bank
+// holds pairs of doubles {w, w / p}:
+//   [0, 8192)                               w = omega_8192^i
+//   [NTT_PASS_BASE + (Q - 32) + k*(Q/16) + n] w = omega_Q^{n k}, Q = 32 .. 4096, k < 16, n < Q/16
+// ninv[k] = (2^k)^{-1} mod p as a double, ninv_q[k] = ninv[k] / p.
+constexpr int NTT_TW_N = 8192;
+constexpr int NTT_PASS_BASE = NTT_TW_N;
+constexpr int NTT_BANK_ENTRIES = NTT_TW_N + (2 * 4096 - 32);
 struct NttTables {
-    const uint2* tw = nullptr;
-    uint2 ninv_r[24];
+    const double* bank = nullptr;
+    double ninv[24];
+    double ninv_q[24];
 };
 
 // Exact NTT causal convolution for L <= FUSED_MAX_L, M = max(64, next power of two >= L).

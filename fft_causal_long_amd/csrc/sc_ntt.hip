@@ -4,23 +4,30 @@
 // (abstract): float FFT convolutions leak future tokens through round-off; an FFT done on
 // integers only cannot.  Here the pad-to-2L recipe of "Caracal: Causal Architecture via
 // Spectral Mixing" (key designs 1 and 2) runs in Z_p, p = 998244353 = 119*2^23 + 1, with
-// omega_n = 3^((p-1)/n) in place of exp(-2 pi i / n).  Every operation is an exact
-// residue operation, so output t is a function of v_0..v_t and g_0..g_t alone.
+// omega_n = 3^((p-1)/n) in place of exp(-2 pi i / n).  Every step is an exact residue
+// computation, so output t is a function of v_0..v_t and g_0..g_t alone.
 //
 // Per channel, with N = 2M and the upper half of the padded inputs zero, the first
 // decimation-in-frequency stage is a twiddle only:  V_{2j+b} = NTT_M(v_n omega_N^{b n})_j,
-// likewise G.  For b = 0, 1 ("branches") the workgroup computes NTT_M of v and g, the
-// product X = V G N^{-1}, and e^b = INTT_M(X^b).  Then for n < L
-//     x_n = N^{-1} sum_k X_k omega_N^{-nk} = e^0_n + omega_N^{-n} e^1_n     (N^{-1} folded)
-// and the residue is lifted to [-(p-1)/2, (p-1)/2].
+// likewise G.  For b = 0, 1 ("branches") the workgroup computes NTT_M of v and of g, the
+// product X = V G N^{-1} and e^b = INTT_M(X^b); for n < L
+//     x_n = N^{-1} sum_k X_k omega_N^{-nk} = e^0_n + omega_N^{-n} e^1_n      (N^{-1} folded)
+// and the residue is lifted to [-(p-1)/2, (p-1)/2].  The inverse uses
+//     INTT_M(X)_n = NTT_M(X)_{(M - n) mod M}
+// so one forward transform serves both directions.
+//
+// Arithmetic.  Residues are integers carried in float64 registers: sums and differences
+// are exact while magnitudes stay below 2^53 (here below 2^36), so butterflies need no
+// reduction.  A product a*w mod p (|a| < 2^36, 0 <= w < p) is exact in six full-rate fp64
+// operations:
+//     h = fl(a w);  l = fma(a, w, -h)            (the exact rounding error, an integer)
+//     q = round(a w / p)                         (fma with w/p and the 1.5*2^52 shift)
+//     r = fma(-q, p, h) + l = a w - q p          (exact: |h - q p| < 2^31)
+// giving |r| <= 1.5 p.  LDS holds int32 values (|x| < 2^31) between passes.
 //
 // Layout as in the float kernel: 512 threads, a length-M transform held by TB = M/16
-// threads with 16 residues each (element tau + TB*r in register r), Stockham radix-16
-// passes through LDS (a v and a g array per branch unit), 68 KB of LDS per workgroup.
-//
-// Arithmetic: residues are kept fully reduced in [0, p) as uint32.  Multiplication by a
-// known constant w uses Shoup's method with w' = floor(w 2^32 / p) from a table;
-// the pointwise product of two variables uses Montgomery reduction with R = 2^32.
+// threads with 16 values each, Stockham radix-16 passes through LDS (a v and a g array per
+// branch unit), 68 KB of LDS per workgroup.
 
 #include "sc_device.h"
 #include "sc_internal.h"
@@ -29,120 +36,191 @@ namespace sc {
 
 namespace ntt {
 
-constexpr uint32_t P = 998244353u;
+constexpr double P = 998244353.0;
+constexpr double PINV = 1.0 / 998244353.0;
+constexpr double SHIFT = 6755399441055744.0;   // 1.5 * 2^52: x + SHIFT - SHIFT = round(x), |x| < 2^51
 
-constexpr uint32_t inv_mod_2_32(uint32_t a)
-{
-    uint32_t x = a;                  // correct to 3 bits for odd a; each step doubles
-    for (int i = 0; i < 5; ++i) x *= 2u - a * x;
-    return x;
-}
-constexpr uint32_t PINV = inv_mod_2_32(P);   // p^{-1} mod 2^32
-static_assert((uint32_t)(P * PINV) == 1u, "p^{-1} mod 2^32");
+// a constant residue w with w / p rounded to double
+struct W {
+    double w, q;
+};
 
-__device__ __forceinline__ uint32_t addm(uint32_t a, uint32_t b)
+constexpr uint64_t powmod_c(uint64_t b, uint64_t e)
 {
-    const uint32_t s = a + b;          // < 2p < 2^31
-    return min(s, s - P);
-}
-__device__ __forceinline__ uint32_t subm(uint32_t a, uint32_t b)
-{
-    const uint32_t d = a - b;          // wraps when a < b
-    return min(d, d + P);
-}
-// a * w mod p for a < 2^32, w < p, wq = floor(w * 2^32 / p)  (Shoup)
-__device__ __forceinline__ uint32_t mulc(uint32_t a, uint2 w)
-{
-    const uint32_t q = __umulhi(a, w.y);
-    const uint32_t r = a * w.x - q * P;   // exact value in [0, 2p)
-    return min(r, r - P);
-}
-// a * b * 2^-32 mod p for a, b < p  (Montgomery)
-__device__ __forceinline__ uint32_t mont(uint32_t a, uint32_t b)
-{
-    const uint32_t lo = a * b, hi = __umulhi(a, b);
-    const uint32_t m = lo * PINV;
-    const uint32_t r = hi - __umulhi(m, P);  // in (-p, p)
-    return min(r, r + P);
-}
-
-// omega_n^e (or omega_n^-e) with its Shoup companion, from the table of omega_8192^i
-template <bool INV>
-__device__ __forceinline__ uint2 tw(const uint2* __restrict__ t, int n, int e)
-{
-    int i = (e & (n - 1)) * (FUSED_TW_N / n);
-    if (INV) i = (FUSED_TW_N - i) & (FUSED_TW_N - 1);
-    return t[i];
-}
-
-// in-register DFT_R over Z_p, natural order in and out (decimation in frequency)
-template <int R, bool INV>
-__device__ __forceinline__ void dft(uint32_t* a, const uint2* __restrict__ t)
-{
-    if constexpr (R == 2) {
-        const uint32_t x = a[0];
-        a[0] = addm(x, a[1]);
-        a[1] = subm(x, a[1]);
-    } else if constexpr (R == 4) {
-        const uint2 w4 = tw<INV>(t, 4, 1);
-        const uint32_t t0 = addm(a[0], a[2]), t1 = subm(a[0], a[2]);
-        const uint32_t t2 = addm(a[1], a[3]), t3 = mulc(subm(a[1], a[3]), w4);
-        a[0] = addm(t0, t2);
-        a[2] = subm(t0, t2);
-        a[1] = addm(t1, t3);
-        a[3] = subm(t1, t3);
-    } else {
-        constexpr int H = R / 2;
-        uint32_t u[H], w[H];
-#pragma unroll
-        for (int n = 0; n < H; ++n) {
-            u[n] = addm(a[n], a[n + H]);
-            const uint32_t d = subm(a[n], a[n + H]);
-            w[n] = n == 0 ? d : mulc(d, tw<INV>(t, R, n));
-        }
-        dft<H, INV>(u, t);
-        dft<H, INV>(w, t);
-#pragma unroll
-        for (int k = 0; k < H; ++k) {
-            a[2 * k] = u[k];
-            a[2 * k + 1] = w[k];
-        }
+    uint64_t r = 1;
+    b %= 998244353ull;
+    while (e) {
+        if (e & 1) r = r * b % 998244353ull;
+        b = b * b % 998244353ull;
+        e >>= 1;
     }
+    return r;
+}
+// omega_n^k as a W constant (n | p - 1)
+constexpr W root_c(uint64_t n, uint64_t k)
+{
+    const uint64_t w = powmod_c(powmod_c(3, 998244352ull / n), k);
+    return W{(double)w, (double)w / 998244353.0};
+}
+
+__device__ __forceinline__ double round_int(double x)
+{
+    return (x + SHIFT) - SHIFT;
+}
+// a * w mod p, |result| <= 1.5 p
+__device__ __forceinline__ double mulc(double a, W w)
+{
+    const double h = a * w.w;
+    const double l = __builtin_fma(a, w.w, -h);
+    const double q = __builtin_fma(a, w.q, SHIFT) - SHIFT;
+    return __builtin_fma(-q, P, h) + l;
+}
+// a * b mod p for |a|, |b| <= p, |result| <= p
+__device__ __forceinline__ double mulv(double a, double b)
+{
+    const double h = a * b;
+    const double l = __builtin_fma(a, b, -h);
+    const double q = __builtin_fma(h, PINV, SHIFT) - SHIFT;
+    return __builtin_fma(-q, P, h) + l;
+}
+// a mod p into [-p/2, p/2] (up to one p at the edges), |a| < 2^51
+__device__ __forceinline__ double reduce(double a)
+{
+    const double q = __builtin_fma(a, PINV, SHIFT) - SHIFT;
+    return __builtin_fma(-q, P, a);
+}
+
+// twiddle bank entry i as W (double2 {w, w/p})
+struct Tw {
+    __amdgpu_buffer_rsrc_t rs;
+    __device__ __forceinline__ W at(int voff_elems, int soff_elems) const
+    {
+        const auto d = __builtin_amdgcn_raw_buffer_load_b128(rs, voff_elems * 16, soff_elems * 16, 0);
+        return __builtin_bit_cast(W, d);
+    }
+};
+
+// in-register DFT_R over Z_p (forward, omega_R), natural order in and out, inputs < 2^33
+template <int R>
+__device__ __forceinline__ void dft(double* a);
+
+template <>
+__device__ __forceinline__ void dft<2>(double* a)
+{
+    const double x = a[0];
+    a[0] = x + a[1];
+    a[1] = x - a[1];
+}
+
+template <>
+__device__ __forceinline__ void dft<4>(double* a)
+{
+    constexpr W w4 = root_c(4, 1);
+    const double t0 = a[0] + a[2], t1 = a[0] - a[2];
+    const double t2 = a[1] + a[3], t3 = mulc(a[1] - a[3], w4);
+    a[0] = t0 + t2;
+    a[2] = t0 - t2;
+    a[1] = t1 + t3;
+    a[3] = t1 - t3;
+}
+
+template <>
+__device__ __forceinline__ void dft<8>(double* a)
+{
+    constexpr W w1 = root_c(8, 1), w2 = root_c(8, 2), w3 = root_c(8, 3);
+    double u[4], t[4];
+#pragma unroll
+    for (int n = 0; n < 4; ++n) {
+        u[n] = a[n] + a[n + 4];
+        t[n] = a[n] - a[n + 4];
+    }
+    t[1] = mulc(t[1], w1);
+    t[2] = mulc(t[2], w2);
+    t[3] = mulc(t[3], w3);
+    dft<4>(u);
+    dft<4>(t);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        a[2 * k] = u[k];
+        a[2 * k + 1] = t[k];
+    }
+}
+
+// 16 = 4 x 4:  X[4 k1 + k2] = sum_{n1} w4^{n1 k1} w16^{n1 k2} sum_{n2} x[n1 + 4 n2] w4^{n2 k2}
+template <>
+__device__ __forceinline__ void dft<16>(double* a)
+{
+    double c[4];
+#pragma unroll
+    for (int n1 = 0; n1 < 4; ++n1) {
+        c[0] = a[n1]; c[1] = a[n1 + 4]; c[2] = a[n1 + 8]; c[3] = a[n1 + 12];
+        dft<4>(c);
+        a[n1] = c[0]; a[n1 + 4] = c[1]; a[n1 + 8] = c[2]; a[n1 + 12] = c[3];
+    }
+    // a[n1 + 4 k2] *= w16^{n1 k2}
+    a[5] = mulc(a[5], root_c(16, 1));
+    a[9] = mulc(a[9], root_c(16, 2));
+    a[13] = mulc(a[13], root_c(16, 3));
+    a[6] = mulc(a[6], root_c(16, 2));
+    a[10] = mulc(a[10], root_c(16, 4));
+    a[14] = mulc(a[14], root_c(16, 6));
+    a[7] = mulc(a[7], root_c(16, 3));
+    a[11] = mulc(a[11], root_c(16, 6));
+    a[15] = mulc(a[15], root_c(16, 9));
+#pragma unroll
+    for (int k2 = 0; k2 < 4; ++k2) dft<4>(a + 4 * k2);
+    // a[4 k2 + k1] = X[4 k1 + k2]: transpose to natural order
+    double t;
+    t = a[1]; a[1] = a[4]; a[4] = t;
+    t = a[2]; a[2] = a[8]; a[8] = t;
+    t = a[3]; a[3] = a[12]; a[12] = t;
+    t = a[6]; a[6] = a[9]; a[9] = t;
+    t = a[7]; a[7] = a[13]; a[13] = t;
+    t = a[11]; a[11] = a[14]; a[14] = t;
 }
 
 __device__ __forceinline__ int lds_pad(int a) { return a + (a >> 4); }
 
-// One Stockham DIF pass (index scheme as in the float kernel) over NA arrays that share
-// the twiddles.
-template <int M, int R, int S, bool INV, int NA>
-__device__ __forceinline__ void pass(uint32_t (&x)[NA][16], uint32_t* __restrict__ buf0,
-                                     uint32_t* __restrict__ buf1, int tau,
-                                     const uint2* __restrict__ t)
+template <int TB>
+__device__ __forceinline__ int reg_off(int tau, int q)
 {
-    constexpr int TB = M / 16, NB = 16 / R, Q = M / S, QN = Q / R;
+    if constexpr (TB % 16 == 0) return tau + (tau >> 4) + q * (TB + TB / 16);
+    else return lds_pad(tau + TB * q);
+}
+
+// One Stockham DIF pass (index scheme as in the float kernel) over NA arrays sharing the
+// twiddles.  Passes with twiddles are radix 16 with one item per thread; their outputs are
+// reduced below 2^31 (k2 > 0 by the twiddle product, k2 = 0 explicitly) and stored as int32.
+template <int M, int R, int S, int NA>
+__device__ __forceinline__ void pass(double (&x)[NA][16], int32_t* __restrict__ buf0,
+                                     int32_t* __restrict__ buf1, int tau, const Tw& tw)
+{
+    constexpr int NB = 16 / R, Q = M / S, QN = Q / R;
+    if constexpr (QN > 1) {
+        static_assert(R == 16, "passes with twiddles are radix 16");
+        const int s = tau & (S - 1), n1 = tau / S;
+        W w[16];
 #pragma unroll
-    for (int q = 0; q < NB; ++q) {
-        const int item = tau + TB * q;
-        const int s = item & (S - 1);
-        const int n1 = item / S;
-        uint2 wt[R];
-        if constexpr (QN > 1) {
-#pragma unroll
-            for (int k2 = 1; k2 < R; ++k2) wt[k2] = tw<INV>(t, Q, n1 * k2);
-        }
+        for (int k2 = 1; k2 < 16; ++k2) w[k2] = tw.at(n1, NTT_PASS_BASE + (Q - 32) + k2 * (Q / 16));
+        constexpr int STEP = S == 1 ? 1 : S + S / 16;
+        const int base = S == 1 ? 17 * n1 : (s + (s >> 4)) + 16 * n1 * STEP;
 #pragma unroll
         for (int a = 0; a < NA; ++a) {
-            uint32_t b[R];
+            dft<16>(x[a]);
+            int32_t* buf = a == 0 ? buf0 : buf1;
+            buf[base] = (int32_t)reduce(x[a][0]);
 #pragma unroll
-            for (int n2 = 0; n2 < R; ++n2) b[n2] = x[a][q + NB * n2];
-            dft<R, INV>(b, t);
-            if constexpr (QN > 1) {
-                uint32_t* buf = a == 0 ? buf0 : buf1;
+            for (int k2 = 1; k2 < 16; ++k2) buf[base + k2 * STEP] = (int32_t)mulc(x[a][k2], w[k2]);
+        }
+    } else {
 #pragma unroll
-                for (int k2 = 1; k2 < R; ++k2) b[k2] = mulc(b[k2], wt[k2]);
+        for (int a = 0; a < NA; ++a) {
 #pragma unroll
-                for (int k2 = 0; k2 < R; ++k2) buf[lds_pad(s + S * (k2 + R * n1))] = b[k2];
-            } else {
+            for (int q = 0; q < NB; ++q) {
+                double b[R];
+#pragma unroll
+                for (int n2 = 0; n2 < R; ++n2) b[n2] = x[a][q + NB * n2];
+                dft<R>(b);
 #pragma unroll
                 for (int k2 = 0; k2 < R; ++k2) x[a][q + NB * k2] = b[k2];
             }
@@ -150,70 +228,67 @@ __device__ __forceinline__ void pass(uint32_t (&x)[NA][16], uint32_t* __restrict
     }
 }
 
-template <int M, bool INV, int NA, int S = 1>
-__device__ __forceinline__ void passes(uint32_t (&x)[NA][16], uint32_t* __restrict__ buf0,
-                                       uint32_t* __restrict__ buf1, int tau,
-                                       const uint2* __restrict__ t)
+template <int M, int NA, int S = 1>
+__device__ __forceinline__ void passes(double (&x)[NA][16], int32_t* __restrict__ buf0,
+                                       int32_t* __restrict__ buf1, int tau, const Tw& tw)
 {
     constexpr int TB = M / 16, Q = M / S, R = Q >= 16 ? 16 : Q;
     if constexpr (Q / R > 1) {
-        pass<M, R, S, INV, NA>(x, buf0, buf1, tau, t);
+        pass<M, R, S, NA>(x, buf0, buf1, tau, tw);
         __syncthreads();
 #pragma unroll
         for (int q = 0; q < 16; ++q) {
-            x[0][q] = buf0[lds_pad(tau + TB * q)];
-            if constexpr (NA > 1) x[1][q] = buf1[lds_pad(tau + TB * q)];
+            x[0][q] = (double)buf0[reg_off<TB>(tau, q)];
+            if constexpr (NA > 1) x[1][q] = (double)buf1[reg_off<TB>(tau, q)];
         }
         __syncthreads();
-        passes<M, INV, NA, S * R>(x, buf0, buf1, tau, t);
+        passes<M, NA, S * R>(x, buf0, buf1, tau, tw);
     } else {
-        pass<M, R, S, INV, NA>(x, buf0, buf1, tau, t);
+        pass<M, R, S, NA>(x, buf0, buf1, tau, tw);
     }
-}
-
-// int32 -> residue in [0, p)
-__device__ __forceinline__ uint32_t to_zp(int32_t x)
-{
-    int32_t r = x % (int32_t)P;
-    return (uint32_t)(r < 0 ? r + (int32_t)P : r);
 }
 
 }  // namespace ntt
 
 template <int M>
-__global__ __launch_bounds__(512) void ntt_conv_kernel(const int32_t* __restrict__ v,
+__global__ __launch_bounds__(512, 4) void ntt_conv_kernel(const int32_t* __restrict__ v,
                                                        const int32_t* __restrict__ g,
                                                        int32_t* __restrict__ r, int64_t nch,
-                                                       int L, const uint2* __restrict__ t,
-                                                       uint2 ninv_r)
+                                                       int L, const double* __restrict__ bank,
+                                                       double ninv, double ninv_q)
 {
     using namespace ntt;
     static_assert(M >= 64 && M <= 4096, "fused NTT handles 64 <= M <= 4096");
     constexpr int N = 2 * M, TB = M / 16, UNITS = 512 / TB, CPW = UNITS / 2;
     constexpr int REG = M + M / 16;
-    __shared__ uint32_t lds[UNITS * 2 * REG];
+    __shared__ int32_t lds[UNITS * 2 * REG];
 
+    const Tw tw{__builtin_amdgcn_make_buffer_rsrc((void*)bank, (short)0, NTT_BANK_ENTRIES * 16,
+                                                  0x00020000)};
     const int tid = threadIdx.x;
     const int unit = tid / TB, tau = tid % TB;
     const int cl = unit >> 1, beta = unit & 1;
-    const int64_t ch = (int64_t)blockIdx.x * CPW + cl;
-    const bool valid = ch < nch;
-    uint32_t* bv = lds + unit * 2 * REG;
-    uint32_t* bg = bv + REG;
-    const int64_t base = ch * (int64_t)L;
+    const int64_t ch0 = (int64_t)blockIdx.x * CPW;
+    const int nvalid = (int)((nch - ch0) < CPW ? (nch - ch0) : CPW);
+    const Span vs = make_span(v, ch0 * L, (int64_t)nvalid * L);
+    const Span gs = make_span(g, ch0 * L, (int64_t)nvalid * L);
+    const Span rs = make_span(r, ch0 * L, (int64_t)nvalid * L);
+    int32_t* bv = lds + unit * 2 * REG;
+    int32_t* bg = bv + REG;
+    const int cbase = cl * L;
 
-    // 1. residues of v and g, times omega_N^n on branch 1
-    uint32_t x[2][16];
+    // 1. inputs as exact doubles (|x| < 2^31), times omega_N^n on branch 1
+    double x[2][16];
 #pragma unroll
     for (int q = 0; q < 16; ++q) {
         const int n = tau + TB * q;
-        uint32_t a = 0, b = 0;
-        if (valid && n < L) {
-            a = to_zp(v[base + n]);
-            b = to_zp(g[base + n]);
+        double a = 0.0, b = 0.0;
+        if (L == M || n < L) {
+            a = (double)(int32_t)__builtin_amdgcn_raw_buffer_load_b32(vs.rs, (cbase + n) * 4, 0, 0);
+            b = (double)(int32_t)__builtin_amdgcn_raw_buffer_load_b32(gs.rs, (cbase + n) * 4, 0, 0);
         }
         if (beta) {
-            const uint2 w = tw<false>(t, N, n);
+            const W w = tw.at(n * (NTT_TW_N / N), 0);
             a = mulc(a, w);
             b = mulc(b, w);
         }
@@ -221,36 +296,40 @@ __global__ __launch_bounds__(512) void ntt_conv_kernel(const int32_t* __restrict
         x[1][q] = b;
     }
 
-    // 2. V^beta, G^beta = NTT_M(.), natural order in registers
-    passes<M, false, 2>(x, bv, bg, tau, t);
+    // 2. V, G = NTT_M(.) in natural order (values below 2^36)
+    passes<M, 2>(x, bv, bg, tau, tw);
 
-    // 3. X = V G N^{-1}:  mont(V, G * (N^{-1} 2^32 mod p)) = V G N^{-1}
-    uint32_t y[1][16];
+    // 3. X = V * (G N^{-1})
+    double y[1][16];
 #pragma unroll
-    for (int q = 0; q < 16; ++q) y[0][q] = mont(x[0][q], mulc(x[1][q], ninv_r));
+    for (int q = 0; q < 16; ++q)
+        y[0][q] = mulv(reduce(x[0][q]), reduce(mulc(x[1][q], W{ninv, ninv_q})));
 
-    // 4. e^beta = INTT_M(X^beta)
-    passes<M, true, 1>(y, bv, bv, tau, t);
+    // 4. f = NTT_M(X): e^beta_n = f_{(M - n) mod M}
+    passes<M, 1>(y, bv, bv, tau, tw);
 
-    // 5. x_n = e^0_n + omega_N^{-n} e^1_n: branch 0 finishes q < 8, branch 1 q >= 8;
-    //    each hands the other half to its partner through LDS (region of branch 0)
-    uint32_t* xch = lds + (2 * cl) * 2 * REG;
+    // 5. register q of thread tau holds e^beta at n = (M - tau - TB q) mod M.
+    //    x_n = e^0_n + omega_N^{-n} e^1_n: branch 0 finishes q < 8, branch 1 q >= 8, each
+    //    handing the other half to its partner through LDS (branch 0's v region).
+    int32_t* xch = lds + (2 * cl) * 2 * REG;
+    double own[16];
 #pragma unroll
     for (int q = 0; q < 16; ++q) {
-        const int n = tau + TB * q;
-        if (beta == 0 && q >= 8) xch[lds_pad(n)] = y[0][q];
-        if (beta == 1 && q < 8) xch[lds_pad(n)] = mulc(y[0][q], tw<true>(t, N, n));
+        const int n = (M - tau - TB * q) & (M - 1);
+        // omega_N^{-n} = omega_N^{N - n}
+        own[q] = beta ? mulc(y[0][q], tw.at(((N - n) & (N - 1)) * (NTT_TW_N / N), 0))
+                      : reduce(y[0][q]);
+        if ((q < 8) == (beta == 1)) xch[reg_off<TB>(tau, q)] = (int32_t)own[q];
     }
     __syncthreads();
-    if (valid) {
 #pragma unroll
-        for (int q = 0; q < 16; ++q) {
-            const int n = tau + TB * q;
-            if ((q < 8) != (beta == 0) || n >= L) continue;
-            const uint32_t own = beta ? mulc(y[0][q], tw<true>(t, N, n)) : y[0][q];
-            const uint32_t s = addm(own, xch[lds_pad(n)]);
-            r[base + n] = (int32_t)(s > (P - 1) / 2 ? (int64_t)s - (int64_t)P : (int64_t)s);
-        }
+    for (int q = 0; q < 16; ++q) {
+        if ((q < 8) != (beta == 0)) continue;
+        const int n = (M - tau - TB * q) & (M - 1);
+        if (n >= L) continue;
+        double s = reduce(own[q] + (double)xch[reg_off<TB>(tau, q)]);   // |s| <= p/2 + p
+        s = s > 0.5 * (P - 1.0) ? s - P : (s < -0.5 * (P - 1.0) ? s + P : s);
+        __builtin_amdgcn_raw_buffer_store_b32((uint32_t)(int32_t)s, rs.rs, (cbase + n) * 4, 0, 0);
     }
 }
 
@@ -260,10 +339,9 @@ static hipError_t launch_ntt_m(const int32_t* v, const int32_t* g, int32_t* r, i
 {
     constexpr int CPW = (512 / (M / 16)) / 2;
     const int64_t blocks = (nch + CPW - 1) / CPW;
-    // N^{-1} * 2^32 mod p and its Shoup companion, for N = 2M
-    const uint2 c = tb.ninv_r[__builtin_ctz((unsigned)(2 * M))];
-    hipLaunchKernelGGL((ntt_conv_kernel<M>), dim3((unsigned)blocks), dim3(512), 0, stream, v, g,
-                       r, nch, L, tb.tw, c);
+    const int lg = __builtin_ctz((unsigned)(2 * M));
+    hipLaunchKernelGGL((ntt_conv_kernel<M>), dim3((unsigned)blocks), dim3(512), 0, stream, v, g, r,
+                       nch, L, tb.bank, tb.ninv[lg], tb.ninv_q[lg]);
     return hipGetLastError();
 }
 
