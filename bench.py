@@ -111,6 +111,46 @@ def record_traffic(w, fetch_dir: str, write_dir: str) -> dict:
     return rec
 
 
+def leakage_probe(sc, torch, dev, channels: int = 16) -> dict:
+    """Future-token leakage max_{t<s} |r'_t - r_t| of the float path (fp32, L = 4096,
+    Medium-shaped inputs) and of the exact path (L = 4096, integer inputs): v_s is changed
+    at 8 seeded positions s, the original and the perturbed rows run in one launch."""
+    from workloads import WORKLOADS, bf16_bits_to_f32, make_inputs, perturbation_positions
+
+    def probe(v, g, pos, change):
+        rows = [v] + [change(v.copy(), s) for s in pos]
+        vv = np.concatenate(rows, axis=0)
+        gg = np.concatenate([g] * len(rows), axis=0)
+        out = sc.causal_conv(torch.from_numpy(vv).to(dev), torch.from_numpy(gg).to(dev))
+        r = out.cpu().numpy().astype(np.float64)
+        leak = 0.0
+        for i, s in enumerate(pos):
+            if s > 0:
+                leak = max(leak, float(np.abs(r[i + 1, :, :s] - r[0, :, :s]).max()))
+        return leak, float(np.sqrt(np.mean(r[0] ** 2)))
+
+    w3 = WORKLOADS[3]
+    v, g = make_inputs(w3, B=1, C=channels)
+    v, g = bf16_bits_to_f32(v), bf16_bits_to_f32(g)
+    pos = perturbation_positions(w3.cid, w3.L)
+
+    def bump(a, s):
+        a[:, :, s] += 1.0
+        return a
+    f_leak, f_rms = probe(v, g, pos, bump)
+
+    w5 = WORKLOADS[5]
+    vi, gi = make_inputs(w5, B=1, C=channels)
+    posi = perturbation_positions(w5.cid, w5.L)
+
+    def swap(a, s):
+        a[:, :, s] = np.where(a[:, :, s] >= 0, a[:, :, s] - 100, a[:, :, s] + 100)
+        return a
+    n_leak, _ = probe(vi, gi, posi, swap)
+    return {"fp32_max_abs": f_leak, "fp32_rel_to_rms": f_leak / f_rms, "ntt_max_abs": n_leak,
+            "positions": len(pos), "channels": channels, "L": w3.L}
+
+
 def cpu_baseline(w, v, g, budget_s: float = 10.0):
     """Time the float64 oracle on growing channel samples until one takes >= budget_s/2."""
     import oracle
@@ -258,6 +298,7 @@ def main(argv=None):
                       "p50": round(float(np.median(launch_ms)), 5),
                       "max": round(float(np.max(launch_ms)), 5)},
     }
+    rec["leakage"] = leakage_probe(sc, torch, dev)
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(w, v, g)
     print(json.dumps(rec), flush=True)

@@ -22,6 +22,8 @@
 //
 // HBM traffic per channel: read v, g; write and read T (2M complex) and S (M complex);
 // write r.  Channels are processed in chunks so T and S can stay in the last-level cache.
+// Every twiddle comes from a per-M table (see FsTw in sc_internal.h) laid out so that the
+// lanes of a wave read consecutive entries.
 
 #include "sc_device.h"
 #include "sc_fft_lds.h"
@@ -29,12 +31,6 @@
 
 namespace sc {
 
-// W_N^e from the two-level table: W_N^{(e >> fbits) << fbits} * W_N^{e & (F-1)}
-__device__ __forceinline__ float2 big_tw(const BigTw& t, int e)
-{
-    e &= t.n - 1;
-    return cmul(t.coarse[e >> t.fbits], t.fine[e & ((1 << t.fbits) - 1)]);
-}
 
 // ---------------------------------------------------------------- kernel A: columns, forward
 
@@ -43,7 +39,7 @@ __global__ __launch_bounds__(512) void fs_columns_fwd(const typename IO::T* __re
                                                       const typename IO::T* __restrict__ g,
                                                       float2* __restrict__ T, int64_t ch_begin,
                                                       int L, int M2, const float2* __restrict__ bankp,
-                                                      BigTw tw)
+                                                      FsTw tw)
 {
     constexpr int TQ = M1 / 16, NCOL = 256 / TQ, CREG = M1 + M1 / 16 + 1;
     __shared__ float2 lds[2 * NCOL * CREG];
@@ -62,16 +58,16 @@ __global__ __launch_bounds__(512) void fs_columns_fwd(const typename IO::T* __re
     for (int q = 0; q < 16; ++q) {
         const int n = n1 + M2 * (tau + TQ * q);
         float2 z = make_float2(IO::load(vs, n), IO::load(gs, n));
-        if (beta) z = cmul(z, big_tw(tw, n));
+        if (beta) z = cmul(z, tw.tn[n]);                       // W_N^n
         x[q] = z;
     }
     fft_passes<M1, false>(x, lds + (beta * NCOL + c) * CREG, tau, bank, true);
-    // x[q] = column output k2 = tau + TQ q; times W_M^{n1 k2} = W_N^{2 n1 k2}
+    // x[q] = column output k2 = tau + TQ q; times W_M^{n1 k2}
     float2* out = T + (int64_t)(chl * 2 + beta) * M1 * M2;
 #pragma unroll
     for (int q = 0; q < 16; ++q) {
         const int k2 = tau + TQ * q;
-        out[(int64_t)k2 * M2 + n1] = cmul(x[q], big_tw(tw, 2 * n1 * k2));
+        out[(int64_t)k2 * M2 + n1] = cmul(x[q], tw.ta[(int64_t)k2 * M2 + n1]);
     }
 }
 
@@ -81,9 +77,8 @@ __global__ __launch_bounds__(512) void fs_columns_fwd(const typename IO::T* __re
 // Returns Y_j and Y_{partner}, both scaled by 8 like the fused kernel.
 template <class At>
 __device__ __forceinline__ void fs_unpack(int rho, int k1, int beta, int M1, int M2, int M,
-                                          const At& at, const BigTw& tw, float2& yj, float2& yp)
+                                          const At& at, const FsTw& tw, float2& yj, float2& yp)
 {
-    const int j = M1 * k1 + rho;
     const bool zero = rho + beta == 0;
     const int prow = zero ? 0 : M1 - rho - beta;
     const float2 p1 = at(rho, k1);
@@ -98,7 +93,8 @@ __device__ __forceinline__ void fs_unpack(int rho, int k1, int beta, int M1, int
                                   __builtin_fmaf(s2.y, d2.y, -s2.x * d2.x));
     const float2 sm = make_float2(x1.x + x2.x, x1.y - x2.y);
     const float2 df = make_float2(x1.x - x2.x, x1.y + x2.y);
-    const float2 t = cmulc(df, big_tw(tw, 2 * j + beta));       // W_N^{-k} D, k = 2j + b
+    // W_N^{-k} D with k = 2 (M1 k1 + rho) + b
+    const float2 t = cmulc(df, tw.tu[(int64_t)(2 * rho + beta) * (M2 / 4 + 1) + k1]);
     yj = make_float2(sm.x - t.y, sm.y + t.x);
     yp = make_float2(sm.x + t.y, t.x - sm.y);
     (void)M;
@@ -106,10 +102,10 @@ __device__ __forceinline__ void fs_unpack(int rho, int k1, int beta, int M1, int
 
 template <int M2>
 __global__ __launch_bounds__(512) void fs_rows(const float2* __restrict__ T, float2* __restrict__ S,
-                                               int M1, const float2* __restrict__ bankp, BigTw tw)
+                                               int M1, const float2* __restrict__ bankp, FsTw tw)
 {
     constexpr int TR = M2 / 16, PAIRS = (2048 / M2) > 1 ? 2048 / M2 : 1;
-    constexpr int RREG = M2 + M2 / 16 + 1, H = M2 / 2, TH = H / 16;
+    constexpr int RREG = M2 + M2 / 16 + 1, H = M2 / 2;
     __shared__ float2 lds[PAIRS * 2 * RREG];
     const Bank bank = make_bank(bankp);
     const int M = M1 * M2;
@@ -170,22 +166,18 @@ __global__ __launch_bounds__(512) void fs_rows(const float2* __restrict__ T, flo
     }
     __syncthreads();
 
-    // row inverse DFT of length H (first TH threads of each row)
-    const bool iact = tau < TH;
-    if (iact) {
+    // row inverse DFT of length H, 8 values per thread (H/8 = TR threads per row)
+    float2 y8[8];
 #pragma unroll
-        for (int q = 0; q < 16; ++q) x[q] = mybuf[reg_off<TH>(tau, q)];
-    }
+    for (int q = 0; q < 8; ++q) y8[q] = mybuf[reg_off<TR>(tau, q)];
     __syncthreads();
-    fft_passes<H, true>(x, mybuf, tau, bank, iact);
-    if (iact) {
-        float2* out = S + ((int64_t)(chl * 2 + beta) * M1 + row) * H;
+    fft_passes<H, true, 1, 8>(y8, mybuf, tau, bank, true);
+    float2* out = S + ((int64_t)(chl * 2 + beta) * M1 + row) * H;
+    const float2* twr = tw.tb + (int64_t)row * H;
 #pragma unroll
-        for (int q = 0; q < 16; ++q) {
-            const int m1 = tau + TH * q;
-            // W_{M/2}^{-m1 row} = W_N^{-4 m1 row}
-            out[m1] = cmulc(x[q], big_tw(tw, 4 * m1 * row));
-        }
+    for (int q = 0; q < 8; ++q) {
+        const int m1 = tau + TR * q;
+        out[m1] = cmulc(y8[q], twr[m1]);             // W_{M/2}^{-m1 row}
     }
 }
 
@@ -196,7 +188,7 @@ __global__ __launch_bounds__(512) void fs_columns_inv(const float2* __restrict__
                                                       typename IO::T* __restrict__ r,
                                                       int64_t ch_begin, int L, int M2, int head,
                                                       int pair_store,
-                                                      const float2* __restrict__ bankp, BigTw tw)
+                                                      const float2* __restrict__ bankp, FsTw tw)
 {
     constexpr int TQ = M1 / 16, NCOL = 256 / TQ, CREG = M1 + M1 / 16 + 1;
     __shared__ float2 lds[2 * NCOL * CREG];
@@ -221,7 +213,7 @@ __global__ __launch_bounds__(512) void fs_columns_inv(const float2* __restrict__
 #pragma unroll
         for (int q = 0; q < 16; ++q) {
             const int m = m1 + H * (tau + TQ * q);
-            mybuf[reg_off<TQ>(tau, q)] = cmulc(x[q], big_tw(tw, 2 * m));   // W_M^{-m} o_m
+            mybuf[reg_off<TQ>(tau, q)] = cmulc(x[q], tw.tn[2 * m]);   // W_M^{-m} o_m
         }
     }
     __syncthreads();
@@ -272,7 +264,7 @@ __global__ void head_kernel(const typename IO::T* __restrict__ v, const typename
 template <class IO, int M1>
 static hipError_t launch_cols(bool fwd, const void* v, const void* g, void* r, float2* T,
                               const float2* S, int64_t c0, int nc, int L, int M2, int head,
-                              bool pair, const float2* bank, const BigTw& tw, hipStream_t s)
+                              bool pair, const float2* bank, const FsTw& tw, hipStream_t s)
 {
     constexpr int NCOL = 256 / (M1 / 16);
     if (fwd) {
@@ -292,7 +284,7 @@ static hipError_t launch_cols(bool fwd, const void* v, const void* g, void* r, f
 template <class IO>
 static hipError_t dispatch_cols(bool fwd, int M1, const void* v, const void* g, void* r, float2* T,
                                 const float2* S, int64_t c0, int nc, int L, int M2, int head,
-                                bool pair, const float2* bank, const BigTw& tw, hipStream_t s)
+                                bool pair, const float2* bank, const FsTw& tw, hipStream_t s)
 {
     switch (M1) {
     case 64: return launch_cols<IO, 64>(fwd, v, g, r, T, S, c0, nc, L, M2, head, pair, bank, tw, s);
@@ -306,7 +298,7 @@ static hipError_t dispatch_cols(bool fwd, int M1, const void* v, const void* g, 
 
 template <int M2>
 static hipError_t launch_rows(const float2* T, float2* S, int nc, int M1, const float2* bank,
-                              const BigTw& tw, hipStream_t s)
+                              const FsTw& tw, hipStream_t s)
 {
     constexpr int TR = M2 / 16, PAIRS = (2048 / M2) > 1 ? 2048 / M2 : 1;
     const int64_t blocks = (int64_t)nc * 2 * ((M1 / 2) / PAIRS);
@@ -316,7 +308,7 @@ static hipError_t launch_rows(const float2* T, float2* S, int nc, int M1, const 
 }
 
 static hipError_t dispatch_rows(int M2, const float2* T, float2* S, int nc, int M1,
-                                const float2* bank, const BigTw& tw, hipStream_t s)
+                                const float2* bank, const FsTw& tw, hipStream_t s)
 {
     switch (M2) {
     case 64: return launch_rows<64>(T, S, nc, M1, bank, tw, s);
@@ -345,7 +337,7 @@ size_t fourstep_bytes_per_channel(int M)
 }
 
 hipError_t launch_fourstep(Store st, const void* v, const void* g, void* r, int64_t nch, int L,
-                           int M, int head, bool pair_store, const float2* bank, const BigTw& tw,
+                           int M, int head, bool pair_store, const float2* bank, const FsTw& tw,
                            void* ws, int64_t chunk, hipStream_t stream)
 {
     int M1, M2;

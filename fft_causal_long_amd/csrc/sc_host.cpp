@@ -39,7 +39,7 @@ struct DeviceState {
     float2* fused_tw = nullptr;   // the float twiddle bank (sc_internal.h)
     sc::NttTables ntt{};
     bool ntt_ready = false;
-    std::map<int, sc::BigTw> big;   // four-step tables by N
+    std::map<int, sc::FsTw> fs;     // four-step tables by M
 };
 
 uint64_t powmod(uint64_t b, uint64_t e, uint64_t m)
@@ -135,25 +135,37 @@ sc_status device_state(DeviceState** out, bool need_ntt)
     return SC_OK;
 }
 
-// two-level W_N table for the four-step path (built once per device and N)
-sc_status big_tables(DeviceState& d, int N, sc::BigTw* out)
+// four-step twiddle tables for one M (built once per device and M)
+sc_status fourstep_tables(DeviceState& d, int M, sc::FsTw* out)
 {
-    auto it = d.big.find(N);
-    if (it != d.big.end()) {
+    auto it = d.fs.find(M);
+    if (it != d.fs.end()) {
         *out = it->second;
         return SC_OK;
     }
-    int lg = 0;
-    while ((1 << lg) < N) ++lg;
-    const int fbits = (lg + 1) / 2, F = 1 << fbits, NC = N / F;
-    std::vector<float2> h((size_t)NC + F);
-    for (int i = 0; i < NC; ++i) h[i] = unit_root((int64_t)i * F, N);
-    for (int i = 0; i < F; ++i) h[(size_t)NC + i] = unit_root(i, N);
+    int M1, M2;
+    sc::fourstep_split(M, &M1, &M2);
+    const int64_t N = 2 * (int64_t)M, H = M2 / 2, U = M2 / 4 + 1;
+    const size_t nn = (size_t)N, na = (size_t)M, nb = (size_t)M1 * H, nu = (size_t)2 * M1 * U;
+    std::vector<float2> h(nn + na + nb + nu);
+    float2* tn = h.data();
+    float2* ta = tn + nn;
+    float2* tb = ta + na;
+    float2* tu = tb + nb;
+    for (int64_t e = 0; e < N; ++e) tn[e] = unit_root(e, N);
+    for (int64_t k2 = 0; k2 < M1; ++k2)
+        for (int64_t n1 = 0; n1 < M2; ++n1) ta[k2 * M2 + n1] = unit_root(n1 * k2, M);
+    for (int64_t i2 = 0; i2 < M1; ++i2)
+        for (int64_t m1 = 0; m1 < H; ++m1) tb[i2 * H + m1] = unit_root(m1 * i2, M / 2);
+    for (int64_t r2 = 0; r2 < 2 * M1; ++r2)
+        for (int64_t k1 = 0; k1 < U; ++k1)
+            tu[r2 * U + k1] = unit_root(2 * (M1 * k1 + (r2 >> 1)) + (r2 & 1), N);
     void* p = nullptr;
     sc_status st = upload(h.data(), h.size() * sizeof(float2), &p);
     if (st != SC_OK) return st;
-    sc::BigTw t{(const float2*)p, (const float2*)p + NC, fbits, N};
-    d.big[N] = t;
+    const float2* base = (const float2*)p;
+    sc::FsTw t{base, base + nn, base + nn + na, base + nn + na + nb};
+    d.fs[M] = t;
     *out = t;
     return SC_OK;
 }
@@ -289,10 +301,10 @@ sc_status run(sc_kind kind, const void* v, const void* g, void* r, int64_t B, in
             e = sc::launch_fused(s, v, g, r, nch, (int)L, M, head, pair, d->fused_tw, stream);
         } else {
             const int M = (int)next_pow2(L);
-            sc::BigTw tw;
+            sc::FsTw tw;
             {
                 std::lock_guard<std::mutex> lk(g_mu);
-                st = big_tables(*d, 2 * M, &tw);
+                st = fourstep_tables(*d, M, &tw);
             }
             if (st != SC_OK) return st;
             int64_t chunk;

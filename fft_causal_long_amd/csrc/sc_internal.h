@@ -49,19 +49,23 @@ constexpr int FOURSTEP_MAX_ROW = 4096;
 // Largest sequence length of the four-step path (N = 2M <= 2^23 divides p - 1 as well).
 constexpr int64_t FOURSTEP_MAX_L = (int64_t)1 << 22;
 
-// Two-level table of W_N^e for one N: coarse[h] = W_N^{h F}, fine[l] = W_N^l, F = 2^fbits.
-struct BigTw {
-    const float2* coarse;
-    const float2* fine;
-    int fbits;
-    int n;
+// Twiddle tables of the four-step path for one M = M1 * M2 (N = 2M, H = M2/2):
+//   tn[e]                          W_N^e, e < N
+//   ta[k2 * M2 + n1]               W_M^{n1 k2}        (k2 < M1, n1 < M2)
+//   tb[i2 * H + m1]                W_{M/2}^{m1 i2}    (i2 < M1, m1 < H)
+//   tu[(2 rho + b) * (M2/4 + 1) + k1]  W_N^{2 (M1 k1 + rho) + b}   (rho < M1, b < 2, k1 <= M2/4)
+struct FsTw {
+    const float2* tn;
+    const float2* ta;
+    const float2* tb;
+    const float2* tu;
 };
 
 void fourstep_split(int M, int* M1, int* M2);
 size_t fourstep_bytes_per_channel(int M);
 // ws holds chunk channels of scratch (chunk * fourstep_bytes_per_channel(M) bytes).
 hipError_t launch_fourstep(Store st, const void* v, const void* g, void* r, int64_t nch, int L,
-                           int M, int head, bool pair_store, const float2* bank, const BigTw& tw,
+                           int M, int head, bool pair_store, const float2* bank, const FsTw& tw,
                            void* ws, int64_t chunk, hipStream_t stream);
 
 // Direct summation r_t = sum_{j<=t} v_j g_{t-j} in fp32, one thread per output.
