@@ -65,12 +65,15 @@ COPY_BYTES = 1 << 30   # the --calib-copy transfer: 2^28 float32 read and writte
 
 
 def kernel_matches(name: str, storage: str, L: int) -> bool:
-    """Is this profiled kernel part of the timed hot path of the workload?"""
+    """Is this profiled kernel part of the timed hot path of the workload?  (Exact template,
+    so launches of the leakage probe or of other shapes do not count.)"""
+    M = max(64, 1 << (L - 1).bit_length())
     if storage == "i32":
-        return "ntt_conv_kernel" in name
+        return ("ntt_conv_kernel<%d>" % M) in name
     if L > 4096:
         return "fs_" in name or "head_kernel" in name
-    return "fused_conv_kernel" in name
+    io = "bf16_io" if storage == "bf16" else "f32_io"
+    return ("fused_conv_kernel<%d, sc::%s>" % (M, io)) in name
 
 
 def record_traffic(w, fetch_dir: str, write_dir: str) -> dict:
@@ -183,6 +186,8 @@ def main(argv=None):
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-leakage", action="store_true",
+                    help="skip the leakage probe (keeps profiler runs to the timed kernel)")
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run a plain device copy of known size (profiler calibration)")
     ap.add_argument("--record-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
@@ -298,7 +303,8 @@ def main(argv=None):
                       "p50": round(float(np.median(launch_ms)), 5),
                       "max": round(float(np.max(launch_ms)), 5)},
     }
-    rec["leakage"] = leakage_probe(sc, torch, dev)
+    if not args.no_leakage:
+        rec["leakage"] = leakage_probe(sc, torch, dev)
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(w, v, g)
     print(json.dumps(rec), flush=True)

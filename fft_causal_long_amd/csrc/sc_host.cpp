@@ -18,8 +18,12 @@ constexpr int kDefaultHead = 32;
 constexpr int kMaxHead = 64;
 constexpr int64_t kMaxLFused = 4096;     // fused path; longer sequences use the four-step path
 constexpr int64_t kMinLFourStep = 2049;  // the four-step split needs M >= 4096
-// channels per four-step chunk: as many as fit this much scratch (last-level cache sized)
-constexpr int64_t kFourStepChunkBytes = (int64_t)96 << 20;
+// channels per four-step chunk: as many as fit this much scratch (enough channels to
+// fill the GPU in every kernel of the chunk; measured best among 24..384 MB)
+#ifndef SC_FS_CHUNK_MB
+#define SC_FS_CHUNK_MB 192
+#endif
+constexpr int64_t kFourStepChunkBytes = (int64_t)SC_FS_CHUNK_MB << 20;
 constexpr int64_t kMaxLNtt = 4096;
 constexpr int64_t kNttP = 998244353;
 

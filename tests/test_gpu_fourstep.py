@@ -61,12 +61,15 @@ def test_four_step_L65536_few_channels(sc):
 
 
 def test_four_step_several_chunks(sc):
-    # 600 channels at L = 8192 span two scratch chunks
-    L, C = 8192, 600
+    # more channels than one scratch chunk holds, so the call loops over chunks
+    L = 16384
     per = sc.sc_workspace_bytes(sc.KIND_F32, 1, 1, L)
+    chunk = sc.sc_workspace_bytes(sc.KIND_F32, 1, 10**6, L) // per
+    C = chunk + 37
     assert sc.sc_workspace_bytes(sc.KIND_F32, 1, C, L) < per * C
     v, g = make_inputs(WORKLOADS[4], B=1, C=C, L=L, seed_offset=13)
-    check(sc, v, g, "four-step 600 channels", chans=np.array([0, 1, 255, 511, 512, 513, 598, 599]))
+    chans = np.array([0, 1, chunk - 1, chunk, chunk + 1, C - 1])
+    check(sc, v, g, "four-step %d channels (chunk %d)" % (C, chunk), chans=chans)
 
 
 def test_config4_full_size_sampled(sc):
