@@ -178,9 +178,12 @@ struct f32_io {
     static constexpr int SIZE = 4;
     __device__ __forceinline__ static float load(const float* p, int64_t i) { return p[i]; }
     __device__ __forceinline__ static void store(float* p, int64_t i, float x) { p[i] = x; }
+    // Element OOB sits at byte offset 2^31, past every descriptor's range: it reads 0.
+    static constexpr int OOB = (int)(0x80000000u / 4);
     __device__ __forceinline__ static float load(const Span& s, int i)
     {
-        return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(s.rs, i * 4, 0, 0));
+        return __uint_as_float(
+            __builtin_amdgcn_raw_buffer_load_b32(s.rs, (int)((uint32_t)i * 4u), 0, 0));
     }
     __device__ __forceinline__ static void store(const Span& s, int i, float x)
     {
@@ -206,9 +209,11 @@ struct bf16_io {
     {
         p[i] = (uint16_t)pack_bf16x2(x, 0.f);
     }
+    static constexpr int OOB = (int)(0x80000000u / 2);
     __device__ __forceinline__ static float load(const Span& s, int i)
     {
-        return __uint_as_float(((uint32_t)__builtin_amdgcn_raw_buffer_load_b16(s.rs, i * 2, 0, 0)) << 16);
+        const uint32_t w = __builtin_amdgcn_raw_buffer_load_b16(s.rs, (int)((uint32_t)i * 2u), 0, 0);
+        return __uint_as_float(w << 16);
     }
     __device__ __forceinline__ static void store(const Span& s, int i, float x)
     {

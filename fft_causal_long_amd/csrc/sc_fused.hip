@@ -109,11 +109,13 @@ __global__ __launch_bounds__(FUSED_THREADS) void fused_conv_kernel(
                 x[q] = make_float2(IO::load(vs, cbase + n), IO::load(gs, cbase + n));
             }
         } else {
+            // elements past L are read at IO::OOB, beyond the descriptor's range, so they read
+            // 0; a select instead of a branch keeps all 32 loads in flight together
 #pragma unroll
             for (int q = 0; q < 16; ++q) {
                 const int n = tau + TB * q;
-                x[q] = make_float2(0.f, 0.f);
-                if (n < L) x[q] = make_float2(IO::load(vs, cbase + n), IO::load(gs, cbase + n));
+                const int e = n < L ? cbase + n : IO::OOB;
+                x[q] = make_float2(IO::load(vs, e), IO::load(gs, e));
             }
         }
         if (!beta) {
