@@ -19,6 +19,10 @@ blocking or fusion (see ``oracle.c`` for the C side):
   Token Leakage in Convolutional Sequence Modeling and How to Mitigate It", abstract:
   FFTs done on integers only).
 * :func:`causal_conv_f64_at` -- the float64 sum for sampled (channel, t) outputs.
+* :func:`causal_conv_bwd_f64` / :func:`causal_conv_bwd_i64` -- the gradients of
+  sum_t dr[t] r[t]: dv[j] = sum_{t>=j} dr[t] g[t-j], dg[k] = sum_{t>=k} dr[t] v[t-k], with
+  their error scales (the pages' models are trained end to end with a next-token loss,
+  "Caracal", loss function / training strategy).
 * :func:`circular_conv_dft` / :func:`circular_conv_ntt` -- the pages' recipe (zero-pad on
   the right to n, transform, multiply, inverse, keep all n values) with O(n^2) DFT / NTT,
   used only to pin key design 2 against the direct sum.
@@ -81,6 +85,10 @@ def _load():
         lib.oracle_circular_dft_f64.restype = ctypes.c_int
         lib.oracle_circular_ntt.argtypes = [lp, lp, i64, i64, ctypes.c_uint32, ctypes.c_uint32, lp]
         lib.oracle_circular_ntt.restype = ctypes.c_int
+        lib.oracle_conv_bwd_f64.argtypes = [dp] * 7 + [i64, i64, ctypes.c_int]
+        lib.oracle_conv_bwd_f64.restype = ctypes.c_int
+        lib.oracle_conv_bwd_i64.argtypes = [lp] * 5 + [i64, i64, ctypes.c_int]
+        lib.oracle_conv_bwd_i64.restype = ctypes.c_int
         _lib = lib
         return lib
 
@@ -158,6 +166,51 @@ def causal_conv_i64(v, g, nthreads: int | None = None) -> np.ndarray:
     if rc != 0:
         raise RuntimeError("oracle_conv_i64 failed")
     return r
+
+
+def causal_conv_bwd_f64(dr, v, g, nthreads: int | None = None, with_scale: bool = True):
+    """Gradients of sum_t dr[t] r[t] for the causal convolution r of v and g (last axis),
+    float64: returns ``(dv, dg, Sv, Sg)`` with Sv[j] = sum_{t>=j} |dr[t]| |g[t-j]| and Sg
+    likewise (both None when ``with_scale`` is False)."""
+    d64, v64, g64 = as_f64(dr), as_f64(v), as_f64(g)
+    if not (d64.shape == v64.shape == g64.shape):
+        raise ValueError("dr, v and g must have the same shape")
+    shape = v64.shape
+    L = shape[-1] if len(shape) else 0
+    nch = int(np.prod(shape[:-1])) if len(shape) > 1 else 1
+    dv, dg = np.zeros(shape), np.zeros(shape)
+    Sv = np.zeros(shape) if with_scale else None
+    Sg = np.zeros(shape) if with_scale else None
+    if v64.size == 0:
+        return dv, dg, Sv, Sg
+    rc = _load().oracle_conv_bwd_f64(
+        _dptr(d64), _dptr(v64), _dptr(g64), _dptr(dv), _dptr(dg),
+        _dptr(Sv) if with_scale else None, _dptr(Sg) if with_scale else None,
+        nch, L, nthreads or default_threads(),
+    )
+    if rc != 0:
+        raise RuntimeError("oracle_conv_bwd_f64 failed")
+    return dv, dg, Sv, Sg
+
+
+def causal_conv_bwd_i64(dr, v, g, nthreads: int | None = None):
+    """Exact int64 gradients ``(dv, dg)`` of sum_t dr[t] r[t] (last axis)."""
+    d64 = np.ascontiguousarray(dr, dtype=np.int64)
+    v64 = np.ascontiguousarray(v, dtype=np.int64)
+    g64 = np.ascontiguousarray(g, dtype=np.int64)
+    if not (d64.shape == v64.shape == g64.shape):
+        raise ValueError("dr, v and g must have the same shape")
+    shape = v64.shape
+    L = shape[-1] if len(shape) else 0
+    nch = int(np.prod(shape[:-1])) if len(shape) > 1 else 1
+    dv, dg = np.zeros(shape, dtype=np.int64), np.zeros(shape, dtype=np.int64)
+    if v64.size == 0:
+        return dv, dg
+    rc = _load().oracle_conv_bwd_i64(_lptr(d64), _lptr(v64), _lptr(g64), _lptr(dv), _lptr(dg),
+                                     nch, L, nthreads or default_threads())
+    if rc != 0:
+        raise RuntimeError("oracle_conv_bwd_i64 failed")
+    return dv, dg
 
 
 def lift_mod_p(r, p: int = P_NTT) -> np.ndarray:

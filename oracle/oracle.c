@@ -30,8 +30,18 @@
  *                     omega = root^((p-1)/n), pointwise product, inverse with n^{-1} mod p.
  *                     Residues in [0, p).
  *
+ *   oracle_conv_bwd_f64  the gradients of the scalar sum_t dr[t] r[t] with respect to v
+ *                     and g (the pages' models are trained end to end with a next-token
+ *                     loss, "Caracal", loss function / training strategy, so the
+ *                     primitive's backward pass is needed):
+ *                       dv[j] = sum_{t=j..L-1} dr[t] g[t-j],  dg[k] = sum_{t=k..L-1} dr[t] v[t-k]
+ *                     with the error scales sv, sg (the same sums of absolute values).
+ *
+ *   oracle_conv_bwd_i64  the same two sums in exact int64.
+ *
  * Loop order of the direct sums is "for j: for t >= j: r[t] += v[j]*g[t-j]" (an axpy per
- * input tap), which fixes the rounding order and touches r[t] only with v[0..t].
+ * input tap), which fixes the rounding order and touches r[t] only with v[0..t].  The
+ * gradient sums run "for t: for j <= t: dv[j] += dr[t]*g[t-j]" (an axpy per output tap).
  * Build flags: -O2 -ffp-contract=off (no fused multiply-add contraction).
  *
  * Threads: channels are independent, so a channel range is given to each POSIX thread.
@@ -156,6 +166,85 @@ int oracle_conv_i64(const int64_t *v, const int64_t *g, int64_t *r, int64_t nch,
     if (!v || !g || !r) return -1;
     i64_ctx k = {v, g, r, L};
     return for_channels(conv_i64_channel, &k, nch, nthreads);
+}
+
+/* ---------------------------------------------------------------- gradients */
+
+typedef struct {
+    const double *dr, *v, *g;
+    double *dv, *dg, *sv, *sg;
+    int64_t L;
+} bwd_f64_ctx;
+
+static void bwd_f64_channel(void *p, int64_t c)
+{
+    bwd_f64_ctx *k = (bwd_f64_ctx *)p;
+    const int64_t L = k->L;
+    const double *dr = k->dr + c * L, *v = k->v + c * L, *g = k->g + c * L;
+    double *dv = k->dv + c * L, *dg = k->dg + c * L;
+    double *sv = k->sv ? k->sv + c * L : NULL, *sg = k->sg ? k->sg + c * L : NULL;
+    for (int64_t j = 0; j < L; ++j) dv[j] = dg[j] = 0.0;
+    if (sv)
+        for (int64_t j = 0; j < L; ++j) sv[j] = sg[j] = 0.0;
+    for (int64_t t = 0; t < L; ++t) {
+        const double d = dr[t];
+        for (int64_t j = 0; j <= t; ++j) {
+            dv[j] += d * g[t - j];
+            dg[j] += d * v[t - j];
+        }
+        if (sv) {
+            const double a = fabs(d);
+            for (int64_t j = 0; j <= t; ++j) {
+                sv[j] += a * fabs(g[t - j]);
+                sg[j] += a * fabs(v[t - j]);
+            }
+        }
+    }
+}
+
+/* dv, dg (and sv, sg when not NULL): [nch][L].  Returns 0, or -1 on a bad argument. */
+int oracle_conv_bwd_f64(const double *dr, const double *v, const double *g, double *dv,
+                        double *dg, double *sv, double *sg, int64_t nch, int64_t L,
+                        int nthreads)
+{
+    if (nch < 0 || L < 0) return -1;
+    if (nch == 0 || L == 0) return 0;
+    if (!dr || !v || !g || !dv || !dg || (!sv) != (!sg)) return -1;
+    bwd_f64_ctx k = {dr, v, g, dv, dg, sv, sg, L};
+    return for_channels(bwd_f64_channel, &k, nch, nthreads);
+}
+
+typedef struct {
+    const int64_t *dr, *v, *g;
+    int64_t *dv, *dg;
+    int64_t L;
+} bwd_i64_ctx;
+
+static void bwd_i64_channel(void *p, int64_t c)
+{
+    bwd_i64_ctx *k = (bwd_i64_ctx *)p;
+    const int64_t L = k->L;
+    const int64_t *dr = k->dr + c * L, *v = k->v + c * L, *g = k->g + c * L;
+    int64_t *dv = k->dv + c * L, *dg = k->dg + c * L;
+    for (int64_t j = 0; j < L; ++j) dv[j] = dg[j] = 0;
+    for (int64_t t = 0; t < L; ++t) {
+        const int64_t d = dr[t];
+        for (int64_t j = 0; j <= t; ++j) {
+            dv[j] += d * g[t - j];
+            dg[j] += d * v[t - j];
+        }
+    }
+}
+
+/* Exact while every partial sum fits in int64. */
+int oracle_conv_bwd_i64(const int64_t *dr, const int64_t *v, const int64_t *g, int64_t *dv,
+                        int64_t *dg, int64_t nch, int64_t L, int nthreads)
+{
+    if (nch < 0 || L < 0) return -1;
+    if (nch == 0 || L == 0) return 0;
+    if (!dr || !v || !g || !dv || !dg) return -1;
+    bwd_i64_ctx k = {dr, v, g, dv, dg, L};
+    return for_channels(bwd_i64_channel, &k, nch, nthreads);
 }
 
 /* ---------------------------------------------------------------- sampled outputs */

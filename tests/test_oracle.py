@@ -283,3 +283,110 @@ def test_empty_and_bad_shapes():
     assert r.shape == (3, 0)
     with pytest.raises(ValueError):
         causal_conv_f64(np.zeros((2, 4)), np.zeros((2, 5)))
+
+
+# ---------------------------------------------------------------- gradients
+
+GOLDEN_BWD = os.path.join(os.path.dirname(__file__), "golden", "hand_cases_bwd.txt")
+
+
+def _golden_bwd():
+    cases = []
+    with open(GOLDEN_BWD) as f:
+        for line in f:
+            line = line.strip()
+            if not line or line.startswith("#"):
+                continue
+            fields = [x.strip() for x in line.split("|")]
+            cases.append((fields[0],) + tuple([int(x) for x in f_.split()] for f_ in fields[1:]))
+    assert len(cases) >= 5
+    return cases
+
+
+@pytest.mark.parametrize("case", _golden_bwd(), ids=lambda c: c[0])
+def test_golden_bwd(case):
+    _, dr, v, g, edv, edg = case
+    dv, dg, Sv, Sg = oracle.causal_conv_bwd_f64(np.array(dr, np.float64), np.array(v, np.float64),
+                                                np.array(g, np.float64))
+    assert dv.tolist() == [float(x) for x in edv]
+    assert dg.tolist() == [float(x) for x in edg]
+    assert np.all(Sv >= np.abs(dv)) and np.all(Sg >= np.abs(dg))
+    idv, idg = oracle.causal_conv_bwd_i64(np.array(dr), np.array(v), np.array(g))
+    assert idv.tolist() == edv and idg.tolist() == edg
+
+
+@pytest.mark.parametrize("L", [1, 2, 3, 17, 64, 200])
+def test_bwd_matches_numpy_correlate(L):
+    # numpy.correlate(a, b, "full")[L-1+j] = sum_n a[n+j] b[n]: with a = dr, b = g that is dv_j
+    rng = np.random.default_rng(500 + L)
+    dr, v, g = rng.standard_normal((3, 2, L))
+    dv, dg, _, _ = oracle.causal_conv_bwd_f64(dr, v, g)
+    for c in range(2):
+        np.testing.assert_allclose(dv[c], np.correlate(dr[c], g[c], "full")[L - 1:], rtol=0,
+                                   atol=1e-12 * L)
+        np.testing.assert_allclose(dg[c], np.correlate(dr[c], v[c], "full")[L - 1:], rtol=0,
+                                   atol=1e-12 * L)
+    ir, iv, ig = rng.integers(-50, 51, size=(3, 2, L))
+    idv, idg = oracle.causal_conv_bwd_i64(ir, iv, ig)
+    for c in range(2):
+        assert np.array_equal(idv[c], np.correlate(ir[c], ig[c], "full")[L - 1:])
+        assert np.array_equal(idg[c], np.correlate(ir[c], iv[c], "full")[L - 1:])
+
+
+def test_bwd_adjoint_and_reversal_identities_exact():
+    # sum_t dr_t r_t = sum_j dv_j v_j = sum_k dg_k g_k (the loss is bilinear), and
+    # dv = rev(causal(rev(dr), g)), dg = rev(causal(rev(dr), v)), against the forward oracle
+    rng = np.random.default_rng(7)
+    for L in (1, 5, 33, 128):
+        dr, v, g = rng.integers(-100, 101, size=(3, 3, L))
+        r = causal_conv_i64(v, g)
+        dv, dg = oracle.causal_conv_bwd_i64(dr, v, g)
+        loss = (dr * r).sum(axis=-1)
+        assert np.array_equal((dv * v).sum(axis=-1), loss)
+        assert np.array_equal((dg * g).sum(axis=-1), loss)
+        assert np.array_equal(dv, causal_conv_i64(dr[:, ::-1], g)[:, ::-1])
+        assert np.array_equal(dg, causal_conv_i64(dr[:, ::-1], v)[:, ::-1])
+
+
+def test_bwd_matches_torch_autograd():
+    # torch's conv1d (a library convolution) and its autograd, in float64 on the CPU
+    import torch
+    rng = np.random.default_rng(11)
+    nch, L = 3, 40
+    dr, v, g = rng.standard_normal((3, nch, L))
+    tv = torch.tensor(v, requires_grad=True)
+    tg = torch.tensor(g, requires_grad=True)
+    # r[c, t] = sum_k g[c, k] v[c, t-k]: cross-correlation of left-padded v with flipped g
+    x = torch.nn.functional.pad(tv, (L - 1, 0)).unsqueeze(0)            # (1, nch, 2L-1)
+    w = torch.flip(tg, dims=[-1]).unsqueeze(1)                          # (nch, 1, L)
+    r = torch.nn.functional.conv1d(x, w, groups=nch)[0]                 # (nch, L)
+    (torch.tensor(dr) * r).sum().backward()
+    dv, dg, _, _ = oracle.causal_conv_bwd_f64(dr, v, g)
+    np.testing.assert_allclose(r.detach().numpy(), causal_conv_f64(v, g)[0], atol=1e-12)
+    np.testing.assert_allclose(tv.grad.numpy(), dv, atol=1e-12)
+    np.testing.assert_allclose(tg.grad.numpy(), dg, atol=1e-12)
+
+
+def test_bwd_anticausal_and_scales():
+    # dv_j reads dr_t only for t >= j: perturbing dr_s leaves dv_j, dg_j for j > s unchanged
+    rng = np.random.default_rng(12)
+    L = 50
+    dr, v, g = rng.standard_normal((3, L))
+    dv, dg, Sv, Sg = oracle.causal_conv_bwd_f64(dr, v, g)
+    for s in (0, 17, L - 1):
+        d2 = dr.copy()
+        d2[s] += 1.0
+        dv2, dg2, _, _ = oracle.causal_conv_bwd_f64(d2, v, g)
+        assert np.array_equal(dv2[s + 1:], dv[s + 1:]) and np.array_equal(dg2[s + 1:], dg[s + 1:])
+        assert dv2[s] != dv[s]
+    # the scales are the gradients of the absolute values
+    av, ag, _, _ = oracle.causal_conv_bwd_f64(np.abs(dr), np.abs(v), np.abs(g), with_scale=False)
+    np.testing.assert_allclose(Sv, av, rtol=1e-14)
+    np.testing.assert_allclose(Sg, ag, rtol=1e-14)
+    assert np.all(Sv >= np.abs(dv)) and np.all(Sg >= np.abs(dg))
+    # threads do not change bits; empty input is fine
+    a = oracle.causal_conv_bwd_f64(np.tile(dr, (5, 1)), np.tile(v, (5, 1)), np.tile(g, (5, 1)), nthreads=1)
+    b = oracle.causal_conv_bwd_f64(np.tile(dr, (5, 1)), np.tile(v, (5, 1)), np.tile(g, (5, 1)), nthreads=4)
+    assert all(np.array_equal(x, y) for x, y in zip(a, b))
+    e = oracle.causal_conv_bwd_f64(np.zeros((2, 0)), np.zeros((2, 0)), np.zeros((2, 0)))
+    assert e[0].shape == (2, 0)
