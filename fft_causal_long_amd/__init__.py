@@ -12,7 +12,9 @@ There is no CPU fallback: if the library is missing, importing this package fail
 Public names mirror the C ABI of ``include/specconv.h``:
 ``sc_causal_conv_f32``, ``sc_causal_conv_bf16``, ``sc_causal_conv_ntt_i32``, their
 ``_ws`` variants, ``sc_causal_conv_ex``, ``sc_workspace_bytes``, ``sc_ntt_range_ok``,
-``sc_status_string``, ``sc_version``; plus :func:`causal_conv`, which dispatches on dtype.
+``sc_status_string``, ``sc_version``, and the gradient calls ``sc_causal_conv_bwd_f32``,
+``sc_causal_conv_bwd_bf16``, ``sc_causal_conv_bwd_ntt_i32``, ``sc_causal_conv_bwd_ex``; plus
+:func:`causal_conv` and :func:`causal_conv_bwd`, which dispatch on dtype.
 """
 from __future__ import annotations
 
@@ -25,8 +27,10 @@ __all__ = [
     "SpecConvError", "lib", "causal_conv", "sc_causal_conv_f32", "sc_causal_conv_bf16",
     "sc_causal_conv_ntt_i32", "sc_causal_conv_f32_ws", "sc_causal_conv_bf16_ws",
     "sc_causal_conv_ntt_i32_ws", "sc_causal_conv_ex", "sc_workspace_bytes", "sc_ntt_range_ok",
-    "sc_status_string", "sc_version", "KIND_F32", "KIND_BF16", "KIND_NTT_I32", "PATH_AUTO",
-    "PATH_FUSED", "PATH_FOUR_STEP", "PATH_DIRECT", "LIB_PATH",
+    "sc_status_string", "sc_version", "causal_conv_bwd", "sc_causal_conv_bwd_f32",
+    "sc_causal_conv_bwd_bf16", "sc_causal_conv_bwd_ntt_i32", "sc_causal_conv_bwd_ex",
+    "KIND_F32", "KIND_BF16", "KIND_NTT_I32", "PATH_AUTO", "PATH_FUSED", "PATH_FOUR_STEP",
+    "PATH_DIRECT", "LIB_PATH",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libspecconv.so")
@@ -63,6 +67,13 @@ def _open():
     h.sc_causal_conv_ex.argtypes = [st, vp, vp, vp, i64, i64, i64,
                                     ctypes.POINTER(sc_options), vp, sz, vp]
     h.sc_causal_conv_ex.restype = st
+    for name in ("sc_causal_conv_bwd_f32", "sc_causal_conv_bwd_bf16", "sc_causal_conv_bwd_ntt_i32"):
+        f = getattr(h, name)
+        f.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, vp]
+        f.restype = st
+    h.sc_causal_conv_bwd_ex.argtypes = [st, vp, vp, vp, vp, vp, i64, i64, i64,
+                                        ctypes.POINTER(sc_options), vp, sz, vp]
+    h.sc_causal_conv_bwd_ex.restype = st
     h.sc_workspace_bytes.argtypes = [st, i64, i64, i64]
     h.sc_workspace_bytes.restype = sz
     h.sc_ntt_range_ok.argtypes = [i64, i64, i64]
@@ -110,6 +121,22 @@ def sc_causal_conv_ntt_i32_ws(v, g, r, B, C, L, ws, ws_bytes, stream):
 
 def sc_causal_conv_ex(kind, v, g, r, B, C, L, opt, ws, ws_bytes, stream):
     return _lib.sc_causal_conv_ex(kind, v, g, r, B, C, L, opt, ws, ws_bytes, stream)
+
+
+def sc_causal_conv_bwd_f32(dr, v, g, dv, dg, B, C, L, stream):
+    return _lib.sc_causal_conv_bwd_f32(dr, v, g, dv, dg, B, C, L, stream)
+
+
+def sc_causal_conv_bwd_bf16(dr, v, g, dv, dg, B, C, L, stream):
+    return _lib.sc_causal_conv_bwd_bf16(dr, v, g, dv, dg, B, C, L, stream)
+
+
+def sc_causal_conv_bwd_ntt_i32(dr, v, g, dv, dg, B, C, L, stream):
+    return _lib.sc_causal_conv_bwd_ntt_i32(dr, v, g, dv, dg, B, C, L, stream)
+
+
+def sc_causal_conv_bwd_ex(kind, dr, v, g, dv, dg, B, C, L, opt, ws, ws_bytes, stream):
+    return _lib.sc_causal_conv_bwd_ex(kind, dr, v, g, dv, dg, B, C, L, opt, ws, ws_bytes, stream)
 
 
 def sc_workspace_bytes(kind, B, C, L) -> int:
@@ -194,3 +221,54 @@ def causal_conv(v: torch.Tensor, g: torch.Tensor, out: torch.Tensor | None = Non
     if st != SC_OK:
         raise SpecConvError(st, "causal_conv")
     return out
+
+
+def _out_like(x: torch.Tensor, out: torch.Tensor | None, name: str) -> torch.Tensor:
+    if out is None:
+        return torch.empty_like(x)
+    if out.shape != x.shape or out.dtype != x.dtype or out.device != x.device \
+            or not out.is_contiguous():
+        raise ValueError("%s must match the inputs in shape, dtype, device and be contiguous"
+                         % name)
+    return out
+
+
+def causal_conv_bwd(dr: torch.Tensor, v: torch.Tensor, g: torch.Tensor,
+                    dv: torch.Tensor | None = None, dg: torch.Tensor | None = None, *,
+                    path: int | None = None, head: int | None = None,
+                    workspace: torch.Tensor | None = None):
+    """Gradients of sum(dr * causal_conv(v, g)) along the last axis: returns (dv, dg) with
+    dv[..., j] = sum_{t>=j} dr[..., t] g[..., t-j] and dg[..., k] = sum_{t>=k} dr[..., t]
+    v[..., t-k].  Same dtype rules, devices, stream and options as :func:`causal_conv`."""
+    if not (dr.shape == v.shape == g.shape) or not (dr.dtype == v.dtype == g.dtype):
+        raise ValueError("dr, v and g must have the same shape and dtype")
+    if v.dtype not in _KIND_OF_DTYPE:
+        raise TypeError("unsupported dtype %s" % v.dtype)
+    if not (dr.is_cuda and v.is_cuda and g.is_cuda) or not (dr.device == v.device == g.device):
+        raise ValueError("dr, v and g must be on the same GPU")
+    if not (dr.is_contiguous() and v.is_contiguous() and g.is_contiguous()):
+        raise ValueError("dr, v and g must be contiguous")
+    dv = _out_like(v, dv, "dv")
+    dg = _out_like(v, dg, "dg")
+    B, C, L = _shape3(v)
+    kind = _KIND_OF_DTYPE[v.dtype]
+    ws_ptr, ws_bytes = None, 0
+    if workspace is not None:
+        if not workspace.is_cuda or workspace.device != v.device or not workspace.is_contiguous():
+            raise ValueError("workspace must be a contiguous tensor on v's device")
+        ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
+    ptrs = (dr.data_ptr(), v.data_ptr(), g.data_ptr(), dv.data_ptr(), dg.data_ptr())
+    with torch.cuda.device(v.device):
+        stream = torch.cuda.current_stream(v.device).cuda_stream
+        if path is None and head is None and ws_ptr is None:
+            fn = (_lib.sc_causal_conv_bwd_f32, _lib.sc_causal_conv_bwd_bf16,
+                  _lib.sc_causal_conv_bwd_ntt_i32)[kind]
+            st = fn(*ptrs, B, C, L, stream)
+        else:
+            opt = sc_options(PATH_AUTO if path is None else int(path),
+                             -1 if head is None else int(head))
+            st = _lib.sc_causal_conv_bwd_ex(kind, *ptrs, B, C, L, ctypes.byref(opt), ws_ptr,
+                                            ws_bytes, stream)
+    if st != SC_OK:
+        raise SpecConvError(st, "causal_conv_bwd")
+    return dv, dg

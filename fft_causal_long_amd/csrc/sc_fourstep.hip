@@ -34,7 +34,9 @@ namespace sc {
 
 // ---------------------------------------------------------------- kernel A: columns, forward
 
-template <int M1, class IO>
+// REV (the gradient kernels): v is read reversed here and the output is written reversed by
+// kernel C and the head kernel: rev(causal(rev(dr), b))_j = sum_{t>=j} dr_t b_{t-j}.
+template <int M1, class IO, bool REV>
 __global__ __launch_bounds__(512) void fs_columns_fwd(const typename IO::T* __restrict__ v,
                                                       const typename IO::T* __restrict__ g,
                                                       float2* __restrict__ T, int64_t ch_begin,
@@ -57,7 +59,8 @@ __global__ __launch_bounds__(512) void fs_columns_fwd(const typename IO::T* __re
 #pragma unroll
     for (int q = 0; q < 16; ++q) {
         const int n = n1 + M2 * (tau + TQ * q);
-        float2 z = make_float2(IO::load(vs, n), IO::load(gs, n));
+        const int nv = REV ? (n < L ? L - 1 - n : IO::OOB) : n;
+        float2 z = make_float2(IO::load(vs, nv), IO::load(gs, n));
         if (beta) z = cmul(z, tw.tn[n]);                       // W_N^n
         x[q] = z;
     }
@@ -183,7 +186,7 @@ __global__ __launch_bounds__(512) void fs_rows(const float2* __restrict__ T, flo
 
 // ---------------------------------------------------------------- kernel C: columns, inverse
 
-template <int M1, class IO>
+template <int M1, class IO, bool REV>
 __global__ __launch_bounds__(512) void fs_columns_inv(const float2* __restrict__ S,
                                                       typename IO::T* __restrict__ r,
                                                       int64_t ch_begin, int L, int M2, int head,
@@ -228,15 +231,17 @@ __global__ __launch_bounds__(512) void fs_columns_inv(const float2* __restrict__
             if (tt < head || tt >= L) continue;
             const float2 o = obuf[reg_off<TQ>(tau, q)];
             const float a = (x[q].x + o.x) * scale, b = (x[q].y + o.y) * scale;
+            // outputs tt, tt+1 (at L-1-tt, L-2-tt when REV; pairs need L even)
             if (tt + 1 < L) {
                 if (pair_store) {
-                    IO::store2(rs, tt, a, b);
+                    if (REV) IO::store2(rs, L - 2 - tt, b, a);
+                    else IO::store2(rs, tt, a, b);
                 } else {
-                    IO::store(rs, tt, a);
-                    IO::store(rs, tt + 1, b);
+                    IO::store(rs, REV ? L - 1 - tt : tt, a);
+                    IO::store(rs, REV ? L - 2 - tt : tt + 1, b);
                 }
             } else {
-                IO::store(rs, tt, a);
+                IO::store(rs, REV ? L - 1 - tt : tt, a);
             }
         }
     }
@@ -244,7 +249,7 @@ __global__ __launch_bounds__(512) void fs_columns_inv(const float2* __restrict__
 
 // ---------------------------------------------------------------- direct head
 
-template <class IO>
+template <class IO, bool REV>
 __global__ void head_kernel(const typename IO::T* __restrict__ v, const typename IO::T* __restrict__ g,
                             typename IO::T* __restrict__ r, int64_t nch, int L, int head)
 {
@@ -255,13 +260,14 @@ __global__ void head_kernel(const typename IO::T* __restrict__ v, const typename
     const int64_t base = c * (int64_t)L;
     float acc = 0.f;
     for (int j = 0; j <= t; ++j)
-        acc = __builtin_fmaf(IO::load(v, base + j), IO::load(g, base + t - j), acc);
-    IO::store(r, base + t, acc);
+        acc = __builtin_fmaf(IO::load(v, base + (REV ? L - 1 - j : j)), IO::load(g, base + t - j),
+                             acc);
+    IO::store(r, base + (REV ? L - 1 - t : t), acc);
 }
 
 // ---------------------------------------------------------------- launch
 
-template <class IO, int M1>
+template <class IO, bool REV, int M1>
 static hipError_t launch_cols(bool fwd, const void* v, const void* g, void* r, float2* T,
                               const float2* S, int64_t c0, int nc, int L, int M2, int head,
                               bool pair, const float2* bank, const FsTw& tw, hipStream_t s)
@@ -269,29 +275,29 @@ static hipError_t launch_cols(bool fwd, const void* v, const void* g, void* r, f
     constexpr int NCOL = 256 / (M1 / 16);
     if (fwd) {
         const int64_t blocks = (int64_t)nc * (M2 / NCOL);
-        hipLaunchKernelGGL((fs_columns_fwd<M1, IO>), dim3((unsigned)blocks), dim3(512), 0, s,
+        hipLaunchKernelGGL((fs_columns_fwd<M1, IO, REV>), dim3((unsigned)blocks), dim3(512), 0, s,
                            (const typename IO::T*)v, (const typename IO::T*)g, T, c0, L, M2, bank,
                            tw);
     } else {
         const int H = M2 / 2;
         const int64_t blocks = (int64_t)nc * ((H + NCOL - 1) / NCOL);
-        hipLaunchKernelGGL((fs_columns_inv<M1, IO>), dim3((unsigned)blocks), dim3(512), 0, s, S,
+        hipLaunchKernelGGL((fs_columns_inv<M1, IO, REV>), dim3((unsigned)blocks), dim3(512), 0, s, S,
                            (typename IO::T*)r, c0, L, M2, head, pair ? 1 : 0, bank, tw);
     }
     return hipGetLastError();
 }
 
-template <class IO>
+template <class IO, bool REV>
 static hipError_t dispatch_cols(bool fwd, int M1, const void* v, const void* g, void* r, float2* T,
                                 const float2* S, int64_t c0, int nc, int L, int M2, int head,
                                 bool pair, const float2* bank, const FsTw& tw, hipStream_t s)
 {
     switch (M1) {
-    case 64: return launch_cols<IO, 64>(fwd, v, g, r, T, S, c0, nc, L, M2, head, pair, bank, tw, s);
-    case 128: return launch_cols<IO, 128>(fwd, v, g, r, T, S, c0, nc, L, M2, head, pair, bank, tw, s);
-    case 256: return launch_cols<IO, 256>(fwd, v, g, r, T, S, c0, nc, L, M2, head, pair, bank, tw, s);
-    case 512: return launch_cols<IO, 512>(fwd, v, g, r, T, S, c0, nc, L, M2, head, pair, bank, tw, s);
-    case 1024: return launch_cols<IO, 1024>(fwd, v, g, r, T, S, c0, nc, L, M2, head, pair, bank, tw, s);
+    case 64: return launch_cols<IO, REV, 64>(fwd, v, g, r, T, S, c0, nc, L, M2, head, pair, bank, tw, s);
+    case 128: return launch_cols<IO, REV, 128>(fwd, v, g, r, T, S, c0, nc, L, M2, head, pair, bank, tw, s);
+    case 256: return launch_cols<IO, REV, 256>(fwd, v, g, r, T, S, c0, nc, L, M2, head, pair, bank, tw, s);
+    case 512: return launch_cols<IO, REV, 512>(fwd, v, g, r, T, S, c0, nc, L, M2, head, pair, bank, tw, s);
+    case 1024: return launch_cols<IO, REV, 1024>(fwd, v, g, r, T, S, c0, nc, L, M2, head, pair, bank, tw, s);
     default: return hipErrorInvalidValue;
     }
 }
@@ -336,9 +342,10 @@ size_t fourstep_bytes_per_channel(int M)
     return (size_t)3 * (size_t)M * sizeof(float2);
 }
 
-hipError_t launch_fourstep(Store st, const void* v, const void* g, void* r, int64_t nch, int L,
-                           int M, int head, bool pair_store, const float2* bank, const FsTw& tw,
-                           void* ws, int64_t chunk, hipStream_t stream)
+template <bool REV>
+static hipError_t launch_fourstep_rev(Store st, const void* v, const void* g, void* r, int64_t nch,
+                                      int L, int M, int head, bool pair_store, const float2* bank,
+                                      const FsTw& tw, void* ws, int64_t chunk, hipStream_t stream)
 {
     int M1, M2;
     fourstep_split(M, &M1, &M2);
@@ -348,20 +355,20 @@ hipError_t launch_fourstep(Store st, const void* v, const void* g, void* r, int6
         const int nc = (int)((nch - c0) < chunk ? (nch - c0) : chunk);
         hipError_t e;
         if (st == Store::F32)
-            e = dispatch_cols<f32_io>(true, M1, v, g, r, T, S, c0, nc, L, M2, head, pair_store,
-                                      bank, tw, stream);
+            e = dispatch_cols<f32_io, REV>(true, M1, v, g, r, T, S, c0, nc, L, M2, head, pair_store,
+                                           bank, tw, stream);
         else
-            e = dispatch_cols<bf16_io>(true, M1, v, g, r, T, S, c0, nc, L, M2, head, pair_store,
-                                       bank, tw, stream);
+            e = dispatch_cols<bf16_io, REV>(true, M1, v, g, r, T, S, c0, nc, L, M2, head,
+                                            pair_store, bank, tw, stream);
         if (e != hipSuccess) return e;
         e = dispatch_rows(M2, T, S, nc, M1, bank, tw, stream);
         if (e != hipSuccess) return e;
         if (st == Store::F32)
-            e = dispatch_cols<f32_io>(false, M1, v, g, r, T, S, c0, nc, L, M2, head, pair_store,
-                                      bank, tw, stream);
+            e = dispatch_cols<f32_io, REV>(false, M1, v, g, r, T, S, c0, nc, L, M2, head,
+                                           pair_store, bank, tw, stream);
         else
-            e = dispatch_cols<bf16_io>(false, M1, v, g, r, T, S, c0, nc, L, M2, head, pair_store,
-                                       bank, tw, stream);
+            e = dispatch_cols<bf16_io, REV>(false, M1, v, g, r, T, S, c0, nc, L, M2, head,
+                                            pair_store, bank, tw, stream);
         if (e != hipSuccess) return e;
     }
     if (head > 0) {
@@ -369,14 +376,25 @@ hipError_t launch_fourstep(Store st, const void* v, const void* g, void* r, int6
         const int threads = 256;
         const int64_t blocks = (total + threads - 1) / threads;
         if (st == Store::F32)
-            hipLaunchKernelGGL(head_kernel<f32_io>, dim3((unsigned)blocks), dim3(threads), 0, stream,
-                               (const float*)v, (const float*)g, (float*)r, nch, L, head);
+            hipLaunchKernelGGL((head_kernel<f32_io, REV>), dim3((unsigned)blocks), dim3(threads), 0,
+                               stream, (const float*)v, (const float*)g, (float*)r, nch, L, head);
         else
-            hipLaunchKernelGGL(head_kernel<bf16_io>, dim3((unsigned)blocks), dim3(threads), 0, stream,
-                               (const uint16_t*)v, (const uint16_t*)g, (uint16_t*)r, nch, L, head);
+            hipLaunchKernelGGL((head_kernel<bf16_io, REV>), dim3((unsigned)blocks), dim3(threads), 0,
+                               stream, (const uint16_t*)v, (const uint16_t*)g, (uint16_t*)r, nch, L,
+                               head);
         return hipGetLastError();
     }
     return hipSuccess;
+}
+
+hipError_t launch_fourstep(Store st, const void* v, const void* g, void* r, int64_t nch, int L,
+                           int M, int head, bool pair_store, bool rev, const float2* bank,
+                           const FsTw& tw, void* ws, int64_t chunk, hipStream_t stream)
+{
+    return rev ? launch_fourstep_rev<true>(st, v, g, r, nch, L, M, head, pair_store, bank, tw, ws,
+                                           chunk, stream)
+               : launch_fourstep_rev<false>(st, v, g, r, nch, L, M, head, pair_store, bank, tw, ws,
+                                            chunk, stream);
 }
 
 }  // namespace sc

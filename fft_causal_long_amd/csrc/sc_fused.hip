@@ -74,7 +74,10 @@ __device__ __forceinline__ void unpack_pair(int k, const float2* __restrict__ u0
     ymk = make_float2(sm.x + t.y, t.x - sm.y);
 }
 
-template <int M, class IO>
+// REV (the gradient kernels): the first input is read reversed and the output is written
+// reversed, which turns the causal convolution into the correlation of the backward pass:
+// rev(causal(rev(dr), b))_j = sum_{t>=j} dr_t b_{t-j}.
+template <int M, class IO, bool REV>
 __global__ __launch_bounds__(FUSED_THREADS) void fused_conv_kernel(
     const typename IO::T* __restrict__ v, const typename IO::T* __restrict__ g,
     typename IO::T* __restrict__ r, int64_t nch, int L, int head, int pair_store,
@@ -106,7 +109,8 @@ __global__ __launch_bounds__(FUSED_THREADS) void fused_conv_kernel(
 #pragma unroll
             for (int q = 0; q < 16; ++q) {
                 const int n = tau + TB * q;
-                x[q] = make_float2(IO::load(vs, cbase + n), IO::load(gs, cbase + n));
+                x[q] = make_float2(IO::load(vs, cbase + (REV ? L - 1 - n : n)),
+                                   IO::load(gs, cbase + n));
             }
         } else {
             // elements past L are read at IO::OOB, beyond the descriptor's range, so they read
@@ -115,7 +119,8 @@ __global__ __launch_bounds__(FUSED_THREADS) void fused_conv_kernel(
             for (int q = 0; q < 16; ++q) {
                 const int n = tau + TB * q;
                 const int e = n < L ? cbase + n : IO::OOB;
-                x[q] = make_float2(IO::load(vs, e), IO::load(gs, e));
+                const int ev = n < L ? cbase + (REV ? L - 1 - n : n) : IO::OOB;
+                x[q] = make_float2(IO::load(vs, ev), IO::load(gs, e));
             }
         }
         if (!beta) {
@@ -175,16 +180,22 @@ __global__ __launch_bounds__(FUSED_THREADS) void fused_conv_kernel(
     fft_passes<M, true>(x, ybuf, itau, bank, iact);
 
     // 5. store: x[q] = 8 M y_m with m = itau + TB q; r_{2m} = Re y_m, r_{2m+1} = Im y_m
+    //    (at L-1-2m and L-2-2m when REV; pairs need L even, which the host ensures)
     const Span rs = make_span(r, ch0 * L, (int64_t)nvalid * L);
+    // output t of local channel c at flat index c L + t
+    auto put = [&](int c, int t, float a) { IO::store(rs, c * L + (REV ? L - 1 - t : t), a); };
+    auto put2 = [&](int c, int t, float a, float b) {
+        if (REV) IO::store2(rs, c * L + L - 2 - t, b, a);
+        else IO::store2(rs, c * L + t, a, b);
+    };
     if (iact) {
         const float scale = 1.0f / (8.0f * (float)M);
-        const int cbase = icl * L;
         if (L == M && pair_store) {
 #pragma unroll
             for (int q = 0; q < 8; ++q) {
                 const int t = 2 * (itau + TB * q);
                 if (2 * TB * q >= HEAD_MAX || t >= head)
-                    IO::store2(rs, cbase + t, x[q].x * scale, x[q].y * scale);
+                    put2(icl, t, x[q].x * scale, x[q].y * scale);
             }
         } else {
 #pragma unroll
@@ -194,13 +205,13 @@ __global__ __launch_bounds__(FUSED_THREADS) void fused_conv_kernel(
                     const float a = x[q].x * scale, b = x[q].y * scale;
                     if (t + 1 < L) {
                         if (pair_store) {
-                            IO::store2(rs, cbase + t, a, b);
+                            put2(icl, t, a, b);
                         } else {
-                            IO::store(rs, cbase + t, a);
-                            IO::store(rs, cbase + t + 1, b);
+                            put(icl, t, a);
+                            put(icl, t + 1, b);
                         }
                     } else {
-                        IO::store(rs, cbase + t, a);
+                        put(icl, t, a);
                     }
                 }
             }
@@ -215,13 +226,13 @@ __global__ __launch_bounds__(FUSED_THREADS) void fused_conv_kernel(
                 const float* hg = hv + HEAD_MAX;
                 float acc = 0.f;
                 for (int j = 0; j <= t; ++j) acc = __builtin_fmaf(hv[j], hg[t - j], acc);
-                IO::store(rs, c2 * L + t, acc);
+                put(c2, t, acc);
             }
         }
     }
 }
 
-template <class IO>
+template <class IO, bool REV>
 __global__ void direct_conv_kernel(const typename IO::T* __restrict__ v,
                                    const typename IO::T* __restrict__ g,
                                    typename IO::T* __restrict__ r, int64_t nch, int L)
@@ -233,59 +244,70 @@ __global__ void direct_conv_kernel(const typename IO::T* __restrict__ v,
     const int64_t base = c * (int64_t)L;
     float acc = 0.f;
     for (int j = 0; j <= t; ++j)
-        acc = __builtin_fmaf(IO::load(v, base + j), IO::load(g, base + t - j), acc);
-    IO::store(r, base + t, acc);
+        acc = __builtin_fmaf(IO::load(v, base + (REV ? L - 1 - j : j)), IO::load(g, base + t - j),
+                             acc);
+    IO::store(r, base + (REV ? L - 1 - t : t), acc);
 }
 
-template <int M, class IO>
+template <int M, class IO, bool REV>
 static hipError_t launch_fused_m(const void* v, const void* g, void* r, int64_t nch, int L,
                                  int head, bool pair, const float2* tw, hipStream_t stream)
 {
     constexpr int CPW = (FUSED_THREADS / (M / 16)) / 2;
     const int64_t blocks = (nch + CPW - 1) / CPW;
-    hipLaunchKernelGGL((fused_conv_kernel<M, IO>), dim3((unsigned)blocks), dim3(FUSED_THREADS), 0,
+    hipLaunchKernelGGL((fused_conv_kernel<M, IO, REV>), dim3((unsigned)blocks), dim3(FUSED_THREADS), 0,
                        stream, (const typename IO::T*)v, (const typename IO::T*)g,
                        (typename IO::T*)r, nch, L, head, pair ? 1 : 0, tw);
     return hipGetLastError();
 }
 
-template <class IO>
+template <class IO, bool REV>
 static hipError_t launch_fused_io(const void* v, const void* g, void* r, int64_t nch, int L, int M,
                                   int head, bool pair, const float2* tw, hipStream_t s)
 {
     switch (M) {
-    case 64: return launch_fused_m<64, IO>(v, g, r, nch, L, head, pair, tw, s);
-    case 128: return launch_fused_m<128, IO>(v, g, r, nch, L, head, pair, tw, s);
-    case 256: return launch_fused_m<256, IO>(v, g, r, nch, L, head, pair, tw, s);
-    case 512: return launch_fused_m<512, IO>(v, g, r, nch, L, head, pair, tw, s);
-    case 1024: return launch_fused_m<1024, IO>(v, g, r, nch, L, head, pair, tw, s);
-    case 2048: return launch_fused_m<2048, IO>(v, g, r, nch, L, head, pair, tw, s);
-    case 4096: return launch_fused_m<4096, IO>(v, g, r, nch, L, head, pair, tw, s);
+    case 64: return launch_fused_m<64, IO, REV>(v, g, r, nch, L, head, pair, tw, s);
+    case 128: return launch_fused_m<128, IO, REV>(v, g, r, nch, L, head, pair, tw, s);
+    case 256: return launch_fused_m<256, IO, REV>(v, g, r, nch, L, head, pair, tw, s);
+    case 512: return launch_fused_m<512, IO, REV>(v, g, r, nch, L, head, pair, tw, s);
+    case 1024: return launch_fused_m<1024, IO, REV>(v, g, r, nch, L, head, pair, tw, s);
+    case 2048: return launch_fused_m<2048, IO, REV>(v, g, r, nch, L, head, pair, tw, s);
+    case 4096: return launch_fused_m<4096, IO, REV>(v, g, r, nch, L, head, pair, tw, s);
     default: return hipErrorInvalidValue;
     }
 }
 
 hipError_t launch_fused(Store st, const void* v, const void* g, void* r, int64_t nch, int L, int M,
-                        int head, bool pair_store, const float2* tw, hipStream_t stream)
+                        int head, bool pair_store, bool rev, const float2* tw, hipStream_t stream)
 {
     if (st == Store::F32)
-        return launch_fused_io<f32_io>(v, g, r, nch, L, M, head, pair_store, tw, stream);
-    return launch_fused_io<bf16_io>(v, g, r, nch, L, M, head, pair_store, tw, stream);
+        return rev ? launch_fused_io<f32_io, true>(v, g, r, nch, L, M, head, pair_store, tw, stream)
+                   : launch_fused_io<f32_io, false>(v, g, r, nch, L, M, head, pair_store, tw, stream);
+    return rev ? launch_fused_io<bf16_io, true>(v, g, r, nch, L, M, head, pair_store, tw, stream)
+               : launch_fused_io<bf16_io, false>(v, g, r, nch, L, M, head, pair_store, tw, stream);
 }
 
-hipError_t launch_direct(Store st, const void* v, const void* g, void* r, int64_t nch, int L,
-                         hipStream_t stream)
+template <bool REV>
+static hipError_t launch_direct_rev(Store st, const void* v, const void* g, void* r, int64_t nch,
+                                    int L, hipStream_t stream)
 {
     const int64_t total = nch * (int64_t)L;
     const int threads = 256;
     const int64_t blocks = (total + threads - 1) / threads;
     if (st == Store::F32)
-        hipLaunchKernelGGL(direct_conv_kernel<f32_io>, dim3((unsigned)blocks), dim3(threads), 0,
-                           stream, (const float*)v, (const float*)g, (float*)r, nch, L);
+        hipLaunchKernelGGL((direct_conv_kernel<f32_io, REV>), dim3((unsigned)blocks), dim3(threads),
+                           0, stream, (const float*)v, (const float*)g, (float*)r, nch, L);
     else
-        hipLaunchKernelGGL(direct_conv_kernel<bf16_io>, dim3((unsigned)blocks), dim3(threads), 0,
-                           stream, (const uint16_t*)v, (const uint16_t*)g, (uint16_t*)r, nch, L);
+        hipLaunchKernelGGL((direct_conv_kernel<bf16_io, REV>), dim3((unsigned)blocks), dim3(threads),
+                           0, stream, (const uint16_t*)v, (const uint16_t*)g, (uint16_t*)r, nch, L);
     return hipGetLastError();
+}
+
+hipError_t launch_direct(Store st, const void* v, const void* g, void* r, int64_t nch, int L,
+                         bool rev, hipStream_t stream)
+{
+    return rev ? launch_direct_rev<true>(st, v, g, r, nch, L, stream)
+               : launch_direct_rev<false>(st, v, g, r, nch, L, stream);
 }
 
 }  // namespace sc

@@ -264,12 +264,20 @@ void fourstep_plan(int64_t nch, int64_t L, int64_t* chunk, size_t* bytes)
     *bytes = (size_t)(c * per);
 }
 
-sc_status run(sc_kind kind, const void* v, const void* g, void* r, int64_t B, int64_t C,
-              int64_t L, const sc_options* opt, void* ws, size_t ws_bytes, hipStream_t stream)
+// One convolution of a call: o = causal(a, b) per channel, or with rev the gradient form
+// o = rev(causal(rev(a), b)).
+struct Job {
+    const void* a;
+    const void* b;
+    void* o;
+};
+
+// Runs the jobs of one call (arguments already checked) on one path with one scratch area,
+// which the jobs use one after the other in stream order.
+sc_status run_jobs(sc_kind kind, const Job* jobs, int njobs, bool rev, int64_t n, int64_t B,
+                   int64_t C, int64_t L, const sc_options* opt, void* ws, size_t ws_bytes,
+                   hipStream_t stream)
 {
-    int64_t n = 0;
-    sc_status st = check_args(kind, v, g, r, B, C, L, &n);
-    if (st != SC_OK) return st;
     int32_t req = SC_PATH_AUTO, head = kDefaultHead;
     if (opt) {
         for (int i = 0; i < 6; ++i)
@@ -281,7 +289,7 @@ sc_status run(sc_kind kind, const void* v, const void* g, void* r, int64_t B, in
         }
     }
     sc_path path;
-    st = resolve_path(kind, L, req, &path);
+    sc_status st = resolve_path(kind, L, req, &path);
     if (st != SC_OK) return st;
     if (n == 0) return SC_OK;
     const int64_t nch = B * C;
@@ -293,44 +301,84 @@ sc_status run(sc_kind kind, const void* v, const void* g, void* r, int64_t B, in
     hipError_t e = hipSuccess;
     if (kind == SC_KIND_NTT_I32) {
         const int M = (int)std::max<int64_t>(64, next_pow2(L));
-        e = sc::launch_ntt((const int32_t*)v, (const int32_t*)g, (int32_t*)r, nch, (int)L, M,
-                           d->ntt, stream);
+        for (int k = 0; k < njobs && e == hipSuccess; ++k)
+            e = sc::launch_ntt((const int32_t*)jobs[k].a, (const int32_t*)jobs[k].b,
+                               (int32_t*)jobs[k].o, nch, (int)L, M, rev, d->ntt, stream);
+        return e == hipSuccess ? SC_OK : SC_ERR_HIP;
+    }
+    const sc::Store s = kind == SC_KIND_F32 ? sc::Store::F32 : sc::Store::BF16;
+    bool pair = L % 2 == 0;
+    for (int k = 0; k < njobs; ++k)
+        pair = pair && (uintptr_t)jobs[k].o % (2 * elt_size(kind)) == 0;
+    if (path == SC_PATH_DIRECT) {
+        for (int k = 0; k < njobs && e == hipSuccess; ++k)
+            e = sc::launch_direct(s, jobs[k].a, jobs[k].b, jobs[k].o, nch, (int)L, rev, stream);
+    } else if (path == SC_PATH_FUSED) {
+        const int M = (int)std::max<int64_t>(64, next_pow2(L));
+        for (int k = 0; k < njobs && e == hipSuccess; ++k)
+            e = sc::launch_fused(s, jobs[k].a, jobs[k].b, jobs[k].o, nch, (int)L, M, head, pair,
+                                 rev, d->fused_tw, stream);
     } else {
-        const sc::Store s = kind == SC_KIND_F32 ? sc::Store::F32 : sc::Store::BF16;
-        const bool pair = (L % 2 == 0) && ((uintptr_t)r % (2 * elt_size(kind)) == 0);
-        if (path == SC_PATH_DIRECT) {
-            e = sc::launch_direct(s, v, g, r, nch, (int)L, stream);
-        } else if (path == SC_PATH_FUSED) {
-            const int M = (int)std::max<int64_t>(64, next_pow2(L));
-            e = sc::launch_fused(s, v, g, r, nch, (int)L, M, head, pair, d->fused_tw, stream);
-        } else {
-            const int M = (int)next_pow2(L);
-            sc::FsTw tw;
-            {
-                std::lock_guard<std::mutex> lk(g_mu);
-                st = fourstep_tables(*d, M, &tw);
-            }
-            if (st != SC_OK) return st;
-            int64_t chunk;
-            size_t need;
-            fourstep_plan(nch, L, &chunk, &need);
-            void* scratch = ws;
-            bool own = false;
-            if (ws) {
-                if (ws_bytes < need) return SC_ERR_WORKSPACE;
-                if ((uintptr_t)ws % 256) return SC_ERR_INVALID_ARGUMENT;
-            } else {
-                if (ws_bytes) return SC_ERR_INVALID_ARGUMENT;
-                if (hipMallocAsync(&scratch, need, stream) != hipSuccess) return SC_ERR_HIP;
-                own = true;
-            }
-            e = sc::launch_fourstep(s, v, g, r, nch, (int)L, M, head, pair, d->fused_tw, tw,
-                                    scratch, chunk, stream);
-            if (own && hipFreeAsync(scratch, stream) != hipSuccess && e == hipSuccess)
-                e = hipErrorUnknown;
+        const int M = (int)next_pow2(L);
+        sc::FsTw tw;
+        {
+            std::lock_guard<std::mutex> lk(g_mu);
+            st = fourstep_tables(*d, M, &tw);
         }
+        if (st != SC_OK) return st;
+        int64_t chunk;
+        size_t need;
+        fourstep_plan(nch, L, &chunk, &need);
+        void* scratch = ws;
+        bool own = false;
+        if (ws) {
+            if (ws_bytes < need) return SC_ERR_WORKSPACE;
+            if ((uintptr_t)ws % 256) return SC_ERR_INVALID_ARGUMENT;
+        } else {
+            if (ws_bytes) return SC_ERR_INVALID_ARGUMENT;
+            if (hipMallocAsync(&scratch, need, stream) != hipSuccess) return SC_ERR_HIP;
+            own = true;
+        }
+        for (int k = 0; k < njobs && e == hipSuccess; ++k)
+            e = sc::launch_fourstep(s, jobs[k].a, jobs[k].b, jobs[k].o, nch, (int)L, M, head, pair,
+                                    rev, d->fused_tw, tw, scratch, chunk, stream);
+        if (own && hipFreeAsync(scratch, stream) != hipSuccess && e == hipSuccess)
+            e = hipErrorUnknown;
     }
     return e == hipSuccess ? SC_OK : SC_ERR_HIP;
+}
+
+sc_status run(sc_kind kind, const void* v, const void* g, void* r, int64_t B, int64_t C,
+              int64_t L, const sc_options* opt, void* ws, size_t ws_bytes, hipStream_t stream)
+{
+    int64_t n = 0;
+    const sc_status st = check_args(kind, v, g, r, B, C, L, &n);
+    if (st != SC_OK) return st;
+    const Job job{v, g, r};
+    return run_jobs(kind, &job, 1, false, n, B, C, L, opt, ws, ws_bytes, stream);
+}
+
+// Gradients: dv = rev(causal(rev(dr), g)), dg = rev(causal(rev(dr), v)).
+sc_status run_bwd(sc_kind kind, const void* dr, const void* v, const void* g, void* dv, void* dg,
+                  int64_t B, int64_t C, int64_t L, const sc_options* opt, void* ws,
+                  size_t ws_bytes, hipStream_t stream)
+{
+    int64_t n = 0;
+    sc_status st = check_shape(kind, B, C, L, &n);
+    if (st != SC_OK) return st;
+    if (n > 0) {
+        if (!dr || !v || !g || !dv || !dg) return SC_ERR_INVALID_ARGUMENT;
+        const size_t es = elt_size(kind);
+        if (((uintptr_t)dr | (uintptr_t)v | (uintptr_t)g | (uintptr_t)dv | (uintptr_t)dg) % es)
+            return SC_ERR_INVALID_ARGUMENT;
+        const uint64_t bytes = (uint64_t)n * es;
+        for (const void* out : {(const void*)dv, (const void*)dg})
+            for (const void* in : {dr, v, g})
+                if (overlaps(out, in, bytes)) return SC_ERR_INVALID_ARGUMENT;
+        if (overlaps(dv, dg, bytes)) return SC_ERR_INVALID_ARGUMENT;
+    }
+    const Job jobs[2] = {{dr, g, dv}, {dr, v, dg}};
+    return run_jobs(kind, jobs, 2, true, n, B, C, L, opt, ws, ws_bytes, stream);
 }
 
 template <class F>
@@ -411,6 +459,41 @@ sc_status sc_causal_conv_ex(sc_kind kind, const void* v, const void* g, void* r,
     return guarded([&] { return run(kind, v, g, r, B, C, L, opt, ws, ws_bytes, stream); });
 }
 
+sc_status sc_causal_conv_bwd_f32(const float* dr, const float* v, const float* g, float* dv,
+                                 float* dg, int64_t B, int64_t C, int64_t L, hipStream_t stream)
+{
+    return guarded([&] {
+        return run_bwd(SC_KIND_F32, dr, v, g, dv, dg, B, C, L, nullptr, nullptr, 0, stream);
+    });
+}
+
+sc_status sc_causal_conv_bwd_bf16(const uint16_t* dr, const uint16_t* v, const uint16_t* g,
+                                  uint16_t* dv, uint16_t* dg, int64_t B, int64_t C, int64_t L,
+                                  hipStream_t stream)
+{
+    return guarded([&] {
+        return run_bwd(SC_KIND_BF16, dr, v, g, dv, dg, B, C, L, nullptr, nullptr, 0, stream);
+    });
+}
+
+sc_status sc_causal_conv_bwd_ntt_i32(const int32_t* dr, const int32_t* v, const int32_t* g,
+                                     int32_t* dv, int32_t* dg, int64_t B, int64_t C, int64_t L,
+                                     hipStream_t stream)
+{
+    return guarded([&] {
+        return run_bwd(SC_KIND_NTT_I32, dr, v, g, dv, dg, B, C, L, nullptr, nullptr, 0, stream);
+    });
+}
+
+sc_status sc_causal_conv_bwd_ex(sc_kind kind, const void* dr, const void* v, const void* g,
+                                void* dv, void* dg, int64_t B, int64_t C, int64_t L,
+                                const sc_options* opt, void* ws, size_t ws_bytes,
+                                hipStream_t stream)
+{
+    return guarded(
+        [&] { return run_bwd(kind, dr, v, g, dv, dg, B, C, L, opt, ws, ws_bytes, stream); });
+}
+
 int sc_ntt_range_ok(int64_t max_abs_v, int64_t max_abs_g, int64_t L)
 {
     if (max_abs_v < 0 || max_abs_g < 0 || L < 0) return 0;
@@ -430,6 +513,6 @@ const char* sc_status_string(sc_status s)
     }
 }
 
-int sc_version(void) { return 100; }
+int sc_version(void) { return 200; }
 
 }  // extern "C"

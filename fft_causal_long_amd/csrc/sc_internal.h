@@ -20,10 +20,15 @@ constexpr int DIRECT_MAX_L = 32;
 
 enum class Store { F32, BF16 };
 
+// Every launcher computes r = causal(v, g) per channel; with rev it computes the gradient
+// form r = rev(causal(rev(v), g)), i.e. r_j = sum_{t>=j} v_t g_{t-j} (v read reversed, r
+// written reversed).
+
 // Fused in-LDS causal convolution for DIRECT_MAX_L < L <= FUSED_MAX_L.
 // M = next power of two >= L.  head = number of leading outputs computed directly (even).
 hipError_t launch_fused(Store st, const void* v, const void* g, void* r, int64_t nch, int L,
-                        int M, int head, bool pair_store, const float2* tw, hipStream_t stream);
+                        int M, int head, bool pair_store, bool rev, const float2* tw,
+                        hipStream_t stream);
 
 // Constants of the exact path modulo p = 998244353 (omega_n = 3^((p-1)/n)).  The bank
 // holds pairs of doubles {w, w / p}:
@@ -41,7 +46,7 @@ struct NttTables {
 
 // Exact NTT causal convolution for L <= FUSED_MAX_L, M = max(64, next power of two >= L).
 hipError_t launch_ntt(const int32_t* v, const int32_t* g, int32_t* r, int64_t nch, int L, int M,
-                      const NttTables& tables, hipStream_t stream);
+                      bool rev, const NttTables& tables, hipStream_t stream);
 
 // ---- four-step path (L > FUSED_MAX_L)
 // Longest row transform of the four-step split M = M1 * M2 (M2 <= this, M1 >= 64).
@@ -65,11 +70,11 @@ void fourstep_split(int M, int* M1, int* M2);
 size_t fourstep_bytes_per_channel(int M);
 // ws holds chunk channels of scratch (chunk * fourstep_bytes_per_channel(M) bytes).
 hipError_t launch_fourstep(Store st, const void* v, const void* g, void* r, int64_t nch, int L,
-                           int M, int head, bool pair_store, const float2* bank, const FsTw& tw,
-                           void* ws, int64_t chunk, hipStream_t stream);
+                           int M, int head, bool pair_store, bool rev, const float2* bank,
+                           const FsTw& tw, void* ws, int64_t chunk, hipStream_t stream);
 
 // Direct summation r_t = sum_{j<=t} v_j g_{t-j} in fp32, one thread per output.
 hipError_t launch_direct(Store st, const void* v, const void* g, void* r, int64_t nch, int L,
-                         hipStream_t stream);
+                         bool rev, hipStream_t stream);
 
 }  // namespace sc

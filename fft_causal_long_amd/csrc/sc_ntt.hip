@@ -250,7 +250,9 @@ __device__ __forceinline__ void passes(double (&x)[NA][16], int32_t* __restrict_
 
 }  // namespace ntt
 
-template <int M>
+// REV (the gradient kernels): the first input is read reversed and the output is written
+// reversed: rev(causal(rev(dr), b))_j = sum_{t>=j} dr_t b_{t-j}.
+template <int M, bool REV>
 __global__ __launch_bounds__(512, 4) void ntt_conv_kernel(const int32_t* __restrict__ v,
                                                        const int32_t* __restrict__ g,
                                                        int32_t* __restrict__ r, int64_t nch,
@@ -277,16 +279,18 @@ __global__ __launch_bounds__(512, 4) void ntt_conv_kernel(const int32_t* __restr
     int32_t* bg = bv + REG;
     const int cbase = cl * L;
 
-    // 1. inputs as exact doubles (|x| < 2^31), times omega_N^n on branch 1
+    // 1. inputs as exact doubles (|x| < 2^31), times omega_N^n on branch 1.  Positions past
+    //    L are read at byte offset 2^31, beyond the descriptor's range, so they read 0 (a
+    //    select instead of a branch keeps all the loads in flight together).
     double x[2][16];
 #pragma unroll
     for (int q = 0; q < 16; ++q) {
         const int n = tau + TB * q;
-        double a = 0.0, b = 0.0;
-        if (L == M || n < L) {
-            a = (double)(int32_t)__builtin_amdgcn_raw_buffer_load_b32(vs.rs, (cbase + n) * 4, 0, 0);
-            b = (double)(int32_t)__builtin_amdgcn_raw_buffer_load_b32(gs.rs, (cbase + n) * 4, 0, 0);
-        }
+        const bool in = L == M || n < L;
+        const uint32_t ob = in ? (uint32_t)(cbase + n) * 4u : 0x80000000u;
+        const uint32_t oa = in ? (uint32_t)(cbase + (REV ? L - 1 - n : n)) * 4u : 0x80000000u;
+        double a = (double)(int32_t)__builtin_amdgcn_raw_buffer_load_b32(vs.rs, (int)oa, 0, 0);
+        double b = (double)(int32_t)__builtin_amdgcn_raw_buffer_load_b32(gs.rs, (int)ob, 0, 0);
         if (beta) {
             const W w = tw.at(n * (NTT_TW_N / N), 0);
             a = mulc(a, w);
@@ -329,35 +333,44 @@ __global__ __launch_bounds__(512, 4) void ntt_conv_kernel(const int32_t* __restr
         if (n >= L) continue;
         double s = reduce(own[q] + (double)xch[reg_off<TB>(tau, q)]);   // |s| <= p/2 + p
         s = s > 0.5 * (P - 1.0) ? s - P : (s < -0.5 * (P - 1.0) ? s + P : s);
-        __builtin_amdgcn_raw_buffer_store_b32((uint32_t)(int32_t)s, rs.rs, (cbase + n) * 4, 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b32((uint32_t)(int32_t)s, rs.rs,
+                                              (cbase + (REV ? L - 1 - n : n)) * 4, 0, 0);
     }
 }
 
-template <int M>
+template <int M, bool REV>
 static hipError_t launch_ntt_m(const int32_t* v, const int32_t* g, int32_t* r, int64_t nch,
                                int L, const NttTables& tb, hipStream_t stream)
 {
     constexpr int CPW = (512 / (M / 16)) / 2;
     const int64_t blocks = (nch + CPW - 1) / CPW;
     const int lg = __builtin_ctz((unsigned)(2 * M));
-    hipLaunchKernelGGL((ntt_conv_kernel<M>), dim3((unsigned)blocks), dim3(512), 0, stream, v, g, r,
+    hipLaunchKernelGGL((ntt_conv_kernel<M, REV>), dim3((unsigned)blocks), dim3(512), 0, stream, v, g, r,
                        nch, L, tb.bank, tb.ninv[lg], tb.ninv_q[lg]);
     return hipGetLastError();
 }
 
-hipError_t launch_ntt(const int32_t* v, const int32_t* g, int32_t* r, int64_t nch, int L, int M,
-                      const NttTables& tb, hipStream_t s)
+template <bool REV>
+static hipError_t launch_ntt_rev(const int32_t* v, const int32_t* g, int32_t* r, int64_t nch,
+                                 int L, int M, const NttTables& tb, hipStream_t s)
 {
     switch (M) {
-    case 64: return launch_ntt_m<64>(v, g, r, nch, L, tb, s);
-    case 128: return launch_ntt_m<128>(v, g, r, nch, L, tb, s);
-    case 256: return launch_ntt_m<256>(v, g, r, nch, L, tb, s);
-    case 512: return launch_ntt_m<512>(v, g, r, nch, L, tb, s);
-    case 1024: return launch_ntt_m<1024>(v, g, r, nch, L, tb, s);
-    case 2048: return launch_ntt_m<2048>(v, g, r, nch, L, tb, s);
-    case 4096: return launch_ntt_m<4096>(v, g, r, nch, L, tb, s);
+    case 64: return launch_ntt_m<64, REV>(v, g, r, nch, L, tb, s);
+    case 128: return launch_ntt_m<128, REV>(v, g, r, nch, L, tb, s);
+    case 256: return launch_ntt_m<256, REV>(v, g, r, nch, L, tb, s);
+    case 512: return launch_ntt_m<512, REV>(v, g, r, nch, L, tb, s);
+    case 1024: return launch_ntt_m<1024, REV>(v, g, r, nch, L, tb, s);
+    case 2048: return launch_ntt_m<2048, REV>(v, g, r, nch, L, tb, s);
+    case 4096: return launch_ntt_m<4096, REV>(v, g, r, nch, L, tb, s);
     default: return hipErrorInvalidValue;
     }
+}
+
+hipError_t launch_ntt(const int32_t* v, const int32_t* g, int32_t* r, int64_t nch, int L, int M,
+                      bool rev, const NttTables& tb, hipStream_t s)
+{
+    return rev ? launch_ntt_rev<true>(v, g, r, nch, L, M, tb, s)
+               : launch_ntt_rev<false>(v, g, r, nch, L, M, tb, s);
 }
 
 }  // namespace sc

@@ -156,6 +156,44 @@ sc_status sc_causal_conv_ex(sc_kind kind, const void* v, const void* g, void* r,
                             size_t ws_bytes, hipStream_t stream);
 
 /*
+ * Gradients (backward pass).  The Caracal models are trained end to end with a next-token
+ * loss ("Caracal: Causal Architecture via Spectral Mixing", loss function / training
+ * strategy), so the convolution of key design 1 needs its vector-Jacobian product: for the
+ * output gradient dr = dLoss/dr (same layout as r),
+ *
+ *     dv[b][c][j] = sum_{t=j..L-1} dr[b][c][t] * g[b][c][t-j]
+ *     dg[b][c][k] = sum_{t=k..L-1} dr[b][c][t] * v[b][c][t-k]
+ *
+ * i.e. dv = rev(causal_conv(rev(dr), g)) and dg = rev(causal_conv(rev(dr), v)), where rev
+ * reverses t.  The library computes each as a causal convolution on the same paths as the
+ * forward call (the first input read reversed, the output written reversed): same pad-2L
+ * transform, same accuracy statement with the error scale
+ *     sum_{t>=j} |dr_t| |g_{t-j}|   (for dv)   and   sum_{t>=k} |dr_t| |v_{t-k}|   (for dg),
+ * and the last 32 outputs (j >= L-32), whose scale holds few products, by direct fp32
+ * summation.  The exact kind returns the residues of the two sums mod p in the symmetric
+ * range; dv_j depends on dr_j..dr_{L-1} only, bit for bit.
+ *
+ * Arguments: dr, v, g as in the forward call; dv, dg are outputs of the same shape, and may
+ * overlap neither each other nor any input (-> SC_ERR_INVALID_ARGUMENT).  The other
+ * conventions, limits and errors are those of the forward call of the same kind.  Scratch:
+ * the two gradients run one after the other and share one workspace, so a call needs
+ * sc_workspace_bytes(kind, B, C, L) bytes, the same as the forward call of that shape.
+ */
+sc_status sc_causal_conv_bwd_f32(const float* dr, const float* v, const float* g, float* dv,
+                                 float* dg, int64_t B, int64_t C, int64_t L, hipStream_t stream);
+sc_status sc_causal_conv_bwd_bf16(const uint16_t* dr, const uint16_t* v, const uint16_t* g,
+                                  uint16_t* dv, uint16_t* dg, int64_t B, int64_t C, int64_t L,
+                                  hipStream_t stream);
+sc_status sc_causal_conv_bwd_ntt_i32(const int32_t* dr, const int32_t* v, const int32_t* g,
+                                     int32_t* dv, int32_t* dg, int64_t B, int64_t C, int64_t L,
+                                     hipStream_t stream);
+/* any kind, with options and an optional caller workspace, as sc_causal_conv_ex */
+sc_status sc_causal_conv_bwd_ex(sc_kind kind, const void* dr, const void* v, const void* g,
+                                void* dv, void* dg, int64_t B, int64_t C, int64_t L,
+                                const sc_options* opt, void* ws, size_t ws_bytes,
+                                hipStream_t stream);
+
+/*
  * sc_ntt_range_ok -- 1 if every |v_j| <= max_abs_v and |g_j| <= max_abs_g guarantee that
  *   the exact sums fit the symmetric residue range, i.e. L * max_abs_v * max_abs_g <=
  *   (p-1)/2; 0 otherwise (or on negative arguments).  Host only.
@@ -165,7 +203,7 @@ int sc_ntt_range_ok(int64_t max_abs_v, int64_t max_abs_g, int64_t L);
 /* Human-readable name of a status code (static storage).  Host only. */
 const char* sc_status_string(sc_status s);
 
-/* Library version: major * 10000 + minor * 100 + patch.  Host only. */
+/* Library version: major * 10000 + minor * 100 + patch (this header: 200).  Host only. */
 int sc_version(void);
 
 #ifdef __cplusplus

@@ -125,3 +125,58 @@ def test_host_helpers(sc):
     assert sc.sc_workspace_bytes(sc.KIND_NTT_I32, 1, 1, 4096) == 0
     assert sc.sc_workspace_bytes(sc.KIND_F32, -1, 1, 65536) == 0
     assert sc.sc_workspace_bytes(sc.KIND_F32, 1, 1, 2**23) == 0      # above the maximum
+
+
+D_, E_ = 0x400000, 0x500000   # fake output pointers of the gradient calls
+
+
+def test_header_declares_the_gradient_calls():
+    names = declared_functions()
+    for n in ("sc_causal_conv_bwd_f32", "sc_causal_conv_bwd_bf16", "sc_causal_conv_bwd_ntt_i32",
+              "sc_causal_conv_bwd_ex"):
+        assert n in names
+
+
+@pytest.mark.parametrize("fn", ["sc_causal_conv_bwd_f32", "sc_causal_conv_bwd_bf16",
+                                "sc_causal_conv_bwd_ntt_i32"])
+def test_bwd_host_validation(sc, fn):
+    f = getattr(sc.lib(), fn)
+    INVALID, OK = sc.SC_ERR_INVALID_ARGUMENT, sc.SC_OK
+    good = [A, B_, C_, D_, E_]
+    assert f(*good, -1, 1, 1, None) == INVALID
+    assert f(*good, 1, 1, -2, None) == INVALID
+    for i in range(5):                                   # each pointer null
+        p = list(good)
+        p[i] = None
+        assert f(*p, 1, 1, 4, None) == INVALID, i
+    for i in range(5):                                   # each pointer misaligned
+        p = list(good)
+        p[i] += 1
+        assert f(*p, 1, 1, 4, None) == INVALID, i
+    for out in (3, 4):                                   # an output on any input or the other output
+        for other in range(5):
+            if other == out:
+                continue
+            p = list(good)
+            p[out] = p[other] + 4
+            assert f(*p, 1, 1, 4, None) == INVALID, (out, other)
+    assert f(*good, 2**40, 2**40, 2**40, None) == INVALID
+    assert f(None, None, None, None, None, 0, 5, 5, None) == OK
+    assert f(None, None, None, None, None, 5, 5, 0, None) == OK
+
+
+def test_bwd_unsupported_and_options(sc):
+    h = sc.lib()
+    UNSUP, INVALID = sc.SC_ERR_UNSUPPORTED, sc.SC_ERR_INVALID_ARGUMENT
+    assert h.sc_causal_conv_bwd_ntt_i32(A, B_, C_, D_, E_, 1, 1, 5000, None) == UNSUP
+    far = [k << 32 for k in range(1, 6)]
+    assert h.sc_causal_conv_bwd_f32(*far, 1, 1, 2**22 + 1, None) == UNSUP
+    opt = sc.sc_options(sc.PATH_FUSED, -1)
+    assert h.sc_causal_conv_bwd_ex(0, A, B_, C_, D_, E_, 1, 1, 4097, ctypes.byref(opt), None, 0,
+                                   None) == UNSUP
+    opt = sc.sc_options(0, -1)
+    opt.reserved[0] = 3
+    assert h.sc_causal_conv_bwd_ex(1, A, B_, C_, D_, E_, 1, 1, 64, ctypes.byref(opt), None, 0,
+                                   None) == INVALID
+    assert h.sc_causal_conv_bwd_ex(5, A, B_, C_, D_, E_, 1, 1, 64, None, None, 0, None) == INVALID
+    assert sc.sc_version() >= 200

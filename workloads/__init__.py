@@ -5,8 +5,8 @@ smoke check, bench) and therefore holds none of the convolution's arithmetic: it
 draws random numbers, shapes them like the pages' models and rounds them to the stored
 dtype.  Every array is generated in float64 from ``numpy.random.default_rng`` seeded with
 ``SeedSequence([config_id, stream_id])`` (stream 0 = v, 1 = gate pre-activation,
-2 = gate conv weights, 3 = extra draws such as perturbation positions), then rounded once
-to the stored dtype.
+2 = gate conv weights, 3 = extra draws such as perturbation positions, 4 = the upstream
+gradient dr of the backward pass), then rounded once to the stored dtype.
 
 Workload shapes (the model shapes follow "Caracal: Causal Architecture via Spectral
 Mixing": the multi-head Fourier module mixes C = n_head * head_dim channels per batch
@@ -141,6 +141,23 @@ def make_inputs(w: Workload, B: int | None = None, C: int | None = None,
     if w.storage == "bf16":
         return f32_to_bf16_bits(v32), f32_to_bf16_bits(g32)
     return v32, g32
+
+
+def make_grad(w: Workload, B: int | None = None, C: int | None = None, L: int | None = None,
+              seed_offset: int = 0) -> np.ndarray:
+    """Upstream gradient ``dr`` = dLoss/dr for the backward pass, shape (B, C, L) in the
+    workload's stored dtype: N(0,1) for the float workloads (the gradient of a next-token
+    loss reaching the mixer has no structure to imitate here), uniform integers in
+    [-127, 127] for the exact workload."""
+    B = w.B if B is None else B
+    C = w.C if C is None else C
+    L = w.L if L is None else L
+    cid = w.cid + 1000 * seed_offset
+    shape = (B, C, L)
+    if w.gate == "int":
+        return rng(cid, 4).integers(-127, 128, size=shape, dtype=np.int32)
+    d32 = rng(cid, 4).standard_normal(shape).astype(np.float32)
+    return f32_to_bf16_bits(d32) if w.storage == "bf16" else d32
 
 
 def perturbation_positions(cid: int, L: int, count: int = 8) -> np.ndarray:
