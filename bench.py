@@ -5,6 +5,8 @@
 One step = one call of the library's hot path over one batch of synthetic input (for the
 default workload, sc_causal_conv_bf16 at B=8, C=1024, L=4096: load v and g, pad-to-2L FFT,
 spectral product, inverse FFT, truncation, direct head, store r -- a single kernel).
+After the timed region, the gradient call of the same workload (dv, dg from dr, v, g) is
+timed the same way and reported in the `bwd` object (skip with --no-bwd).
 Inputs are resident in HBM before the timed region.  Several copies of the buffers are
 rotated so that the 256 MB last-level cache cannot hold a step's working set.
 
@@ -64,16 +66,19 @@ def measured_traffic(workload: str):
 COPY_BYTES = 1 << 30   # the --calib-copy transfer: 2^28 float32 read and written
 
 
-def kernel_matches(name: str, storage: str, L: int) -> bool:
-    """Is this profiled kernel part of the timed hot path of the workload?  (Exact template,
-    so launches of the leakage probe or of other shapes do not count.)"""
+def kernel_matches(name: str, storage: str, L: int, rev: bool = False) -> bool:
+    """Is this profiled kernel part of the timed hot path of the workload (the forward call,
+    or with rev the gradient call)?  Exact template, so launches of the leakage probe, of
+    other shapes or of the other direction do not count."""
     M = max(64, 1 << (L - 1).bit_length())
+    flag = "true" if rev else "false"
     if storage == "i32":
-        return ("ntt_conv_kernel<%d>" % M) in name
+        return ("ntt_conv_kernel<%d, %s>" % (M, flag)) in name
     if L > 4096:
-        return "fs_" in name or "head_kernel" in name
+        return "fs_rows<" in name or (("fs_columns" in name or "head_kernel" in name)
+                                      and (", %s>" % flag) in name)
     io = "bf16_io" if storage == "bf16" else "f32_io"
-    return ("fused_conv_kernel<%d, sc::%s>" % (M, io)) in name
+    return ("fused_conv_kernel<%d, sc::%s, %s>" % (M, io, flag)) in name
 
 
 def record_traffic(w, fetch_dir: str, write_dir: str) -> dict:
@@ -179,6 +184,58 @@ def cpu_baseline(w, v, g, budget_s: float = 10.0):
     }
 
 
+def bwd_measure(sc, torch, w, dev, steps: int, warmup: int) -> dict:
+    """Time the gradient call (dv and dg for one upstream gradient dr) on the same workload:
+    inputs dr, v, g resident, buffers rotated like the forward, HIP events around each call
+    on the launch stream.  Algorithmic work per position: read dr, v, g and write dv, dg
+    (5 elements); two reversed causal convolutions, 2 x (12.75 log2 L + 28) flops."""
+    from workloads import make_grad, make_inputs
+    kind = {"f32": ("sc_causal_conv_bwd_f32", 4), "bf16": ("sc_causal_conv_bwd_bf16", 2),
+            "i32": ("sc_causal_conv_bwd_ntt_i32", 4)}[w.storage]
+    fn, esz = getattr(sc.lib(), kind[0]), kind[1]
+    v, g = make_inputs(w)
+    dr = make_grad(w)
+    tdtype = {"f32": torch.float32, "bf16": torch.int16, "i32": torch.int32}[w.storage]
+    host = [torch.from_numpy(x.view(np.int16) if w.storage == "bf16" else x) for x in (dr, v, g)]
+    set_bytes = 5 * w.outputs * esz
+    nsets = max(1, -(-2 * CACHE_BYTES // set_bytes))
+    bufs = [[x.to(dev) for x in host] + [torch.empty(w.outputs, dtype=tdtype, device=dev)
+                                         for _ in range(2)] for _ in range(nsets)]
+    stream = torch.cuda.current_stream(dev)
+    sptr = stream.cuda_stream
+
+    def call(i):
+        b = bufs[i % nsets]
+        st = fn(*[t.data_ptr() for t in b], w.B, w.C, w.L, sptr)
+        if st != 0:
+            raise RuntimeError("%s failed: %s" % (kind[0], sc.sc_status_string(st)))
+
+    for i in range(warmup):
+        call(i)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    torch.cuda.synchronize()
+    for i in range(steps):
+        ev[i][0].record(stream)
+        call(i)
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    alg_bytes = 5 * w.outputs * esz
+    gbps = alg_bytes / (ms * 1e-3) / 1e9
+    rec = {"entry": kind[0], "ms_per_call": round(ms, 5),
+           "value": round(w.outputs / (ms * 1e-3), 1), "unit": "positions/s",
+           "buffer_sets": nsets,
+           "hbm": {"algorithmic_bytes_per_call": alg_bytes, "achieved_GBps": round(gbps, 1),
+                   "frac": round(gbps / HBM_PEAK_GBPS, 4)}}
+    if w.storage != "i32":
+        tf = 2 * algorithmic_flops_per_output(w.L) * w.outputs / (ms * 1e-3) / 1e12
+        rec["alu"] = {"achieved_TFLOPs": round(tf, 2), "peak": FP32_VECTOR_PEAK_TFLOPS,
+                      "frac": round(tf / FP32_VECTOR_PEAK_TFLOPS, 4)}
+    del bufs
+    return rec
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -188,6 +245,9 @@ def main(argv=None):
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-leakage", action="store_true",
                     help="skip the leakage probe (keeps profiler runs to the timed kernel)")
+    ap.add_argument("--no-bwd", action="store_true",
+                    help="skip the timing of the gradient call (keeps profiler runs to the "
+                         "forward kernel)")
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run a plain device copy of known size (profiler calibration)")
     ap.add_argument("--record-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
@@ -303,6 +363,9 @@ def main(argv=None):
                       "p50": round(float(np.median(launch_ms)), 5),
                       "max": round(float(np.max(launch_ms)), 5)},
     }
+    if not args.no_bwd:
+        del bufs
+        rec["bwd"] = bwd_measure(sc, torch, w, dev, max(5, args.steps // 2), args.warmup)
     if not args.no_leakage:
         rec["leakage"] = leakage_probe(sc, torch, dev)
     if not args.no_cpu_baseline:
