@@ -23,6 +23,14 @@ blocking or fusion (see ``oracle.c`` for the C side):
   sum_t dr[t] r[t]: dv[j] = sum_{t>=j} dr[t] g[t-j], dg[k] = sum_{t>=k} dr[t] v[t-k], with
   their error scales (the pages' models are trained end to end with a next-token loss,
   "Caracal", loss function / training strategy).
+* :func:`fixed_encode`, :func:`causal_conv_i128`, :func:`fixed_decode_f32`,
+  :func:`causal_conv_fixed_f32` -- the exactly causal real-valued convolution: inputs
+  encoded as integers V = round(v 2^fv), G = round(g 2^fg) (nearest, ties to even), the
+  exact integer causal sum R (signed 128-bit), and r = R 2^-(fv+fg) rounded once to
+  float32 (nearest, ties to even, subnormals included).  The leakage page proposes
+  transforms executed on integers only ("Catastrophic Token Leakage ...", abstract); a
+  fixed-point encoding with caller-chosen scales carries real activations onto integers
+  without letting any output depend on a later input.
 * :func:`circular_conv_dft` / :func:`circular_conv_ntt` -- the pages' recipe (zero-pad on
   the right to n, transform, multiply, inverse, keep all n values) with O(n^2) DFT / NTT,
   used only to pin key design 2 against the direct sum.
@@ -88,6 +96,9 @@ def _load():
         lib.oracle_conv_bwd_f64.argtypes = [dp] * 7 + [i64, i64, ctypes.c_int]
         lib.oracle_conv_bwd_f64.restype = ctypes.c_int
         lib.oracle_conv_bwd_i64.argtypes = [lp] * 5 + [i64, i64, ctypes.c_int]
+        lib.oracle_conv_i128.argtypes = [lp, lp, lp, ctypes.POINTER(ctypes.c_uint64), i64, i64,
+                                         ctypes.c_int]
+        lib.oracle_conv_i128.restype = ctypes.c_int
         lib.oracle_conv_bwd_i64.restype = ctypes.c_int
         _lib = lib
         return lib
@@ -211,6 +222,83 @@ def causal_conv_bwd_i64(dr, v, g, nthreads: int | None = None):
     if rc != 0:
         raise RuntimeError("oracle_conv_bwd_i64 failed")
     return dv, dg
+
+
+def fixed_encode(x, f: int) -> np.ndarray:
+    """V = round(x * 2^f) (nearest, ties to even) as int64, exact: x is widened exactly from
+    its stored dtype, the power-of-two scaling is exact in float64, and numpy.rint rounds
+    half to even.  Raises OverflowError when some |x 2^f| reaches 2^62."""
+    y = np.ldexp(as_f64(x), int(f))
+    if y.size and not np.all(np.abs(y) < 2.0 ** 62):
+        raise OverflowError("fixed_encode: |x * 2^f| >= 2^62")
+    return np.rint(y).astype(np.int64)
+
+
+def causal_conv_i128(V, G, nthreads: int | None = None) -> np.ndarray:
+    """Exact causal sum of int64 sequences in 128-bit arithmetic; returns Python integers
+    (numpy object array of the input shape)."""
+    v64 = np.ascontiguousarray(V, dtype=np.int64)
+    g64 = np.ascontiguousarray(G, dtype=np.int64)
+    if v64.shape != g64.shape:
+        raise ValueError("V and G must have the same shape")
+    shape = v64.shape
+    L = shape[-1] if len(shape) else 0
+    nch = int(np.prod(shape[:-1])) if len(shape) > 1 else 1
+    hi = np.zeros(shape, dtype=np.int64)
+    lo = np.zeros(shape, dtype=np.uint64)
+    if v64.size:
+        rc = _load().oracle_conv_i128(_lptr(v64), _lptr(g64), _lptr(hi),
+                                      lo.ctypes.data_as(ctypes.POINTER(ctypes.c_uint64)),
+                                      nch, L, nthreads or default_threads())
+        if rc != 0:
+            raise RuntimeError("oracle_conv_i128 failed")
+    out = np.empty(shape, dtype=object)
+    flat_hi, flat_lo, flat = hi.ravel(), lo.ravel(), out.reshape(-1)
+    for i in range(flat.size):
+        flat[i] = (int(flat_hi[i]) << 64) + int(flat_lo[i])
+    return out
+
+
+def _rne_to_f32(R: int, F: int) -> float:
+    """The float32 nearest to R * 2^-F (ties to even; subnormals; overflow to inf)."""
+    if R == 0:
+        return 0.0
+    m = -R if R < 0 else R
+    e = m.bit_length() - 1 - F                  # R 2^-F lies in [2^e, 2^(e+1))
+    qexp = max(e - 23, -149)                    # spacing of float32 numbers there
+    sh = F + qexp                               # keep m / 2^sh, rounded to an integer
+    if sh <= 0:
+        mant = m << (-sh)
+    else:
+        mant = m >> sh
+        rem = m - (mant << sh)
+        half = 1 << (sh - 1)
+        if rem > half or (rem == half and (mant & 1)):
+            mant += 1
+    if mant >= (1 << 24) and qexp + 24 > 128:   # rounds past the largest finite float32
+        val = float("inf")
+    else:
+        val = float(mant) * 2.0 ** qexp          # exact in float64
+        if val >= 2.0 ** 128:
+            val = float("inf")
+    return -val if R < 0 else val
+
+
+def fixed_decode_f32(R, F: int) -> np.ndarray:
+    """Round each exact integer R (object array) times 2^-F once to float32."""
+    R = np.asarray(R, dtype=object)
+    out = np.empty(R.shape, dtype=np.float32)
+    flat, o = R.reshape(-1), out.reshape(-1)
+    for i in range(flat.size):
+        o[i] = np.float32(_rne_to_f32(int(flat[i]), int(F)))
+    return out
+
+
+def causal_conv_fixed_f32(v, g, fv: int, fg: int, nthreads: int | None = None) -> np.ndarray:
+    """The exactly causal real-valued convolution: float32 result of
+    round_f32(sum_{j<=t} round(v_j 2^fv) round(g_{t-j} 2^fg) * 2^-(fv+fg))."""
+    return fixed_decode_f32(causal_conv_i128(fixed_encode(v, fv), fixed_encode(g, fg),
+                                             nthreads), fv + fg)
 
 
 def lift_mod_p(r, p: int = P_NTT) -> np.ndarray:

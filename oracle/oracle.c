@@ -39,6 +39,13 @@
  *
  *   oracle_conv_bwd_i64  the same two sums in exact int64.
  *
+ *   oracle_conv_i128  r[t] = sum_{j<=t} v[j] * g[t-j] for int64 inputs in exact signed
+ *                     128-bit arithmetic (returned as high and low 64-bit halves): the
+ *                     exact sum of fixed-point encodings of real inputs, for the exactly
+ *                     causal real-valued path (number-theoretic transforms on integers,
+ *                     "Catastrophic Token Leakage ...", abstract, applied to real
+ *                     activations through a fixed-point encoding).
+ *
  * Loop order of the direct sums is "for j: for t >= j: r[t] += v[j]*g[t-j]" (an axpy per
  * input tap), which fixes the rounding order and touches r[t] only with v[0..t].  The
  * gradient sums run "for t: for j <= t: dv[j] += dr[t]*g[t-j]" (an axpy per output tap).
@@ -245,6 +252,45 @@ int oracle_conv_bwd_i64(const int64_t *dr, const int64_t *v, const int64_t *g, i
     if (!dr || !v || !g || !dv || !dg) return -1;
     bwd_i64_ctx k = {dr, v, g, dv, dg, L};
     return for_channels(bwd_i64_channel, &k, nch, nthreads);
+}
+
+/* ---------------------------------------------------------------- int128 direct sum */
+
+typedef struct {
+    const int64_t *v, *g;
+    int64_t *hi;
+    uint64_t *lo;
+    int64_t L;
+} i128_ctx;
+
+static void conv_i128_channel(void *p, int64_t c)
+{
+    i128_ctx *k = (i128_ctx *)p;
+    const int64_t L = k->L;
+    const int64_t *v = k->v + c * L, *g = k->g + c * L;
+    __int128 *acc = (__int128 *)calloc((size_t)(L > 0 ? L : 1), sizeof(__int128));
+    if (!acc) return;
+    for (int64_t j = 0; j < L; ++j) {
+        const __int128 vj = v[j];
+        for (int64_t t = j; t < L; ++t) acc[t] += vj * (__int128)g[t - j];
+    }
+    for (int64_t t = 0; t < L; ++t) {
+        const unsigned __int128 u = (unsigned __int128)acc[t];
+        k->lo[c * L + t] = (uint64_t)u;
+        k->hi[c * L + t] = (int64_t)(uint64_t)(u >> 64);
+    }
+    free(acc);
+}
+
+/* Exact while |v|, |g| < 2^63 and every partial sum fits in 127 bits.  r = hi * 2^64 + lo. */
+int oracle_conv_i128(const int64_t *v, const int64_t *g, int64_t *hi, uint64_t *lo, int64_t nch,
+                     int64_t L, int nthreads)
+{
+    if (nch < 0 || L < 0) return -1;
+    if (nch == 0 || L == 0) return 0;
+    if (!v || !g || !hi || !lo) return -1;
+    i128_ctx k = {v, g, hi, lo, L};
+    return for_channels(conv_i128_channel, &k, nch, nthreads);
 }
 
 /* ---------------------------------------------------------------- sampled outputs */

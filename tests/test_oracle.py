@@ -390,3 +390,174 @@ def test_bwd_anticausal_and_scales():
     assert all(np.array_equal(x, y) for x, y in zip(a, b))
     e = oracle.causal_conv_bwd_f64(np.zeros((2, 0)), np.zeros((2, 0)), np.zeros((2, 0)))
     assert e[0].shape == (2, 0)
+
+
+# ---------------------------------------------------------------- fixed-point exact path
+
+def test_fixed_encode_rounding():
+    # nearest, ties to even, on the stored value times 2^f
+    x = np.array([0.5, 1.5, 2.5, -0.5, -1.5, 3.25, 0.75, -2.75], dtype=np.float32)
+    assert oracle.fixed_encode(x, 0).tolist() == [0, 2, 2, 0, -2, 3, 1, -3]
+    assert oracle.fixed_encode(x, 1).tolist() == [1, 3, 5, -1, -3, 6, 2, -6]
+    # bf16 bits are decoded exactly: 0x3FC0 = 1.5
+    assert oracle.fixed_encode(np.array([0x3FC0], dtype=np.uint16), 3).tolist() == [12]
+    with pytest.raises(OverflowError):
+        oracle.fixed_encode(np.array([1.0], dtype=np.float32), 62)
+
+
+def test_int128_sum_against_python_integers():
+    rng = np.random.default_rng(41)
+    for L in (1, 3, 17):
+        v = rng.integers(-2**40, 2**40, size=(2, L), dtype=np.int64)
+        g = rng.integers(-2**40, 2**40, size=(2, L), dtype=np.int64)
+        r = oracle.causal_conv_i128(v, g)
+        for c in range(2):
+            for t in range(L):
+                assert r[c, t] == sum(int(v[c, j]) * int(g[c, t - j]) for j in range(t + 1))
+    small = rng.integers(-1000, 1000, size=(3, 50))
+    assert np.array_equal(oracle.causal_conv_i128(small, small[::-1]).astype(np.int64),
+                          causal_conv_i64(small, small[::-1]))
+
+
+def test_rne_to_f32_cases():
+    d = oracle.fixed_decode_f32
+    # ties to even at the 24-bit boundary, both directions, and negative values
+    assert d(np.array([2**24 + 1, 2**24 + 3, -(2**24 + 1)], dtype=object), 0).tolist() == \
+        [16777216.0, 16777220.0, -16777216.0]
+    # scaling: 3 * 2^-2 exact; 2^25 + 1 at scale 2^-1 rounds to 2^24
+    assert d(np.array([3, 2**25 + 1], dtype=object), 2).tolist() == [0.75, 8388608.0]
+    # subnormals: smallest, half of it (tie -> 0), three quarters (-> smallest), 1.5x (tie -> 2x)
+    sub = np.float32(2.0 ** -149)
+    got = d(np.array([1, 3], dtype=object), 149)
+    assert oracle._rne_to_f32(1, 149) == float(sub)
+    assert oracle._rne_to_f32(1, 150) == 0.0
+    assert oracle._rne_to_f32(3, 151) == float(sub)
+    assert oracle._rne_to_f32(3, 150) == 2 * float(sub)
+    # largest finite float32 and overflow
+    fmax = float(np.finfo(np.float32).max)
+    assert oracle._rne_to_f32((2**24 - 1) << 104, 0) == fmax
+    assert oracle._rne_to_f32(1 << 128, 0) == float("inf")
+    assert oracle._rne_to_f32(-(1 << 130), 1) == float("-inf")
+    assert got.dtype == np.float32 and got.tolist() == [float(sub), 3 * float(sub)]
+
+
+def test_rne_to_f32_matches_numpy_single_rounding():
+    # for |R| < 2^53 the float64 value R 2^-F is exact, and numpy's float32 cast of it is the
+    # one rounding the definition asks for
+    rng = np.random.default_rng(42)
+    R = [int(x) for x in rng.integers(-2**52, 2**52, size=400)] + [0, 1, -1, 2**52 - 1]
+    for F in (0, 7, 30, 60, 130):
+        got = oracle.fixed_decode_f32(np.array(R, dtype=object), F)
+        want = np.array([np.float32(np.ldexp(float(x), -F)) for x in R], dtype=np.float32)
+        assert np.array_equal(got.view(np.uint32), want.view(np.uint32)), F
+
+
+def test_fixed_path_exact_on_dyadic_inputs():
+    # inputs that are exact fixed-point numbers: the encoded sum is the real sum, so the
+    # result is that sum rounded once to float32 (the float64 oracle is exact here)
+    rng = np.random.default_rng(43)
+    fv, fg = 6, 9
+    v = (rng.integers(-500, 500, size=(3, 300)) * 2.0 ** -fv).astype(np.float32)
+    g = (rng.integers(-500, 500, size=(3, 300)) * 2.0 ** -fg).astype(np.float32)
+    r = oracle.causal_conv_fixed_f32(v, g, fv, fg)
+    ref, _ = causal_conv_f64(v, g)
+    assert np.array_equal(r, ref.astype(np.float32))
+
+
+def test_fixed_path_error_bound_and_causality():
+    rng = np.random.default_rng(44)
+    L, fv, fg = 200, 20, 22
+    v = rng.standard_normal((2, L)).astype(np.float32)
+    g = (1 / (1 + np.exp(-rng.standard_normal((2, L))))).astype(np.float32)
+    r = oracle.causal_conv_fixed_f32(v, g, fv, fg)
+    ref, _ = causal_conv_f64(v, g)
+    # quantization (half a unit of each encoding) plus the final float32 rounding
+    cg = np.cumsum(np.abs(g.astype(np.float64)), axis=-1)
+    cv = np.cumsum(np.abs(v.astype(np.float64)), axis=-1)
+    t = np.arange(1, L + 1)
+    bnd = 2.0 ** -(fv + 1) * cg + 2.0 ** -(fg + 1) * cv + t * 2.0 ** -(fv + fg + 2) \
+        + 2.0 ** -24 * np.abs(ref)
+    assert np.all(np.abs(r - ref) <= bnd)
+    for s in (1, 77, L - 1):
+        v2 = v.copy()
+        v2[:, s] += 0.25
+        r2 = oracle.causal_conv_fixed_f32(v2, g, fv, fg)
+        assert np.array_equal(r2[:, :s].view(np.uint32), r[:, :s].view(np.uint32))
+        assert not np.array_equal(r2[:, s], r[:, s])
+
+
+def _is_prime(n):
+    if n < 2:
+        return False
+    i = 2
+    while i * i <= n:
+        if n % i == 0:
+            return False
+        i += 1
+    return True
+
+
+def test_crt_primes():
+    # the three NTT primes the exact real-valued path uses: prime, 2^21 | p - 1, 3 a
+    # primitive root, product above 2^88 (the exact range is |R| <= (P - 1) / 2)
+    primes = [998244353, 1004535809, 469762049]
+    for p in primes:
+        assert _is_prime(p)
+        assert (p - 1) % (1 << 21) == 0
+        m, f = p - 1, 2
+        factors = set()
+        while f * f <= m:
+            while m % f == 0:
+                factors.add(f)
+                m //= f
+            f += 1
+        if m > 1:
+            factors.add(m)
+        assert all(pow(3, (p - 1) // q, p) != 1 for q in factors)
+    P = primes[0] * primes[1] * primes[2]
+    assert P > 2 ** 88
+    # Garner's mixed-radix digits (balanced) reconstruct every R with |R| <= (P-1)/2
+    rng = np.random.default_rng(45)
+    p0, p1, p2 = primes
+
+    def bal(x, p):
+        x %= p
+        return x - p if x > (p - 1) // 2 else x
+
+    for R in [0, 1, -1, (P - 1) // 2, -(P - 1) // 2] + [int(x) * 2**60 + int(y) for x, y in
+                                                         zip(rng.integers(-2**27, 2**27, 50),
+                                                             rng.integers(0, 2**60, 50))]:
+        s0, s1, s2 = bal(R, p0), bal(R, p1), bal(R, p2)
+        a0 = s0
+        a1 = bal((s1 - a0) * pow(p0, -1, p1), p1)
+        a2 = bal((s2 - a0 - a1 * p0) * pow(p0 * p1, -1, p2), p2)
+        assert a0 + a1 * p0 + a2 * p0 * p1 == R
+
+
+GOLDEN_FIXED = os.path.join(os.path.dirname(__file__), "golden", "hand_cases_fixed.txt")
+
+
+def _golden_fixed():
+    cases = []
+    with open(GOLDEN_FIXED) as f:
+        for line in f:
+            line = line.strip()
+            if not line or line.startswith("#"):
+                continue
+            name, fs, v, g, R, r = [x.strip() for x in line.split("|")]
+            fv, fg = [int(x) for x in fs.split()]
+            cases.append((name, fv, fg, [float(x) for x in v.split()],
+                          [float(x) for x in g.split()], [int(x) for x in R.split()],
+                          [float(x) for x in r.split()]))
+    assert len(cases) >= 3
+    return cases
+
+
+@pytest.mark.parametrize("case", _golden_fixed(), ids=lambda c: c[0])
+def test_golden_fixed(case):
+    _, fv, fg, v, g, R, r = case
+    V = oracle.fixed_encode(np.array(v, np.float32), fv)
+    G = oracle.fixed_encode(np.array(g, np.float32), fg)
+    assert oracle.causal_conv_i128(V, G).tolist() == R
+    assert oracle.causal_conv_fixed_f32(np.array(v, np.float32), np.array(g, np.float32),
+                                        fv, fg).tolist() == r
