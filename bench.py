@@ -73,7 +73,7 @@ def kernel_matches(name: str, storage: str, L: int, rev: bool = False) -> bool:
     M = max(64, 1 << (L - 1).bit_length())
     flag = "true" if rev else "false"
     if storage == "i32":
-        return ("ntt_conv_kernel<%d, %s>" % (M, flag)) in name
+        return ("ntt_conv_kernel<%d, %s, sc::ntt::PrimeA, false>" % (M, flag)) in name
     if L > 4096:
         return "fs_rows<" in name or (("fs_columns" in name or "head_kernel" in name)
                                       and (", %s>" % flag) in name)

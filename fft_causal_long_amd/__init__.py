@@ -14,7 +14,9 @@ Public names mirror the C ABI of ``include/specconv.h``:
 ``_ws`` variants, ``sc_causal_conv_ex``, ``sc_workspace_bytes``, ``sc_ntt_range_ok``,
 ``sc_status_string``, ``sc_version``, and the gradient calls ``sc_causal_conv_bwd_f32``,
 ``sc_causal_conv_bwd_bf16``, ``sc_causal_conv_bwd_ntt_i32``, ``sc_causal_conv_bwd_ex``; plus
-:func:`causal_conv` and :func:`causal_conv_bwd`, which dispatch on dtype.
+:func:`causal_conv` and :func:`causal_conv_bwd`, which dispatch on dtype; the exactly causal
+real-valued calls ``sc_causal_conv_fixed_f32``, ``sc_causal_conv_fixed_f32_ws``,
+``sc_fixed_range_ok`` and :func:`causal_conv_fixed`.
 """
 from __future__ import annotations
 
@@ -29,14 +31,15 @@ __all__ = [
     "sc_causal_conv_ntt_i32_ws", "sc_causal_conv_ex", "sc_workspace_bytes", "sc_ntt_range_ok",
     "sc_status_string", "sc_version", "causal_conv_bwd", "sc_causal_conv_bwd_f32",
     "sc_causal_conv_bwd_bf16", "sc_causal_conv_bwd_ntt_i32", "sc_causal_conv_bwd_ex",
-    "KIND_F32", "KIND_BF16", "KIND_NTT_I32", "PATH_AUTO", "PATH_FUSED", "PATH_FOUR_STEP",
+    "causal_conv_fixed", "sc_causal_conv_fixed_f32", "sc_causal_conv_fixed_f32_ws",
+    "sc_fixed_range_ok", "KIND_F32", "KIND_BF16", "KIND_NTT_I32", "KIND_FIXED_F32", "PATH_AUTO", "PATH_FUSED", "PATH_FOUR_STEP",
     "PATH_DIRECT", "LIB_PATH",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libspecconv.so")
 
 SC_OK, SC_ERR_INVALID_ARGUMENT, SC_ERR_UNSUPPORTED, SC_ERR_HIP, SC_ERR_WORKSPACE = range(5)
-KIND_F32, KIND_BF16, KIND_NTT_I32 = 0, 1, 2
+KIND_F32, KIND_BF16, KIND_NTT_I32, KIND_FIXED_F32 = 0, 1, 2, 3
 PATH_AUTO, PATH_FUSED, PATH_FOUR_STEP, PATH_DIRECT = 0, 1, 2, 3
 
 
@@ -48,7 +51,8 @@ class SpecConvError(RuntimeError):
 
 class sc_options(ctypes.Structure):
     _fields_ = [("path", ctypes.c_int32), ("head", ctypes.c_int32),
-                ("reserved", ctypes.c_int32 * 6)]
+                ("frac_v", ctypes.c_int32), ("frac_g", ctypes.c_int32),
+                ("reserved", ctypes.c_int32 * 4)]
 
 
 def _open():
@@ -74,6 +78,15 @@ def _open():
     h.sc_causal_conv_bwd_ex.argtypes = [st, vp, vp, vp, vp, vp, i64, i64, i64,
                                         ctypes.POINTER(sc_options), vp, sz, vp]
     h.sc_causal_conv_bwd_ex.restype = st
+    h.sc_causal_conv_fixed_f32.argtypes = [vp, vp, vp, i64, i64, i64, ctypes.c_int32,
+                                           ctypes.c_int32, vp]
+    h.sc_causal_conv_fixed_f32.restype = st
+    h.sc_causal_conv_fixed_f32_ws.argtypes = [vp, vp, vp, i64, i64, i64, ctypes.c_int32,
+                                              ctypes.c_int32, vp, sz, vp]
+    h.sc_causal_conv_fixed_f32_ws.restype = st
+    h.sc_fixed_range_ok.argtypes = [ctypes.c_double, ctypes.c_double, ctypes.c_int32,
+                                    ctypes.c_int32, i64]
+    h.sc_fixed_range_ok.restype = ctypes.c_int
     h.sc_workspace_bytes.argtypes = [st, i64, i64, i64]
     h.sc_workspace_bytes.restype = sz
     h.sc_ntt_range_ok.argtypes = [i64, i64, i64]
@@ -137,6 +150,20 @@ def sc_causal_conv_bwd_ntt_i32(dr, v, g, dv, dg, B, C, L, stream):
 
 def sc_causal_conv_bwd_ex(kind, dr, v, g, dv, dg, B, C, L, opt, ws, ws_bytes, stream):
     return _lib.sc_causal_conv_bwd_ex(kind, dr, v, g, dv, dg, B, C, L, opt, ws, ws_bytes, stream)
+
+
+def sc_causal_conv_fixed_f32(v, g, r, B, C, L, frac_v, frac_g, stream):
+    return _lib.sc_causal_conv_fixed_f32(v, g, r, B, C, L, frac_v, frac_g, stream)
+
+
+def sc_causal_conv_fixed_f32_ws(v, g, r, B, C, L, frac_v, frac_g, ws, ws_bytes, stream):
+    return _lib.sc_causal_conv_fixed_f32_ws(v, g, r, B, C, L, frac_v, frac_g, ws, ws_bytes,
+                                            stream)
+
+
+def sc_fixed_range_ok(max_abs_v, max_abs_g, frac_v, frac_g, L) -> bool:
+    return bool(_lib.sc_fixed_range_ok(float(max_abs_v), float(max_abs_g), int(frac_v),
+                                       int(frac_g), int(L)))
 
 
 def sc_workspace_bytes(kind, B, C, L) -> int:
@@ -272,3 +299,34 @@ def causal_conv_bwd(dr: torch.Tensor, v: torch.Tensor, g: torch.Tensor,
     if st != SC_OK:
         raise SpecConvError(st, "causal_conv_bwd")
     return dv, dg
+
+
+def causal_conv_fixed(v: torch.Tensor, g: torch.Tensor, frac_v: int, frac_g: int,
+                      out: torch.Tensor | None = None, *,
+                      workspace: torch.Tensor | None = None) -> torch.Tensor:
+    """Exactly causal float32 convolution on fixed-point encodings (sc_causal_conv_fixed_f32):
+    r_t = round_f32(sum_{j<=t} round(v_j 2^frac_v) round(g_{t-j} 2^frac_g) 2^-(frac_v+frac_g))
+    along the last axis.  v, g: contiguous float32 tensors on one GPU."""
+    if v.shape != g.shape or v.dtype != torch.float32 or g.dtype != torch.float32:
+        raise ValueError("v and g must be float32 tensors of one shape")
+    if not (v.is_cuda and g.is_cuda) or v.device != g.device:
+        raise ValueError("v and g must be on the same GPU")
+    if not (v.is_contiguous() and g.is_contiguous()):
+        raise ValueError("v and g must be contiguous")
+    out = _out_like(v, out, "out")
+    B, C, L = _shape3(v)
+    with torch.cuda.device(v.device):
+        stream = torch.cuda.current_stream(v.device).cuda_stream
+        if workspace is None:
+            st = _lib.sc_causal_conv_fixed_f32(v.data_ptr(), g.data_ptr(), out.data_ptr(), B, C,
+                                               L, int(frac_v), int(frac_g), stream)
+        else:
+            if not workspace.is_cuda or workspace.device != v.device or \
+                    not workspace.is_contiguous():
+                raise ValueError("workspace must be a contiguous tensor on v's device")
+            st = _lib.sc_causal_conv_fixed_f32_ws(
+                v.data_ptr(), g.data_ptr(), out.data_ptr(), B, C, L, int(frac_v), int(frac_g),
+                workspace.data_ptr(), workspace.numel() * workspace.element_size(), stream)
+    if st != SC_OK:
+        raise SpecConvError(st, "causal_conv_fixed")
+    return out

@@ -26,6 +26,7 @@ constexpr int64_t kMinLFourStep = 2049;  // the four-step split needs M >= 4096
 constexpr int64_t kFourStepChunkBytes = (int64_t)SC_FS_CHUNK_MB << 20;
 constexpr int64_t kMaxLNtt = 4096;
 constexpr int64_t kNttP = 998244353;
+constexpr int32_t kMaxFrac = 64;          // |fixed-point fraction bits| of the exact real kind
 
 sc_status upload(const void* host, size_t bytes, void** dev)
 {
@@ -41,7 +42,7 @@ sc_status upload(const void* host, size_t bytes, void** dev)
 
 struct DeviceState {
     float2* fused_tw = nullptr;   // the float twiddle bank (sc_internal.h)
-    sc::NttTables ntt{};
+    sc::NttTables ntt[3]{};       // primes A, B, C (sc::NTT_PRIMES)
     bool ntt_ready = false;
     std::map<int, sc::FsTw> fs;     // four-step tables by M
 };
@@ -58,9 +59,8 @@ uint64_t powmod(uint64_t b, uint64_t e, uint64_t m)
     return r;
 }
 
-sc_status build_ntt_tables(sc::NttTables* t)
+sc_status build_ntt_tables(sc::NttTables* t, uint64_t p)
 {
-    const uint64_t p = (uint64_t)kNttP;
     std::vector<double> h(2 * (size_t)sc::NTT_BANK_ENTRIES);
     auto put = [&](size_t i, uint64_t w) {
         h[2 * i] = (double)w;
@@ -131,8 +131,10 @@ sc_status device_state(DeviceState** out, bool need_ntt)
         d.fused_tw = (float2*)p;
     }
     if (need_ntt && !d.ntt_ready) {
-        sc_status st = build_ntt_tables(&d.ntt);
-        if (st != SC_OK) return st;
+        for (int k = 0; k < 3; ++k) {
+            sc_status st = build_ntt_tables(&d.ntt[k], sc::NTT_PRIMES[k]);
+            if (st != SC_OK) return st;
+        }
         d.ntt_ready = true;
     }
     *out = &d;
@@ -189,10 +191,13 @@ bool overlaps(const void* a, const void* b, uint64_t bytes)
     return x < y + bytes && y < x + bytes;
 }
 
+bool exact_kind(sc_kind k) { return k == SC_KIND_NTT_I32 || k == SC_KIND_FIXED_F32; }
+
 // Kind and shape checks.  *n receives B*C*L.
 sc_status check_shape(sc_kind kind, int64_t B, int64_t C, int64_t L, int64_t* n)
 {
-    if (kind != SC_KIND_F32 && kind != SC_KIND_BF16 && kind != SC_KIND_NTT_I32)
+    if (kind != SC_KIND_F32 && kind != SC_KIND_BF16 && kind != SC_KIND_NTT_I32 &&
+        kind != SC_KIND_FIXED_F32)
         return SC_ERR_INVALID_ARGUMENT;
     if (B < 0 || C < 0 || L < 0) return SC_ERR_INVALID_ARGUMENT;
     const __int128 total = (__int128)B * (__int128)C * (__int128)L;
@@ -219,7 +224,7 @@ sc_status check_args(sc_kind kind, const void* v, const void* g, const void* r, 
 
 sc_status resolve_path(sc_kind kind, int64_t L, int32_t requested, sc_path* out)
 {
-    const bool fl = kind != SC_KIND_NTT_I32;
+    const bool fl = !exact_kind(kind);
     switch (requested) {
     case SC_PATH_AUTO:
         if (!fl) {
@@ -252,6 +257,9 @@ sc_status resolve_path(sc_kind kind, int64_t L, int32_t requested, sc_path* out)
     }
 }
 
+// scratch of the exact real-valued kind: three int32 residues per output
+size_t fixed_bytes(int64_t n) { return (size_t)n * 3 * sizeof(int32_t); }
+
 // four-step scratch: channels per chunk and bytes needed
 void fourstep_plan(int64_t nch, int64_t L, int64_t* chunk, size_t* bytes)
 {
@@ -278,32 +286,70 @@ sc_status run_jobs(sc_kind kind, const Job* jobs, int njobs, bool rev, int64_t n
                    int64_t C, int64_t L, const sc_options* opt, void* ws, size_t ws_bytes,
                    hipStream_t stream)
 {
-    int32_t req = SC_PATH_AUTO, head = kDefaultHead;
+    int32_t req = SC_PATH_AUTO, head = kDefaultHead, fv = 0, fg = 0;
     if (opt) {
-        for (int i = 0; i < 6; ++i)
+        for (int i = 0; i < 4; ++i)
             if (opt->reserved[i]) return SC_ERR_INVALID_ARGUMENT;
         req = opt->path;
         if (opt->head != -1) {
             if (opt->head < 0 || opt->head > kMaxHead) return SC_ERR_INVALID_ARGUMENT;
             head = (opt->head + 1) & ~1;
         }
+        fv = opt->frac_v;
+        fg = opt->frac_g;
+        if (kind != SC_KIND_FIXED_F32 && (fv || fg)) return SC_ERR_INVALID_ARGUMENT;
+        if (fv < -kMaxFrac || fv > kMaxFrac || fg < -kMaxFrac || fg > kMaxFrac)
+            return SC_ERR_INVALID_ARGUMENT;
     }
+    if (kind == SC_KIND_FIXED_F32 && rev) return SC_ERR_UNSUPPORTED;
     sc_path path;
     sc_status st = resolve_path(kind, L, req, &path);
     if (st != SC_OK) return st;
     if (n == 0) return SC_OK;
     const int64_t nch = B * C;
 
+    // scratch of this path, checked against a caller workspace before any HIP call
+    size_t need = 0;
+    int64_t chunk = 0;
+    if (kind == SC_KIND_FIXED_F32)
+        need = fixed_bytes(n);
+    else if (path == SC_PATH_FOUR_STEP)
+        fourstep_plan(nch, L, &chunk, &need);
+    if (need > 0) {
+        if (ws) {
+            if (ws_bytes < need) return SC_ERR_WORKSPACE;
+            if ((uintptr_t)ws % 256) return SC_ERR_INVALID_ARGUMENT;
+        } else if (ws_bytes) {
+            return SC_ERR_INVALID_ARGUMENT;
+        }
+    }
+
     DeviceState* d = nullptr;
-    st = device_state(&d, kind == SC_KIND_NTT_I32);
+    st = device_state(&d, exact_kind(kind));
     if (st != SC_OK) return st;
 
     hipError_t e = hipSuccess;
+    if (kind == SC_KIND_FIXED_F32) {
+        const int M = (int)std::max<int64_t>(64, next_pow2(L));
+        void* scratch = ws;
+        bool own = false;
+        if (!ws) {
+            if (hipMallocAsync(&scratch, need, stream) != hipSuccess) return SC_ERR_HIP;
+            own = true;
+        }
+        for (int k = 0; k < njobs && e == hipSuccess; ++k)
+            e = sc::launch_fixed((const float*)jobs[k].a, (const float*)jobs[k].b,
+                                 (float*)jobs[k].o, (int32_t*)scratch, nch, (int)L, M, fv, fg,
+                                 d->ntt, stream);
+        if (own && hipFreeAsync(scratch, stream) != hipSuccess && e == hipSuccess)
+            e = hipErrorUnknown;
+        return e == hipSuccess ? SC_OK : SC_ERR_HIP;
+    }
     if (kind == SC_KIND_NTT_I32) {
         const int M = (int)std::max<int64_t>(64, next_pow2(L));
         for (int k = 0; k < njobs && e == hipSuccess; ++k)
             e = sc::launch_ntt((const int32_t*)jobs[k].a, (const int32_t*)jobs[k].b,
-                               (int32_t*)jobs[k].o, nch, (int)L, M, rev, d->ntt, stream);
+                               (int32_t*)jobs[k].o, nch, (int)L, M, rev, d->ntt[0], stream);
         return e == hipSuccess ? SC_OK : SC_ERR_HIP;
     }
     const sc::Store s = kind == SC_KIND_F32 ? sc::Store::F32 : sc::Store::BF16;
@@ -326,16 +372,9 @@ sc_status run_jobs(sc_kind kind, const Job* jobs, int njobs, bool rev, int64_t n
             st = fourstep_tables(*d, M, &tw);
         }
         if (st != SC_OK) return st;
-        int64_t chunk;
-        size_t need;
-        fourstep_plan(nch, L, &chunk, &need);
         void* scratch = ws;
         bool own = false;
-        if (ws) {
-            if (ws_bytes < need) return SC_ERR_WORKSPACE;
-            if ((uintptr_t)ws % 256) return SC_ERR_INVALID_ARGUMENT;
-        } else {
-            if (ws_bytes) return SC_ERR_INVALID_ARGUMENT;
+        if (!ws) {
             if (hipMallocAsync(&scratch, need, stream) != hipSuccess) return SC_ERR_HIP;
             own = true;
         }
@@ -421,6 +460,7 @@ size_t sc_workspace_bytes(sc_kind kind, int64_t B, int64_t C, int64_t L)
         if (check_shape(kind, B, C, L, &n) != SC_OK || n == 0) return 0;
         sc_path path;
         if (resolve_path(kind, L, SC_PATH_AUTO, &path) != SC_OK) return 0;
+        if (kind == SC_KIND_FIXED_F32) return fixed_bytes(n);
         if (path != SC_PATH_FOUR_STEP) return 0;
         int64_t chunk;
         size_t need;
@@ -494,6 +534,44 @@ sc_status sc_causal_conv_bwd_ex(sc_kind kind, const void* dr, const void* v, con
         [&] { return run_bwd(kind, dr, v, g, dv, dg, B, C, L, opt, ws, ws_bytes, stream); });
 }
 
+sc_status sc_causal_conv_fixed_f32(const float* v, const float* g, float* r, int64_t B,
+                                   int64_t C, int64_t L, int32_t frac_v, int32_t frac_g,
+                                   hipStream_t stream)
+{
+    return guarded([&] {
+        sc_options o{SC_PATH_AUTO, -1, frac_v, frac_g, {0, 0, 0, 0}};
+        return run(SC_KIND_FIXED_F32, v, g, r, B, C, L, &o, nullptr, 0, stream);
+    });
+}
+
+sc_status sc_causal_conv_fixed_f32_ws(const float* v, const float* g, float* r, int64_t B,
+                                      int64_t C, int64_t L, int32_t frac_v, int32_t frac_g,
+                                      void* ws, size_t ws_bytes, hipStream_t stream)
+{
+    return guarded([&] {
+        sc_options o{SC_PATH_AUTO, -1, frac_v, frac_g, {0, 0, 0, 0}};
+        return run(SC_KIND_FIXED_F32, v, g, r, B, C, L, &o, ws, ws_bytes, stream);
+    });
+}
+
+int sc_fixed_range_ok(double max_abs_v, double max_abs_g, int32_t frac_v, int32_t frac_g,
+                      int64_t L)
+{
+    if (!(max_abs_v >= 0) || !(max_abs_g >= 0) || L < 0) return 0;   // also rejects NaN
+    if (frac_v < -kMaxFrac || frac_v > kMaxFrac || frac_g < -kMaxFrac || frac_g > kMaxFrac)
+        return 0;
+    // largest encodings: round(x 2^f) <= ceil(x 2^f); each must stay below 2^51
+    const double bv = std::ceil(std::ldexp(max_abs_v, frac_v));
+    const double bg = std::ceil(std::ldexp(max_abs_g, frac_g));
+    if (!(bv < 0x1p51) || !(bg < 0x1p51)) return 0;
+    // L * bv * bg <= (A B C - 1) / 2, in 128-bit integers (bv, bg < 2^51, L < 2^63)
+    const unsigned __int128 P = (unsigned __int128)sc::NTT_PRIMES[0] * sc::NTT_PRIMES[1] *
+                                sc::NTT_PRIMES[2];
+    const unsigned __int128 prod = (unsigned __int128)(uint64_t)bv * (uint64_t)bg;
+    if (prod != 0 && (unsigned __int128)L > ((P - 1) / 2) / prod) return 0;
+    return 1;
+}
+
 int sc_ntt_range_ok(int64_t max_abs_v, int64_t max_abs_g, int64_t L)
 {
     if (max_abs_v < 0 || max_abs_g < 0 || L < 0) return 0;
@@ -513,6 +591,6 @@ const char* sc_status_string(sc_status s)
     }
 }
 
-int sc_version(void) { return 200; }
+int sc_version(void) { return 300; }
 
 }  // extern "C"

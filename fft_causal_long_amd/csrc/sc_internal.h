@@ -44,9 +44,20 @@ struct NttTables {
     double ninv_q[24];
 };
 
-// Exact NTT causal convolution for L <= FUSED_MAX_L, M = max(64, next power of two >= L).
+// The exact paths' primes: A = 998244353 (the exact int32 kind), B = 1004535809 and
+// C = 469762049; all have 2^21 | p - 1 and primitive root 3.
+constexpr uint64_t NTT_PRIMES[3] = {998244353ull, 1004535809ull, 469762049ull};
+
+// Exact NTT causal convolution for L <= FUSED_MAX_L, M = max(64, next power of two >= L),
+// modulo prime A, output lifted to the balanced range.
 hipError_t launch_ntt(const int32_t* v, const int32_t* g, int32_t* r, int64_t nch, int L, int M,
                       bool rev, const NttTables& tables, hipStream_t stream);
+
+// Exact real-valued causal convolution: V = round(v 2^fv), G = round(g 2^fg), the exact
+// integer sum R through primes A, B, C (tables[0..2]) into scratch (3 * nch * L int32), then
+// r = round_f32(R 2^-(fv+fg)).
+hipError_t launch_fixed(const float* v, const float* g, float* r, int32_t* scratch, int64_t nch,
+                        int L, int M, int fv, int fg, const NttTables* tables, hipStream_t stream);
 
 // ---- four-step path (L > FUSED_MAX_L)
 // Longest row transform of the four-step split M = M1 * M2 (M2 <= this, M1 >= 64).

@@ -36,58 +36,86 @@ namespace sc {
 
 namespace ntt {
 
-constexpr double P = 998244353.0;
-constexpr double PINV = 1.0 / 998244353.0;
 constexpr double SHIFT = 6755399441055744.0;   // 1.5 * 2^52: x + SHIFT - SHIFT = round(x), |x| < 2^51
+
+// The NTT primes: p - 1 is divisible by 2^21 (transform lengths up to 2^21 have roots of
+// unity) and 3 is a primitive root.  PrimeA is the exact kind's modulus; the three together
+// carry the exact real-valued path (residues combined by the Chinese remainder theorem).
+struct PrimeA {
+    static constexpr uint64_t p = 998244353ull;    // 119 * 2^23 + 1
+};
+struct PrimeB {
+    static constexpr uint64_t p = 1004535809ull;   // 479 * 2^21 + 1
+};
+struct PrimeC {
+    static constexpr uint64_t p = 469762049ull;    // 7 * 2^26 + 1
+};
+constexpr uint64_t ROOT = 3;
 
 // a constant residue w with w / p rounded to double
 struct W {
     double w, q;
 };
 
+template <class Pr>
 constexpr uint64_t powmod_c(uint64_t b, uint64_t e)
 {
     uint64_t r = 1;
-    b %= 998244353ull;
+    b %= Pr::p;
     while (e) {
-        if (e & 1) r = r * b % 998244353ull;
-        b = b * b % 998244353ull;
+        if (e & 1) r = r * b % Pr::p;
+        b = b * b % Pr::p;
         e >>= 1;
     }
     return r;
 }
 // omega_n^k as a W constant (n | p - 1)
+template <class Pr>
 constexpr W root_c(uint64_t n, uint64_t k)
 {
-    const uint64_t w = powmod_c(powmod_c(3, 998244352ull / n), k);
-    return W{(double)w, (double)w / 998244353.0};
+    const uint64_t w = powmod_c<Pr>(powmod_c<Pr>(ROOT, (Pr::p - 1) / n), k);
+    return W{(double)w, (double)w / (double)Pr::p};
 }
 
 __device__ __forceinline__ double round_int(double x)
 {
     return (x + SHIFT) - SHIFT;
 }
-// a * w mod p, |result| <= 1.5 p
+// a * w mod p, |a| < 2^36, |result| <= 1.5 p
+template <class Pr>
 __device__ __forceinline__ double mulc(double a, W w)
 {
+    constexpr double P = (double)Pr::p;
     const double h = a * w.w;
     const double l = __builtin_fma(a, w.w, -h);
     const double q = __builtin_fma(a, w.q, SHIFT) - SHIFT;
     return __builtin_fma(-q, P, h) + l;
 }
 // a * b mod p for |a|, |b| <= p, |result| <= p
+template <class Pr>
 __device__ __forceinline__ double mulv(double a, double b)
 {
+    constexpr double P = (double)Pr::p, PINV = 1.0 / (double)Pr::p;
     const double h = a * b;
     const double l = __builtin_fma(a, b, -h);
     const double q = __builtin_fma(h, PINV, SHIFT) - SHIFT;
     return __builtin_fma(-q, P, h) + l;
 }
 // a mod p into [-p/2, p/2] (up to one p at the edges), |a| < 2^51
+template <class Pr>
 __device__ __forceinline__ double reduce(double a)
 {
+    constexpr double P = (double)Pr::p, PINV = 1.0 / (double)Pr::p;
     const double q = __builtin_fma(a, PINV, SHIFT) - SHIFT;
     return __builtin_fma(-q, P, a);
+}
+// the balanced representative in [-(p-1)/2, (p-1)/2] of a value with |a| <= 2 p
+template <class Pr>
+__device__ __forceinline__ double balance(double a)
+{
+    constexpr double P = (double)Pr::p, H = 0.5 * ((double)Pr::p - 1.0);
+    a = a > H ? a - P : (a < -H ? a + P : a);
+    return a > H ? a - P : (a < -H ? a + P : a);
 }
 
 // twiddle bank entry i as W (double2 {w, w/p})
@@ -100,83 +128,71 @@ struct Tw {
     }
 };
 
-// in-register DFT_R over Z_p (forward, omega_R), natural order in and out, inputs < 2^33
-template <int R>
-__device__ __forceinline__ void dft(double* a);
-
-template <>
-__device__ __forceinline__ void dft<2>(double* a)
+// in-register DFT_R over Z_p (forward, omega_R), natural order in and out, inputs < 2^33.
+// R = 16 = 4 x 4:  X[4 k1 + k2] = sum_{n1} w4^{n1 k1} w16^{n1 k2} sum_{n2} x[n1 + 4 n2] w4^{n2 k2}
+template <int R, class Pr>
+__device__ __forceinline__ void dft(double* a)
 {
-    const double x = a[0];
-    a[0] = x + a[1];
-    a[1] = x - a[1];
-}
-
-template <>
-__device__ __forceinline__ void dft<4>(double* a)
-{
-    constexpr W w4 = root_c(4, 1);
-    const double t0 = a[0] + a[2], t1 = a[0] - a[2];
-    const double t2 = a[1] + a[3], t3 = mulc(a[1] - a[3], w4);
-    a[0] = t0 + t2;
-    a[2] = t0 - t2;
-    a[1] = t1 + t3;
-    a[3] = t1 - t3;
-}
-
-template <>
-__device__ __forceinline__ void dft<8>(double* a)
-{
-    constexpr W w1 = root_c(8, 1), w2 = root_c(8, 2), w3 = root_c(8, 3);
-    double u[4], t[4];
+    if constexpr (R == 2) {
+        const double x = a[0];
+        a[0] = x + a[1];
+        a[1] = x - a[1];
+    } else if constexpr (R == 4) {
+        constexpr W w4 = root_c<Pr>(4, 1);
+        const double t0 = a[0] + a[2], t1 = a[0] - a[2];
+        const double t2 = a[1] + a[3], t3 = mulc<Pr>(a[1] - a[3], w4);
+        a[0] = t0 + t2;
+        a[2] = t0 - t2;
+        a[1] = t1 + t3;
+        a[3] = t1 - t3;
+    } else if constexpr (R == 8) {
+        constexpr W w1 = root_c<Pr>(8, 1), w2 = root_c<Pr>(8, 2), w3 = root_c<Pr>(8, 3);
+        double u[4], t[4];
 #pragma unroll
-    for (int n = 0; n < 4; ++n) {
-        u[n] = a[n] + a[n + 4];
-        t[n] = a[n] - a[n + 4];
+        for (int n = 0; n < 4; ++n) {
+            u[n] = a[n] + a[n + 4];
+            t[n] = a[n] - a[n + 4];
+        }
+        t[1] = mulc<Pr>(t[1], w1);
+        t[2] = mulc<Pr>(t[2], w2);
+        t[3] = mulc<Pr>(t[3], w3);
+        dft<4, Pr>(u);
+        dft<4, Pr>(t);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            a[2 * k] = u[k];
+            a[2 * k + 1] = t[k];
+        }
+    } else {
+        static_assert(R == 16, "radix 2, 4, 8 or 16");
+        double c[4];
+#pragma unroll
+        for (int n1 = 0; n1 < 4; ++n1) {
+            c[0] = a[n1]; c[1] = a[n1 + 4]; c[2] = a[n1 + 8]; c[3] = a[n1 + 12];
+            dft<4, Pr>(c);
+            a[n1] = c[0]; a[n1 + 4] = c[1]; a[n1 + 8] = c[2]; a[n1 + 12] = c[3];
+        }
+        // a[n1 + 4 k2] *= w16^{n1 k2}
+        a[5] = mulc<Pr>(a[5], root_c<Pr>(16, 1));
+        a[9] = mulc<Pr>(a[9], root_c<Pr>(16, 2));
+        a[13] = mulc<Pr>(a[13], root_c<Pr>(16, 3));
+        a[6] = mulc<Pr>(a[6], root_c<Pr>(16, 2));
+        a[10] = mulc<Pr>(a[10], root_c<Pr>(16, 4));
+        a[14] = mulc<Pr>(a[14], root_c<Pr>(16, 6));
+        a[7] = mulc<Pr>(a[7], root_c<Pr>(16, 3));
+        a[11] = mulc<Pr>(a[11], root_c<Pr>(16, 6));
+        a[15] = mulc<Pr>(a[15], root_c<Pr>(16, 9));
+#pragma unroll
+        for (int k2 = 0; k2 < 4; ++k2) dft<4, Pr>(a + 4 * k2);
+        // a[4 k2 + k1] = X[4 k1 + k2]: transpose to natural order
+        double t;
+        t = a[1]; a[1] = a[4]; a[4] = t;
+        t = a[2]; a[2] = a[8]; a[8] = t;
+        t = a[3]; a[3] = a[12]; a[12] = t;
+        t = a[6]; a[6] = a[9]; a[9] = t;
+        t = a[7]; a[7] = a[13]; a[13] = t;
+        t = a[11]; a[11] = a[14]; a[14] = t;
     }
-    t[1] = mulc(t[1], w1);
-    t[2] = mulc(t[2], w2);
-    t[3] = mulc(t[3], w3);
-    dft<4>(u);
-    dft<4>(t);
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-        a[2 * k] = u[k];
-        a[2 * k + 1] = t[k];
-    }
-}
-
-// 16 = 4 x 4:  X[4 k1 + k2] = sum_{n1} w4^{n1 k1} w16^{n1 k2} sum_{n2} x[n1 + 4 n2] w4^{n2 k2}
-template <>
-__device__ __forceinline__ void dft<16>(double* a)
-{
-    double c[4];
-#pragma unroll
-    for (int n1 = 0; n1 < 4; ++n1) {
-        c[0] = a[n1]; c[1] = a[n1 + 4]; c[2] = a[n1 + 8]; c[3] = a[n1 + 12];
-        dft<4>(c);
-        a[n1] = c[0]; a[n1 + 4] = c[1]; a[n1 + 8] = c[2]; a[n1 + 12] = c[3];
-    }
-    // a[n1 + 4 k2] *= w16^{n1 k2}
-    a[5] = mulc(a[5], root_c(16, 1));
-    a[9] = mulc(a[9], root_c(16, 2));
-    a[13] = mulc(a[13], root_c(16, 3));
-    a[6] = mulc(a[6], root_c(16, 2));
-    a[10] = mulc(a[10], root_c(16, 4));
-    a[14] = mulc(a[14], root_c(16, 6));
-    a[7] = mulc(a[7], root_c(16, 3));
-    a[11] = mulc(a[11], root_c(16, 6));
-    a[15] = mulc(a[15], root_c(16, 9));
-#pragma unroll
-    for (int k2 = 0; k2 < 4; ++k2) dft<4>(a + 4 * k2);
-    // a[4 k2 + k1] = X[4 k1 + k2]: transpose to natural order
-    double t;
-    t = a[1]; a[1] = a[4]; a[4] = t;
-    t = a[2]; a[2] = a[8]; a[8] = t;
-    t = a[3]; a[3] = a[12]; a[12] = t;
-    t = a[6]; a[6] = a[9]; a[9] = t;
-    t = a[7]; a[7] = a[13]; a[13] = t;
-    t = a[11]; a[11] = a[14]; a[14] = t;
 }
 
 __device__ __forceinline__ int lds_pad(int a) { return a + (a >> 4); }
@@ -191,7 +207,7 @@ __device__ __forceinline__ int reg_off(int tau, int q)
 // One Stockham DIF pass (index scheme as in the float kernel) over NA arrays sharing the
 // twiddles.  Passes with twiddles are radix 16 with one item per thread; their outputs are
 // reduced below 2^31 (k2 > 0 by the twiddle product, k2 = 0 explicitly) and stored as int32.
-template <int M, int R, int S, int NA>
+template <int M, int R, int S, int NA, class Pr>
 __device__ __forceinline__ void pass(double (&x)[NA][16], int32_t* __restrict__ buf0,
                                      int32_t* __restrict__ buf1, int tau, const Tw& tw)
 {
@@ -206,11 +222,12 @@ __device__ __forceinline__ void pass(double (&x)[NA][16], int32_t* __restrict__ 
         const int base = S == 1 ? 17 * n1 : (s + (s >> 4)) + 16 * n1 * STEP;
 #pragma unroll
         for (int a = 0; a < NA; ++a) {
-            dft<16>(x[a]);
+            dft<16, Pr>(x[a]);
             int32_t* buf = a == 0 ? buf0 : buf1;
-            buf[base] = (int32_t)reduce(x[a][0]);
+            buf[base] = (int32_t)reduce<Pr>(x[a][0]);
 #pragma unroll
-            for (int k2 = 1; k2 < 16; ++k2) buf[base + k2 * STEP] = (int32_t)mulc(x[a][k2], w[k2]);
+            for (int k2 = 1; k2 < 16; ++k2)
+                buf[base + k2 * STEP] = (int32_t)mulc<Pr>(x[a][k2], w[k2]);
         }
     } else {
 #pragma unroll
@@ -220,7 +237,7 @@ __device__ __forceinline__ void pass(double (&x)[NA][16], int32_t* __restrict__ 
                 double b[R];
 #pragma unroll
                 for (int n2 = 0; n2 < R; ++n2) b[n2] = x[a][q + NB * n2];
-                dft<R>(b);
+                dft<R, Pr>(b);
 #pragma unroll
                 for (int k2 = 0; k2 < R; ++k2) x[a][q + NB * k2] = b[k2];
             }
@@ -228,13 +245,13 @@ __device__ __forceinline__ void pass(double (&x)[NA][16], int32_t* __restrict__ 
     }
 }
 
-template <int M, int NA, int S = 1>
+template <int M, int NA, class Pr, int S = 1>
 __device__ __forceinline__ void passes(double (&x)[NA][16], int32_t* __restrict__ buf0,
                                        int32_t* __restrict__ buf1, int tau, const Tw& tw)
 {
     constexpr int TB = M / 16, Q = M / S, R = Q >= 16 ? 16 : Q;
     if constexpr (Q / R > 1) {
-        pass<M, R, S, NA>(x, buf0, buf1, tau, tw);
+        pass<M, R, S, NA, Pr>(x, buf0, buf1, tau, tw);
         __syncthreads();
 #pragma unroll
         for (int q = 0; q < 16; ++q) {
@@ -242,9 +259,9 @@ __device__ __forceinline__ void passes(double (&x)[NA][16], int32_t* __restrict_
             if constexpr (NA > 1) x[1][q] = (double)buf1[reg_off<TB>(tau, q)];
         }
         __syncthreads();
-        passes<M, NA, S * R>(x, buf0, buf1, tau, tw);
+        passes<M, NA, Pr, S * R>(x, buf0, buf1, tau, tw);
     } else {
-        pass<M, R, S, NA>(x, buf0, buf1, tau, tw);
+        pass<M, R, S, NA, Pr>(x, buf0, buf1, tau, tw);
     }
 }
 
@@ -252,12 +269,15 @@ __device__ __forceinline__ void passes(double (&x)[NA][16], int32_t* __restrict_
 
 // REV (the gradient kernels): the first input is read reversed and the output is written
 // reversed: rev(causal(rev(dr), b))_j = sum_{t>=j} dr_t b_{t-j}.
-template <int M, bool REV>
-__global__ __launch_bounds__(512, 4) void ntt_conv_kernel(const int32_t* __restrict__ v,
-                                                       const int32_t* __restrict__ g,
+// FIX: float32 inputs encoded as integers round(v 2^fv), round(g 2^fg) (nearest, ties to
+// even; sv = 2^fv, sg = 2^fg, |v sv|, |g sg| < 2^51) instead of int32 inputs.
+template <int M, bool REV, class Pr, bool FIX>
+__global__ __launch_bounds__(512, 4) void ntt_conv_kernel(const void* __restrict__ v,
+                                                       const void* __restrict__ g,
                                                        int32_t* __restrict__ r, int64_t nch,
                                                        int L, const double* __restrict__ bank,
-                                                       double ninv, double ninv_q)
+                                                       double ninv, double ninv_q, double sv,
+                                                       double sg)
 {
     using namespace ntt;
     static_assert(M >= 64 && M <= 4096, "fused NTT handles 64 <= M <= 4096");
@@ -272,8 +292,9 @@ __global__ __launch_bounds__(512, 4) void ntt_conv_kernel(const int32_t* __restr
     const int cl = unit >> 1, beta = unit & 1;
     const int64_t ch0 = (int64_t)blockIdx.x * CPW;
     const int nvalid = (int)((nch - ch0) < CPW ? (nch - ch0) : CPW);
-    const Span vs = make_span(v, ch0 * L, (int64_t)nvalid * L);
-    const Span gs = make_span(g, ch0 * L, (int64_t)nvalid * L);
+    // both input kinds have 4-byte elements
+    const Span vs = make_span((const int32_t*)v, ch0 * L, (int64_t)nvalid * L);
+    const Span gs = make_span((const int32_t*)g, ch0 * L, (int64_t)nvalid * L);
     const Span rs = make_span(r, ch0 * L, (int64_t)nvalid * L);
     int32_t* bv = lds + unit * 2 * REG;
     int32_t* bg = bv + REG;
@@ -289,28 +310,37 @@ __global__ __launch_bounds__(512, 4) void ntt_conv_kernel(const int32_t* __restr
         const bool in = L == M || n < L;
         const uint32_t ob = in ? (uint32_t)(cbase + n) * 4u : 0x80000000u;
         const uint32_t oa = in ? (uint32_t)(cbase + (REV ? L - 1 - n : n)) * 4u : 0x80000000u;
-        double a = (double)(int32_t)__builtin_amdgcn_raw_buffer_load_b32(vs.rs, (int)oa, 0, 0);
-        double b = (double)(int32_t)__builtin_amdgcn_raw_buffer_load_b32(gs.rs, (int)ob, 0, 0);
+        const uint32_t wa = __builtin_amdgcn_raw_buffer_load_b32(vs.rs, (int)oa, 0, 0);
+        const uint32_t wb = __builtin_amdgcn_raw_buffer_load_b32(gs.rs, (int)ob, 0, 0);
+        double a, b;
+        if constexpr (FIX) {
+            // exact: a float times a power of two, rounded to an integer, reduced mod p
+            a = reduce<Pr>(round_int((double)__uint_as_float(wa) * sv));
+            b = reduce<Pr>(round_int((double)__uint_as_float(wb) * sg));
+        } else {
+            a = (double)(int32_t)wa;
+            b = (double)(int32_t)wb;
+        }
         if (beta) {
             const W w = tw.at(n * (NTT_TW_N / N), 0);
-            a = mulc(a, w);
-            b = mulc(b, w);
+            a = mulc<Pr>(a, w);
+            b = mulc<Pr>(b, w);
         }
         x[0][q] = a;
         x[1][q] = b;
     }
 
     // 2. V, G = NTT_M(.) in natural order (values below 2^36)
-    passes<M, 2>(x, bv, bg, tau, tw);
+    passes<M, 2, Pr>(x, bv, bg, tau, tw);
 
     // 3. X = V * (G N^{-1})
     double y[1][16];
 #pragma unroll
     for (int q = 0; q < 16; ++q)
-        y[0][q] = mulv(reduce(x[0][q]), reduce(mulc(x[1][q], W{ninv, ninv_q})));
+        y[0][q] = mulv<Pr>(reduce<Pr>(x[0][q]), reduce<Pr>(mulc<Pr>(x[1][q], W{ninv, ninv_q})));
 
     // 4. f = NTT_M(X): e^beta_n = f_{(M - n) mod M}
-    passes<M, 1>(y, bv, bv, tau, tw);
+    passes<M, 1, Pr>(y, bv, bv, tau, tw);
 
     // 5. register q of thread tau holds e^beta at n = (M - tau - TB q) mod M.
     //    x_n = e^0_n + omega_N^{-n} e^1_n: branch 0 finishes q < 8, branch 1 q >= 8, each
@@ -321,8 +351,8 @@ __global__ __launch_bounds__(512, 4) void ntt_conv_kernel(const int32_t* __restr
     for (int q = 0; q < 16; ++q) {
         const int n = (M - tau - TB * q) & (M - 1);
         // omega_N^{-n} = omega_N^{N - n}
-        own[q] = beta ? mulc(y[0][q], tw.at(((N - n) & (N - 1)) * (NTT_TW_N / N), 0))
-                      : reduce(y[0][q]);
+        own[q] = beta ? mulc<Pr>(y[0][q], tw.at(((N - n) & (N - 1)) * (NTT_TW_N / N), 0))
+                      : reduce<Pr>(y[0][q]);
         if ((q < 8) == (beta == 1)) xch[reg_off<TB>(tau, q)] = (int32_t)own[q];
     }
     __syncthreads();
@@ -331,37 +361,101 @@ __global__ __launch_bounds__(512, 4) void ntt_conv_kernel(const int32_t* __restr
         if ((q < 8) != (beta == 0)) continue;
         const int n = (M - tau - TB * q) & (M - 1);
         if (n >= L) continue;
-        double s = reduce(own[q] + (double)xch[reg_off<TB>(tau, q)]);   // |s| <= p/2 + p
-        s = s > 0.5 * (P - 1.0) ? s - P : (s < -0.5 * (P - 1.0) ? s + P : s);
+        const double s = balance<Pr>(reduce<Pr>(own[q] + (double)xch[reg_off<TB>(tau, q)]));
         __builtin_amdgcn_raw_buffer_store_b32((uint32_t)(int32_t)s, rs.rs,
                                               (cbase + (REV ? L - 1 - n : n)) * 4, 0, 0);
     }
 }
 
-template <int M, bool REV>
-static hipError_t launch_ntt_m(const int32_t* v, const int32_t* g, int32_t* r, int64_t nch,
-                               int L, const NttTables& tb, hipStream_t stream)
+// ---------------------------------------------------------------- Chinese remainder decode
+
+namespace ntt {
+
+// constants of Garner's algorithm for the primes A, B, C (as residues with w/p)
+template <class Pr>
+constexpr W wconst(uint64_t w)
+{
+    return W{(double)(w % Pr::p), (double)(w % Pr::p) / (double)Pr::p};
+}
+constexpr uint64_t PA = PrimeA::p, PB = PrimeB::p, PC = PrimeC::p;
+constexpr W INV_A_MOD_B = wconst<PrimeB>(powmod_c<PrimeB>(PA % PB, PB - 2));
+constexpr W A_MOD_C = wconst<PrimeC>(PA % PC);
+constexpr W INV_AB_MOD_C = wconst<PrimeC>(powmod_c<PrimeC>((PA % PC) * (PB % PC) % PC, PC - 2));
+
+// The float32 nearest to m 2^-F (m > 0, m < 2^127), ties to even, subnormals included.
+__device__ __forceinline__ float rne_scaled(unsigned __int128 m, int F)
+{
+    const uint64_t hi = (uint64_t)(m >> 64), lo = (uint64_t)m;
+    const int b = hi ? 128 - __builtin_clzll(hi) : 64 - __builtin_clzll(lo);   // bit length
+    const int e = b - 1 - F;                       // m 2^-F lies in [2^e, 2^(e+1))
+    const int qexp = e - 23 > -149 ? e - 23 : -149; // spacing of float32 numbers there
+    const int sh = F + qexp;                       // keep m / 2^sh, rounded to an integer
+    uint64_t mant;
+    if (sh <= 0) {
+        mant = lo << (-sh);                        // here m < 2^24 and -sh <= 23: exact
+    } else if (sh >= 127) {
+        mant = 0;                                  // m < 2^(sh-1): below half a unit
+    } else {
+        mant = (uint64_t)(m >> sh);
+        const unsigned __int128 rem = m - ((unsigned __int128)mant << sh);
+        const unsigned __int128 half = (unsigned __int128)1 << (sh - 1);
+        if (rem > half || (rem == half && (mant & 1))) ++mant;
+    }
+    return ldexpf((float)mant, qexp);              // mant <= 2^24: exact (or inf past the range)
+}
+
+}  // namespace ntt
+
+// r = round_f32(R 2^-F) where R is the integer with the balanced residues sa, sb, sc modulo
+// the primes A, B, C and |R| <= (A B C - 1) / 2.
+__global__ void crt_decode_kernel(const int32_t* __restrict__ sa, const int32_t* __restrict__ sb,
+                                  const int32_t* __restrict__ sc, float* __restrict__ r,
+                                  int64_t n, int F)
+{
+    using namespace ntt;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
+         i += (int64_t)gridDim.x * blockDim.x) {
+        const double a0 = (double)sa[i];
+        const double a1 = balance<PrimeB>(mulc<PrimeB>((double)sb[i] - a0, INV_A_MOD_B));
+        const double t2 = (double)sc[i] - a0 - mulc<PrimeC>(a1, A_MOD_C);
+        const double a2 = balance<PrimeC>(mulc<PrimeC>(t2, INV_AB_MOD_C));
+        // R = a0 + a1 A + a2 A B, every digit balanced, so |R| <= (A B C - 1) / 2
+        const __int128 R = (__int128)(int64_t)a2 * (__int128)(PA * PB) +
+                           (__int128)((int64_t)a1 * (int64_t)PA + (int64_t)a0);
+        float out = 0.f;
+        if (R != 0) {
+            const bool neg = R < 0;
+            out = rne_scaled(neg ? (unsigned __int128)(-R) : (unsigned __int128)R, F);
+            if (neg) out = -out;
+        }
+        r[i] = out;
+    }
+}
+
+template <int M, bool REV, class Pr, bool FIX>
+static hipError_t launch_ntt_m(const void* v, const void* g, int32_t* r, int64_t nch, int L,
+                               const NttTables& tb, double sv, double sg, hipStream_t stream)
 {
     constexpr int CPW = (512 / (M / 16)) / 2;
     const int64_t blocks = (nch + CPW - 1) / CPW;
     const int lg = __builtin_ctz((unsigned)(2 * M));
-    hipLaunchKernelGGL((ntt_conv_kernel<M, REV>), dim3((unsigned)blocks), dim3(512), 0, stream, v, g, r,
-                       nch, L, tb.bank, tb.ninv[lg], tb.ninv_q[lg]);
+    hipLaunchKernelGGL((ntt_conv_kernel<M, REV, Pr, FIX>), dim3((unsigned)blocks), dim3(512), 0,
+                       stream, v, g, r, nch, L, tb.bank, tb.ninv[lg], tb.ninv_q[lg], sv, sg);
     return hipGetLastError();
 }
 
-template <bool REV>
-static hipError_t launch_ntt_rev(const int32_t* v, const int32_t* g, int32_t* r, int64_t nch,
-                                 int L, int M, const NttTables& tb, hipStream_t s)
+template <bool REV, class Pr, bool FIX>
+static hipError_t launch_ntt_any(const void* v, const void* g, int32_t* r, int64_t nch, int L,
+                                 int M, const NttTables& tb, double sv, double sg, hipStream_t s)
 {
     switch (M) {
-    case 64: return launch_ntt_m<64, REV>(v, g, r, nch, L, tb, s);
-    case 128: return launch_ntt_m<128, REV>(v, g, r, nch, L, tb, s);
-    case 256: return launch_ntt_m<256, REV>(v, g, r, nch, L, tb, s);
-    case 512: return launch_ntt_m<512, REV>(v, g, r, nch, L, tb, s);
-    case 1024: return launch_ntt_m<1024, REV>(v, g, r, nch, L, tb, s);
-    case 2048: return launch_ntt_m<2048, REV>(v, g, r, nch, L, tb, s);
-    case 4096: return launch_ntt_m<4096, REV>(v, g, r, nch, L, tb, s);
+    case 64: return launch_ntt_m<64, REV, Pr, FIX>(v, g, r, nch, L, tb, sv, sg, s);
+    case 128: return launch_ntt_m<128, REV, Pr, FIX>(v, g, r, nch, L, tb, sv, sg, s);
+    case 256: return launch_ntt_m<256, REV, Pr, FIX>(v, g, r, nch, L, tb, sv, sg, s);
+    case 512: return launch_ntt_m<512, REV, Pr, FIX>(v, g, r, nch, L, tb, sv, sg, s);
+    case 1024: return launch_ntt_m<1024, REV, Pr, FIX>(v, g, r, nch, L, tb, sv, sg, s);
+    case 2048: return launch_ntt_m<2048, REV, Pr, FIX>(v, g, r, nch, L, tb, sv, sg, s);
+    case 4096: return launch_ntt_m<4096, REV, Pr, FIX>(v, g, r, nch, L, tb, sv, sg, s);
     default: return hipErrorInvalidValue;
     }
 }
@@ -369,8 +463,30 @@ static hipError_t launch_ntt_rev(const int32_t* v, const int32_t* g, int32_t* r,
 hipError_t launch_ntt(const int32_t* v, const int32_t* g, int32_t* r, int64_t nch, int L, int M,
                       bool rev, const NttTables& tb, hipStream_t s)
 {
-    return rev ? launch_ntt_rev<true>(v, g, r, nch, L, M, tb, s)
-               : launch_ntt_rev<false>(v, g, r, nch, L, M, tb, s);
+    return rev ? launch_ntt_any<true, ntt::PrimeA, false>(v, g, r, nch, L, M, tb, 0.0, 0.0, s)
+               : launch_ntt_any<false, ntt::PrimeA, false>(v, g, r, nch, L, M, tb, 0.0, 0.0, s);
+}
+
+hipError_t launch_fixed(const float* v, const float* g, float* r, int32_t* scratch, int64_t nch,
+                        int L, int M, int fv, int fg, const NttTables* tb, hipStream_t s)
+{
+    const int64_t n = nch * (int64_t)L;
+    const double sv = ldexp(1.0, fv), sg = ldexp(1.0, fg);
+    hipError_t e = launch_ntt_any<false, ntt::PrimeA, true>(v, g, scratch, nch, L, M, tb[0], sv,
+                                                           sg, s);
+    if (e == hipSuccess)
+        e = launch_ntt_any<false, ntt::PrimeB, true>(v, g, scratch + n, nch, L, M, tb[1], sv, sg,
+                                                     s);
+    if (e == hipSuccess)
+        e = launch_ntt_any<false, ntt::PrimeC, true>(v, g, scratch + 2 * n, nch, L, M, tb[2], sv,
+                                                     sg, s);
+    if (e != hipSuccess) return e;
+    const int threads = 256;
+    int64_t blocks = (n + threads - 1) / threads;
+    if (blocks > 65536) blocks = 65536;
+    hipLaunchKernelGGL(crt_decode_kernel, dim3((unsigned)blocks), dim3(threads), 0, s, scratch,
+                       scratch + n, scratch + 2 * n, r, n, fv + fg);
+    return hipGetLastError();
 }
 
 }  // namespace sc

@@ -66,9 +66,11 @@ typedef enum sc_status {
 } sc_status;
 
 typedef enum sc_kind {
-    SC_KIND_F32 = 0,     /* float32 storage, float32 arithmetic                    */
-    SC_KIND_BF16 = 1,    /* bfloat16 storage, float32 arithmetic                   */
-    SC_KIND_NTT_I32 = 2  /* int32 storage, exact arithmetic in Z_p, p = 998244353   */
+    SC_KIND_F32 = 0,      /* float32 storage, float32 arithmetic                    */
+    SC_KIND_BF16 = 1,     /* bfloat16 storage, float32 arithmetic                   */
+    SC_KIND_NTT_I32 = 2,  /* int32 storage, exact arithmetic in Z_p, p = 998244353   */
+    SC_KIND_FIXED_F32 = 3 /* float32 storage, exact arithmetic on fixed-point
+                             encodings (see sc_causal_conv_fixed_f32)               */
 } sc_kind;
 
 typedef enum sc_path {
@@ -85,7 +87,10 @@ typedef struct sc_options {
     int32_t head;      /* float kinds: outputs t < head are computed by direct fp32
                           summation instead of the transform.  -1 = default (32);
                           0 disables; odd values are rounded up to even; at most 64.  */
-    int32_t reserved[6]; /* must be zero */
+    int32_t frac_v;    /* SC_KIND_FIXED_F32: fraction bits fv of v's encoding, in
+                          [-64, 64]; must be 0 for the other kinds                   */
+    int32_t frac_g;    /* likewise fg for g                                          */
+    int32_t reserved[4]; /* must be zero */
 } sc_options;
 
 /*
@@ -124,6 +129,42 @@ sc_status sc_causal_conv_ntt_i32(const int32_t* v, const int32_t* g, int32_t* r,
                                  int64_t C, int64_t L, hipStream_t stream);
 
 /*
+ * sc_causal_conv_fixed_f32 -- exactly causal convolution of float32 data ("Catastrophic
+ *   Token Leakage ...", abstract: a number-theoretic FFT on integers leaks no future token;
+ *   here real activations reach the integers through a fixed-point encoding whose scales
+ *   the caller fixes, so no scale depends on the data):
+ *       V_j = round(v_j 2^frac_v),  G_j = round(g_j 2^frac_g)     (nearest, ties to even)
+ *       R_t = sum_{j<=t} V_j G_{t-j}                              (exact integer)
+ *       r_t = R_t 2^-(frac_v + frac_g) rounded once to float32    (nearest, ties to even,
+ *                                                                  subnormals included)
+ *   R_t is computed exactly with the pad-2L recipe modulo three primes (998244353,
+ *   1004535809, 469762049) and the Chinese remainder theorem, so output t depends on
+ *   v_0..v_t and g_0..g_t alone, bit for bit, and equals the definition above whenever
+ *   |V_j|, |G_j| < 2^51 and |R_t| <= (p_A p_B p_C - 1) / 2 (about 2^87.6): a caller
+ *   precondition, checked from bounds by sc_fixed_range_ok.  Accuracy against the real sum:
+ *   |r_t - sum v_j g_{t-j}| <= 2^-(frac_v+1) sum_j |g_j| + 2^-(frac_g+1) sum_j |v_j| + (one
+ *   float32 rounding) -- e.g. frac_v = frac_g = 24 for activations of magnitude below 8.
+ *   frac_v, frac_g in [-64, 64].  Largest L: 4096.  Scratch: 12 bytes per output
+ *   (sc_workspace_bytes(SC_KIND_FIXED_F32, ...)), allocated stream-ordered by this call;
+ *   the _ws variant takes it from the caller.  Gradients are not offered for this kind
+ *   (SC_ERR_UNSUPPORTED from sc_causal_conv_bwd_ex).
+ */
+sc_status sc_causal_conv_fixed_f32(const float* v, const float* g, float* r, int64_t B,
+                                   int64_t C, int64_t L, int32_t frac_v, int32_t frac_g,
+                                   hipStream_t stream);
+sc_status sc_causal_conv_fixed_f32_ws(const float* v, const float* g, float* r, int64_t B,
+                                      int64_t C, int64_t L, int32_t frac_v, int32_t frac_g,
+                                      void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * sc_fixed_range_ok -- 1 if |v_j| <= max_abs_v and |g_j| <= max_abs_g guarantee the
+ *   preconditions of sc_causal_conv_fixed_f32 for these fraction bits and L (encodings below
+ *   2^51, L * max|V| * max|G| <= (p_A p_B p_C - 1) / 2); 0 otherwise.  Host only.
+ */
+int sc_fixed_range_ok(double max_abs_v, double max_abs_g, int32_t frac_v, int32_t frac_g,
+                      int64_t L);
+
+/*
  * sc_workspace_bytes -- device scratch bytes a call of this kind and shape needs
  *   (0 when the chosen path needs none, e.g. the fused path).  Returns 0 for invalid
  *   arguments as well.
@@ -149,7 +190,8 @@ sc_status sc_causal_conv_ntt_i32_ws(const int32_t* v, const int32_t* g, int32_t*
  * sc_causal_conv_ex -- any kind, with options (opt may be null = defaults) and an optional
  *   caller workspace (ws null and ws_bytes 0: allocate stream-ordered when needed).
  *   v, g, r point to elements of the kind's storage type.  A path that cannot serve the
- *   kind and L -> SC_ERR_UNSUPPORTED; nonzero reserved fields -> SC_ERR_INVALID_ARGUMENT.
+ *   kind and L -> SC_ERR_UNSUPPORTED; nonzero reserved fields, or nonzero frac_v/frac_g for
+ *   a kind other than SC_KIND_FIXED_F32 -> SC_ERR_INVALID_ARGUMENT.
  */
 sc_status sc_causal_conv_ex(sc_kind kind, const void* v, const void* g, void* r, int64_t B,
                             int64_t C, int64_t L, const sc_options* opt, void* ws,
@@ -203,7 +245,7 @@ int sc_ntt_range_ok(int64_t max_abs_v, int64_t max_abs_g, int64_t L);
 /* Human-readable name of a status code (static storage).  Host only. */
 const char* sc_status_string(sc_status s);
 
-/* Library version: major * 10000 + minor * 100 + patch (this header: 200).  Host only. */
+/* Library version: major * 10000 + minor * 100 + patch (this header: 300).  Host only. */
 int sc_version(void);
 
 #ifdef __cplusplus

@@ -180,3 +180,40 @@ def test_bwd_unsupported_and_options(sc):
                                    None) == INVALID
     assert h.sc_causal_conv_bwd_ex(5, A, B_, C_, D_, E_, 1, 1, 64, None, None, 0, None) == INVALID
     assert sc.sc_version() >= 200
+
+
+def test_fixed_kind_host_checks(sc):
+    h = sc.lib()
+    INVALID, UNSUP = sc.SC_ERR_INVALID_ARGUMENT, sc.SC_ERR_UNSUPPORTED
+    f = h.sc_causal_conv_fixed_f32
+    assert f(A, B_, C_, 1, 1, 64, 65, 0, None) == INVALID            # fraction bits in [-64, 64]
+    assert f(A, B_, C_, 1, 1, 64, 0, -65, None) == INVALID
+    assert f(A, B_, C_, 1, 1, 4097, 20, 20, None) == UNSUP            # exact paths: L <= 4096
+    assert f(A, B_, A, 1, 1, 64, 20, 20, None) == INVALID             # r aliases v
+    assert f(None, None, None, 0, 1, 64, 20, 20, None) == sc.SC_OK
+    # fraction bits are only meaningful for the fixed kind
+    opt = sc.sc_options(0, -1, 3, 0)
+    assert h.sc_causal_conv_ex(0, A, B_, C_, 1, 1, 64, ctypes.byref(opt), None, 0, None) == INVALID
+    # no gradients for the fixed kind
+    assert h.sc_causal_conv_bwd_ex(3, A, B_, C_, D_, E_, 1, 1, 64, None, None, 0, None) == UNSUP
+    # scratch: three int32 residues per output; a short caller workspace is refused
+    assert sc.sc_workspace_bytes(sc.KIND_FIXED_F32, 2, 3, 100) == 12 * 600
+    assert sc.sc_workspace_bytes(sc.KIND_FIXED_F32, 1, 1, 5000) == 0
+    assert h.sc_causal_conv_fixed_f32_ws(A, B_, C_, 1, 1, 64, 8, 8, D_, 12 * 64 - 4, None) == \
+        sc.SC_ERR_WORKSPACE
+
+
+def test_fixed_range_helper(sc):
+    ok = sc.sc_fixed_range_ok
+    assert ok(8.0, 1.0, 24, 24, 4096)             # 4096 * 2^27 * 2^24 = 2^63
+    assert not ok(8.0, 1.0, 40, 40, 4096)         # 2^12 * 2^43 * 2^40 > 2^87.6
+    assert not ok(1.0, 1.0, 51, 0, 1)             # an encoding reaches 2^51
+    assert ok(1.0, 1.0, 50, 0, 1)
+    assert not ok(float("nan"), 1.0, 0, 0, 1)
+    assert not ok(1.0, 1.0, 65, 0, 1)
+    assert ok(0.0, 0.0, 64, 64, 4096)
+    # the boundary: L * 2^43 * 2^43 against (P - 1) / 2 with P ~ 2^88.6
+    P = 998244353 * 1004535809 * 469762049
+    L = ((P - 1) // 2) // (2 ** 86)
+    assert ok(2.0 ** 43, 2.0 ** 43, 0, 0, L)
+    assert not ok(2.0 ** 43, 2.0 ** 43, 0, 0, L + 1)
