@@ -6,7 +6,8 @@ One step = one call of the library's hot path over one batch of synthetic input 
 default workload, sc_causal_conv_bf16 at B=8, C=1024, L=4096: load v and g, pad-to-2L FFT,
 spectral product, inverse FFT, truncation, direct head, store r -- a single kernel).
 After the timed region, the gradient call of the same workload (dv, dg from dr, v, g) is
-timed the same way and reported in the `bwd` object (skip with --no-bwd).
+timed the same way and reported in the `bwd` object (skip with --no-bwd), and the exactly
+causal real-valued call on the same inputs in the `fixed` object (skip with --no-fixed).
 Inputs are resident in HBM before the timed region.  Several copies of the buffers are
 rotated so that the 256 MB last-level cache cannot hold a step's working set.
 
@@ -119,17 +120,22 @@ def record_traffic(w, fetch_dir: str, write_dir: str) -> dict:
     return rec
 
 
+FIXED_FRAC = 24   # fraction bits of both encodings in the exact real-valued measurements
+
+
 def leakage_probe(sc, torch, dev, channels: int = 16) -> dict:
     """Future-token leakage max_{t<s} |r'_t - r_t| of the float path (fp32, L = 4096,
-    Medium-shaped inputs) and of the exact path (L = 4096, integer inputs): v_s is changed
-    at 8 seeded positions s, the original and the perturbed rows run in one launch."""
+    Medium-shaped inputs), of the exact real-valued path on the same inputs, and of the
+    exact integer path (L = 4096, integer inputs): v_s is changed at 8 seeded positions s,
+    the original and the perturbed rows run in one launch."""
     from workloads import WORKLOADS, bf16_bits_to_f32, make_inputs, perturbation_positions
 
-    def probe(v, g, pos, change):
+    def probe(v, g, pos, change, conv=None):
+        conv = conv or sc.causal_conv
         rows = [v] + [change(v.copy(), s) for s in pos]
         vv = np.concatenate(rows, axis=0)
         gg = np.concatenate([g] * len(rows), axis=0)
-        out = sc.causal_conv(torch.from_numpy(vv).to(dev), torch.from_numpy(gg).to(dev))
+        out = conv(torch.from_numpy(vv).to(dev), torch.from_numpy(gg).to(dev))
         r = out.cpu().numpy().astype(np.float64)
         leak = 0.0
         for i, s in enumerate(pos):
@@ -146,6 +152,8 @@ def leakage_probe(sc, torch, dev, channels: int = 16) -> dict:
         a[:, :, s] += 1.0
         return a
     f_leak, f_rms = probe(v, g, pos, bump)
+    x_leak, _ = probe(v, g, pos, bump,
+                      lambda a, b: sc.causal_conv_fixed(a, b, FIXED_FRAC, FIXED_FRAC))
 
     w5 = WORKLOADS[5]
     vi, gi = make_inputs(w5, B=1, C=channels)
@@ -156,7 +164,52 @@ def leakage_probe(sc, torch, dev, channels: int = 16) -> dict:
         return a
     n_leak, _ = probe(vi, gi, posi, swap)
     return {"fp32_max_abs": f_leak, "fp32_rel_to_rms": f_leak / f_rms, "ntt_max_abs": n_leak,
-            "positions": len(pos), "channels": channels, "L": w3.L}
+            "fixed_max_abs": x_leak, "positions": len(pos), "channels": channels, "L": w3.L}
+
+
+def fixed_measure(sc, torch, w, dev, steps: int, warmup: int) -> dict:
+    """Time the exactly causal real-valued call (sc_causal_conv_fixed_f32_ws, fraction bits
+    FIXED_FRAC for v and g) on the workload's inputs widened to float32, with a caller
+    workspace so that no allocation is timed.  Algorithmic bytes per output: read v, g and
+    write r as float32 (12)."""
+    from workloads import bf16_bits_to_f32, make_inputs
+    v, g = make_inputs(w)
+    if w.storage == "bf16":
+        v, g = bf16_bits_to_f32(v), bf16_bits_to_f32(g)
+    if not sc.sc_fixed_range_ok(float(np.abs(v).max()), float(np.abs(g).max()), FIXED_FRAC,
+                                FIXED_FRAC, w.L):
+        raise RuntimeError("fixed-point range check failed for %s" % w.name)
+    tv, tg = torch.from_numpy(v).to(dev), torch.from_numpy(g).to(dev)
+    out = torch.empty_like(tv)
+    need = sc.sc_workspace_bytes(sc.KIND_FIXED_F32, w.B, w.C, w.L)
+    ws = torch.empty(need, dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    fn = sc.lib().sc_causal_conv_fixed_f32_ws
+
+    def call():
+        st = fn(tv.data_ptr(), tg.data_ptr(), out.data_ptr(), w.B, w.C, w.L, FIXED_FRAC,
+                FIXED_FRAC, ws.data_ptr(), need, stream.cuda_stream)
+        if st != 0:
+            raise RuntimeError("sc_causal_conv_fixed_f32_ws failed: %s" % sc.sc_status_string(st))
+
+    for _ in range(warmup):
+        call()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    torch.cuda.synchronize()
+    for i in range(steps):
+        ev[i][0].record(stream)
+        call()
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    gbps = 12 * w.outputs / (ms * 1e-3) / 1e9
+    return {"entry": "sc_causal_conv_fixed_f32_ws", "frac_bits": [FIXED_FRAC, FIXED_FRAC],
+            "ms_per_call": round(ms, 5), "value": round(w.outputs / (ms * 1e-3), 1),
+            "unit": "outputs/s", "hbm": {"algorithmic_bytes_per_call": 12 * w.outputs,
+                                         "achieved_GBps": round(gbps, 1),
+                                         "frac": round(gbps / HBM_PEAK_GBPS, 4)},
+            "scratch_bytes": need}
 
 
 def cpu_baseline(w, v, g, budget_s: float = 10.0):
@@ -248,6 +301,8 @@ def main(argv=None):
     ap.add_argument("--no-bwd", action="store_true",
                     help="skip the timing of the gradient call (keeps profiler runs to the "
                          "forward kernel)")
+    ap.add_argument("--no-fixed", action="store_true",
+                    help="skip the timing of the exactly causal real-valued call")
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run a plain device copy of known size (profiler calibration)")
     ap.add_argument("--record-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
@@ -366,6 +421,8 @@ def main(argv=None):
     if not args.no_bwd:
         del bufs
         rec["bwd"] = bwd_measure(sc, torch, w, dev, max(5, args.steps // 2), args.warmup)
+    if not args.no_fixed and w.storage != "i32" and w.L <= 4096:
+        rec["fixed"] = fixed_measure(sc, torch, w, dev, max(5, args.steps // 5), 2)
     if not args.no_leakage:
         rec["leakage"] = leakage_probe(sc, torch, dev)
     if not args.no_cpu_baseline:
