@@ -77,6 +77,32 @@ __device__ __forceinline__ void unpack_pair(int k, const float2* __restrict__ u0
 // REV (the gradient kernels): the first input is read reversed and the output is written
 // reversed, which turns the causal convolution into the correlation of the backward pass:
 // rev(causal(rev(dr), b))_j = sum_{t>=j} dr_t b_{t-j}.
+// Direct fp32 head r_t = sum_{j<=t} v_j g_{t-j}, t < head, of ncl channels whose first
+// HEAD_MAX inputs are staged in hb (v then g per channel), by NT threads lt = 0..NT-1 made
+// of whole waves.  Each output's sum is split over S consecutive lanes (terms j = s, s + S,
+// ...; S <= 8, as many as the threads allow) and reduced with lane shuffles, so the head
+// costs a few dependent steps instead of up to HEAD_MAX.
+template <int NT, class Put>
+__device__ __forceinline__ void direct_head(const float* __restrict__ hb, int ncl, int nvalid,
+                                            int L, int head, int lt, const Put& put)
+{
+    const int nout = ncl * head;
+    int S = 1;
+    while (S < 8 && 2 * S * nout <= NT) S *= 2;
+    for (int base = 0; base < nout * S; base += NT) {
+        const int idx = base + lt, o = idx / S, s = idx - o * S;
+        const int c2 = o / head, t = o - c2 * head;
+        float acc = 0.f;
+        if (o < nout) {
+            const float* hv = hb + c2 * 2 * HEAD_MAX;
+            const float* hg = hv + HEAD_MAX;
+            for (int j = s; j <= t; j += S) acc = __builtin_fmaf(hv[j], hg[t - j], acc);
+        }
+        for (int d = 1; d < S; d <<= 1) acc += __shfl_xor(acc, d);
+        if (o < nout && s == 0 && c2 < nvalid && t < L) put(c2, t, acc);
+    }
+}
+
 template <int M, class IO, bool REV>
 __global__ __launch_bounds__(FUSED_THREADS) void fused_conv_kernel(
     const typename IO::T* __restrict__ v, const typename IO::T* __restrict__ g,
@@ -168,7 +194,18 @@ __global__ __launch_bounds__(FUSED_THREADS) void fused_conv_kernel(
     }
     __syncthreads();
 
-    // 4. y = IDFT_M(Y): threads [c*TB, (c+1)*TB) serve local channel c; the rest idle
+    // output t of local channel c at flat index c L + t (at L-1-t when REV; pairs need L
+    // even, which the host ensures)
+    const Span rs = make_span(r, ch0 * L, (int64_t)nvalid * L);
+    auto put = [&](int c, int t, float a) { IO::store(rs, c * L + (REV ? L - 1 - t : t), a); };
+    auto put2 = [&](int c, int t, float a, float b) {
+        if (REV) IO::store2(rs, c * L + L - 2 - t, b, a);
+        else IO::store2(rs, c * L + t, a, b);
+    };
+
+    // 4. y = IDFT_M(Y): threads [c*TB, (c+1)*TB) serve local channel c.  The other half of
+    //    the workgroup computes the direct head meanwhile, from the inputs staged at load
+    //    time: r_t = sum_{j<=t} v_j g_{t-j} in fp32 for t < head.
     const bool iact = tid < CPW * TB;
     const int icl = iact ? tid / TB : 0, itau = tid % TB;
     float2* ybuf = lds + (2 * icl) * REG;
@@ -177,17 +214,13 @@ __global__ __launch_bounds__(FUSED_THREADS) void fused_conv_kernel(
         for (int q = 0; q < 16; ++q) x[q] = ybuf[reg_off<TB>(itau, q)];
     }
     __syncthreads();
+    // between this barrier and the first one of the inverse, where the active threads run
+    // their first radix-16 pass
+    if (!iact)
+        direct_head<FUSED_THREADS - CPW * TB>(hbuf, CPW, nvalid, L, head, tid - CPW * TB, put);
     fft_passes<M, true>(x, ybuf, itau, bank, iact);
 
     // 5. store: x[q] = 8 M y_m with m = itau + TB q; r_{2m} = Re y_m, r_{2m+1} = Im y_m
-    //    (at L-1-2m and L-2-2m when REV; pairs need L even, which the host ensures)
-    const Span rs = make_span(r, ch0 * L, (int64_t)nvalid * L);
-    // output t of local channel c at flat index c L + t
-    auto put = [&](int c, int t, float a) { IO::store(rs, c * L + (REV ? L - 1 - t : t), a); };
-    auto put2 = [&](int c, int t, float a, float b) {
-        if (REV) IO::store2(rs, c * L + L - 2 - t, b, a);
-        else IO::store2(rs, c * L + t, a, b);
-    };
     if (iact) {
         const float scale = 1.0f / (8.0f * (float)M);
         if (L == M && pair_store) {
@@ -214,19 +247,6 @@ __global__ __launch_bounds__(FUSED_THREADS) void fused_conv_kernel(
                         put(icl, t, a);
                     }
                 }
-            }
-        }
-    } else {
-        // 6. direct head from the staged inputs: r_t = sum_{j<=t} v_j g_{t-j}, fp32, t < head
-        const int nidle = FUSED_THREADS - CPW * TB;
-        for (int idx = tid - CPW * TB; idx < CPW * head; idx += nidle) {
-            const int c2 = idx / head, t = idx - c2 * head;
-            if (c2 < nvalid && t < L) {
-                const float* hv = hbuf + c2 * 2 * HEAD_MAX;
-                const float* hg = hv + HEAD_MAX;
-                float acc = 0.f;
-                for (int j = 0; j <= t; ++j) acc = __builtin_fmaf(hv[j], hg[t - j], acc);
-                put(c2, t, acc);
             }
         }
     }
