@@ -16,7 +16,10 @@ Public names mirror the C ABI of ``include/specconv.h``:
 ``sc_causal_conv_bwd_bf16``, ``sc_causal_conv_bwd_ntt_i32``, ``sc_causal_conv_bwd_ex``; plus
 :func:`causal_conv` and :func:`causal_conv_bwd`, which dispatch on dtype; the exactly causal
 real-valued calls ``sc_causal_conv_fixed_f32``, ``sc_causal_conv_fixed_f32_ws``,
-``sc_fixed_range_ok`` and :func:`causal_conv_fixed`.
+``sc_fixed_range_ok`` and :func:`causal_conv_fixed`; and for a filter shared by the batch
+``sc_filter_spectrum_bytes``, ``sc_filter_spectrum_{f32,bf16}``, ``sc_causal_conv_spec_{f32,bf16}``,
+``sc_causal_conv_shared_{f32,bf16}`` with :func:`filter_spectrum`, :func:`causal_conv_spec`,
+:func:`causal_conv_shared`.
 """
 from __future__ import annotations
 
@@ -32,7 +35,10 @@ __all__ = [
     "sc_status_string", "sc_version", "causal_conv_bwd", "sc_causal_conv_bwd_f32",
     "sc_causal_conv_bwd_bf16", "sc_causal_conv_bwd_ntt_i32", "sc_causal_conv_bwd_ex",
     "causal_conv_fixed", "sc_causal_conv_fixed_f32", "sc_causal_conv_fixed_f32_ws",
-    "sc_fixed_range_ok", "KIND_F32", "KIND_BF16", "KIND_NTT_I32", "KIND_FIXED_F32", "PATH_AUTO", "PATH_FUSED", "PATH_FOUR_STEP",
+    "sc_fixed_range_ok", "filter_spectrum", "causal_conv_spec", "causal_conv_shared",
+    "sc_filter_spectrum_bytes", "sc_filter_spectrum_f32", "sc_filter_spectrum_bf16",
+    "sc_causal_conv_spec_f32", "sc_causal_conv_spec_bf16", "sc_causal_conv_shared_f32",
+    "sc_causal_conv_shared_bf16", "KIND_F32", "KIND_BF16", "KIND_NTT_I32", "KIND_FIXED_F32", "PATH_AUTO", "PATH_FUSED", "PATH_FOUR_STEP",
     "PATH_DIRECT", "LIB_PATH",
 ]
 
@@ -87,6 +93,17 @@ def _open():
     h.sc_fixed_range_ok.argtypes = [ctypes.c_double, ctypes.c_double, ctypes.c_int32,
                                     ctypes.c_int32, i64]
     h.sc_fixed_range_ok.restype = ctypes.c_int
+    h.sc_filter_spectrum_bytes.argtypes = [i64, i64]
+    h.sc_filter_spectrum_bytes.restype = sz
+    for name in ("sc_filter_spectrum_f32", "sc_filter_spectrum_bf16"):
+        f = getattr(h, name)
+        f.argtypes = [vp, vp, i64, i64, vp]
+        f.restype = st
+    for name in ("sc_causal_conv_spec_f32", "sc_causal_conv_spec_bf16",
+                 "sc_causal_conv_shared_f32", "sc_causal_conv_shared_bf16"):
+        f = getattr(h, name)
+        f.argtypes = [vp, vp, vp, i64, i64, i64, vp]
+        f.restype = st
     h.sc_workspace_bytes.argtypes = [st, i64, i64, i64]
     h.sc_workspace_bytes.restype = sz
     h.sc_ntt_range_ok.argtypes = [i64, i64, i64]
@@ -164,6 +181,34 @@ def sc_causal_conv_fixed_f32_ws(v, g, r, B, C, L, frac_v, frac_g, ws, ws_bytes, 
 def sc_fixed_range_ok(max_abs_v, max_abs_g, frac_v, frac_g, L) -> bool:
     return bool(_lib.sc_fixed_range_ok(float(max_abs_v), float(max_abs_g), int(frac_v),
                                        int(frac_g), int(L)))
+
+
+def sc_filter_spectrum_bytes(C, L) -> int:
+    return int(_lib.sc_filter_spectrum_bytes(C, L))
+
+
+def sc_filter_spectrum_f32(k, spec, C, L, stream):
+    return _lib.sc_filter_spectrum_f32(k, spec, C, L, stream)
+
+
+def sc_filter_spectrum_bf16(k, spec, C, L, stream):
+    return _lib.sc_filter_spectrum_bf16(k, spec, C, L, stream)
+
+
+def sc_causal_conv_spec_f32(v, spec, r, B, C, L, stream):
+    return _lib.sc_causal_conv_spec_f32(v, spec, r, B, C, L, stream)
+
+
+def sc_causal_conv_spec_bf16(v, spec, r, B, C, L, stream):
+    return _lib.sc_causal_conv_spec_bf16(v, spec, r, B, C, L, stream)
+
+
+def sc_causal_conv_shared_f32(v, k, r, B, C, L, stream):
+    return _lib.sc_causal_conv_shared_f32(v, k, r, B, C, L, stream)
+
+
+def sc_causal_conv_shared_bf16(v, k, r, B, C, L, stream):
+    return _lib.sc_causal_conv_shared_bf16(v, k, r, B, C, L, stream)
 
 
 def sc_workspace_bytes(kind, B, C, L) -> int:
@@ -329,4 +374,88 @@ def causal_conv_fixed(v: torch.Tensor, g: torch.Tensor, frac_v: int, frac_g: int
                 workspace.data_ptr(), workspace.numel() * workspace.element_size(), stream)
     if st != SC_OK:
         raise SpecConvError(st, "causal_conv_fixed")
+    return out
+
+
+def _bcl(v: torch.Tensor, k: torch.Tensor):
+    """(B, C, L) of v for a filter k of shape (C, L): v is (..., C, L)."""
+    if k.dim() != 2 or v.dim() < 2 or tuple(v.shape[-2:]) != tuple(k.shape):
+        raise ValueError("k must be (C, L) and v (..., C, L)")
+    C, L = int(k.shape[0]), int(k.shape[1])
+    B = 1
+    for s_ in v.shape[:-2]:
+        B *= int(s_)
+    return B, C, L
+
+
+_SPEC_FN = {torch.float32: ("sc_filter_spectrum_f32", "sc_causal_conv_spec_f32",
+                            "sc_causal_conv_shared_f32"),
+            torch.bfloat16: ("sc_filter_spectrum_bf16", "sc_causal_conv_spec_bf16",
+                             "sc_causal_conv_shared_bf16")}
+
+
+def _check_float(*ts):
+    for t in ts:
+        if t.dtype not in _SPEC_FN:
+            raise TypeError("filter calls take float32 or bfloat16 tensors")
+        if not t.is_cuda or not t.is_contiguous():
+            raise ValueError("tensors must be contiguous and on the GPU")
+    if len({t.dtype for t in ts}) != 1 or len({t.device for t in ts}) != 1:
+        raise ValueError("tensors must share dtype and device")
+
+
+def filter_spectrum(k: torch.Tensor) -> torch.Tensor:
+    """Spectrum of the filters k (C, L), float32 or bfloat16, as an opaque uint8 device tensor
+    for :func:`causal_conv_spec` (sc_filter_spectrum_*)."""
+    _check_float(k)
+    if k.dim() != 2:
+        raise ValueError("k must be (C, L)")
+    C, L = int(k.shape[0]), int(k.shape[1])
+    nbytes = sc_filter_spectrum_bytes(C, L)
+    if nbytes == 0 and C > 0:
+        raise SpecConvError(SC_ERR_UNSUPPORTED, "filter_spectrum")
+    spec = torch.empty(max(nbytes, 8), dtype=torch.uint8, device=k.device)
+    with torch.cuda.device(k.device):
+        stream = torch.cuda.current_stream(k.device).cuda_stream
+        st = getattr(_lib, _SPEC_FN[k.dtype][0])(k.data_ptr(), spec.data_ptr(), C, L, stream)
+    if st != SC_OK:
+        raise SpecConvError(st, "filter_spectrum")
+    spec.sc_shape = (C, L, k.dtype)
+    return spec
+
+
+def causal_conv_spec(v: torch.Tensor, spec: torch.Tensor, C: int, L: int,
+                     out: torch.Tensor | None = None) -> torch.Tensor:
+    """r[b, c, t] = sum_{j<=t} v[b, c, j] k[c, t-j] from the spectrum of k (made by
+    :func:`filter_spectrum` for this C and L); v is (..., C, L)."""
+    _check_float(v)
+    if tuple(v.shape[-2:]) != (C, L):
+        raise ValueError("v must be (..., C, L)")
+    if spec.dtype != torch.uint8 or spec.device != v.device or \
+            spec.numel() < sc_filter_spectrum_bytes(C, L):
+        raise ValueError("spec must be a spectrum tensor of this C and L on v's device")
+    out = _out_like(v, out, "out")
+    B = v.numel() // max(C * L, 1)
+    with torch.cuda.device(v.device):
+        stream = torch.cuda.current_stream(v.device).cuda_stream
+        st = getattr(_lib, _SPEC_FN[v.dtype][1])(v.data_ptr(), spec.data_ptr(), out.data_ptr(),
+                                                 B, C, L, stream)
+    if st != SC_OK:
+        raise SpecConvError(st, "causal_conv_spec")
+    return out
+
+
+def causal_conv_shared(v: torch.Tensor, k: torch.Tensor,
+                       out: torch.Tensor | None = None) -> torch.Tensor:
+    """r[b, c, t] = sum_{j<=t} v[b, c, j] k[c, t-j] with one filter per channel shared by the
+    batch (sc_causal_conv_shared_*); v is (..., C, L), k is (C, L)."""
+    _check_float(v, k)
+    B, C, L = _bcl(v, k)
+    out = _out_like(v, out, "out")
+    with torch.cuda.device(v.device):
+        stream = torch.cuda.current_stream(v.device).cuda_stream
+        st = getattr(_lib, _SPEC_FN[v.dtype][2])(v.data_ptr(), k.data_ptr(), out.data_ptr(), B,
+                                                 C, L, stream)
+    if st != SC_OK:
+        raise SpecConvError(st, "causal_conv_shared")
     return out

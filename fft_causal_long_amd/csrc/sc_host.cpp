@@ -572,6 +572,161 @@ int sc_fixed_range_ok(double max_abs_v, double max_abs_g, int32_t frac_v, int32_
     return 1;
 }
 
+// ---- filter shared by the batch
+
+size_t sc_filter_spectrum_bytes(int64_t C, int64_t L)
+{
+    if (C < 0 || L < 1 || L > kMaxLFused) return 0;
+    const int M = (int)std::max<int64_t>(64, next_pow2(L));
+    const __int128 bytes = (__int128)C * sc::shared_spec_stride(M) * (int64_t)sizeof(float2);
+    return bytes > (__int128)INT64_MAX ? 0 : (size_t)bytes;
+}
+
+namespace {
+
+sc_status spectrum_run(sc_kind kind, const void* k, void* spec, int64_t C, int64_t L,
+                       hipStream_t stream)
+{
+    if (kind != SC_KIND_F32 && kind != SC_KIND_BF16) return SC_ERR_INVALID_ARGUMENT;
+    if (C < 0 || L < 0) return SC_ERR_INVALID_ARGUMENT;
+    if (L > kMaxLFused) return SC_ERR_UNSUPPORTED;
+    if (C == 0 || L == 0) return SC_OK;
+    const size_t es = elt_size(kind);
+    if ((__int128)C * L * (int64_t)es >= ((__int128)1 << 31)) return SC_ERR_UNSUPPORTED;
+    if (!k || !spec) return SC_ERR_INVALID_ARGUMENT;
+    if ((uintptr_t)k % es || (uintptr_t)spec % sizeof(float2)) return SC_ERR_INVALID_ARGUMENT;
+    const size_t sbytes = sc_filter_spectrum_bytes(C, L);
+    if ((uintptr_t)k < (uintptr_t)spec + sbytes && (uintptr_t)spec < (uintptr_t)k + C * L * es)
+        return SC_ERR_INVALID_ARGUMENT;
+    DeviceState* d = nullptr;
+    sc_status st = device_state(&d, false);
+    if (st != SC_OK) return st;
+    const int M = (int)std::max<int64_t>(64, next_pow2(L));
+    const sc::Store s = kind == SC_KIND_F32 ? sc::Store::F32 : sc::Store::BF16;
+    return sc::launch_shared_spectrum(s, k, (float2*)spec, (int)C, (int)L, M, d->fused_tw,
+                                      stream) == hipSuccess
+               ? SC_OK
+               : SC_ERR_HIP;
+}
+
+// checks of an apply call; *n receives B*C*L
+sc_status apply_check(sc_kind kind, const void* v, const void* spec, const void* r, int64_t B,
+                      int64_t C, int64_t L, int64_t* n)
+{
+    if (kind != SC_KIND_F32 && kind != SC_KIND_BF16) return SC_ERR_INVALID_ARGUMENT;
+    sc_status st = check_shape(kind, B, C, L, n);
+    if (st != SC_OK) return st;
+    if (L > kMaxLFused) return SC_ERR_UNSUPPORTED;
+    if (*n == 0) return SC_OK;
+    const size_t es = elt_size(kind);
+    if ((__int128)C * L * (int64_t)es >= ((__int128)1 << 31)) return SC_ERR_UNSUPPORTED;
+    if (!v || !spec || !r) return SC_ERR_INVALID_ARGUMENT;
+    if (((uintptr_t)v | (uintptr_t)r) % es || (uintptr_t)spec % sizeof(float2))
+        return SC_ERR_INVALID_ARGUMENT;
+    const uint64_t bytes = (uint64_t)*n * es;
+    if (overlaps(r, v, bytes)) return SC_ERR_INVALID_ARGUMENT;
+    const uint64_t sb = sc_filter_spectrum_bytes(C, L);
+    if ((uintptr_t)r < (uintptr_t)spec + sb && (uintptr_t)spec < (uintptr_t)r + bytes)
+        return SC_ERR_INVALID_ARGUMENT;
+    return SC_OK;
+}
+
+// batch rows per launch so that one launch's v and r stay below 2^31 bytes
+sc_status apply_run(sc_kind kind, const void* v, const void* spec, void* r, int64_t B, int64_t C,
+                    int64_t L, hipStream_t stream)
+{
+    DeviceState* d = nullptr;
+    sc_status st = device_state(&d, false);
+    if (st != SC_OK) return st;
+    const int M = (int)std::max<int64_t>(64, next_pow2(L));
+    const sc::Store s = kind == SC_KIND_F32 ? sc::Store::F32 : sc::Store::BF16;
+    const size_t es = elt_size(kind);
+    const int64_t row = C * L * (int64_t)es;
+    const int64_t rows = std::max<int64_t>(1, std::min<int64_t>(B, (((int64_t)1 << 31) - 1) / row));
+    for (int64_t b0 = 0; b0 < B; b0 += rows) {
+        const int64_t nb = std::min<int64_t>(rows, B - b0);
+        const hipError_t e = sc::launch_shared_apply(
+            s, (const char*)v + b0 * row, (const float2*)spec, (char*)r + b0 * row, (int)nb,
+            (int)C, (int)L, M, kDefaultHead, d->fused_tw, stream);
+        if (e != hipSuccess) return SC_ERR_HIP;
+    }
+    return SC_OK;
+}
+
+sc_status shared_run(sc_kind kind, const void* v, const void* k, void* r, int64_t B, int64_t C,
+                     int64_t L, hipStream_t stream)
+{
+    int64_t n = 0;
+    // k plays the role of the spectrum in the checks; its own layout is checked below
+    sc_status st = check_shape(kind, B, C, L, &n);
+    if (st != SC_OK) return st;
+    if (kind != SC_KIND_F32 && kind != SC_KIND_BF16) return SC_ERR_INVALID_ARGUMENT;
+    if (L > kMaxLFused) return SC_ERR_UNSUPPORTED;
+    if (n == 0) return SC_OK;
+    const size_t es = elt_size(kind);
+    if (!v || !k || !r) return SC_ERR_INVALID_ARGUMENT;
+    if (((uintptr_t)v | (uintptr_t)k | (uintptr_t)r) % es) return SC_ERR_INVALID_ARGUMENT;
+    if ((__int128)C * L * (int64_t)es >= ((__int128)1 << 31)) return SC_ERR_UNSUPPORTED;
+    if (overlaps(r, v, (uint64_t)n * es)) return SC_ERR_INVALID_ARGUMENT;
+    if ((uintptr_t)r < (uintptr_t)k + C * L * es && (uintptr_t)k < (uintptr_t)r + n * es)
+        return SC_ERR_INVALID_ARGUMENT;
+    void* spec = nullptr;
+    if (hipMallocAsync(&spec, sc_filter_spectrum_bytes(C, L), stream) != hipSuccess)
+        return SC_ERR_HIP;
+    st = spectrum_run(kind, k, spec, C, L, stream);
+    if (st == SC_OK) st = apply_run(kind, v, spec, r, B, C, L, stream);
+    if (hipFreeAsync(spec, stream) != hipSuccess && st == SC_OK) st = SC_ERR_HIP;
+    return st;
+}
+
+}  // namespace
+
+sc_status sc_filter_spectrum_f32(const float* k, void* spec, int64_t C, int64_t L,
+                                 hipStream_t stream)
+{
+    return guarded([&] { return spectrum_run(SC_KIND_F32, k, spec, C, L, stream); });
+}
+
+sc_status sc_filter_spectrum_bf16(const uint16_t* k, void* spec, int64_t C, int64_t L,
+                                  hipStream_t stream)
+{
+    return guarded([&] { return spectrum_run(SC_KIND_BF16, k, spec, C, L, stream); });
+}
+
+sc_status sc_causal_conv_spec_f32(const float* v, const void* spec, float* r, int64_t B,
+                                  int64_t C, int64_t L, hipStream_t stream)
+{
+    return guarded([&] {
+        int64_t n = 0;
+        sc_status st = apply_check(SC_KIND_F32, v, spec, r, B, C, L, &n);
+        if (st != SC_OK || n == 0) return st;
+        return apply_run(SC_KIND_F32, v, spec, r, B, C, L, stream);
+    });
+}
+
+sc_status sc_causal_conv_spec_bf16(const uint16_t* v, const void* spec, uint16_t* r, int64_t B,
+                                   int64_t C, int64_t L, hipStream_t stream)
+{
+    return guarded([&] {
+        int64_t n = 0;
+        sc_status st = apply_check(SC_KIND_BF16, v, spec, r, B, C, L, &n);
+        if (st != SC_OK || n == 0) return st;
+        return apply_run(SC_KIND_BF16, v, spec, r, B, C, L, stream);
+    });
+}
+
+sc_status sc_causal_conv_shared_f32(const float* v, const float* k, float* r, int64_t B,
+                                    int64_t C, int64_t L, hipStream_t stream)
+{
+    return guarded([&] { return shared_run(SC_KIND_F32, v, k, r, B, C, L, stream); });
+}
+
+sc_status sc_causal_conv_shared_bf16(const uint16_t* v, const uint16_t* k, uint16_t* r, int64_t B,
+                                     int64_t C, int64_t L, hipStream_t stream)
+{
+    return guarded([&] { return shared_run(SC_KIND_BF16, v, k, r, B, C, L, stream); });
+}
+
 int sc_ntt_range_ok(int64_t max_abs_v, int64_t max_abs_g, int64_t L)
 {
     if (max_abs_v < 0 || max_abs_g < 0 || L < 0) return 0;
@@ -591,6 +746,6 @@ const char* sc_status_string(sc_status s)
     }
 }
 
-int sc_version(void) { return 300; }
+int sc_version(void) { return 400; }
 
 }  // extern "C"

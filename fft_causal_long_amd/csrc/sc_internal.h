@@ -84,6 +84,16 @@ hipError_t launch_fourstep(Store st, const void* v, const void* g, void* r, int6
                            int M, int head, bool pair_store, bool rev, const float2* bank,
                            const FsTw& tw, void* ws, int64_t chunk, hipStream_t stream);
 
+// ---- filter shared by the batch (L <= FUSED_MAX_L, M = max(64, next power of two >= L))
+// Spectrum of the filters k[C][L]: shared_spec_stride(M) float2 per channel.
+int64_t shared_spec_stride(int M);
+hipError_t launch_shared_spectrum(Store st, const void* k, float2* spec, int C, int L, int M,
+                                  const float2* tw, hipStream_t stream);
+// r[b][c][t] = sum_{j<=t} v[b][c][j] k[c][t-j] from the spectrum; B * C * L elements of v and
+// r must stay below 2^31 bytes (the host splits larger batches).
+hipError_t launch_shared_apply(Store st, const void* v, const float2* spec, void* r, int B, int C,
+                               int L, int M, int head, const float2* tw, hipStream_t stream);
+
 // Direct summation r_t = sum_{j<=t} v_j g_{t-j} in fp32, one thread per output.
 hipError_t launch_direct(Store st, const void* v, const void* g, void* r, int64_t nch, int L,
                          bool rev, hipStream_t stream);

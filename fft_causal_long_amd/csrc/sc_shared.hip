@@ -1,0 +1,332 @@
+// Causal convolution with a filter shared by the whole batch (gfx950), L <= 4096.
+//
+//     r[b][c][t] = sum_{j<=t} v[b][c][j] * k[c][t-j]
+//
+// The Caracal notes contrast their data-dependent gate with filters that do not depend on
+// the input ("Caracal: Causal Architecture via Spectral Mixing", related work: Hyena's
+// position-based filter, FlashButterfly's static global kernel).  With such a filter the
+// pad-to-2L recipe (key designs 1 and 2) needs the filter's spectrum only once per channel,
+// and two batch rows share one complex transform: k is real, so for z = v_b + i v_{b+1}
+//     IDFT_N(K Z) = (v_b * k) + i (v_{b+1} * k)      (* = circular convolution of length N)
+// and the first L values of the real and imaginary parts are r_b and r_{b+1}.
+//
+// Spectrum kernel (once per filter): for channel pairs (c, c+1), Z = DFT_N(k_c + i k_{c+1}),
+// K_c = (Z_k + conj Z_{N-k}) / 2, K_{c+1} = (Z_k - conj Z_{N-k}) / (2i), stored divided by N.
+// Apply kernel: per job (channel c, rows 2p and 2p+1) the branch-b unit (b = 0, 1) computes
+// U = DFT_M(z_n W_N^{b n}) = Z_{2j+b} (the zero half prunes the first stage), multiplies by
+// K_{2j+b} and inverts in place: e^b = IDFT_M(K Z)_n restricted to parity b; then
+//     y_n = e^0_n + W_N^{-n} e^1_n = IDFT_N(K Z)_n   (n < M).
+// Every thread works in every phase (two length-M transforms per output row instead of the
+// three of the per-row-gate kernel).  Outputs t < head use direct fp32 summation, as there.
+//
+// Spectrum layout per channel c (SPEC_STRIDE float2): [b][j] = K_{2j+b} / N for b < 2,
+// j < M, then the filter's first HEAD_MAX values (float32, two per float2).
+
+#include "sc_device.h"
+#include "sc_fft_lds.h"
+#include "sc_internal.h"
+
+namespace sc {
+
+namespace {
+
+constexpr int SH_THREADS = 512;
+constexpr int SH_HEAD_MAX = 64;
+constexpr int SH_LDS_EXTRA = 24;
+
+template <int M>
+__host__ __device__ constexpr int spec_stride()
+{
+    return 2 * M + SH_HEAD_MAX / 2;
+}
+
+}  // namespace
+
+int64_t shared_spec_stride(int M)
+{
+    return 2 * (int64_t)M + SH_HEAD_MAX / 2;
+}
+
+// ---------------------------------------------------------------- filter spectrum
+
+template <int M, class IO>
+__global__ __launch_bounds__(SH_THREADS) void shared_spectrum_kernel(
+    const typename IO::T* __restrict__ k, float2* __restrict__ spec, int C, int L,
+    const float2* __restrict__ tw)
+{
+    constexpr int N = 2 * M, TB = M / 16, UNITS = SH_THREADS / TB, PPW = UNITS / 2;
+    constexpr int REG = M + M / 16 + (M >= 256 ? SH_LDS_EXTRA : 0);
+    constexpr int SS = spec_stride<M>();
+    __shared__ float2 lds[UNITS * REG];
+
+    const Bank bank = make_bank(tw);
+    const int tid = threadIdx.x;
+    const int unit = tid / TB, tau = tid % TB;
+    const int pl = unit >> 1, beta = unit & 1;
+    const int c0 = 2 * (blockIdx.x * PPW + pl), c1 = c0 + 1;
+    const bool v0 = c0 < C, v1 = c1 < C;
+    const Span ks = make_span(k, 0, (int64_t)C * L);
+    float2* ubuf = lds + unit * REG;
+
+    float2 x[16];
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+        const int n = tau + TB * q;
+        const int e0 = (v0 && n < L) ? c0 * L + n : IO::OOB;
+        const int e1 = (v1 && n < L) ? c1 * L + n : IO::OOB;
+        x[q] = make_float2(IO::load(ks, e0), IO::load(ks, e1));
+    }
+    if (!beta) {
+        // the filters' first values for the direct head: k_c[n] in float, n < SH_HEAD_MAX
+#pragma unroll
+        for (int q = 0; q < (TB >= SH_HEAD_MAX ? 1 : SH_HEAD_MAX / TB); ++q) {
+            const int n = tau + TB * q;
+            if (n < SH_HEAD_MAX) {
+                float* h0 = (float*)(spec + (int64_t)c0 * SS + 2 * M);
+                float* h1 = (float*)(spec + (int64_t)c1 * SS + 2 * M);
+                if (v0) h0[n] = x[q].x;
+                if (v1) h1[n] = x[q].y;
+            }
+        }
+    } else {
+#pragma unroll
+        for (int q = 0; q < 16; ++q) x[q] = cmul(x[q], tw_get<false>(bank, N, tau + TB * q));
+    }
+    fft_passes<M, false>(x, ubuf, tau, bank, true);
+#pragma unroll
+    for (int q = 0; q < 16; ++q) ubuf[reg_off<TB>(tau, q)] = x[q];
+    __syncthreads();
+    // x[q] = Z_k with k = 2 j + beta, j = tau + TB q; its mirror Z_{N-k} is Z_{2 (M - j - beta) + beta}
+    const float inv = 1.0f / (float)N;
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+        const int j = tau + TB * q;
+        const float2 z = x[q];
+        const float2 w = conjf2(ubuf[lds_pad((M - j - beta) & (M - 1))]);
+        const float2 s = cadd(z, w), d = csub(z, w);
+        // K_c = s / 2, K_{c+1} = d / (2i) = (d.y - i d.x) / 2
+        if (v0) spec[(int64_t)c0 * SS + beta * M + j] = make_float2(0.5f * inv * s.x, 0.5f * inv * s.y);
+        if (v1) spec[(int64_t)c1 * SS + beta * M + j] = make_float2(0.5f * inv * d.y, -0.5f * inv * d.x);
+    }
+}
+
+// ---------------------------------------------------------------- apply
+
+template <int M, class IO>
+__global__ __launch_bounds__(SH_THREADS, (M >= 512 ? 4 : 1)) void shared_apply_kernel(
+    const typename IO::T* __restrict__ v, const float2* __restrict__ spec,
+    typename IO::T* __restrict__ r, int B, int C, int L, int head,
+    const float2* __restrict__ tw)
+{
+    constexpr int N = 2 * M, TB = M / 16, UNITS = SH_THREADS / TB, JPW = UNITS / 2;
+    constexpr int REG = M + M / 16 + (M >= 256 ? SH_LDS_EXTRA : 0);
+    constexpr int SS = spec_stride<M>();
+    __shared__ float2 lds[UNITS * REG];
+    // per job: v of row 2p, v of row 2p+1, k (first SH_HEAD_MAX values each)
+    __shared__ float hbuf[JPW * 3 * SH_HEAD_MAX];
+
+    const Bank bank = make_bank(tw);
+    const int tid = threadIdx.x;
+    const int unit = tid / TB, tau = tid % TB;
+    const int jl = unit >> 1, beta = unit & 1;
+    const int P = (B + 1) / 2;
+    // Workgroups are dealt to the 8 XCDs round-robin; renumber them so that the workgroups
+    // of one XCD take consecutive jobs, i.e. the pairs of one channel share that XCD's L2
+    // and its filter spectrum is fetched from memory about once.
+    const int g8 = gridDim.x >> 3;                       // the grid is a multiple of 8
+    const int w = (blockIdx.x & 7) * g8 + (blockIdx.x >> 3);
+    const int J = w * JPW + jl;                          // job: channel c, rows 2p, 2p+1
+    const bool jv = J < C * P;
+    const int c = jv ? J / P : 0, p = jv ? J - c * P : 0;
+    const bool has1 = 2 * p + 1 < B;
+    const int row0 = (2 * p * C + c) * L, row1 = ((2 * p + 1) * C + c) * L;
+    const Span vs = make_span(v, 0, (int64_t)B * C * L);
+    const Span rs = make_span(r, 0, (int64_t)B * C * L);
+    float2* ubuf = lds + unit * REG;
+    float* hb = hbuf + jl * 3 * SH_HEAD_MAX;
+    const float2* sp = spec + (int64_t)c * SS;
+
+    // 1. z_n = v[2p][c][n] + i v[2p+1][c][n] (zero past L and for a missing second row)
+    float2 x[16];
+    if (L == M) {
+        // unconditional loads from rows that exist (their offsets fold into the
+        // instructions), masked afterwards
+        const bool m0 = jv, m1 = jv && has1;
+        const int a0 = m0 ? row0 : 0, a1 = m1 ? row1 : a0;
+#pragma unroll
+        for (int q = 0; q < 16; ++q) {
+            const int n = tau + TB * q;
+            const float f0 = IO::load(vs, a0 + n), f1 = IO::load(vs, a1 + n);
+            x[q] = make_float2(m0 ? f0 : 0.f, m1 ? f1 : 0.f);
+        }
+    } else {
+#pragma unroll
+        for (int q = 0; q < 16; ++q) {
+            const int n = tau + TB * q;
+            const int e0 = (jv && n < L) ? row0 + n : IO::OOB;
+            const int e1 = (jv && has1 && n < L) ? row1 + n : IO::OOB;
+            x[q] = make_float2(IO::load(vs, e0), IO::load(vs, e1));
+        }
+    }
+    if (!beta) {
+#pragma unroll
+        for (int q = 0; q < (TB >= SH_HEAD_MAX ? 1 : SH_HEAD_MAX / TB); ++q) {
+            const int n = tau + TB * q;
+            if (n < head) {
+                hb[n] = x[q].x;
+                hb[SH_HEAD_MAX + n] = x[q].y;
+                hb[2 * SH_HEAD_MAX + n] = ((const float*)(sp + 2 * M))[n];
+            }
+        }
+    } else {
+#pragma unroll
+        for (int q = 0; q < 16; ++q) x[q] = cmul(x[q], tw_get<false>(bank, N, tau + TB * q));
+    }
+
+    // 2. U = DFT_M(.) = Z_{2j+beta}, times K_{2j+beta} / N
+    fft_passes<M, false>(x, ubuf, tau, bank, true);
+    // From here on an opaque copy of tau addresses the spectrum and the inverse's twiddles,
+    // so those loads are neither hoisted above the forward transform nor merged with its
+    // identical twiddle loads, which would hold them in registers in between.
+    int tk = tau;
+    asm volatile("" : "+v"(tk));
+#pragma unroll
+    for (int q = 0; q < 16; ++q) x[q] = cmul(x[q], sp[beta * M + tk + TB * q]);
+
+    // 3. e^beta = IDFT_M(K Z restricted to parity beta), natural order.  (The forward's last
+    //    pass runs in registers after a barrier that follows its last read of ubuf, so the
+    //    inverse may write ubuf at once.)
+    fft_passes<M, true>(x, ubuf, tk, bank, true);
+
+    // 4. y_n = e^0_n + W_N^{-n} e^1_n: branch 1 hands W_N^{-n} e^1_n to branch 0 through LDS
+    float2* xch = lds + (2 * jl + 1) * REG;
+    if (beta) {
+#pragma unroll
+        for (int q = 0; q < 16; ++q) {
+            const int n = tk + TB * q;   // (W_N^n was also read for the pre-twiddle: keep apart)
+            xch[lds_pad(n)] = cmulc(x[q], tw_get<false>(bank, N, n));
+        }
+    }
+    __syncthreads();
+    if (!beta) {
+        if (jv) {
+#pragma unroll
+            for (int q = 0; q < 16; ++q) {
+                const int n = tau + TB * q;
+                if (n < head || n >= L) continue;
+                const float2 y = cadd(x[q], xch[lds_pad(n)]);
+                IO::store(rs, row0 + n, y.x);
+                if (has1) IO::store(rs, row1 + n, y.y);
+            }
+        }
+    } else if (jv) {
+        // direct head of both rows: r_t = sum_{j<=t} v_j k_{t-j}, fp32, t < head, each sum
+        // split over S lanes of this unit and reduced with lane shuffles
+        const int nout = 2 * head;
+        int S = 1;
+        while (S < 8 && 2 * S * nout <= TB) S *= 2;
+        if (TB >= 64) {
+            for (int base = 0; base < nout * S; base += TB) {
+                const int idx = base + tau, o = idx / S, s = idx - o * S;
+                const int row = o >= head ? 1 : 0, t = o - row * head;
+                float acc = 0.f;
+                if (o < nout) {
+                    const float* hv = hb + row * SH_HEAD_MAX;
+                    const float* hk = hb + 2 * SH_HEAD_MAX;
+                    for (int j = s; j <= t; j += S) acc = __builtin_fmaf(hv[j], hk[t - j], acc);
+                }
+                for (int d = 1; d < S; d <<= 1) acc += __shfl_xor(acc, d);
+                if (o < nout && s == 0 && t < L && (row == 0 || has1))
+                    IO::store(rs, (row ? row1 : row0) + t, acc);
+            }
+        } else {
+            // units narrower than a wave: one lane per output
+            for (int o = tau; o < nout; o += TB) {
+                const int row = o >= head ? 1 : 0, t = o - row * head;
+                if (t >= L || (row && !has1)) continue;
+                const float* hv = hb + row * SH_HEAD_MAX;
+                const float* hk = hb + 2 * SH_HEAD_MAX;
+                float acc = 0.f;
+                for (int j = 0; j <= t; ++j) acc = __builtin_fmaf(hv[j], hk[t - j], acc);
+                IO::store(rs, (row ? row1 : row0) + t, acc);
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------- launch
+
+namespace {
+
+template <int M, class IO>
+hipError_t spectrum_m(const void* k, float2* spec, int C, int L, const float2* tw, hipStream_t s)
+{
+    constexpr int PPW = (SH_THREADS / (M / 16)) / 2;
+    const int64_t pairs = ((int64_t)C + 1) / 2;
+    const int64_t blocks = (pairs + PPW - 1) / PPW;
+    hipLaunchKernelGGL((shared_spectrum_kernel<M, IO>), dim3((unsigned)blocks), dim3(SH_THREADS),
+                       0, s, (const typename IO::T*)k, spec, C, L, tw);
+    return hipGetLastError();
+}
+
+template <int M, class IO>
+hipError_t apply_m(const void* v, const float2* spec, void* r, int B, int C, int L, int head,
+                   const float2* tw, hipStream_t s)
+{
+    constexpr int JPW = (SH_THREADS / (M / 16)) / 2;
+    const int64_t jobs = (int64_t)C * ((B + 1) / 2);
+    const int64_t blocks = ((jobs + JPW - 1) / JPW + 7) / 8 * 8;   // a multiple of 8
+    hipLaunchKernelGGL((shared_apply_kernel<M, IO>), dim3((unsigned)blocks), dim3(SH_THREADS), 0,
+                       s, (const typename IO::T*)v, spec, (typename IO::T*)r, B, C, L, head, tw);
+    return hipGetLastError();
+}
+
+template <class IO>
+hipError_t spectrum_io(const void* k, float2* spec, int C, int L, int M, const float2* tw,
+                       hipStream_t s)
+{
+    switch (M) {
+    case 64: return spectrum_m<64, IO>(k, spec, C, L, tw, s);
+    case 128: return spectrum_m<128, IO>(k, spec, C, L, tw, s);
+    case 256: return spectrum_m<256, IO>(k, spec, C, L, tw, s);
+    case 512: return spectrum_m<512, IO>(k, spec, C, L, tw, s);
+    case 1024: return spectrum_m<1024, IO>(k, spec, C, L, tw, s);
+    case 2048: return spectrum_m<2048, IO>(k, spec, C, L, tw, s);
+    case 4096: return spectrum_m<4096, IO>(k, spec, C, L, tw, s);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+template <class IO>
+hipError_t apply_io(const void* v, const float2* spec, void* r, int B, int C, int L, int M,
+                    int head, const float2* tw, hipStream_t s)
+{
+    switch (M) {
+    case 64: return apply_m<64, IO>(v, spec, r, B, C, L, head, tw, s);
+    case 128: return apply_m<128, IO>(v, spec, r, B, C, L, head, tw, s);
+    case 256: return apply_m<256, IO>(v, spec, r, B, C, L, head, tw, s);
+    case 512: return apply_m<512, IO>(v, spec, r, B, C, L, head, tw, s);
+    case 1024: return apply_m<1024, IO>(v, spec, r, B, C, L, head, tw, s);
+    case 2048: return apply_m<2048, IO>(v, spec, r, B, C, L, head, tw, s);
+    case 4096: return apply_m<4096, IO>(v, spec, r, B, C, L, head, tw, s);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace
+
+hipError_t launch_shared_spectrum(Store st, const void* k, float2* spec, int C, int L, int M,
+                                  const float2* tw, hipStream_t s)
+{
+    return st == Store::F32 ? spectrum_io<f32_io>(k, spec, C, L, M, tw, s)
+                            : spectrum_io<bf16_io>(k, spec, C, L, M, tw, s);
+}
+
+hipError_t launch_shared_apply(Store st, const void* v, const float2* spec, void* r, int B, int C,
+                               int L, int M, int head, const float2* tw, hipStream_t s)
+{
+    return st == Store::F32 ? apply_io<f32_io>(v, spec, r, B, C, L, M, head, tw, s)
+                            : apply_io<bf16_io>(v, spec, r, B, C, L, M, head, tw, s);
+}
+
+}  // namespace sc

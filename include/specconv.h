@@ -236,6 +236,46 @@ sc_status sc_causal_conv_bwd_ex(sc_kind kind, const void* dr, const void* v, con
                                 hipStream_t stream);
 
 /*
+ * Filter shared by the batch.  The Caracal notes contrast their data-dependent gate with
+ * filters that do not depend on the input ("Caracal: Causal Architecture via Spectral
+ * Mixing", related work: Hyena's position-based filter, FlashButterfly's static global
+ * kernel).  For such a filter k[C][L] (one per channel, the same for every batch row):
+ *
+ *     r[b][c][t] = sum_{j=0..t} v[b][c][j] * k[c][t-j]
+ *
+ * by the same pad-2L method, with the filter's spectrum computed once (and reusable across
+ * calls) and two batch rows sharing one complex transform (k is real, so the transform of
+ * v_b + i v_{b+1} times K gives both rows).  Accuracy as sc_causal_conv_f32 / _bf16 with
+ * g_{t-j} = k_{t-j}; the first 32 outputs use direct fp32 summation.  1 <= L <= 4096 (else
+ * SC_ERR_UNSUPPORTED), C * L elements of k, and the whole batch of v and r, processed in
+ * launches of at most 2^31 bytes of rows each; C * L * element size must stay below 2^31
+ * bytes (SC_ERR_UNSUPPORTED otherwise).  Float kinds only.
+ *
+ *  sc_filter_spectrum_bytes(C, L) -- bytes of the spectrum of C filters of length L
+ *      (C * (2M + 32) * 8 with M = max(64, next power of two >= L)); 0 for unsupported L.
+ *  sc_filter_spectrum_*(k, spec, C, L, stream) -- writes that spectrum (device memory
+ *      owned by the caller, 8-byte aligned, not overlapping k).  Its contents are private
+ *      to this library version; it is valid for this C and L only.
+ *  sc_causal_conv_spec_*(v, spec, r, B, C, L, stream) -- r from v and a spectrum made for
+ *      the same C and L.  r may not overlap v or spec.  Allocates nothing.
+ *  sc_causal_conv_shared_*(v, k, r, B, C, L, stream) -- both steps in one call, the
+ *      spectrum in stream-ordered scratch (hipMallocAsync / hipFreeAsync on `stream`).
+ */
+size_t sc_filter_spectrum_bytes(int64_t C, int64_t L);
+sc_status sc_filter_spectrum_f32(const float* k, void* spec, int64_t C, int64_t L,
+                                 hipStream_t stream);
+sc_status sc_filter_spectrum_bf16(const uint16_t* k, void* spec, int64_t C, int64_t L,
+                                  hipStream_t stream);
+sc_status sc_causal_conv_spec_f32(const float* v, const void* spec, float* r, int64_t B,
+                                  int64_t C, int64_t L, hipStream_t stream);
+sc_status sc_causal_conv_spec_bf16(const uint16_t* v, const void* spec, uint16_t* r, int64_t B,
+                                   int64_t C, int64_t L, hipStream_t stream);
+sc_status sc_causal_conv_shared_f32(const float* v, const float* k, float* r, int64_t B,
+                                    int64_t C, int64_t L, hipStream_t stream);
+sc_status sc_causal_conv_shared_bf16(const uint16_t* v, const uint16_t* k, uint16_t* r,
+                                     int64_t B, int64_t C, int64_t L, hipStream_t stream);
+
+/*
  * sc_ntt_range_ok -- 1 if every |v_j| <= max_abs_v and |g_j| <= max_abs_g guarantee that
  *   the exact sums fit the symmetric residue range, i.e. L * max_abs_v * max_abs_g <=
  *   (p-1)/2; 0 otherwise (or on negative arguments).  Host only.
@@ -245,7 +285,7 @@ int sc_ntt_range_ok(int64_t max_abs_v, int64_t max_abs_g, int64_t L);
 /* Human-readable name of a status code (static storage).  Host only. */
 const char* sc_status_string(sc_status s);
 
-/* Library version: major * 10000 + minor * 100 + patch (this header: 300).  Host only. */
+/* Library version: major * 10000 + minor * 100 + patch (this header: 400).  Host only. */
 int sc_version(void);
 
 #ifdef __cplusplus

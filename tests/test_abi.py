@@ -217,3 +217,35 @@ def test_fixed_range_helper(sc):
     L = ((P - 1) // 2) // (2 ** 86)
     assert ok(2.0 ** 43, 2.0 ** 43, 0, 0, L)
     assert not ok(2.0 ** 43, 2.0 ** 43, 0, 0, L + 1)
+
+
+def test_shared_filter_host_checks(sc):
+    h = sc.lib()
+    INVALID, UNSUP, OK = sc.SC_ERR_INVALID_ARGUMENT, sc.SC_ERR_UNSUPPORTED, sc.SC_OK
+    # spectrum size: C * (2M + 32) float2, M = max(64, next_pow2(L)); 0 for unsupported L
+    assert sc.sc_filter_spectrum_bytes(3, 100) == 3 * (2 * 128 + 32) * 8
+    assert sc.sc_filter_spectrum_bytes(1, 1) == (2 * 64 + 32) * 8
+    assert sc.sc_filter_spectrum_bytes(1, 4097) == 0
+    assert sc.sc_filter_spectrum_bytes(-1, 64) == 0
+    for name in ("sc_filter_spectrum_f32", "sc_filter_spectrum_bf16"):
+        f = getattr(h, name)
+        assert f(A, B_, 4, 5000, None) == UNSUP
+        assert f(None, B_, 4, 64, None) == INVALID
+        assert f(A, None, 4, 64, None) == INVALID
+        assert f(A, B_ + 4, 4, 64, None) == INVALID            # spectrum not 8-byte aligned
+        assert f(A, A + 64, 4, 64, None) == INVALID            # spectrum overlaps k
+        assert f(A, B_, -1, 64, None) == INVALID
+        assert f(None, None, 0, 64, None) == OK
+    for name in ("sc_causal_conv_spec_f32", "sc_causal_conv_spec_bf16",
+                 "sc_causal_conv_shared_f32", "sc_causal_conv_shared_bf16"):
+        f = getattr(h, name)
+        assert f(A, B_, C_, 2, 4, 5000, None) == UNSUP, name
+        assert f(None, B_, C_, 2, 4, 64, None) == INVALID, name
+        assert f(A, None, C_, 2, 4, 64, None) == INVALID, name
+        assert f(A, B_, None, 2, 4, 64, None) == INVALID, name
+        assert f(A, B_, A + 8, 2, 4, 64, None) == INVALID, name   # r overlaps v
+        assert f(A, B_, B_, 2, 4, 64, None) == INVALID, name      # r overlaps k / spectrum
+        assert f(A, B_, C_, -2, 4, 64, None) == INVALID, name
+        assert f(None, None, None, 0, 4, 64, None) == OK, name
+    # one filter set must fit a 32-bit span: C * L * 4 bytes < 2^31
+    assert h.sc_causal_conv_shared_f32(1 << 40, 2 << 40, 3 << 40, 1, 1 << 19, 4096, None) == UNSUP

@@ -1,0 +1,91 @@
+"""GPU parity of the filter-shared-by-the-batch calls against the float64 oracle.
+
+r[b, c, t] = sum_{j<=t} v[b, c, j] k[c, t-j]: the oracle is the direct sum with k broadcast
+over the batch (the same pinned oracle as the per-row gate).  Bounds as for the forward
+call: |r - r_ref| <= 1e-4 * S (plus one bf16 rounding for bf16 storage).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from tests.gpu_util import assert_within_bound, to_device, to_host
+from workloads import WORKLOADS, make_inputs, make_shared_filter
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def sc():
+    import fft_causal_long_amd as m
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    return m
+
+
+def inputs(cid, B, C, L, seed):
+    w = WORKLOADS[cid]
+    v, _ = make_inputs(w, B=B, C=C, L=L, seed_offset=seed)
+    k = make_shared_filter(w, C=C, L=L, seed_offset=seed)
+    return v, k
+
+
+def check(r, v, k, what, chans=None):
+    B, C, L = v.shape
+    kk = np.broadcast_to(k[None], v.shape)
+    if chans is not None:
+        v, kk, r = [x.reshape(-1, L)[chans] for x in (v, kk, r)]
+    ref, S = oracle.causal_conv_f64(v, np.ascontiguousarray(kk))
+    worst = assert_within_bound(r, ref, S, v.dtype == np.uint16, what)
+    print("%s: worst err/bound %.3g" % (what, worst), flush=True)
+
+
+@pytest.mark.parametrize("L", [1, 5, 32, 33, 64, 100, 256, 1000, 1024, 3000, 4095, 4096])
+def test_lengths_f32(sc, L):
+    v, k = inputs(2, 3, 5, L, L)
+    print("case shared f32 L=%d" % L, flush=True)
+    r = to_host(sc.causal_conv_shared(to_device(v), to_device(k)))
+    check(r, v, k, "shared f32 L=%d" % L)
+
+
+@pytest.mark.parametrize("B,C", [(1, 1), (2, 7), (5, 3), (8, 16)])
+def test_batch_shapes_bf16(sc, B, C):
+    v, k = inputs(3, B, C, 4096, B * 100 + C)
+    print("case shared bf16 B=%d C=%d" % (B, C), flush=True)
+    r = to_host(sc.causal_conv_shared(to_device(v), to_device(k)))
+    check(r, v, k, "shared bf16 B=%d C=%d" % (B, C))
+
+
+def test_spectrum_reused_across_calls(sc):
+    L, C = 2048, 12
+    w = WORKLOADS[2]
+    k = make_shared_filter(w, C=C, L=L, seed_offset=7)
+    spec = sc.filter_spectrum(to_device(k))
+    for seed, B in ((8, 4), (9, 3)):
+        v, _ = make_inputs(w, B=B, C=C, L=L, seed_offset=seed)
+        print("case spectrum reuse B=%d" % B, flush=True)
+        r = to_host(sc.causal_conv_spec(to_device(v), spec, C, L))
+        check(r, v, k, "spectrum reuse B=%d" % B)
+        # the one-shot call gives the same bits
+        r2 = to_host(sc.causal_conv_shared(to_device(v), to_device(k)))
+        assert np.array_equal(r.view(np.uint32), r2.view(np.uint32))
+
+
+def test_medium_shape_sampled(sc):
+    w = WORKLOADS[3]
+    v, k = inputs(3, w.B, w.C, w.L, 0)
+    print("case shared medium full shape", flush=True)
+    r = to_host(sc.causal_conv_shared(to_device(v), to_device(k)))
+    check(r, v, k, "shared medium", chans=np.array([0, 1, 1023, 1024, 4097, 8191]))
+
+
+def test_deterministic_and_causal(sc):
+    v, k = inputs(2, 4, 8, 1024, 11)
+    a = to_host(sc.causal_conv_shared(to_device(v), to_device(k)))
+    b = to_host(sc.causal_conv_shared(to_device(v), to_device(k)))
+    assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+    # rows of a pair do not leak into each other: changing row 1 leaves row 0 bitwise equal
+    v2 = v.copy()
+    v2[1] += np.float32(1.0)
+    c = to_host(sc.causal_conv_shared(to_device(v2), to_device(k)))
+    assert np.array_equal(c[0].view(np.uint32), a[0].view(np.uint32)) or \
+        np.max(np.abs(c[0] - a[0])) <= 1e-5 * np.max(np.abs(a[0]))

@@ -6,7 +6,8 @@ draws random numbers, shapes them like the pages' models and rounds them to the 
 dtype.  Every array is generated in float64 from ``numpy.random.default_rng`` seeded with
 ``SeedSequence([config_id, stream_id])`` (stream 0 = v, 1 = gate pre-activation,
 2 = gate conv weights, 3 = extra draws such as perturbation positions, 4 = the upstream
-gradient dr of the backward pass), then rounded once to the stored dtype.
+gradient dr of the backward pass, 5 = a filter shared by the batch), then rounded once to
+the stored dtype.
 
 Workload shapes (the model shapes follow "Caracal: Causal Architecture via Spectral
 Mixing": the multi-head Fourier module mixes C = n_head * head_dim channels per batch
@@ -158,6 +159,21 @@ def make_grad(w: Workload, B: int | None = None, C: int | None = None, L: int | 
         return rng(cid, 4).integers(-127, 128, size=shape, dtype=np.int32)
     d32 = rng(cid, 4).standard_normal(shape).astype(np.float32)
     return f32_to_bf16_bits(d32) if w.storage == "bf16" else d32
+
+
+def make_shared_filter(w: Workload, C: int | None = None, L: int | None = None,
+                       seed_offset: int = 0) -> np.ndarray:
+    """A filter per channel, shared by every batch row, shape (C, L), in the workload's
+    stored dtype: k[c][t] = N(0,1) * exp(-t / tau_c) with tau_c log-spaced over [16, L]
+    (a decaying long filter like the position-based filters the Caracal notes contrast with
+    their data-dependent gate).  Drawn from stream 5."""
+    C = w.C if C is None else C
+    L = w.L if L is None else L
+    cid = w.cid + 1000 * seed_offset
+    tau = np.exp(np.linspace(np.log(16.0), np.log(max(L, 17)), C))[:, None]
+    k64 = rng(cid, 5).standard_normal((C, L)) * np.exp(-np.arange(L)[None, :] / tau)
+    k32 = k64.astype(np.float32)
+    return f32_to_bf16_bits(k32) if w.storage == "bf16" else k32
 
 
 def perturbation_positions(cid: int, L: int, count: int = 8) -> np.ndarray:
