@@ -7,7 +7,9 @@ default workload, sc_causal_conv_bf16 at B=8, C=1024, L=4096: load v and g, pad-
 spectral product, inverse FFT, truncation, direct head, store r -- a single kernel).
 After the timed region, the gradient call of the same workload (dv, dg from dr, v, g) is
 timed the same way and reported in the `bwd` object (skip with --no-bwd), and the exactly
-causal real-valued call on the same inputs in the `fixed` object (skip with --no-fixed).
+causal real-valued call on the same inputs in the `fixed` object (skip with --no-fixed),
+and the calls for a filter shared by the batch on the same shape in the `shared` object
+(skip with --no-shared).
 Inputs are resident in HBM before the timed region.  Several copies of the buffers are
 rotated so that the 256 MB last-level cache cannot hold a step's working set.
 
@@ -289,6 +291,70 @@ def bwd_measure(sc, torch, w, dev, steps: int, warmup: int) -> dict:
     return rec
 
 
+def shared_measure(sc, torch, w, dev, steps: int, warmup: int) -> dict:
+    """Time the filter-shared-by-the-batch calls on the workload's shape: the apply call
+    sc_causal_conv_spec_* (v and the filter spectrum resident, buffers rotated like the
+    forward) and, separately, the spectrum call sc_filter_spectrum_*.  Algorithmic bytes per
+    output: read v, write r (2 elements; the spectrum is per channel, not per output)."""
+    from workloads import make_inputs, make_shared_filter
+    bf = w.storage == "bf16"
+    esz = 2 if bf else 4
+    kname = "bf16" if bf else "f32"
+    v, _ = make_inputs(w)
+    k = make_shared_filter(w)
+    to = (lambda a: torch.from_numpy(a.view(np.int16)).to(dev)) if bf else \
+        (lambda a: torch.from_numpy(a).to(dev))
+    set_bytes = 2 * w.outputs * esz
+    nsets = max(1, -(-2 * CACHE_BYTES // set_bytes))
+    bufs = [(to(v), torch.empty(w.outputs, dtype=torch.int16 if bf else torch.float32,
+                                device=dev)) for _ in range(nsets)]
+    tk = to(k)
+    spec = torch.empty(sc.sc_filter_spectrum_bytes(w.C, w.L), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    sptr = stream.cuda_stream
+    fspec = getattr(sc.lib(), "sc_filter_spectrum_" + kname)
+    fapply = getattr(sc.lib(), "sc_causal_conv_spec_" + kname)
+
+    def mk_spec(i):
+        st = fspec(tk.data_ptr(), spec.data_ptr(), w.C, w.L, sptr)
+        if st != 0:
+            raise RuntimeError("sc_filter_spectrum failed: %s" % sc.sc_status_string(st))
+
+    def apply(i):
+        a, o = bufs[i % nsets]
+        st = fapply(a.data_ptr(), spec.data_ptr(), o.data_ptr(), w.B, w.C, w.L, sptr)
+        if st != 0:
+            raise RuntimeError("sc_causal_conv_spec failed: %s" % sc.sc_status_string(st))
+
+    def timed(fn, n):
+        for i in range(warmup):
+            fn(i)
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(n)]
+        torch.cuda.synchronize()
+        for i in range(n):
+            ev[i][0].record(stream)
+            fn(i)
+            ev[i][1].record(stream)
+        torch.cuda.synchronize()
+        return float(np.mean([a.elapsed_time(b) for a, b in ev]))
+
+    t_spec = timed(mk_spec, 5)
+    t_apply = timed(apply, steps)
+    gbps = 2 * w.outputs * esz / (t_apply * 1e-3) / 1e9
+    tf = 2.0 / 3.0 * algorithmic_flops_per_output(w.L) * w.outputs / (t_apply * 1e-3) / 1e12
+    del bufs
+    return {"entry": "sc_causal_conv_spec_" + kname, "filter": "one per channel, shared by "
+            "the %d batch rows (decaying random filters)" % w.B,
+            "ms_per_call": round(t_apply, 5), "value": round(w.outputs / (t_apply * 1e-3), 1),
+            "unit": "outputs/s", "spectrum_ms": round(t_spec, 5),
+            "hbm": {"algorithmic_bytes_per_call": 2 * w.outputs * esz,
+                    "achieved_GBps": round(gbps, 1), "frac": round(gbps / HBM_PEAK_GBPS, 4)},
+            "alu": {"achieved_TFLOPs": round(tf, 2), "peak": FP32_VECTOR_PEAK_TFLOPS,
+                    "frac": round(tf / FP32_VECTOR_PEAK_TFLOPS, 4),
+                    "flops_per_output": "2/3 of the per-row-gate method's"}}
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -301,6 +367,8 @@ def main(argv=None):
     ap.add_argument("--no-bwd", action="store_true",
                     help="skip the timing of the gradient call (keeps profiler runs to the "
                          "forward kernel)")
+    ap.add_argument("--no-shared", action="store_true",
+                    help="skip the timing of the filter-shared-by-the-batch calls")
     ap.add_argument("--no-fixed", action="store_true",
                     help="skip the timing of the exactly causal real-valued call")
     ap.add_argument("--calib-copy", action="store_true",
@@ -421,6 +489,8 @@ def main(argv=None):
     if not args.no_bwd:
         del bufs
         rec["bwd"] = bwd_measure(sc, torch, w, dev, max(5, args.steps // 2), args.warmup)
+    if not args.no_shared and w.storage != "i32" and w.L <= 4096:
+        rec["shared"] = shared_measure(sc, torch, w, dev, max(5, args.steps // 2), args.warmup)
     if not args.no_fixed and w.storage != "i32" and w.L <= 4096:
         rec["fixed"] = fixed_measure(sc, torch, w, dev, max(5, args.steps // 5), 2)
     if not args.no_leakage:
