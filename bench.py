@@ -38,6 +38,26 @@ FP32_VECTOR_PEAK_TFLOPS = 157.3  # MI355X fp32 vector, AMD published
 CACHE_BYTES = 256 << 20          # MI355X last-level (Infinity) cache
 
 
+def time_rounds(torch, stream, fn, n: int, rounds: int = 5):
+    """Mean milliseconds per call of fn(i), i < n, launched back to back on `stream`, with
+    HIP events recorded on that stream only at the boundaries of `rounds` equal rounds (an
+    event between every two launches would add its own gap to each).  Returns (mean over
+    all calls, [mean per call of each round])."""
+    rounds = max(1, min(rounds, n))
+    bounds = [round(r * n / rounds) for r in range(rounds + 1)]
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(rounds + 1)]
+    torch.cuda.synchronize()
+    evs[0].record(stream)
+    for r in range(rounds):
+        for i in range(bounds[r], bounds[r + 1]):
+            fn(i)
+        evs[r + 1].record(stream)
+    torch.cuda.synchronize()
+    per_round = [evs[r].elapsed_time(evs[r + 1]) / (bounds[r + 1] - bounds[r])
+                 for r in range(rounds)]
+    return evs[0].elapsed_time(evs[rounds]) / n, per_round
+
+
 def algorithmic_flops_per_output(L: int) -> float:
     """Real flops per output of the pad-2L FFT method with real-pair packing, the pruned
     first forward stage and the half-length real inverse: (12.75 log2 L + 28)."""
@@ -196,15 +216,7 @@ def fixed_measure(sc, torch, w, dev, steps: int, warmup: int) -> dict:
 
     for _ in range(warmup):
         call()
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(steps)]
-    torch.cuda.synchronize()
-    for i in range(steps):
-        ev[i][0].record(stream)
-        call()
-        ev[i][1].record(stream)
-    torch.cuda.synchronize()
-    ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    ms, _ = time_rounds(torch, stream, lambda i: call(), steps)
     gbps = 12 * w.outputs / (ms * 1e-3) / 1e9
     return {"entry": "sc_causal_conv_fixed_f32_ws", "frac_bits": [FIXED_FRAC, FIXED_FRAC],
             "ms_per_call": round(ms, 5), "value": round(w.outputs / (ms * 1e-3), 1),
@@ -267,15 +279,7 @@ def bwd_measure(sc, torch, w, dev, steps: int, warmup: int) -> dict:
 
     for i in range(warmup):
         call(i)
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(steps)]
-    torch.cuda.synchronize()
-    for i in range(steps):
-        ev[i][0].record(stream)
-        call(i)
-        ev[i][1].record(stream)
-    torch.cuda.synchronize()
-    ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    ms, _ = time_rounds(torch, stream, call, steps)
     alg_bytes = 5 * w.outputs * esz
     gbps = alg_bytes / (ms * 1e-3) / 1e9
     rec = {"entry": kind[0], "ms_per_call": round(ms, 5),
@@ -329,15 +333,7 @@ def shared_measure(sc, torch, w, dev, steps: int, warmup: int) -> dict:
     def timed(fn, n):
         for i in range(warmup):
             fn(i)
-        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-              for _ in range(n)]
-        torch.cuda.synchronize()
-        for i in range(n):
-            ev[i][0].record(stream)
-            fn(i)
-            ev[i][1].record(stream)
-        torch.cuda.synchronize()
-        return float(np.mean([a.elapsed_time(b) for a, b in ev]))
+        return time_rounds(torch, stream, fn, n)[0]
 
     t_spec = timed(mk_spec, 5)
     t_apply = timed(apply, steps)
@@ -426,22 +422,12 @@ def main(argv=None):
         step(i)
     torch.cuda.synchronize()
 
-    # per-launch events on the launch stream, plus one pair around the whole region
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(args.steps)]
-    t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t_start.record(stream)
-    for i in range(args.steps):
-        ev[i][0].record(stream)
-        step(i)
-        ev[i][1].record(stream)
-    t_end.record(stream)
-    torch.cuda.synchronize()
-    total_ms = t_start.elapsed_time(t_end)
-    launch_ms = [a.elapsed_time(b) for a, b in ev]
-    ms_per_step = total_ms / args.steps
-    kernel_ms = float(np.mean(launch_ms))
+    # the K steps back to back on the launch stream, HIP events at 5 round boundaries (and
+    # synchronisation on both sides); one step is one kernel launch, so the mean launch
+    # duration is the region's time per step
+    ms_per_step, round_ms = time_rounds(torch, stream, step, args.steps)
+    total_ms = ms_per_step * args.steps
+    kernel_ms = ms_per_step
 
     if args.calib_copy:
         # 1 GiB device-to-device copy: a known-size reference for the profiler's byte counters
@@ -482,9 +468,9 @@ def main(argv=None):
         "roofline": roof,
         "hbm": {"algorithmic_bytes_per_launch": alg_bytes, "achieved_GBps": round(hbm_gbps, 1),
                 "peak_GBps": HBM_PEAK_GBPS, "frac": round(hbm_gbps / HBM_PEAK_GBPS, 4)},
-        "kernel_ms": {"mean": round(kernel_ms, 5), "min": round(float(np.min(launch_ms)), 5),
-                      "p50": round(float(np.median(launch_ms)), 5),
-                      "max": round(float(np.max(launch_ms)), 5)},
+        "kernel_ms": {"mean": round(kernel_ms, 5), "rounds": [round(x, 5) for x in round_ms],
+                      "method": "launches back to back, HIP events on the launch stream at "
+                                "round boundaries"},
     }
     if not args.no_bwd:
         del bufs
