@@ -19,6 +19,8 @@ blocking or fusion (see ``oracle.c`` for the C side):
   Token Leakage in Convolutional Sequence Modeling and How to Mitigate It", abstract:
   FFTs done on integers only).
 * :func:`causal_conv_f64_at` -- the float64 sum for sampled (channel, t) outputs.
+* :func:`shared_conv_bwd_f64` -- the same gradients for a filter shared by the batch: dv
+  per row, dk summed over the batch rows (the filter is one parameter for all of them).
 * :func:`causal_conv_bwd_f64` / :func:`causal_conv_bwd_i64` -- the gradients of
   sum_t dr[t] r[t]: dv[j] = sum_{t>=j} dr[t] g[t-j], dg[k] = sum_{t>=k} dr[t] v[t-k], with
   their error scales (the pages' models are trained end to end with a next-token loss,
@@ -299,6 +301,19 @@ def causal_conv_fixed_f32(v, g, fv: int, fg: int, nthreads: int | None = None) -
     round_f32(sum_{j<=t} round(v_j 2^fv) round(g_{t-j} 2^fg) * 2^-(fv+fg))."""
     return fixed_decode_f32(causal_conv_i128(fixed_encode(v, fv), fixed_encode(g, fg),
                                              nthreads), fv + fg)
+
+
+def shared_conv_bwd_f64(dr, v, k, nthreads: int | None = None):
+    """Gradients for a filter shared by the batch, r[b, c] = causal(v[b, c], k[c]):
+    dv[b, c, j] = sum_{t>=j} dr[b, c, t] k[c, t-j] and dk[c, j] = sum_b sum_{t>=j}
+    dr[b, c, t] v[b, c, t-j] (the batch sum of the per-row gradient), float64, with their
+    error scales.  dr, v: (B, C, L); k: (C, L).  Returns (dv, dk, Sv, Sk)."""
+    d64, v64, k64 = as_f64(dr), as_f64(v), as_f64(k)
+    if d64.shape != v64.shape or v64.ndim != 3 or k64.shape != v64.shape[1:]:
+        raise ValueError("dr, v must be (B, C, L) and k (C, L)")
+    kb = np.ascontiguousarray(np.broadcast_to(k64[None], v64.shape))
+    dv, dkb, Sv, Skb = causal_conv_bwd_f64(d64, v64, kb, nthreads)
+    return dv, dkb.sum(axis=0), Sv, Skb.sum(axis=0)
 
 
 def lift_mod_p(r, p: int = P_NTT) -> np.ndarray:

@@ -561,3 +561,29 @@ def test_golden_fixed(case):
     assert oracle.causal_conv_i128(V, G).tolist() == R
     assert oracle.causal_conv_fixed_f32(np.array(v, np.float32), np.array(g, np.float32),
                                         fv, fg).tolist() == r
+
+
+def test_shared_filter_gradients():
+    # against torch autograd of a batch of conv1d with one weight per channel (shared by the
+    # batch), float64 on the CPU; and the adjoint identity sum dr r = sum dk k exactly on integers
+    import torch
+    rng = np.random.default_rng(60)
+    B, C, L = 3, 2, 30
+    dr, v = rng.standard_normal((2, B, C, L))
+    k = rng.standard_normal((C, L))
+    tv = torch.tensor(v, requires_grad=True)
+    tk = torch.tensor(k, requires_grad=True)
+    x = torch.nn.functional.pad(tv, (L - 1, 0))                       # (B, C, 2L-1)
+    w = torch.flip(tk, dims=[-1]).unsqueeze(1)                        # (C, 1, L)
+    r = torch.nn.functional.conv1d(x, w, groups=C)                    # (B, C, L)
+    (torch.tensor(dr) * r).sum().backward()
+    dv, dk, Sv, Sk = oracle.shared_conv_bwd_f64(dr, v, k)
+    np.testing.assert_allclose(tv.grad.numpy(), dv, atol=1e-12)
+    np.testing.assert_allclose(tk.grad.numpy(), dk, atol=1e-12)
+    assert np.all(Sv >= np.abs(dv)) and np.all(Sk >= np.abs(dk))
+    ir = rng.integers(-20, 21, (B, C, L))
+    iv = rng.integers(-20, 21, (B, C, L))
+    ik = rng.integers(-20, 21, (C, L))
+    rr = causal_conv_i64(iv, np.broadcast_to(ik[None], iv.shape))
+    _, dki, _, _ = oracle.shared_conv_bwd_f64(ir.astype(float), iv.astype(float), ik.astype(float))
+    assert (ir * rr).sum() == int(round((dki * ik).sum()))
