@@ -38,7 +38,9 @@ __all__ = [
     "sc_fixed_range_ok", "filter_spectrum", "causal_conv_spec", "causal_conv_shared",
     "sc_filter_spectrum_bytes", "sc_filter_spectrum_f32", "sc_filter_spectrum_bf16",
     "sc_causal_conv_spec_f32", "sc_causal_conv_spec_bf16", "sc_causal_conv_shared_f32",
-    "sc_causal_conv_shared_bf16", "KIND_F32", "KIND_BF16", "KIND_NTT_I32", "KIND_FIXED_F32", "PATH_AUTO", "PATH_FUSED", "PATH_FOUR_STEP",
+    "sc_causal_conv_shared_bf16", "causal_conv_spec_bwd", "causal_conv_shared_bwd",
+    "sc_causal_conv_spec_bwd_f32", "sc_causal_conv_spec_bwd_bf16",
+    "sc_causal_conv_shared_bwd_f32", "sc_causal_conv_shared_bwd_bf16", "KIND_F32", "KIND_BF16", "KIND_NTT_I32", "KIND_FIXED_F32", "PATH_AUTO", "PATH_FUSED", "PATH_FOUR_STEP",
     "PATH_DIRECT", "LIB_PATH",
 ]
 
@@ -103,6 +105,11 @@ def _open():
                  "sc_causal_conv_shared_f32", "sc_causal_conv_shared_bf16"):
         f = getattr(h, name)
         f.argtypes = [vp, vp, vp, i64, i64, i64, vp]
+        f.restype = st
+    for name in ("sc_causal_conv_spec_bwd_f32", "sc_causal_conv_spec_bwd_bf16",
+                 "sc_causal_conv_shared_bwd_f32", "sc_causal_conv_shared_bwd_bf16"):
+        f = getattr(h, name)
+        f.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, vp]
         f.restype = st
     h.sc_workspace_bytes.argtypes = [st, i64, i64, i64]
     h.sc_workspace_bytes.restype = sz
@@ -209,6 +216,22 @@ def sc_causal_conv_shared_f32(v, k, r, B, C, L, stream):
 
 def sc_causal_conv_shared_bf16(v, k, r, B, C, L, stream):
     return _lib.sc_causal_conv_shared_bf16(v, k, r, B, C, L, stream)
+
+
+def sc_causal_conv_spec_bwd_f32(dr, v, spec, dv, dk, B, C, L, stream):
+    return _lib.sc_causal_conv_spec_bwd_f32(dr, v, spec, dv, dk, B, C, L, stream)
+
+
+def sc_causal_conv_spec_bwd_bf16(dr, v, spec, dv, dk, B, C, L, stream):
+    return _lib.sc_causal_conv_spec_bwd_bf16(dr, v, spec, dv, dk, B, C, L, stream)
+
+
+def sc_causal_conv_shared_bwd_f32(dr, v, k, dv, dk, B, C, L, stream):
+    return _lib.sc_causal_conv_shared_bwd_f32(dr, v, k, dv, dk, B, C, L, stream)
+
+
+def sc_causal_conv_shared_bwd_bf16(dr, v, k, dv, dk, B, C, L, stream):
+    return _lib.sc_causal_conv_shared_bwd_bf16(dr, v, k, dv, dk, B, C, L, stream)
 
 
 def sc_workspace_bytes(kind, B, C, L) -> int:
@@ -459,3 +482,57 @@ def causal_conv_shared(v: torch.Tensor, k: torch.Tensor,
     if st != SC_OK:
         raise SpecConvError(st, "causal_conv_shared")
     return out
+
+
+_BWD_FN = {torch.float32: ("sc_causal_conv_spec_bwd_f32", "sc_causal_conv_shared_bwd_f32"),
+           torch.bfloat16: ("sc_causal_conv_spec_bwd_bf16", "sc_causal_conv_shared_bwd_bf16")}
+
+
+def _filter_grad_like(v: torch.Tensor, C: int, L: int, dk: torch.Tensor | None) -> torch.Tensor:
+    if dk is None:
+        return torch.empty((C, L), dtype=v.dtype, device=v.device)
+    if dk.dtype != v.dtype or dk.device != v.device or tuple(dk.shape) != (C, L) or \
+            not dk.is_contiguous():
+        raise ValueError("dk must be a contiguous (C, L) tensor of v's dtype and device")
+    return dk
+
+
+def causal_conv_spec_bwd(dr: torch.Tensor, v: torch.Tensor, spec: torch.Tensor, C: int, L: int,
+                         dv: torch.Tensor | None = None, dk: torch.Tensor | None = None):
+    """(dv, dk) of r = causal_conv_spec(v, spec) for the output gradient dr, with dk summed over
+    the batch (sc_causal_conv_spec_bwd_*); spec from :func:`filter_spectrum` for this C, L."""
+    _check_float(dr, v)
+    if tuple(v.shape[-2:]) != (C, L) or dr.shape != v.shape:
+        raise ValueError("dr and v must be (..., C, L) of one shape")
+    if spec.dtype != torch.uint8 or spec.device != v.device or \
+            spec.numel() < sc_filter_spectrum_bytes(C, L):
+        raise ValueError("spec must be a spectrum tensor of this C and L on v's device")
+    dv = _out_like(v, dv, "dv")
+    dk = _filter_grad_like(v, C, L, dk)
+    B = v.numel() // max(C * L, 1)
+    with torch.cuda.device(v.device):
+        stream = torch.cuda.current_stream(v.device).cuda_stream
+        st = getattr(_lib, _BWD_FN[v.dtype][0])(dr.data_ptr(), v.data_ptr(), spec.data_ptr(),
+                                                dv.data_ptr(), dk.data_ptr(), B, C, L, stream)
+    if st != SC_OK:
+        raise SpecConvError(st, "causal_conv_spec_bwd")
+    return dv, dk
+
+
+def causal_conv_shared_bwd(dr: torch.Tensor, v: torch.Tensor, k: torch.Tensor,
+                           dv: torch.Tensor | None = None, dk: torch.Tensor | None = None):
+    """(dv, dk) of r = causal_conv_shared(v, k) for the output gradient dr, with dk summed over
+    the batch (sc_causal_conv_shared_bwd_*)."""
+    _check_float(dr, v, k)
+    B, C, L = _bcl(v, k)
+    if dr.shape != v.shape:
+        raise ValueError("dr must have v's shape")
+    dv = _out_like(v, dv, "dv")
+    dk = _filter_grad_like(v, C, L, dk)
+    with torch.cuda.device(v.device):
+        stream = torch.cuda.current_stream(v.device).cuda_stream
+        st = getattr(_lib, _BWD_FN[v.dtype][1])(dr.data_ptr(), v.data_ptr(), k.data_ptr(),
+                                                dv.data_ptr(), dk.data_ptr(), B, C, L, stream)
+    if st != SC_OK:
+        raise SpecConvError(st, "causal_conv_shared_bwd")
+    return dv, dk

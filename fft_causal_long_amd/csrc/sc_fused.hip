@@ -43,40 +43,6 @@ constexpr int HEAD_MAX = 64;   // largest direct head (the host clamps to this)
 // unpack's alternating reads of u0[j] and u1[j] land in different banks
 constexpr int LDS_EXTRA = SC_LDS_EXTRA;
 
-// From the branch spectra u0[j] = Z_{2j}, u1[j] = Z_{2j+1} (natural order, padded) form
-// Y_k and Y_{M-k} of the real-output inverse, both scaled by 8 (constants folded later).
-template <int M>
-__device__ __forceinline__ void unpack_pair(int k, const float2* __restrict__ u0,
-                                            const float2* __restrict__ u1, const Bank& bank,
-                                            float2& yk, float2& ymk)
-{
-    constexpr int N = 2 * M;
-    const int b = k & 1, j = k >> 1;
-    const float2* u = b ? u1 : u0;
-    // bins k, N-k, M-k, M+k of Z
-    const float2 p1 = u[lds_pad(j)];
-    const float2 q1 = conjf2(u[lds_pad((M - j - b) & (M - 1))]);
-    const float2 p2 = u[lds_pad((M / 2 - j - b) & (M - 1))];
-    const float2 q2 = conjf2(u[lds_pad(M / 2 + j)]);
-    // 4 X = 4 V G = -i (P + Q)(P - Q)
-    const float2 s1 = cadd(p1, q1), d1 = csub(p1, q1);
-    const float2 s2 = cadd(p2, q2), d2 = csub(p2, q2);
-    const float2 x1 = make_float2(__builtin_fmaf(s1.x, d1.y, s1.y * d1.x),
-                                  __builtin_fmaf(s1.y, d1.y, -s1.x * d1.x));   // 4 X_k
-    const float2 x2 = make_float2(__builtin_fmaf(s2.x, d2.y, s2.y * d2.x),
-                                  __builtin_fmaf(s2.y, d2.y, -s2.x * d2.x));   // 4 X_{M-k}
-    // S = X_k + X_{k+M}, D = X_k - X_{k+M} with X_{k+M} = conj X_{M-k}
-    const float2 sm = make_float2(x1.x + x2.x, x1.y - x2.y);
-    const float2 df = make_float2(x1.x - x2.x, x1.y + x2.y);
-    const float2 t = cmulc(df, tw_get<false>(bank, N, k));        // W_N^{-k} D
-    // Y_k = S + i T,  Y_{M-k} = conj(S - i T)
-    yk = make_float2(sm.x - t.y, sm.y + t.x);
-    ymk = make_float2(sm.x + t.y, t.x - sm.y);
-}
-
-// REV (the gradient kernels): the first input is read reversed and the output is written
-// reversed, which turns the causal convolution into the correlation of the backward pass:
-// rev(causal(rev(dr), b))_j = sum_{t>=j} dr_t b_{t-j}.
 // Direct fp32 head r_t = sum_{j<=t} v_j g_{t-j}, t < head, of ncl channels whose first
 // HEAD_MAX inputs are staged in hb (v then g per channel), by NT threads lt = 0..NT-1 made
 // of whole waves.  Each output's sum is split over S consecutive lanes (terms j = s, s + S,

@@ -633,7 +633,7 @@ sc_status apply_check(sc_kind kind, const void* v, const void* spec, const void*
 
 // batch rows per launch so that one launch's v and r stay below 2^31 bytes
 sc_status apply_run(sc_kind kind, const void* v, const void* spec, void* r, int64_t B, int64_t C,
-                    int64_t L, hipStream_t stream)
+                    int64_t L, hipStream_t stream, bool rev = false)
 {
     DeviceState* d = nullptr;
     sc_status st = device_state(&d, false);
@@ -647,7 +647,7 @@ sc_status apply_run(sc_kind kind, const void* v, const void* spec, void* r, int6
         const int64_t nb = std::min<int64_t>(rows, B - b0);
         const hipError_t e = sc::launch_shared_apply(
             s, (const char*)v + b0 * row, (const float2*)spec, (char*)r + b0 * row, (int)nb,
-            (int)C, (int)L, M, kDefaultHead, d->fused_tw, stream);
+            (int)C, (int)L, M, kDefaultHead, rev, d->fused_tw, stream);
         if (e != hipSuccess) return SC_ERR_HIP;
     }
     return SC_OK;
@@ -679,7 +679,96 @@ sc_status shared_run(sc_kind kind, const void* v, const void* k, void* r, int64_
     return st;
 }
 
+// gradients for a filter shared by the batch: dv from the spectrum (made here from k when
+// spec is null), dk by the batch-summing kernel
+sc_status shared_bwd_run(sc_kind kind, const void* dr, const void* v, const void* k,
+                         const void* spec, void* dv, void* dk, int64_t B, int64_t C, int64_t L,
+                         hipStream_t stream)
+{
+    int64_t n = 0;
+    sc_status st = check_shape(kind, B, C, L, &n);
+    if (st != SC_OK) return st;
+    if (kind != SC_KIND_F32 && kind != SC_KIND_BF16) return SC_ERR_INVALID_ARGUMENT;
+    if (L > kMaxLFused) return SC_ERR_UNSUPPORTED;
+    if (n == 0) return SC_OK;
+    const size_t es = elt_size(kind);
+    if ((__int128)C * L * (int64_t)es >= ((__int128)1 << 31)) return SC_ERR_UNSUPPORTED;
+    const void* filt = spec ? spec : k;
+    if (!dr || !v || !filt || !dv || !dk) return SC_ERR_INVALID_ARGUMENT;
+    if (((uintptr_t)dr | (uintptr_t)v | (uintptr_t)dv | (uintptr_t)dk) % es)
+        return SC_ERR_INVALID_ARGUMENT;
+    if (spec ? (uintptr_t)spec % sizeof(float2) : (uintptr_t)k % es) return SC_ERR_INVALID_ARGUMENT;
+    const uint64_t nb = (uint64_t)n * es, kb = (uint64_t)(C * L) * es;
+    const uint64_t fb = spec ? sc_filter_spectrum_bytes(C, L) : kb;
+    struct Buf { const void* p; uint64_t b; };
+    const Buf ins[3] = {{dr, nb}, {v, nb}, {filt, fb}};
+    const Buf outs[2] = {{dv, nb}, {dk, kb}};
+    for (const Buf& o : outs)
+        for (const Buf& i : ins)
+            if ((uintptr_t)o.p < (uintptr_t)i.p + i.b && (uintptr_t)i.p < (uintptr_t)o.p + o.b)
+                return SC_ERR_INVALID_ARGUMENT;
+    if ((uintptr_t)dv < (uintptr_t)dk + kb && (uintptr_t)dk < (uintptr_t)dv + nb)
+        return SC_ERR_INVALID_ARGUMENT;
+    DeviceState* d = nullptr;
+    st = device_state(&d, false);
+    if (st != SC_OK) return st;
+    void* own = nullptr;
+    if (!spec) {
+        if (hipMallocAsync(&own, sc_filter_spectrum_bytes(C, L), stream) != hipSuccess)
+            return SC_ERR_HIP;
+        st = spectrum_run(kind, k, own, C, L, stream);
+        spec = own;
+    }
+    if (st == SC_OK) st = apply_run(kind, dr, spec, dv, B, C, L, stream, true);
+    if (st == SC_OK) {
+        const int M = (int)std::max<int64_t>(64, next_pow2(L));
+        const sc::Store s = kind == SC_KIND_F32 ? sc::Store::F32 : sc::Store::BF16;
+        const bool pair = L % 2 == 0 && (uintptr_t)dk % (2 * es) == 0;
+        if (sc::launch_shared_dk(s, dr, v, dk, (int)B, (int)C, (int)L, M, kDefaultHead, pair,
+                                 d->fused_tw, stream) != hipSuccess)
+            st = SC_ERR_HIP;
+    }
+    if (own && hipFreeAsync(own, stream) != hipSuccess && st == SC_OK) st = SC_ERR_HIP;
+    return st;
+}
+
 }  // namespace
+
+sc_status sc_causal_conv_spec_bwd_f32(const float* dr, const float* v, const void* spec,
+                                      float* dv, float* dk, int64_t B, int64_t C, int64_t L,
+                                      hipStream_t stream)
+{
+    return guarded([&] {
+        return shared_bwd_run(SC_KIND_F32, dr, v, nullptr, spec, dv, dk, B, C, L, stream);
+    });
+}
+
+sc_status sc_causal_conv_spec_bwd_bf16(const uint16_t* dr, const uint16_t* v, const void* spec,
+                                       uint16_t* dv, uint16_t* dk, int64_t B, int64_t C,
+                                       int64_t L, hipStream_t stream)
+{
+    return guarded([&] {
+        return shared_bwd_run(SC_KIND_BF16, dr, v, nullptr, spec, dv, dk, B, C, L, stream);
+    });
+}
+
+sc_status sc_causal_conv_shared_bwd_f32(const float* dr, const float* v, const float* k, float* dv,
+                                        float* dk, int64_t B, int64_t C, int64_t L,
+                                        hipStream_t stream)
+{
+    return guarded([&] {
+        return shared_bwd_run(SC_KIND_F32, dr, v, k, nullptr, dv, dk, B, C, L, stream);
+    });
+}
+
+sc_status sc_causal_conv_shared_bwd_bf16(const uint16_t* dr, const uint16_t* v, const uint16_t* k,
+                                         uint16_t* dv, uint16_t* dk, int64_t B, int64_t C,
+                                         int64_t L, hipStream_t stream)
+{
+    return guarded([&] {
+        return shared_bwd_run(SC_KIND_BF16, dr, v, k, nullptr, dv, dk, B, C, L, stream);
+    });
+}
 
 sc_status sc_filter_spectrum_f32(const float* k, void* spec, int64_t C, int64_t L,
                                  hipStream_t stream)
@@ -746,6 +835,6 @@ const char* sc_status_string(sc_status s)
     }
 }
 
-int sc_version(void) { return 400; }
+int sc_version(void) { return 500; }
 
 }  // extern "C"

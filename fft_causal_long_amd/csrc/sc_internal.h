@@ -91,8 +91,13 @@ hipError_t launch_shared_spectrum(Store st, const void* k, float2* spec, int C, 
                                   const float2* tw, hipStream_t stream);
 // r[b][c][t] = sum_{j<=t} v[b][c][j] k[c][t-j] from the spectrum; B * C * L elements of v and
 // r must stay below 2^31 bytes (the host splits larger batches).
+// With rev: r[b][c][j] = sum_{t>=j} v[b][c][t] k[c][t-j] (the gradient dv for v = dr).
 hipError_t launch_shared_apply(Store st, const void* v, const float2* spec, void* r, int B, int C,
-                               int L, int M, int head, const float2* tw, hipStream_t stream);
+                               int L, int M, int head, bool rev, const float2* tw,
+                               hipStream_t stream);
+// dk[c][j] = sum_b sum_{t>=j} dr[b][c][t] v[b][c][t-j]; pair_store as the fused kernel's.
+hipError_t launch_shared_dk(Store st, const void* dr, const void* v, void* dk, int B, int C, int L,
+                            int M, int head, bool pair_store, const float2* tw, hipStream_t stream);
 
 // Direct summation r_t = sum_{j<=t} v_j g_{t-j} in fp32, one thread per output.
 hipError_t launch_direct(Store st, const void* v, const void* g, void* r, int64_t nch, int L,

@@ -112,7 +112,9 @@ __global__ __launch_bounds__(SH_THREADS) void shared_spectrum_kernel(
 
 // ---------------------------------------------------------------- apply
 
-template <int M, class IO>
+// REV (the gradient dv): v is read reversed and r written reversed, so with v = dr the
+// kernel gives dv[b][c][j] = sum_{t>=j} dr[b][c][t] k[c][t-j].
+template <int M, class IO, bool REV>
 __global__ __launch_bounds__(SH_THREADS, (M >= 512 ? 4 : 1)) void shared_apply_kernel(
     const typename IO::T* __restrict__ v, const float2* __restrict__ spec,
     typename IO::T* __restrict__ r, int B, int C, int L, int head,
@@ -156,15 +158,17 @@ __global__ __launch_bounds__(SH_THREADS, (M >= 512 ? 4 : 1)) void shared_apply_k
 #pragma unroll
         for (int q = 0; q < 16; ++q) {
             const int n = tau + TB * q;
-            const float f0 = IO::load(vs, a0 + n), f1 = IO::load(vs, a1 + n);
+            const int nn = REV ? L - 1 - n : n;
+            const float f0 = IO::load(vs, a0 + nn), f1 = IO::load(vs, a1 + nn);
             x[q] = make_float2(m0 ? f0 : 0.f, m1 ? f1 : 0.f);
         }
     } else {
 #pragma unroll
         for (int q = 0; q < 16; ++q) {
             const int n = tau + TB * q;
-            const int e0 = (jv && n < L) ? row0 + n : IO::OOB;
-            const int e1 = (jv && has1 && n < L) ? row1 + n : IO::OOB;
+            const int nn = REV ? L - 1 - n : n;
+            const int e0 = (jv && n < L) ? row0 + nn : IO::OOB;
+            const int e1 = (jv && has1 && n < L) ? row1 + nn : IO::OOB;
             x[q] = make_float2(IO::load(vs, e0), IO::load(vs, e1));
         }
     }
@@ -215,8 +219,9 @@ __global__ __launch_bounds__(SH_THREADS, (M >= 512 ? 4 : 1)) void shared_apply_k
                 const int n = tau + TB * q;
                 if (n < head || n >= L) continue;
                 const float2 y = cadd(x[q], xch[lds_pad(n)]);
-                IO::store(rs, row0 + n, y.x);
-                if (has1) IO::store(rs, row1 + n, y.y);
+                const int nn = REV ? L - 1 - n : n;
+                IO::store(rs, row0 + nn, y.x);
+                if (has1) IO::store(rs, row1 + nn, y.y);
             }
         }
     } else if (jv) {
@@ -237,7 +242,7 @@ __global__ __launch_bounds__(SH_THREADS, (M >= 512 ? 4 : 1)) void shared_apply_k
                 }
                 for (int d = 1; d < S; d <<= 1) acc += __shfl_xor(acc, d);
                 if (o < nout && s == 0 && t < L && (row == 0 || has1))
-                    IO::store(rs, (row ? row1 : row0) + t, acc);
+                    IO::store(rs, (row ? row1 : row0) + (REV ? L - 1 - t : t), acc);
             }
         } else {
             // units narrower than a wave: one lane per output
@@ -248,7 +253,155 @@ __global__ __launch_bounds__(SH_THREADS, (M >= 512 ? 4 : 1)) void shared_apply_k
                 const float* hk = hb + 2 * SH_HEAD_MAX;
                 float acc = 0.f;
                 for (int j = 0; j <= t; ++j) acc = __builtin_fmaf(hv[j], hk[t - j], acc);
-                IO::store(rs, (row ? row1 : row0) + t, acc);
+                IO::store(rs, (row ? row1 : row0) + (REV ? L - 1 - t : t), acc);
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------- filter gradient
+
+// dk[c][j] = sum_b sum_{t>=j} dr[b][c][t] v[b][c][t-j] = sum_b rev(causal(rev(dr_b), v_b))_j.
+// Per channel and batch row the transform of z = rev(dr_b) + i v_b carries both spectra;
+// the unpacked inverse input Y_k of the real-output inverse is linear in X = DR' V, so it is
+// summed over the rows in registers and inverted once.  The direct head (t < head) is
+// summed over the rows in LDS.  A workgroup serves 4096/M channels, as the per-row-gate
+// kernel, looping over the B rows.
+template <int M, class IO>
+__global__ __launch_bounds__(SH_THREADS) void shared_dk_kernel(
+    const typename IO::T* __restrict__ dr, const typename IO::T* __restrict__ v,
+    typename IO::T* __restrict__ dk, int B, int C, int L, int head, int pair_store,
+    const float2* __restrict__ tw)
+{
+    constexpr int N = 2 * M, TB = M / 16, UNITS = SH_THREADS / TB, CPW = UNITS / 2;
+    constexpr int CT = CPW * TB;
+    constexpr int REG = M + M / 16 + (M >= 256 ? SH_LDS_EXTRA : 0);
+    __shared__ float2 lds[UNITS * REG];
+    __shared__ float hbuf[CPW * 2 * SH_HEAD_MAX];    // rev(dr_b) then v_b, first values
+    __shared__ float hsum[CPW * SH_HEAD_MAX];        // the head, summed over the rows
+
+    const Bank bank = make_bank(tw);
+    const int tid = threadIdx.x;
+    const int unit = tid / TB, tau = tid % TB;
+    const int cl = unit >> 1, beta = unit & 1;
+    const int c0 = blockIdx.x * CPW;
+    const int nvalid = (C - c0) < CPW ? (C - c0) : CPW;
+    float2* ubuf = lds + unit * REG;
+    float2* u0 = lds + (2 * cl) * REG;
+    const float2* u1 = u0 + REG;
+    const int lt = tid - cl * 2 * TB;
+    const int cbase = cl * L;
+    // head work of the upper half: output o (of CPW * head) split over S lanes
+    const int nout = CPW * head;
+    int S = 1;
+    while (S < 8 && 2 * S * nout <= SH_THREADS - CT) S *= 2;
+    for (int i = tid; i < CPW * SH_HEAD_MAX; i += SH_THREADS) hsum[i] = 0.f;
+
+    float2 yacc[4], ymacc[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) yacc[i] = ymacc[i] = make_float2(0.f, 0.f);
+
+    for (int b = 0; b < B; ++b) {
+        const int64_t row = ((int64_t)b * C + c0) * L;
+        const Span ds_ = make_span(dr, row, (int64_t)nvalid * L);
+        const Span vs_ = make_span(v, row, (int64_t)nvalid * L);
+        float2 x[16];
+#pragma unroll
+        for (int q = 0; q < 16; ++q) {
+            const int n = tau + TB * q;
+            const int e = n < L ? cbase + n : IO::OOB;
+            const int er = n < L ? cbase + L - 1 - n : IO::OOB;
+            x[q] = make_float2(IO::load(ds_, er), IO::load(vs_, e));
+        }
+        if (!beta) {
+#pragma unroll
+            for (int q = 0; q < (TB >= SH_HEAD_MAX ? 1 : SH_HEAD_MAX / TB); ++q) {
+                const int n = tau + TB * q;
+                if (n < head) {
+                    hbuf[cl * 2 * SH_HEAD_MAX + n] = x[q].x;
+                    hbuf[cl * 2 * SH_HEAD_MAX + SH_HEAD_MAX + n] = x[q].y;
+                }
+            }
+        } else {
+#pragma unroll
+            for (int q = 0; q < 16; ++q) x[q] = cmul(x[q], tw_get<false>(bank, N, tau + TB * q));
+        }
+        fft_passes<M, false>(x, ubuf, tau, bank, true);
+#pragma unroll
+        for (int q = 0; q < 16; ++q) ubuf[reg_off<TB>(tau, q)] = x[q];
+        __syncthreads();
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int k = lt + 2 * TB * i;
+            float2 yk, ymk;
+            unpack_pair<M>(k, u0, u1, bank, yk, ymk);
+            if (k == 0) {
+                float2 unused;
+                unpack_pair<M>(M / 2, u0, u1, bank, ymk, unused);
+            }
+            yacc[i] = cadd(yacc[i], yk);
+            ymacc[i] = cadd(ymacc[i], ymk);
+        }
+        if (tid >= CT) {
+            // this row's head terms, added to hsum by the group's first lane
+            for (int base = 0; base < nout * S; base += SH_THREADS - CT) {
+                const int idx = base + tid - CT, o = idx / S, sl = idx - o * S;
+                const int c2 = o / (head > 0 ? head : 1), t = o - c2 * head;
+                float acc = 0.f;
+                if (o < nout) {
+                    const float* hv = hbuf + c2 * 2 * SH_HEAD_MAX;
+                    const float* hg = hv + SH_HEAD_MAX;
+                    for (int j = sl; j <= t; j += S) acc = __builtin_fmaf(hv[j], hg[t - j], acc);
+                }
+                for (int d = 1; d < S; d <<= 1) acc += __shfl_xor(acc, d);
+                if (o < nout && sl == 0) hsum[c2 * SH_HEAD_MAX + t] += acc;
+            }
+        }
+        __syncthreads();   // ubuf and hbuf are rewritten for the next row
+    }
+
+    // the summed Y into branch 0's region, then one inverse (as the per-row-gate kernel)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int k = lt + 2 * TB * i;
+        u0[lds_pad(k)] = yacc[i];
+        u0[lds_pad(k == 0 ? M / 2 : M - k)] = ymacc[i];
+    }
+    __syncthreads();
+    const Span ks = make_span(dk, (int64_t)c0 * L, (int64_t)nvalid * L);
+    const bool iact = tid < CT;
+    const int icl = iact ? tid / TB : 0, itau = tid % TB;
+    float2* ybuf = lds + (2 * icl) * REG;
+    float2 x[16];
+    if (iact) {
+#pragma unroll
+        for (int q = 0; q < 16; ++q) x[q] = ybuf[reg_off<TB>(itau, q)];
+    }
+    __syncthreads();
+    if (!iact) {
+        // the head, reversed like the rest: dk_{L-1-t} for t < head
+        for (int o = tid - CT; o < nout; o += SH_THREADS - CT) {
+            const int c2 = o / head, t = o - c2 * head;
+            if (c2 < nvalid && t < L) IO::store(ks, c2 * L + L - 1 - t, hsum[c2 * SH_HEAD_MAX + t]);
+        }
+    }
+    fft_passes<M, true>(x, ybuf, itau, bank, iact);
+    if (iact && icl < nvalid) {
+        const float scale = 1.0f / (8.0f * (float)M);
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+            const int t = 2 * (itau + TB * q);
+            if (t < head || t >= L) continue;
+            const float a = x[q].x * scale, bb = x[q].y * scale;
+            if (t + 1 < L) {
+                if (pair_store) {
+                    IO::store2(ks, icl * L + L - 2 - t, bb, a);
+                } else {
+                    IO::store(ks, icl * L + L - 1 - t, a);
+                    IO::store(ks, icl * L + L - 2 - t, bb);
+                }
+            } else {
+                IO::store(ks, icl * L + L - 1 - t, a);
             }
         }
     }
@@ -269,16 +422,44 @@ hipError_t spectrum_m(const void* k, float2* spec, int C, int L, const float2* t
     return hipGetLastError();
 }
 
-template <int M, class IO>
+template <int M, class IO, bool REV>
 hipError_t apply_m(const void* v, const float2* spec, void* r, int B, int C, int L, int head,
                    const float2* tw, hipStream_t s)
 {
     constexpr int JPW = (SH_THREADS / (M / 16)) / 2;
     const int64_t jobs = (int64_t)C * ((B + 1) / 2);
     const int64_t blocks = ((jobs + JPW - 1) / JPW + 7) / 8 * 8;   // a multiple of 8
-    hipLaunchKernelGGL((shared_apply_kernel<M, IO>), dim3((unsigned)blocks), dim3(SH_THREADS), 0,
+    hipLaunchKernelGGL((shared_apply_kernel<M, IO, REV>), dim3((unsigned)blocks), dim3(SH_THREADS), 0,
                        s, (const typename IO::T*)v, spec, (typename IO::T*)r, B, C, L, head, tw);
     return hipGetLastError();
+}
+
+template <int M, class IO>
+hipError_t dk_m(const void* dr, const void* v, void* dk, int B, int C, int L, int head, bool pair,
+                const float2* tw, hipStream_t s)
+{
+    constexpr int CPW = (SH_THREADS / (M / 16)) / 2;
+    const int64_t blocks = ((int64_t)C + CPW - 1) / CPW;
+    hipLaunchKernelGGL((shared_dk_kernel<M, IO>), dim3((unsigned)blocks), dim3(SH_THREADS), 0, s,
+                       (const typename IO::T*)dr, (const typename IO::T*)v, (typename IO::T*)dk, B,
+                       C, L, head, pair ? 1 : 0, tw);
+    return hipGetLastError();
+}
+
+template <class IO>
+hipError_t dk_io(const void* dr, const void* v, void* dk, int B, int C, int L, int M, int head,
+                 bool pair, const float2* tw, hipStream_t s)
+{
+    switch (M) {
+    case 64: return dk_m<64, IO>(dr, v, dk, B, C, L, head, pair, tw, s);
+    case 128: return dk_m<128, IO>(dr, v, dk, B, C, L, head, pair, tw, s);
+    case 256: return dk_m<256, IO>(dr, v, dk, B, C, L, head, pair, tw, s);
+    case 512: return dk_m<512, IO>(dr, v, dk, B, C, L, head, pair, tw, s);
+    case 1024: return dk_m<1024, IO>(dr, v, dk, B, C, L, head, pair, tw, s);
+    case 2048: return dk_m<2048, IO>(dr, v, dk, B, C, L, head, pair, tw, s);
+    case 4096: return dk_m<4096, IO>(dr, v, dk, B, C, L, head, pair, tw, s);
+    default: return hipErrorInvalidValue;
+    }
 }
 
 template <class IO>
@@ -297,18 +478,18 @@ hipError_t spectrum_io(const void* k, float2* spec, int C, int L, int M, const f
     }
 }
 
-template <class IO>
+template <class IO, bool REV>
 hipError_t apply_io(const void* v, const float2* spec, void* r, int B, int C, int L, int M,
                     int head, const float2* tw, hipStream_t s)
 {
     switch (M) {
-    case 64: return apply_m<64, IO>(v, spec, r, B, C, L, head, tw, s);
-    case 128: return apply_m<128, IO>(v, spec, r, B, C, L, head, tw, s);
-    case 256: return apply_m<256, IO>(v, spec, r, B, C, L, head, tw, s);
-    case 512: return apply_m<512, IO>(v, spec, r, B, C, L, head, tw, s);
-    case 1024: return apply_m<1024, IO>(v, spec, r, B, C, L, head, tw, s);
-    case 2048: return apply_m<2048, IO>(v, spec, r, B, C, L, head, tw, s);
-    case 4096: return apply_m<4096, IO>(v, spec, r, B, C, L, head, tw, s);
+    case 64: return apply_m<64, IO, REV>(v, spec, r, B, C, L, head, tw, s);
+    case 128: return apply_m<128, IO, REV>(v, spec, r, B, C, L, head, tw, s);
+    case 256: return apply_m<256, IO, REV>(v, spec, r, B, C, L, head, tw, s);
+    case 512: return apply_m<512, IO, REV>(v, spec, r, B, C, L, head, tw, s);
+    case 1024: return apply_m<1024, IO, REV>(v, spec, r, B, C, L, head, tw, s);
+    case 2048: return apply_m<2048, IO, REV>(v, spec, r, B, C, L, head, tw, s);
+    case 4096: return apply_m<4096, IO, REV>(v, spec, r, B, C, L, head, tw, s);
     default: return hipErrorInvalidValue;
     }
 }
@@ -323,10 +504,20 @@ hipError_t launch_shared_spectrum(Store st, const void* k, float2* spec, int C, 
 }
 
 hipError_t launch_shared_apply(Store st, const void* v, const float2* spec, void* r, int B, int C,
-                               int L, int M, int head, const float2* tw, hipStream_t s)
+                               int L, int M, int head, bool rev, const float2* tw, hipStream_t s)
 {
-    return st == Store::F32 ? apply_io<f32_io>(v, spec, r, B, C, L, M, head, tw, s)
-                            : apply_io<bf16_io>(v, spec, r, B, C, L, M, head, tw, s);
+    if (st == Store::F32)
+        return rev ? apply_io<f32_io, true>(v, spec, r, B, C, L, M, head, tw, s)
+                   : apply_io<f32_io, false>(v, spec, r, B, C, L, M, head, tw, s);
+    return rev ? apply_io<bf16_io, true>(v, spec, r, B, C, L, M, head, tw, s)
+               : apply_io<bf16_io, false>(v, spec, r, B, C, L, M, head, tw, s);
+}
+
+hipError_t launch_shared_dk(Store st, const void* dr, const void* v, void* dk, int B, int C, int L,
+                            int M, int head, bool pair_store, const float2* tw, hipStream_t s)
+{
+    return st == Store::F32 ? dk_io<f32_io>(dr, v, dk, B, C, L, M, head, pair_store, tw, s)
+                            : dk_io<bf16_io>(dr, v, dk, B, C, L, M, head, pair_store, tw, s);
 }
 
 }  // namespace sc

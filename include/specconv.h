@@ -276,6 +276,31 @@ sc_status sc_causal_conv_shared_bf16(const uint16_t* v, const uint16_t* k, uint1
                                      int64_t B, int64_t C, int64_t L, hipStream_t stream);
 
 /*
+ * Gradients for a filter shared by the batch, for the output gradient dr (as r):
+ *     dv[b][c][j] = sum_{t=j..L-1} dr[b][c][t] k[c][t-j]
+ *     dk[c][j]    = sum_b sum_{t=j..L-1} dr[b][c][t] v[b][c][t-j]
+ * dv by the apply kernel run on dr reversed (with the filter's spectrum: the _spec_ calls
+ * take one made by sc_filter_spectrum_* for this C and L, the _shared_ calls make it in
+ * stream-ordered scratch), dk by a kernel that sums the spectral products over the batch
+ * rows and inverts once per channel.  Accuracy as the forward calls with the error scales
+ * sum_t |dr_t||k_{t-j}| and sum_b sum_t |dr_t||v_{t-j}|; the last 32 positions of dv and dk
+ * use direct fp32 summation.  dv (B*C*L elements) and dk (C*L) may overlap neither each
+ * other nor dr, v, k or the spectrum.  Limits and errors as sc_causal_conv_shared_*.
+ */
+sc_status sc_causal_conv_spec_bwd_f32(const float* dr, const float* v, const void* spec,
+                                      float* dv, float* dk, int64_t B, int64_t C, int64_t L,
+                                      hipStream_t stream);
+sc_status sc_causal_conv_spec_bwd_bf16(const uint16_t* dr, const uint16_t* v, const void* spec,
+                                       uint16_t* dv, uint16_t* dk, int64_t B, int64_t C,
+                                       int64_t L, hipStream_t stream);
+sc_status sc_causal_conv_shared_bwd_f32(const float* dr, const float* v, const float* k, float* dv,
+                                        float* dk, int64_t B, int64_t C, int64_t L,
+                                        hipStream_t stream);
+sc_status sc_causal_conv_shared_bwd_bf16(const uint16_t* dr, const uint16_t* v, const uint16_t* k,
+                                         uint16_t* dv, uint16_t* dk, int64_t B, int64_t C,
+                                         int64_t L, hipStream_t stream);
+
+/*
  * sc_ntt_range_ok -- 1 if every |v_j| <= max_abs_v and |g_j| <= max_abs_g guarantee that
  *   the exact sums fit the symmetric residue range, i.e. L * max_abs_v * max_abs_g <=
  *   (p-1)/2; 0 otherwise (or on negative arguments).  Host only.
@@ -285,7 +310,7 @@ int sc_ntt_range_ok(int64_t max_abs_v, int64_t max_abs_g, int64_t L);
 /* Human-readable name of a status code (static storage).  Host only. */
 const char* sc_status_string(sc_status s);
 
-/* Library version: major * 10000 + minor * 100 + patch (this header: 400).  Host only. */
+/* Library version: major * 10000 + minor * 100 + patch (this header: 500).  Host only. */
 int sc_version(void);
 
 #ifdef __cplusplus

@@ -249,3 +249,26 @@ def test_shared_filter_host_checks(sc):
         assert f(None, None, None, 0, 4, 64, None) == OK, name
     # one filter set must fit a 32-bit span: C * L * 4 bytes < 2^31
     assert h.sc_causal_conv_shared_f32(1 << 40, 2 << 40, 3 << 40, 1, 1 << 19, 4096, None) == UNSUP
+
+
+def test_shared_filter_bwd_host_checks(sc):
+    h = sc.lib()
+    INVALID, UNSUP, OK = sc.SC_ERR_INVALID_ARGUMENT, sc.SC_ERR_UNSUPPORTED, sc.SC_OK
+    for name in ("sc_causal_conv_spec_bwd_f32", "sc_causal_conv_spec_bwd_bf16",
+                 "sc_causal_conv_shared_bwd_f32", "sc_causal_conv_shared_bwd_bf16"):
+        f = getattr(h, name)
+        assert f(A, B_, C_, D_, E_, 2, 4, 5000, None) == UNSUP, name
+        for i in range(5):                                        # any null pointer
+            args = [A, B_, C_, D_, E_]
+            args[i] = None
+            assert f(*args, 2, 4, 64, None) == INVALID, (name, i)
+        assert f(A, B_, C_, A + 8, E_, 2, 4, 64, None) == INVALID, name   # dv overlaps dr
+        assert f(A, B_, C_, D_, B_ + 8, 2, 4, 64, None) == INVALID, name  # dk overlaps v
+        assert f(A, B_, C_, D_, C_, 2, 4, 64, None) == INVALID, name      # dk overlaps k
+        assert f(A, B_, C_, D_, D_ + 64, 2, 4, 64, None) == INVALID, name  # dk overlaps dv
+        assert f(A, B_, C_, D_ + 1, E_, 2, 4, 64, None) == INVALID, name  # misaligned dv
+        assert f(A, B_, C_, D_, E_, -2, 4, 64, None) == INVALID, name
+        assert f(None, None, None, None, None, 0, 4, 64, None) == OK, name
+    assert h.sc_causal_conv_spec_bwd_f32(A, B_, C_ + 4, D_, E_, 2, 4, 64, None) == INVALID
+    assert h.sc_causal_conv_shared_bwd_f32(1 << 40, 2 << 40, 3 << 40, 4 << 40, 5 << 40, 1,
+                                           1 << 19, 4096, None) == UNSUP

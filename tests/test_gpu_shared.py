@@ -10,7 +10,7 @@ import torch
 
 import oracle
 from tests.gpu_util import assert_within_bound, to_device, to_host
-from workloads import WORKLOADS, make_inputs, make_shared_filter
+from workloads import WORKLOADS, make_grad, make_inputs, make_shared_filter
 
 pytestmark = pytest.mark.gpu
 
@@ -89,3 +89,74 @@ def test_deterministic_and_causal(sc):
     c = to_host(sc.causal_conv_shared(to_device(v2), to_device(k)))
     assert np.array_equal(c[0].view(np.uint32), a[0].view(np.uint32)) or \
         np.max(np.abs(c[0] - a[0])) <= 1e-5 * np.max(np.abs(a[0]))
+
+
+# ---------------------------------------------------------------- gradients
+
+def grad_inputs(cid, B, C, L, seed):
+    w = WORKLOADS[cid]
+    v, k = inputs(cid, B, C, L, seed)
+    dr = make_grad(w, B=B, C=C, L=L, seed_offset=seed)
+    return dr, v, k
+
+
+def check_bwd(dv, dk, dr, v, k, what, chans=None):
+    bf = v.dtype == np.uint16
+    if chans is not None:
+        dr, v, k, dv, dk = dr[:, chans], v[:, chans], k[chans], dv[:, chans], dk[chans]
+    dv_ref, dk_ref, Sv, Sk = oracle.shared_conv_bwd_f64(dr, v, k)
+    a = assert_within_bound(dv, dv_ref, Sv, bf, what + " dv")
+    b = assert_within_bound(dk, dk_ref, Sk, bf, what + " dk")
+    print("%s: worst err/bound dv %.3g dk %.3g" % (what, a, b), flush=True)
+
+
+@pytest.mark.parametrize("L", [1, 5, 32, 33, 64, 100, 256, 1000, 1024, 3000, 4095, 4096])
+def test_bwd_lengths_f32(sc, L):
+    dr, v, k = grad_inputs(2, 3, 5, L, L + 50)
+    print("case shared bwd f32 L=%d" % L, flush=True)
+    dv, dk = sc.causal_conv_shared_bwd(to_device(dr), to_device(v), to_device(k))
+    check_bwd(to_host(dv), to_host(dk), dr, v, k, "shared bwd f32 L=%d" % L)
+
+
+@pytest.mark.parametrize("B,C,L", [(1, 1, 4096), (2, 7, 4096), (5, 3, 4096), (8, 16, 4096),
+                                   (3, 4, 999), (1, 2, 2)])
+def test_bwd_batch_shapes_bf16(sc, B, C, L):
+    dr, v, k = grad_inputs(3, B, C, L, B * 100 + C + 7)
+    print("case shared bwd bf16 B=%d C=%d L=%d" % (B, C, L), flush=True)
+    dv, dk = sc.causal_conv_shared_bwd(to_device(dr), to_device(v), to_device(k))
+    check_bwd(to_host(dv), to_host(dk), dr, v, k, "shared bwd bf16 B=%d C=%d L=%d" % (B, C, L))
+
+
+def test_bwd_spectrum_path_matches_one_shot(sc):
+    L, C, B = 2048, 6, 4
+    dr, v, k = grad_inputs(2, B, C, L, 21)
+    kd = to_device(k)
+    spec = sc.filter_spectrum(kd)
+    print("case shared bwd from spectrum", flush=True)
+    dv, dk = sc.causal_conv_spec_bwd(to_device(dr), to_device(v), spec, C, L)
+    dv, dk = to_host(dv), to_host(dk)
+    check_bwd(dv, dk, dr, v, k, "shared bwd spectrum")
+    dv2, dk2 = sc.causal_conv_shared_bwd(to_device(dr), to_device(v), kd)
+    assert np.array_equal(dv.view(np.uint32), to_host(dv2).view(np.uint32))
+    assert np.array_equal(dk.view(np.uint32), to_host(dk2).view(np.uint32))
+
+
+def test_bwd_odd_offset_outputs(sc):
+    # dk at an odd element offset with even L: pair stores must give way to single ones
+    dr, v, k = grad_inputs(2, 2, 3, 1000, 33)
+    dev = torch.device("cuda:0")
+    dk_buf = torch.zeros(3 * 1000 + 1, dtype=torch.float32, device=dev)
+    dk_view = dk_buf[1:].view(3, 1000)
+    print("case shared bwd odd offset", flush=True)
+    dv, dk = sc.causal_conv_shared_bwd(to_device(dr), to_device(v), to_device(k), dk=dk_view)
+    assert float(dk_buf[0]) == 0.0
+    check_bwd(to_host(dv), to_host(dk), dr, v, k, "shared bwd odd offset")
+
+
+def test_bwd_medium_shape_sampled(sc):
+    w = WORKLOADS[3]
+    dr, v, k = grad_inputs(3, w.B, w.C, w.L, 1)
+    print("case shared bwd medium full shape", flush=True)
+    dv, dk = sc.causal_conv_shared_bwd(to_device(dr), to_device(v), to_device(k))
+    check_bwd(to_host(dv), to_host(dk), dr, v, k, "shared bwd medium",
+              chans=np.array([0, 1, 511, w.C - 1]))
