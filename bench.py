@@ -298,9 +298,11 @@ def bwd_measure(sc, torch, w, dev, steps: int, warmup: int) -> dict:
 def shared_measure(sc, torch, w, dev, steps: int, warmup: int) -> dict:
     """Time the filter-shared-by-the-batch calls on the workload's shape: the apply call
     sc_causal_conv_spec_* (v and the filter spectrum resident, buffers rotated like the
-    forward) and, separately, the spectrum call sc_filter_spectrum_*.  Algorithmic bytes per
-    output: read v, write r (2 elements; the spectrum is per channel, not per output)."""
-    from workloads import make_inputs, make_shared_filter
+    forward), the spectrum call sc_filter_spectrum_*, and the gradient call
+    sc_causal_conv_spec_bwd_* (dv and dk).  Algorithmic bytes per output: read v, write r
+    (2 elements; the spectrum is per channel, not per output); for the gradients read dr and
+    v, write dv (3 elements; dk is per channel)."""
+    from workloads import make_grad, make_inputs, make_shared_filter
     bf = w.storage == "bf16"
     esz = 2 if bf else 4
     kname = "bf16" if bf else "f32"
@@ -340,6 +342,25 @@ def shared_measure(sc, torch, w, dev, steps: int, warmup: int) -> dict:
     gbps = 2 * w.outputs * esz / (t_apply * 1e-3) / 1e9
     tf = 2.0 / 3.0 * algorithmic_flops_per_output(w.L) * w.outputs / (t_apply * 1e-3) / 1e12
     del bufs
+
+    dr = make_grad(w)
+    et = torch.int16 if bf else torch.float32
+    gsets = max(1, -(-2 * CACHE_BYTES // (3 * w.outputs * esz)))
+    gbufs = [(to(dr), to(v), torch.empty(w.outputs, dtype=et, device=dev))
+             for _ in range(gsets)]
+    dk = torch.empty(w.C * w.L, dtype=et, device=dev)
+    fbwd = getattr(sc.lib(), "sc_causal_conv_spec_bwd_" + kname)
+
+    def bwd(i):
+        d, a, o = gbufs[i % gsets]
+        st = fbwd(d.data_ptr(), a.data_ptr(), spec.data_ptr(), o.data_ptr(), dk.data_ptr(),
+                  w.B, w.C, w.L, sptr)
+        if st != 0:
+            raise RuntimeError("sc_causal_conv_spec_bwd failed: %s" % sc.sc_status_string(st))
+
+    t_bwd = timed(bwd, steps)
+    del gbufs
+    gb_bwd = 3 * w.outputs * esz / (t_bwd * 1e-3) / 1e9
     return {"entry": "sc_causal_conv_spec_" + kname, "filter": "one per channel, shared by "
             "the %d batch rows (decaying random filters)" % w.B,
             "ms_per_call": round(t_apply, 5), "value": round(w.outputs / (t_apply * 1e-3), 1),
@@ -348,7 +369,12 @@ def shared_measure(sc, torch, w, dev, steps: int, warmup: int) -> dict:
                     "achieved_GBps": round(gbps, 1), "frac": round(gbps / HBM_PEAK_GBPS, 4)},
             "alu": {"achieved_TFLOPs": round(tf, 2), "peak": FP32_VECTOR_PEAK_TFLOPS,
                     "frac": round(tf / FP32_VECTOR_PEAK_TFLOPS, 4),
-                    "flops_per_output": "2/3 of the per-row-gate method's"}}
+                    "flops_per_output": "2/3 of the per-row-gate method's"},
+            "bwd": {"entry": "sc_causal_conv_spec_bwd_" + kname, "ms_per_call": round(t_bwd, 5),
+                    "value": round(w.outputs / (t_bwd * 1e-3), 1), "unit": "outputs/s",
+                    "algorithmic_bytes_per_call": 3 * w.outputs * esz,
+                    "achieved_GBps": round(gb_bwd, 1),
+                    "kernels": "apply (reversed) for dv, then the batch-summing dk kernel"}}
 
 
 def main(argv=None):

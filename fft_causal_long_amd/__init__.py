@@ -40,7 +40,9 @@ __all__ = [
     "sc_causal_conv_spec_f32", "sc_causal_conv_spec_bf16", "sc_causal_conv_shared_f32",
     "sc_causal_conv_shared_bf16", "causal_conv_spec_bwd", "causal_conv_shared_bwd",
     "sc_causal_conv_spec_bwd_f32", "sc_causal_conv_spec_bwd_bf16",
-    "sc_causal_conv_shared_bwd_f32", "sc_causal_conv_shared_bwd_bf16", "KIND_F32", "KIND_BF16", "KIND_NTT_I32", "KIND_FIXED_F32", "PATH_AUTO", "PATH_FUSED", "PATH_FOUR_STEP",
+    "sc_causal_conv_shared_bwd_f32", "sc_causal_conv_shared_bwd_bf16", "causal_conv_blc",
+    "sc_blc_workspace_bytes", "sc_causal_conv_blc_f32", "sc_causal_conv_blc_bf16",
+    "sc_causal_conv_blc_ex", "KIND_F32", "KIND_BF16", "KIND_NTT_I32", "KIND_FIXED_F32", "PATH_AUTO", "PATH_FUSED", "PATH_FOUR_STEP",
     "PATH_DIRECT", "LIB_PATH",
 ]
 
@@ -79,6 +81,15 @@ def _open():
     h.sc_causal_conv_ex.argtypes = [st, vp, vp, vp, i64, i64, i64,
                                     ctypes.POINTER(sc_options), vp, sz, vp]
     h.sc_causal_conv_ex.restype = st
+    h.sc_blc_workspace_bytes.argtypes = [st, i64, i64, i64]
+    h.sc_blc_workspace_bytes.restype = sz
+    for name in ("sc_causal_conv_blc_f32", "sc_causal_conv_blc_bf16"):
+        f = getattr(h, name)
+        f.argtypes = [vp, vp, vp, i64, i64, i64, vp]
+        f.restype = st
+    h.sc_causal_conv_blc_ex.argtypes = [st, vp, vp, vp, i64, i64, i64,
+                                        ctypes.POINTER(sc_options), vp, sz, vp]
+    h.sc_causal_conv_blc_ex.restype = st
     for name in ("sc_causal_conv_bwd_f32", "sc_causal_conv_bwd_bf16", "sc_causal_conv_bwd_ntt_i32"):
         f = getattr(h, name)
         f.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, vp]
@@ -234,6 +245,22 @@ def sc_causal_conv_shared_bwd_bf16(dr, v, k, dv, dk, B, C, L, stream):
     return _lib.sc_causal_conv_shared_bwd_bf16(dr, v, k, dv, dk, B, C, L, stream)
 
 
+def sc_blc_workspace_bytes(kind, B, L, C) -> int:
+    return int(_lib.sc_blc_workspace_bytes(kind, B, L, C))
+
+
+def sc_causal_conv_blc_f32(v, g, r, B, L, C, stream):
+    return _lib.sc_causal_conv_blc_f32(v, g, r, B, L, C, stream)
+
+
+def sc_causal_conv_blc_bf16(v, g, r, B, L, C, stream):
+    return _lib.sc_causal_conv_blc_bf16(v, g, r, B, L, C, stream)
+
+
+def sc_causal_conv_blc_ex(kind, v, g, r, B, L, C, opt, ws, ws_bytes, stream):
+    return _lib.sc_causal_conv_blc_ex(kind, v, g, r, B, L, C, opt, ws, ws_bytes, stream)
+
+
 def sc_workspace_bytes(kind, B, C, L) -> int:
     return int(_lib.sc_workspace_bytes(kind, B, C, L))
 
@@ -315,6 +342,44 @@ def causal_conv(v: torch.Tensor, g: torch.Tensor, out: torch.Tensor | None = Non
                                         B, C, L, ctypes.byref(opt), ws_ptr, ws_bytes, stream)
     if st != SC_OK:
         raise SpecConvError(st, "causal_conv")
+    return out
+
+
+def causal_conv_blc(v: torch.Tensor, g: torch.Tensor, out: torch.Tensor | None = None, *,
+                    path: int | None = None, head: int | None = None,
+                    workspace: torch.Tensor | None = None) -> torch.Tensor:
+    """r[..., t, c] = sum_{j<=t} v[..., j, c] g[..., t-j, c]: the causal convolution along the
+    second-to-last axis of token-major (..., L, C) tensors (sc_causal_conv_blc_ex).  Kinds as
+    :func:`causal_conv` (float32, bfloat16, int32 exact); ``workspace`` optional, at least
+    sc_blc_workspace_bytes(kind, B, L, C) bytes."""
+    if v.shape != g.shape or v.dtype != g.dtype:
+        raise ValueError("v and g must have the same shape and dtype")
+    if v.dtype not in _KIND_OF_DTYPE:
+        raise TypeError("unsupported dtype %s" % v.dtype)
+    if not (v.is_cuda and g.is_cuda) or v.device != g.device:
+        raise ValueError("v and g must be on the same GPU")
+    if not (v.is_contiguous() and g.is_contiguous()):
+        raise ValueError("v and g must be contiguous")
+    if v.dim() < 2:
+        raise ValueError("v must be (..., L, C)")
+    out = _out_like(v, out, "out")
+    L, C = int(v.shape[-2]), int(v.shape[-1])
+    B = 1
+    for s_ in v.shape[:-2]:
+        B *= int(s_)
+    kind = _KIND_OF_DTYPE[v.dtype]
+    ws_ptr, ws_bytes = None, 0
+    if workspace is not None:
+        if not workspace.is_cuda or workspace.device != v.device or not workspace.is_contiguous():
+            raise ValueError("workspace must be a contiguous tensor on v's device")
+        ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
+    opt = sc_options(PATH_AUTO if path is None else int(path), -1 if head is None else int(head))
+    with torch.cuda.device(v.device):
+        stream = torch.cuda.current_stream(v.device).cuda_stream
+        st = _lib.sc_causal_conv_blc_ex(kind, v.data_ptr(), g.data_ptr(), out.data_ptr(), B, L,
+                                        C, ctypes.byref(opt), ws_ptr, ws_bytes, stream)
+    if st != SC_OK:
+        raise SpecConvError(st, "causal_conv_blc")
     return out
 
 

@@ -420,6 +420,110 @@ sc_status run_bwd(sc_kind kind, const void* dr, const void* v, const void* g, vo
     return run_jobs(kind, jobs, 2, true, n, B, C, L, opt, ws, ws_bytes, stream);
 }
 
+// ---------------------------------------------------------------- token-major layout
+
+// Elements per staged buffer of the token-major calls: three such buffers (v, g, r of one
+// chunk) stay well inside the 256 MB last-level cache.
+constexpr int64_t kBlcChunkElems = (int64_t)8 << 20;
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+struct BlcPlan {
+    int64_t nb, cw;   // batch rows and channels per chunk
+    size_t stage;     // bytes of one staged buffer
+    size_t inner;     // scratch of the convolution path for one chunk
+    size_t total;
+};
+
+// Chunks of whole batch rows when one row's C L elements fit a buffer, else blocks of 64k
+// channels of one row.
+sc_status blc_plan(sc_kind kind, int64_t B, int64_t L, int64_t C, const sc_options* opt,
+                   BlcPlan* p)
+{
+    if (C * L <= kBlcChunkElems) {
+        p->cw = C;
+        p->nb = std::min<int64_t>(B, std::max<int64_t>(1, kBlcChunkElems / (C * L)));
+    } else {
+        p->nb = 1;
+        p->cw = std::min<int64_t>(C, std::max<int64_t>(64, kBlcChunkElems / L / 64 * 64));
+    }
+    const int64_t nch = p->nb * p->cw;
+    p->stage = align256((size_t)(nch * L) * elt_size(kind));
+    sc_path path;
+    const sc_status st = resolve_path(kind, L, opt ? opt->path : SC_PATH_AUTO, &path);
+    if (st != SC_OK) return st;
+    p->inner = 0;
+    if (kind == SC_KIND_FIXED_F32) {
+        p->inner = fixed_bytes(nch * L);
+    } else if (path == SC_PATH_FOUR_STEP) {
+        int64_t chunk;
+        fourstep_plan(nch, L, &chunk, &p->inner);
+    }
+    p->total = 3 * p->stage + align256(p->inner);
+    return SC_OK;
+}
+
+// v, g, r in (B, L, C): per chunk, transpose v and g into channel rows, convolve, transpose
+// the result back.
+sc_status blc_run(sc_kind kind, const void* v, const void* g, void* r, int64_t B, int64_t L,
+                  int64_t C, const sc_options* opt, void* ws, size_t ws_bytes, hipStream_t stream)
+{
+    int64_t n = 0;
+    sc_status st = check_args(kind, v, g, r, B, C, L, &n);
+    if (st != SC_OK) return st;
+    sc_path path;
+    st = resolve_path(kind, L, opt ? opt->path : SC_PATH_AUTO, &path);
+    if (st != SC_OK) return st;
+    if (n == 0) return SC_OK;
+    BlcPlan p;
+    st = blc_plan(kind, B, L, C, opt, &p);
+    if (st != SC_OK) return st;
+    const size_t es = elt_size(kind);
+    if (ws) {
+        if (ws_bytes < p.total) return SC_ERR_WORKSPACE;
+        if ((uintptr_t)ws % 256) return SC_ERR_INVALID_ARGUMENT;
+        const uintptr_t w0 = (uintptr_t)ws, w1 = w0 + p.total, nbytes = (uintptr_t)n * es;
+        for (const void* t : {v, g, (const void*)r})
+            if ((uintptr_t)t < w1 && w0 < (uintptr_t)t + nbytes) return SC_ERR_INVALID_ARGUMENT;
+    } else if (ws_bytes) {
+        return SC_ERR_INVALID_ARGUMENT;
+    }
+    DeviceState* d = nullptr;
+    st = device_state(&d, exact_kind(kind));
+    if (st != SC_OK) return st;
+    void* base = ws;
+    bool own = false;
+    if (!ws) {
+        if (hipMallocAsync(&base, p.total, stream) != hipSuccess) return SC_ERR_HIP;
+        own = true;
+    }
+    char* wv = (char*)base;
+    char* wg = wv + p.stage;
+    char* wr = wg + p.stage;
+    void* inner = p.inner ? (void*)(wr + p.stage) : nullptr;
+    for (int64_t b0 = 0; b0 < B && st == SC_OK; b0 += p.nb) {
+        const int64_t nb = std::min(p.nb, B - b0);
+        for (int64_t c0 = 0; c0 < C && st == SC_OK; c0 += p.cw) {
+            const int64_t cw = std::min(p.cw, C - c0);
+            const int64_t off = (b0 * L * C + c0) * (int64_t)es;
+            if (sc::launch_transpose((int)es, (const char*)v + off, wv, (const char*)g + off, wg, L,
+                                     cw, C, L, L * C, cw * L, nb, stream) != hipSuccess) {
+                st = SC_ERR_HIP;
+                break;
+            }
+            const Job job{wv, wg, wr};
+            st = run_jobs(kind, &job, 1, false, nb * cw * L, nb, cw, L, opt, inner,
+                          inner ? p.inner : 0, stream);
+            if (st != SC_OK) break;
+            if (sc::launch_transpose((int)es, wr, (char*)r + off, nullptr, nullptr, cw, L, L, C,
+                                     cw * L, L * C, nb, stream) != hipSuccess)
+                st = SC_ERR_HIP;
+        }
+    }
+    if (own && hipFreeAsync(base, stream) != hipSuccess && st == SC_OK) st = SC_ERR_HIP;
+    return st;
+}
+
 template <class F>
 sc_status guarded(F&& f)
 {
@@ -469,6 +573,38 @@ size_t sc_workspace_bytes(sc_kind kind, int64_t B, int64_t C, int64_t L)
     } catch (...) {
         return 0;
     }
+}
+
+size_t sc_blc_workspace_bytes(sc_kind kind, int64_t B, int64_t L, int64_t C)
+{
+    try {
+        int64_t n = 0;
+        if (check_shape(kind, B, C, L, &n) != SC_OK || n == 0) return 0;
+        BlcPlan p;
+        if (blc_plan(kind, B, L, C, nullptr, &p) != SC_OK) return 0;
+        return p.total;
+    } catch (...) {
+        return 0;
+    }
+}
+
+sc_status sc_causal_conv_blc_f32(const float* v, const float* g, float* r, int64_t B, int64_t L,
+                                 int64_t C, hipStream_t stream)
+{
+    return guarded([&] { return blc_run(SC_KIND_F32, v, g, r, B, L, C, nullptr, nullptr, 0, stream); });
+}
+
+sc_status sc_causal_conv_blc_bf16(const uint16_t* v, const uint16_t* g, uint16_t* r, int64_t B,
+                                  int64_t L, int64_t C, hipStream_t stream)
+{
+    return guarded([&] { return blc_run(SC_KIND_BF16, v, g, r, B, L, C, nullptr, nullptr, 0, stream); });
+}
+
+sc_status sc_causal_conv_blc_ex(sc_kind kind, const void* v, const void* g, void* r, int64_t B,
+                                int64_t L, int64_t C, const sc_options* opt, void* ws,
+                                size_t ws_bytes, hipStream_t stream)
+{
+    return guarded([&] { return blc_run(kind, v, g, r, B, L, C, opt, ws, ws_bytes, stream); });
 }
 
 sc_status sc_causal_conv_f32_ws(const float* v, const float* g, float* r, int64_t B, int64_t C,
@@ -835,6 +971,6 @@ const char* sc_status_string(sc_status s)
     }
 }
 
-int sc_version(void) { return 500; }
+int sc_version(void) { return 600; }
 
 }  // extern "C"

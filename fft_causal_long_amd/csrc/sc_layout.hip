@@ -1,0 +1,91 @@
+// Layout change between the token-major (B, L, C) tensors of a model layer and the
+// channel-major rows the convolution kernels read (gfx950).
+//
+// The Caracal notes build v and g by linear projections of the normalised activations
+// ("Caracal: Causal Architecture via Spectral Mixing", key design 1), so in a model they
+// arrive token-major: element (b, t, c) at (b L + t) C + c.  A convolution workgroup needs
+// one channel's whole sequence; read in place, every 128-byte line of a (B, L, C) tensor
+// carries 32 to 64 channels of one position, so each workgroup would pull a line through
+// L2 for each 2 or 4 useful bytes.  The library instead moves a chunk of channels at a
+// time between the two layouts with this tiled transpose (both sides coalesced) into a
+// workspace small enough to stay in the 256 MB last-level cache, and runs the ordinary
+// kernels on the workspace.
+//
+// transpose_kernel: for each of npair (src, dst) pairs and each batch z < nz,
+//     dst[z dz + j ds + i] = src[z sz + i ss + j],   i < R, j < Cc
+// in 64 x 64 tiles through LDS; one workgroup per tile, the tiles of all pairs and batches
+// in one flat grid.  Elements are moved as raw 2- or 4-byte words.
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "sc_internal.h"
+
+namespace sc {
+
+namespace {
+
+constexpr int TT = 64;          // tile edge
+constexpr int TP_THREADS = 256;
+
+template <typename W>
+__global__ __launch_bounds__(TP_THREADS) void transpose_kernel(
+    const W* __restrict__ src0, W* __restrict__ dst0, const W* __restrict__ src1,
+    W* __restrict__ dst1, int64_t R, int64_t Cc, int64_t ss, int64_t ds, int64_t sz, int64_t dz,
+    int64_t nz, int64_t tr, int64_t tc)
+{
+    __shared__ uint32_t tile[TT][TT + 1];
+    int64_t id = blockIdx.x;
+    const int64_t jt = id % tc;
+    id /= tc;
+    const int64_t it = id % tr;
+    id /= tr;
+    const int64_t z = id % nz;
+    const int pair = (int)(id / nz);
+    const W* src = (pair ? src1 : src0) + z * sz;
+    W* dst = (pair ? dst1 : dst0) + z * dz;
+    const int64_t i0 = it * TT, j0 = jt * TT;
+    const int tx = threadIdx.x % TT, ty = threadIdx.x / TT;
+
+    // rows i0 + ty + 4k of the source, columns j0 + tx: one coalesced row per wave
+    const bool jin = j0 + tx < Cc;
+#pragma unroll
+    for (int k = 0; k < TT / 4; ++k) {
+        const int ii = ty + 4 * k;
+        if (jin && i0 + ii < R) tile[ii][tx] = (uint32_t)src[(i0 + ii) * ss + j0 + tx];
+    }
+    __syncthreads();
+    // rows j0 + ty + 4k of the destination, columns i0 + tx
+    const bool iin = i0 + tx < R;
+#pragma unroll
+    for (int k = 0; k < TT / 4; ++k) {
+        const int jj = ty + 4 * k;
+        if (iin && j0 + jj < Cc) dst[(j0 + jj) * ds + i0 + tx] = (W)tile[tx][jj];
+    }
+}
+
+}  // namespace
+
+hipError_t launch_transpose(int elt_bytes, const void* src0, void* dst0, const void* src1,
+                            void* dst1, int64_t R, int64_t Cc, int64_t ss, int64_t ds, int64_t sz,
+                            int64_t dz, int64_t nz, hipStream_t s)
+{
+    if (R <= 0 || Cc <= 0 || nz <= 0) return hipSuccess;
+    const int64_t tr = (R + TT - 1) / TT, tc = (Cc + TT - 1) / TT;
+    const int64_t blocks = tr * tc * nz * (src1 ? 2 : 1);
+    if (blocks > 0x7fffffff) return hipErrorInvalidValue;
+    if (elt_bytes == 2)
+        hipLaunchKernelGGL(transpose_kernel<uint16_t>, dim3((unsigned)blocks), dim3(TP_THREADS), 0,
+                           s, (const uint16_t*)src0, (uint16_t*)dst0, (const uint16_t*)src1,
+                           (uint16_t*)dst1, R, Cc, ss, ds, sz, dz, nz, tr, tc);
+    else if (elt_bytes == 4)
+        hipLaunchKernelGGL(transpose_kernel<uint32_t>, dim3((unsigned)blocks), dim3(TP_THREADS), 0,
+                           s, (const uint32_t*)src0, (uint32_t*)dst0, (const uint32_t*)src1,
+                           (uint32_t*)dst1, R, Cc, ss, ds, sz, dz, nz, tr, tc);
+    else
+        return hipErrorInvalidValue;
+    return hipGetLastError();
+}
+
+}  // namespace sc

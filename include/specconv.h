@@ -198,6 +198,37 @@ sc_status sc_causal_conv_ex(sc_kind kind, const void* v, const void* g, void* r,
                             size_t ws_bytes, hipStream_t stream);
 
 /*
+ * Token-major layout.  In the Caracal layer v and g are linear projections (for g, followed
+ * by a grouped convolution) of the normalised activations ("Caracal: Causal Architecture
+ * via Spectral Mixing", key design 1), so a model holds them token-major, (B, L, C):
+ * element (b, t, c) at (b L + t) C + c.  These calls take v, g and r in that layout and
+ * compute the same r as sc_causal_conv_* (every kind and path, same accuracy and limits;
+ * the argument order B, L, C follows the layout).  They move a chunk of channels at a
+ * time into channel rows in a staging workspace, run the ordinary kernels there and move
+ * the result back, so no caller transpose of the whole tensors is needed.
+ *
+ *  sc_blc_workspace_bytes(kind, B, L, C) -- bytes of that workspace (three staging buffers
+ *      of at most 2^23 elements each, plus the path's own scratch for one chunk); 0 for
+ *      invalid arguments or an empty call.
+ *  sc_causal_conv_blc_f32 / _bf16 -- allocate the workspace stream-ordered
+ *      (hipMallocAsync / hipFreeAsync on `stream`).
+ *  sc_causal_conv_blc_ex -- any kind, with options as sc_causal_conv_ex and a caller
+ *      workspace: ws null (the call allocates) with ws_bytes 0, or a 256-byte aligned
+ *      device buffer of at least sc_blc_workspace_bytes(kind, B, L, C) bytes (else
+ *      SC_ERR_WORKSPACE) that overlaps none of v, g, r (else SC_ERR_INVALID_ARGUMENT).
+ *
+ * r may not overlap v or g.  Errors as sc_causal_conv_ex.
+ */
+size_t sc_blc_workspace_bytes(sc_kind kind, int64_t B, int64_t L, int64_t C);
+sc_status sc_causal_conv_blc_f32(const float* v, const float* g, float* r, int64_t B, int64_t L,
+                                 int64_t C, hipStream_t stream);
+sc_status sc_causal_conv_blc_bf16(const uint16_t* v, const uint16_t* g, uint16_t* r, int64_t B,
+                                  int64_t L, int64_t C, hipStream_t stream);
+sc_status sc_causal_conv_blc_ex(sc_kind kind, const void* v, const void* g, void* r, int64_t B,
+                                int64_t L, int64_t C, const sc_options* opt, void* ws,
+                                size_t ws_bytes, hipStream_t stream);
+
+/*
  * Gradients (backward pass).  The Caracal models are trained end to end with a next-token
  * loss ("Caracal: Causal Architecture via Spectral Mixing", loss function / training
  * strategy), so the convolution of key design 1 needs its vector-Jacobian product: for the
@@ -310,7 +341,7 @@ int sc_ntt_range_ok(int64_t max_abs_v, int64_t max_abs_g, int64_t L);
 /* Human-readable name of a status code (static storage).  Host only. */
 const char* sc_status_string(sc_status s);
 
-/* Library version: major * 10000 + minor * 100 + patch (this header: 500).  Host only. */
+/* Library version: major * 10000 + minor * 100 + patch (this header: 600).  Host only. */
 int sc_version(void);
 
 #ifdef __cplusplus

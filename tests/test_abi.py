@@ -272,3 +272,44 @@ def test_shared_filter_bwd_host_checks(sc):
     assert h.sc_causal_conv_spec_bwd_f32(A, B_, C_ + 4, D_, E_, 2, 4, 64, None) == INVALID
     assert h.sc_causal_conv_shared_bwd_f32(1 << 40, 2 << 40, 3 << 40, 4 << 40, 5 << 40, 1,
                                            1 << 19, 4096, None) == UNSUP
+
+
+def test_token_major_host_checks(sc):
+    h = sc.lib()
+    INVALID, UNSUP, OK, WS = (sc.SC_ERR_INVALID_ARGUMENT, sc.SC_ERR_UNSUPPORTED, sc.SC_OK,
+                              sc.SC_ERR_WORKSPACE)
+    F32, BF16, NTT = sc.KIND_F32, sc.KIND_BF16, sc.KIND_NTT_I32
+    MiB = 1 << 20
+    # whole batch rows per chunk while a row's C L elements fit 2^23: here 2 rows of 4M
+    assert sc.sc_blc_workspace_bytes(F32, 8, 4096, 1024) == 3 * 32 * MiB
+    assert sc.sc_blc_workspace_bytes(BF16, 8, 4096, 1024) == 3 * 16 * MiB
+    assert sc.sc_blc_workspace_bytes(F32, 1, 256, 64) == 3 * 64 * 1024
+    # longer rows: blocks of 64k channels, plus the four-step scratch of one block
+    inner = sc.sc_workspace_bytes(F32, 1, 128, 65536)
+    assert inner > 0
+    assert sc.sc_blc_workspace_bytes(F32, 1, 65536, 1536) == 3 * 32 * MiB + (inner + 255) // 256 * 256
+    assert sc.sc_blc_workspace_bytes(NTT, 1, 8192, 4) == 0          # beyond the exact path
+    assert sc.sc_blc_workspace_bytes(F32, 0, 64, 4) == 0
+    assert sc.sc_blc_workspace_bytes(7, 1, 64, 4) == 0
+
+    opt = sc.sc_options(0, -1)
+    W = 0x10000000           # a fake 256-aligned workspace far from A, B_, C_
+    need = sc.sc_blc_workspace_bytes(F32, 2, 64, 4)
+    f = h.sc_causal_conv_blc_ex
+    assert f(F32, A, B_, C_, 2, 64, 4, None, W, need - 1, None) == WS
+    assert f(F32, A, B_, C_, 2, 64, 4, None, W + 8, need, None) == INVALID     # alignment
+    assert f(F32, A, B_, C_, 2, 64, 4, None, A - 256, need, None) == INVALID  # ws overlaps v
+    assert f(F32, A, B_, C_, 2, 64, 4, None, None, 16, None) == INVALID       # bytes, no ws
+    assert f(F32, None, B_, C_, 2, 64, 4, None, W, need, None) == INVALID
+    assert f(F32, A, B_, A + 4, 2, 64, 4, None, W, need, None) == INVALID     # r overlaps v
+    assert f(F32, A, B_, C_, -1, 64, 4, None, W, need, None) == INVALID
+    assert f(F32, A, B_, C_, 2, 64, 4, ctypes.byref(sc.sc_options(9, -1)), W, need,
+             None) == INVALID
+    assert f(NTT, A, B_, C_, 2, 8192, 4, None, W, need, None) == UNSUP
+    assert f(F32, 1 << 40, 2 << 40, 3 << 40, 1, (1 << 22) + 1, 1, None, None, 0, None) == UNSUP
+    assert f(F32, None, None, None, 0, 64, 4, ctypes.byref(opt), None, 0, None) == OK
+    for name in ("sc_causal_conv_blc_f32", "sc_causal_conv_blc_bf16"):
+        g = getattr(h, name)
+        assert g(None, B_, C_, 2, 64, 4, None) == INVALID, name
+        assert g(A, B_, B_ + 2, 2, 64, 4, None) == INVALID, name
+        assert g(None, None, None, 2, 0, 4, None) == OK, name
