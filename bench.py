@@ -9,7 +9,8 @@ After the timed region, the gradient call of the same workload (dv, dg from dr, 
 timed the same way and reported in the `bwd` object (skip with --no-bwd), and the exactly
 causal real-valued call on the same inputs in the `fixed` object (skip with --no-fixed),
 and the calls for a filter shared by the batch on the same shape in the `shared` object
-(skip with --no-shared).
+(skip with --no-shared), and the token-major (B, L, C) call on the same inputs in the
+`token_major` object (skip with --no-blc).
 Inputs are resident in HBM before the timed region.  Several copies of the buffers are
 rotated so that the 256 MB last-level cache cannot hold a step's working set.
 
@@ -377,6 +378,62 @@ def shared_measure(sc, torch, w, dev, steps: int, warmup: int) -> dict:
                     "kernels": "apply (reversed) for dv, then the batch-summing dk kernel"}}
 
 
+def blc_measure(sc, torch, w, dev, steps: int, warmup: int, conv_ms: float) -> dict:
+    """Time the token-major call sc_causal_conv_blc_ex on the workload's inputs in (B, L, C)
+    with a caller workspace (no allocation in the timed region), and beside it the same
+    result made by torch transposes around the channel-major call (what a caller would do
+    without it).  Algorithmic bytes as the channel-major call."""
+    import ctypes
+    from workloads import make_inputs
+    v, g = make_inputs(w)
+    kind = {"f32": sc.KIND_F32, "bf16": sc.KIND_BF16, "i32": sc.KIND_NTT_I32}[w.storage]
+    et = {"f32": torch.float32, "bf16": torch.bfloat16, "i32": torch.int32}[w.storage]
+    esz = {"f32": 4, "bf16": 2, "i32": 4}[w.storage]
+
+    def tm(a):
+        t = torch.from_numpy(np.ascontiguousarray(np.swapaxes(a, 1, 2)))
+        if w.storage == "bf16":
+            t = t.view(torch.int16)
+        return t.to(dev).view(et)
+    set_bytes = 3 * w.outputs * esz
+    nsets = max(1, -(-2 * CACHE_BYTES // set_bytes))
+    bufs = [(tm(v), tm(g), torch.empty((w.B, w.L, w.C), dtype=et, device=dev))
+            for _ in range(nsets)]
+    nbytes = sc.sc_blc_workspace_bytes(kind, w.B, w.L, w.C)
+    ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    sptr = stream.cuda_stream
+    fblc = sc.lib().sc_causal_conv_blc_ex
+
+    def call(i):
+        a, b, o = bufs[i % nsets]
+        st = fblc(kind, a.data_ptr(), b.data_ptr(), o.data_ptr(), w.B, w.L, w.C, None,
+                  ws.data_ptr(), nbytes, sptr)
+        if st != 0:
+            raise RuntimeError("sc_causal_conv_blc_ex failed: %s" % sc.sc_status_string(st))
+
+    def torch_route(i):
+        a, b, o = bufs[i % nsets]
+        r = sc.causal_conv(a.transpose(1, 2).contiguous(), b.transpose(1, 2).contiguous())
+        o.copy_(r.transpose(1, 2))
+
+    for i in range(warmup):
+        call(i)
+    t_blc = time_rounds(torch, stream, call, steps)[0]
+    for i in range(warmup):
+        torch_route(i)
+    t_torch = time_rounds(torch, stream, torch_route, max(3, steps // 2))[0]
+    del bufs, ws
+    return {"entry": "sc_causal_conv_blc_ex", "layout": "(B, L, C)",
+            "ms_per_call": round(t_blc, 5), "value": round(w.outputs / (t_blc * 1e-3), 1),
+            "unit": "outputs/s", "workspace_bytes": nbytes,
+            "channel_major_ms": round(conv_ms, 5),
+            "overhead_vs_channel_major": round(t_blc / conv_ms, 3),
+            "torch_transposes_ms": round(t_torch, 5),
+            "torch_transposes_note": "x.transpose(1, 2).contiguous() of v and g, the "
+                                     "channel-major call, and a copy back to (B, L, C)"}
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -391,6 +448,8 @@ def main(argv=None):
                          "forward kernel)")
     ap.add_argument("--no-shared", action="store_true",
                     help="skip the timing of the filter-shared-by-the-batch calls")
+    ap.add_argument("--no-blc", action="store_true",
+                    help="skip the timing of the token-major (B, L, C) call")
     ap.add_argument("--no-fixed", action="store_true",
                     help="skip the timing of the exactly causal real-valued call")
     ap.add_argument("--calib-copy", action="store_true",
@@ -503,6 +562,9 @@ def main(argv=None):
         rec["bwd"] = bwd_measure(sc, torch, w, dev, max(5, args.steps // 2), args.warmup)
     if not args.no_shared and w.storage != "i32" and w.L <= 4096:
         rec["shared"] = shared_measure(sc, torch, w, dev, max(5, args.steps // 2), args.warmup)
+    if not args.no_blc:
+        rec["token_major"] = blc_measure(sc, torch, w, dev, max(5, args.steps // 2), args.warmup,
+                                         kernel_ms)
     if not args.no_fixed and w.storage != "i32" and w.L <= 4096:
         rec["fixed"] = fixed_measure(sc, torch, w, dev, max(5, args.steps // 5), 2)
     if not args.no_leakage:

@@ -65,6 +65,55 @@ __global__ __launch_bounds__(TP_THREADS) void transpose_kernel(
     }
 }
 
+// The same with element pairs: each lane loads columns (j, j+1) of a source row as one
+// word and stores rows (i, i+1) of a destination row as one word (4 bytes for 2-byte
+// elements, 8 for 4-byte ones), so a wave moves two 64-element rows per instruction.  Needs
+// even R, Cc, strides and element offsets (the host checks).
+template <typename E, typename P>
+__global__ __launch_bounds__(TP_THREADS) void transpose_pair_kernel(
+    const E* __restrict__ src0, E* __restrict__ dst0, const E* __restrict__ src1,
+    E* __restrict__ dst1, int64_t R, int64_t Cc, int64_t ss, int64_t ds, int64_t sz, int64_t dz,
+    int64_t nz, int64_t tr, int64_t tc)
+{
+    __shared__ E tile[TT][TT + (sizeof(E) == 4 ? 1 : 2)];
+    int64_t id = blockIdx.x;
+    const int64_t jt = id % tc;
+    id /= tc;
+    const int64_t it = id % tr;
+    id /= tr;
+    const int64_t z = id % nz;
+    const int pair = (int)(id / nz);
+    const E* src = (pair ? src1 : src0) + z * sz;
+    E* dst = (pair ? dst1 : dst0) + z * dz;
+    const int64_t i0 = it * TT, j0 = jt * TT;
+    const int hx = threadIdx.x % (TT / 2), hy = threadIdx.x / (TT / 2);   // 32 x 8
+
+    const bool jin = j0 + 2 * hx < Cc;
+#pragma unroll
+    for (int k = 0; k < TT / 8; ++k) {
+        const int ii = hy + 8 * k;
+        if (jin && i0 + ii < R) {
+            const P w = *(const P*)(src + (i0 + ii) * ss + j0 + 2 * hx);
+            const E* e = (const E*)&w;
+            tile[ii][2 * hx] = e[0];
+            tile[ii][2 * hx + 1] = e[1];
+        }
+    }
+    __syncthreads();
+    const bool iin = i0 + 2 * hx < R;
+#pragma unroll
+    for (int k = 0; k < TT / 8; ++k) {
+        const int jj = hy + 8 * k;
+        if (iin && j0 + jj < Cc) {
+            P w;
+            E* e = (E*)&w;
+            e[0] = tile[2 * hx][jj];
+            e[1] = tile[2 * hx + 1][jj];
+            *(P*)(dst + (j0 + jj) * ds + i0 + 2 * hx) = w;
+        }
+    }
+}
+
 }  // namespace
 
 hipError_t launch_transpose(int elt_bytes, const void* src0, void* dst0, const void* src1,
@@ -75,6 +124,23 @@ hipError_t launch_transpose(int elt_bytes, const void* src0, void* dst0, const v
     const int64_t tr = (R + TT - 1) / TT, tc = (Cc + TT - 1) / TT;
     const int64_t blocks = tr * tc * nz * (src1 ? 2 : 1);
     if (blocks > 0x7fffffff) return hipErrorInvalidValue;
+    const bool even = ((R | Cc | ss | ds | sz | dz) & 1) == 0 &&
+                      ((uintptr_t)src0 | (uintptr_t)dst0 | (uintptr_t)src1 | (uintptr_t)dst1) %
+                              (2 * elt_bytes) == 0;
+    if (even && elt_bytes == 2) {
+        hipLaunchKernelGGL((transpose_pair_kernel<uint16_t, uint32_t>), dim3((unsigned)blocks),
+                           dim3(TP_THREADS), 0, s, (const uint16_t*)src0, (uint16_t*)dst0,
+                           (const uint16_t*)src1, (uint16_t*)dst1, R, Cc, ss, ds, sz, dz, nz, tr,
+                           tc);
+        return hipGetLastError();
+    }
+    if (even && elt_bytes == 4) {
+        hipLaunchKernelGGL((transpose_pair_kernel<uint32_t, uint2>), dim3((unsigned)blocks),
+                           dim3(TP_THREADS), 0, s, (const uint32_t*)src0, (uint32_t*)dst0,
+                           (const uint32_t*)src1, (uint32_t*)dst1, R, Cc, ss, ds, sz, dz, nz, tr,
+                           tc);
+        return hipGetLastError();
+    }
     if (elt_bytes == 2)
         hipLaunchKernelGGL(transpose_kernel<uint16_t>, dim3((unsigned)blocks), dim3(TP_THREADS), 0,
                            s, (const uint16_t*)src0, (uint16_t*)dst0, (const uint16_t*)src1,
