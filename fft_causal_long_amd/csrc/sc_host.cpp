@@ -507,7 +507,7 @@ sc_status blc_run(sc_kind kind, const void* v, const void* g, void* r, int64_t B
             const int64_t cw = std::min(p.cw, C - c0);
             const int64_t off = (b0 * L * C + c0) * (int64_t)es;
             if (sc::launch_transpose((int)es, (const char*)v + off, wv, (const char*)g + off, wg, L,
-                                     cw, C, L, L * C, cw * L, nb, stream) != hipSuccess) {
+                                     cw, C, L, L * C, cw * L, nb, false, stream) != hipSuccess) {
                 st = SC_ERR_HIP;
                 break;
             }
@@ -516,7 +516,7 @@ sc_status blc_run(sc_kind kind, const void* v, const void* g, void* r, int64_t B
                           inner ? p.inner : 0, stream);
             if (st != SC_OK) break;
             if (sc::launch_transpose((int)es, wr, (char*)r + off, nullptr, nullptr, cw, L, L, C,
-                                     cw * L, L * C, nb, stream) != hipSuccess)
+                                     cw * L, L * C, nb, true, stream) != hipSuccess)
                 st = SC_ERR_HIP;
         }
     }

@@ -104,9 +104,11 @@ hipError_t launch_direct(Store st, const void* v, const void* g, void* r, int64_
                          bool rev, hipStream_t stream);
 
 // dst[z dz + j ds + i] = src[z sz + i ss + j] for i < R, j < Cc, z < nz, of 2- or 4-byte
-// elements, for the pair (src0, dst0) and, when src1 is not null, (src1, dst1)
+// elements, for the pair (src0, dst0) and, when src1 is not null, (src1, dst1); dst_major
+// orders the tiles along the destination rows (for a destination in HBM), else along the
+// source rows
 hipError_t launch_transpose(int elt_bytes, const void* src0, void* dst0, const void* src1,
                             void* dst1, int64_t R, int64_t Cc, int64_t ss, int64_t ds, int64_t sz,
-                            int64_t dz, int64_t nz, hipStream_t s);
+                            int64_t dz, int64_t nz, bool dst_major, hipStream_t s);
 
 }  // namespace sc

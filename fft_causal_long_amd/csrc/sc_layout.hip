@@ -33,28 +33,43 @@ template <typename W>
 __global__ __launch_bounds__(TP_THREADS) void transpose_kernel(
     const W* __restrict__ src0, W* __restrict__ dst0, const W* __restrict__ src1,
     W* __restrict__ dst1, int64_t R, int64_t Cc, int64_t ss, int64_t ds, int64_t sz, int64_t dz,
-    int64_t nz, int64_t tr, int64_t tc)
+    int64_t nz, int64_t tr, int64_t tc, int dst_major)
 {
     __shared__ uint32_t tile[TT][TT + 1];
-    int64_t id = blockIdx.x;
-    const int64_t jt = id % tc;
-    id /= tc;
-    const int64_t it = id % tr;
-    id /= tr;
-    const int64_t z = id % nz;
-    const int pair = (int)(id / nz);
+    // consecutive workgroups take neighbouring tiles along the source rows, or with
+    // dst_major along the destination rows, so that the side in HBM is visited in order
+    // (the grid has fewer than 2^31 tiles, so the decomposition runs in 32 bits)
+    uint32_t id = blockIdx.x, it, jt;
+    if (dst_major) {
+        it = id % (uint32_t)tr;
+        id /= (uint32_t)tr;
+        jt = id % (uint32_t)tc;
+        id /= (uint32_t)tc;
+    } else {
+        jt = id % (uint32_t)tc;
+        id /= (uint32_t)tc;
+        it = id % (uint32_t)tr;
+        id /= (uint32_t)tr;
+    }
+    const int64_t z = id % (uint32_t)nz;
+    const int pair = (int)(id / (uint32_t)nz);
     const W* src = (pair ? src1 : src0) + z * sz;
     W* dst = (pair ? dst1 : dst0) + z * dz;
-    const int64_t i0 = it * TT, j0 = jt * TT;
+    const int64_t i0 = (int64_t)it * TT, j0 = (int64_t)jt * TT;
     const int tx = threadIdx.x % TT, ty = threadIdx.x / TT;
 
-    // rows i0 + ty + 4k of the source, columns j0 + tx: one coalesced row per wave
-    const bool jin = j0 + tx < Cc;
+    // rows i0 + ty + 4k of the source, columns j0 + tx: one coalesced row per wave.  Indices
+    // past the matrix are clamped to its last row / column, so every load is unconditional
+    // and all of them are in flight together; those values are never stored.
+    const int64_t jc = j0 + tx < Cc ? j0 + tx : Cc - 1;
+    uint32_t w[TT / 4];
 #pragma unroll
     for (int k = 0; k < TT / 4; ++k) {
-        const int ii = ty + 4 * k;
-        if (jin && i0 + ii < R) tile[ii][tx] = (uint32_t)src[(i0 + ii) * ss + j0 + tx];
+        const int64_t ic = i0 + ty + 4 * k < R ? i0 + ty + 4 * k : R - 1;
+        w[k] = (uint32_t)src[ic * ss + jc];
     }
+#pragma unroll
+    for (int k = 0; k < TT / 4; ++k) tile[ty + 4 * k][tx] = w[k];
     __syncthreads();
     // rows j0 + ty + 4k of the destination, columns i0 + tx
     const bool iin = i0 + tx < R;
@@ -73,31 +88,44 @@ template <typename E, typename P>
 __global__ __launch_bounds__(TP_THREADS) void transpose_pair_kernel(
     const E* __restrict__ src0, E* __restrict__ dst0, const E* __restrict__ src1,
     E* __restrict__ dst1, int64_t R, int64_t Cc, int64_t ss, int64_t ds, int64_t sz, int64_t dz,
-    int64_t nz, int64_t tr, int64_t tc)
+    int64_t nz, int64_t tr, int64_t tc, int dst_major)
 {
     __shared__ E tile[TT][TT + (sizeof(E) == 4 ? 1 : 2)];
-    int64_t id = blockIdx.x;
-    const int64_t jt = id % tc;
-    id /= tc;
-    const int64_t it = id % tr;
-    id /= tr;
-    const int64_t z = id % nz;
-    const int pair = (int)(id / nz);
+    // consecutive workgroups take neighbouring tiles along the source rows, or with
+    // dst_major along the destination rows, so that the side in HBM is visited in order
+    // (the grid has fewer than 2^31 tiles, so the decomposition runs in 32 bits)
+    uint32_t id = blockIdx.x, it, jt;
+    if (dst_major) {
+        it = id % (uint32_t)tr;
+        id /= (uint32_t)tr;
+        jt = id % (uint32_t)tc;
+        id /= (uint32_t)tc;
+    } else {
+        jt = id % (uint32_t)tc;
+        id /= (uint32_t)tc;
+        it = id % (uint32_t)tr;
+        id /= (uint32_t)tr;
+    }
+    const int64_t z = id % (uint32_t)nz;
+    const int pair = (int)(id / (uint32_t)nz);
     const E* src = (pair ? src1 : src0) + z * sz;
     E* dst = (pair ? dst1 : dst0) + z * dz;
-    const int64_t i0 = it * TT, j0 = jt * TT;
+    const int64_t i0 = (int64_t)it * TT, j0 = (int64_t)jt * TT;
     const int hx = threadIdx.x % (TT / 2), hy = threadIdx.x / (TT / 2);   // 32 x 8
 
-    const bool jin = j0 + 2 * hx < Cc;
+    // clamped, unconditional loads as in transpose_kernel (Cc is even, so Cc - 2 starts a pair)
+    const int64_t jc = j0 + 2 * hx < Cc ? j0 + 2 * hx : Cc - 2;
+    P w[TT / 8];
 #pragma unroll
     for (int k = 0; k < TT / 8; ++k) {
-        const int ii = hy + 8 * k;
-        if (jin && i0 + ii < R) {
-            const P w = *(const P*)(src + (i0 + ii) * ss + j0 + 2 * hx);
-            const E* e = (const E*)&w;
-            tile[ii][2 * hx] = e[0];
-            tile[ii][2 * hx + 1] = e[1];
-        }
+        const int64_t ic = i0 + hy + 8 * k < R ? i0 + hy + 8 * k : R - 1;
+        w[k] = *(const P*)(src + ic * ss + jc);
+    }
+#pragma unroll
+    for (int k = 0; k < TT / 8; ++k) {
+        const E* e = (const E*)&w[k];
+        tile[hy + 8 * k][2 * hx] = e[0];
+        tile[hy + 8 * k][2 * hx + 1] = e[1];
     }
     __syncthreads();
     const bool iin = i0 + 2 * hx < R;
@@ -118,7 +146,7 @@ __global__ __launch_bounds__(TP_THREADS) void transpose_pair_kernel(
 
 hipError_t launch_transpose(int elt_bytes, const void* src0, void* dst0, const void* src1,
                             void* dst1, int64_t R, int64_t Cc, int64_t ss, int64_t ds, int64_t sz,
-                            int64_t dz, int64_t nz, hipStream_t s)
+                            int64_t dz, int64_t nz, bool dst_major, hipStream_t s)
 {
     if (R <= 0 || Cc <= 0 || nz <= 0) return hipSuccess;
     const int64_t tr = (R + TT - 1) / TT, tc = (Cc + TT - 1) / TT;
@@ -131,24 +159,26 @@ hipError_t launch_transpose(int elt_bytes, const void* src0, void* dst0, const v
         hipLaunchKernelGGL((transpose_pair_kernel<uint16_t, uint32_t>), dim3((unsigned)blocks),
                            dim3(TP_THREADS), 0, s, (const uint16_t*)src0, (uint16_t*)dst0,
                            (const uint16_t*)src1, (uint16_t*)dst1, R, Cc, ss, ds, sz, dz, nz, tr,
-                           tc);
+                           tc, dst_major ? 1 : 0);
         return hipGetLastError();
     }
     if (even && elt_bytes == 4) {
         hipLaunchKernelGGL((transpose_pair_kernel<uint32_t, uint2>), dim3((unsigned)blocks),
                            dim3(TP_THREADS), 0, s, (const uint32_t*)src0, (uint32_t*)dst0,
                            (const uint32_t*)src1, (uint32_t*)dst1, R, Cc, ss, ds, sz, dz, nz, tr,
-                           tc);
+                           tc, dst_major ? 1 : 0);
         return hipGetLastError();
     }
     if (elt_bytes == 2)
         hipLaunchKernelGGL(transpose_kernel<uint16_t>, dim3((unsigned)blocks), dim3(TP_THREADS), 0,
                            s, (const uint16_t*)src0, (uint16_t*)dst0, (const uint16_t*)src1,
-                           (uint16_t*)dst1, R, Cc, ss, ds, sz, dz, nz, tr, tc);
+                           (uint16_t*)dst1, R, Cc, ss, ds, sz, dz, nz, tr, tc,
+                           dst_major ? 1 : 0);
     else if (elt_bytes == 4)
         hipLaunchKernelGGL(transpose_kernel<uint32_t>, dim3((unsigned)blocks), dim3(TP_THREADS), 0,
                            s, (const uint32_t*)src0, (uint32_t*)dst0, (const uint32_t*)src1,
-                           (uint32_t*)dst1, R, Cc, ss, ds, sz, dz, nz, tr, tc);
+                           (uint32_t*)dst1, R, Cc, ss, ds, sz, dz, nz, tr, tc,
+                           dst_major ? 1 : 0);
     else
         return hipErrorInvalidValue;
     return hipGetLastError();

@@ -100,3 +100,23 @@ def test_caller_workspace_and_head_option(sc):
     r = blc_and_reference(sc, v, g, path=sc.PATH_FUSED, head=8)
     ref, S = oracle.causal_conv_f64(v, g)
     assert_within_bound(r, ref, S, False, "blc options")
+
+
+def test_ordering_on_a_side_stream(sc):
+    # several chunks (two per batch row of 9 M elements) on a non-default stream: the call's
+    # result is complete for the next work on that stream, without a host synchronisation,
+    # and its inputs may be overwritten by that work
+    B, L, C = 3, 4096, 2200
+    v, g = make_inputs(WORKLOADS[2], B=B, C=C, L=L, seed_offset=77)
+    vd, gd = to_device(token_major(v)), to_device(token_major(g))
+    ref = to_host(sc.causal_conv_blc(vd, gd))
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    print("case blc side stream", flush=True)
+    with torch.cuda.stream(side):
+        r = sc.causal_conv_blc(vd, gd)
+        twice = r * 2
+        vd.zero_()
+    torch.cuda.current_stream().wait_stream(side)
+    assert np.array_equal(to_host(r).view(np.uint32), ref.view(np.uint32))
+    assert np.array_equal(to_host(twice), ref * 2)
