@@ -33,6 +33,11 @@ blocking or fusion (see ``oracle.c`` for the C side):
   transforms executed on integers only ("Catastrophic Token Leakage ...", abstract); a
   fixed-point encoding with caller-chosen scales carries real activations onto integers
   without letting any output depend on a later input.
+* :func:`gate_f64` -- the gate stream of the multi-head Fourier module ("Caracal", key
+  design 1): a causal convolution with kernel 3 over sigma(s), grouped by head (the
+  channels of one group mix with each other only), g[co, t] = sum_{i, k} W[co, i, k]
+  sigma(s[c0 + i, t + k - 2]) with the convolution's input zero before t = 0, and its error
+  scale sum |W| sigma(s).
 * :func:`circular_conv_dft` / :func:`circular_conv_ntt` -- the pages' recipe (zero-pad on
   the right to n, transform, multiply, inverse, keep all n values) with O(n^2) DFT / NTT,
   used only to pin key design 2 against the direct sum.
@@ -314,6 +319,35 @@ def shared_conv_bwd_f64(dr, v, k, nthreads: int | None = None):
     kb = np.ascontiguousarray(np.broadcast_to(k64[None], v64.shape))
     dv, dkb, Sv, Skb = causal_conv_bwd_f64(d64, v64, kb, nthreads)
     return dv, dkb.sum(axis=0), Sv, Skb.sum(axis=0)
+
+
+def gate_f64(s, W):
+    """Gate stream g = Conv1d_G2(sigma(s)), float64, with its error scale.
+
+    s: (B, C, L) pre-activation (stored values, decoded exactly); W: (C, cg, 3) weights of a
+    convolution grouped into C / cg groups of cg channels, PyTorch's tap order (tap k
+    multiplies the input at t + k - 2, i.e. causal left padding by 2 of sigma(s), the padded
+    entries being 0).  Returns (g, Sg) with Sg[b, co, t] = sum_{i, k} |W[co, i, k]|
+    sigma(s[b, c0 + i, t + k - 2]), where c0 is the first channel of co's group."""
+    s64, w64 = as_f64(s), as_f64(W)
+    if s64.ndim != 3 or w64.ndim != 3 or w64.shape[2] != 3 or w64.shape[0] != s64.shape[1]:
+        raise ValueError("s must be (B, C, L) and W (C, cg, 3)")
+    B, C, L = s64.shape
+    cg = w64.shape[1]
+    if cg < 1 or C % cg:
+        raise ValueError("the group size must divide C")
+    sig = 1.0 / (1.0 + np.exp(-s64))
+    # the convolution's input, zero at t = -2, -1
+    padded = np.concatenate([np.zeros((B, C, 2)), sig], axis=2)
+    g = np.zeros((B, C, L))
+    Sg = np.zeros((B, C, L))
+    for c0 in range(0, C, cg):
+        wg = w64[c0:c0 + cg]                                  # (cg out, cg in, 3)
+        for k in range(3):
+            x = padded[:, c0:c0 + cg, k:k + L]                 # input at t + k - 2
+            g[:, c0:c0 + cg] += np.matmul(wg[:, :, k], x)
+            Sg[:, c0:c0 + cg] += np.matmul(np.abs(wg[:, :, k]), x)
+    return g, Sg
 
 
 def lift_mod_p(r, p: int = P_NTT) -> np.ndarray:

@@ -587,3 +587,71 @@ def test_shared_filter_gradients():
     rr = causal_conv_i64(iv, np.broadcast_to(ik[None], iv.shape))
     _, dki, _, _ = oracle.shared_conv_bwd_f64(ir.astype(float), iv.astype(float), ik.astype(float))
     assert (ir * rr).sum() == int(round((dki * ik).sum()))
+
+
+# ---------------------------------------------------------------- gate stream
+
+def test_gate_hand_case_zero_padding():
+    # s = 0 gives sigma = 1/2 everywhere; W = (1, 2, 3) on taps (t-2, t-1, t).  The padded
+    # inputs before t = 0 are zeros of the convolution's input, not sigma(0):
+    # g = 1/2 (3, 2+3, 1+2+3, 1+2+3)
+    s = np.zeros((1, 1, 4))
+    W = np.array([[[1.0, 2.0, 3.0]]])
+    g, Sg = oracle.gate_f64(s, W)
+    assert np.array_equal(g[0, 0], [1.5, 2.5, 3.0, 3.0])
+    assert np.array_equal(Sg, g)
+
+
+def test_gate_identity_and_shift_taps():
+    rng = np.random.default_rng(11)
+    B, C, L, cg = 2, 8, 9, 4
+    s = rng.standard_normal((B, C, L))
+    sig = 1.0 / (1.0 + np.exp(-s))
+    for k, shift in ((2, 0), (1, 1), (0, 2)):
+        W = np.zeros((C, cg, 3))
+        for co in range(C):
+            W[co, co % cg, k] = 1.0
+        g, _ = oracle.gate_f64(s, W)
+        ref = np.zeros_like(sig)
+        ref[:, :, shift:] = sig[:, :, :L - shift]
+        assert np.array_equal(g, ref), k
+    # sigma(x) + sigma(-x) = 1 through the identity tap
+    W = np.zeros((C, cg, 3))
+    for co in range(C):
+        W[co, co % cg, 2] = 1.0
+    a, _ = oracle.gate_f64(s, W)
+    b, _ = oracle.gate_f64(-s, W)
+    np.testing.assert_allclose(a + b, 1.0, rtol=0, atol=1e-15)
+
+
+def test_gate_against_torch_grouped_conv1d():
+    import torch
+    rng = np.random.default_rng(12)
+    for B, C, L, cg in ((2, 12, 17, 4), (1, 128, 40, 64), (3, 6, 2, 6), (1, 5, 1, 1)):
+        s = rng.standard_normal((B, C, L))
+        W = rng.standard_normal((C, cg, 3)) / np.sqrt(3.0)
+        g, Sg = oracle.gate_f64(s, W)
+        x = torch.sigmoid(torch.from_numpy(s))
+        x = torch.nn.functional.pad(x, (2, 0))
+        ref = torch.nn.functional.conv1d(x, torch.from_numpy(W), groups=C // cg).numpy()
+        np.testing.assert_allclose(g, ref, rtol=1e-12, atol=1e-12)
+        assert np.all(Sg >= np.abs(g) * (1 - 1e-12))
+
+
+def test_gate_groups_do_not_mix():
+    rng = np.random.default_rng(13)
+    B, C, L, cg = 1, 8, 11, 4
+    s = rng.standard_normal((B, C, L))
+    W = rng.standard_normal((C, cg, 3))
+    g, _ = oracle.gate_f64(s, W)
+    s2 = s.copy()
+    s2[:, cg:] += 1.0                       # the second group's inputs
+    g2, _ = oracle.gate_f64(s2, W)
+    assert np.array_equal(g[:, :cg], g2[:, :cg])
+    assert not np.array_equal(g[:, cg:], g2[:, cg:])
+    # bf16 storage is decoded exactly: the same values as float64 inputs
+    from workloads import f32_to_bf16_bits
+    sb = f32_to_bf16_bits(s.astype(np.float32))
+    gb, _ = oracle.gate_f64(sb, W)
+    gd, _ = oracle.gate_f64(oracle.as_f64(sb), W)
+    assert np.array_equal(gb, gd)

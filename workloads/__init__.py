@@ -144,6 +144,26 @@ def make_inputs(w: Workload, B: int | None = None, C: int | None = None,
     return v32, g32
 
 
+def make_gate_inputs(w: Workload, B: int | None = None, C: int | None = None,
+                     L: int | None = None, seed_offset: int = 0, cg: int = 64):
+    """Inputs ``(v, s, W)`` of the gate-stream calls, in the workload's float storage: v
+    (B, C, L) as :func:`make_inputs`, the gate pre-activation s (B, C, L) ~ N(0, 1) and the
+    grouped kernel-3 weights W (C, cg, 3) ~ N(0, variance 1/3) (the same streams 0, 1, 2)."""
+    if w.storage not in ("f32", "bf16"):
+        raise ValueError("the gate calls take float storage")
+    B = w.B if B is None else B
+    C = w.C if C is None else C
+    L = w.L if L is None else L
+    cid = w.cid + 1000 * seed_offset
+    shape = (B, C, L)
+    v32 = rng(cid, 0).standard_normal(shape).astype(np.float32)
+    s32 = rng(cid, 1).standard_normal(shape).astype(np.float32)
+    w32 = (rng(cid, 2).standard_normal((C, cg, 3)) * np.sqrt(1.0 / 3.0)).astype(np.float32)
+    if w.storage == "bf16":
+        return f32_to_bf16_bits(v32), f32_to_bf16_bits(s32), f32_to_bf16_bits(w32)
+    return v32, s32, w32
+
+
 def make_grad(w: Workload, B: int | None = None, C: int | None = None, L: int | None = None,
               seed_offset: int = 0) -> np.ndarray:
     """Upstream gradient ``dr`` = dLoss/dr for the backward pass, shape (B, C, L) in the
