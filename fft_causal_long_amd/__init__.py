@@ -42,7 +42,9 @@ __all__ = [
     "sc_causal_conv_spec_bwd_f32", "sc_causal_conv_spec_bwd_bf16",
     "sc_causal_conv_shared_bwd_f32", "sc_causal_conv_shared_bwd_bf16", "causal_conv_blc",
     "sc_blc_workspace_bytes", "sc_causal_conv_blc_f32", "sc_causal_conv_blc_bf16",
-    "sc_causal_conv_blc_ex", "KIND_F32", "KIND_BF16", "KIND_NTT_I32", "KIND_FIXED_F32", "PATH_AUTO", "PATH_FUSED", "PATH_FOUR_STEP",
+    "sc_causal_conv_blc_ex", "gate", "gate_conv", "gate_conv_blc", "sc_gate_f32", "sc_gate_bf16",
+    "sc_gate_conv_workspace_bytes", "sc_gate_conv_blc_workspace_bytes", "sc_gate_conv_ex",
+    "sc_gate_conv_blc_ex", "sc_gate_conv_blc_f32", "sc_gate_conv_blc_bf16", "KIND_F32", "KIND_BF16", "KIND_NTT_I32", "KIND_FIXED_F32", "PATH_AUTO", "PATH_FUSED", "PATH_FOUR_STEP",
     "PATH_DIRECT", "LIB_PATH",
 ]
 
@@ -90,6 +92,22 @@ def _open():
     h.sc_causal_conv_blc_ex.argtypes = [st, vp, vp, vp, i64, i64, i64,
                                         ctypes.POINTER(sc_options), vp, sz, vp]
     h.sc_causal_conv_blc_ex.restype = st
+    for name in ("sc_gate_f32", "sc_gate_bf16"):
+        f = getattr(h, name)
+        f.argtypes = [vp, vp, vp, i64, i64, i64, vp]
+        f.restype = st
+    for name in ("sc_gate_conv_workspace_bytes", "sc_gate_conv_blc_workspace_bytes"):
+        f = getattr(h, name)
+        f.argtypes = [st, i64, i64, i64]
+        f.restype = sz
+    for name in ("sc_gate_conv_ex", "sc_gate_conv_blc_ex"):
+        f = getattr(h, name)
+        f.argtypes = [st, vp, vp, vp, vp, i64, i64, i64, ctypes.POINTER(sc_options), vp, sz, vp]
+        f.restype = st
+    for name in ("sc_gate_conv_blc_f32", "sc_gate_conv_blc_bf16"):
+        f = getattr(h, name)
+        f.argtypes = [vp, vp, vp, vp, i64, i64, i64, vp]
+        f.restype = st
     for name in ("sc_causal_conv_bwd_f32", "sc_causal_conv_bwd_bf16", "sc_causal_conv_bwd_ntt_i32"):
         f = getattr(h, name)
         f.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, vp]
@@ -259,6 +277,38 @@ def sc_causal_conv_blc_bf16(v, g, r, B, L, C, stream):
 
 def sc_causal_conv_blc_ex(kind, v, g, r, B, L, C, opt, ws, ws_bytes, stream):
     return _lib.sc_causal_conv_blc_ex(kind, v, g, r, B, L, C, opt, ws, ws_bytes, stream)
+
+
+def sc_gate_f32(s, W, g, B, C, L, stream):
+    return _lib.sc_gate_f32(s, W, g, B, C, L, stream)
+
+
+def sc_gate_bf16(s, W, g, B, C, L, stream):
+    return _lib.sc_gate_bf16(s, W, g, B, C, L, stream)
+
+
+def sc_gate_conv_workspace_bytes(kind, B, C, L) -> int:
+    return int(_lib.sc_gate_conv_workspace_bytes(kind, B, C, L))
+
+
+def sc_gate_conv_blc_workspace_bytes(kind, B, L, C) -> int:
+    return int(_lib.sc_gate_conv_blc_workspace_bytes(kind, B, L, C))
+
+
+def sc_gate_conv_ex(kind, v, s, W, r, B, C, L, opt, ws, ws_bytes, stream):
+    return _lib.sc_gate_conv_ex(kind, v, s, W, r, B, C, L, opt, ws, ws_bytes, stream)
+
+
+def sc_gate_conv_blc_ex(kind, v, s, W, r, B, L, C, opt, ws, ws_bytes, stream):
+    return _lib.sc_gate_conv_blc_ex(kind, v, s, W, r, B, L, C, opt, ws, ws_bytes, stream)
+
+
+def sc_gate_conv_blc_f32(v, s, W, r, B, L, C, stream):
+    return _lib.sc_gate_conv_blc_f32(v, s, W, r, B, L, C, stream)
+
+
+def sc_gate_conv_blc_bf16(v, s, W, r, B, L, C, stream):
+    return _lib.sc_gate_conv_blc_bf16(v, s, W, r, B, L, C, stream)
 
 
 def sc_workspace_bytes(kind, B, C, L) -> int:
@@ -601,3 +651,86 @@ def causal_conv_shared_bwd(dr: torch.Tensor, v: torch.Tensor, k: torch.Tensor,
     if st != SC_OK:
         raise SpecConvError(st, "causal_conv_shared_bwd")
     return dv, dk
+
+
+def _gate_args(s: torch.Tensor, W: torch.Tensor, *others: torch.Tensor):
+    for t in (s, W) + others:
+        if t.dtype not in (torch.float32, torch.bfloat16):
+            raise TypeError("gate calls take float32 or bfloat16 tensors")
+        if not t.is_cuda or not t.is_contiguous():
+            raise ValueError("tensors must be contiguous and on the GPU")
+    if len({t.dtype for t in (s, W) + others}) != 1 or \
+            len({t.device for t in (s, W) + others}) != 1:
+        raise ValueError("tensors must share dtype and device")
+    if W.dim() != 3 or W.shape[1] != 64 or W.shape[2] != 3:
+        raise ValueError("W must be (C, 64, 3)")
+    return KIND_F32 if s.dtype == torch.float32 else KIND_BF16
+
+
+def _ws_args(workspace, dev):
+    if workspace is None:
+        return None, 0
+    if not workspace.is_cuda or workspace.device != dev or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous tensor on the inputs' device")
+    return workspace.data_ptr(), workspace.numel() * workspace.element_size()
+
+
+def gate(s: torch.Tensor, W: torch.Tensor, out: torch.Tensor | None = None) -> torch.Tensor:
+    """g = Conv1d_G2(sigmoid(s)) (sc_gate_*): s (..., C, L) channel-major, W (C, 64, 3)."""
+    kind = _gate_args(s, W)
+    if s.dim() < 2 or s.shape[-2] != W.shape[0]:
+        raise ValueError("s must be (..., C, L) with C = W.shape[0]")
+    C, L = int(s.shape[-2]), int(s.shape[-1])
+    B = s.numel() // max(C * L, 1)
+    out = _out_like(s, out, "out")
+    fn = _lib.sc_gate_f32 if kind == KIND_F32 else _lib.sc_gate_bf16
+    with torch.cuda.device(s.device):
+        stream = torch.cuda.current_stream(s.device).cuda_stream
+        st = fn(s.data_ptr(), W.data_ptr(), out.data_ptr(), B, C, L, stream)
+    if st != SC_OK:
+        raise SpecConvError(st, "gate")
+    return out
+
+
+def gate_conv(v: torch.Tensor, s: torch.Tensor, W: torch.Tensor, out: torch.Tensor | None = None,
+              *, path: int | None = None, head: int | None = None,
+              workspace: torch.Tensor | None = None) -> torch.Tensor:
+    """r = causal_conv(v, gate(s, W)) with v, s (..., C, L) channel-major (sc_gate_conv_ex)."""
+    kind = _gate_args(s, W, v)
+    if v.shape != s.shape or v.dim() < 2 or v.shape[-2] != W.shape[0]:
+        raise ValueError("v and s must be (..., C, L) of one shape, C = W.shape[0]")
+    C, L = int(v.shape[-2]), int(v.shape[-1])
+    B = v.numel() // max(C * L, 1)
+    out = _out_like(v, out, "out")
+    ws_ptr, ws_bytes = _ws_args(workspace, v.device)
+    opt = sc_options(PATH_AUTO if path is None else int(path), -1 if head is None else int(head))
+    with torch.cuda.device(v.device):
+        stream = torch.cuda.current_stream(v.device).cuda_stream
+        st = _lib.sc_gate_conv_ex(kind, v.data_ptr(), s.data_ptr(), W.data_ptr(), out.data_ptr(),
+                                  B, C, L, ctypes.byref(opt), ws_ptr, ws_bytes, stream)
+    if st != SC_OK:
+        raise SpecConvError(st, "gate_conv")
+    return out
+
+
+def gate_conv_blc(v: torch.Tensor, s: torch.Tensor, W: torch.Tensor,
+                  out: torch.Tensor | None = None, *, path: int | None = None,
+                  head: int | None = None, workspace: torch.Tensor | None = None) -> torch.Tensor:
+    """r = causal_conv(v, gate(s, W)) along the token axis of token-major (..., L, C) tensors
+    (sc_gate_conv_blc_ex)."""
+    kind = _gate_args(s, W, v)
+    if v.shape != s.shape or v.dim() < 2 or v.shape[-1] != W.shape[0]:
+        raise ValueError("v and s must be (..., L, C) of one shape, C = W.shape[0]")
+    L, C = int(v.shape[-2]), int(v.shape[-1])
+    B = v.numel() // max(C * L, 1)
+    out = _out_like(v, out, "out")
+    ws_ptr, ws_bytes = _ws_args(workspace, v.device)
+    opt = sc_options(PATH_AUTO if path is None else int(path), -1 if head is None else int(head))
+    with torch.cuda.device(v.device):
+        stream = torch.cuda.current_stream(v.device).cuda_stream
+        st = _lib.sc_gate_conv_blc_ex(kind, v.data_ptr(), s.data_ptr(), W.data_ptr(),
+                                      out.data_ptr(), B, L, C, ctypes.byref(opt), ws_ptr,
+                                      ws_bytes, stream)
+    if st != SC_OK:
+        raise SpecConvError(st, "gate_conv_blc")
+    return out

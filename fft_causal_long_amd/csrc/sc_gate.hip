@@ -1,0 +1,276 @@
+// Gate stream of the multi-head Fourier module on MFMA (gfx950).
+//
+// "Caracal: Causal Architecture via Spectral Mixing" (key design 1) makes the convolution
+// kernel of each channel from the input: g = Conv1d_G2(sigma(s)) with s a linear projection
+// of the normalised activations and Conv1d_G2 a causal convolution with kernel 3 grouped by
+// head, so that the channels of one head mix with each other only:
+//
+//     g[b][co][t] = sum_{i<64} sum_{k<3} W[co][i][k] * sigma(s[b][c0+i][t+k-2])
+//
+// (c0 the first channel of co's group of 64, the convolution's input zero before t = 0).
+// Per token this is a 64 x 192 matrix times a 192-vector, so a tile of T tokens of one group
+// is a dense 64 x 192 x T contraction: it runs on the matrix cores, as three shifted
+// products W_k (64 x 64) * sigma(S)[:, t+k-2] accumulated in fp32.
+//
+// One workgroup (4 waves) per (batch row, group, tile of T tokens):
+//  1. sigma(s) for tokens t0-2 .. t0+T-1 into LDS, one row per token (the 64 channels of
+//     the group contiguous), zero before t = 0; bf16 storage rounds sigma to bf16, the
+//     precision a bf16 layer computes it in.
+//  2. each wave holds the W fragments of its 32 output channels (all 3 taps, all 64 inputs)
+//     in registers and accumulates 32 x 32 output blocks over T/2 tokens;
+//  3. the blocks go through LDS to coalesced stores of g rows (channel-major, t contiguous).
+// s is read token-major ((B, L, C): one 64-channel row per token, 16-byte vector loads) or
+// channel-major ((B, C, L): t contiguous, element loads).
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "sc_device.h"
+#include "sc_internal.h"
+
+namespace sc {
+
+namespace {
+
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+
+constexpr int GT = 256;      // threads
+constexpr int GC = 64;       // channels per group
+
+template <class IO>
+struct GateCfg;
+
+template <>
+struct GateCfg<bf16_io> {
+    static constexpr int T = 256;       // tokens per tile
+    static constexpr int SP = 72;       // LDS row pitch (elements): 144 bytes
+    static constexpr int KS = 16;       // reduction depth of one MFMA
+};
+
+template <>
+struct GateCfg<f32_io> {
+    static constexpr int T = 128;
+    static constexpr int SP = 65;
+    static constexpr int KS = 2;
+};
+
+__device__ __forceinline__ float sigmoid(float x) { return 1.0f / (1.0f + __expf(-x)); }
+
+__device__ __forceinline__ uint16_t to_bf16(float x) { return (uint16_t)pack_bf16x2(x, 0.f); }
+
+template <class IO, bool TM>
+__global__ __launch_bounds__(GT) void gate_kernel(const typename IO::T* __restrict__ s,
+                                                  const typename IO::T* __restrict__ W,
+                                                  typename IO::T* __restrict__ g, int C, int L,
+                                                  int gcs, int ngroups, int ntiles, int vec_out)
+{
+    using E = typename IO::T;
+    constexpr bool BF = sizeof(E) == 2;
+    constexpr int T = GateCfg<IO>::T, SP = GateCfg<IO>::SP, KS = GateCfg<IO>::KS;
+    constexpr int CS = GC / KS;          // MFMA steps per tap
+    constexpr int NB = T / 64;           // 32-token blocks per wave
+    constexpr int S_BYTES = (T + 2) * SP * (int)sizeof(E);
+    constexpr int O_BYTES = GC * T * (int)sizeof(E);
+    constexpr int LDS_BYTES = S_BYTES > O_BYTES ? S_BYTES : O_BYTES;
+    __shared__ __attribute__((aligned(16))) unsigned char smem[LDS_BYTES];
+    E* S = (E*)smem;                     // S[tt][ci], tt = t - t0 + 2
+    E* O = (E*)smem;                     // O[co][tl], after the products
+
+    uint32_t id = blockIdx.x;
+    const int tile = (int)(id % (uint32_t)ntiles);
+    id /= (uint32_t)ntiles;
+    const int grp = (int)(id % (uint32_t)ngroups);
+    const int64_t z = id / (uint32_t)ngroups;
+    const int t0 = tile * T, c0 = grp * GC;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+
+    // 1. sigma(s) into LDS
+    if constexpr (TM) {
+        constexpr int EPV = 16 / (int)sizeof(E);      // elements per 16-byte vector
+        constexpr int VPR = GC / EPV;                 // vectors per token row
+        constexpr int NV = T * VPR / GT;
+        const E* sz = s + z * (int64_t)L * C + c0;
+        uint4 raw[NV];
+#pragma unroll
+        for (int q = 0; q < NV; ++q) {
+            const int vid = tid + GT * q, r = vid / VPR, p = vid % VPR;
+            const int tc = t0 + r < L ? t0 + r : L - 1;
+            raw[q] = *(const uint4*)(sz + (int64_t)tc * C + p * EPV);
+        }
+        uint4 halo = make_uint4(0, 0, 0, 0);
+        const int hr = tid / VPR, hp = tid % VPR, ht = t0 - 2 + hr;
+        if (tid < 2 * VPR && ht >= 0) halo = *(const uint4*)(sz + (int64_t)ht * C + hp * EPV);
+        auto put = [&](int row, int col, const uint4& w, bool valid) {
+            if constexpr (BF) {
+                const uint32_t u[4] = {w.x, w.y, w.z, w.w};
+                uint32_t o[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const float a = valid ? sigmoid(__uint_as_float(u[e] << 16)) : 0.f;
+                    const float b = valid ? sigmoid(__uint_as_float(u[e] & 0xffff0000u)) : 0.f;
+                    o[e] = pack_bf16x2(a, b);
+                }
+                *(uint4*)(S + row * SP + col) = make_uint4(o[0], o[1], o[2], o[3]);
+            } else {
+                const uint32_t u[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    S[row * SP + col + e] = valid ? sigmoid(__uint_as_float(u[e])) : 0.f;
+            }
+        };
+#pragma unroll
+        for (int q = 0; q < NV; ++q) {
+            const int vid = tid + GT * q, r = vid / VPR, p = vid % VPR;
+            put(r + 2, p * EPV, raw[q], t0 + r < L);
+        }
+        if (tid < 2 * VPR) put(hr, hp * EPV, halo, ht >= 0);
+    } else {
+        constexpr int NE = T * GC / GT;
+        const E* sz = s + (z * C + c0) * (int64_t)L;
+        float val[NE];
+#pragma unroll
+        for (int q = 0; q < NE; ++q) {
+            const int e = tid + GT * q, r = e % T, ci = e / T;
+            const int tc = t0 + r < L ? t0 + r : L - 1;
+            val[q] = IO::load(sz, (int64_t)ci * L + tc);
+        }
+        float hv = 0.f;
+        const int hci = tid >> 1, hr = tid & 1, ht = t0 - 2 + hr;
+        if (tid < 2 * GC && ht >= 0) hv = IO::load(sz, (int64_t)hci * L + ht);
+#pragma unroll
+        for (int q = 0; q < NE; ++q) {
+            const int e = tid + GT * q, r = e % T, ci = e / T;
+            const float x = t0 + r < L ? sigmoid(val[q]) : 0.f;
+            if constexpr (BF) S[(r + 2) * SP + ci] = to_bf16(x);
+            else S[(r + 2) * SP + ci] = x;
+        }
+        if (tid < 2 * GC) {
+            const float x = ht >= 0 ? sigmoid(hv) : 0.f;
+            if constexpr (BF) S[hr * SP + hci] = to_bf16(x);
+            else S[hr * SP + hci] = x;
+        }
+    }
+
+    // 2. W fragments of this wave's 32 output channels: A[i = co][kk = ci] of tap k
+    const int cb = wave & 1, th = wave >> 1;
+    const int co = c0 + 32 * cb + (lane & 31);
+    const E* wrow = W + (int64_t)co * (GC * 3);
+    const int half = lane >> 5;
+    f32x16 acc[NB];
+#pragma unroll
+    for (int m = 0; m < NB; ++m)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[m][r] = 0.f;
+
+    if constexpr (BF) {
+        uint4 a[3][CS];
+#pragma unroll
+        for (int k = 0; k < 3; ++k)
+#pragma unroll
+            for (int cs = 0; cs < CS; ++cs) {
+                const int ci = KS * cs + 8 * half;
+                uint32_t u[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    u[e] = (uint32_t)wrow[(ci + 2 * e) * 3 + k] |
+                           ((uint32_t)wrow[(ci + 2 * e + 1) * 3 + k] << 16);
+                a[k][cs] = make_uint4(u[0], u[1], u[2], u[3]);
+            }
+        __syncthreads();
+#pragma unroll
+        for (int k = 0; k < 3; ++k)
+#pragma unroll
+            for (int cs = 0; cs < CS; ++cs) {
+                const bf16x8 av = __builtin_bit_cast(bf16x8, a[k][cs]);
+#pragma unroll
+                for (int m = 0; m < NB; ++m) {
+                    const int tl = th * (T / 2) + 32 * m + (lane & 31);
+                    const uint4 bw = *(const uint4*)(S + (tl + k) * SP + KS * cs + 8 * half);
+                    acc[m] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                        av, __builtin_bit_cast(bf16x8, bw), acc[m], 0, 0, 0);
+                }
+            }
+    } else {
+        float a[3][CS];
+#pragma unroll
+        for (int k = 0; k < 3; ++k)
+#pragma unroll
+            for (int cs = 0; cs < CS; ++cs) a[k][cs] = wrow[(KS * cs + half) * 3 + k];
+        __syncthreads();
+#pragma unroll
+        for (int k = 0; k < 3; ++k)
+#pragma unroll
+            for (int cs = 0; cs < CS; ++cs)
+#pragma unroll
+                for (int m = 0; m < NB; ++m) {
+                    const int tl = th * (T / 2) + 32 * m + (lane & 31);
+                    const float bv = S[(tl + k) * SP + KS * cs + half];
+                    acc[m] = __builtin_amdgcn_mfma_f32_32x32x2f32(a[k][cs], bv, acc[m], 0, 0, 0);
+                }
+    }
+    __syncthreads();   // every wave is done reading S
+
+    // 3. blocks to LDS (output storage type), then whole rows to g
+#pragma unroll
+    for (int m = 0; m < NB; ++m) {
+        const int tl = th * (T / 2) + 32 * m + (lane & 31);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int i = 8 * (r >> 2) + 4 * half + (r & 3);
+            if constexpr (BF) O[(32 * cb + i) * T + tl] = to_bf16(acc[m][r]);
+            else O[(32 * cb + i) * T + tl] = acc[m][r];
+        }
+    }
+    __syncthreads();
+    E* gz = g + (z * gcs + c0) * (int64_t)L;
+    if (vec_out) {
+        // L is a multiple of the vector's elements and g rows are 16-byte aligned
+        constexpr int EPV = 16 / (int)sizeof(E), VPR = T / EPV, NV = GC * VPR / GT;
+#pragma unroll
+        for (int q = 0; q < NV; ++q) {
+            const int vid = tid + GT * q, row = vid / VPR, p = vid % VPR;
+            if (t0 + p * EPV < L)
+                *(uint4*)(gz + (int64_t)row * L + t0 + p * EPV) = *(const uint4*)(O + row * T + p * EPV);
+        }
+    } else {
+        constexpr int NE = GC * T / GT;
+#pragma unroll
+        for (int q = 0; q < NE; ++q) {
+            const int e = tid + GT * q, tl = e % T, row = e / T;
+            if (t0 + tl < L) gz[(int64_t)row * L + t0 + tl] = O[row * T + tl];
+        }
+    }
+}
+
+template <class IO, bool TM>
+hipError_t gate_launch(const void* s, const void* W, void* g, int64_t nb, int64_t C, int64_t cw,
+                       int64_t L, int64_t gcs, bool vec_out, hipStream_t st)
+{
+    constexpr int T = GateCfg<IO>::T;
+    const int64_t ntiles = (L + T - 1) / T, ngroups = cw / GC;
+    const int64_t blocks = ntiles * ngroups * nb;
+    if (blocks <= 0) return hipSuccess;
+    if (blocks > 0x7fffffff) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((gate_kernel<IO, TM>), dim3((unsigned)blocks), dim3(GT), 0, st,
+                       (const typename IO::T*)s, (const typename IO::T*)W, (typename IO::T*)g,
+                       (int)C, (int)L, (int)gcs, (int)ngroups, (int)ntiles, vec_out ? 1 : 0);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_gate(Store st, bool token_major, const void* s, const void* W, void* g,
+                       int64_t nb, int64_t C, int64_t cw, int64_t L, int64_t gcs, hipStream_t s_)
+{
+    const size_t es = st == Store::F32 ? 4 : 2;
+    const bool vec_out = L % (int64_t)(16 / es) == 0 && (uintptr_t)g % 16 == 0;
+    if (st == Store::F32)
+        return token_major ? gate_launch<f32_io, true>(s, W, g, nb, C, cw, L, gcs, vec_out, s_)
+                           : gate_launch<f32_io, false>(s, W, g, nb, C, cw, L, gcs, vec_out, s_);
+    return token_major ? gate_launch<bf16_io, true>(s, W, g, nb, C, cw, L, gcs, vec_out, s_)
+                       : gate_launch<bf16_io, false>(s, W, g, nb, C, cw, L, gcs, vec_out, s_);
+}
+
+}  // namespace sc

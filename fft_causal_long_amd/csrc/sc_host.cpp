@@ -191,6 +191,13 @@ bool overlaps(const void* a, const void* b, uint64_t bytes)
     return x < y + bytes && y < x + bytes;
 }
 
+// [a, a + na) and [b, b + nb) share a byte
+bool ranges_overlap(const void* a, uint64_t na, const void* b, uint64_t nb)
+{
+    const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
+    return na && nb && x < y + nb && y < x + na;
+}
+
 bool exact_kind(sc_kind k) { return k == SC_KIND_NTT_I32 || k == SC_KIND_FIXED_F32; }
 
 // Kind and shape checks.  *n receives B*C*L.
@@ -420,11 +427,12 @@ sc_status run_bwd(sc_kind kind, const void* dr, const void* v, const void* g, vo
     return run_jobs(kind, jobs, 2, true, n, B, C, L, opt, ws, ws_bytes, stream);
 }
 
-// ---------------------------------------------------------------- token-major layout
+// ---------------------------------------------------------------- staged calls
 
-// Elements per staged buffer of the token-major calls: three such buffers (v, g, r of one
-// chunk) stay well inside the 256 MB last-level cache.
+// Elements per staged buffer of the token-major and gate calls: three such buffers (v, g, r
+// of one chunk) stay well inside the 256 MB last-level cache.
 constexpr int64_t kBlcChunkElems = (int64_t)8 << 20;
+constexpr int64_t kGateGroup = 64;   // channels per gate group (one head)
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
@@ -436,9 +444,9 @@ struct BlcPlan {
 };
 
 // Chunks of whole batch rows when one row's C L elements fit a buffer, else blocks of 64k
-// channels of one row.
+// channels of one row (64k also keeps gate groups whole).
 sc_status blc_plan(sc_kind kind, int64_t B, int64_t L, int64_t C, const sc_options* opt,
-                   BlcPlan* p)
+                   int nstage, BlcPlan* p)
 {
     if (C * L <= kBlcChunkElems) {
         p->cw = C;
@@ -459,32 +467,51 @@ sc_status blc_plan(sc_kind kind, int64_t B, int64_t L, int64_t C, const sc_optio
         int64_t chunk;
         fourstep_plan(nch, L, &chunk, &p->inner);
     }
-    p->total = 3 * p->stage + align256(p->inner);
+    p->total = (size_t)nstage * p->stage + align256(p->inner);
     return SC_OK;
 }
 
-// v, g, r in (B, L, C): per chunk, transpose v and g into channel rows, convolve, transpose
-// the result back.
-sc_status blc_run(sc_kind kind, const void* v, const void* g, void* r, int64_t B, int64_t L,
-                  int64_t C, const sc_options* opt, void* ws, size_t ws_bytes, hipStream_t stream)
+// Staged calls, chunk by chunk through a workspace:
+//  * token-major (tm) without gate: v, g, r in (B, L, C); transpose v and g into channel
+//    rows, convolve, transpose the result back;
+//  * token-major with gate (W not null; s takes g's place): transpose v, make g from s by
+//    the gate kernel straight into channel rows, convolve, transpose back;
+//  * channel-major with gate: g of the chunk from s into the workspace, convolve v with it
+//    into r in place.
+sc_status staged_run(sc_kind kind, bool tm, const void* v, const void* g, const void* W,
+                     void* r, int64_t B, int64_t L, int64_t C, const sc_options* opt, void* ws,
+                     size_t ws_bytes, hipStream_t stream)
 {
+    const bool gate = W != nullptr;
     int64_t n = 0;
     sc_status st = check_args(kind, v, g, r, B, C, L, &n);
     if (st != SC_OK) return st;
+    const size_t es = elt_size(kind);
+    if (gate) {
+        if (kind != SC_KIND_F32 && kind != SC_KIND_BF16) return SC_ERR_INVALID_ARGUMENT;
+        if (C % kGateGroup || C > INT32_MAX) return SC_ERR_UNSUPPORTED;
+        if (n > 0) {
+            if ((uintptr_t)W % es) return SC_ERR_INVALID_ARGUMENT;
+            if (tm && (uintptr_t)g % 16) return SC_ERR_INVALID_ARGUMENT;
+            if (ranges_overlap(r, (uint64_t)n * es, W, (uint64_t)C * kGateGroup * 3 * es))
+                return SC_ERR_INVALID_ARGUMENT;
+        }
+    }
     sc_path path;
     st = resolve_path(kind, L, opt ? opt->path : SC_PATH_AUTO, &path);
     if (st != SC_OK) return st;
     if (n == 0) return SC_OK;
     BlcPlan p;
-    st = blc_plan(kind, B, L, C, opt, &p);
+    st = blc_plan(kind, B, L, C, opt, tm ? 3 : 1, &p);
     if (st != SC_OK) return st;
-    const size_t es = elt_size(kind);
     if (ws) {
         if (ws_bytes < p.total) return SC_ERR_WORKSPACE;
         if ((uintptr_t)ws % 256) return SC_ERR_INVALID_ARGUMENT;
         const uintptr_t w0 = (uintptr_t)ws, w1 = w0 + p.total, nbytes = (uintptr_t)n * es;
         for (const void* t : {v, g, (const void*)r})
             if ((uintptr_t)t < w1 && w0 < (uintptr_t)t + nbytes) return SC_ERR_INVALID_ARGUMENT;
+        if (gate && ranges_overlap(ws, p.total, W, (uint64_t)C * kGateGroup * 3 * es))
+            return SC_ERR_INVALID_ARGUMENT;
     } else if (ws_bytes) {
         return SC_ERR_INVALID_ARGUMENT;
     }
@@ -497,31 +524,81 @@ sc_status blc_run(sc_kind kind, const void* v, const void* g, void* r, int64_t B
         if (hipMallocAsync(&base, p.total, stream) != hipSuccess) return SC_ERR_HIP;
         own = true;
     }
-    char* wv = (char*)base;
-    char* wg = wv + p.stage;
-    char* wr = wg + p.stage;
-    void* inner = p.inner ? (void*)(wr + p.stage) : nullptr;
+    const sc::Store sk = kind == SC_KIND_F32 ? sc::Store::F32 : sc::Store::BF16;
+    char* wg = (char*)base;                       // g of the chunk
+    char* wv = tm ? wg + p.stage : nullptr;       // v of the chunk (token-major)
+    char* wr = tm ? wv + p.stage : nullptr;       // r of the chunk (token-major)
+    void* inner = p.inner ? (void*)((char*)base + (tm ? 3 : 1) * p.stage) : nullptr;
     for (int64_t b0 = 0; b0 < B && st == SC_OK; b0 += p.nb) {
         const int64_t nb = std::min(p.nb, B - b0);
         for (int64_t c0 = 0; c0 < C && st == SC_OK; c0 += p.cw) {
             const int64_t cw = std::min(p.cw, C - c0);
-            const int64_t off = (b0 * L * C + c0) * (int64_t)es;
-            if (sc::launch_transpose((int)es, (const char*)v + off, wv, (const char*)g + off, wg, L,
-                                     cw, C, L, L * C, cw * L, nb, false, stream) != hipSuccess) {
+            const int64_t off = (tm ? b0 * L * C + c0 : (b0 * C + c0) * L) * (int64_t)es;
+            hipError_t e = hipSuccess;
+            if (tm)
+                e = sc::launch_transpose((int)es, (const char*)v + off, wv,
+                                         gate ? nullptr : (const char*)g + off, gate ? nullptr : wg,
+                                         L, cw, C, L, L * C, cw * L, nb, false, stream);
+            if (e == hipSuccess && gate)
+                e = sc::launch_gate(sk, tm, (const char*)g + off,
+                                    (const char*)W + c0 * kGateGroup * 3 * (int64_t)es, wg, nb, C,
+                                    cw, L, cw, stream);
+            if (e != hipSuccess) {
                 st = SC_ERR_HIP;
                 break;
             }
-            const Job job{wv, wg, wr};
+            const Job job{tm ? (const void*)wv : (const char*)v + off, wg,
+                          tm ? (void*)wr : (char*)r + off};
             st = run_jobs(kind, &job, 1, false, nb * cw * L, nb, cw, L, opt, inner,
                           inner ? p.inner : 0, stream);
             if (st != SC_OK) break;
-            if (sc::launch_transpose((int)es, wr, (char*)r + off, nullptr, nullptr, cw, L, L, C,
-                                     cw * L, L * C, nb, true, stream) != hipSuccess)
+            if (tm && sc::launch_transpose((int)es, wr, (char*)r + off, nullptr, nullptr, cw, L, L,
+                                           C, cw * L, L * C, nb, true, stream) != hipSuccess)
                 st = SC_ERR_HIP;
         }
     }
     if (own && hipFreeAsync(base, stream) != hipSuccess && st == SC_OK) st = SC_ERR_HIP;
     return st;
+}
+
+sc_status blc_run(sc_kind kind, const void* v, const void* g, void* r, int64_t B, int64_t L,
+                  int64_t C, const sc_options* opt, void* ws, size_t ws_bytes, hipStream_t stream)
+{
+    return staged_run(kind, true, v, g, nullptr, r, B, L, C, opt, ws, ws_bytes, stream);
+}
+
+size_t staged_bytes(sc_kind kind, bool tm, bool gate, int64_t B, int64_t L, int64_t C)
+{
+    int64_t n = 0;
+    if (check_shape(kind, B, C, L, &n) != SC_OK || n == 0) return 0;
+    if (gate && ((kind != SC_KIND_F32 && kind != SC_KIND_BF16) || C % kGateGroup)) return 0;
+    BlcPlan p;
+    if (blc_plan(kind, B, L, C, nullptr, tm ? 3 : 1, &p) != SC_OK) return 0;
+    return p.total;
+}
+
+// g = gate(s, W), channel-major, written directly
+sc_status gate_run(sc_kind kind, const void* s, const void* W, void* g, int64_t B, int64_t C,
+                   int64_t L, hipStream_t stream)
+{
+    int64_t n = 0;
+    sc_status st = check_shape(kind, B, C, L, &n);
+    if (st != SC_OK) return st;
+    if (kind != SC_KIND_F32 && kind != SC_KIND_BF16) return SC_ERR_INVALID_ARGUMENT;
+    if (C % kGateGroup || C > INT32_MAX || L > INT32_MAX) return SC_ERR_UNSUPPORTED;
+    if (n == 0) return SC_OK;
+    if (!s || !W || !g) return SC_ERR_INVALID_ARGUMENT;
+    const size_t es = elt_size(kind);
+    if (((uintptr_t)s | (uintptr_t)W | (uintptr_t)g) % es) return SC_ERR_INVALID_ARGUMENT;
+    const uint64_t nbytes = (uint64_t)n * es, wbytes = (uint64_t)C * kGateGroup * 3 * es;
+    if (overlaps(g, s, nbytes) || ranges_overlap(g, nbytes, W, wbytes))
+        return SC_ERR_INVALID_ARGUMENT;
+    DeviceState* d = nullptr;
+    st = device_state(&d, false);
+    if (st != SC_OK) return st;
+    const sc::Store sk = kind == SC_KIND_F32 ? sc::Store::F32 : sc::Store::BF16;
+    return sc::launch_gate(sk, false, s, W, g, B, C, C, L, C, stream) == hipSuccess ? SC_OK
+                                                                                    : SC_ERR_HIP;
 }
 
 template <class F>
@@ -578,14 +655,74 @@ size_t sc_workspace_bytes(sc_kind kind, int64_t B, int64_t C, int64_t L)
 size_t sc_blc_workspace_bytes(sc_kind kind, int64_t B, int64_t L, int64_t C)
 {
     try {
-        int64_t n = 0;
-        if (check_shape(kind, B, C, L, &n) != SC_OK || n == 0) return 0;
-        BlcPlan p;
-        if (blc_plan(kind, B, L, C, nullptr, &p) != SC_OK) return 0;
-        return p.total;
+        return staged_bytes(kind, true, false, B, L, C);
     } catch (...) {
         return 0;
     }
+}
+
+sc_status sc_gate_f32(const float* s, const float* W, float* g, int64_t B, int64_t C, int64_t L,
+                      hipStream_t stream)
+{
+    return guarded([&] { return gate_run(SC_KIND_F32, s, W, g, B, C, L, stream); });
+}
+
+sc_status sc_gate_bf16(const uint16_t* s, const uint16_t* W, uint16_t* g, int64_t B, int64_t C,
+                       int64_t L, hipStream_t stream)
+{
+    return guarded([&] { return gate_run(SC_KIND_BF16, s, W, g, B, C, L, stream); });
+}
+
+size_t sc_gate_conv_workspace_bytes(sc_kind kind, int64_t B, int64_t C, int64_t L)
+{
+    try {
+        return staged_bytes(kind, false, true, B, L, C);
+    } catch (...) {
+        return 0;
+    }
+}
+
+size_t sc_gate_conv_blc_workspace_bytes(sc_kind kind, int64_t B, int64_t L, int64_t C)
+{
+    try {
+        return staged_bytes(kind, true, true, B, L, C);
+    } catch (...) {
+        return 0;
+    }
+}
+
+sc_status sc_gate_conv_ex(sc_kind kind, const void* v, const void* s, const void* W, void* r,
+                          int64_t B, int64_t C, int64_t L, const sc_options* opt, void* ws,
+                          size_t ws_bytes, hipStream_t stream)
+{
+    return guarded([&] {
+        if (!W && B != 0 && C != 0 && L != 0) return SC_ERR_INVALID_ARGUMENT;
+        return staged_run(kind, false, v, s, W ? W : (const void*)1, r, B, L, C, opt, ws, ws_bytes,
+                          stream);
+    });
+}
+
+sc_status sc_gate_conv_blc_ex(sc_kind kind, const void* v, const void* s, const void* W, void* r,
+                              int64_t B, int64_t L, int64_t C, const sc_options* opt, void* ws,
+                              size_t ws_bytes, hipStream_t stream)
+{
+    return guarded([&] {
+        if (!W && B != 0 && C != 0 && L != 0) return SC_ERR_INVALID_ARGUMENT;
+        return staged_run(kind, true, v, s, W ? W : (const void*)1, r, B, L, C, opt, ws, ws_bytes,
+                          stream);
+    });
+}
+
+sc_status sc_gate_conv_blc_f32(const float* v, const float* s, const float* W, float* r,
+                               int64_t B, int64_t L, int64_t C, hipStream_t stream)
+{
+    return sc_gate_conv_blc_ex(SC_KIND_F32, v, s, W, r, B, L, C, nullptr, nullptr, 0, stream);
+}
+
+sc_status sc_gate_conv_blc_bf16(const uint16_t* v, const uint16_t* s, const uint16_t* W,
+                                uint16_t* r, int64_t B, int64_t L, int64_t C, hipStream_t stream)
+{
+    return sc_gate_conv_blc_ex(SC_KIND_BF16, v, s, W, r, B, L, C, nullptr, nullptr, 0, stream);
 }
 
 sc_status sc_causal_conv_blc_f32(const float* v, const float* g, float* r, int64_t B, int64_t L,
@@ -971,6 +1108,6 @@ const char* sc_status_string(sc_status s)
     }
 }
 
-int sc_version(void) { return 600; }
+int sc_version(void) { return 700; }
 
 }  // extern "C"

@@ -111,4 +111,11 @@ hipError_t launch_transpose(int elt_bytes, const void* src0, void* dst0, const v
                             void* dst1, int64_t R, int64_t Cc, int64_t ss, int64_t ds, int64_t sz,
                             int64_t dz, int64_t nz, bool dst_major, hipStream_t s);
 
+// g = Conv1d_G2(sigma(s)) for nb batch rows and the cw channels (whole groups of 64) of a
+// chunk: s token-major (element (z, c, t) at z L C + t C + c, 16-byte aligned) or
+// channel-major (at (z C + c) L + t) with C the channel count of s's rows; W (cw, 64, 3) of
+// the chunk; g channel-major with gcs channels per batch row
+hipError_t launch_gate(Store st, bool token_major, const void* s, const void* W, void* g,
+                       int64_t nb, int64_t C, int64_t cw, int64_t L, int64_t gcs, hipStream_t s_);
+
 }  // namespace sc

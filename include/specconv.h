@@ -229,6 +229,51 @@ sc_status sc_causal_conv_blc_ex(sc_kind kind, const void* v, const void* g, void
                                 size_t ws_bytes, hipStream_t stream);
 
 /*
+ * Gate stream.  The Caracal layer makes each channel's convolution kernel from the input
+ * ("Caracal: Causal Architecture via Spectral Mixing", key design 1): g = Conv1d_G2(sigma(s)),
+ * s a linear projection of the normalised activations, Conv1d_G2 a causal convolution with
+ * kernel 3 grouped by head (64 channels per group), so that
+ *
+ *     g[b][co][t] = sum_{i<64} sum_{k<3} W[co][i][k] * sigmoid(s[b][c0+i][t+k-2])
+ *
+ * with c0 = 64 * (co / 64), the convolution's input zero before t = 0 (left padding 2),
+ * W of shape (C, 64, 3) row-major (PyTorch's Conv1d weight with groups = C / 64).  The
+ * contraction runs on the matrix cores with fp32 accumulation; bfloat16 storage rounds
+ * sigmoid(s) to bfloat16 before the product (the precision a bfloat16 layer computes it in)
+ * and g once at the end.  C must be a multiple of 64 (else SC_ERR_UNSUPPORTED).
+ *
+ *  sc_gate_f32 / _bf16(s, W, g, B, C, L, stream) -- g from s, both channel-major (B, C, L).
+ *      g may overlap neither s nor W.  Allocates nothing.
+ *  sc_gate_conv_ex(kind, v, s, W, r, B, C, L, opt, ws, ws_bytes, stream) -- the layer's
+ *      mixing step r = causal_conv(v, gate(s, W)) with v, s, r channel-major: g is made
+ *      chunk by chunk into the workspace (sc_gate_conv_workspace_bytes; ws null with
+ *      ws_bytes 0 allocates it stream-ordered) and never written to r's side of memory.
+ *  sc_gate_conv_blc_ex / _f32 / _bf16 -- the same with v, s, r token-major (B, L, C), as in
+ *      a model: per chunk v is moved into channel rows, g made from s straight into channel
+ *      rows, convolved and moved back (sc_gate_conv_blc_workspace_bytes; the _f32 / _bf16
+ *      calls allocate).  s must be 16-byte aligned.
+ * kind is SC_KIND_F32 or SC_KIND_BF16; opt, ws and the convolution's limits and accuracy as
+ * sc_causal_conv_ex / sc_causal_conv_blc_ex, for g as computed here.  r may not overlap v, s
+ * or W.  Errors as sc_causal_conv_ex.
+ */
+sc_status sc_gate_f32(const float* s, const float* W, float* g, int64_t B, int64_t C, int64_t L,
+                      hipStream_t stream);
+sc_status sc_gate_bf16(const uint16_t* s, const uint16_t* W, uint16_t* g, int64_t B, int64_t C,
+                       int64_t L, hipStream_t stream);
+size_t sc_gate_conv_workspace_bytes(sc_kind kind, int64_t B, int64_t C, int64_t L);
+size_t sc_gate_conv_blc_workspace_bytes(sc_kind kind, int64_t B, int64_t L, int64_t C);
+sc_status sc_gate_conv_ex(sc_kind kind, const void* v, const void* s, const void* W, void* r,
+                          int64_t B, int64_t C, int64_t L, const sc_options* opt, void* ws,
+                          size_t ws_bytes, hipStream_t stream);
+sc_status sc_gate_conv_blc_ex(sc_kind kind, const void* v, const void* s, const void* W, void* r,
+                              int64_t B, int64_t L, int64_t C, const sc_options* opt, void* ws,
+                              size_t ws_bytes, hipStream_t stream);
+sc_status sc_gate_conv_blc_f32(const float* v, const float* s, const float* W, float* r,
+                               int64_t B, int64_t L, int64_t C, hipStream_t stream);
+sc_status sc_gate_conv_blc_bf16(const uint16_t* v, const uint16_t* s, const uint16_t* W,
+                                uint16_t* r, int64_t B, int64_t L, int64_t C, hipStream_t stream);
+
+/*
  * Gradients (backward pass).  The Caracal models are trained end to end with a next-token
  * loss ("Caracal: Causal Architecture via Spectral Mixing", loss function / training
  * strategy), so the convolution of key design 1 needs its vector-Jacobian product: for the
@@ -341,7 +386,7 @@ int sc_ntt_range_ok(int64_t max_abs_v, int64_t max_abs_g, int64_t L);
 /* Human-readable name of a status code (static storage).  Host only. */
 const char* sc_status_string(sc_status s);
 
-/* Library version: major * 10000 + minor * 100 + patch (this header: 600).  Host only. */
+/* Library version: major * 10000 + minor * 100 + patch (this header: 700).  Host only. */
 int sc_version(void);
 
 #ifdef __cplusplus

@@ -313,3 +313,47 @@ def test_token_major_host_checks(sc):
         assert g(None, B_, C_, 2, 64, 4, None) == INVALID, name
         assert g(A, B_, B_ + 2, 2, 64, 4, None) == INVALID, name
         assert g(None, None, None, 2, 0, 4, None) == OK, name
+
+
+def test_gate_host_checks(sc):
+    h = sc.lib()
+    INVALID, UNSUP, OK, WS = (sc.SC_ERR_INVALID_ARGUMENT, sc.SC_ERR_UNSUPPORTED, sc.SC_OK,
+                              sc.SC_ERR_WORKSPACE)
+    F32, BF16, NTT = sc.KIND_F32, sc.KIND_BF16, sc.KIND_NTT_I32
+    MiB = 1 << 20
+    for name in ("sc_gate_f32", "sc_gate_bf16"):
+        f = getattr(h, name)
+        assert f(A, B_, C_, 1, 100, 16, None) == UNSUP, name           # C not a multiple of 64
+        assert f(None, B_, C_, 1, 64, 16, None) == INVALID, name
+        assert f(A, None, C_, 1, 64, 16, None) == INVALID, name
+        assert f(A, B_, None, 1, 64, 16, None) == INVALID, name
+        assert f(A, B_, A + 64, 1, 64, 16, None) == INVALID, name       # g overlaps s
+        assert f(A, B_, B_ + 64, 1, 64, 16, None) == INVALID, name      # g overlaps W
+        assert f(A + 1, B_, C_, 1, 64, 16, None) == INVALID, name       # misaligned
+        assert f(A, B_, C_, -1, 64, 16, None) == INVALID, name
+        assert f(None, None, None, 0, 64, 16, None) == OK, name
+    # staging: one g buffer (channel-major) or v, g, r buffers (token-major) per chunk
+    assert sc.sc_gate_conv_workspace_bytes(BF16, 8, 1024, 4096) == 16 * MiB
+    assert sc.sc_gate_conv_blc_workspace_bytes(BF16, 8, 4096, 1024) == 3 * 16 * MiB
+    assert sc.sc_gate_conv_workspace_bytes(F32, 1, 100, 64) == 0     # C not a multiple of 64
+    assert sc.sc_gate_conv_workspace_bytes(NTT, 1, 64, 64) == 0
+    D, E = 0x400000, 0x500000
+    W = 0x10000000
+    for name in ("sc_gate_conv_ex", "sc_gate_conv_blc_ex"):
+        f = getattr(h, name)
+        # argument order (v, s, W, r) and sizes B, then C, L (channel-major) or L, C
+        sizes = (1, 64, 16) if name == "sc_gate_conv_ex" else (1, 16, 64)
+        need = (sc.sc_gate_conv_workspace_bytes(F32, 1, 64, 16) if name == "sc_gate_conv_ex"
+                else sc.sc_gate_conv_blc_workspace_bytes(F32, 1, 16, 64))
+        assert need > 0
+        assert f(NTT, A, B_, C_, D, *sizes, None, None, 0, None) == INVALID, name
+        assert f(F32, A, B_, None, D, *sizes, None, None, 0, None) == INVALID, name
+        assert f(F32, A, B_, C_, A + 4, *sizes, None, None, 0, None) == INVALID, name  # r on v
+        assert f(F32, A, B_, C_, C_ + 4, *sizes, None, None, 0, None) == INVALID, name  # r on W
+        assert f(F32, A, B_, C_, D, *sizes, None, W, need - 1, None) == WS, name
+        assert f(F32, A, B_, C_, D, *sizes, None, W + 8, need, None) == INVALID, name
+        assert f(F32, None, None, None, None, 0, *sizes[1:], None, None, 0, None) == OK, name
+    bad = (1, 100, 16)
+    assert h.sc_gate_conv_ex(F32, A, B_, C_, D, *bad, None, None, 0, None) == UNSUP
+    # token-major s must be 16-byte aligned (row vectors)
+    assert h.sc_gate_conv_blc_ex(F32, A, B_ + 4, C_, D, 1, 16, 64, None, None, 0, None) == INVALID
