@@ -9,8 +9,10 @@ After the timed region, the gradient call of the same workload (dv, dg from dr, 
 timed the same way and reported in the `bwd` object (skip with --no-bwd), and the exactly
 causal real-valued call on the same inputs in the `fixed` object (skip with --no-fixed),
 and the calls for a filter shared by the batch on the same shape in the `shared` object
-(skip with --no-shared), and the token-major (B, L, C) call on the same inputs in the
-`token_major` object (skip with --no-blc).
+(skip with --no-shared), the token-major (B, L, C) call on the same inputs in the
+`token_major` object (skip with --no-blc), and the gate-stream calls (g from the gate
+pre-activation on MFMA, alone and as the mixing step's prologue) in the `gate` object (skip
+with --no-gate).
 Inputs are resident in HBM before the timed region.  Several copies of the buffers are
 rotated so that the 256 MB last-level cache cannot hold a step's working set.
 
@@ -434,6 +436,83 @@ def blc_measure(sc, torch, w, dev, steps: int, warmup: int, conv_ms: float) -> d
                                      "channel-major call, and a copy back to (B, L, C)"}
 
 
+def gate_measure(sc, torch, w, dev, steps: int, warmup: int, conv_ms: float) -> dict:
+    """Time the gate calls on the workload's shape: sc_gate_* (s -> g, channel-major), the
+    mixing step with the gate as prologue sc_gate_conv_ex (channel-major) and
+    sc_gate_conv_blc_ex (token-major), each with a caller workspace.  The gate kernel reads s
+    and writes g (2 elements per output) and does 2 * 64 * 3 flops per output on MFMA."""
+    import ctypes
+    from workloads import make_gate_inputs
+    bf = w.storage == "bf16"
+    kind = sc.KIND_BF16 if bf else sc.KIND_F32
+    et = torch.bfloat16 if bf else torch.float32
+    esz = 2 if bf else 4
+    v, s, W = make_gate_inputs(w)
+
+    def dev_t(a, tm=False):
+        if tm:
+            a = np.ascontiguousarray(np.swapaxes(a, 1, 2))
+        t = torch.from_numpy(a.view(np.int16) if bf else a)
+        return t.to(dev).view(et)
+    nsets = max(1, -(-2 * CACHE_BYTES // (3 * w.outputs * esz)))
+    cm = [(dev_t(v), dev_t(s), torch.empty(w.outputs, dtype=et, device=dev)) for _ in range(nsets)]
+    Wd = dev_t(W)
+    stream = torch.cuda.current_stream(dev)
+    sptr = stream.cuda_stream
+    lib = sc.lib()
+    fgate = lib.sc_gate_bf16 if bf else lib.sc_gate_f32
+    ws_cm = sc.sc_gate_conv_workspace_bytes(kind, w.B, w.C, w.L)
+    ws_tm = sc.sc_gate_conv_blc_workspace_bytes(kind, w.B, w.L, w.C)
+    ws = torch.empty(max(ws_cm, ws_tm, 256), dtype=torch.uint8, device=dev)
+
+    def check(st, what):
+        if st != 0:
+            raise RuntimeError("%s failed: %s" % (what, sc.sc_status_string(st)))
+
+    def gate_only(i):
+        _, a, o = cm[i % nsets]
+        check(fgate(a.data_ptr(), Wd.data_ptr(), o.data_ptr(), w.B, w.C, w.L, sptr), "sc_gate")
+
+    def gate_conv(i):
+        a, b, o = cm[i % nsets]
+        check(lib.sc_gate_conv_ex(kind, a.data_ptr(), b.data_ptr(), Wd.data_ptr(), o.data_ptr(),
+                                  w.B, w.C, w.L, None, ws.data_ptr(), ws_cm, sptr),
+              "sc_gate_conv_ex")
+
+    def timed(fn, n):
+        for i in range(warmup):
+            fn(i)
+        return time_rounds(torch, stream, fn, n)[0]
+
+    t_gate = timed(gate_only, steps)
+    t_gc = timed(gate_conv, steps)
+    del cm
+    tm = [(dev_t(v, True), dev_t(s, True), torch.empty(w.outputs, dtype=et, device=dev))
+          for _ in range(nsets)]
+
+    def gate_conv_tm(i):
+        a, b, o = tm[i % nsets]
+        check(lib.sc_gate_conv_blc_ex(kind, a.data_ptr(), b.data_ptr(), Wd.data_ptr(),
+                                      o.data_ptr(), w.B, w.L, w.C, None, ws.data_ptr(), ws_tm,
+                                      sptr), "sc_gate_conv_blc_ex")
+    t_gtm = timed(gate_conv_tm, steps)
+    del tm, ws
+    gb = 2 * w.outputs * esz / (t_gate * 1e-3) / 1e9
+    tf = 2 * 64 * 3 * w.outputs / (t_gate * 1e-3) / 1e12
+    peak_tf = 2500.0 if bf else 157.3
+    return {"entries": ["sc_gate_" + ("bf16" if bf else "f32"), "sc_gate_conv_ex",
+                        "sc_gate_conv_blc_ex"],
+            "gate_ms": round(t_gate, 5),
+            "gate_hbm": {"algorithmic_bytes_per_call": 2 * w.outputs * esz,
+                         "achieved_GBps": round(gb, 1), "frac": round(gb / HBM_PEAK_GBPS, 4)},
+            "gate_mfma": {"flops_per_output": 2 * 64 * 3, "achieved_TFLOPs": round(tf, 2),
+                          "peak_TFLOPs": peak_tf, "frac": round(tf / peak_tf, 4)},
+            "gate_conv_ms": round(t_gc, 5), "gate_conv_blc_ms": round(t_gtm, 5),
+            "conv_ms": round(conv_ms, 5),
+            "gate_conv_value": round(w.outputs / (t_gc * 1e-3), 1),
+            "gate_conv_blc_value": round(w.outputs / (t_gtm * 1e-3), 1), "unit": "outputs/s"}
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -450,6 +529,8 @@ def main(argv=None):
                     help="skip the timing of the filter-shared-by-the-batch calls")
     ap.add_argument("--no-blc", action="store_true",
                     help="skip the timing of the token-major (B, L, C) call")
+    ap.add_argument("--no-gate", action="store_true",
+                    help="skip the timing of the gate-stream calls")
     ap.add_argument("--no-fixed", action="store_true",
                     help="skip the timing of the exactly causal real-valued call")
     ap.add_argument("--calib-copy", action="store_true",
@@ -565,6 +646,9 @@ def main(argv=None):
     if not args.no_blc:
         rec["token_major"] = blc_measure(sc, torch, w, dev, max(5, args.steps // 2), args.warmup,
                                          kernel_ms)
+    if not args.no_gate and w.storage != "i32" and w.C % 64 == 0:
+        rec["gate"] = gate_measure(sc, torch, w, dev, max(5, args.steps // 2), args.warmup,
+                                   kernel_ms)
     if not args.no_fixed and w.storage != "i32" and w.L <= 4096:
         rec["fixed"] = fixed_measure(sc, torch, w, dev, max(5, args.steps // 5), 2)
     if not args.no_leakage:

@@ -16,8 +16,10 @@
 //  1. sigma(s) for tokens t0-2 .. t0+T-1 into LDS, one row per token (the 64 channels of
 //     the group contiguous), zero before t = 0; bf16 storage rounds sigma to bf16, the
 //     precision a bf16 layer computes it in.
-//  2. each wave holds the W fragments of its 32 output channels (all 3 taps, all 64 inputs)
-//     in registers and accumulates 32 x 32 output blocks over T/2 tokens;
+//  2. the group's W (64 x 64 x 3, contiguous) is read with 16-byte loads and passed through
+//     LDS (before the sigma tile, in the same space) into registers: each wave holds the W
+//     fragments of its 32 output channels (all 3 taps, all 64 inputs) and accumulates
+//     32 x 32 output blocks over T/2 tokens;
 //  3. the blocks go through LDS to coalesced stores of g rows (channel-major, t contiguous).
 // s is read token-major ((B, L, C): one 64-channel row per token, 16-byte vector loads) or
 // channel-major ((B, C, L): t contiguous, element loads).
@@ -25,6 +27,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
+#include <type_traits>
 
 #include "sc_device.h"
 #include "sc_internal.h"
@@ -44,7 +47,7 @@ struct GateCfg;
 
 template <>
 struct GateCfg<bf16_io> {
-    static constexpr int T = 256;       // tokens per tile
+    static constexpr int T = 128;       // tokens per tile
     static constexpr int SP = 72;       // LDS row pitch (elements): 144 bytes
     static constexpr int KS = 16;       // reduction depth of one MFMA
 };
@@ -56,7 +59,12 @@ struct GateCfg<f32_io> {
     static constexpr int KS = 2;
 };
 
-__device__ __forceinline__ float sigmoid(float x) { return 1.0f / (1.0f + __expf(-x)); }
+// 1 / (1 + e^-x) with the hardware exponential and reciprocal (each about 1 ulp; far below
+// the fp32 tolerance of this path and below the rounding of sigma to bf16)
+__device__ __forceinline__ float sigmoid(float x)
+{
+    return __builtin_amdgcn_rcpf(1.0f + __expf(-x));
+}
 
 __device__ __forceinline__ uint16_t to_bf16(float x) { return (uint16_t)pack_bf16x2(x, 0.f); }
 
@@ -73,10 +81,16 @@ __global__ __launch_bounds__(GT) void gate_kernel(const typename IO::T* __restri
     constexpr int NB = T / 64;           // 32-token blocks per wave
     constexpr int S_BYTES = (T + 2) * SP * (int)sizeof(E);
     constexpr int O_BYTES = GC * T * (int)sizeof(E);
-    constexpr int LDS_BYTES = S_BYTES > O_BYTES ? S_BYTES : O_BYTES;
+    // W rows of one output channel (192 elements) padded so that the 32 lanes of a fragment
+    // read (32 output channels) spread over the LDS banks, and 16-byte aligned
+    constexpr int WP = GC * 3 + (BF ? 8 : 4);
+    constexpr int W_BYTES = GC * WP * (int)sizeof(E);
+    constexpr int SO_BYTES = S_BYTES > O_BYTES ? S_BYTES : O_BYTES;
+    constexpr int LDS_BYTES = SO_BYTES > W_BYTES ? SO_BYTES : W_BYTES;
     __shared__ __attribute__((aligned(16))) unsigned char smem[LDS_BYTES];
     E* S = (E*)smem;                     // S[tt][ci], tt = t - t0 + 2
     E* O = (E*)smem;                     // O[co][tl], after the products
+    E* Wl = (E*)smem;                    // Wl[co * WP + ci * 3 + k], before the sigma tile
 
     uint32_t id = blockIdx.x;
     const int tile = (int)(id % (uint32_t)ntiles);
@@ -86,38 +100,101 @@ __global__ __launch_bounds__(GT) void gate_kernel(const typename IO::T* __restri
     const int t0 = tile * T, c0 = grp * GC;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
 
-    // 1. sigma(s) into LDS
+    // all global loads first: the group's W (64 * 192 contiguous elements, 16-byte vectors,
+    // W 16-byte aligned) and this tile's s, then W through LDS into registers, then sigma(s)
+    // into the same LDS space
+    constexpr int WEPV = 16 / (int)sizeof(E), WNV = GC * GC * 3 / WEPV / GT;
+    uint4 wraw[WNV];
+    const E* wg = W + (int64_t)c0 * (GC * 3);
+#pragma unroll
+    for (int q = 0; q < WNV; ++q) wraw[q] = *(const uint4*)(wg + (tid + GT * q) * WEPV);
+
+    constexpr int EPV = 16 / (int)sizeof(E);          // elements per 16-byte vector
+    constexpr int VPR = GC / EPV;                     // vectors per token row (token-major)
+    constexpr int NV = T * VPR / GT;                  // token-major vectors per thread
+    constexpr int NE = T * GC / GT;                   // channel-major elements per thread
+    uint4 raw[TM ? NV : 1];
+    float val[TM ? 1 : NE];
+    uint4 halo = make_uint4(0, 0, 0, 0);
+    float hv = 0.f;
+    const int hr = TM ? tid / VPR : (tid & 1);
+    const int hc = TM ? tid % VPR : (tid >> 1);
+    const int ht = t0 - 2 + hr;
+    const bool hact = tid < (TM ? 2 * VPR : 2 * GC) && ht >= 0;
     if constexpr (TM) {
-        constexpr int EPV = 16 / (int)sizeof(E);      // elements per 16-byte vector
-        constexpr int VPR = GC / EPV;                 // vectors per token row
-        constexpr int NV = T * VPR / GT;
         const E* sz = s + z * (int64_t)L * C + c0;
-        uint4 raw[NV];
 #pragma unroll
         for (int q = 0; q < NV; ++q) {
             const int vid = tid + GT * q, r = vid / VPR, p = vid % VPR;
             const int tc = t0 + r < L ? t0 + r : L - 1;
             raw[q] = *(const uint4*)(sz + (int64_t)tc * C + p * EPV);
         }
-        uint4 halo = make_uint4(0, 0, 0, 0);
-        const int hr = tid / VPR, hp = tid % VPR, ht = t0 - 2 + hr;
-        if (tid < 2 * VPR && ht >= 0) halo = *(const uint4*)(sz + (int64_t)ht * C + hp * EPV);
-        auto put = [&](int row, int col, const uint4& w, bool valid) {
+        if (hact) halo = *(const uint4*)(sz + (int64_t)ht * C + hc * EPV);
+    } else {
+        const E* sz = s + (z * C + c0) * (int64_t)L;
+#pragma unroll
+        for (int q = 0; q < NE; ++q) {
+            const int e = tid + GT * q, r = e % T, ci = e / T;
+            const int tc = t0 + r < L ? t0 + r : L - 1;
+            val[q] = IO::load(sz, (int64_t)ci * L + tc);
+        }
+        if (hact) hv = IO::load(sz, (int64_t)hc * L + ht);
+    }
+
+    // W into LDS, row by row (a 16-byte vector never crosses a 192-element row)
+#pragma unroll
+    for (int q = 0; q < WNV; ++q) {
+        const int f = (tid + GT * q) * WEPV;
+        *(uint4*)(Wl + (f / (GC * 3)) * WP + f % (GC * 3)) = wraw[q];
+    }
+    __syncthreads();
+
+    // 2. this wave's W fragments: A[i = co][kk = ci] of tap k
+    const int cb = wave & 1, th = wave >> 1;
+    const int col = 32 * cb + (lane & 31);
+    const int half = lane >> 5;
+    f32x16 acc[NB];
+#pragma unroll
+    for (int m = 0; m < NB; ++m)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[m][r] = 0.f;
+    using AF = typename std::conditional<BF, uint4, float>::type;
+    AF a[3][CS];
+    const E* wl = Wl + col * WP + (BF ? 8 * half : half) * 3;   // then + (KS cs + e) 3 + k
+#pragma unroll
+    for (int k = 0; k < 3; ++k)
+#pragma unroll
+        for (int cs = 0; cs < CS; ++cs) {
             if constexpr (BF) {
-                const uint32_t u[4] = {w.x, w.y, w.z, w.w};
+                uint32_t u[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    u[e] = (uint32_t)wl[(KS * cs + 2 * e) * 3 + k] |
+                           ((uint32_t)wl[(KS * cs + 2 * e + 1) * 3 + k] << 16);
+                a[k][cs] = make_uint4(u[0], u[1], u[2], u[3]);
+            } else {
+                a[k][cs] = wl[KS * cs * 3 + k];
+            }
+        }
+    __syncthreads();   // every wave has its fragments: the space takes sigma(s) now
+
+    // 1 (cont.). sigma(s) into LDS: S[tt][ci], zero before t = 0 and from t = L on
+    if constexpr (TM) {
+        auto put = [&](int row, int cc, const uint4& w, bool valid) {
+            const uint32_t u[4] = {w.x, w.y, w.z, w.w};
+            if constexpr (BF) {
                 uint32_t o[4];
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    const float a = valid ? sigmoid(__uint_as_float(u[e] << 16)) : 0.f;
-                    const float b = valid ? sigmoid(__uint_as_float(u[e] & 0xffff0000u)) : 0.f;
-                    o[e] = pack_bf16x2(a, b);
+                    const float lo = valid ? sigmoid(__uint_as_float(u[e] << 16)) : 0.f;
+                    const float hi = valid ? sigmoid(__uint_as_float(u[e] & 0xffff0000u)) : 0.f;
+                    o[e] = pack_bf16x2(lo, hi);
                 }
-                *(uint4*)(S + row * SP + col) = make_uint4(o[0], o[1], o[2], o[3]);
+                *(uint4*)(S + row * SP + cc) = make_uint4(o[0], o[1], o[2], o[3]);
             } else {
-                const uint32_t u[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
                 for (int e = 0; e < 4; ++e)
-                    S[row * SP + col + e] = valid ? sigmoid(__uint_as_float(u[e])) : 0.f;
+                    S[row * SP + cc + e] = valid ? sigmoid(__uint_as_float(u[e])) : 0.f;
             }
         };
 #pragma unroll
@@ -125,20 +202,8 @@ __global__ __launch_bounds__(GT) void gate_kernel(const typename IO::T* __restri
             const int vid = tid + GT * q, r = vid / VPR, p = vid % VPR;
             put(r + 2, p * EPV, raw[q], t0 + r < L);
         }
-        if (tid < 2 * VPR) put(hr, hp * EPV, halo, ht >= 0);
+        if (tid < 2 * VPR) put(hr, hc * EPV, halo, ht >= 0);
     } else {
-        constexpr int NE = T * GC / GT;
-        const E* sz = s + (z * C + c0) * (int64_t)L;
-        float val[NE];
-#pragma unroll
-        for (int q = 0; q < NE; ++q) {
-            const int e = tid + GT * q, r = e % T, ci = e / T;
-            const int tc = t0 + r < L ? t0 + r : L - 1;
-            val[q] = IO::load(sz, (int64_t)ci * L + tc);
-        }
-        float hv = 0.f;
-        const int hci = tid >> 1, hr = tid & 1, ht = t0 - 2 + hr;
-        if (tid < 2 * GC && ht >= 0) hv = IO::load(sz, (int64_t)hci * L + ht);
 #pragma unroll
         for (int q = 0; q < NE; ++q) {
             const int e = tid + GT * q, r = e % T, ci = e / T;
@@ -148,68 +213,30 @@ __global__ __launch_bounds__(GT) void gate_kernel(const typename IO::T* __restri
         }
         if (tid < 2 * GC) {
             const float x = ht >= 0 ? sigmoid(hv) : 0.f;
-            if constexpr (BF) S[hr * SP + hci] = to_bf16(x);
-            else S[hr * SP + hci] = x;
+            if constexpr (BF) S[hr * SP + hc] = to_bf16(x);
+            else S[hr * SP + hc] = x;
         }
     }
+    __syncthreads();
 
-    // 2. W fragments of this wave's 32 output channels: A[i = co][kk = ci] of tap k
-    const int cb = wave & 1, th = wave >> 1;
-    const int co = c0 + 32 * cb + (lane & 31);
-    const E* wrow = W + (int64_t)co * (GC * 3);
-    const int half = lane >> 5;
-    f32x16 acc[NB];
+    // 2 (cont.). the products
 #pragma unroll
-    for (int m = 0; m < NB; ++m)
+    for (int k = 0; k < 3; ++k)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) acc[m][r] = 0.f;
-
-    if constexpr (BF) {
-        uint4 a[3][CS];
+        for (int cs = 0; cs < CS; ++cs)
 #pragma unroll
-        for (int k = 0; k < 3; ++k)
-#pragma unroll
-            for (int cs = 0; cs < CS; ++cs) {
-                const int ci = KS * cs + 8 * half;
-                uint32_t u[4];
-#pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    u[e] = (uint32_t)wrow[(ci + 2 * e) * 3 + k] |
-                           ((uint32_t)wrow[(ci + 2 * e + 1) * 3 + k] << 16);
-                a[k][cs] = make_uint4(u[0], u[1], u[2], u[3]);
-            }
-        __syncthreads();
-#pragma unroll
-        for (int k = 0; k < 3; ++k)
-#pragma unroll
-            for (int cs = 0; cs < CS; ++cs) {
-                const bf16x8 av = __builtin_bit_cast(bf16x8, a[k][cs]);
-#pragma unroll
-                for (int m = 0; m < NB; ++m) {
-                    const int tl = th * (T / 2) + 32 * m + (lane & 31);
+            for (int m = 0; m < NB; ++m) {
+                const int tl = th * (T / 2) + 32 * m + (lane & 31);
+                if constexpr (BF) {
                     const uint4 bw = *(const uint4*)(S + (tl + k) * SP + KS * cs + 8 * half);
                     acc[m] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                        av, __builtin_bit_cast(bf16x8, bw), acc[m], 0, 0, 0);
-                }
-            }
-    } else {
-        float a[3][CS];
-#pragma unroll
-        for (int k = 0; k < 3; ++k)
-#pragma unroll
-            for (int cs = 0; cs < CS; ++cs) a[k][cs] = wrow[(KS * cs + half) * 3 + k];
-        __syncthreads();
-#pragma unroll
-        for (int k = 0; k < 3; ++k)
-#pragma unroll
-            for (int cs = 0; cs < CS; ++cs)
-#pragma unroll
-                for (int m = 0; m < NB; ++m) {
-                    const int tl = th * (T / 2) + 32 * m + (lane & 31);
+                        __builtin_bit_cast(bf16x8, a[k][cs]), __builtin_bit_cast(bf16x8, bw),
+                        acc[m], 0, 0, 0);
+                } else {
                     const float bv = S[(tl + k) * SP + KS * cs + half];
                     acc[m] = __builtin_amdgcn_mfma_f32_32x32x2f32(a[k][cs], bv, acc[m], 0, 0, 0);
                 }
-    }
+            }
     __syncthreads();   // every wave is done reading S
 
     // 3. blocks to LDS (output storage type), then whole rows to g
@@ -227,17 +254,17 @@ __global__ __launch_bounds__(GT) void gate_kernel(const typename IO::T* __restri
     E* gz = g + (z * gcs + c0) * (int64_t)L;
     if (vec_out) {
         // L is a multiple of the vector's elements and g rows are 16-byte aligned
-        constexpr int EPV = 16 / (int)sizeof(E), VPR = T / EPV, NV = GC * VPR / GT;
+        constexpr int OVPR = T / EPV, ONV = GC * OVPR / GT;
 #pragma unroll
-        for (int q = 0; q < NV; ++q) {
-            const int vid = tid + GT * q, row = vid / VPR, p = vid % VPR;
+        for (int q = 0; q < ONV; ++q) {
+            const int vid = tid + GT * q, row = vid / OVPR, p = vid % OVPR;
             if (t0 + p * EPV < L)
                 *(uint4*)(gz + (int64_t)row * L + t0 + p * EPV) = *(const uint4*)(O + row * T + p * EPV);
         }
     } else {
-        constexpr int NE = GC * T / GT;
+        constexpr int ONE = GC * T / GT;
 #pragma unroll
-        for (int q = 0; q < NE; ++q) {
+        for (int q = 0; q < ONE; ++q) {
             const int e = tid + GT * q, tl = e % T, row = e / T;
             if (t0 + tl < L) gz[(int64_t)row * L + t0 + tl] = O[row * T + tl];
         }

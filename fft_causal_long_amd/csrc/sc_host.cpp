@@ -429,9 +429,9 @@ sc_status run_bwd(sc_kind kind, const void* dr, const void* v, const void* g, vo
 
 // ---------------------------------------------------------------- staged calls
 
-// Elements per staged buffer of the token-major and gate calls: three such buffers (v, g, r
-// of one chunk) stay well inside the 256 MB last-level cache.
-constexpr int64_t kBlcChunkElems = (int64_t)8 << 20;
+// Staging budget of the token-major and gate calls: the staged buffers of one chunk (v, g, r,
+// or g alone) share about this many bytes, well inside the 256 MB last-level cache.
+constexpr int64_t kStageBudget = (int64_t)96 << 20;
 constexpr int64_t kGateGroup = 64;   // channels per gate group (one head)
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -448,12 +448,13 @@ struct BlcPlan {
 sc_status blc_plan(sc_kind kind, int64_t B, int64_t L, int64_t C, const sc_options* opt,
                    int nstage, BlcPlan* p)
 {
-    if (C * L <= kBlcChunkElems) {
+    const int64_t elems = kStageBudget / nstage / (int64_t)elt_size(kind);   // per buffer
+    if (C * L <= elems) {
         p->cw = C;
-        p->nb = std::min<int64_t>(B, std::max<int64_t>(1, kBlcChunkElems / (C * L)));
+        p->nb = std::min<int64_t>(B, std::max<int64_t>(1, elems / (C * L)));
     } else {
         p->nb = 1;
-        p->cw = std::min<int64_t>(C, std::max<int64_t>(64, kBlcChunkElems / L / 64 * 64));
+        p->cw = std::min<int64_t>(C, std::max<int64_t>(64, elems / L / 64 * 64));
     }
     const int64_t nch = p->nb * p->cw;
     p->stage = align256((size_t)(nch * L) * elt_size(kind));
@@ -491,7 +492,7 @@ sc_status staged_run(sc_kind kind, bool tm, const void* v, const void* g, const 
         if (kind != SC_KIND_F32 && kind != SC_KIND_BF16) return SC_ERR_INVALID_ARGUMENT;
         if (C % kGateGroup || C > INT32_MAX) return SC_ERR_UNSUPPORTED;
         if (n > 0) {
-            if ((uintptr_t)W % es) return SC_ERR_INVALID_ARGUMENT;
+            if ((uintptr_t)W % 16) return SC_ERR_INVALID_ARGUMENT;
             if (tm && (uintptr_t)g % 16) return SC_ERR_INVALID_ARGUMENT;
             if (ranges_overlap(r, (uint64_t)n * es, W, (uint64_t)C * kGateGroup * 3 * es))
                 return SC_ERR_INVALID_ARGUMENT;
@@ -589,7 +590,7 @@ sc_status gate_run(sc_kind kind, const void* s, const void* W, void* g, int64_t 
     if (n == 0) return SC_OK;
     if (!s || !W || !g) return SC_ERR_INVALID_ARGUMENT;
     const size_t es = elt_size(kind);
-    if (((uintptr_t)s | (uintptr_t)W | (uintptr_t)g) % es) return SC_ERR_INVALID_ARGUMENT;
+    if (((uintptr_t)s | (uintptr_t)g) % es || (uintptr_t)W % 16) return SC_ERR_INVALID_ARGUMENT;
     const uint64_t nbytes = (uint64_t)n * es, wbytes = (uint64_t)C * kGateGroup * 3 * es;
     if (overlaps(g, s, nbytes) || ranges_overlap(g, nbytes, W, wbytes))
         return SC_ERR_INVALID_ARGUMENT;

@@ -208,8 +208,8 @@ sc_status sc_causal_conv_ex(sc_kind kind, const void* v, const void* g, void* r,
  * the result back, so no caller transpose of the whole tensors is needed.
  *
  *  sc_blc_workspace_bytes(kind, B, L, C) -- bytes of that workspace (three staging buffers
- *      of at most 2^23 elements each, plus the path's own scratch for one chunk); 0 for
- *      invalid arguments or an empty call.
+ *      of at most 32 MiB each, plus the path's own scratch for one chunk); 0 for invalid
+ *      arguments or an empty call.
  *  sc_causal_conv_blc_f32 / _bf16 -- allocate the workspace stream-ordered
  *      (hipMallocAsync / hipFreeAsync on `stream`).
  *  sc_causal_conv_blc_ex -- any kind, with options as sc_causal_conv_ex and a caller
@@ -240,7 +240,8 @@ sc_status sc_causal_conv_blc_ex(sc_kind kind, const void* v, const void* g, void
  * W of shape (C, 64, 3) row-major (PyTorch's Conv1d weight with groups = C / 64).  The
  * contraction runs on the matrix cores with fp32 accumulation; bfloat16 storage rounds
  * sigmoid(s) to bfloat16 before the product (the precision a bfloat16 layer computes it in)
- * and g once at the end.  C must be a multiple of 64 (else SC_ERR_UNSUPPORTED).
+ * and g once at the end.  C must be a multiple of 64 (else SC_ERR_UNSUPPORTED); W must be
+ * 16-byte aligned (else SC_ERR_INVALID_ARGUMENT).
  *
  *  sc_gate_f32 / _bf16(s, W, g, B, C, L, stream) -- g from s, both channel-major (B, C, L).
  *      g may overlap neither s nor W.  Allocates nothing.

@@ -280,9 +280,10 @@ def test_token_major_host_checks(sc):
                               sc.SC_ERR_WORKSPACE)
     F32, BF16, NTT = sc.KIND_F32, sc.KIND_BF16, sc.KIND_NTT_I32
     MiB = 1 << 20
-    # whole batch rows per chunk while a row's C L elements fit 2^23: here 2 rows of 4M
+    # whole batch rows per chunk while a row fits one third of the 96 MiB staging budget:
+    # here 2 rows of 4M float32 or 4 rows of 4M bfloat16
     assert sc.sc_blc_workspace_bytes(F32, 8, 4096, 1024) == 3 * 32 * MiB
-    assert sc.sc_blc_workspace_bytes(BF16, 8, 4096, 1024) == 3 * 16 * MiB
+    assert sc.sc_blc_workspace_bytes(BF16, 8, 4096, 1024) == 3 * 32 * MiB
     assert sc.sc_blc_workspace_bytes(F32, 1, 256, 64) == 3 * 64 * 1024
     # longer rows: blocks of 64k channels, plus the four-step scratch of one block
     inner = sc.sc_workspace_bytes(F32, 1, 128, 65536)
@@ -330,11 +331,12 @@ def test_gate_host_checks(sc):
         assert f(A, B_, A + 64, 1, 64, 16, None) == INVALID, name       # g overlaps s
         assert f(A, B_, B_ + 64, 1, 64, 16, None) == INVALID, name      # g overlaps W
         assert f(A + 1, B_, C_, 1, 64, 16, None) == INVALID, name       # misaligned
+        assert f(A, B_ + 4, C_, 1, 64, 16, None) == INVALID, name       # W not 16-byte aligned
         assert f(A, B_, C_, -1, 64, 16, None) == INVALID, name
         assert f(None, None, None, 0, 64, 16, None) == OK, name
-    # staging: one g buffer (channel-major) or v, g, r buffers (token-major) per chunk
-    assert sc.sc_gate_conv_workspace_bytes(BF16, 8, 1024, 4096) == 16 * MiB
-    assert sc.sc_gate_conv_blc_workspace_bytes(BF16, 8, 4096, 1024) == 3 * 16 * MiB
+    # staging: one g buffer (channel-major, the whole budget) or v, g, r buffers (token-major)
+    assert sc.sc_gate_conv_workspace_bytes(BF16, 8, 1024, 4096) == 64 * MiB
+    assert sc.sc_gate_conv_blc_workspace_bytes(BF16, 8, 4096, 1024) == 3 * 32 * MiB
     assert sc.sc_gate_conv_workspace_bytes(F32, 1, 100, 64) == 0     # C not a multiple of 64
     assert sc.sc_gate_conv_workspace_bytes(NTT, 1, 64, 64) == 0
     D, E = 0x400000, 0x500000
