@@ -120,3 +120,22 @@ def test_ordering_on_a_side_stream(sc):
     torch.cuda.current_stream().wait_stream(side)
     assert np.array_equal(to_host(r).view(np.uint32), ref.view(np.uint32))
     assert np.array_equal(to_host(twice), ref * 2)
+
+
+def test_fixed_kind_bit_exact(sc):
+    # the exact real-valued kind through the token-major call: bit for bit the oracle's
+    # fixed-point result (fraction bits 24 and 24)
+    import ctypes
+    B, L, C = 2, 1000, 70
+    v, g = make_inputs(WORKLOADS[2], B=B, C=C, L=L, seed_offset=91)
+    opt = sc.sc_options(sc.PATH_AUTO, -1, 24, 24)
+    vt, gt = to_device(token_major(v)), to_device(token_major(g))
+    r = torch.empty_like(vt)
+    print("case blc fixed kind", flush=True)
+    st = sc.sc_causal_conv_blc_ex(sc.KIND_FIXED_F32, vt.data_ptr(), gt.data_ptr(), r.data_ptr(),
+                                  B, L, C, ctypes.byref(opt), None, 0,
+                                  torch.cuda.current_stream().cuda_stream)
+    assert st == sc.SC_OK, sc.sc_status_string(st)
+    got = np.ascontiguousarray(np.swapaxes(to_host(r), 1, 2))
+    ref = oracle.causal_conv_fixed_f32(v, g, 24, 24)
+    assert np.array_equal(got.view(np.uint32), ref.astype(np.float32).view(np.uint32))
