@@ -169,48 +169,85 @@ __global__ __launch_bounds__(FUSED_THREADS) void fused_conv_kernel(
         else IO::store2(rs, c * L + t, a, b);
     };
 
-    // 4. y = IDFT_M(Y): threads [c*TB, (c+1)*TB) serve local channel c.  The other half of
-    //    the workgroup computes the direct head meanwhile, from the inputs staged at load
-    //    time: r_t = sum_{j<=t} v_j g_{t-j} in fp32 for t < head.
-    const bool iact = tid < CPW * TB;
-    const int icl = iact ? tid / TB : 0, itau = tid % TB;
-    float2* ybuf = lds + (2 * icl) * REG;
-    if (iact) {
+    if constexpr (M <= 512) {
+        // 4. y = IDFT_M(Y) with 8 values per thread: threads [c*TBI, (c+1)*TBI) serve local
+        //    channel c, every thread of the workgroup busy (radix-8 passes).  For short
+        //    transforms this beats the split below (M = 64: 86 -> 62 us per 64K channels;
+        //    M = 512: 3%), from M = 1024 on it is slower (one more pass and exchange).
+        constexpr int TBI = M / 8;
+        const int icl = tid / TBI, itau = tid % TBI;
+        float2* ybuf = lds + (2 * icl) * REG;
+        float2 y[8];
 #pragma unroll
-        for (int q = 0; q < 16; ++q) x[q] = ybuf[reg_off<TB>(itau, q)];
-    }
-    __syncthreads();
-    // between this barrier and the first one of the inverse, where the active threads run
-    // their first radix-16 pass
-    if (!iact)
-        direct_head<FUSED_THREADS - CPW * TB>(hbuf, CPW, nvalid, L, head, tid - CPW * TB, put);
-    fft_passes<M, true>(x, ybuf, itau, bank, iact);
+        for (int q = 0; q < 8; ++q) y[q] = ybuf[reg_off<TBI>(itau, q)];
+        __syncthreads();
+        fft_passes<M, true, 1, 8>(y, ybuf, itau, bank, true);
 
-    // 5. store: x[q] = 8 M y_m with m = itau + TB q; r_{2m} = Re y_m, r_{2m+1} = Im y_m
-    if (iact) {
+        // 5. store: y[q] = 8 M y_m with m = itau + TBI q (q < 4 covers m < M/2)
         const float scale = 1.0f / (8.0f * (float)M);
-        if (L == M && pair_store) {
 #pragma unroll
-            for (int q = 0; q < 8; ++q) {
-                const int t = 2 * (itau + TB * q);
-                if (2 * TB * q >= HEAD_MAX || t >= head)
-                    put2(icl, t, x[q].x * scale, x[q].y * scale);
-            }
-        } else {
-#pragma unroll
-            for (int q = 0; q < 8; ++q) {
-                const int t = 2 * (itau + TB * q);
-                if (t >= head && t < L) {
-                    const float a = x[q].x * scale, b = x[q].y * scale;
-                    if (t + 1 < L) {
-                        if (pair_store) {
-                            put2(icl, t, a, b);
-                        } else {
-                            put(icl, t, a);
-                            put(icl, t + 1, b);
-                        }
+        for (int q = 0; q < 4; ++q) {
+            const int t = 2 * (itau + TBI * q);
+            if (t >= head && t < L) {
+                const float a = y[q].x * scale, b = y[q].y * scale;
+                if (t + 1 < L) {
+                    if (pair_store) {
+                        put2(icl, t, a, b);
                     } else {
                         put(icl, t, a);
+                        put(icl, t + 1, b);
+                    }
+                } else {
+                    put(icl, t, a);
+                }
+            }
+        }
+        // 6. the direct head, by all threads: r_t = sum_{j<=t} v_j g_{t-j}, fp32, t < head
+        direct_head<FUSED_THREADS>(hbuf, CPW, nvalid, L, head, tid, put);
+    } else {
+        // 4. y = IDFT_M(Y): threads [c*TB, (c+1)*TB) serve local channel c.  The other half of
+        //    the workgroup computes the direct head meanwhile, from the inputs staged at load
+        //    time: r_t = sum_{j<=t} v_j g_{t-j} in fp32 for t < head.
+        const bool iact = tid < CPW * TB;
+        const int icl = iact ? tid / TB : 0, itau = tid % TB;
+        float2* ybuf = lds + (2 * icl) * REG;
+        if (iact) {
+#pragma unroll
+            for (int q = 0; q < 16; ++q) x[q] = ybuf[reg_off<TB>(itau, q)];
+        }
+        __syncthreads();
+        // between this barrier and the first one of the inverse, where the active threads run
+        // their first radix-16 pass
+        if (!iact)
+            direct_head<FUSED_THREADS - CPW * TB>(hbuf, CPW, nvalid, L, head, tid - CPW * TB, put);
+        fft_passes<M, true>(x, ybuf, itau, bank, iact);
+
+        // 5. store: x[q] = 8 M y_m with m = itau + TB q; r_{2m} = Re y_m, r_{2m+1} = Im y_m
+        if (iact) {
+            const float scale = 1.0f / (8.0f * (float)M);
+            if (L == M && pair_store) {
+#pragma unroll
+                for (int q = 0; q < 8; ++q) {
+                    const int t = 2 * (itau + TB * q);
+                    if (2 * TB * q >= HEAD_MAX || t >= head)
+                        put2(icl, t, x[q].x * scale, x[q].y * scale);
+                }
+            } else {
+#pragma unroll
+                for (int q = 0; q < 8; ++q) {
+                    const int t = 2 * (itau + TB * q);
+                    if (t >= head && t < L) {
+                        const float a = x[q].x * scale, b = x[q].y * scale;
+                        if (t + 1 < L) {
+                            if (pair_store) {
+                                put2(icl, t, a, b);
+                            } else {
+                                put(icl, t, a);
+                                put(icl, t + 1, b);
+                            }
+                        } else {
+                            put(icl, t, a);
+                        }
                     }
                 }
             }
