@@ -302,32 +302,42 @@ __global__ __launch_bounds__(512, 4) void ntt_conv_kernel(const void* __restrict
 
     // 1. inputs as exact doubles (|x| < 2^31), times omega_N^n on branch 1.  Positions past
     //    L are read at byte offset 2^31, beyond the descriptor's range, so they read 0 (a
-    //    select instead of a branch keeps all the loads in flight together).
-    double x[2][16];
+    //    select instead of a branch keeps all the loads in flight together).  All 32 element
+    //    loads are issued first and branch 1's 16 twiddle loads right after them: converting
+    //    and multiplying element by element under the branch made every element wait for
+    //    its own loads, one memory latency per element.
+    uint32_t wa[16], wb[16];
 #pragma unroll
     for (int q = 0; q < 16; ++q) {
         const int n = tau + TB * q;
         const bool in = L == M || n < L;
         const uint32_t ob = in ? (uint32_t)(cbase + n) * 4u : 0x80000000u;
         const uint32_t oa = in ? (uint32_t)(cbase + (REV ? L - 1 - n : n)) * 4u : 0x80000000u;
-        const uint32_t wa = __builtin_amdgcn_raw_buffer_load_b32(vs.rs, (int)oa, 0, 0);
-        const uint32_t wb = __builtin_amdgcn_raw_buffer_load_b32(gs.rs, (int)ob, 0, 0);
-        double a, b;
-        if constexpr (FIX) {
-            // exact: a float times a power of two, rounded to an integer, reduced mod p
-            a = reduce<Pr>(round_int((double)__uint_as_float(wa) * sv));
-            b = reduce<Pr>(round_int((double)__uint_as_float(wb) * sg));
-        } else {
-            a = (double)(int32_t)wa;
-            b = (double)(int32_t)wb;
+        wa[q] = __builtin_amdgcn_raw_buffer_load_b32(vs.rs, (int)oa, 0, 0);
+        wb[q] = __builtin_amdgcn_raw_buffer_load_b32(gs.rs, (int)ob, 0, 0);
+    }
+    auto to_residue = [&](uint32_t w, double scale) -> double {
+        if constexpr (FIX)   // exact: a float times a power of two, rounded, reduced mod p
+            return reduce<Pr>(round_int((double)__uint_as_float(w) * scale));
+        else
+            return (double)(int32_t)w;
+    };
+    double x[2][16];
+    if (beta) {
+        W wq[16];
+#pragma unroll
+        for (int q = 0; q < 16; ++q) wq[q] = tw.at((tau + TB * q) * (NTT_TW_N / N), 0);
+#pragma unroll
+        for (int q = 0; q < 16; ++q) {
+            x[0][q] = mulc<Pr>(to_residue(wa[q], sv), wq[q]);
+            x[1][q] = mulc<Pr>(to_residue(wb[q], sg), wq[q]);
         }
-        if (beta) {
-            const W w = tw.at(n * (NTT_TW_N / N), 0);
-            a = mulc<Pr>(a, w);
-            b = mulc<Pr>(b, w);
+    } else {
+#pragma unroll
+        for (int q = 0; q < 16; ++q) {
+            x[0][q] = to_residue(wa[q], sv);
+            x[1][q] = to_residue(wb[q], sg);
         }
-        x[0][q] = a;
-        x[1][q] = b;
     }
 
     // 2. V, G = NTT_M(.) in natural order (values below 2^36)
@@ -347,14 +357,23 @@ __global__ __launch_bounds__(512, 4) void ntt_conv_kernel(const void* __restrict
     //    handing the other half to its partner through LDS (branch 0's v region).
     int32_t* xch = lds + (2 * cl) * 2 * REG;
     double own[16];
+    if (beta) {
+        // omega_N^{-n} = omega_N^{N - n}; the 16 twiddle loads issued together
+        W wq[16];
 #pragma unroll
-    for (int q = 0; q < 16; ++q) {
-        const int n = (M - tau - TB * q) & (M - 1);
-        // omega_N^{-n} = omega_N^{N - n}
-        own[q] = beta ? mulc<Pr>(y[0][q], tw.at(((N - n) & (N - 1)) * (NTT_TW_N / N), 0))
-                      : reduce<Pr>(y[0][q]);
-        if ((q < 8) == (beta == 1)) xch[reg_off<TB>(tau, q)] = (int32_t)own[q];
+        for (int q = 0; q < 16; ++q) {
+            const int n = (M - tau - TB * q) & (M - 1);
+            wq[q] = tw.at(((N - n) & (N - 1)) * (NTT_TW_N / N), 0);
+        }
+#pragma unroll
+        for (int q = 0; q < 16; ++q) own[q] = mulc<Pr>(y[0][q], wq[q]);
+    } else {
+#pragma unroll
+        for (int q = 0; q < 16; ++q) own[q] = reduce<Pr>(y[0][q]);
     }
+#pragma unroll
+    for (int q = 0; q < 16; ++q)
+        if ((q < 8) == (beta == 1)) xch[reg_off<TB>(tau, q)] = (int32_t)own[q];
     __syncthreads();
 #pragma unroll
     for (int q = 0; q < 16; ++q) {
