@@ -55,14 +55,21 @@ __global__ __launch_bounds__(512) void fs_columns_fwd(const typename IO::T* __re
     const Span vs = make_span(v, (ch_begin + chl) * (int64_t)L, L);
     const Span gs = make_span(g, (ch_begin + chl) * (int64_t)L, L);
 
+    // all 32 input loads first, then (branch 1) the 16 twiddles W_N^n together: a multiply
+    // under the branch inside the load loop made each element wait for its own loads
     float2 x[16];
 #pragma unroll
     for (int q = 0; q < 16; ++q) {
         const int n = n1 + M2 * (tau + TQ * q);
         const int nv = REV ? (n < L ? L - 1 - n : IO::OOB) : n;
-        float2 z = make_float2(IO::load(vs, nv), IO::load(gs, n));
-        if (beta) z = cmul(z, tw.tn[n]);                       // W_N^n
-        x[q] = z;
+        x[q] = make_float2(IO::load(vs, nv), IO::load(gs, n));
+    }
+    if (beta) {
+        float2 w[16];
+#pragma unroll
+        for (int q = 0; q < 16; ++q) w[q] = tw.tn[n1 + M2 * (tau + TQ * q)];
+#pragma unroll
+        for (int q = 0; q < 16; ++q) x[q] = cmul(x[q], w[q]);
     }
     fft_passes<M1, false>(x, lds + (beta * NCOL + c) * CREG, tau, bank, true);
     // x[q] = column output k2 = tau + TQ q; times W_M^{n1 k2}
