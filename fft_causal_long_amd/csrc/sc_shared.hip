@@ -305,10 +305,15 @@ __global__ __launch_bounds__(SH_THREADS) void shared_dk_kernel(
         const int64_t row = ((int64_t)b * C + c0) * L;
         const Span ds_ = make_span(dr, row, (int64_t)nvalid * L);
         const Span vs_ = make_span(v, row, (int64_t)nvalid * L);
+        // Opaque copies of the thread's indices: the twiddle and LDS addresses below are the
+        // same in every row, and without these the compiler hoists the twiddle loads out of
+        // the row loop and holds them all in registers (175 VGPRs, serialised loads).
+        int tau_r = tau, lt_r = lt;
+        asm volatile("" : "+v"(tau_r), "+v"(lt_r));
         float2 x[16];
 #pragma unroll
         for (int q = 0; q < 16; ++q) {
-            const int n = tau + TB * q;
+            const int n = tau_r + TB * q;
             const int e = n < L ? cbase + n : IO::OOB;
             const int er = n < L ? cbase + L - 1 - n : IO::OOB;
             x[q] = make_float2(IO::load(ds_, er), IO::load(vs_, e));
@@ -316,23 +321,26 @@ __global__ __launch_bounds__(SH_THREADS) void shared_dk_kernel(
         if (!beta) {
 #pragma unroll
             for (int q = 0; q < (TB >= SH_HEAD_MAX ? 1 : SH_HEAD_MAX / TB); ++q) {
-                const int n = tau + TB * q;
+                const int n = tau_r + TB * q;
                 if (n < head) {
                     hbuf[cl * 2 * SH_HEAD_MAX + n] = x[q].x;
                     hbuf[cl * 2 * SH_HEAD_MAX + SH_HEAD_MAX + n] = x[q].y;
                 }
             }
         } else {
+            float2 w[16];
 #pragma unroll
-            for (int q = 0; q < 16; ++q) x[q] = cmul(x[q], tw_get<false>(bank, N, tau + TB * q));
+            for (int q = 0; q < 16; ++q) w[q] = tw_get<false>(bank, N, tau_r + TB * q);
+#pragma unroll
+            for (int q = 0; q < 16; ++q) x[q] = cmul(x[q], w[q]);
         }
-        fft_passes<M, false>(x, ubuf, tau, bank, true);
+        fft_passes<M, false>(x, ubuf, tau_r, bank, true);
 #pragma unroll
-        for (int q = 0; q < 16; ++q) ubuf[reg_off<TB>(tau, q)] = x[q];
+        for (int q = 0; q < 16; ++q) ubuf[reg_off<TB>(tau_r, q)] = x[q];
         __syncthreads();
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const int k = lt + 2 * TB * i;
+            const int k = lt_r + 2 * TB * i;
             float2 yk, ymk;
             unpack_pair<M>(k, u0, u1, bank, yk, ymk);
             if (k == 0) {
