@@ -324,13 +324,19 @@ __global__ __launch_bounds__(512, 4) void ntt_conv_kernel(const void* __restrict
     };
     double x[2][16];
     if (beta) {
-        W wq[16];
+        // the twiddles in two batches of 8, which bounds the registers held at once
 #pragma unroll
-        for (int q = 0; q < 16; ++q) wq[q] = tw.at((tau + TB * q) * (NTT_TW_N / N), 0);
+        for (int h = 0; h < 2; ++h) {
+            W wq[8];
 #pragma unroll
-        for (int q = 0; q < 16; ++q) {
-            x[0][q] = mulc<Pr>(to_residue(wa[q], sv), wq[q]);
-            x[1][q] = mulc<Pr>(to_residue(wb[q], sg), wq[q]);
+            for (int i = 0; i < 8; ++i)
+                wq[i] = tw.at((tau + TB * (8 * h + i)) * (NTT_TW_N / N), 0);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const int q = 8 * h + i;
+                x[0][q] = mulc<Pr>(to_residue(wa[q], sv), wq[i]);
+                x[1][q] = mulc<Pr>(to_residue(wb[q], sg), wq[i]);
+            }
         }
     } else {
 #pragma unroll
