@@ -254,6 +254,68 @@ def cpu_baseline(w, v, g, budget_s: float = 10.0):
     }
 
 
+def oracle_rate(run, total: int, per_unit: int, what: str, budget_s: float = 3.0) -> dict:
+    """Time run(n) (an oracle function on the first n units of a workload) on growing n until
+    one call takes >= budget_s / 2; report per_unit * n / time."""
+    import oracle
+    n = 1
+    while True:
+        t0 = time.perf_counter()
+        run(n)
+        dt = time.perf_counter() - t0
+        if dt >= budget_s / 2 or n >= total:
+            break
+        n = min(total, max(2 * n, int(n * (budget_s / 2) / max(dt, 1e-3))))
+    return {"value": round(per_unit * n / dt, 1), "cores": oracle.default_threads(),
+            "kind": "oracle", "sample": "%d of %d %s, %.2f s wall" % (n, total, what, dt)}
+
+
+def next_rows_oracles(w, rec: dict) -> None:
+    """The oracle of each measured NEXT-row call, timed on a bounded sample of the same
+    workload (host cores), beside the GPU figure: gradients, exact real-valued call,
+    shared filter (apply and gradients), gate."""
+    import oracle
+    from workloads import (bf16_bits_to_f32, make_gate_inputs, make_grad, make_inputs,
+                           make_shared_filter)
+    v, g = make_inputs(w)
+    L = w.L
+    if "bwd" in rec:
+        dr = make_grad(w)
+        d2, v2, g2 = dr.reshape(-1, L), v.reshape(-1, L), g.reshape(-1, L)
+        f = oracle.causal_conv_bwd_i64 if w.storage == "i32" else \
+            (lambda a, b, c: oracle.causal_conv_bwd_f64(a, b, c, with_scale=False))
+        rec["bwd"]["cpu_oracle"] = dict(
+            oracle_rate(lambda n: f(d2[:n], v2[:n], g2[:n]), d2.shape[0], L, "channels"),
+            unit="positions/s")
+    if "fixed" in rec:
+        vf, gf = v.reshape(-1, L), g.reshape(-1, L)
+        if w.storage == "bf16":
+            vf, gf = bf16_bits_to_f32(vf), bf16_bits_to_f32(gf)
+        rec["fixed"]["cpu_oracle"] = dict(
+            oracle_rate(lambda n: oracle.causal_conv_fixed_f32(vf[:n], gf[:n], FIXED_FRAC,
+                                                               FIXED_FRAC),
+                        vf.shape[0], L, "channels", budget_s=2.0), unit="outputs/s")
+    if "shared" in rec:
+        k = make_shared_filter(w)
+        dr = make_grad(w)
+
+        def apply_(n):
+            kb = np.ascontiguousarray(np.broadcast_to(oracle.as_f64(k[:n])[None], (w.B, n, L)))
+            oracle.causal_conv_f64(v[:, :n], kb, with_scale=False)
+        rec["shared"]["cpu_oracle"] = dict(oracle_rate(apply_, w.C, w.B * L, "channels (all rows)"),
+                                           unit="outputs/s")
+        rec["shared"]["bwd"]["cpu_oracle"] = dict(
+            oracle_rate(lambda n: oracle.shared_conv_bwd_f64(dr[:, :n], v[:, :n], k[:n]), w.C,
+                        w.B * L, "channels (all rows)"), unit="positions/s")
+    if "gate" in rec:
+        _, s_, W = make_gate_inputs(w, B=1)
+        rec["gate"]["cpu_oracle"] = dict(
+            oracle_rate(lambda n: oracle.gate_f64(s_[:, :64 * n], W[:64 * n]), w.C // 64, 64 * L,
+                        "64-channel groups of one batch row"), unit="outputs/s")
+    if "token_major" in rec:
+        rec["token_major"]["cpu_oracle"] = "the channel-major oracle (cpu_baseline): the same sums"
+
+
 def bwd_measure(sc, torch, w, dev, steps: int, warmup: int) -> dict:
     """Time the gradient call (dv and dg for one upstream gradient dr) on the same workload:
     inputs dr, v, g resident, buffers rotated like the forward, HIP events around each call
@@ -426,7 +488,10 @@ def blc_measure(sc, torch, w, dev, steps: int, warmup: int, conv_ms: float) -> d
         torch_route(i)
     t_torch = time_rounds(torch, stream, torch_route, max(3, steps // 2))[0]
     del bufs, ws
+    gb = 3 * w.outputs * esz / (t_blc * 1e-3) / 1e9
     return {"entry": "sc_causal_conv_blc_ex", "layout": "(B, L, C)",
+            "hbm": {"algorithmic_bytes_per_call": 3 * w.outputs * esz,
+                    "achieved_GBps": round(gb, 1), "frac": round(gb / HBM_PEAK_GBPS, 4)},
             "ms_per_call": round(t_blc, 5), "value": round(w.outputs / (t_blc * 1e-3), 1),
             "unit": "outputs/s", "workspace_bytes": nbytes,
             "channel_major_ms": round(conv_ms, 5),
@@ -655,6 +720,7 @@ def main(argv=None):
         rec["leakage"] = leakage_probe(sc, torch, dev)
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(w, v, g)
+        next_rows_oracles(w, rec)
     print(json.dumps(rec), flush=True)
     return 0
 
