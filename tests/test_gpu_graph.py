@@ -1,0 +1,74 @@
+"""The library under HIP graph capture: the fused call and the token-major call (caller
+workspace) are captured in a torch CUDA graph on a side stream, the graph is replayed several
+times with the program's own eager work in between, and every replay must equal the eager
+result bit for bit.  The library allocates nothing on these paths, so capture is valid."""
+import numpy as np
+import pytest
+import torch
+
+from tests.gpu_util import to_device, to_host
+from workloads import WORKLOADS, make_inputs
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def sc():
+    import fft_causal_long_amd as m
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    return m
+
+
+def replay_check(graph, out, ref, refresh):
+    for i in range(3):
+        out.zero_()
+        refresh(i)                       # eager work between replays
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int16) if out.dtype == torch.bfloat16 else out,
+                           ref.view(torch.int16) if ref.dtype == torch.bfloat16 else ref), i
+
+
+def test_fused_call_in_a_graph(sc):
+    v, g = make_inputs(WORKLOADS[3], B=2, C=64, L=4096, seed_offset=61)
+    vd, gd = to_device(v), to_device(g)
+    ref = sc.causal_conv(vd, gd)
+    out = torch.empty_like(ref)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    print("case graph fused", flush=True)
+    with torch.cuda.stream(side):
+        sc.causal_conv(vd, gd, out=out)          # warm-up on the capture stream
+        torch.cuda.synchronize()
+        with torch.cuda.graph(graph, stream=side):
+            sc.causal_conv(vd, gd, out=out)
+    torch.cuda.synchronize()
+    replay_check(graph, out, ref, lambda i: torch.mul(vd, 1, out=torch.empty_like(vd)))
+
+
+def test_token_major_call_in_a_graph(sc):
+    B, L, C = 2, 1000, 130
+    v, g = make_inputs(WORKLOADS[2], B=B, C=C, L=L, seed_offset=62)
+    vt = to_device(np.ascontiguousarray(np.swapaxes(v, 1, 2)))
+    gt = to_device(np.ascontiguousarray(np.swapaxes(g, 1, 2)))
+    ws = torch.empty(sc.sc_blc_workspace_bytes(sc.KIND_F32, B, L, C), dtype=torch.uint8,
+                     device="cuda:0")
+    ref = sc.causal_conv_blc(vt, gt, workspace=ws)
+    out = torch.empty_like(ref)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    print("case graph token-major", flush=True)
+    with torch.cuda.stream(side):
+        sc.causal_conv_blc(vt, gt, out=out, workspace=ws)
+        torch.cuda.synchronize()
+        with torch.cuda.graph(graph, stream=side):
+            sc.causal_conv_blc(vt, gt, out=out, workspace=ws)
+    torch.cuda.synchronize()
+    # eager work that reuses the workspace between replays
+    replay_check(graph, out, ref,
+                 lambda i: sc.causal_conv_blc(vt, gt, out=torch.empty_like(vt), workspace=ws))
