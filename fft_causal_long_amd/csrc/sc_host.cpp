@@ -27,6 +27,9 @@ constexpr int64_t kFourStepChunkBytes = (int64_t)SC_FS_CHUNK_MB << 20;
 constexpr int64_t kMaxLNtt = 4096;
 constexpr int64_t kNttP = 998244353;
 constexpr int32_t kMaxFrac = 64;          // |fixed-point fraction bits| of the exact real kind
+// the shared-filter gradients take the one-kernel path when it has at least this many
+// workgroups (its row loop runs per channel group; fewer groups leave CUs idle)
+constexpr int64_t kSharedBwdMinBlocks = 512;
 
 sc_status upload(const void* host, size_t bytes, void** dev)
 {
@@ -993,14 +996,26 @@ sc_status shared_bwd_run(sc_kind kind, const void* dr, const void* v, const void
         st = spectrum_run(kind, k, own, C, L, stream);
         spec = own;
     }
-    if (st == SC_OK) st = apply_run(kind, dr, spec, dv, B, C, L, stream, true);
     if (st == SC_OK) {
         const int M = (int)std::max<int64_t>(64, next_pow2(L));
         const sc::Store s = kind == SC_KIND_F32 ? sc::Store::F32 : sc::Store::BF16;
-        const bool pair = L % 2 == 0 && (uintptr_t)dk % (2 * es) == 0;
-        if (sc::launch_shared_dk(s, dr, v, dk, (int)B, (int)C, (int)L, M, kDefaultHead, pair,
-                                 d->fused_tw, stream) != hipSuccess)
-            st = SC_ERR_HIP;
+        if (B <= INT32_MAX && sc::shared_bwd_blocks(C, M) >= kSharedBwdMinBlocks) {
+            // one kernel: dv and dk from the same transform per row
+            const bool pair = L % 2 == 0 && ((uintptr_t)dk | (uintptr_t)dv) % (2 * es) == 0;
+            if (sc::launch_shared_bwd(s, dr, v, (const float2*)spec, dv, dk, (int)B, (int)C,
+                                      (int)L, M, kDefaultHead, pair, d->fused_tw,
+                                      stream) != hipSuccess)
+                st = SC_ERR_HIP;
+        } else {
+            // too few channel groups to fill the GPU with the row loop alone: dv by the
+            // apply kernel on every row pair, dk by the row-looping kernel
+            st = apply_run(kind, dr, spec, dv, B, C, L, stream, true);
+            const bool pair = L % 2 == 0 && (uintptr_t)dk % (2 * es) == 0;
+            if (st == SC_OK &&
+                sc::launch_shared_dk(s, dr, v, dk, (int)B, (int)C, (int)L, M, kDefaultHead, pair,
+                                     d->fused_tw, stream) != hipSuccess)
+                st = SC_ERR_HIP;
+        }
     }
     if (own && hipFreeAsync(own, stream) != hipSuccess && st == SC_OK) st = SC_ERR_HIP;
     return st;

@@ -98,6 +98,14 @@ hipError_t launch_shared_apply(Store st, const void* v, const float2* spec, void
 // dk[c][j] = sum_b sum_{t>=j} dr[b][c][t] v[b][c][t-j]; pair_store as the fused kernel's.
 hipError_t launch_shared_dk(Store st, const void* dr, const void* v, void* dk, int B, int C, int L,
                             int M, int head, bool pair_store, const float2* tw, hipStream_t stream);
+// workgroups launch_shared_bwd uses for C channels at transform length M
+int64_t shared_bwd_blocks(int64_t C, int M);
+// gradients for the upstream gradient dr: dv[b][c][j] = sum_{t>=j} dr[b][c][t] k[c][t-j] from
+// the spectrum, dk[c][j] = sum_b sum_{t>=j} dr[b][c][t] v[b][c][t-j]; pair_store as the fused
+// kernel's (for both outputs).  C L elements stay below 2^31 bytes (host check).
+hipError_t launch_shared_bwd(Store st, const void* dr, const void* v, const float2* spec, void* dv,
+                             void* dk, int B, int C, int L, int M, int head, bool pair_store,
+                             const float2* tw, hipStream_t stream);
 
 // Direct summation r_t = sum_{j<=t} v_j g_{t-j} in fp32, one thread per output.
 hipError_t launch_direct(Store st, const void* v, const void* g, void* r, int64_t nch, int L,

@@ -259,7 +259,7 @@ __global__ __launch_bounds__(SH_THREADS, (M >= 512 ? 4 : 1)) void shared_apply_k
     }
 }
 
-// ---------------------------------------------------------------- filter gradient
+// ---------------------------------------------------------------- filter gradient (row loop)
 
 // dk[c][j] = sum_b sum_{t>=j} dr[b][c][t] v[b][c][t-j] = sum_b rev(causal(rev(dr_b), v_b))_j.
 // Per channel and batch row the transform of z = rev(dr_b) + i v_b carries both spectra;
@@ -415,6 +415,258 @@ __global__ __launch_bounds__(SH_THREADS) void shared_dk_kernel(
     }
 }
 
+// ---------------------------------------------------------------- both gradients, one kernel
+
+// From the branch spectra of z = rev(dr_b) + i v_b (u0[j] = Z_{2j}, u1[j] = Z_{2j+1}) form, at
+// bins k and M - k, the real-output inverse inputs of both gradients:
+//   dk: Y of X = DR' V (scaled by 8, as unpack_pair), summed over the rows by the caller;
+//   dv: Y of X' = DR' K with K from the filter spectrum (stored / N), scaled by 1/(2N)
+//       relative to the dk scaling, so dv takes the output scale 1/2 where dk takes 1/(8M).
+// DR'_k = (Z_k + conj Z_{N-k}) / 2 and V_k = (Z_k - conj Z_{N-k}) / (2i).
+template <int M>
+__device__ __forceinline__ void y_of(float2 x1, float2 x2, float2 w, float2& yk, float2& ymk)
+{
+    // S = X_k + X_{k+M}, D = X_k - X_{k+M} with X_{k+M} = conj X_{M-k}
+    const float2 sm = make_float2(x1.x + x2.x, x1.y - x2.y);
+    const float2 df = make_float2(x1.x - x2.x, x1.y + x2.y);
+    const float2 t = cmulc(df, w);                                 // W_N^{-k} D
+    yk = make_float2(sm.x - t.y, sm.y + t.x);
+    ymk = make_float2(sm.x + t.y, t.x - sm.y);
+}
+
+template <int M>
+__device__ __forceinline__ void unpack_grads(int k, const float2* __restrict__ u0,
+                                             const float2* __restrict__ u1,
+                                             const float2* __restrict__ sp, const Bank& bank,
+                                             float2& yk, float2& ymk, float2& zk, float2& zmk)
+{
+    constexpr int N = 2 * M;
+    const int b = k & 1, j = k >> 1, jm = (M / 2 - j - b) & (M - 1);
+    const float2* u = b ? u1 : u0;
+    const float2 p1 = u[lds_pad(j)];
+    const float2 q1 = conjf2(u[lds_pad((M - j - b) & (M - 1))]);
+    const float2 p2 = u[lds_pad(jm)];
+    const float2 q2 = conjf2(u[lds_pad(M / 2 + j)]);
+    const float2 s1 = cadd(p1, q1), d1 = csub(p1, q1);
+    const float2 s2 = cadd(p2, q2), d2 = csub(p2, q2);
+    const float2 w = tw_get<false>(bank, N, k);
+    // dk: 4 X = -i (P + Q)(P - Q) at k and M - k
+    const float2 x1 = make_float2(__builtin_fmaf(s1.x, d1.y, s1.y * d1.x),
+                                  __builtin_fmaf(s1.y, d1.y, -s1.x * d1.x));
+    const float2 x2 = make_float2(__builtin_fmaf(s2.x, d2.y, s2.y * d2.x),
+                                  __builtin_fmaf(s2.y, d2.y, -s2.x * d2.x));
+    y_of<M>(x1, x2, w, yk, ymk);
+    // dv: (P + Q) K / N = 2 DR' K / N at k and M - k
+    y_of<M>(cmul(s1, sp[b * M + j]), cmul(s2, sp[b * M + jm]), w, zk, zmk);
+}
+
+// Gradients for a filter shared by the batch, one kernel:
+//   dv[b][c][j] = sum_{t>=j} dr[b][c][t] k[c][t-j] = rev(causal(rev(dr_b), k))_j
+//   dk[c][j]    = sum_b sum_{t>=j} dr[b][c][t] v[b][c][t-j] = sum_b rev(causal(rev(dr_b), v_b))_j
+// A workgroup serves 4096/M channels (as the per-row-gate kernel) and loops over the B rows.
+// Per row, one transform of z = rev(dr_b) + i v_b carries the spectra of rev(dr_b) and v_b;
+// the unpack gives the inverse input of dv_b (times the filter's spectrum), which is inverted
+// and stored at once, and that of dk (times V), which is linear in the product and summed
+// over the rows in registers and inverted once at the end.  Direct heads (t < head): dv_b's
+// per row, dk's summed over the rows in LDS, both by the half of the workgroup that is idle
+// during an inverse.  Outputs are written reversed.
+template <int M, class IO>
+__global__ __launch_bounds__(SH_THREADS, (M >= 512 ? 4 : 1)) void shared_bwd_kernel(
+    const typename IO::T* __restrict__ dr, const typename IO::T* __restrict__ v,
+    const float2* __restrict__ spec, typename IO::T* __restrict__ dv,
+    typename IO::T* __restrict__ dk, int B, int C, int L, int head, int pair_store,
+    const float2* __restrict__ tw)
+{
+    constexpr int N = 2 * M, TB = M / 16, UNITS = SH_THREADS / TB, CPW = UNITS / 2;
+    constexpr int CT = CPW * TB;
+    constexpr int REG = M + M / 16 + (M >= 256 ? SH_LDS_EXTRA : 0);
+    constexpr int SS = spec_stride<M>();
+    __shared__ float2 lds[UNITS * REG];
+    __shared__ float hbuf[CPW * 3 * SH_HEAD_MAX];    // rev(dr_b), v_b, k: first values
+    __shared__ float hsum[CPW * SH_HEAD_MAX];        // dk's head, summed over the rows
+
+    const Bank bank = make_bank(tw);
+    const int tid = threadIdx.x;
+    const int unit = tid / TB, tau = tid % TB;
+    const int cl = unit >> 1, beta = unit & 1;
+    const int c0 = blockIdx.x * CPW;
+    const int nvalid = (C - c0) < CPW ? (C - c0) : CPW;
+    float2* ubuf = lds + unit * REG;
+    float2* u0 = lds + (2 * cl) * REG;
+    const float2* u1 = u0 + REG;
+    const int lt = tid - cl * 2 * TB;
+    const int cbase = cl * L;
+    const float2* sp = spec + (int64_t)(c0 + (cl < nvalid ? cl : 0)) * SS;
+    // inverse: the first CT threads, one channel per TB of them; heads: the others
+    const bool iact = tid < CT;
+    const int icl = iact ? tid / TB : 0, itau = tid % TB;
+    float2* ybuf = lds + (2 * icl) * REG;
+    const int nout = CPW * head;
+    int S = 1;
+    while (S < 8 && 2 * S * nout <= SH_THREADS - CT) S *= 2;
+    for (int i = tid; i < CPW * SH_HEAD_MAX; i += SH_THREADS) {
+        hsum[i] = 0.f;
+        const int c2 = i / SH_HEAD_MAX, n = i - c2 * SH_HEAD_MAX;
+        hbuf[c2 * 3 * SH_HEAD_MAX + 2 * SH_HEAD_MAX + n] =
+            c2 < nvalid ? ((const float*)(spec + (int64_t)(c0 + c2) * SS + 2 * M))[n] : 0.f;
+    }
+
+    float2 yacc[4], ymacc[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) yacc[i] = ymacc[i] = make_float2(0.f, 0.f);
+
+    for (int b = 0; b < B; ++b) {
+        const int64_t row = ((int64_t)b * C + c0) * L;
+        const Span ds_ = make_span(dr, row, (int64_t)nvalid * L);
+        const Span vs_ = make_span(v, row, (int64_t)nvalid * L);
+        const Span os_ = make_span(dv, row, (int64_t)nvalid * L);
+        // Opaque copies of the thread's indices: the twiddle, spectrum and LDS addresses
+        // below are the same in every row, and the compiler would otherwise hoist their loads
+        // out of the row loop and hold them all in registers.
+        int tau_r = tau, lt_r = lt, itau_r = itau;
+        asm volatile("" : "+v"(tau_r), "+v"(lt_r), "+v"(itau_r));
+        float2 x[16];
+#pragma unroll
+        for (int q = 0; q < 16; ++q) {
+            const int n = tau_r + TB * q;
+            const int e = n < L ? cbase + n : IO::OOB;
+            const int er = n < L ? cbase + L - 1 - n : IO::OOB;
+            x[q] = make_float2(IO::load(ds_, er), IO::load(vs_, e));
+        }
+        if (!beta) {
+#pragma unroll
+            for (int q = 0; q < (TB >= SH_HEAD_MAX ? 1 : SH_HEAD_MAX / TB); ++q) {
+                const int n = tau_r + TB * q;
+                if (n < head) {
+                    hbuf[cl * 3 * SH_HEAD_MAX + n] = x[q].x;
+                    hbuf[cl * 3 * SH_HEAD_MAX + SH_HEAD_MAX + n] = x[q].y;
+                }
+            }
+        } else {
+            float2 w[16];
+#pragma unroll
+            for (int q = 0; q < 16; ++q) w[q] = tw_get<false>(bank, N, tau_r + TB * q);
+#pragma unroll
+            for (int q = 0; q < 16; ++q) x[q] = cmul(x[q], w[q]);
+        }
+        fft_passes<M, false>(x, ubuf, tau_r, bank, true);
+#pragma unroll
+        for (int q = 0; q < 16; ++q) ubuf[reg_off<TB>(tau_r, q)] = x[q];
+        __syncthreads();
+
+        // unpack: dk's Y summed, dv's Y kept
+        float2 zk[4], zmk[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int k = lt_r + 2 * TB * i;
+            float2 yk, ymk;
+            unpack_grads<M>(k, u0, u1, sp, bank, yk, ymk, zk[i], zmk[i]);
+            if (k == 0) {
+                // Y_{M/2} in place of the absent Y_M
+                float2 u_, v_;
+                unpack_grads<M>(M / 2, u0, u1, sp, bank, ymk, u_, zmk[i], v_);
+            }
+            yacc[i] = cadd(yacc[i], yk);
+            ymacc[i] = cadd(ymacc[i], ymk);
+        }
+        __syncthreads();   // every unpack has read Z
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int k = lt_r + 2 * TB * i;
+            u0[lds_pad(k)] = zk[i];
+            u0[lds_pad(k == 0 ? M / 2 : M - k)] = zmk[i];
+        }
+        __syncthreads();
+        if (iact) {
+#pragma unroll
+            for (int q = 0; q < 16; ++q) x[q] = ybuf[reg_off<TB>(itau_r, q)];
+        }
+        __syncthreads();
+        if (!iact) {
+            // this row's heads: dv_{L-1-t} = sum_{j<=t} rev(dr)_j k_{t-j} (stored), and the
+            // row's share of dk's head sum_{j<=t} rev(dr)_j v_{t-j} (added to hsum by the
+            // group's first lane); each sum split over S lanes
+            for (int base = 0; base < 2 * nout * S; base += SH_THREADS - CT) {
+                const int idx = base + tid - CT, o2 = idx / S, sl = idx - o2 * S;
+                const int which = o2 >= nout ? 1 : 0, o = o2 - which * nout;
+                const int c2 = o / (head > 0 ? head : 1), t = o - c2 * head;
+                float acc = 0.f;
+                if (o2 < 2 * nout) {
+                    const float* hd = hbuf + c2 * 3 * SH_HEAD_MAX;
+                    const float* hg = hd + (which ? SH_HEAD_MAX : 2 * SH_HEAD_MAX);
+                    for (int j = sl; j <= t; j += S) acc = __builtin_fmaf(hd[j], hg[t - j], acc);
+                }
+                for (int d = 1; d < S; d <<= 1) acc += __shfl_xor(acc, d);
+                if (o2 < 2 * nout && sl == 0) {
+                    if (which) hsum[c2 * SH_HEAD_MAX + t] += acc;
+                    else if (c2 < nvalid && t < L) IO::store(os_, c2 * L + L - 1 - t, acc);
+                }
+            }
+        }
+        fft_passes<M, true>(x, ybuf, itau_r, bank, iact);
+        if (iact && icl < nvalid) {
+#pragma unroll
+            for (int q = 0; q < 8; ++q) {
+                const int t = 2 * (itau_r + TB * q);
+                if (t < head || t >= L) continue;
+                const float a = x[q].x * 0.5f, bb = x[q].y * 0.5f;
+                if (t + 1 < L) {
+                    if (pair_store) {
+                        IO::store2(os_, icl * L + L - 2 - t, bb, a);
+                    } else {
+                        IO::store(os_, icl * L + L - 1 - t, a);
+                        IO::store(os_, icl * L + L - 2 - t, bb);
+                    }
+                } else {
+                    IO::store(os_, icl * L + L - 1 - t, a);
+                }
+            }
+        }
+    }
+
+    // dk: the summed Y into branch 0's region, one inverse
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int k = lt + 2 * TB * i;
+        u0[lds_pad(k)] = yacc[i];
+        u0[lds_pad(k == 0 ? M / 2 : M - k)] = ymacc[i];
+    }
+    __syncthreads();
+    const Span ks = make_span(dk, (int64_t)c0 * L, (int64_t)nvalid * L);
+    float2 x[16];
+    if (iact) {
+#pragma unroll
+        for (int q = 0; q < 16; ++q) x[q] = ybuf[reg_off<TB>(itau, q)];
+    }
+    __syncthreads();
+    if (!iact) {
+        for (int o = tid - CT; o < nout; o += SH_THREADS - CT) {
+            const int c2 = o / head, t = o - c2 * head;
+            if (c2 < nvalid && t < L) IO::store(ks, c2 * L + L - 1 - t, hsum[c2 * SH_HEAD_MAX + t]);
+        }
+    }
+    fft_passes<M, true>(x, ybuf, itau, bank, iact);
+    if (iact && icl < nvalid) {
+        const float scale = 1.0f / (8.0f * (float)M);
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+            const int t = 2 * (itau + TB * q);
+            if (t < head || t >= L) continue;
+            const float a = x[q].x * scale, bb = x[q].y * scale;
+            if (t + 1 < L) {
+                if (pair_store) {
+                    IO::store2(ks, icl * L + L - 2 - t, bb, a);
+                } else {
+                    IO::store(ks, icl * L + L - 1 - t, a);
+                    IO::store(ks, icl * L + L - 2 - t, bb);
+                }
+            } else {
+                IO::store(ks, icl * L + L - 1 - t, a);
+            }
+        }
+    }
+}
+
 // ---------------------------------------------------------------- launch
 
 namespace {
@@ -466,6 +718,35 @@ hipError_t dk_io(const void* dr, const void* v, void* dk, int B, int C, int L, i
     case 1024: return dk_m<1024, IO>(dr, v, dk, B, C, L, head, pair, tw, s);
     case 2048: return dk_m<2048, IO>(dr, v, dk, B, C, L, head, pair, tw, s);
     case 4096: return dk_m<4096, IO>(dr, v, dk, B, C, L, head, pair, tw, s);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+template <int M, class IO>
+hipError_t bwd_m(const void* dr, const void* v, const float2* spec, void* dv, void* dk, int B,
+                 int C, int L, int head, bool pair, const float2* tw, hipStream_t s)
+{
+    constexpr int CPW = (SH_THREADS / (M / 16)) / 2;
+    const int64_t blocks = ((int64_t)C + CPW - 1) / CPW;
+    hipLaunchKernelGGL((shared_bwd_kernel<M, IO>), dim3((unsigned)blocks), dim3(SH_THREADS), 0,
+                       s, (const typename IO::T*)dr, (const typename IO::T*)v, spec,
+                       (typename IO::T*)dv, (typename IO::T*)dk, B, C, L, head, pair ? 1 : 0,
+                       tw);
+    return hipGetLastError();
+}
+
+template <class IO>
+hipError_t bwd_io(const void* dr, const void* v, const float2* spec, void* dv, void* dk, int B,
+                  int C, int L, int M, int head, bool pair, const float2* tw, hipStream_t s)
+{
+    switch (M) {
+    case 64: return bwd_m<64, IO>(dr, v, spec, dv, dk, B, C, L, head, pair, tw, s);
+    case 128: return bwd_m<128, IO>(dr, v, spec, dv, dk, B, C, L, head, pair, tw, s);
+    case 256: return bwd_m<256, IO>(dr, v, spec, dv, dk, B, C, L, head, pair, tw, s);
+    case 512: return bwd_m<512, IO>(dr, v, spec, dv, dk, B, C, L, head, pair, tw, s);
+    case 1024: return bwd_m<1024, IO>(dr, v, spec, dv, dk, B, C, L, head, pair, tw, s);
+    case 2048: return bwd_m<2048, IO>(dr, v, spec, dv, dk, B, C, L, head, pair, tw, s);
+    case 4096: return bwd_m<4096, IO>(dr, v, spec, dv, dk, B, C, L, head, pair, tw, s);
     default: return hipErrorInvalidValue;
     }
 }
@@ -526,6 +807,21 @@ hipError_t launch_shared_dk(Store st, const void* dr, const void* v, void* dk, i
 {
     return st == Store::F32 ? dk_io<f32_io>(dr, v, dk, B, C, L, M, head, pair_store, tw, s)
                             : dk_io<bf16_io>(dr, v, dk, B, C, L, M, head, pair_store, tw, s);
+}
+
+int64_t shared_bwd_blocks(int64_t C, int M)
+{
+    const int64_t cpw = (SH_THREADS / (M / 16)) / 2;
+    return (C + cpw - 1) / cpw;
+}
+
+hipError_t launch_shared_bwd(Store st, const void* dr, const void* v, const float2* spec, void* dv,
+                             void* dk, int B, int C, int L, int M, int head, bool pair_store,
+                             const float2* tw, hipStream_t s)
+{
+    return st == Store::F32
+               ? bwd_io<f32_io>(dr, v, spec, dv, dk, B, C, L, M, head, pair_store, tw, s)
+               : bwd_io<bf16_io>(dr, v, spec, dv, dk, B, C, L, M, head, pair_store, tw, s);
 }
 
 }  // namespace sc

@@ -160,3 +160,28 @@ def test_bwd_medium_shape_sampled(sc):
     dv, dk = sc.causal_conv_shared_bwd(to_device(dr), to_device(v), to_device(k))
     check_bwd(to_host(dv), to_host(dk), dr, v, k, "shared bwd medium",
               chans=np.array([0, 1, 511, w.C - 1]))
+
+
+# shapes with at least 512 channel groups take the one-kernel gradient path (dv and dk from
+# the same transform per row); smaller ones the apply + row-loop pair tested above
+@pytest.mark.parametrize("cid,B,C,L", [(2, 2, 512, 4096), (3, 3, 512, 3001), (2, 2, 1024, 2048),
+                                       (3, 2, 2048, 1000), (2, 1, 4096, 256)])
+def test_bwd_one_kernel_path(sc, cid, B, C, L):
+    dr, v, k = grad_inputs(cid, B, C, L, B + C + L)
+    print("case shared bwd one-kernel cid=%d B=%d C=%d L=%d" % (cid, B, C, L), flush=True)
+    dv, dk = sc.causal_conv_shared_bwd(to_device(dr), to_device(v), to_device(k))
+    chans = np.array([0, 1, C // 2 - 1, C // 2, C - 2, C - 1])
+    check_bwd(to_host(dv), to_host(dk), dr, v, k, "one-kernel cid=%d C=%d L=%d" % (cid, C, L),
+              chans=chans)
+
+
+def test_bwd_one_kernel_misaligned_dk(sc):
+    B, C, L = 2, 512, 4096
+    dr, v, k = grad_inputs(2, B, C, L, 5)
+    dk_buf = torch.zeros(C * L + 1, dtype=torch.float32, device="cuda:0")
+    dk_view = dk_buf[1:].view(C, L)
+    print("case shared bwd one-kernel misaligned dk", flush=True)
+    dv, dk = sc.causal_conv_shared_bwd(to_device(dr), to_device(v), to_device(k), dk=dk_view)
+    assert float(dk_buf[0]) == 0.0
+    check_bwd(to_host(dv), to_host(dk), dr, v, k, "one-kernel misaligned",
+              chans=np.array([0, 255, 511]))
