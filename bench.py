@@ -145,6 +145,44 @@ def record_traffic(w, fetch_dir: str, write_dir: str) -> dict:
     return rec
 
 
+def record_valu(w, sq_dir: str) -> dict:
+    """From a rocprofv3 counter run with SQ_INSTS_VALU (summed over the chip, per dispatch),
+    the VALU instructions one launch of the hot kernel issues."""
+    import csv
+    per = {}
+    for r in csv.DictReader(open(os.path.join(sq_dir, "run_counter_collection.csv"))):
+        if r["Counter_Name"] == "SQ_INSTS_VALU" and kernel_matches(r["Kernel_Name"], w.storage, w.L):
+            per[r["Dispatch_Id"]] = per.get(r["Dispatch_Id"], 0.0) + float(r["Counter_Value"])
+    if not per:
+        raise RuntimeError("%s: no SQ_INSTS_VALU rows for the hot kernel" % sq_dir)
+    rec = {"workload": w.name, "source_hash": kernel_source_hash(),
+           "valu_instructions_per_launch": round(float(np.mean(list(per.values())))),
+           "dispatches": len(per)}
+    path = os.path.join(ROOT, "profiles", "valu_%s.json" % w.name)
+    with open(path, "w") as f:
+        json.dump(rec, f, indent=1)
+        f.write("\n")
+    return rec
+
+
+def alu_issue(workload: str, kernel_ms: float):
+    """The VALU issue floor of the hot kernel: its VALU instructions per launch (committed
+    counter run on the current sources, else None) x 4 cycles per wave instruction over the
+    1024 SIMDs at the nominal 2.4 GHz, against the live kernel time."""
+    path = os.path.join(ROOT, "profiles", "valu_%s.json" % workload)
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("source_hash") != kernel_source_hash():
+        return None
+    floor_us = rec["valu_instructions_per_launch"] * 4 / 1024 / 2.4e9 * 1e6
+    return {"valu_instructions_per_launch": rec["valu_instructions_per_launch"],
+            "issue_floor_us_at_2.4GHz": round(floor_us, 1), "kernel_us": round(kernel_ms * 1e3, 1),
+            "frac": round(floor_us / (kernel_ms * 1e3), 4),
+            "source": "profiles/valu_%s.json (rocprofv3 SQ_INSTS_VALU)" % workload}
+
+
 FIXED_FRAC = 24   # fraction bits of both encodings in the exact real-valued measurements
 
 
@@ -600,11 +638,18 @@ def main(argv=None):
                     help="skip the timing of the exactly causal real-valued call")
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run a plain device copy of known size (profiler calibration)")
+    ap.add_argument("--record-valu", metavar="SQ_DIR",
+                    help="write profiles/valu_<workload>.json from a rocprofv3 --pmc run of "
+                         "this script that collected SQ_INSTS_VALU")
     ap.add_argument("--record-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="write profiles/traffic_<workload>.json from two rocprofv3 --pmc "
                          "runs (FETCH_SIZE, WRITE_SIZE) of this script with --calib-copy")
     args = ap.parse_args(argv)
 
+    if args.record_valu:
+        from workloads import WORKLOADS
+        print(json.dumps(record_valu(WORKLOADS[args.config], args.record_valu)))
+        return 0
     if args.record_traffic:
         from workloads import WORKLOADS
         print(json.dumps(record_traffic(WORKLOADS[args.config], *args.record_traffic)))
@@ -697,6 +742,7 @@ def main(argv=None):
         "config": {"workload": w.name, "B": w.B, "C": w.C, "L": w.L, "storage": w.storage,
                    "entry": fn_name, "buffer_sets": nsets},
         "roofline": roof,
+        "alu_issue": alu_issue(w.name, kernel_ms),
         "hbm": {"algorithmic_bytes_per_launch": alg_bytes, "achieved_GBps": round(hbm_gbps, 1),
                 "peak_GBps": HBM_PEAK_GBPS, "frac": round(hbm_gbps / HBM_PEAK_GBPS, 4)},
         "kernel_ms": {"mean": round(kernel_ms, 5), "rounds": [round(x, 5) for x in round_ms],
