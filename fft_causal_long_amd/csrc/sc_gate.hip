@@ -22,7 +22,10 @@
 //     32 x 32 output blocks over T/2 tokens;
 //  3. the blocks go through LDS to coalesced stores of g rows (channel-major, t contiguous).
 // s is read token-major ((B, L, C): one 64-channel row per token, 16-byte vector loads) or
-// channel-major ((B, C, L): t contiguous, element loads).
+// channel-major ((B, C, L): t contiguous). Channel-major bf16 rows whose length is a multiple
+// of 8 and that start 16-byte aligned are read with 16-byte vectors along t into a
+// channel-row LDS tile and turned into token rows by an LDS transpose (sigma applied on the
+// way); other channel-major shapes use element loads.
 
 #include <hip/hip_runtime.h>
 
@@ -68,7 +71,7 @@ __device__ __forceinline__ float sigmoid(float x)
 
 __device__ __forceinline__ uint16_t to_bf16(float x) { return (uint16_t)pack_bf16x2(x, 0.f); }
 
-template <class IO, bool TM>
+template <class IO, bool TM, bool VIN>
 __global__ __launch_bounds__(GT) void gate_kernel(const typename IO::T* __restrict__ s,
                                                   const typename IO::T* __restrict__ W,
                                                   typename IO::T* __restrict__ g, int C, int L,
@@ -85,12 +88,21 @@ __global__ __launch_bounds__(GT) void gate_kernel(const typename IO::T* __restri
     // read (32 output channels) spread over the LDS banks, and 16-byte aligned
     constexpr int WP = GC * 3 + (BF ? 8 : 4);
     constexpr int W_BYTES = GC * WP * (int)sizeof(E);
-    constexpr int SO_BYTES = S_BYTES > O_BYTES ? S_BYTES : O_BYTES;
+    // VIN: channel rows of the tile, N[ci][NP]: tokens t0 .. t0+T-1, then t0-2 and t0-1,
+    // padded so that each row starts 16-byte aligned; past both W and S (N is written with W
+    // and read while S is written)
+    static_assert(!VIN || (BF && !TM), "vector channel-major input is a bf16 path");
+    constexpr int NP = T + 8;
+    constexpr int NOFF = S_BYTES > W_BYTES ? S_BYTES : W_BYTES;
+    static_assert(!VIN || (NOFF % 16 == 0 && (NP * (int)sizeof(E)) % 16 == 0), "16-byte rows");
+    constexpr int SN_BYTES = VIN ? NOFF + GC * NP * (int)sizeof(E) : S_BYTES;
+    constexpr int SO_BYTES = SN_BYTES > O_BYTES ? SN_BYTES : O_BYTES;
     constexpr int LDS_BYTES = SO_BYTES > W_BYTES ? SO_BYTES : W_BYTES;
     __shared__ __attribute__((aligned(16))) unsigned char smem[LDS_BYTES];
     E* S = (E*)smem;                     // S[tt][ci], tt = t - t0 + 2
     E* O = (E*)smem;                     // O[co][tl], after the products
     E* Wl = (E*)smem;                    // Wl[co * WP + ci * 3 + k], before the sigma tile
+    E* N = (E*)(smem + NOFF);            // VIN only
 
     uint32_t id = blockIdx.x;
     const int tile = (int)(id % (uint32_t)ntiles);
@@ -113,10 +125,13 @@ __global__ __launch_bounds__(GT) void gate_kernel(const typename IO::T* __restri
     constexpr int VPR = GC / EPV;                     // vectors per token row (token-major)
     constexpr int NV = T * VPR / GT;                  // token-major vectors per thread
     constexpr int NE = T * GC / GT;                   // channel-major elements per thread
-    uint4 raw[TM ? NV : 1];
-    float val[TM ? 1 : NE];
+    constexpr int VPC = T / EPV;                      // vectors per channel row (VIN)
+    constexpr int NVC = GC * VPC / GT;                // VIN vectors per thread
+    uint4 raw[TM ? NV : (VIN ? NVC : 1)];
+    float val[(TM || VIN) ? 1 : NE];
     uint4 halo = make_uint4(0, 0, 0, 0);
     float hv = 0.f;
+    uint32_t hw = 0;
     const int hr = TM ? tid / VPR : (tid & 1);
     const int hc = TM ? tid % VPR : (tid >> 1);
     const int ht = t0 - 2 + hr;
@@ -130,6 +145,18 @@ __global__ __launch_bounds__(GT) void gate_kernel(const typename IO::T* __restri
             raw[q] = *(const uint4*)(sz + (int64_t)tc * C + p * EPV);
         }
         if (hact) halo = *(const uint4*)(sz + (int64_t)ht * C + hc * EPV);
+    } else if constexpr (VIN) {
+        // L is a multiple of 8 and rows are 16-byte aligned: a vector lies wholly inside or
+        // wholly past the row (then it is clamped to the last one and later zeroed); the halo
+        // tokens t0-2, t0-1 of channel tid are one aligned 4-byte word, present when t0 > 0
+        const E* sz = s + (z * C + c0) * (int64_t)L;
+#pragma unroll
+        for (int q = 0; q < NVC; ++q) {
+            const int vid = tid + GT * q, ci = vid / VPC, p = vid % VPC;
+            const int tv = t0 + p * EPV < L ? t0 + p * EPV : L - EPV;
+            raw[q] = *(const uint4*)(sz + (int64_t)ci * L + tv);
+        }
+        if (tid < GC && t0 > 0) hw = *(const uint32_t*)(sz + (int64_t)tid * L + t0 - 2);
     } else {
         const E* sz = s + (z * C + c0) * (int64_t)L;
 #pragma unroll
@@ -146,6 +173,14 @@ __global__ __launch_bounds__(GT) void gate_kernel(const typename IO::T* __restri
     for (int q = 0; q < WNV; ++q) {
         const int f = (tid + GT * q) * WEPV;
         *(uint4*)(Wl + (f / (GC * 3)) * WP + f % (GC * 3)) = wraw[q];
+    }
+    if constexpr (VIN) {
+#pragma unroll
+        for (int q = 0; q < NVC; ++q) {
+            const int vid = tid + GT * q, ci = vid / VPC, p = vid % VPC;
+            *(uint4*)(N + ci * NP + p * EPV) = raw[q];
+        }
+        if (tid < GC) *(uint32_t*)(N + tid * NP + T) = hw;
     }
     __syncthreads();
 
@@ -203,6 +238,30 @@ __global__ __launch_bounds__(GT) void gate_kernel(const typename IO::T* __restri
             put(r + 2, p * EPV, raw[q], t0 + r < L);
         }
         if (tid < 2 * VPR) put(hr, hc * EPV, halo, ht >= 0);
+    } else if constexpr (VIN) {
+        // transpose: 8 channels of one token column into one 16-byte token-row vector;
+        // consecutive lanes take consecutive tokens (conflict-free 2-byte reads)
+        auto row8 = [&](int col, int cg, bool valid) {
+            const E* nc = N + 8 * cg * NP + col;
+            uint32_t o[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const float lo = valid ? sigmoid(__uint_as_float((uint32_t)nc[2 * e * NP] << 16)) : 0.f;
+                const float hi = valid ? sigmoid(__uint_as_float((uint32_t)nc[(2 * e + 1) * NP] << 16)) : 0.f;
+                o[e] = pack_bf16x2(lo, hi);
+            }
+            return make_uint4(o[0], o[1], o[2], o[3]);
+        };
+        static_assert(T * (GC / 8) % GT == 0, "whole transpose rounds");
+#pragma unroll
+        for (int q = 0; q < T * (GC / 8) / GT; ++q) {
+            const int vid = tid + GT * q, j = vid % T, cg = vid / T;
+            *(uint4*)(S + (j + 2) * SP + 8 * cg) = row8(j, cg, t0 + j < L);
+        }
+        if (tid < 2 * (GC / 8)) {
+            const int r = tid / (GC / 8), cg = tid % (GC / 8);
+            *(uint4*)(S + r * SP + 8 * cg) = row8(T + r, cg, t0 > 0);
+        }
     } else {
 #pragma unroll
         for (int q = 0; q < NE; ++q) {
@@ -271,7 +330,7 @@ __global__ __launch_bounds__(GT) void gate_kernel(const typename IO::T* __restri
     }
 }
 
-template <class IO, bool TM>
+template <class IO, bool TM, bool VIN = false>
 hipError_t gate_launch(const void* s, const void* W, void* g, int64_t nb, int64_t C, int64_t cw,
                        int64_t L, int64_t gcs, bool vec_out, hipStream_t st)
 {
@@ -280,7 +339,7 @@ hipError_t gate_launch(const void* s, const void* W, void* g, int64_t nb, int64_
     const int64_t blocks = ntiles * ngroups * nb;
     if (blocks <= 0) return hipSuccess;
     if (blocks > 0x7fffffff) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((gate_kernel<IO, TM>), dim3((unsigned)blocks), dim3(GT), 0, st,
+    hipLaunchKernelGGL((gate_kernel<IO, TM, VIN>), dim3((unsigned)blocks), dim3(GT), 0, st,
                        (const typename IO::T*)s, (const typename IO::T*)W, (typename IO::T*)g,
                        (int)C, (int)L, (int)gcs, (int)ngroups, (int)ntiles, vec_out ? 1 : 0);
     return hipGetLastError();
@@ -296,8 +355,11 @@ hipError_t launch_gate(Store st, bool token_major, const void* s, const void* W,
     if (st == Store::F32)
         return token_major ? gate_launch<f32_io, true>(s, W, g, nb, C, cw, L, gcs, vec_out, s_)
                            : gate_launch<f32_io, false>(s, W, g, nb, C, cw, L, gcs, vec_out, s_);
-    return token_major ? gate_launch<bf16_io, true>(s, W, g, nb, C, cw, L, gcs, vec_out, s_)
-                       : gate_launch<bf16_io, false>(s, W, g, nb, C, cw, L, gcs, vec_out, s_);
+    if (token_major) return gate_launch<bf16_io, true>(s, W, g, nb, C, cw, L, gcs, vec_out, s_);
+    // channel-major bf16 rows: 16-byte input vectors when every row starts aligned
+    const bool vec_in = L % 8 == 0 && (uintptr_t)s % 16 == 0;
+    return vec_in ? gate_launch<bf16_io, false, true>(s, W, g, nb, C, cw, L, gcs, vec_out, s_)
+                  : gate_launch<bf16_io, false>(s, W, g, nb, C, cw, L, gcs, vec_out, s_);
 }
 
 }  // namespace sc

@@ -140,3 +140,24 @@ def test_adjacent_buffers_are_not_overlapping(sc):
     print("case gate adjacent buffers", flush=True)
     sc.gate(to_device(s), Wd, out=g)
     check_gate(to_host(g), s, W, "gate adjacent")
+
+
+@pytest.mark.parametrize("L", [256, 1000, 4096])
+def test_channel_major_vector_and_element_inputs_agree(sc, L):
+    # bf16 rows of a multiple of 8 tokens starting 16-byte aligned go through 16-byte loads
+    # and an LDS transpose; s one element off its alignment takes the element loads: both
+    # feed the same sigma values to the same products, so g is bit for bit the same
+    v, s, W = make_gate_inputs(WORKLOADS[3], B=2, C=128, L=L, seed_offset=L + 3)
+    n = s.size
+    Wd = to_device(W)
+    buf = torch.empty(n + 8, dtype=torch.bfloat16, device="cuda:0")
+    s_al = buf[8:8 + n].view(s.shape)
+    s_al.copy_(to_device(s))
+    s_un = torch.empty(n + 1, dtype=torch.bfloat16, device="cuda:0")[1:].view(s.shape)
+    s_un.copy_(to_device(s))
+    assert s_al.data_ptr() % 16 == 0 and s_un.data_ptr() % 16 != 0
+    print("case gate channel-major aligned/unaligned L=%d" % L, flush=True)
+    g_al = to_host(sc.gate(s_al, Wd))
+    g_un = to_host(sc.gate(s_un, Wd))
+    assert np.array_equal(g_al.view(np.uint16), g_un.view(np.uint16))
+    check_gate(g_al, s, W, "gate aligned L=%d" % L)
