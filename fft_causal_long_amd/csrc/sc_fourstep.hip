@@ -21,7 +21,9 @@
 //  A small kernel recomputes the first `head` outputs by direct fp32 summation.
 //
 // HBM traffic per channel: read v, g; write and read T (2M complex) and S (M complex);
-// write r.  Channels are processed in chunks so T and S can stay in the last-level cache.
+// write r.  Channels are processed in chunks so T and S can stay in the last-level cache;
+// the chunks can alternate between two streams, so that the memory-bound column kernels of
+// one overlap the row kernel of the other.
 // Every twiddle comes from a per-M table (see FsTw in sc_internal.h) laid out so that the
 // lanes of a wave read consecutive entries.
 
@@ -352,32 +354,49 @@ size_t fourstep_bytes_per_channel(int M)
 template <bool REV>
 static hipError_t launch_fourstep_rev(Store st, const void* v, const void* g, void* r, int64_t nch,
                                       int L, int M, int head, bool pair_store, const float2* bank,
-                                      const FsTw& tw, void* ws, int64_t chunk, hipStream_t stream)
+                                      const FsTw& tw, void* ws, int64_t chunk, hipStream_t stream,
+                                      hipStream_t side, hipEvent_t fork, hipEvent_t join)
 {
     int M1, M2;
     fourstep_split(M, &M1, &M2);
-    float2* T = (float2*)ws;
-    float2* S = T + (size_t)chunk * 2 * M;
-    for (int64_t c0 = 0; c0 < nch; c0 += chunk) {
-        const int nc = (int)((nch - c0) < chunk ? (nch - c0) : chunk);
-        hipError_t e;
-        if (st == Store::F32)
-            e = dispatch_cols<f32_io, REV>(true, M1, v, g, r, T, S, c0, nc, L, M2, head, pair_store,
-                                           bank, tw, stream);
-        else
-            e = dispatch_cols<bf16_io, REV>(true, M1, v, g, r, T, S, c0, nc, L, M2, head,
-                                            pair_store, bank, tw, stream);
-        if (e != hipSuccess) return e;
-        e = dispatch_rows(M2, T, S, nc, M1, bank, tw, stream);
-        if (e != hipSuccess) return e;
-        if (st == Store::F32)
-            e = dispatch_cols<f32_io, REV>(false, M1, v, g, r, T, S, c0, nc, L, M2, head,
-                                           pair_store, bank, tw, stream);
-        else
-            e = dispatch_cols<bf16_io, REV>(false, M1, v, g, r, T, S, c0, nc, L, M2, head,
-                                            pair_store, bank, tw, stream);
+    const int64_t part = side ? (chunk / 2 > 0 ? chunk / 2 : 1) : chunk;
+    hipError_t e = hipSuccess;
+    if (side) {
+        e = hipEventRecord(fork, stream);
+        if (e == hipSuccess) e = hipStreamWaitEvent(side, fork, 0);
         if (e != hipSuccess) return e;
     }
+    // part i on stream (i even) or side (i odd), with its own scratch: T (2 branches x M
+    // complex per channel), then S (2 branches x M/2)
+    int64_t i = 0;
+    for (int64_t c0 = 0; c0 < nch && e == hipSuccess; c0 += part, ++i) {
+        const int nc = (int)((nch - c0) < part ? (nch - c0) : part);
+        const hipStream_t s = (i & 1) ? side : stream;
+        float2* T = (float2*)ws + (size_t)(i & 1) * (size_t)part * 3 * M;
+        float2* S = T + (size_t)part * 2 * M;
+        if (st == Store::F32)
+            e = dispatch_cols<f32_io, REV>(true, M1, v, g, r, T, S, c0, nc, L, M2, head, pair_store,
+                                           bank, tw, s);
+        else
+            e = dispatch_cols<bf16_io, REV>(true, M1, v, g, r, T, S, c0, nc, L, M2, head,
+                                            pair_store, bank, tw, s);
+        if (e != hipSuccess) break;
+        e = dispatch_rows(M2, T, S, nc, M1, bank, tw, s);
+        if (e != hipSuccess) break;
+        if (st == Store::F32)
+            e = dispatch_cols<f32_io, REV>(false, M1, v, g, r, T, S, c0, nc, L, M2, head,
+                                           pair_store, bank, tw, s);
+        else
+            e = dispatch_cols<bf16_io, REV>(false, M1, v, g, r, T, S, c0, nc, L, M2, head,
+                                            pair_store, bank, tw, s);
+    }
+    if (side) {
+        // join even after a failed launch, so that nothing of this call is left unordered
+        hipError_t ej = hipEventRecord(join, side);
+        if (ej == hipSuccess) ej = hipStreamWaitEvent(stream, join, 0);
+        if (e == hipSuccess) e = ej;
+    }
+    if (e != hipSuccess) return e;
     if (head > 0) {
         const int64_t total = nch * (int64_t)head;
         const int threads = 256;
@@ -396,12 +415,13 @@ static hipError_t launch_fourstep_rev(Store st, const void* v, const void* g, vo
 
 hipError_t launch_fourstep(Store st, const void* v, const void* g, void* r, int64_t nch, int L,
                            int M, int head, bool pair_store, bool rev, const float2* bank,
-                           const FsTw& tw, void* ws, int64_t chunk, hipStream_t stream)
+                           const FsTw& tw, void* ws, int64_t chunk, hipStream_t stream,
+                           hipStream_t side, hipEvent_t fork, hipEvent_t join)
 {
     return rev ? launch_fourstep_rev<true>(st, v, g, r, nch, L, M, head, pair_store, bank, tw, ws,
-                                           chunk, stream)
+                                           chunk, stream, side, fork, join)
                : launch_fourstep_rev<false>(st, v, g, r, nch, L, M, head, pair_store, bank, tw, ws,
-                                            chunk, stream);
+                                            chunk, stream, side, fork, join);
 }
 
 }  // namespace sc

@@ -19,7 +19,8 @@ constexpr int kMaxHead = 64;
 constexpr int64_t kMaxLFused = 4096;     // fused path; longer sequences use the four-step path
 constexpr int64_t kMinLFourStep = 2049;  // the four-step split needs M >= 4096
 // channels per four-step chunk: as many as fit this much scratch (enough channels to
-// fill the GPU in every kernel of the chunk; measured best among 24..384 MB)
+// fill the GPU in every kernel of a half chunk; measured best among 128..256 MB with the
+// halves on two streams, and among 24..384 MB on one)
 #ifndef SC_FS_CHUNK_MB
 #define SC_FS_CHUNK_MB 192
 #endif
@@ -48,6 +49,12 @@ struct DeviceState {
     sc::NttTables ntt[3]{};       // primes A, B, C (sc::NTT_PRIMES)
     bool ntt_ready = false;
     std::map<int, sc::FsTw> fs;     // four-step tables by M
+    // the four-step path's second stream (default priority, non-blocking) and its fork/join
+    // events; fs_mu keeps one call's fork, launches and join together, since the events are
+    // shared by every call on the device
+    hipStream_t fs_side = nullptr;
+    hipEvent_t fs_fork = nullptr, fs_join = nullptr;
+    std::mutex fs_mu;
 };
 
 uint64_t powmod(uint64_t b, uint64_t e, uint64_t m)
@@ -270,6 +277,26 @@ sc_status resolve_path(sc_kind kind, int64_t L, int32_t requested, sc_path* out)
 // scratch of the exact real-valued kind: three int32 residues per output
 size_t fixed_bytes(int64_t n) { return (size_t)n * 3 * sizeof(int32_t); }
 
+// the four-step path's second stream and events of the current device, made on first use
+sc_status fourstep_streams(DeviceState& d)
+{
+    std::lock_guard<std::mutex> lk(g_mu);
+    if (d.fs_side) return SC_OK;
+    hipStream_t s = nullptr;
+    hipEvent_t f = nullptr, j = nullptr;
+    if (hipStreamCreateWithFlags(&s, hipStreamNonBlocking) != hipSuccess) return SC_ERR_HIP;
+    if (hipEventCreateWithFlags(&f, hipEventDisableTiming) != hipSuccess ||
+        hipEventCreateWithFlags(&j, hipEventDisableTiming) != hipSuccess) {
+        if (f) (void)hipEventDestroy(f);
+        (void)hipStreamDestroy(s);
+        return SC_ERR_HIP;
+    }
+    d.fs_fork = f;
+    d.fs_join = j;
+    d.fs_side = s;
+    return SC_OK;
+}
+
 // four-step scratch: channels per chunk and bytes needed
 void fourstep_plan(int64_t nch, int64_t L, int64_t* chunk, size_t* bytes)
 {
@@ -382,6 +409,15 @@ sc_status run_jobs(sc_kind kind, const Job* jobs, int njobs, bool rev, int64_t n
             st = fourstep_tables(*d, M, &tw);
         }
         if (st != SC_OK) return st;
+        // two streams take alternate halves of the chunks (measured 1.54 -> 1.34 ms on the
+        // long workload: one part's memory-bound column kernels overlap the other's rows),
+        // unless there is a single part or the caller's stream is being captured into a graph
+        hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+        if (hipStreamIsCapturing(stream, &cap) != hipSuccess) return SC_ERR_HIP;
+        const bool two = cap == hipStreamCaptureStatusNone && chunk >= 2 && nch > chunk / 2;
+        if (two && (st = fourstep_streams(*d)) != SC_OK) return st;
+        std::unique_lock<std::mutex> order(d->fs_mu, std::defer_lock);
+        if (two) order.lock();
         void* scratch = ws;
         bool own = false;
         if (!ws) {
@@ -390,7 +426,8 @@ sc_status run_jobs(sc_kind kind, const Job* jobs, int njobs, bool rev, int64_t n
         }
         for (int k = 0; k < njobs && e == hipSuccess; ++k)
             e = sc::launch_fourstep(s, jobs[k].a, jobs[k].b, jobs[k].o, nch, (int)L, M, head, pair,
-                                    rev, d->fused_tw, tw, scratch, chunk, stream);
+                                    rev, d->fused_tw, tw, scratch, chunk, stream,
+                                    two ? d->fs_side : nullptr, d->fs_fork, d->fs_join);
         if (own && hipFreeAsync(scratch, stream) != hipSuccess && e == hipSuccess)
             e = hipErrorUnknown;
     }

@@ -79,10 +79,15 @@ struct FsTw {
 
 void fourstep_split(int M, int* M1, int* M2);
 size_t fourstep_bytes_per_channel(int M);
-// ws holds chunk channels of scratch (chunk * fourstep_bytes_per_channel(M) bytes).
+// ws holds chunk channels of scratch (chunk * fourstep_bytes_per_channel(M) bytes).  With a
+// second stream `side` (and two events, fork and join), the channels go in parts of chunk/2
+// that alternate between the two streams, each part with its own half of ws: side waits
+// for stream at the start (fork) and stream for side at the end (join), so the call stays
+// ordered on `stream` as a whole.
 hipError_t launch_fourstep(Store st, const void* v, const void* g, void* r, int64_t nch, int L,
                            int M, int head, bool pair_store, bool rev, const float2* bank,
-                           const FsTw& tw, void* ws, int64_t chunk, hipStream_t stream);
+                           const FsTw& tw, void* ws, int64_t chunk, hipStream_t stream,
+                           hipStream_t side, hipEvent_t fork, hipEvent_t join);
 
 // ---- filter shared by the batch (L <= FUSED_MAX_L, M = max(64, next power of two >= L))
 // Spectrum of the filters k[C][L]: shared_spec_stride(M) float2 per channel.

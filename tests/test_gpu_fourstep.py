@@ -68,8 +68,36 @@ def test_four_step_several_chunks(sc):
     C = chunk + 37
     assert sc.sc_workspace_bytes(sc.KIND_F32, 1, C, L) < per * C
     v, g = make_inputs(WORKLOADS[4], B=1, C=C, L=L, seed_offset=13)
-    chans = np.array([0, 1, chunk - 1, chunk, chunk + 1, C - 1])
+    h = chunk // 2
+    chans = np.array([0, 1, h - 1, h, h + 1, chunk - 1, chunk, chunk + 1, C - 1])
     check(sc, v, g, "four-step %d channels (chunk %d)" % (C, chunk), chans=chans)
+
+
+def test_four_step_two_streams_same_bits(sc):
+    # a call with more channels than half a chunk alternates its parts between the caller's
+    # stream and a second one; calls of at most half a chunk stay on one stream: the same
+    # kernels per channel, so the same bits
+    L = 16384
+    per = sc.sc_workspace_bytes(sc.KIND_F32, 1, 1, L)
+    chunk = sc.sc_workspace_bytes(sc.KIND_F32, 1, 10**6, L) // per
+    h = chunk // 2
+    C = chunk + 37
+    v, g = make_inputs(WORKLOADS[4], B=1, C=C, L=L, seed_offset=16)
+    print("case four-step two streams C=%d half chunk %d" % (C, h), flush=True)
+    tv, tg = to_device(v), to_device(g)
+    whole = sc.causal_conv(tv, tg)
+    parts = [sc.causal_conv(tv[:, c0:c0 + h].contiguous(), tg[:, c0:c0 + h].contiguous())
+             for c0 in range(0, C, h)]
+    torch.cuda.synchronize()
+    assert torch.equal(whole.view(torch.int32), torch.cat(parts, dim=1).view(torch.int32))
+    # and the gradient calls, which share the launcher
+    dr = to_device(make_inputs(WORKLOADS[4], B=1, C=C, L=L, seed_offset=17)[0])
+    dv, dg = sc.causal_conv_bwd(dr, tv, tg)
+    for c0 in range(0, C, h):
+        pv, pg = sc.causal_conv_bwd(dr[:, c0:c0 + h].contiguous(), tv[:, c0:c0 + h].contiguous(),
+                                    tg[:, c0:c0 + h].contiguous())
+        assert torch.equal(dv[:, c0:c0 + h].view(torch.int32), pv.view(torch.int32))
+        assert torch.equal(dg[:, c0:c0 + h].view(torch.int32), pg.view(torch.int32))
 
 
 def test_config4_full_size_sampled(sc):
