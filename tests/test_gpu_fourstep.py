@@ -131,3 +131,43 @@ def test_four_step_deterministic(sc):
     a = run(sc, v, g)
     b = run(sc, v, g)
     assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+
+
+def test_four_step_concurrent_callers(sc):
+    # two host threads, each on a stream of its own, call the two-stream path at the same
+    # time: they share the device's second stream and its events, and each call must still
+    # see only its own inputs and finish before its caller's stream goes on
+    import threading
+    L = 16384
+    per = sc.sc_workspace_bytes(sc.KIND_F32, 1, 1, L)
+    chunk = sc.sc_workspace_bytes(sc.KIND_F32, 1, 10**6, L) // per
+    C = chunk // 2 + 40
+    dev = []
+    for k in range(2):
+        v, g = make_inputs(WORKLOADS[4], B=1, C=C, L=L, seed_offset=20 + k)
+        dev.append((to_device(v), to_device(g)))
+    ref = [sc.causal_conv(a, b) for a, b in dev]
+    torch.cuda.synchronize()
+    print("case four-step concurrent callers C=%d" % C, flush=True)
+    outs = [[None] * 3 for _ in range(2)]
+    errs = []
+
+    def work(k):
+        try:
+            s = torch.cuda.Stream()
+            with torch.cuda.stream(s):
+                for i in range(3):
+                    outs[k][i] = sc.causal_conv(*dev[k])
+            s.synchronize()
+        except Exception as e:  # reported on the main thread
+            errs.append(e)
+
+    threads = [threading.Thread(target=work, args=(k,)) for k in range(2)]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join()
+    assert not errs, errs
+    for k in range(2):
+        for i in range(3):
+            assert torch.equal(outs[k][i].view(torch.int32), ref[k].view(torch.int32)), (k, i)
