@@ -407,26 +407,59 @@ constexpr W INV_A_MOD_B = wconst<PrimeB>(powmod_c<PrimeB>(PA % PB, PB - 2));
 constexpr W A_MOD_C = wconst<PrimeC>(PA % PC);
 constexpr W INV_AB_MOD_C = wconst<PrimeC>(powmod_c<PrimeC>((PA % PC) * (PB % PC) % PC, PC - 2));
 
-// The float32 nearest to m 2^-F (m > 0, m < 2^127), ties to even, subnormals included.
-__device__ __forceinline__ float rne_scaled(unsigned __int128 m, int F)
+// A B as the sum of two doubles: the nearest double and the (small, exact) rest
+constexpr uint64_t AB = PA * PB;
+constexpr double AB_HI = (double)AB;
+constexpr double AB_LO = (double)((int64_t)AB - (int64_t)(uint64_t)AB_HI);
+
+// error-free transformations: s + e == a + b (Knuth's two-sum) and p + e == a b (with an FMA).
+// No contraction here: a product fused into a later sum would no longer be the p whose
+// error e describes, and the sums would lose their exactness.
+__device__ __forceinline__ void two_sum(double a, double b, double& s, double& e)
 {
-    const uint64_t hi = (uint64_t)(m >> 64), lo = (uint64_t)m;
-    const int b = hi ? 128 - __builtin_clzll(hi) : 64 - __builtin_clzll(lo);   // bit length
-    const int e = b - 1 - F;                       // m 2^-F lies in [2^e, 2^(e+1))
-    const int qexp = e - 23 > -149 ? e - 23 : -149; // spacing of float32 numbers there
-    const int sh = F + qexp;                       // keep m / 2^sh, rounded to an integer
-    uint64_t mant;
-    if (sh <= 0) {
-        mant = lo << (-sh);                        // here m < 2^24 and -sh <= 23: exact
-    } else if (sh >= 127) {
-        mant = 0;                                  // m < 2^(sh-1): below half a unit
+#pragma clang fp contract(off)
+    s = a + b;
+    const double bb = s - a;
+    e = (a - (s - bb)) + (b - bb);
+}
+__device__ __forceinline__ void two_prod(double a, double b, double& p, double& e)
+{
+#pragma clang fp contract(off)
+    p = a * b;
+    e = __builtin_fma(a, b, -p);
+}
+
+// The float32 nearest to R 2^-F (ties to even, subnormals included) for the integer
+// R = a0 + a1 A + a2 A B with balanced digits (|R| < 2^89).  R is first written exactly as
+// hi + lo + e3 (doubles, |lo + e3| below the gap between hi and its neighbour on that
+// side), then rounded to 53 bits by rounding to odd (hi, or its neighbour towards the rest
+// when hi's last bit is even and the rest is not zero); from 53 bits a single rounding to
+// float32's 24 (or fewer, subnormal) bits is the correct rounding of R itself (rounding to
+// odd with at least two spare bits; Boldo and Melquiond, "When double rounding is odd").
+// The scaling by 2^-F is exact in float64, since 1 <= |R| and F <= 128.
+__device__ __forceinline__ float crt_to_f32(double a0, double a1, double a2, int F)
+{
+#pragma clang fp contract(off)
+    double p1, e1, q1, e2;
+    two_prod(a2, AB_HI, p1, e1);                 // |p1| < 2^88, |e1| <= 2^34
+    two_prod(a1, (double)PA, q1, e2);            // |q1| < 2^59, |e2| <= 2^6
+    // integers below 2^36 in magnitude: every sum is exact
+    const double s = ((e1 + a2 * AB_LO) + e2) + a0;
+    double h, l, H, e, lo, e3, hi, lo2;
+    two_sum(q1, s, h, l);
+    two_sum(p1, h, H, e);
+    two_sum(e, l, lo, e3);
+    two_sum(H, lo, hi, lo2);                     // R = hi + lo2 + e3, hi = R rounded
+    double d = hi;
+    if (hi == 0.0) {
+        d = e3;                                  // then R = e3 exactly
     } else {
-        mant = (uint64_t)(m >> sh);
-        const unsigned __int128 rem = m - ((unsigned __int128)mant << sh);
-        const unsigned __int128 half = (unsigned __int128)1 << (sh - 1);
-        if (rem > half || (rem == half && (mant & 1))) ++mant;
+        const double rest = lo2 != 0.0 ? lo2 : e3;
+        const long long b = __double_as_longlong(hi);
+        if (rest != 0.0 && (b & 1) == 0)
+            d = __longlong_as_double(b + (((rest > 0.0) == (hi > 0.0)) ? 1 : -1));
     }
-    return ldexpf((float)mant, qexp);              // mant <= 2^24: exact (or inf past the range)
+    return (float)ldexp(d, -F);
 }
 
 }  // namespace ntt
@@ -445,15 +478,7 @@ __global__ void crt_decode_kernel(const int32_t* __restrict__ sa, const int32_t*
         const double t2 = (double)sc[i] - a0 - mulc<PrimeC>(a1, A_MOD_C);
         const double a2 = balance<PrimeC>(mulc<PrimeC>(t2, INV_AB_MOD_C));
         // R = a0 + a1 A + a2 A B, every digit balanced, so |R| <= (A B C - 1) / 2
-        const __int128 R = (__int128)(int64_t)a2 * (__int128)(PA * PB) +
-                           (__int128)((int64_t)a1 * (int64_t)PA + (int64_t)a0);
-        float out = 0.f;
-        if (R != 0) {
-            const bool neg = R < 0;
-            out = rne_scaled(neg ? (unsigned __int128)(-R) : (unsigned __int128)R, F);
-            if (neg) out = -out;
-        }
-        r[i] = out;
+        r[i] = crt_to_f32(a0, a1, a2, F);
     }
 }
 

@@ -88,6 +88,27 @@ def test_subnormal_and_tiny_results(sc):
     check(sc, v * np.float32(2.0 ** -64), g * np.float32(2.0 ** -64), 64, 64, "tiny")
 
 
+@pytest.mark.parametrize("fv,fg", [(0, 0), (10, 6)])
+def test_exact_ties_round_to_even(sc, fv, fg):
+    # r_1 = R_0 + x with R_0 = 2^24 or 2^25: float32 spacing 2 or 4 there, so odd x (resp.
+    # x = 2 mod 4) lands exactly halfway between two floats and must go to the even one
+    base = [2.0 ** 24, 2.0 ** 24, 2.0 ** 24, 2.0 ** 24, 2.0 ** 25, 2.0 ** 25, -2.0 ** 24, -2.0 ** 24]
+    xs = [1.0, 3.0, 5.0, -1.0, 2.0, 6.0, -1.0, -3.0]
+    want = [2.0 ** 24, 2.0 ** 24 + 4, 2.0 ** 24 + 4, 2.0 ** 24 - 1, 2.0 ** 25, 2.0 ** 25 + 8,
+            -2.0 ** 24, -(2.0 ** 24 + 4)]
+    n = len(base)
+    v = np.zeros((1, n, 2), np.float32)
+    g = np.zeros((1, n, 2), np.float32)
+    v[0, :, 0] = np.array(base) * 2.0 ** -fv
+    v[0, :, 1] = np.array(xs) * 2.0 ** -fv
+    g[0, :, :] = 2.0 ** -fg                       # G = (1, 1): R_1 = base + x
+    check(sc, v, g, fv, fg, "ties fv=%d fg=%d" % (fv, fg))
+    r = run(sc, v, g, fv, fg)
+    sc_ = 2.0 ** -(fv + fg)
+    assert r[0, :, 0].tolist() == [b_ * sc_ for b_ in base]
+    assert r[0, :, 1].tolist() == [w_ * sc_ for w_ in want]
+
+
 def test_ragged_channels_and_workspace(sc):
     v, g = make_inputs(WORKLOADS[2], B=3, C=5, L=500, seed_offset=9)
     check(sc, v, g, 20, 22, "ragged channels")
