@@ -21,11 +21,15 @@
 // error scale sum_j |v_j||g_{t-j}| holds only t+1 products, far below the global round-off
 // of any float FFT.
 //
-// Workgroup = 512 threads.  A length-M transform is held by TB = M/16 threads with 16
-// values each (element tau + TB*r sits in register r of thread tau, at the input and the
-// output of every transform); between radix passes the values go through LDS.  A
-// workgroup serves CPW = 4096/M channels (two branch units per channel) and uses
-// 2*CPW*(M + M/16) complex values = 68 KB of LDS for every M, so two workgroups fit a CU.
+// A length-M transform is held by TB = M/16 threads with 16 values each (element
+// tau + TB*r sits in register r of thread tau, at the input and the output of every
+// transform); between radix passes the values go through LDS.  A workgroup of
+// max(64, M/8) threads serves CPW channels (two branch units of TB threads per channel):
+// one channel from M = 512 on, as many as fill one wave below.  It uses
+// 2*CPW*(M + M/16) complex values of LDS (68 KB at M = 4096, two workgroups per CU).
+// Small workgroups let workgroups at different phases share a CU: at M = 1024 one channel
+// per workgroup took 44 -> 39 us against four channels per 512-thread workgroup, at M = 256
+// (64 channels) 11 -> 7 us, bit for bit the same.
 // HBM traffic is read v, read g, write r: nothing else leaves the chip.
 
 #include "sc_device.h"
@@ -34,7 +38,9 @@
 
 namespace sc {
 
-constexpr int FUSED_THREADS = 512;
+// threads of the workgroup for length-M transforms
+template <int M>
+constexpr int fused_threads() { return M / 8 > 64 ? M / 8 : 64; }
 constexpr int HEAD_MAX = 64;   // largest direct head (the host clamps to this)
 #ifndef SC_LDS_EXTRA
 #define SC_LDS_EXTRA 24
@@ -70,13 +76,15 @@ __device__ __forceinline__ void direct_head(const float* __restrict__ hb, int nc
 }
 
 template <int M, class IO, bool REV>
-__global__ __launch_bounds__(FUSED_THREADS) void fused_conv_kernel(
+__global__ __launch_bounds__(fused_threads<M>()) void fused_conv_kernel(
     const typename IO::T* __restrict__ v, const typename IO::T* __restrict__ g,
     typename IO::T* __restrict__ r, int64_t nch, int L, int head, int pair_store,
     const float2* __restrict__ tw)
 {
     static_assert(M >= 64 && M <= 4096, "fused path handles 64 <= M <= 4096");
-    constexpr int N = 2 * M, TB = M / 16, UNITS = FUSED_THREADS / TB, CPW = UNITS / 2;
+    constexpr int FT = fused_threads<M>();
+    constexpr int N = 2 * M, TB = M / 16, UNITS = FT / TB, CPW = UNITS / 2;
+    static_assert(CPW >= 1 && FT % 64 == 0, "whole waves, two branch units per channel");
     constexpr int REG = M + M / 16 + (M >= 256 ? LDS_EXTRA : 0);
     __shared__ float2 lds[UNITS * REG];
     // first HEAD_MAX inputs of each local channel (v then g) for the direct head
@@ -203,7 +211,7 @@ __global__ __launch_bounds__(FUSED_THREADS) void fused_conv_kernel(
             }
         }
         // 6. the direct head, by all threads: r_t = sum_{j<=t} v_j g_{t-j}, fp32, t < head
-        direct_head<FUSED_THREADS>(hbuf, CPW, nvalid, L, head, tid, put);
+        direct_head<FT>(hbuf, CPW, nvalid, L, head, tid, put);
     } else {
         // 4. y = IDFT_M(Y): threads [c*TB, (c+1)*TB) serve local channel c.  The other half of
         //    the workgroup computes the direct head meanwhile, from the inputs staged at load
@@ -219,7 +227,7 @@ __global__ __launch_bounds__(FUSED_THREADS) void fused_conv_kernel(
         // between this barrier and the first one of the inverse, where the active threads run
         // their first radix-16 pass
         if (!iact)
-            direct_head<FUSED_THREADS - CPW * TB>(hbuf, CPW, nvalid, L, head, tid - CPW * TB, put);
+            direct_head<FT - CPW * TB>(hbuf, CPW, nvalid, L, head, tid - CPW * TB, put);
         fft_passes<M, true>(x, ybuf, itau, bank, iact);
 
         // 5. store: x[q] = 8 M y_m with m = itau + TB q; r_{2m} = Re y_m, r_{2m+1} = Im y_m
@@ -276,9 +284,9 @@ template <int M, class IO, bool REV>
 static hipError_t launch_fused_m(const void* v, const void* g, void* r, int64_t nch, int L,
                                  int head, bool pair, const float2* tw, hipStream_t stream)
 {
-    constexpr int CPW = (FUSED_THREADS / (M / 16)) / 2;
+    constexpr int CPW = (fused_threads<M>() / (M / 16)) / 2;
     const int64_t blocks = (nch + CPW - 1) / CPW;
-    hipLaunchKernelGGL((fused_conv_kernel<M, IO, REV>), dim3((unsigned)blocks), dim3(FUSED_THREADS), 0,
+    hipLaunchKernelGGL((fused_conv_kernel<M, IO, REV>), dim3((unsigned)blocks), dim3(fused_threads<M>()), 0,
                        stream, (const typename IO::T*)v, (const typename IO::T*)g,
                        (typename IO::T*)r, nch, L, head, pair ? 1 : 0, tw);
     return hipGetLastError();
