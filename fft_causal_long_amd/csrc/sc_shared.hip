@@ -31,6 +31,11 @@ namespace sc {
 namespace {
 
 constexpr int SH_THREADS = 512;
+// threads of the spectrum and apply workgroups for length-M transforms: one unit pair (a
+// filter pair, or a job) per workgroup from M = 512 on, as many as fill one wave below
+// (as the per-row-gate kernel: small workgroups share a CU at different phases)
+template <int M>
+constexpr int sh_threads() { return M / 8 > 64 ? M / 8 : 64; }
 constexpr int SH_HEAD_MAX = 64;
 constexpr int SH_LDS_EXTRA = 24;
 
@@ -50,11 +55,11 @@ int64_t shared_spec_stride(int M)
 // ---------------------------------------------------------------- filter spectrum
 
 template <int M, class IO>
-__global__ __launch_bounds__(SH_THREADS) void shared_spectrum_kernel(
+__global__ __launch_bounds__(sh_threads<M>()) void shared_spectrum_kernel(
     const typename IO::T* __restrict__ k, float2* __restrict__ spec, int C, int L,
     const float2* __restrict__ tw)
 {
-    constexpr int N = 2 * M, TB = M / 16, UNITS = SH_THREADS / TB, PPW = UNITS / 2;
+    constexpr int N = 2 * M, TB = M / 16, UNITS = sh_threads<M>() / TB, PPW = UNITS / 2;
     constexpr int REG = M + M / 16 + (M >= 256 ? SH_LDS_EXTRA : 0);
     constexpr int SS = spec_stride<M>();
     __shared__ float2 lds[UNITS * REG];
@@ -115,12 +120,12 @@ __global__ __launch_bounds__(SH_THREADS) void shared_spectrum_kernel(
 // REV (the gradient dv): v is read reversed and r written reversed, so with v = dr the
 // kernel gives dv[b][c][j] = sum_{t>=j} dr[b][c][t] k[c][t-j].
 template <int M, class IO, bool REV>
-__global__ __launch_bounds__(SH_THREADS, (M >= 512 ? 4 : 1)) void shared_apply_kernel(
+__global__ __launch_bounds__(sh_threads<M>(), (M >= 512 ? 4 : 1)) void shared_apply_kernel(
     const typename IO::T* __restrict__ v, const float2* __restrict__ spec,
     typename IO::T* __restrict__ r, int B, int C, int L, int head,
     const float2* __restrict__ tw)
 {
-    constexpr int N = 2 * M, TB = M / 16, UNITS = SH_THREADS / TB, JPW = UNITS / 2;
+    constexpr int N = 2 * M, TB = M / 16, UNITS = sh_threads<M>() / TB, JPW = UNITS / 2;
     constexpr int REG = M + M / 16 + (M >= 256 ? SH_LDS_EXTRA : 0);
     constexpr int SS = spec_stride<M>();
     __shared__ float2 lds[UNITS * REG];
@@ -674,10 +679,10 @@ namespace {
 template <int M, class IO>
 hipError_t spectrum_m(const void* k, float2* spec, int C, int L, const float2* tw, hipStream_t s)
 {
-    constexpr int PPW = (SH_THREADS / (M / 16)) / 2;
+    constexpr int PPW = (sh_threads<M>() / (M / 16)) / 2;
     const int64_t pairs = ((int64_t)C + 1) / 2;
     const int64_t blocks = (pairs + PPW - 1) / PPW;
-    hipLaunchKernelGGL((shared_spectrum_kernel<M, IO>), dim3((unsigned)blocks), dim3(SH_THREADS),
+    hipLaunchKernelGGL((shared_spectrum_kernel<M, IO>), dim3((unsigned)blocks), dim3(sh_threads<M>()),
                        0, s, (const typename IO::T*)k, spec, C, L, tw);
     return hipGetLastError();
 }
@@ -686,10 +691,10 @@ template <int M, class IO, bool REV>
 hipError_t apply_m(const void* v, const float2* spec, void* r, int B, int C, int L, int head,
                    const float2* tw, hipStream_t s)
 {
-    constexpr int JPW = (SH_THREADS / (M / 16)) / 2;
+    constexpr int JPW = (sh_threads<M>() / (M / 16)) / 2;
     const int64_t jobs = (int64_t)C * ((B + 1) / 2);
     const int64_t blocks = ((jobs + JPW - 1) / JPW + 7) / 8 * 8;   // a multiple of 8
-    hipLaunchKernelGGL((shared_apply_kernel<M, IO, REV>), dim3((unsigned)blocks), dim3(SH_THREADS), 0,
+    hipLaunchKernelGGL((shared_apply_kernel<M, IO, REV>), dim3((unsigned)blocks), dim3(sh_threads<M>()), 0,
                        s, (const typename IO::T*)v, spec, (typename IO::T*)r, B, C, L, head, tw);
     return hipGetLastError();
 }
