@@ -25,9 +25,9 @@
 //     r = fma(-q, p, h) + l = a w - q p          (exact: |h - q p| < 2^31)
 // giving |r| <= 1.5 p.  LDS holds int32 values (|x| < 2^31) between passes.
 //
-// Layout as in the float kernel: 512 threads, a length-M transform held by TB = M/16
+// Layout as in the float kernel: max(64, M/8) threads, a length-M transform held by TB = M/16
 // threads with 16 values each, Stockham radix-16 passes through LDS (a v and a g array per
-// branch unit), 68 KB of LDS per workgroup.
+// branch unit), 68 KB of LDS per workgroup at M = 4096.
 
 #include "sc_device.h"
 #include "sc_internal.h"
@@ -271,8 +271,13 @@ __device__ __forceinline__ void passes(double (&x)[NA][16], int32_t* __restrict_
 // reversed: rev(causal(rev(dr), b))_j = sum_{t>=j} dr_t b_{t-j}.
 // FIX: float32 inputs encoded as integers round(v 2^fv), round(g 2^fg) (nearest, ties to
 // even; sv = 2^fv, sg = 2^fg, |v sv|, |g sg| < 2^51) instead of int32 inputs.
+// Threads of the workgroup for length-M transforms: one channel from M = 512 on, as many
+// as fill one wave below (as the float kernel).
+template <int M>
+constexpr int ntt_threads() { return M / 8 > 64 ? M / 8 : 64; }
+
 template <int M, bool REV, class Pr, bool FIX>
-__global__ __launch_bounds__(512, 4) void ntt_conv_kernel(const void* __restrict__ v,
+__global__ __launch_bounds__(ntt_threads<M>(), 4) void ntt_conv_kernel(const void* __restrict__ v,
                                                        const void* __restrict__ g,
                                                        int32_t* __restrict__ r, int64_t nch,
                                                        int L, const double* __restrict__ bank,
@@ -281,7 +286,7 @@ __global__ __launch_bounds__(512, 4) void ntt_conv_kernel(const void* __restrict
 {
     using namespace ntt;
     static_assert(M >= 64 && M <= 4096, "fused NTT handles 64 <= M <= 4096");
-    constexpr int N = 2 * M, TB = M / 16, UNITS = 512 / TB, CPW = UNITS / 2;
+    constexpr int N = 2 * M, TB = M / 16, UNITS = ntt_threads<M>() / TB, CPW = UNITS / 2;
     constexpr int REG = M + M / 16;
     __shared__ int32_t lds[UNITS * 2 * REG];
 
@@ -486,10 +491,10 @@ template <int M, bool REV, class Pr, bool FIX>
 static hipError_t launch_ntt_m(const void* v, const void* g, int32_t* r, int64_t nch, int L,
                                const NttTables& tb, double sv, double sg, hipStream_t stream)
 {
-    constexpr int CPW = (512 / (M / 16)) / 2;
+    constexpr int CPW = (ntt_threads<M>() / (M / 16)) / 2;
     const int64_t blocks = (nch + CPW - 1) / CPW;
     const int lg = __builtin_ctz((unsigned)(2 * M));
-    hipLaunchKernelGGL((ntt_conv_kernel<M, REV, Pr, FIX>), dim3((unsigned)blocks), dim3(512), 0,
+    hipLaunchKernelGGL((ntt_conv_kernel<M, REV, Pr, FIX>), dim3((unsigned)blocks), dim3(ntt_threads<M>()), 0,
                        stream, v, g, r, nch, L, tb.bank, tb.ninv[lg], tb.ninv_q[lg], sv, sg);
     return hipGetLastError();
 }
