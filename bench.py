@@ -656,7 +656,7 @@ def main(argv=None):
         return 0
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
+        print("bench.py measures one GPU only: the library has no multi-GPU path "
               "(channels shard across GPUs with no communication; run one process per GPU)",
               file=sys.stderr)
         return 2
