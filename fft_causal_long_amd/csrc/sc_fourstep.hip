@@ -284,12 +284,14 @@ static hipError_t launch_cols(bool fwd, const void* v, const void* g, void* r, f
     constexpr int NCOL = 256 / (M1 / 16);
     if (fwd) {
         const int64_t blocks = (int64_t)nc * (M2 / NCOL);
+        if (!grid_ok(blocks, 512)) return hipErrorInvalidValue;
         hipLaunchKernelGGL((fs_columns_fwd<M1, IO, REV>), dim3((unsigned)blocks), dim3(512), 0, s,
                            (const typename IO::T*)v, (const typename IO::T*)g, T, c0, L, M2, bank,
                            tw);
     } else {
         const int H = M2 / 2;
         const int64_t blocks = (int64_t)nc * ((H + NCOL - 1) / NCOL);
+        if (!grid_ok(blocks, 512)) return hipErrorInvalidValue;
         hipLaunchKernelGGL((fs_columns_inv<M1, IO, REV>), dim3((unsigned)blocks), dim3(512), 0, s, S,
                            (typename IO::T*)r, c0, L, M2, head, pair ? 1 : 0, bank, tw);
     }
@@ -317,6 +319,7 @@ static hipError_t launch_rows(const float2* T, float2* S, int nc, int M1, const 
 {
     constexpr int TR = M2 / 16, PAIRS = (2048 / M2) > 1 ? 2048 / M2 : 1;
     const int64_t blocks = (int64_t)nc * 2 * ((M1 / 2) / PAIRS);
+    if (!grid_ok(blocks, PAIRS * 2 * TR)) return hipErrorInvalidValue;
     hipLaunchKernelGGL((fs_rows<M2>), dim3((unsigned)blocks), dim3(PAIRS * 2 * TR), 0, s, T, S, M1,
                        bank, tw);
     return hipGetLastError();
@@ -401,6 +404,7 @@ static hipError_t launch_fourstep_rev(Store st, const void* v, const void* g, vo
         const int64_t total = nch * (int64_t)head;
         const int threads = 256;
         const int64_t blocks = (total + threads - 1) / threads;
+        if (!grid_ok(blocks, threads)) return hipErrorInvalidValue;
         if (st == Store::F32)
             hipLaunchKernelGGL((head_kernel<f32_io, REV>), dim3((unsigned)blocks), dim3(threads), 0,
                                stream, (const float*)v, (const float*)g, (float*)r, nch, L, head);

@@ -286,6 +286,7 @@ static hipError_t launch_fused_m(const void* v, const void* g, void* r, int64_t 
 {
     constexpr int CPW = (fused_threads<M>() / (M / 16)) / 2;
     const int64_t blocks = (nch + CPW - 1) / CPW;
+    if (!grid_ok(blocks, fused_threads<M>())) return hipErrorInvalidValue;
     hipLaunchKernelGGL((fused_conv_kernel<M, IO, REV>), dim3((unsigned)blocks), dim3(fused_threads<M>()), 0,
                        stream, (const typename IO::T*)v, (const typename IO::T*)g,
                        (typename IO::T*)r, nch, L, head, pair ? 1 : 0, tw);
@@ -325,6 +326,7 @@ static hipError_t launch_direct_rev(Store st, const void* v, const void* g, void
     const int64_t total = nch * (int64_t)L;
     const int threads = 256;
     const int64_t blocks = (total + threads - 1) / threads;
+    if (!grid_ok(blocks, threads)) return hipErrorInvalidValue;
     if (st == Store::F32)
         hipLaunchKernelGGL((direct_conv_kernel<f32_io, REV>), dim3((unsigned)blocks), dim3(threads),
                            0, stream, (const float*)v, (const float*)g, (float*)r, nch, L);

@@ -338,7 +338,7 @@ hipError_t gate_launch(const void* s, const void* W, void* g, int64_t nb, int64_
     const int64_t ntiles = (L + T - 1) / T, ngroups = cw / GC;
     const int64_t blocks = ntiles * ngroups * nb;
     if (blocks <= 0) return hipSuccess;
-    if (blocks > 0x7fffffff) return hipErrorInvalidValue;
+    if (!grid_ok(blocks, GT)) return hipErrorInvalidValue;
     hipLaunchKernelGGL((gate_kernel<IO, TM, VIN>), dim3((unsigned)blocks), dim3(GT), 0, st,
                        (const typename IO::T*)s, (const typename IO::T*)W, (typename IO::T*)g,
                        (int)C, (int)L, (int)gcs, (int)ngroups, (int)ntiles, vec_out ? 1 : 0);

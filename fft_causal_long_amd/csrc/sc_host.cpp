@@ -427,7 +427,8 @@ sc_status run_jobs(sc_kind kind, const Job* jobs, int njobs, bool rev, int64_t n
         for (int k = 0; k < njobs && e == hipSuccess; ++k)
             e = sc::launch_fourstep(s, jobs[k].a, jobs[k].b, jobs[k].o, nch, (int)L, M, head, pair,
                                     rev, d->fused_tw, tw, scratch, chunk, stream,
-                                    two ? d->fs_side : nullptr, d->fs_fork, d->fs_join);
+                                    two ? d->fs_side : nullptr, two ? d->fs_fork : nullptr,
+                                    two ? d->fs_join : nullptr);
         if (own && hipFreeAsync(scratch, stream) != hipSuccess && e == hipSuccess)
             e = hipErrorUnknown;
     }

@@ -77,6 +77,13 @@ struct FsTw {
     const float2* tu;
 };
 
+// A 1-D launch keeps its block count below 2^31 and its work-items below 2^32 (the dispatch
+// packet's grid size is 32 bits); launchers refuse larger grids with hipErrorInvalidValue.
+inline bool grid_ok(int64_t blocks, int64_t threads)
+{
+    return blocks >= 0 && blocks <= 0x7fffffff && blocks * threads <= 0xffffffffLL;
+}
+
 void fourstep_split(int M, int* M1, int* M2);
 size_t fourstep_bytes_per_channel(int M);
 // ws holds chunk channels of scratch (chunk * fourstep_bytes_per_channel(M) bytes).  With a

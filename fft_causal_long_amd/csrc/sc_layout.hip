@@ -151,7 +151,7 @@ hipError_t launch_transpose(int elt_bytes, const void* src0, void* dst0, const v
     if (R <= 0 || Cc <= 0 || nz <= 0) return hipSuccess;
     const int64_t tr = (R + TT - 1) / TT, tc = (Cc + TT - 1) / TT;
     const int64_t blocks = tr * tc * nz * (src1 ? 2 : 1);
-    if (blocks > 0x7fffffff) return hipErrorInvalidValue;
+    if (!grid_ok(blocks, TP_THREADS)) return hipErrorInvalidValue;
     const bool even = ((R | Cc | ss | ds | sz | dz) & 1) == 0 &&
                       ((uintptr_t)src0 | (uintptr_t)dst0 | (uintptr_t)src1 | (uintptr_t)dst1) %
                               (2 * elt_bytes) == 0;

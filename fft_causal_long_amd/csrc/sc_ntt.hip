@@ -494,6 +494,7 @@ static hipError_t launch_ntt_m(const void* v, const void* g, int32_t* r, int64_t
     constexpr int CPW = (ntt_threads<M>() / (M / 16)) / 2;
     const int64_t blocks = (nch + CPW - 1) / CPW;
     const int lg = __builtin_ctz((unsigned)(2 * M));
+    if (!grid_ok(blocks, ntt_threads<M>())) return hipErrorInvalidValue;
     hipLaunchKernelGGL((ntt_conv_kernel<M, REV, Pr, FIX>), dim3((unsigned)blocks), dim3(ntt_threads<M>()), 0,
                        stream, v, g, r, nch, L, tb.bank, tb.ninv[lg], tb.ninv_q[lg], sv, sg);
     return hipGetLastError();

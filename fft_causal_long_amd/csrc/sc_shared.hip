@@ -682,6 +682,7 @@ hipError_t spectrum_m(const void* k, float2* spec, int C, int L, const float2* t
     constexpr int PPW = (sh_threads<M>() / (M / 16)) / 2;
     const int64_t pairs = ((int64_t)C + 1) / 2;
     const int64_t blocks = (pairs + PPW - 1) / PPW;
+    if (!grid_ok(blocks, sh_threads<M>())) return hipErrorInvalidValue;
     hipLaunchKernelGGL((shared_spectrum_kernel<M, IO>), dim3((unsigned)blocks), dim3(sh_threads<M>()),
                        0, s, (const typename IO::T*)k, spec, C, L, tw);
     return hipGetLastError();
@@ -694,6 +695,7 @@ hipError_t apply_m(const void* v, const float2* spec, void* r, int B, int C, int
     constexpr int JPW = (sh_threads<M>() / (M / 16)) / 2;
     const int64_t jobs = (int64_t)C * ((B + 1) / 2);
     const int64_t blocks = ((jobs + JPW - 1) / JPW + 7) / 8 * 8;   // a multiple of 8
+    if (!grid_ok(blocks, sh_threads<M>())) return hipErrorInvalidValue;
     hipLaunchKernelGGL((shared_apply_kernel<M, IO, REV>), dim3((unsigned)blocks), dim3(sh_threads<M>()), 0,
                        s, (const typename IO::T*)v, spec, (typename IO::T*)r, B, C, L, head, tw);
     return hipGetLastError();
@@ -705,6 +707,7 @@ hipError_t dk_m(const void* dr, const void* v, void* dk, int B, int C, int L, in
 {
     constexpr int CPW = (SH_THREADS / (M / 16)) / 2;
     const int64_t blocks = ((int64_t)C + CPW - 1) / CPW;
+    if (!grid_ok(blocks, SH_THREADS)) return hipErrorInvalidValue;
     hipLaunchKernelGGL((shared_dk_kernel<M, IO>), dim3((unsigned)blocks), dim3(SH_THREADS), 0, s,
                        (const typename IO::T*)dr, (const typename IO::T*)v, (typename IO::T*)dk, B,
                        C, L, head, pair ? 1 : 0, tw);
@@ -733,6 +736,7 @@ hipError_t bwd_m(const void* dr, const void* v, const float2* spec, void* dv, vo
 {
     constexpr int CPW = (SH_THREADS / (M / 16)) / 2;
     const int64_t blocks = ((int64_t)C + CPW - 1) / CPW;
+    if (!grid_ok(blocks, SH_THREADS)) return hipErrorInvalidValue;
     hipLaunchKernelGGL((shared_bwd_kernel<M, IO>), dim3((unsigned)blocks), dim3(SH_THREADS), 0,
                        s, (const typename IO::T*)dr, (const typename IO::T*)v, spec,
                        (typename IO::T*)dv, (typename IO::T*)dk, B, C, L, head, pair ? 1 : 0,
