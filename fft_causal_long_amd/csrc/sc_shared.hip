@@ -36,6 +36,10 @@ constexpr int SH_THREADS = 512;
 // (as the per-row-gate kernel: small workgroups share a CU at different phases)
 template <int M>
 constexpr int sh_threads() { return M / 8 > 64 ? M / 8 : 64; }
+// threads of the gradient workgroups: one channel per workgroup from M = 1024 on (their
+// head work goes to the threads past the transforms, which must be whole waves), 512 below
+template <int M>
+constexpr int sh_grad_threads() { return M >= 1024 ? M / 8 : SH_THREADS; }
 constexpr int SH_HEAD_MAX = 64;
 constexpr int SH_LDS_EXTRA = 24;
 
@@ -270,15 +274,15 @@ __global__ __launch_bounds__(sh_threads<M>(), (M >= 512 ? 4 : 1)) void shared_ap
 // Per channel and batch row the transform of z = rev(dr_b) + i v_b carries both spectra;
 // the unpacked inverse input Y_k of the real-output inverse is linear in X = DR' V, so it is
 // summed over the rows in registers and inverted once.  The direct head (t < head) is
-// summed over the rows in LDS.  A workgroup serves 4096/M channels, as the per-row-gate
-// kernel, looping over the B rows.
+// summed over the rows in LDS.  A workgroup serves sh_grad_threads/(M/8) channels (one from
+// M = 1024 on), looping over the B rows.
 template <int M, class IO>
-__global__ __launch_bounds__(SH_THREADS) void shared_dk_kernel(
+__global__ __launch_bounds__(sh_grad_threads<M>()) void shared_dk_kernel(
     const typename IO::T* __restrict__ dr, const typename IO::T* __restrict__ v,
     typename IO::T* __restrict__ dk, int B, int C, int L, int head, int pair_store,
     const float2* __restrict__ tw)
 {
-    constexpr int N = 2 * M, TB = M / 16, UNITS = SH_THREADS / TB, CPW = UNITS / 2;
+    constexpr int N = 2 * M, TB = M / 16, UNITS = sh_grad_threads<M>() / TB, CPW = UNITS / 2;
     constexpr int CT = CPW * TB;
     constexpr int REG = M + M / 16 + (M >= 256 ? SH_LDS_EXTRA : 0);
     __shared__ float2 lds[UNITS * REG];
@@ -299,8 +303,8 @@ __global__ __launch_bounds__(SH_THREADS) void shared_dk_kernel(
     // head work of the upper half: output o (of CPW * head) split over S lanes
     const int nout = CPW * head;
     int S = 1;
-    while (S < 8 && 2 * S * nout <= SH_THREADS - CT) S *= 2;
-    for (int i = tid; i < CPW * SH_HEAD_MAX; i += SH_THREADS) hsum[i] = 0.f;
+    while (S < 8 && 2 * S * nout <= sh_grad_threads<M>() - CT) S *= 2;
+    for (int i = tid; i < CPW * SH_HEAD_MAX; i += sh_grad_threads<M>()) hsum[i] = 0.f;
 
     float2 yacc[4], ymacc[4];
 #pragma unroll
@@ -357,7 +361,7 @@ __global__ __launch_bounds__(SH_THREADS) void shared_dk_kernel(
         }
         if (tid >= CT) {
             // this row's head terms, added to hsum by the group's first lane
-            for (int base = 0; base < nout * S; base += SH_THREADS - CT) {
+            for (int base = 0; base < nout * S; base += sh_grad_threads<M>() - CT) {
                 const int idx = base + tid - CT, o = idx / S, sl = idx - o * S;
                 const int c2 = o / (head > 0 ? head : 1), t = o - c2 * head;
                 float acc = 0.f;
@@ -393,7 +397,7 @@ __global__ __launch_bounds__(SH_THREADS) void shared_dk_kernel(
     __syncthreads();
     if (!iact) {
         // the head, reversed like the rest: dk_{L-1-t} for t < head
-        for (int o = tid - CT; o < nout; o += SH_THREADS - CT) {
+        for (int o = tid - CT; o < nout; o += sh_grad_threads<M>() - CT) {
             const int c2 = o / head, t = o - c2 * head;
             if (c2 < nvalid && t < L) IO::store(ks, c2 * L + L - 1 - t, hsum[c2 * SH_HEAD_MAX + t]);
         }
@@ -468,7 +472,8 @@ __device__ __forceinline__ void unpack_grads(int k, const float2* __restrict__ u
 // Gradients for a filter shared by the batch, one kernel:
 //   dv[b][c][j] = sum_{t>=j} dr[b][c][t] k[c][t-j] = rev(causal(rev(dr_b), k))_j
 //   dk[c][j]    = sum_b sum_{t>=j} dr[b][c][t] v[b][c][t-j] = sum_b rev(causal(rev(dr_b), v_b))_j
-// A workgroup serves 4096/M channels (as the per-row-gate kernel) and loops over the B rows.
+// A workgroup serves sh_grad_threads/(M/8) channels (one from M = 1024 on) and loops over the
+// B rows.
 // Per row, one transform of z = rev(dr_b) + i v_b carries the spectra of rev(dr_b) and v_b;
 // the unpack gives the inverse input of dv_b (times the filter's spectrum), which is inverted
 // and stored at once, and that of dk (times V), which is linear in the product and summed
@@ -476,13 +481,13 @@ __device__ __forceinline__ void unpack_grads(int k, const float2* __restrict__ u
 // per row, dk's summed over the rows in LDS, both by the half of the workgroup that is idle
 // during an inverse.  Outputs are written reversed.
 template <int M, class IO>
-__global__ __launch_bounds__(SH_THREADS, (M >= 512 ? 4 : 1)) void shared_bwd_kernel(
+__global__ __launch_bounds__(sh_grad_threads<M>(), (M >= 512 ? 4 : 1)) void shared_bwd_kernel(
     const typename IO::T* __restrict__ dr, const typename IO::T* __restrict__ v,
     const float2* __restrict__ spec, typename IO::T* __restrict__ dv,
     typename IO::T* __restrict__ dk, int B, int C, int L, int head, int pair_store,
     const float2* __restrict__ tw)
 {
-    constexpr int N = 2 * M, TB = M / 16, UNITS = SH_THREADS / TB, CPW = UNITS / 2;
+    constexpr int N = 2 * M, TB = M / 16, UNITS = sh_grad_threads<M>() / TB, CPW = UNITS / 2;
     constexpr int CT = CPW * TB;
     constexpr int REG = M + M / 16 + (M >= 256 ? SH_LDS_EXTRA : 0);
     constexpr int SS = spec_stride<M>();
@@ -508,8 +513,8 @@ __global__ __launch_bounds__(SH_THREADS, (M >= 512 ? 4 : 1)) void shared_bwd_ker
     float2* ybuf = lds + (2 * icl) * REG;
     const int nout = CPW * head;
     int S = 1;
-    while (S < 8 && 2 * S * nout <= SH_THREADS - CT) S *= 2;
-    for (int i = tid; i < CPW * SH_HEAD_MAX; i += SH_THREADS) {
+    while (S < 8 && 2 * S * nout <= sh_grad_threads<M>() - CT) S *= 2;
+    for (int i = tid; i < CPW * SH_HEAD_MAX; i += sh_grad_threads<M>()) {
         hsum[i] = 0.f;
         const int c2 = i / SH_HEAD_MAX, n = i - c2 * SH_HEAD_MAX;
         hbuf[c2 * 3 * SH_HEAD_MAX + 2 * SH_HEAD_MAX + n] =
@@ -591,7 +596,7 @@ __global__ __launch_bounds__(SH_THREADS, (M >= 512 ? 4 : 1)) void shared_bwd_ker
             // this row's heads: dv_{L-1-t} = sum_{j<=t} rev(dr)_j k_{t-j} (stored), and the
             // row's share of dk's head sum_{j<=t} rev(dr)_j v_{t-j} (added to hsum by the
             // group's first lane); each sum split over S lanes
-            for (int base = 0; base < 2 * nout * S; base += SH_THREADS - CT) {
+            for (int base = 0; base < 2 * nout * S; base += sh_grad_threads<M>() - CT) {
                 const int idx = base + tid - CT, o2 = idx / S, sl = idx - o2 * S;
                 const int which = o2 >= nout ? 1 : 0, o = o2 - which * nout;
                 const int c2 = o / (head > 0 ? head : 1), t = o - c2 * head;
@@ -645,7 +650,7 @@ __global__ __launch_bounds__(SH_THREADS, (M >= 512 ? 4 : 1)) void shared_bwd_ker
     }
     __syncthreads();
     if (!iact) {
-        for (int o = tid - CT; o < nout; o += SH_THREADS - CT) {
+        for (int o = tid - CT; o < nout; o += sh_grad_threads<M>() - CT) {
             const int c2 = o / head, t = o - c2 * head;
             if (c2 < nvalid && t < L) IO::store(ks, c2 * L + L - 1 - t, hsum[c2 * SH_HEAD_MAX + t]);
         }
@@ -705,10 +710,10 @@ template <int M, class IO>
 hipError_t dk_m(const void* dr, const void* v, void* dk, int B, int C, int L, int head, bool pair,
                 const float2* tw, hipStream_t s)
 {
-    constexpr int CPW = (SH_THREADS / (M / 16)) / 2;
+    constexpr int CPW = (sh_grad_threads<M>() / (M / 16)) / 2;
     const int64_t blocks = ((int64_t)C + CPW - 1) / CPW;
-    if (!grid_ok(blocks, SH_THREADS)) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((shared_dk_kernel<M, IO>), dim3((unsigned)blocks), dim3(SH_THREADS), 0, s,
+    if (!grid_ok(blocks, sh_grad_threads<M>())) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((shared_dk_kernel<M, IO>), dim3((unsigned)blocks), dim3(sh_grad_threads<M>()), 0, s,
                        (const typename IO::T*)dr, (const typename IO::T*)v, (typename IO::T*)dk, B,
                        C, L, head, pair ? 1 : 0, tw);
     return hipGetLastError();
@@ -734,10 +739,10 @@ template <int M, class IO>
 hipError_t bwd_m(const void* dr, const void* v, const float2* spec, void* dv, void* dk, int B,
                  int C, int L, int head, bool pair, const float2* tw, hipStream_t s)
 {
-    constexpr int CPW = (SH_THREADS / (M / 16)) / 2;
+    constexpr int CPW = (sh_grad_threads<M>() / (M / 16)) / 2;
     const int64_t blocks = ((int64_t)C + CPW - 1) / CPW;
-    if (!grid_ok(blocks, SH_THREADS)) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((shared_bwd_kernel<M, IO>), dim3((unsigned)blocks), dim3(SH_THREADS), 0,
+    if (!grid_ok(blocks, sh_grad_threads<M>())) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((shared_bwd_kernel<M, IO>), dim3((unsigned)blocks), dim3(sh_grad_threads<M>()), 0,
                        s, (const typename IO::T*)dr, (const typename IO::T*)v, spec,
                        (typename IO::T*)dv, (typename IO::T*)dk, B, C, L, head, pair ? 1 : 0,
                        tw);
@@ -820,7 +825,7 @@ hipError_t launch_shared_dk(Store st, const void* dr, const void* v, void* dk, i
 
 int64_t shared_bwd_blocks(int64_t C, int M)
 {
-    const int64_t cpw = (SH_THREADS / (M / 16)) / 2;
+    const int64_t cpw = ((M >= 1024 ? M / 8 : SH_THREADS) / (M / 16)) / 2;   // sh_grad_threads
     return (C + cpw - 1) / cpw;
 }
 
