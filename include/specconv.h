@@ -39,7 +39,12 @@
  *      a failed HIP call or kernel launch       -> SC_ERR_HIP
  *  - Library-owned state: per-device constant tables (twiddles, modular constants), built on
  *    the first call on a device (a blocking host-to-device copy) and kept until the process
- *    ends.  Calls from several host threads are safe.
+ *    ends; and, for the four-step path (L > 4096), a second stream and two events per
+ *    device, made on first use: such a call may run half of its channel chunks on that
+ *    stream, which waits for `stream` at the start of the call, and `stream` waits for it
+ *    at the end, so the call stays ordered on `stream` as a whole.  While `stream` is being
+ *    captured into a graph the call uses `stream` alone.  Calls from several host threads
+ *    are safe.
  *  - Any L >= 1 is accepted; internally N = 2M with M the next power of two >= L.
  *    Throughput is best for powers of two.
  *  - Inputs of the float paths must be finite.  (A NaN or Inf at v_s reaches every output of
