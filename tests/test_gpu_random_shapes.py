@@ -1,0 +1,60 @@
+"""GPU parity on seeded random shapes: every float kind and path the automatic choice
+takes (direct, fused, four-step), forward and gradients, and the exact kind bit for bit,
+at lengths drawn log-uniformly over 1 .. 9000 and channel counts that leave partial
+workgroups.  The bounds are those of the fixed-shape tests (tests/gpu_util.py)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from tests.gpu_util import assert_within_bound, to_device, to_host
+from workloads import WORKLOADS, make_inputs
+
+pytestmark = pytest.mark.gpu
+
+_rng = np.random.default_rng(20261203)
+SHAPES = []
+for _ in range(16):
+    L = int(np.exp(_rng.uniform(0.0, np.log(9000.0))))
+    B = int(_rng.integers(1, 4))
+    C = int(_rng.integers(1, 40))
+    SHAPES.append((B, C, max(L, 1)))
+
+
+@pytest.fixture(scope="module")
+def sc():
+    import fft_causal_long_amd as m
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    return m
+
+
+@pytest.mark.parametrize("i", range(len(SHAPES)))
+def test_random_shape_float_forward_and_gradients(sc, i):
+    B, C, L = SHAPES[i]
+    cid = 4 if i % 2 == 0 else 3                  # fp32 (long-context recipe) or bf16
+    v, g = make_inputs(WORKLOADS[cid], B=B, C=C, L=L, seed_offset=300 + i)
+    dr, _ = make_inputs(WORKLOADS[cid], B=B, C=C, L=L, seed_offset=400 + i)
+    bf = v.dtype == np.uint16
+    what = "random %d: B=%d C=%d L=%d %s" % (i, B, C, L, "bf16" if bf else "f32")
+    print("case " + what, flush=True)
+    tv, tg, td = to_device(v), to_device(g), to_device(dr)
+    r = to_host(sc.causal_conv(tv, tg))
+    dv, dg = sc.causal_conv_bwd(td, tv, tg)
+    torch.cuda.synchronize()
+    r_ref, S = oracle.causal_conv_f64(v, g)
+    assert_within_bound(r, r_ref, S, bf, what)
+    dv_ref, dg_ref, Sv, Sg = oracle.causal_conv_bwd_f64(dr, v, g)
+    assert_within_bound(to_host(dv), dv_ref, Sv, bf, what + " dv")
+    assert_within_bound(to_host(dg), dg_ref, Sg, bf, what + " dg")
+
+
+@pytest.mark.parametrize("i", range(len(SHAPES)))
+def test_random_shape_exact(sc, i):
+    B, C, L = SHAPES[i]
+    L = min(L, 4096)                              # the exact kind's fused range
+    v, g = make_inputs(WORKLOADS[5], B=B, C=C, L=L, seed_offset=500 + i)
+    print("case random exact %d: B=%d C=%d L=%d" % (i, B, C, L), flush=True)
+    r = to_host(sc.causal_conv(to_device(v), to_device(g)))
+    torch.cuda.synchronize()
+    ref = oracle.lift_mod_p(oracle.causal_conv_i64(v, g))
+    assert np.array_equal(r.astype(np.int64), ref)
