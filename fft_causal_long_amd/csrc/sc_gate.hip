@@ -41,6 +41,7 @@ namespace {
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef uint32_t u32x16 __attribute__((ext_vector_type(16)));
 
 constexpr int GT = 256;      // threads
 constexpr int GC = 64;       // channels per group
@@ -72,7 +73,7 @@ __device__ __forceinline__ float sigmoid(float x)
 __device__ __forceinline__ uint16_t to_bf16(float x) { return (uint16_t)pack_bf16x2(x, 0.f); }
 
 template <class IO, bool TM, bool VIN>
-__global__ __launch_bounds__(GT) void gate_kernel(const typename IO::T* __restrict__ s,
+__global__ __launch_bounds__(GT, VIN ? 4 : 1) void gate_kernel(const typename IO::T* __restrict__ s,
                                                   const typename IO::T* __restrict__ W,
                                                   typename IO::T* __restrict__ g, int C, int L,
                                                   int gcs, int ngroups, int ntiles, int vec_out)
@@ -89,11 +90,12 @@ __global__ __launch_bounds__(GT) void gate_kernel(const typename IO::T* __restri
     constexpr int WP = GC * 3 + (BF ? 8 : 4);
     constexpr int W_BYTES = GC * WP * (int)sizeof(E);
     // VIN: channel rows of the tile, N[ci][NP]: tokens t0 .. t0+T-1, then t0-2 and t0-1,
-    // padded so that each row starts 16-byte aligned; past both W and S (N is written with W
-    // and read while S is written)
+    // padded so that each row starts 16-byte aligned; right after S, in space W has used
+    // (N is written once every wave holds its W fragments, and read while S is written):
+    // 36 KB of LDS and at most 128 registers keep four workgroups on a CU
     static_assert(!VIN || (BF && !TM), "vector channel-major input is a bf16 path");
     constexpr int NP = T + 8;
-    constexpr int NOFF = S_BYTES > W_BYTES ? S_BYTES : W_BYTES;
+    constexpr int NOFF = S_BYTES;
     static_assert(!VIN || (NOFF % 16 == 0 && (NP * (int)sizeof(E)) % 16 == 0), "16-byte rows");
     constexpr int SN_BYTES = VIN ? NOFF + GC * NP * (int)sizeof(E) : S_BYTES;
     constexpr int SO_BYTES = SN_BYTES > O_BYTES ? SN_BYTES : O_BYTES;
@@ -127,7 +129,11 @@ __global__ __launch_bounds__(GT) void gate_kernel(const typename IO::T* __restri
     constexpr int NE = T * GC / GT;                   // channel-major elements per thread
     constexpr int VPC = T / EPV;                      // vectors per channel row (VIN)
     constexpr int NVC = GC * VPC / GT;                // VIN vectors per thread
-    uint4 raw[TM ? NV : (VIN ? NVC : 1)];
+    uint4 raw[TM ? NV : 1];
+    // VIN: the tile's 16-byte vectors as one vector value (held across the W fragment reads;
+    // an array there was kept in scratch memory)
+    static_assert(!VIN || NVC == 4, "four vectors per thread");
+    u32x16 rv = {};
     float val[(TM || VIN) ? 1 : NE];
     uint4 halo = make_uint4(0, 0, 0, 0);
     float hv = 0.f;
@@ -154,7 +160,11 @@ __global__ __launch_bounds__(GT) void gate_kernel(const typename IO::T* __restri
         for (int q = 0; q < NVC; ++q) {
             const int vid = tid + GT * q, ci = vid / VPC, p = vid % VPC;
             const int tv = t0 + p * EPV < L ? t0 + p * EPV : L - EPV;
-            raw[q] = *(const uint4*)(sz + (int64_t)ci * L + tv);
+            const uint4 w = *(const uint4*)(sz + (int64_t)ci * L + tv);
+            rv[4 * q] = w.x;
+            rv[4 * q + 1] = w.y;
+            rv[4 * q + 2] = w.z;
+            rv[4 * q + 3] = w.w;
         }
         if (tid < GC && t0 > 0) hw = *(const uint32_t*)(sz + (int64_t)tid * L + t0 - 2);
     } else {
@@ -173,14 +183,6 @@ __global__ __launch_bounds__(GT) void gate_kernel(const typename IO::T* __restri
     for (int q = 0; q < WNV; ++q) {
         const int f = (tid + GT * q) * WEPV;
         *(uint4*)(Wl + (f / (GC * 3)) * WP + f % (GC * 3)) = wraw[q];
-    }
-    if constexpr (VIN) {
-#pragma unroll
-        for (int q = 0; q < NVC; ++q) {
-            const int vid = tid + GT * q, ci = vid / VPC, p = vid % VPC;
-            *(uint4*)(N + ci * NP + p * EPV) = raw[q];
-        }
-        if (tid < GC) *(uint32_t*)(N + tid * NP + T) = hw;
     }
     __syncthreads();
 
@@ -239,6 +241,14 @@ __global__ __launch_bounds__(GT) void gate_kernel(const typename IO::T* __restri
         }
         if (tid < 2 * VPR) put(hr, hc * EPV, halo, ht >= 0);
     } else if constexpr (VIN) {
+        // the tile's channel rows into N, then
+#pragma unroll
+        for (int q = 0; q < NVC; ++q) {
+            const int vid = tid + GT * q, ci = vid / VPC, p = vid % VPC;
+            *(uint4*)(N + ci * NP + p * EPV) = make_uint4(rv[4 * q], rv[4 * q + 1], rv[4 * q + 2], rv[4 * q + 3]);
+        }
+        if (tid < GC) *(uint32_t*)(N + tid * NP + T) = hw;
+        __syncthreads();
         // transpose: 8 channels of one token column into one 16-byte token-row vector;
         // consecutive lanes take consecutive tokens (conflict-free 2-byte reads)
         auto row8 = [&](int col, int cg, bool valid) {
