@@ -44,7 +44,8 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef uint32_t u32x16 __attribute__((ext_vector_type(16)));
 
 constexpr int GT = 256;      // threads
-// waves per SIMD the token-major bf16 form is compiled for (registers <= 512 / waves)
+// waves per SIMD the token-major bf16 form is compiled for (registers <= 512 / waves; the
+// fp32 form takes 3, which its 50 KB of LDS allows anyway)
 #ifndef SC_GATE_TM_WAVES
 #define SC_GATE_TM_WAVES 5
 #endif
@@ -77,7 +78,7 @@ __device__ __forceinline__ float sigmoid(float x)
 __device__ __forceinline__ uint16_t to_bf16(float x) { return (uint16_t)pack_bf16x2(x, 0.f); }
 
 template <class IO, bool TM, bool VIN>
-__global__ __launch_bounds__(GT, VIN ? 4 : ((TM && sizeof(typename IO::T) == 2) ? SC_GATE_TM_WAVES : 1)) void gate_kernel(const typename IO::T* __restrict__ s,
+__global__ __launch_bounds__(GT, VIN ? 4 : (TM ? (sizeof(typename IO::T) == 2 ? SC_GATE_TM_WAVES : 3) : 1)) void gate_kernel(const typename IO::T* __restrict__ s,
                                                   const typename IO::T* __restrict__ W,
                                                   typename IO::T* __restrict__ g, int C, int L,
                                                   int gcs, int ngroups, int ntiles, int vec_out)
