@@ -58,3 +58,35 @@ def test_random_shape_exact(sc, i):
     torch.cuda.synchronize()
     ref = oracle.lift_mod_p(oracle.causal_conv_i64(v, g))
     assert np.array_equal(r.astype(np.int64), ref)
+
+
+@pytest.mark.parametrize("i", range(0, len(SHAPES), 2))
+def test_random_shape_token_major(sc, i):
+    # the (B, L, C) call gives the bits of the channel-major call on the transposed tensors
+    B, C, L = SHAPES[i]
+    v, g = make_inputs(WORKLOADS[3], B=B, C=C, L=L, seed_offset=600 + i)
+    print("case random token-major %d: B=%d C=%d L=%d" % (i, B, C, L), flush=True)
+    tv, tg = to_device(v), to_device(g)
+    r_cm = sc.causal_conv(tv, tg)
+    r_tm = sc.causal_conv_blc(tv.transpose(1, 2).contiguous(), tg.transpose(1, 2).contiguous())
+    torch.cuda.synchronize()
+    assert torch.equal(r_tm.transpose(1, 2).contiguous().view(torch.int16), r_cm.view(torch.int16))
+
+
+@pytest.mark.parametrize("i", range(1, len(SHAPES), 4))
+def test_random_shape_gate_mixing_step(sc, i):
+    # channel counts rounded up to whole gate groups; both layouts give the bits of the gate
+    # call followed by the convolution
+    from workloads import make_gate_inputs
+    B, C, L = SHAPES[i]
+    C = 64 * ((C + 63) // 64)
+    v, s, W = make_gate_inputs(WORKLOADS[3], B=B, C=C, L=L, seed_offset=700 + i)
+    print("case random gate %d: B=%d C=%d L=%d" % (i, B, C, L), flush=True)
+    tv, ts, tW = to_device(v), to_device(s), to_device(W)
+    g = sc.gate(ts, tW)
+    r_sep = sc.causal_conv(tv, g)
+    r_cm = sc.gate_conv(tv, ts, tW)
+    r_tm = sc.gate_conv_blc(tv.transpose(1, 2).contiguous(), ts.transpose(1, 2).contiguous(), tW)
+    torch.cuda.synchronize()
+    assert torch.equal(r_cm.view(torch.int16), r_sep.view(torch.int16))
+    assert torch.equal(r_tm.transpose(1, 2).contiguous().view(torch.int16), r_sep.view(torch.int16))
