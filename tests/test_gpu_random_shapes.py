@@ -90,3 +90,27 @@ def test_random_shape_gate_mixing_step(sc, i):
     torch.cuda.synchronize()
     assert torch.equal(r_cm.view(torch.int16), r_sep.view(torch.int16))
     assert torch.equal(r_tm.transpose(1, 2).contiguous().view(torch.int16), r_sep.view(torch.int16))
+
+
+@pytest.mark.parametrize("i", [i for i in range(len(SHAPES)) if SHAPES[i][2] <= 4096 and i % 3 == 0])
+def test_random_shape_shared_filter(sc, i):
+    # one filter per channel shared by the batch: forward and both gradients (dk summed
+    # over the batch) against the oracle's bounds
+    from workloads import make_grad, make_shared_filter
+    B, C, L = SHAPES[i]
+    w = WORKLOADS[4 if i % 2 == 0 else 3]
+    v, _ = make_inputs(w, B=B, C=C, L=L, seed_offset=800 + i)
+    k = make_shared_filter(w, C=C, L=L, seed_offset=800 + i)
+    dr = make_grad(w, B=B, C=C, L=L, seed_offset=900 + i)
+    bf = v.dtype == np.uint16
+    what = "random shared %d: B=%d C=%d L=%d %s" % (i, B, C, L, "bf16" if bf else "f32")
+    print("case " + what, flush=True)
+    tv, tk, td = to_device(v), to_device(k), to_device(dr)
+    r = to_host(sc.causal_conv_shared(tv, tk))
+    dv, dk = sc.causal_conv_shared_bwd(td, tv, tk)
+    torch.cuda.synchronize()
+    r_ref, S = oracle.causal_conv_f64(v, np.ascontiguousarray(np.broadcast_to(k[None], v.shape)))
+    assert_within_bound(r, r_ref, S, bf, what)
+    dv_ref, dk_ref, Sv, Sk = oracle.shared_conv_bwd_f64(dr, v, k)
+    assert_within_bound(to_host(dv), dv_ref, Sv, bf, what + " dv")
+    assert_within_bound(to_host(dk), dk_ref, Sk, bf, what + " dk")
