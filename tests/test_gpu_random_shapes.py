@@ -114,3 +114,16 @@ def test_random_shape_shared_filter(sc, i):
     dv_ref, dk_ref, Sv, Sk = oracle.shared_conv_bwd_f64(dr, v, k)
     assert_within_bound(to_host(dv), dv_ref, Sv, bf, what + " dv")
     assert_within_bound(to_host(dk), dk_ref, Sk, bf, what + " dk")
+
+
+@pytest.mark.parametrize("i", [i for i in range(len(SHAPES)) if SHAPES[i][2] <= 4096 and i % 3 == 1])
+def test_random_shape_exact_real_valued(sc, i):
+    # fixed-point encoding with 20 + 20 fraction bits, three primes: bit for bit the oracle
+    B, C, L = SHAPES[i]
+    v, g = make_inputs(WORKLOADS[4], B=B, C=C, L=L, seed_offset=1000 + i)
+    assert sc.sc_fixed_range_ok(float(np.abs(v).max()), float(np.abs(g).max()), 20, 20, L)
+    print("case random exact real-valued %d: B=%d C=%d L=%d" % (i, B, C, L), flush=True)
+    r = to_host(sc.causal_conv_fixed(to_device(v), to_device(g), 20, 20))
+    torch.cuda.synchronize()
+    ref = oracle.causal_conv_fixed_f32(v, g, 20, 20)
+    assert np.array_equal(r.view(np.uint32), ref.view(np.uint32))
