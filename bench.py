@@ -616,6 +616,53 @@ def gate_measure(sc, torch, w, dev, steps: int, warmup: int, conv_ms: float) -> 
             "gate_conv_blc_value": round(w.outputs / (t_gtm * 1e-3), 1), "unit": "outputs/s"}
 
 
+def other_measure(sc, torch, w, dev, steps: int, warmup: int) -> dict:
+    """The plain call on another workload of the set (same timing method as the headline:
+    launches back to back on the launch stream, buffer sets rotated through HBM)."""
+    from workloads import make_inputs
+    fn_name, esz = {"i32": ("sc_causal_conv_ntt_i32", 4), "bf16": ("sc_causal_conv_bf16", 2),
+                    "f32": ("sc_causal_conv_f32", 4)}[w.storage]
+    fn = getattr(sc.lib(), fn_name)
+    v, g = make_inputs(w)
+    tdtype = {"f32": torch.float32, "bf16": torch.int16, "i32": torch.int32}[w.storage]
+    hv = torch.from_numpy(v.view(np.int16) if w.storage == "bf16" else v)
+    hg = torch.from_numpy(g.view(np.int16) if w.storage == "bf16" else g)
+    nsets = max(1, min(3, -(-2 * CACHE_BYTES // (3 * w.outputs * esz))))
+    bufs = [(hv.to(dev), hg.to(dev), torch.empty(w.outputs, dtype=tdtype, device=dev))
+            for _ in range(nsets)]
+    nbytes = sc.sc_workspace_bytes(sc.KIND_F32 if w.storage == "f32" else
+                                   sc.KIND_BF16 if w.storage == "bf16" else sc.KIND_NTT_I32,
+                                   w.B, w.C, w.L)
+    stream = torch.cuda.current_stream(dev)
+    sptr = stream.cuda_stream
+    ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=dev)
+    fn_ws = getattr(sc.lib(), fn_name + "_ws")
+
+    def step(i):
+        a, b, c = bufs[i % nsets]
+        st = fn_ws(a.data_ptr(), b.data_ptr(), c.data_ptr(), w.B, w.C, w.L,
+                   ws.data_ptr() if nbytes else None, nbytes, sptr)
+        if st != 0:
+            raise RuntimeError("%s_ws failed: %s" % (fn_name, sc.sc_status_string(st)))
+
+    for i in range(warmup):
+        step(i)
+    ms, _ = time_rounds(torch, stream, step, steps)
+    alg_bytes = w.outputs * 3 * esz
+    rec = {"workload": w.name, "entry": fn_name + "_ws", "ms_per_call": round(ms, 5),
+           "value": round(w.outputs / (ms * 1e-3), 1), "unit": "outputs/s",
+           "hbm": {"algorithmic_bytes_per_call": alg_bytes,
+                   "achieved_GBps": round(alg_bytes / (ms * 1e-3) / 1e9, 1),
+                   "frac": round(alg_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)}}
+    if w.storage != "i32":
+        tf = algorithmic_flops_per_output(w.L) * w.outputs / (ms * 1e-3) / 1e12
+        rec["alu"] = {"achieved_TFLOPs": round(tf, 2), "peak": FP32_VECTOR_PEAK_TFLOPS,
+                      "frac": round(tf / FP32_VECTOR_PEAK_TFLOPS, 4)}
+    del bufs, ws
+    torch.cuda.empty_cache()
+    return rec
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -636,6 +683,8 @@ def main(argv=None):
                     help="skip the timing of the gate-stream calls")
     ap.add_argument("--no-fixed", action="store_true",
                     help="skip the timing of the exactly causal real-valued call")
+    ap.add_argument("--no-others", action="store_true",
+                    help="skip the plain call on the other workloads (Small, exact, long)")
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run a plain device copy of known size (profiler calibration)")
     ap.add_argument("--record-valu", metavar="SQ_DIR",
@@ -762,6 +811,9 @@ def main(argv=None):
                                    kernel_ms)
     if not args.no_fixed and w.storage != "i32" and w.L <= 4096:
         rec["fixed"] = fixed_measure(sc, torch, w, dev, max(5, args.steps // 5), 2)
+    if not args.no_others and args.config == 3:
+        rec["other_workloads"] = [other_measure(sc, torch, WORKLOADS[c], dev, 20, 3)
+                                  for c in (2, 5, 4)]
     if not args.no_leakage:
         rec["leakage"] = leakage_probe(sc, torch, dev)
     if not args.no_cpu_baseline:
