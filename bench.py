@@ -776,7 +776,7 @@ def main(argv=None):
                 "unit": "TFLOP/s", "frac": round(tf / FP32_VECTOR_PEAK_TFLOPS, 4),
                 "traffic": traffic}
     rec = {
-        "metric": "causal-conv outputs/sec (B*C*L) at L=%d + %% HBM roofline" % w.L,
+        "metric": "causal-conv outputs/sec (B\u00b7C\u00b7L) at L=%d + %% HBM roofline; NTT leakage=0" % w.L,
         "value": round(value, 1),
         "unit": "outputs/s",
         "n_gpus": 1,
