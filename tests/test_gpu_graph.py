@@ -72,3 +72,33 @@ def test_token_major_call_in_a_graph(sc):
     # eager work that reuses the workspace between replays
     replay_check(graph, out, ref,
                  lambda i: sc.causal_conv_blc(vt, gt, out=torch.empty_like(vt), workspace=ws))
+
+
+def test_four_step_call_in_a_graph(sc):
+    # eagerly, this many channels alternate between the caller's stream and a second one;
+    # under capture the call must stay on the capturing stream (caller workspace, tables made
+    # by the warm-up call), and every replay must give the eager bits
+    L = 16384
+    per = sc.sc_workspace_bytes(sc.KIND_F32, 1, 1, L)
+    chunk = sc.sc_workspace_bytes(sc.KIND_F32, 1, 10**6, L) // per
+    C = chunk // 2 + 44
+    v, g = make_inputs(WORKLOADS[4], B=1, C=C, L=L, seed_offset=63)
+    vd, gd = to_device(v), to_device(g)
+    ws = torch.empty(sc.sc_workspace_bytes(sc.KIND_F32, 1, C, L), dtype=torch.uint8,
+                     device="cuda:0")
+    ref = sc.causal_conv(vd, gd, workspace=ws)
+    out = torch.empty_like(ref)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    print("case graph four-step C=%d L=%d" % (C, L), flush=True)
+    with torch.cuda.stream(side):
+        sc.causal_conv(vd, gd, out=out, workspace=ws)
+        torch.cuda.synchronize()
+        with torch.cuda.graph(graph, stream=side):
+            sc.causal_conv(vd, gd, out=out, workspace=ws)
+    torch.cuda.synchronize()
+    # eager two-stream calls that reuse the workspace between replays
+    replay_check(graph, out, ref,
+                 lambda i: sc.causal_conv(vd, gd, out=torch.empty_like(vd), workspace=ws))
