@@ -171,3 +171,22 @@ def test_four_step_concurrent_callers(sc):
     for k in range(2):
         for i in range(3):
             assert torch.equal(outs[k][i].view(torch.int32), ref[k].view(torch.int32)), (k, i)
+
+
+@pytest.mark.parametrize("wl,L", [(4, 1 << 22), (3, (1 << 22) - 3)])
+def test_four_step_longest_length_sampled(sc, wl, L):
+    # the longest length the library takes (2^22, and a ragged one just below it in bf16):
+    # sampled outputs, the first and last positions of each channel among them, against
+    # the float64 oracle summed one output at a time
+    v, g = make_inputs(WORKLOADS[wl], B=1, C=2, L=L, seed_offset=70 + wl)
+    print("case four-step longest wl=%d L=%d" % (wl, L), flush=True)
+    r = run(sc, v, g).reshape(2, L)
+    rng = np.random.default_rng(L)
+    t = np.concatenate([[0, 1, 31, 32, 33, 4095, 4096, L // 2, L - 2, L - 1],
+                        rng.integers(0, L, 150)])
+    ch = np.repeat(np.arange(2), t.size)
+    t = np.tile(t, 2)
+    r_ref, S = oracle.causal_conv_f64_at(v.reshape(2, L), g.reshape(2, L), ch, t)
+    worst = assert_within_bound(r[ch, t], r_ref, S, v.dtype == np.uint16,
+                                "four-step L=%d sampled" % L)
+    print("four-step L=%d: worst err/bound = %.3g" % (L, worst), flush=True)
