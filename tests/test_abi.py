@@ -359,3 +359,29 @@ def test_gate_host_checks(sc):
     assert h.sc_gate_conv_ex(F32, A, B_, C_, D, *bad, None, None, 0, None) == UNSUP
     # token-major s must be 16-byte aligned (row vectors)
     assert h.sc_gate_conv_blc_ex(F32, A, B_ + 4, C_, D, 1, 16, 64, None, None, 0, None) == INVALID
+
+
+def test_tensor_front_end_refuses_host_tensors(sc):
+    # there is no CPU path: host tensors are refused before any library call
+    import torch
+    v = torch.ones(1, 2, 8)
+    calls = [lambda: sc.causal_conv(v, v), lambda: sc.causal_conv_blc(v, v),
+             lambda: sc.causal_conv_bwd(v, v, v), lambda: sc.causal_conv_fixed(v, v, 8, 8),
+             lambda: sc.filter_spectrum(v[0]), lambda: sc.gate(torch.ones(1, 64, 8), torch.ones(64, 64, 3))]
+    for call in calls:
+        with pytest.raises(ValueError, match="GPU"):
+            call()
+
+
+def test_package_without_its_library_fails_to_import(tmp_path):
+    # the Python package with no libspecconv.so beside it raises on import (no fallback)
+    import shutil
+    pkg = tmp_path / "fft_causal_long_amd"
+    pkg.mkdir()
+    for name in ("__init__.py", "build.py"):
+        shutil.copy(os.path.join(ROOT, "fft_causal_long_amd", name), pkg / name)
+    p = subprocess.run(["python", "-c", "import fft_causal_long_amd"], cwd=str(tmp_path),
+                       env=dict(os.environ, PYTHONPATH=str(tmp_path)), capture_output=True,
+                       text=True, timeout=120)
+    assert p.returncode != 0
+    assert "libspecconv.so is not built" in p.stderr
