@@ -1005,9 +1005,17 @@ sc_status shared_bwd_run(sc_kind kind, const void* dr, const void* v, const void
     if (st != SC_OK) return st;
     if (kind != SC_KIND_F32 && kind != SC_KIND_BF16) return SC_ERR_INVALID_ARGUMENT;
     if (L > kMaxLFused) return SC_ERR_UNSUPPORTED;
-    if (n == 0) return SC_OK;
     const size_t es = elt_size(kind);
     if ((__int128)C * L * (int64_t)es >= ((__int128)1 << 31)) return SC_ERR_UNSUPPORTED;
+    if (n == 0) {
+        // no rows: dv is empty, and dk (C x L, when that is not empty) is the sum over no
+        // rows, zero
+        if (C == 0 || L == 0) return SC_OK;
+        if (!dk || (uintptr_t)dk % es) return SC_ERR_INVALID_ARGUMENT;
+        return sc::launch_zero16(dk, C * L * (int64_t)(es / 2), stream) == hipSuccess
+                   ? SC_OK
+                   : SC_ERR_HIP;
+    }
     const void* filt = spec ? spec : k;
     if (!dr || !v || !filt || !dv || !dk) return SC_ERR_INVALID_ARGUMENT;
     if (((uintptr_t)dr | (uintptr_t)v | (uintptr_t)dv | (uintptr_t)dk) % es)

@@ -118,6 +118,9 @@ int64_t shared_bwd_blocks(int64_t C, int M);
 hipError_t launch_shared_bwd(Store st, const void* dr, const void* v, const float2* spec, void* dv,
                              void* dk, int B, int C, int L, int M, int head, bool pair_store,
                              const float2* tw, hipStream_t stream);
+// dk of an empty batch (the sum over no rows): n16 halfwords of p set to zero by a kernel
+// (no memset node, so the call can be captured into a graph)
+hipError_t launch_zero16(void* p, int64_t n16, hipStream_t stream);
 
 // Direct summation r_t = sum_{j<=t} v_j g_{t-j} in fp32, one thread per output.
 hipError_t launch_direct(Store st, const void* v, const void* g, void* r, int64_t nch, int L,

@@ -838,4 +838,20 @@ hipError_t launch_shared_bwd(Store st, const void* dr, const void* v, const floa
                : bwd_io<bf16_io>(dr, v, spec, dv, dk, B, C, L, M, head, pair_store, tw, s);
 }
 
+__global__ void zero16_kernel(uint16_t* __restrict__ p, int64_t n)
+{
+    const int64_t step = (int64_t)gridDim.x * blockDim.x;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += step) p[i] = 0;
+}
+
+hipError_t launch_zero16(void* p, int64_t n16, hipStream_t stream)
+{
+    if (n16 <= 0) return hipSuccess;
+    constexpr int threads = 256;
+    const int64_t want = (n16 + threads - 1) / threads;
+    const unsigned blocks = (unsigned)(want < 4096 ? want : 4096);
+    hipLaunchKernelGGL(zero16_kernel, dim3(blocks), dim3(threads), 0, stream, (uint16_t*)p, n16);
+    return hipGetLastError();
+}
+
 }  // namespace sc

@@ -367,7 +367,8 @@ sc_status sc_causal_conv_shared_bf16(const uint16_t* v, const uint16_t* k, uint1
  * rows and inverts once per channel.  Accuracy as the forward calls with the error scales
  * sum_t |dr_t||k_{t-j}| and sum_b sum_t |dr_t||v_{t-j}|; the last 32 positions of dv and dk
  * use direct fp32 summation.  dv (B*C*L elements) and dk (C*L) may overlap neither each
- * other nor dr, v, k or the spectrum.  Limits and errors as sc_causal_conv_shared_*.
+ * other nor dr, v, k or the spectrum.  With B = 0 (and C*L > 0) only dk is touched: it is
+ * set to zero, the sum over no rows.  Limits and errors as sc_causal_conv_shared_*.
  */
 sc_status sc_causal_conv_spec_bwd_f32(const float* dr, const float* v, const void* spec,
                                       float* dv, float* dk, int64_t B, int64_t C, int64_t L,

@@ -268,7 +268,11 @@ def test_shared_filter_bwd_host_checks(sc):
         assert f(A, B_, C_, D_, D_ + 64, 2, 4, 64, None) == INVALID, name  # dk overlaps dv
         assert f(A, B_, C_, D_ + 1, E_, 2, 4, 64, None) == INVALID, name  # misaligned dv
         assert f(A, B_, C_, D_, E_, -2, 4, 64, None) == INVALID, name
-        assert f(None, None, None, None, None, 0, 4, 64, None) == OK, name
+        # no rows: nothing to read, but dk (C x L) is written (zero), so it must be given
+        assert f(None, None, None, None, None, 4, 0, 64, None) == OK, name
+        assert f(None, None, None, None, None, 0, 4, 0, None) == OK, name
+        assert f(None, None, None, None, None, 0, 4, 64, None) == INVALID, name
+        assert f(None, None, None, None, E_ + 1, 0, 4, 64, None) == INVALID, name
     assert h.sc_causal_conv_spec_bwd_f32(A, B_, C_ + 4, D_, E_, 2, 4, 64, None) == INVALID
     assert h.sc_causal_conv_shared_bwd_f32(1 << 40, 2 << 40, 3 << 40, 4 << 40, 5 << 40, 1,
                                            1 << 19, 4096, None) == UNSUP

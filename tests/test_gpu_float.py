@@ -173,3 +173,24 @@ def test_fp32_leakage_is_small_but_reported(sc):
     print("fp32 leakage max_{t<s}|dr_t| = %.3g (rms r = %.3g)" % (leak, rms), flush=True)
     assert np.isfinite(leak)
     assert leak < 1e-3 * rms     # round-off sized, not a structural leak
+
+
+def test_empty_inputs_on_every_call(sc):
+    # a zero batch, channel or length dimension: every call succeeds with an empty result
+    dev = "cuda:0"
+    for B, C, L in ((0, 64, 16), (2, 0, 16), (2, 64, 0)):
+        print("case empty B=%d C=%d L=%d" % (B, C, L), flush=True)
+        f = torch.zeros((B, C, L), dtype=torch.float32, device=dev)
+        t = f.transpose(1, 2).contiguous()
+        W = torch.zeros((C, 64, 3), dtype=torch.float32, device=dev)
+        assert sc.causal_conv(f.bfloat16(), f.bfloat16()).shape == f.shape
+        assert sc.causal_conv(f.int(), f.int()).shape == f.shape
+        assert all(x.shape == f.shape for x in sc.causal_conv_bwd(f, f, f))
+        assert sc.causal_conv_fixed(f, f, 8, 8).shape == f.shape
+        assert sc.causal_conv_blc(t, t).shape == t.shape
+        assert sc.gate(f, W).shape == f.shape
+        assert sc.gate_conv(f, f, W).shape == f.shape
+        assert sc.gate_conv_blc(t, t, W).shape == t.shape
+        k = torch.zeros((C, L), dtype=torch.float32, device=dev)
+        assert sc.causal_conv_shared(f, k).shape == f.shape
+    torch.cuda.synchronize()

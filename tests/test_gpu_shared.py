@@ -185,3 +185,21 @@ def test_bwd_one_kernel_misaligned_dk(sc):
     assert float(dk_buf[0]) == 0.0
     check_bwd(to_host(dv), to_host(dk), dr, v, k, "one-kernel misaligned",
               chans=np.array([0, 255, 511]))
+
+
+@pytest.mark.parametrize("dt,C,L", [(torch.float32, 8, 1000), (torch.bfloat16, 3, 333)])
+def test_bwd_empty_batch_zeroes_dk(sc, dt, C, L):
+    # dk sums over the batch rows: with no rows it is zero, whatever dk held before
+    print("case shared bwd empty batch %s C=%d L=%d" % (dt, C, L), flush=True)
+    e = torch.empty((0, C, L), dtype=dt, device="cuda:0")
+    k = torch.ones((C, L), dtype=dt, device="cuda:0")
+    dk = torch.full((C, L), 7.0, dtype=dt, device="cuda:0")
+    dv, dk2 = sc.causal_conv_shared_bwd(e, e, k, dk=dk)
+    torch.cuda.synchronize()
+    assert dv.shape == e.shape and dk2.data_ptr() == dk.data_ptr()
+    assert int(torch.count_nonzero(dk)) == 0
+    spec = sc.filter_spectrum(k)
+    dk.fill_(7.0)
+    sc.causal_conv_spec_bwd(e, e, spec, C, L, dk=dk)
+    torch.cuda.synchronize()
+    assert int(torch.count_nonzero(dk)) == 0
