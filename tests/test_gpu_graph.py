@@ -1,5 +1,5 @@
-"""The library under HIP graph capture: the fused call and the token-major call (caller
-workspace) are captured in a torch CUDA graph on a side stream, the graph is replayed several
+"""The library under HIP graph capture: the fused call, the token-major call (caller
+workspace), a four-step call and the gradient calls are captured in a torch CUDA graph on a side stream, the graph is replayed several
 times with the program's own eager work in between, and every replay must equal the eager
 result bit for bit.  The library allocates nothing on these paths, so capture is valid."""
 import numpy as np
@@ -102,3 +102,41 @@ def test_four_step_call_in_a_graph(sc):
     # eager two-stream calls that reuse the workspace between replays
     replay_check(graph, out, ref,
                  lambda i: sc.causal_conv(vd, gd, out=torch.empty_like(vd), workspace=ws))
+
+
+def test_gradient_and_empty_batch_calls_in_a_graph(sc):
+    # the gradient call (fused path) and the shared-filter gradients of an empty batch (whose
+    # dk is cleared by a fill kernel, not a memset) captured together; every replay gives the
+    # eager dv, dg bit for bit and a zero dk
+    v, g = make_inputs(WORKLOADS[3], B=2, C=64, L=4096, seed_offset=64)
+    dr = make_inputs(WORKLOADS[3], B=2, C=64, L=4096, seed_offset=65)[0]
+    vd, gd, drd = to_device(v), to_device(g), to_device(dr)
+    rdv, rdg = sc.causal_conv_bwd(drd, vd, gd)
+    dv, dg = torch.empty_like(rdv), torch.empty_like(rdg)
+    e = torch.empty((0, 3, 333), dtype=torch.bfloat16, device="cuda:0")
+    k = torch.ones((3, 333), dtype=torch.bfloat16, device="cuda:0")
+    dk = torch.full((3, 333), 7.0, dtype=torch.bfloat16, device="cuda:0")
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    print("case graph gradients + empty batch", flush=True)
+    with torch.cuda.stream(side):
+        sc.causal_conv_bwd(drd, vd, gd, dv=dv, dg=dg)
+        sc.causal_conv_shared_bwd(e, e, k, dk=dk)
+        torch.cuda.synchronize()
+        with torch.cuda.graph(graph, stream=side):
+            sc.causal_conv_bwd(drd, vd, gd, dv=dv, dg=dg)
+            sc.causal_conv_shared_bwd(e, e, k, dk=dk)
+    torch.cuda.synchronize()
+    for i in range(3):
+        dv.zero_()
+        dg.zero_()
+        dk.fill_(7.0)
+        torch.mul(vd, 1, out=torch.empty_like(vd))       # eager work between replays
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(dv.view(torch.int16), rdv.view(torch.int16)), i
+        assert torch.equal(dg.view(torch.int16), rdg.view(torch.int16)), i
+        assert int(torch.count_nonzero(dk)) == 0, i
