@@ -12,7 +12,7 @@ There is no CPU fallback: if the library is missing, importing this package fail
 Public names mirror the C ABI of ``include/specconv.h``:
 ``sc_causal_conv_f32``, ``sc_causal_conv_bf16``, ``sc_causal_conv_ntt_i32``, their
 ``_ws`` variants, ``sc_causal_conv_ex``, ``sc_workspace_bytes``, ``sc_ntt_range_ok``,
-``sc_status_string``, ``sc_version``, and the gradient calls ``sc_causal_conv_bwd_f32``,
+``sc_status_string``, ``sc_version``, ``sc_prepare``, and the gradient calls ``sc_causal_conv_bwd_f32``,
 ``sc_causal_conv_bwd_bf16``, ``sc_causal_conv_bwd_ntt_i32``, ``sc_causal_conv_bwd_ex``; plus
 :func:`causal_conv` and :func:`causal_conv_bwd`, which dispatch on dtype; the exactly causal
 real-valued calls ``sc_causal_conv_fixed_f32``, ``sc_causal_conv_fixed_f32_ws``,
@@ -32,7 +32,7 @@ __all__ = [
     "SpecConvError", "lib", "causal_conv", "sc_causal_conv_f32", "sc_causal_conv_bf16",
     "sc_causal_conv_ntt_i32", "sc_causal_conv_f32_ws", "sc_causal_conv_bf16_ws",
     "sc_causal_conv_ntt_i32_ws", "sc_causal_conv_ex", "sc_workspace_bytes", "sc_ntt_range_ok",
-    "sc_status_string", "sc_version", "causal_conv_bwd", "sc_causal_conv_bwd_f32",
+    "sc_status_string", "sc_version", "sc_prepare", "causal_conv_bwd", "sc_causal_conv_bwd_f32",
     "sc_causal_conv_bwd_bf16", "sc_causal_conv_bwd_ntt_i32", "sc_causal_conv_bwd_ex",
     "causal_conv_fixed", "sc_causal_conv_fixed_f32", "sc_causal_conv_fixed_f32_ws",
     "sc_fixed_range_ok", "filter_spectrum", "causal_conv_spec", "causal_conv_shared",
@@ -148,6 +148,8 @@ def _open():
     h.sc_status_string.restype = ctypes.c_char_p
     h.sc_version.argtypes = []
     h.sc_version.restype = ctypes.c_int
+    h.sc_prepare.argtypes = [st, i64]
+    h.sc_prepare.restype = st
     return h
 
 
@@ -325,6 +327,10 @@ def sc_status_string(status: int) -> str:
 
 def sc_version() -> int:
     return int(_lib.sc_version())
+
+
+def sc_prepare(kind, L):
+    return _lib.sc_prepare(kind, L)
 
 
 # ---------------------------------------------------------------- tensor front end

@@ -357,8 +357,9 @@ size_t fourstep_bytes_per_channel(int M)
 template <bool REV>
 static hipError_t launch_fourstep_rev(Store st, const void* v, const void* g, void* r, int64_t nch,
                                       int L, int M, int head, bool pair_store, const float2* bank,
-                                      const FsTw& tw, void* ws, int64_t chunk, hipStream_t stream,
-                                      hipStream_t side, hipEvent_t fork, hipEvent_t join)
+                                      const FsTw& tw, void* ws, size_t ws_bytes, int64_t chunk,
+                                      hipStream_t stream, hipStream_t side, hipEvent_t fork,
+                                      hipEvent_t join)
 {
     int M1, M2;
     fourstep_split(M, &M1, &M2);
@@ -374,9 +375,15 @@ static hipError_t launch_fourstep_rev(Store st, const void* v, const void* g, vo
     int64_t i = 0;
     for (int64_t c0 = 0; c0 < nch && e == hipSuccess; c0 += part, ++i) {
         const int nc = (int)((nch - c0) < part ? (nch - c0) : part);
-        const hipStream_t s = (i & 1) ? side : stream;
-        float2* T = (float2*)ws + (size_t)(i & 1) * (size_t)part * 3 * M;
+        // one stream: every part on `stream`, all in the first `chunk` channels of scratch
+        const int half = side ? (int)(i & 1) : 0;
+        const hipStream_t s = half ? side : stream;
+        float2* T = (float2*)ws + (size_t)half * (size_t)part * 3 * M;
         float2* S = T + (size_t)part * 2 * M;
+        if ((size_t)(half + 1) * (size_t)part * fourstep_bytes_per_channel(M) > ws_bytes) {
+            e = hipErrorInvalidValue;
+            break;
+        }
         if (st == Store::F32)
             e = dispatch_cols<f32_io, REV>(true, M1, v, g, r, T, S, c0, nc, L, M2, head, pair_store,
                                            bank, tw, s);
@@ -419,13 +426,13 @@ static hipError_t launch_fourstep_rev(Store st, const void* v, const void* g, vo
 
 hipError_t launch_fourstep(Store st, const void* v, const void* g, void* r, int64_t nch, int L,
                            int M, int head, bool pair_store, bool rev, const float2* bank,
-                           const FsTw& tw, void* ws, int64_t chunk, hipStream_t stream,
-                           hipStream_t side, hipEvent_t fork, hipEvent_t join)
+                           const FsTw& tw, void* ws, size_t ws_bytes, int64_t chunk,
+                           hipStream_t stream, hipStream_t side, hipEvent_t fork, hipEvent_t join)
 {
     return rev ? launch_fourstep_rev<true>(st, v, g, r, nch, L, M, head, pair_store, bank, tw, ws,
-                                           chunk, stream, side, fork, join)
+                                           ws_bytes, chunk, stream, side, fork, join)
                : launch_fourstep_rev<false>(st, v, g, r, nch, L, M, head, pair_store, bank, tw, ws,
-                                            chunk, stream, side, fork, join);
+                                            ws_bytes, chunk, stream, side, fork, join);
 }
 
 }  // namespace sc

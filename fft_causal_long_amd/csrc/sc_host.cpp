@@ -117,12 +117,26 @@ float2 unit_root(int64_t k, int64_t n)
     return make_float2((float)std::cos(a), (float)-std::sin(a));
 }
 
-sc_status device_state(DeviceState** out, bool need_ntt)
+// Building a table is a blocking upload, which a stream under graph capture must not see:
+// with `stream` being captured, a missing table is SC_ERR_UNSUPPORTED (sc_prepare builds
+// the tables beforehand).
+sc_status capture_forbids_build(hipStream_t stream)
+{
+    hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(stream, &cap) != hipSuccess) return SC_ERR_HIP;
+    return cap == hipStreamCaptureStatusNone ? SC_OK : SC_ERR_UNSUPPORTED;
+}
+
+sc_status device_state(DeviceState** out, bool need_ntt, hipStream_t stream)
 {
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return SC_ERR_HIP;
     std::lock_guard<std::mutex> lk(g_mu);
     DeviceState& d = g_dev[dev];
+    if (!d.fused_tw || (need_ntt && !d.ntt_ready)) {
+        const sc_status cs = capture_forbids_build(stream);
+        if (cs != SC_OK) return cs;
+    }
     if (!d.fused_tw) {
         std::vector<float2> h(sc::FUSED_BANK_FLOAT2);
         for (int i = 0; i < sc::FUSED_TW_N; ++i) h[i] = unit_root(i, sc::FUSED_TW_N);
@@ -152,13 +166,15 @@ sc_status device_state(DeviceState** out, bool need_ntt)
 }
 
 // four-step twiddle tables for one M (built once per device and M)
-sc_status fourstep_tables(DeviceState& d, int M, sc::FsTw* out)
+sc_status fourstep_tables(DeviceState& d, int M, sc::FsTw* out, hipStream_t stream)
 {
     auto it = d.fs.find(M);
     if (it != d.fs.end()) {
         *out = it->second;
         return SC_OK;
     }
+    const sc_status cs = capture_forbids_build(stream);
+    if (cs != SC_OK) return cs;
     int M1, M2;
     sc::fourstep_split(M, &M1, &M2);
     const int64_t N = 2 * (int64_t)M, H = M2 / 2, U = M2 / 4 + 1;
@@ -362,7 +378,7 @@ sc_status run_jobs(sc_kind kind, const Job* jobs, int njobs, bool rev, int64_t n
     }
 
     DeviceState* d = nullptr;
-    st = device_state(&d, exact_kind(kind));
+    st = device_state(&d, exact_kind(kind), stream);
     if (st != SC_OK) return st;
 
     hipError_t e = hipSuccess;
@@ -406,7 +422,7 @@ sc_status run_jobs(sc_kind kind, const Job* jobs, int njobs, bool rev, int64_t n
         sc::FsTw tw;
         {
             std::lock_guard<std::mutex> lk(g_mu);
-            st = fourstep_tables(*d, M, &tw);
+            st = fourstep_tables(*d, M, &tw, stream);
         }
         if (st != SC_OK) return st;
         // two streams take alternate halves of the chunks (measured 1.54 -> 1.34 ms on the
@@ -426,7 +442,7 @@ sc_status run_jobs(sc_kind kind, const Job* jobs, int njobs, bool rev, int64_t n
         }
         for (int k = 0; k < njobs && e == hipSuccess; ++k)
             e = sc::launch_fourstep(s, jobs[k].a, jobs[k].b, jobs[k].o, nch, (int)L, M, head, pair,
-                                    rev, d->fused_tw, tw, scratch, chunk, stream,
+                                    rev, d->fused_tw, tw, scratch, need, chunk, stream,
                                     two ? d->fs_side : nullptr, two ? d->fs_fork : nullptr,
                                     two ? d->fs_join : nullptr);
         if (own && hipFreeAsync(scratch, stream) != hipSuccess && e == hipSuccess)
@@ -558,7 +574,7 @@ sc_status staged_run(sc_kind kind, bool tm, const void* v, const void* g, const 
         return SC_ERR_INVALID_ARGUMENT;
     }
     DeviceState* d = nullptr;
-    st = device_state(&d, exact_kind(kind));
+    st = device_state(&d, exact_kind(kind), stream);
     if (st != SC_OK) return st;
     void* base = ws;
     bool own = false;
@@ -636,7 +652,7 @@ sc_status gate_run(sc_kind kind, const void* s, const void* W, void* g, int64_t 
     if (overlaps(g, s, nbytes) || ranges_overlap(g, nbytes, W, wbytes))
         return SC_ERR_INVALID_ARGUMENT;
     DeviceState* d = nullptr;
-    st = device_state(&d, false);
+    st = device_state(&d, false, stream);
     if (st != SC_OK) return st;
     const sc::Store sk = kind == SC_KIND_F32 ? sc::Store::F32 : sc::Store::BF16;
     return sc::launch_gate(sk, false, s, W, g, B, C, C, L, C, stream) == hipSuccess ? SC_OK
@@ -914,7 +930,7 @@ sc_status spectrum_run(sc_kind kind, const void* k, void* spec, int64_t C, int64
     if ((uintptr_t)k < (uintptr_t)spec + sbytes && (uintptr_t)spec < (uintptr_t)k + C * L * es)
         return SC_ERR_INVALID_ARGUMENT;
     DeviceState* d = nullptr;
-    sc_status st = device_state(&d, false);
+    sc_status st = device_state(&d, false, stream);
     if (st != SC_OK) return st;
     const int M = (int)std::max<int64_t>(64, next_pow2(L));
     const sc::Store s = kind == SC_KIND_F32 ? sc::Store::F32 : sc::Store::BF16;
@@ -951,7 +967,7 @@ sc_status apply_run(sc_kind kind, const void* v, const void* spec, void* r, int6
                     int64_t L, hipStream_t stream, bool rev = false)
 {
     DeviceState* d = nullptr;
-    sc_status st = device_state(&d, false);
+    sc_status st = device_state(&d, false, stream);
     if (st != SC_OK) return st;
     const int M = (int)std::max<int64_t>(64, next_pow2(L));
     const sc::Store s = kind == SC_KIND_F32 ? sc::Store::F32 : sc::Store::BF16;
@@ -1016,6 +1032,8 @@ sc_status shared_bwd_run(sc_kind kind, const void* dr, const void* v, const void
                    ? SC_OK
                    : SC_ERR_HIP;
     }
+    // the row loops count batch rows in 32 bits
+    if (B > INT32_MAX) return SC_ERR_UNSUPPORTED;
     const void* filt = spec ? spec : k;
     if (!dr || !v || !filt || !dv || !dk) return SC_ERR_INVALID_ARGUMENT;
     if (((uintptr_t)dr | (uintptr_t)v | (uintptr_t)dv | (uintptr_t)dk) % es)
@@ -1033,7 +1051,7 @@ sc_status shared_bwd_run(sc_kind kind, const void* dr, const void* v, const void
     if ((uintptr_t)dv < (uintptr_t)dk + kb && (uintptr_t)dk < (uintptr_t)dv + nb)
         return SC_ERR_INVALID_ARGUMENT;
     DeviceState* d = nullptr;
-    st = device_state(&d, false);
+    st = device_state(&d, false, stream);
     if (st != SC_OK) return st;
     void* own = nullptr;
     if (!spec) {
@@ -1045,7 +1063,7 @@ sc_status shared_bwd_run(sc_kind kind, const void* dr, const void* v, const void
     if (st == SC_OK) {
         const int M = (int)std::max<int64_t>(64, next_pow2(L));
         const sc::Store s = kind == SC_KIND_F32 ? sc::Store::F32 : sc::Store::BF16;
-        if (B <= INT32_MAX && sc::shared_bwd_blocks(C, M) >= kSharedBwdMinBlocks) {
+        if (sc::shared_bwd_blocks(C, M) >= kSharedBwdMinBlocks) {
             // one kernel: dv and dk from the same transform per row
             const bool pair = L % 2 == 0 && ((uintptr_t)dk | (uintptr_t)dv) % (2 * es) == 0;
             if (sc::launch_shared_bwd(s, dr, v, (const float2*)spec, dv, dk, (int)B, (int)C,
@@ -1170,6 +1188,24 @@ const char* sc_status_string(sc_status s)
     }
 }
 
-int sc_version(void) { return 700; }
+sc_status sc_prepare(sc_kind kind, int64_t L)
+{
+    return guarded([&] {
+        int64_t n = 0;
+        sc_status st = check_shape(kind, 1, 1, L, &n);
+        if (st != SC_OK) return st;
+        if (L == 0) return SC_OK;   // such a call enqueues nothing and needs no table
+        sc_path path;
+        if ((st = resolve_path(kind, L, SC_PATH_AUTO, &path)) != SC_OK) return st;
+        DeviceState* d = nullptr;
+        st = device_state(&d, exact_kind(kind), nullptr);
+        if (st != SC_OK || path != SC_PATH_FOUR_STEP) return st;
+        sc::FsTw tw;
+        std::lock_guard<std::mutex> lk(g_mu);
+        return fourstep_tables(*d, (int)next_pow2(L), &tw, nullptr);
+    });
+}
+
+int sc_version(void) { return 800; }
 
 }  // extern "C"

@@ -86,15 +86,18 @@ inline bool grid_ok(int64_t blocks, int64_t threads)
 
 void fourstep_split(int M, int* M1, int* M2);
 size_t fourstep_bytes_per_channel(int M);
-// ws holds chunk channels of scratch (chunk * fourstep_bytes_per_channel(M) bytes).  With a
-// second stream `side` (and two events, fork and join), the channels go in parts of chunk/2
-// that alternate between the two streams, each part with its own half of ws: side waits
-// for stream at the start (fork) and stream for side at the end (join), so the call stays
-// ordered on `stream` as a whole.
+// ws holds ws_bytes >= chunk * fourstep_bytes_per_channel(M) bytes of scratch.  Without a
+// second stream (side null) the channels go in parts of chunk, one after the other on
+// `stream`, each reusing the start of ws.  With a second stream `side` (and two events,
+// fork and join), the parts are chunk/2 channels that alternate between the two streams,
+// each stream with its own half of ws: side waits for stream at the start (fork) and stream
+// for side at the end (join), so the call stays ordered on `stream` as a whole.  A part
+// whose scratch would end past ws_bytes is refused (hipErrorInvalidValue) before launch.
 hipError_t launch_fourstep(Store st, const void* v, const void* g, void* r, int64_t nch, int L,
                            int M, int head, bool pair_store, bool rev, const float2* bank,
-                           const FsTw& tw, void* ws, int64_t chunk, hipStream_t stream,
-                           hipStream_t side, hipEvent_t fork, hipEvent_t join);
+                           const FsTw& tw, void* ws, size_t ws_bytes, int64_t chunk,
+                           hipStream_t stream, hipStream_t side, hipEvent_t fork,
+                           hipEvent_t join);
 
 // ---- filter shared by the batch (L <= FUSED_MAX_L, M = max(64, next power of two >= L))
 // Spectrum of the filters k[C][L]: shared_spec_stride(M) float2 per channel.

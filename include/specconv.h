@@ -33,13 +33,21 @@
  *      B, C or L negative, a null pointer with B*C*L > 0, a pointer not aligned to its
  *      element size, r overlapping v or g, byte sizes overflowing int64
  *                                              -> SC_ERR_INVALID_ARGUMENT
- *      B*C*L == 0                              -> SC_OK, nothing enqueued
+ *      B*C*L == 0                              -> SC_OK, nothing enqueued (one exception:
+ *                                                 the shared-filter gradients of an empty
+ *                                                 batch, B == 0 < C*L, set dk to zero with
+ *                                                 a fill kernel and need a valid dk)
  *      L above the path's maximum               -> SC_ERR_UNSUPPORTED
  *      a workspace smaller than required        -> SC_ERR_WORKSPACE
  *      a failed HIP call or kernel launch       -> SC_ERR_HIP
- *  - Library-owned state: per-device constant tables (twiddles, modular constants), built on
- *    the first call on a device (a blocking host-to-device copy) and kept until the process
- *    ends; and, for the four-step path (L > 4096), a second stream and two events per
+ *  - Library-owned state: per-device constant tables, each built by the first call on a
+ *    device that needs it (a blocking host-to-device copy) and kept until the process ends:
+ *    the float twiddle bank (every call), the modular tables (the first call of an exact
+ *    kind: SC_KIND_NTT_I32 or SC_KIND_FIXED_F32), and the four-step tables (the first
+ *    four-step call at each transform length M = next power of two >= L).  A call whose
+ *    `stream` is being captured into a graph and that would have to build a table returns
+ *    SC_ERR_UNSUPPORTED and enqueues nothing; sc_prepare builds them beforehand.  Also,
+ *    for the four-step path (L > 4096), a second stream and two events per
  *    device, made on first use: such a call may run half of its channel chunks on that
  *    stream, which waits for `stream` at the start of the call, and `stream` waits for it
  *    at the end, so the call stays ordered on `stream` as a whole.  While `stream` is being
@@ -393,7 +401,18 @@ int sc_ntt_range_ok(int64_t max_abs_v, int64_t max_abs_g, int64_t L);
 /* Human-readable name of a status code (static storage).  Host only. */
 const char* sc_status_string(sc_status s);
 
-/* Library version: major * 10000 + minor * 100 + patch (this header: 700).  Host only. */
+/*
+ * sc_prepare -- builds, on the current device, every constant table that a call of this
+ *   kind and length needs (see "Library-owned state" above), so that such calls can then be
+ *   captured into a graph.  Blocking (host-to-device copies on the null stream); call it
+ *   outside any capture.  Returns SC_ERR_UNSUPPORTED for a length the kind does not support,
+ *   SC_ERR_INVALID_ARGUMENT for a bad kind or L < 0, SC_ERR_HIP if an allocation or copy
+ *   fails; L == 0 needs no table (SC_OK, nothing done).  Safe to call repeatedly and from
+ *   several host threads.
+ */
+sc_status sc_prepare(sc_kind kind, int64_t L);
+
+/* Library version: major * 10000 + minor * 100 + patch (this header: 800).  Host only. */
 int sc_version(void);
 
 #ifdef __cplusplus

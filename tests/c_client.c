@@ -17,7 +17,7 @@ static int fails = 0;
 
 int main(void)
 {
-    CHECK(sc_version() >= 700);
+    CHECK(sc_version() >= 800);
     CHECK(strcmp(sc_status_string(SC_OK), "SC_OK") == 0);
     /* negative sizes and null pointers with work to do are rejected on the host */
     CHECK(sc_causal_conv_f32(0, 0, 0, -1, 1, 1, 0) == SC_ERR_INVALID_ARGUMENT);

@@ -117,7 +117,13 @@ def test_host_helpers(sc):
     assert sc.sc_status_string(0) == "SC_OK"
     assert sc.sc_status_string(4) == "SC_ERR_WORKSPACE"
     assert sc.sc_status_string(99) == "SC_STATUS_UNKNOWN"
-    assert sc.sc_version() >= 100
+    assert sc.sc_version() >= 800
+    # sc_prepare: argument checks on the host; an empty length needs no table
+    assert sc.sc_prepare(7, 64) == sc.SC_ERR_INVALID_ARGUMENT
+    assert sc.sc_prepare(sc.KIND_F32, -1) == sc.SC_ERR_INVALID_ARGUMENT
+    assert sc.sc_prepare(sc.KIND_NTT_I32, 5000) == sc.SC_ERR_UNSUPPORTED
+    assert sc.sc_prepare(sc.KIND_F32, 2**22 + 1) == sc.SC_ERR_UNSUPPORTED
+    assert sc.sc_prepare(sc.KIND_BF16, 0) == sc.SC_OK
     assert sc.sc_workspace_bytes(sc.KIND_F32, 8, 1024, 4096) == 0
     # four-step lengths need scratch; the exact path and bad shapes need none
     assert sc.sc_workspace_bytes(sc.KIND_F32, 1, 1536, 65536) > 0
@@ -274,6 +280,11 @@ def test_shared_filter_bwd_host_checks(sc):
         assert f(None, None, None, None, None, 0, 4, 64, None) == INVALID, name
         assert f(None, None, None, None, E_ + 1, 0, 4, 64, None) == INVALID, name
     assert h.sc_causal_conv_spec_bwd_f32(A, B_, C_ + 4, D_, E_, 2, 4, 64, None) == INVALID
+    # the row loops count batch rows in 32 bits: B = 2^31 (4 GB of bf16 at C = L = 1) is
+    # refused before any HIP call instead of being truncated
+    big = [k << 40 for k in range(1, 6)]
+    for name in ("sc_causal_conv_spec_bwd_bf16", "sc_causal_conv_shared_bwd_bf16"):
+        assert getattr(h, name)(*big, 1 << 31, 1, 1, None) == UNSUP, name
     assert h.sc_causal_conv_shared_bwd_f32(1 << 40, 2 << 40, 3 << 40, 4 << 40, 5 << 40, 1,
                                            1 << 19, 4096, None) == UNSUP
 

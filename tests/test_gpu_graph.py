@@ -140,3 +140,69 @@ def test_gradient_and_empty_batch_calls_in_a_graph(sc):
         assert torch.equal(dv.view(torch.int16), rdv.view(torch.int16)), i
         assert torch.equal(dg.view(torch.int16), rdg.view(torch.int16)), i
         assert int(torch.count_nonzero(dk)) == 0, i
+
+
+def test_four_step_call_of_several_parts_in_a_graph(sc):
+    # under capture the four-step path stays on the capturing stream; with more channels than
+    # one chunk its parts run one after the other and reuse the start of the workspace, which
+    # is sized exactly (no slack past what the call needs): every replay gives the eager bits
+    L = 16384
+    per = sc.sc_workspace_bytes(sc.KIND_F32, 1, 1, L)
+    chunk = sc.sc_workspace_bytes(sc.KIND_F32, 1, 10**6, L) // per
+    C = chunk + 44
+    v, g = make_inputs(WORKLOADS[4], B=1, C=C, L=L, seed_offset=66)
+    vd, gd = to_device(v), to_device(g)
+    need = sc.sc_workspace_bytes(sc.KIND_F32, 1, C, L)
+    assert need == chunk * per
+    ws = torch.empty(need, dtype=torch.uint8, device="cuda:0")
+    ref = sc.causal_conv(vd, gd, workspace=ws)
+    out = torch.empty_like(ref)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    print("case graph four-step parts C=%d chunk=%d L=%d" % (C, chunk, L), flush=True)
+    with torch.cuda.stream(side):
+        sc.causal_conv(vd, gd, out=out, workspace=ws)
+        torch.cuda.synchronize()
+        with torch.cuda.graph(graph, stream=side):
+            sc.causal_conv(vd, gd, out=out, workspace=ws)
+    torch.cuda.synchronize()
+    replay_check(graph, out, ref,
+                 lambda i: sc.causal_conv(vd, gd, out=torch.empty_like(vd), workspace=ws))
+
+
+def test_capture_needing_a_new_table_is_refused_until_prepared(sc):
+    # the four-step tables for M = 2^21 are built by no other test: captured before
+    # sc_prepare, the call must refuse (nothing enqueued, the capture stays valid); after
+    # sc_prepare the same capture succeeds and replays give the eager bits
+    L = (1 << 20) + 3
+    v, g = make_inputs(WORKLOADS[4], B=1, C=2, L=L, seed_offset=67)
+    vd, gd = to_device(v), to_device(g)
+    need = sc.sc_workspace_bytes(sc.KIND_F32, 1, 2, L)
+    ws = torch.empty(need, dtype=torch.uint8, device="cuda:0")
+    out = torch.empty_like(vd)
+    fn = sc.lib().sc_causal_conv_f32_ws
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    torch.cuda.synchronize()
+    print("case graph refused before sc_prepare L=%d" % L, flush=True)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(graph, stream=side):
+            st = fn(vd.data_ptr(), gd.data_ptr(), out.data_ptr(), 1, 2, L, ws.data_ptr(), need,
+                    side.cuda_stream)
+            torch.mul(vd, 1, out=out)          # keeps the captured graph non-empty
+    torch.cuda.synchronize()
+    assert st == sc.SC_ERR_UNSUPPORTED
+    assert sc.sc_prepare(sc.KIND_F32, L) == sc.SC_OK
+    ref = sc.causal_conv(vd, gd, workspace=ws)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(graph, stream=side):
+            st = fn(vd.data_ptr(), gd.data_ptr(), out.data_ptr(), 1, 2, L, ws.data_ptr(), need,
+                    side.cuda_stream)
+    torch.cuda.synchronize()
+    assert st == sc.SC_OK
+    replay_check(graph, out, ref, lambda i: torch.mul(vd, 1, out=torch.empty_like(vd)))
