@@ -12,6 +12,11 @@ def test_presets_match_shapes():
     assert (w[3].B, w[3].C, w[3].L, w[3].storage, w[3].groups) == (8, 1024, 4096, "bf16", 16)
     assert (w[4].B, w[4].C, w[4].L) == (1, 1536, 65536)
     assert (w[5].B, w[5].C, w[5].L, w[5].storage) == (4, 768, 4096, "i32")
+    assert (w[6].B, w[6].C, w[6].L, w[6].storage, w[6].cid) == (8, 1024, 4096, "f32", 3)
+    # workload 6 stores the draws of workload 3 in fp32: rounding them gives 3's bf16 bits
+    v6, g6 = make_inputs(w[6], B=1, C=16, L=256)
+    v3, g3 = make_inputs(w[3], B=1, C=16, L=256)
+    assert np.array_equal(f32_to_bf16_bits(v6), v3) and np.array_equal(f32_to_bf16_bits(g6), g3)
 
 
 def test_deterministic_and_seed_families_differ():
