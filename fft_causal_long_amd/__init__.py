@@ -12,7 +12,8 @@ There is no CPU fallback: if the library is missing, importing this package fail
 Public names mirror the C ABI of ``include/specconv.h``:
 ``sc_causal_conv_f32``, ``sc_causal_conv_bf16``, ``sc_causal_conv_ntt_i32``, their
 ``_ws`` variants, ``sc_causal_conv_ex``, ``sc_workspace_bytes``, ``sc_ntt_range_ok``,
-``sc_status_string``, ``sc_version``, ``sc_prepare``, and the gradient calls ``sc_causal_conv_bwd_f32``,
+``sc_status_string``, ``sc_version``, ``sc_prepare``, ``sc_causal_conv_noalloc`` (no
+allocation: a static device scratch), and the gradient calls ``sc_causal_conv_bwd_f32``,
 ``sc_causal_conv_bwd_bf16``, ``sc_causal_conv_bwd_ntt_i32``, ``sc_causal_conv_bwd_ex``; plus
 :func:`causal_conv` and :func:`causal_conv_bwd`, which dispatch on dtype; the exactly causal
 real-valued calls ``sc_causal_conv_fixed_f32``, ``sc_causal_conv_fixed_f32_ws``,
@@ -32,7 +33,8 @@ __all__ = [
     "SpecConvError", "lib", "causal_conv", "sc_causal_conv_f32", "sc_causal_conv_bf16",
     "sc_causal_conv_ntt_i32", "sc_causal_conv_f32_ws", "sc_causal_conv_bf16_ws",
     "sc_causal_conv_ntt_i32_ws", "sc_causal_conv_ex", "sc_workspace_bytes", "sc_ntt_range_ok",
-    "sc_status_string", "sc_version", "sc_prepare", "causal_conv_bwd", "sc_causal_conv_bwd_f32",
+    "sc_status_string", "sc_version", "sc_prepare", "sc_causal_conv_noalloc",
+    "causal_conv_bwd", "sc_causal_conv_bwd_f32",
     "sc_causal_conv_bwd_bf16", "sc_causal_conv_bwd_ntt_i32", "sc_causal_conv_bwd_ex",
     "causal_conv_fixed", "sc_causal_conv_fixed_f32", "sc_causal_conv_fixed_f32_ws",
     "sc_fixed_range_ok", "filter_spectrum", "causal_conv_spec", "causal_conv_shared",
@@ -150,6 +152,8 @@ def _open():
     h.sc_version.restype = ctypes.c_int
     h.sc_prepare.argtypes = [st, i64]
     h.sc_prepare.restype = st
+    h.sc_causal_conv_noalloc.argtypes = [st, vp, vp, vp, i64, i64, i64, vp]
+    h.sc_causal_conv_noalloc.restype = st
     return h
 
 
@@ -331,6 +335,10 @@ def sc_version() -> int:
 
 def sc_prepare(kind, L):
     return _lib.sc_prepare(kind, L)
+
+
+def sc_causal_conv_noalloc(kind, v, g, r, B, C, L, stream):
+    return _lib.sc_causal_conv_noalloc(kind, v, g, r, B, C, L, stream)
 
 
 # ---------------------------------------------------------------- tensor front end

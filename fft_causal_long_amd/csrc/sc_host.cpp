@@ -11,6 +11,9 @@
 
 #include "sc_internal.h"
 
+static_assert(SC_NOALLOC_SCRATCH_BYTES == sc::STATIC_SCRATCH_BYTES,
+              "the header states the static scratch size");
+
 namespace {
 
 constexpr int kMaxDevices = 64;
@@ -127,13 +130,15 @@ sc_status capture_forbids_build(hipStream_t stream)
     return cap == hipStreamCaptureStatusNone ? SC_OK : SC_ERR_UNSUPPORTED;
 }
 
-sc_status device_state(DeviceState** out, bool need_ntt, hipStream_t stream)
+sc_status device_state(DeviceState** out, bool need_ntt, hipStream_t stream,
+                       bool may_build = true)
 {
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return SC_ERR_HIP;
     std::lock_guard<std::mutex> lk(g_mu);
     DeviceState& d = g_dev[dev];
     if (!d.fused_tw || (need_ntt && !d.ntt_ready)) {
+        if (!may_build) return SC_ERR_UNSUPPORTED;
         const sc_status cs = capture_forbids_build(stream);
         if (cs != SC_OK) return cs;
     }
@@ -166,13 +171,15 @@ sc_status device_state(DeviceState** out, bool need_ntt, hipStream_t stream)
 }
 
 // four-step twiddle tables for one M (built once per device and M)
-sc_status fourstep_tables(DeviceState& d, int M, sc::FsTw* out, hipStream_t stream)
+sc_status fourstep_tables(DeviceState& d, int M, sc::FsTw* out, hipStream_t stream,
+                          bool may_build = true)
 {
     auto it = d.fs.find(M);
     if (it != d.fs.end()) {
         *out = it->second;
         return SC_OK;
     }
+    if (!may_build) return SC_ERR_UNSUPPORTED;
     const sc_status cs = capture_forbids_build(stream);
     if (cs != SC_OK) return cs;
     int M1, M2;
@@ -314,11 +321,12 @@ sc_status fourstep_streams(DeviceState& d)
 }
 
 // four-step scratch: channels per chunk and bytes needed
-void fourstep_plan(int64_t nch, int64_t L, int64_t* chunk, size_t* bytes)
+void fourstep_plan(int64_t nch, int64_t L, int64_t* chunk, size_t* bytes,
+                   int64_t budget = kFourStepChunkBytes)
 {
     const int M = (int)next_pow2(L);
     const int64_t per = (int64_t)sc::fourstep_bytes_per_channel(M);
-    int64_t c = kFourStepChunkBytes / per;
+    int64_t c = budget / per;
     if (c < 1) c = 1;
     if (c > nch) c = nch;
     *chunk = c;
@@ -335,9 +343,12 @@ struct Job {
 
 // Runs the jobs of one call (arguments already checked) on one path with one scratch area,
 // which the jobs use one after the other in stream order.
+// With noalloc (the allocation-free entry point): ws is the static scratch of ws_bytes,
+// four-step chunks are sized to it (a channel that does not fit is SC_ERR_UNSUPPORTED), the
+// call stays on `stream`, and a missing table is SC_ERR_UNSUPPORTED instead of being built.
 sc_status run_jobs(sc_kind kind, const Job* jobs, int njobs, bool rev, int64_t n, int64_t B,
                    int64_t C, int64_t L, const sc_options* opt, void* ws, size_t ws_bytes,
-                   hipStream_t stream)
+                   hipStream_t stream, bool noalloc = false)
 {
     int32_t req = SC_PATH_AUTO, head = kDefaultHead, fv = 0, fg = 0;
     if (opt) {
@@ -364,10 +375,14 @@ sc_status run_jobs(sc_kind kind, const Job* jobs, int njobs, bool rev, int64_t n
     // scratch of this path, checked against a caller workspace before any HIP call
     size_t need = 0;
     int64_t chunk = 0;
-    if (kind == SC_KIND_FIXED_F32)
+    if (kind == SC_KIND_FIXED_F32) {
         need = fixed_bytes(n);
-    else if (path == SC_PATH_FOUR_STEP)
-        fourstep_plan(nch, L, &chunk, &need);
+    } else if (path == SC_PATH_FOUR_STEP) {
+        if (noalloc &&
+            sc::fourstep_bytes_per_channel((int)next_pow2(L)) > (size_t)ws_bytes)
+            return SC_ERR_UNSUPPORTED;
+        fourstep_plan(nch, L, &chunk, &need, noalloc ? (int64_t)ws_bytes : kFourStepChunkBytes);
+    }
     if (need > 0) {
         if (ws) {
             if (ws_bytes < need) return SC_ERR_WORKSPACE;
@@ -378,7 +393,7 @@ sc_status run_jobs(sc_kind kind, const Job* jobs, int njobs, bool rev, int64_t n
     }
 
     DeviceState* d = nullptr;
-    st = device_state(&d, exact_kind(kind), stream);
+    st = device_state(&d, exact_kind(kind), stream, !noalloc);
     if (st != SC_OK) return st;
 
     hipError_t e = hipSuccess;
@@ -422,15 +437,17 @@ sc_status run_jobs(sc_kind kind, const Job* jobs, int njobs, bool rev, int64_t n
         sc::FsTw tw;
         {
             std::lock_guard<std::mutex> lk(g_mu);
-            st = fourstep_tables(*d, M, &tw, stream);
+            st = fourstep_tables(*d, M, &tw, stream, !noalloc);
         }
         if (st != SC_OK) return st;
         // two streams take alternate halves of the chunks (measured 1.54 -> 1.34 ms on the
         // long workload: one part's memory-bound column kernels overlap the other's rows),
-        // unless there is a single part or the caller's stream is being captured into a graph
+        // unless there is a single part, the caller's stream is being captured into a graph,
+        // or the call may not create the second stream (allocation-free entry point)
         hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
         if (hipStreamIsCapturing(stream, &cap) != hipSuccess) return SC_ERR_HIP;
-        const bool two = cap == hipStreamCaptureStatusNone && chunk >= 2 && nch > chunk / 2;
+        const bool two = !noalloc && cap == hipStreamCaptureStatusNone && chunk >= 2 &&
+                         nch > chunk / 2;
         if (two && (st = fourstep_streams(*d)) != SC_OK) return st;
         std::unique_lock<std::mutex> order(d->fs_mu, std::defer_lock);
         if (two) order.lock();
@@ -1186,6 +1203,28 @@ const char* sc_status_string(sc_status s)
     case SC_ERR_WORKSPACE: return "SC_ERR_WORKSPACE";
     default: return "SC_STATUS_UNKNOWN";
     }
+}
+
+sc_status sc_causal_conv_noalloc(sc_kind kind, const void* v, const void* g, void* r,
+                                 int64_t B, int64_t C, int64_t L, hipStream_t stream)
+{
+    return guarded([&] {
+        if (kind != SC_KIND_F32 && kind != SC_KIND_BF16 && kind != SC_KIND_NTT_I32)
+            return SC_ERR_INVALID_ARGUMENT;
+        int64_t n = 0;
+        sc_status st = check_args(kind, v, g, r, B, C, L, &n);
+        if (st != SC_OK) return st;
+        sc_path path;
+        if ((st = resolve_path(kind, L, SC_PATH_AUTO, &path)) != SC_OK) return st;
+        if (n == 0) return SC_OK;
+        void* ws = nullptr;
+        size_t ws_bytes = 0;
+        if (path == SC_PATH_FOUR_STEP &&
+            sc::static_scratch(&ws, &ws_bytes) != hipSuccess)
+            return SC_ERR_HIP;
+        const Job job{v, g, r};
+        return run_jobs(kind, &job, 1, false, n, B, C, L, nullptr, ws, ws_bytes, stream, true);
+    });
 }
 
 sc_status sc_prepare(sc_kind kind, int64_t L)

@@ -125,6 +125,12 @@ hipError_t launch_shared_bwd(Store st, const void* dr, const void* v, const floa
 // (no memset node, so the call can be captured into a graph)
 hipError_t launch_zero16(void* p, int64_t n16, hipStream_t stream);
 
+// The allocation-free entry point's scratch: a file-scope device array of STATIC_SCRATCH_BYTES
+// per device.  *ptr receives its address on the current device (looked up once per device);
+// every call on a device shares it.
+constexpr size_t STATIC_SCRATCH_BYTES = (size_t)64 << 20;
+hipError_t static_scratch(void** ptr, size_t* bytes);
+
 // Direct summation r_t = sum_{j<=t} v_j g_{t-j} in fp32, one thread per output.
 hipError_t launch_direct(Store st, const void* v, const void* g, void* r, int64_t nch, int L,
                          bool rev, hipStream_t stream);

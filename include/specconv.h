@@ -402,6 +402,27 @@ int sc_ntt_range_ok(int64_t max_abs_v, int64_t max_abs_g, int64_t L);
 const char* sc_status_string(sc_status s);
 
 /*
+ * sc_causal_conv_noalloc -- sc_causal_conv_ex(kind, v, g, r, B, C, L, NULL, ...) for the
+ *   kinds SC_KIND_F32, SC_KIND_BF16 and SC_KIND_NTT_I32, for callers that cannot allocate
+ *   device memory (code under graph capture, tight serving loops, harnesses that forbid
+ *   allocation).  The call allocates nothing and creates nothing: the scratch of the
+ *   four-step path (L > 4096) is a static device array of SC_NOALLOC_SCRATCH_BYTES, one per
+ *   GPU, held from the library's load until the process ends; the call stays on `stream`
+ *   (no second stream); the constant tables must already exist on the device (made by
+ *   sc_prepare(kind, L) or by any earlier call of that kind and transform length),
+ *   otherwise SC_ERR_UNSUPPORTED and nothing is enqueued.  A length whose four-step scratch
+ *   for one channel exceeds SC_NOALLOC_SCRATCH_BYTES (L > 2,097,152) is SC_ERR_UNSUPPORTED;
+ *   more channels than the array holds at once run as several parts on `stream`.
+ *   SC_KIND_FIXED_F32 is SC_ERR_INVALID_ARGUMENT.  Results are bitwise those of
+ *   sc_causal_conv_ex with the same arguments.  Every call on one GPU uses the same array:
+ *   calls that may overlap on one GPU (other streams, other host threads) race and must be
+ *   ordered by the caller.
+ */
+#define SC_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+sc_status sc_causal_conv_noalloc(sc_kind kind, const void* v, const void* g, void* r, int64_t B,
+                                 int64_t C, int64_t L, hipStream_t stream);
+
+/*
  * sc_prepare -- builds, on the current device, every constant table that a call of this
  *   kind and length needs (see "Library-owned state" above), so that such calls can then be
  *   captured into a graph.  Blocking (host-to-device copies on the null stream); call it
