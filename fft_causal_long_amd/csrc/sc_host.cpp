@@ -51,6 +51,8 @@ struct DeviceState {
     float2* fused_tw = nullptr;   // the float twiddle bank (sc_internal.h)
     sc::NttTables ntt[3]{};       // primes A, B, C (sc::NTT_PRIMES)
     bool ntt_ready = false;
+    sc::NttMfmaTables mfma{};     // the matrix-core NTT kernel's tables (prime A)
+    bool mfma_ready = false;
     std::map<int, sc::FsTw> fs;     // four-step tables by M
     // the four-step path's second stream (default priority, non-blocking) and its fork/join
     // events; fs_mu keeps one call's fork, launches and join together, since the events are
@@ -101,6 +103,93 @@ sc_status build_ntt_tables(sc::NttTables* t, uint64_t p)
         t->ninv[k] = (double)ninv;
         t->ninv_q[k] = (double)ninv / (double)p;
     }
+    return SC_OK;
+}
+
+// The int8 matrix-core NTT kernel's tables (layouts in sc_internal.h), one upload.
+sc_status build_mfma_tables(sc::NttMfmaTables* t)
+{
+    const uint64_t p = sc::NTT_PRIMES[0];
+    const size_t digit_bytes = 4 * 16 * 64 * 16;   // per matrix
+    size_t ntw = 0, nroot = 0;
+    for (int lg = 0; lg <= 6; ++lg) {
+        ntw += 2 * (size_t)64 * ((size_t)1 << lg);
+        nroot += (size_t)128 << lg;
+    }
+    const size_t dbytes = 14 * digit_bytes;
+    std::vector<unsigned char> h(dbytes + (ntw + nroot) * 2 * sizeof(double));
+    int8_t* dig = (int8_t*)h.data();
+    double* tw = (double*)(h.data() + dbytes);
+    size_t toff[2][7], roff[7], pos = 0;
+    for (int d = 0; d < 2; ++d)
+        for (int lg = 0; lg <= 6; ++lg) {
+            toff[d][lg] = pos;
+            pos += (size_t)64 << lg;
+        }
+    for (int lg = 0; lg <= 6; ++lg) {
+        roff[lg] = pos;
+        pos += (size_t)128 << lg;
+    }
+    for (int d = 0; d < 2; ++d)
+        for (int lg = 0; lg <= 6; ++lg) {
+            const uint64_t M2 = (uint64_t)1 << lg, M = 64 * M2;
+            // the M2-point DFT matrix (zero-padded), then the digits of 256^b F mod p
+            const uint64_t wm2 = powmod(3, (p - 1) / M2, p);
+            const uint64_t w2 = d ? powmod(wm2, p - 2, p) : wm2;
+            int8_t* out = dig + (size_t)(d * 7 + lg) * digit_bytes;
+            for (uint64_t k = 0; k < 64; ++k)
+                for (uint64_t n = 0; n < 64; ++n) {
+                    const uint64_t f = (k < M2 && n < M2) ? powmod(w2, k * n, p) : 0;
+                    const int w = (int)(k / 16), lane = (int)(k % 16 + 16 * (n / 16));
+                    const int j = (int)(n % 16);
+                    uint64_t fb = f;   // 256^b F mod p
+                    for (int b = 0; b < 4; ++b, fb = fb * 256 % p) {
+                        // balanced base-256 digits: fb = sum_a dg_a 256^a, dg in [-128, 127]
+                        int64_t y = (int64_t)fb;
+                        for (int a = 0; a < 4; ++a) {
+                            int dg = (int)(y & 255);
+                            if (dg >= 128) dg -= 256;
+                            y = (y - dg) >> 8;
+                            out[(((size_t)w * 16 + 4 * a + b) * 64 + lane) * 16 + j] = (int8_t)dg;
+                        }
+                    }
+                }
+            // twiddles omega_M^{+-n2 k1}
+            const uint64_t wm = powmod(3, (p - 1) / M, p);
+            const uint64_t wt = d ? powmod(wm, p - 2, p) : wm;
+            for (uint64_t k1 = 0; k1 < 64; ++k1)
+                for (uint64_t n2 = 0; n2 < M2; ++n2) {
+                    const uint64_t x = powmod(wt, k1 * n2, p);
+                    double* e = tw + 2 * (toff[d][lg] + k1 * M2 + n2);
+                    e[0] = (double)x;
+                    e[1] = (double)x / (double)p;
+                }
+        }
+    for (int lg = 0; lg <= 6; ++lg) {
+        const uint64_t N = (uint64_t)128 << lg;
+        const uint64_t wn = powmod(3, (p - 1) / N, p);
+        uint64_t x = 1;
+        for (uint64_t i = 0; i < N; ++i) {
+            double* e = tw + 2 * (roff[lg] + i);
+            e[0] = (double)x;
+            e[1] = (double)x / (double)p;
+            x = x * wn % p;
+        }
+        const uint64_t ninv = powmod(N % p, p - 2, p);
+        t->ninv[lg] = (double)ninv;
+        t->ninv_q[lg] = (double)ninv / (double)p;
+    }
+    void* dev = nullptr;
+    const sc_status st = upload(h.data(), h.size(), &dev);
+    if (st != SC_OK) return st;
+    const unsigned char* base = (const unsigned char*)dev;
+    const double2* tb = (const double2*)(base + dbytes);
+    for (int d = 0; d < 2; ++d)
+        for (int lg = 0; lg <= 6; ++lg) {
+            t->digits[d][lg] = (const int8_t*)(base + (size_t)(d * 7 + lg) * digit_bytes);
+            t->twiddle[d][lg] = tb + toff[d][lg];
+        }
+    for (int lg = 0; lg <= 6; ++lg) t->roots[lg] = tb + roff[lg];
     return SC_OK;
 }
 
@@ -292,6 +381,10 @@ sc_status resolve_path(sc_kind kind, int64_t L, int32_t requested, sc_path* out)
         if (!fl || L < kMinLFourStep || L > sc::FOURSTEP_MAX_L) return SC_ERR_UNSUPPORTED;
         *out = SC_PATH_FOUR_STEP;
         return SC_OK;
+    case SC_PATH_NTT_MFMA:
+        if (kind != SC_KIND_NTT_I32 || L > kMaxLNtt) return SC_ERR_UNSUPPORTED;
+        *out = SC_PATH_NTT_MFMA;
+        return SC_OK;
     default:
         return SC_ERR_INVALID_ARGUMENT;
     }
@@ -411,6 +504,22 @@ sc_status run_jobs(sc_kind kind, const Job* jobs, int njobs, bool rev, int64_t n
                                  d->ntt, stream);
         if (own && hipFreeAsync(scratch, stream) != hipSuccess && e == hipSuccess)
             e = hipErrorUnknown;
+        return e == hipSuccess ? SC_OK : SC_ERR_HIP;
+    }
+    if (kind == SC_KIND_NTT_I32 && path == SC_PATH_NTT_MFMA) {
+        {
+            std::lock_guard<std::mutex> lk(g_mu);
+            if (!d->mfma_ready) {
+                if (noalloc) return SC_ERR_UNSUPPORTED;
+                if ((st = capture_forbids_build(stream)) != SC_OK) return st;
+                if ((st = build_mfma_tables(&d->mfma)) != SC_OK) return st;
+                d->mfma_ready = true;
+            }
+        }
+        const int M = (int)std::max<int64_t>(64, next_pow2(L));
+        for (int k = 0; k < njobs && e == hipSuccess; ++k)
+            e = sc::launch_ntt_mfma((const int32_t*)jobs[k].a, (const int32_t*)jobs[k].b,
+                                    (int32_t*)jobs[k].o, nch, (int)L, M, rev, d->mfma, stream);
         return e == hipSuccess ? SC_OK : SC_ERR_HIP;
     }
     if (kind == SC_KIND_NTT_I32) {

@@ -90,13 +90,17 @@ typedef enum sc_path {
     SC_PATH_AUTO = 0,      /* the library's choice (below)                         */
     SC_PATH_FUSED = 1,     /* one workgroup per channel, transform held in LDS     */
     SC_PATH_FOUR_STEP = 2, /* column / twiddle / row transforms staged through HBM  */
-    SC_PATH_DIRECT = 3     /* direct fp32 summation (float kinds, small L only)     */
+    SC_PATH_DIRECT = 3,    /* direct fp32 summation (float kinds, small L only)     */
+    SC_PATH_NTT_MFMA = 4   /* SC_KIND_NTT_I32, L <= 4096: the transform stages as int8
+                              matrix products on the matrix cores (the integer-matrix
+                              formulation of "Catastrophic Token Leakage ...", abstract);
+                              the same result bits as SC_PATH_FUSED                  */
 } sc_path;
 
 /* Optional controls for sc_causal_conv_ex (testing and experiments). */
 typedef struct sc_options {
     int32_t path;      /* sc_path; SC_PATH_AUTO picks: L <= 32 direct, L <= 4096 fused,
-                          larger L four-step                                          */
+                          larger L four-step (the exact kinds: fused)                 */
     int32_t head;      /* float kinds: outputs t < head are computed by direct fp32
                           summation instead of the transform.  -1 = default (32);
                           0 disables; odd values are rounded up to even; at most 64.  */
