@@ -116,10 +116,10 @@ sc_status build_mfma_tables(sc::NttMfmaTables* t)
         ntw += 2 * (size_t)64 * ((size_t)1 << lg);
         nroot += (size_t)128 << lg;
     }
-    const size_t dbytes = 14 * digit_bytes;
-    std::vector<unsigned char> h(dbytes + (ntw + nroot) * 2 * sizeof(double));
+    const size_t dbytes = 15 * digit_bytes;   // 7 forward, 7 scaled inverse, the 64-point inverse
+    std::vector<unsigned char> h(dbytes + (ntw + nroot) * sizeof(uint32_t));
     int8_t* dig = (int8_t*)h.data();
-    double* tw = (double*)(h.data() + dbytes);
+    uint32_t* tw = (uint32_t*)(h.data() + dbytes);
     size_t toff[2][7], roff[7], pos = 0;
     for (int d = 0; d < 2; ++d)
         for (int lg = 0; lg <= 6; ++lg) {
@@ -131,15 +131,21 @@ sc_status build_mfma_tables(sc::NttMfmaTables* t)
         pos += (size_t)128 << lg;
     }
     for (int d = 0; d < 2; ++d)
-        for (int lg = 0; lg <= 6; ++lg) {
-            const uint64_t M2 = (uint64_t)1 << lg, M = 64 * M2;
-            // the M2-point DFT matrix (zero-padded), then the digits of 256^b F mod p
+        for (int lg = 0; lg <= 7; ++lg) {
+            if (d == 0 && lg == 7) continue;
+            // lg 7: the plain 64-point inverse matrix
+            const uint64_t M2 = (uint64_t)1 << (lg == 7 ? 6 : lg), M = 64 * M2;
+            const bool scaled = d == 1 && lg < 7;
+            // the M2-point DFT matrix (zero-padded; the inverse times N^{-1} except at lg 7),
+            // then the digits of 256^b F mod p
             const uint64_t wm2 = powmod(3, (p - 1) / M2, p);
             const uint64_t w2 = d ? powmod(wm2, p - 2, p) : wm2;
-            int8_t* out = dig + (size_t)(d * 7 + lg) * digit_bytes;
+            const uint64_t scale = scaled ? powmod(2 * M % p, p - 2, p) : 1;
+            int8_t* out = dig + (size_t)(lg == 7 ? 14 : d * 7 + lg) * digit_bytes;
             for (uint64_t k = 0; k < 64; ++k)
                 for (uint64_t n = 0; n < 64; ++n) {
-                    const uint64_t f = (k < M2 && n < M2) ? powmod(w2, k * n, p) : 0;
+                    const uint64_t f =
+                        (k < M2 && n < M2) ? powmod(w2, k * n, p) * scale % p : 0;
                     const int w = (int)(k / 16), lane = (int)(k % 16 + 16 * (n / 16));
                     const int j = (int)(n % 16);
                     uint64_t fb = f;   // 256^b F mod p
@@ -154,41 +160,34 @@ sc_status build_mfma_tables(sc::NttMfmaTables* t)
                         }
                     }
                 }
+            if (lg == 7) continue;
             // twiddles omega_M^{+-n2 k1}
             const uint64_t wm = powmod(3, (p - 1) / M, p);
             const uint64_t wt = d ? powmod(wm, p - 2, p) : wm;
             for (uint64_t k1 = 0; k1 < 64; ++k1)
-                for (uint64_t n2 = 0; n2 < M2; ++n2) {
-                    const uint64_t x = powmod(wt, k1 * n2, p);
-                    double* e = tw + 2 * (toff[d][lg] + k1 * M2 + n2);
-                    e[0] = (double)x;
-                    e[1] = (double)x / (double)p;
-                }
+                for (uint64_t n2 = 0; n2 < M2; ++n2)
+                    tw[toff[d][lg] + k1 * M2 + n2] = (uint32_t)powmod(wt, k1 * n2, p);
         }
     for (int lg = 0; lg <= 6; ++lg) {
         const uint64_t N = (uint64_t)128 << lg;
         const uint64_t wn = powmod(3, (p - 1) / N, p);
         uint64_t x = 1;
         for (uint64_t i = 0; i < N; ++i) {
-            double* e = tw + 2 * (roff[lg] + i);
-            e[0] = (double)x;
-            e[1] = (double)x / (double)p;
+            tw[roff[lg] + i] = (uint32_t)x;
             x = x * wn % p;
         }
-        const uint64_t ninv = powmod(N % p, p - 2, p);
-        t->ninv[lg] = (double)ninv;
-        t->ninv_q[lg] = (double)ninv / (double)p;
     }
     void* dev = nullptr;
     const sc_status st = upload(h.data(), h.size(), &dev);
     if (st != SC_OK) return st;
     const unsigned char* base = (const unsigned char*)dev;
-    const double2* tb = (const double2*)(base + dbytes);
+    const uint32_t* tb = (const uint32_t*)(base + dbytes);
     for (int d = 0; d < 2; ++d)
         for (int lg = 0; lg <= 6; ++lg) {
             t->digits[d][lg] = (const int8_t*)(base + (size_t)(d * 7 + lg) * digit_bytes);
             t->twiddle[d][lg] = tb + toff[d][lg];
         }
+    t->inv64 = (const int8_t*)(base + 14 * digit_bytes);
     for (int lg = 0; lg <= 6; ++lg) t->roots[lg] = tb + roff[lg];
     return SC_OK;
 }

@@ -56,17 +56,18 @@ hipError_t launch_ntt(const int32_t* v, const int32_t* g, int32_t* r, int64_t nc
 // Tables of the int8 matrix-core NTT kernel (sc_ntt_mfma.hip), modulo prime A, indexed by
 // lg = log2(M2) for M = 64 M2 (M2 = 1 .. 64), direction d (0 forward omega, 1 inverse omega^-1):
 //   digits[d][lg]   the M2-point DFT matrix F[k][n] = omega_M2^{+-k n} zero-padded to 64 x 64,
-//                   as signed base-256 digits f^(b)_a of F^(b) = 256^b F mod p, laid out
-//                   [w < 4][4 a + b][lane < 64][j < 16] = f^(b)_a[16 w + lane % 16][16 (lane / 16) + j]
-//                   (64 KB; lg = 6 is the 64-point matrix of the first stage)
-//   twiddle[d][lg]  {w, w / p} with w = omega_M^{+-n2 k1} at [k1 * M2 + n2], k1 < 64, n2 < M2
-//   roots[lg]       {w, w / p} with w = omega_N^i, i < N = 2 M
-//   ninv[lg]        N^{-1} mod p and ninv_q[lg] = ninv[lg] / p
+//                   the inverse one times N^{-1} (N = 2 M), as signed base-256 digits
+//                   f^(b)_a of F^(b) = 256^b F mod p, laid out [w < 4][4 a + b][lane < 64][j < 16]
+//                   = f^(b)_a[16 w + lane % 16][16 (lane / 16) + j] (64 KB; digits[0][6] is
+//                   also the 64-point forward matrix of the first stage)
+//   inv64           the 64-point inverse matrix omega_64^{-k n} (no N^{-1}), same layout
+//   twiddle[d][lg]  omega_M^{+-n2 k1} at [k1 * M2 + n2], k1 < 64, n2 < M2 (residue words)
+//   roots[lg]       omega_N^i, i < N = 2 M (residue words)
 struct NttMfmaTables {
     const int8_t* digits[2][7];
-    const double2* twiddle[2][7];
-    const double2* roots[7];
-    double ninv[7], ninv_q[7];
+    const int8_t* inv64;
+    const uint32_t* twiddle[2][7];
+    const uint32_t* roots[7];
 };
 
 // The exact int32 convolution mod prime A with the transform stages as int8 matrix products
