@@ -189,6 +189,11 @@ struct f32_io {
     {
         __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(x), s.rs, i * 4, 0, 0);
     }
+    // element i + j with j a uniform (scalar) offset
+    __device__ __forceinline__ static float load_at(const Span& s, int i, int j)
+    {
+        return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(s.rs, i * 4, j * 4, 0));
+    }
     // two consecutive outputs at element i (8-byte aligned)
     __device__ __forceinline__ static void store2(const Span& s, int i, float a, float b)
     {
@@ -218,6 +223,11 @@ struct bf16_io {
     __device__ __forceinline__ static void store(const Span& s, int i, float x)
     {
         __builtin_amdgcn_raw_buffer_store_b16((unsigned short)pack_bf16x2(x, 0.f), s.rs, i * 2, 0, 0);
+    }
+    __device__ __forceinline__ static float load_at(const Span& s, int i, int j)
+    {
+        const uint32_t w = __builtin_amdgcn_raw_buffer_load_b16(s.rs, i * 2, j * 2, 0);
+        return __uint_as_float(w << 16);
     }
     __device__ __forceinline__ static void store2(const Span& s, int i, float a, float b)
     {

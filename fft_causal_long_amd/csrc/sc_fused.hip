@@ -41,39 +41,12 @@ namespace sc {
 // threads of the workgroup for length-M transforms
 template <int M>
 constexpr int fused_threads() { return M / 8 > 64 ? M / 8 : 64; }
-constexpr int HEAD_MAX = 64;   // largest direct head (the host clamps to this)
 #ifndef SC_LDS_EXTRA
 #define SC_LDS_EXTRA 24
 #endif
 // extra float2 between the LDS regions of the two branches of a channel: with it the
 // unpack's alternating reads of u0[j] and u1[j] land in different banks
 constexpr int LDS_EXTRA = SC_LDS_EXTRA;
-
-// Direct fp32 head r_t = sum_{j<=t} v_j g_{t-j}, t < head, of ncl channels whose first
-// HEAD_MAX inputs are staged in hb (v then g per channel), by NT threads lt = 0..NT-1 made
-// of whole waves.  Each output's sum is split over S consecutive lanes (terms j = s, s + S,
-// ...; S <= 8, as many as the threads allow) and reduced with lane shuffles, so the head
-// costs a few dependent steps instead of up to HEAD_MAX.
-template <int NT, class Put>
-__device__ __forceinline__ void direct_head(const float* __restrict__ hb, int ncl, int nvalid,
-                                            int L, int head, int lt, const Put& put)
-{
-    const int nout = ncl * head;
-    int S = 1;
-    while (S < 8 && 2 * S * nout <= NT) S *= 2;
-    for (int base = 0; base < nout * S; base += NT) {
-        const int idx = base + lt, o = idx / S, s = idx - o * S;
-        const int c2 = o / head, t = o - c2 * head;
-        float acc = 0.f;
-        if (o < nout) {
-            const float* hv = hb + c2 * 2 * HEAD_MAX;
-            const float* hg = hv + HEAD_MAX;
-            for (int j = s; j <= t; j += S) acc = __builtin_fmaf(hv[j], hg[t - j], acc);
-        }
-        for (int d = 1; d < S; d <<= 1) acc += __shfl_xor(acc, d);
-        if (o < nout && s == 0 && c2 < nvalid && t < L) put(c2, t, acc);
-    }
-}
 
 template <int M, class IO, bool REV>
 __global__ __launch_bounds__(fused_threads<M>()) void fused_conv_kernel(

@@ -29,6 +29,11 @@ constexpr int64_t kMinLFourStep = 2049;  // the four-step split needs M >= 4096
 #endif
 constexpr int64_t kFourStepChunkBytes = (int64_t)SC_FS_CHUNK_MB << 20;
 constexpr int64_t kMaxLNtt = 4096;
+// M = 4096 float convolutions use the kernel of sc_fused4k.hip (0: the general fused kernel)
+#ifndef SC_FUSED4K
+#define SC_FUSED4K 1
+#endif
+constexpr bool kFused4k = SC_FUSED4K != 0;
 constexpr int64_t kNttP = 998244353;
 constexpr int32_t kMaxFrac = 64;          // |fixed-point fraction bits| of the exact real kind
 // the shared-filter gradients take the one-kernel path when it has at least this many
@@ -49,6 +54,7 @@ sc_status upload(const void* host, size_t bytes, void** dev)
 
 struct DeviceState {
     float2* fused_tw = nullptr;   // the float twiddle bank (sc_internal.h)
+    float2* dit4k = nullptr;      // the M = 4096 fused kernel's (c, t) table (sc_internal.h)
     sc::NttTables ntt[3]{};       // primes A, B, C (sc::NTT_PRIMES)
     bool ntt_ready = false;
     sc::NttMfmaTables mfma{};     // the matrix-core NTT kernel's tables (prime A)
@@ -192,6 +198,47 @@ sc_status build_mfma_tables(sc::NttMfmaTables* t)
     return SC_OK;
 }
 
+// T = c (1 + i t) for the unit root exp(-2 pi i e / n) (conjugated when inv), computed in
+// float64 and rounded once per component; c = 2^-40, t = +-2^40 stand in for c = 0
+float2 tan_pair(double e, double n, bool inv)
+{
+    const double a = 6.283185307179586476925286766559 * e / n;
+    const double c = std::cos(a), s = (inv ? 1.0 : -1.0) * std::sin(a);
+    if (std::fabs(c) < 0x1p-30) return make_float2(0x1p-40f, (float)(s * 0x1p40));
+    return make_float2((float)c, (float)(s / c));
+}
+
+// the pairs B, B^2, F_0, F_0^2, .., F_3, F_3^2 of a radix-16 item with twiddle base
+// A = exp(-+2 pi i a / n): B = A^4, F_p = A W16^{+-p}
+void item_pairs(float2* out, double a, double n, bool inv)
+{
+    out[0] = tan_pair(4 * a, n, inv);
+    out[1] = tan_pair(8 * a, n, inv);
+    for (int p = 0; p < 4; ++p) {
+        // A W16^p = exp(-2 pi i (a / n + p / 16))
+        const double e = a * 16.0 + p * n;   // over 16 n
+        out[2 + 2 * p] = tan_pair(e, 16 * n, inv);
+        out[3 + 2 * p] = tan_pair(2 * e, 16 * n, inv);
+    }
+}
+
+std::vector<float2> dit4k_table()
+{
+    std::vector<float2> h(sc::DIT4K_TABLE_FLOAT2, make_float2(0.f, 0.f));
+    item_pairs(&h[sc::DIT4K_P1B1], 1, 32, false);
+    for (int var = 0; var < 3; ++var) {
+        const bool inv = var == 2;
+        for (int j = 0; j < 16; ++j)
+            item_pairs(&h[sc::DIT4K_P2 + (var * 16 + j) * 10], var == 1 ? 2 * j + 1 : j,
+                       var == 1 ? 512 : 256, inv);
+        for (int j = 0; j < 256; ++j)
+            item_pairs(&h[sc::DIT4K_P3 + (var * 256 + j) * 10], var == 1 ? 2 * j + 1 : j,
+                       var == 1 ? 8192 : 4096, inv);
+    }
+    for (int k = 0; k < 4096; ++k) h[sc::DIT4K_UNP + k] = tan_pair(k, 8192, true);
+    return h;
+}
+
 std::mutex g_mu;
 DeviceState g_dev[kMaxDevices];
 
@@ -245,6 +292,13 @@ sc_status device_state(DeviceState** out, bool need_ntt, hipStream_t stream,
         void* p = nullptr;
         sc_status st = upload(h.data(), h.size() * sizeof(float2), &p);
         if (st != SC_OK) return st;
+        const std::vector<float2> t4 = dit4k_table();
+        void* p4 = nullptr;
+        if ((st = upload(t4.data(), t4.size() * sizeof(float2), &p4)) != SC_OK) {
+            (void)hipFree(p);
+            return st;
+        }
+        d.dit4k = (float2*)p4;
         d.fused_tw = (float2*)p;
     }
     if (need_ntt && !d.ntt_ready) {
@@ -538,8 +592,11 @@ sc_status run_jobs(sc_kind kind, const Job* jobs, int njobs, bool rev, int64_t n
     } else if (path == SC_PATH_FUSED) {
         const int M = (int)std::max<int64_t>(64, next_pow2(L));
         for (int k = 0; k < njobs && e == hipSuccess; ++k)
-            e = sc::launch_fused(s, jobs[k].a, jobs[k].b, jobs[k].o, nch, (int)L, M, head, pair,
-                                 rev, d->fused_tw, stream);
+            e = M == 4096 && kFused4k
+                    ? sc::launch_fused4k(s, jobs[k].a, jobs[k].b, jobs[k].o, nch, (int)L, head,
+                                         pair, rev, d->dit4k, stream)
+                    : sc::launch_fused(s, jobs[k].a, jobs[k].b, jobs[k].o, nch, (int)L, M, head,
+                                       pair, rev, d->fused_tw, stream);
     } else {
         const int M = (int)next_pow2(L);
         sc::FsTw tw;

@@ -30,6 +30,24 @@ hipError_t launch_fused(Store st, const void* v, const void* g, void* r, int64_t
                         int M, int head, bool pair_store, bool rev, const float2* tw,
                         hipStream_t stream);
 
+// The M = 4096 fused kernel (sc_fused4k.hip): its twiddle table of float2 (c, t) pairs,
+// T = c (1 + i t) with t = tan of T's angle (c = 2^-40, t = +-2^40 where T = +-i):
+//   [DIT4K_P1B1 + i]                 branch 1, pass 1: the 10 pairs of base A = W_32
+//   [DIT4K_P2 + (var 16 + j) 10 + i]  pass 2, item j < 16
+//   [DIT4K_P3 + (var 256 + j) 10 + i] pass 3, item j < 256
+//   [DIT4K_UNP + k]                  W_8192^{-k}, k < 4096 (the unpack)
+// where var 0 is branch 0 (A = W_256^j, W_4096^j), var 1 branch 1 (A = W_512^{2j+1},
+// W_8192^{2j+1}), var 2 the inverse (conjugates of var 0), and an item's pairs i < 10 are
+// B, B^2, F_0, F_0^2, .., F_3, F_3^2 with B = A^4, F_p = A W16^p (W16^-p for the inverse).
+constexpr int DIT4K_P1B1 = 0;
+constexpr int DIT4K_P2 = 16;
+constexpr int DIT4K_P3 = DIT4K_P2 + 3 * 16 * 10;
+constexpr int DIT4K_UNP = DIT4K_P3 + 3 * 256 * 10;
+constexpr int DIT4K_TABLE_FLOAT2 = DIT4K_UNP + 4096;
+hipError_t launch_fused4k(Store st, const void* v, const void* g, void* r, int64_t nch, int L,
+                          int head, bool pair_store, bool rev, const float2* table,
+                          hipStream_t stream);
+
 // Constants of the exact path modulo p = 998244353 (omega_n = 3^((p-1)/n)).  The bank
 // holds pairs of doubles {w, w / p}:
 //   [0, 8192)                               w = omega_8192^i
