@@ -138,12 +138,9 @@ def record_traffic(w, fetch_dir: str, write_dir: str) -> dict:
     by (known copy bytes) / (what it reads for the 1 GiB copy)."""
     import csv
 
-    if w.L > 4096:
-        raise SystemExit("--record-traffic handles the single-kernel paths (L <= 4096) only")
-
     def per_dispatch(d, counter):
         rows = list(csv.DictReader(open(os.path.join(d, "run_counter_collection.csv"))))
-        hot, copy = {}, []
+        hot, copy, calls = {}, [], set()
         for r in rows:
             if r["Counter_Name"] != counter:
                 continue
@@ -152,9 +149,17 @@ def record_traffic(w, fetch_dir: str, write_dir: str) -> dict:
                 copy.append(val)
             elif kernel_matches(r["Kernel_Name"], w.storage, w.L):
                 hot[r["Dispatch_Id"]] = hot.get(r["Dispatch_Id"], 0.0) + val
+                if "head_kernel" in r["Kernel_Name"]:
+                    calls.add(r["Dispatch_Id"])
         if not hot or len(copy) != 1:
             raise RuntimeError("%s: expected hot-path dispatches and one calibration copy" % d)
         scale = COPY_BYTES / (copy[0] * 1024.0)
+        if w.L > 4096:
+            # the four-step call is several kernels (columns, rows, columns per part of the
+            # channels, then the head): bytes per call = all of them / calls (one head each)
+            if not calls:
+                raise RuntimeError("%s: no head_kernel dispatch to count four-step calls" % d)
+            return float(sum(hot.values())) / len(calls) * 1024.0 * scale, scale
         return float(np.mean(list(hot.values()))) * 1024.0 * scale, scale
 
     fetch, fs = per_dispatch(fetch_dir, "FETCH_SIZE")

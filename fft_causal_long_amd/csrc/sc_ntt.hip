@@ -121,10 +121,21 @@ __device__ __forceinline__ double balance(double a)
 // twiddle bank entry i as W (double2 {w, w/p})
 struct Tw {
     __amdgpu_buffer_rsrc_t rs;
+    int salt = 0;   // 0, but opaque to the compiler after reseed()
     __device__ __forceinline__ W at(int voff_elems, int soff_elems) const
     {
-        const auto d = __builtin_amdgcn_raw_buffer_load_b128(rs, voff_elems * 16, soff_elems * 16, 0);
+        const auto d = __builtin_amdgcn_raw_buffer_load_b128(rs, voff_elems * 16,
+                                                             soff_elems * 16 + salt, 0);
         return __builtin_bit_cast(W, d);
+    }
+    // Loads issued after this are not merged with earlier identical ones, and cannot be
+    // issued before `after` is computed: a pass loads its twiddles in groups, each after the
+    // previous group's last product, instead of keeping all fifteen live at once
+    __device__ __forceinline__ void reseed(double after)
+    {
+        int z = 0;
+        asm volatile("" : "+s"(z) : "v"(after));
+        salt = z;
     }
 };
 
@@ -215,19 +226,33 @@ __device__ __forceinline__ void pass(double (&x)[NA][16], int32_t* __restrict__ 
     if constexpr (QN > 1) {
         static_assert(R == 16, "passes with twiddles are radix 16");
         const int s = tau & (S - 1), n1 = tau / S;
-        W w[16];
-#pragma unroll
-        for (int k2 = 1; k2 < 16; ++k2) w[k2] = tw.at(n1, NTT_PASS_BASE + (Q - 32) + k2 * (Q / 16));
         constexpr int STEP = S == 1 ? 1 : S + S / 16;
         const int base = S == 1 ? 17 * n1 : (s + (s >> 4)) + 16 * n1 * STEP;
+        // the fifteen twiddles (cached) are loaded per array in two groups, each group after
+        // the previous one's last product, so that at most eight are live: all fifteen held
+        // across both arrays had pushed the kernel past 128 registers into scratch spills
+        Tw t = tw;
+        double last = 0.0;
 #pragma unroll
         for (int a = 0; a < NA; ++a) {
             dft<16, Pr>(x[a]);
             int32_t* buf = a == 0 ? buf0 : buf1;
             buf[base] = (int32_t)reduce<Pr>(x[a][0]);
 #pragma unroll
-            for (int k2 = 1; k2 < 16; ++k2)
-                buf[base + k2 * STEP] = (int32_t)mulc<Pr>(x[a][k2], w[k2]);
+            for (int g = 0; g < 2; ++g) {
+                if (a || g) t.reseed(last);
+                constexpr int K0 = 1;
+                const int lo = g ? 8 : K0, hi = g ? 16 : 8;
+                W w[8];
+#pragma unroll
+                for (int k2 = lo; k2 < hi; ++k2)
+                    w[k2 - lo] = t.at(n1, NTT_PASS_BASE + (Q - 32) + k2 * (Q / 16));
+#pragma unroll
+                for (int k2 = lo; k2 < hi; ++k2) {
+                    last = mulc<Pr>(x[a][k2], w[k2 - lo]);
+                    buf[base + k2 * STEP] = (int32_t)last;
+                }
+            }
         }
     } else {
 #pragma unroll
