@@ -122,7 +122,7 @@ def kernel_matches(name: str, storage: str, L: int, rev: bool = False) -> bool:
     M = max(64, 1 << (L - 1).bit_length())
     flag = "true" if rev else "false"
     if storage == "i32":
-        return ("ntt_conv_kernel<%d, %s, sc::ntt::PrimeA, false>" % (M, flag)) in name
+        return ("ntt_conv_kernel<%d, %s>" % (M, flag)) in name
     if L > 4096:
         return "fs_rows<" in name or (("fs_columns" in name or "head_kernel" in name)
                                       and (", %s>" % flag) in name)
@@ -261,10 +261,10 @@ def leakage_probe(sc, torch, dev, channels: int = 16) -> dict:
 
 
 def fixed_measure(sc, torch, w, dev, steps: int, warmup: int) -> dict:
-    """Time the exactly causal real-valued call (sc_causal_conv_fixed_f32_ws, fraction bits
-    FIXED_FRAC for v and g) on the workload's inputs widened to float32, with a caller
-    workspace so that no allocation is timed.  Algorithmic bytes per output: read v, g and
-    write r as float32 (12)."""
+    """Time the exactly causal real-valued call (sc_causal_conv_fixed_f32, fraction bits
+    FIXED_FRAC for v and g; one kernel, no scratch, no allocation) on the workload's inputs
+    widened to float32.  Algorithmic bytes per output: read v, g and write r as float32
+    (12)."""
     from workloads import bf16_bits_to_f32, make_inputs
     v, g = make_inputs(w)
     if w.storage == "bf16":
@@ -274,22 +274,22 @@ def fixed_measure(sc, torch, w, dev, steps: int, warmup: int) -> dict:
         raise RuntimeError("fixed-point range check failed for %s" % w.name)
     tv, tg = torch.from_numpy(v).to(dev), torch.from_numpy(g).to(dev)
     out = torch.empty_like(tv)
-    need = sc.sc_workspace_bytes(sc.KIND_FIXED_F32, w.B, w.C, w.L)
-    ws = torch.empty(need, dtype=torch.uint8, device=dev)
+    if sc.sc_workspace_bytes(sc.KIND_FIXED_F32, w.B, w.C, w.L) != 0:
+        raise RuntimeError("the exact real-valued call is expected to need no scratch")
     stream = torch.cuda.current_stream(dev)
-    fn = sc.lib().sc_causal_conv_fixed_f32_ws
+    fn = sc.lib().sc_causal_conv_fixed_f32
 
     def call():
         st = fn(tv.data_ptr(), tg.data_ptr(), out.data_ptr(), w.B, w.C, w.L, FIXED_FRAC,
-                FIXED_FRAC, ws.data_ptr(), need, stream.cuda_stream)
+                FIXED_FRAC, stream.cuda_stream)
         if st != 0:
-            raise RuntimeError("sc_causal_conv_fixed_f32_ws failed: %s" % sc.sc_status_string(st))
+            raise RuntimeError("sc_causal_conv_fixed_f32 failed: %s" % sc.sc_status_string(st))
 
     for _ in range(warmup):
         call()
     ms, _ = time_rounds(torch, stream, lambda i: call(), steps)
     gbps = 12 * w.outputs / (ms * 1e-3) / 1e9
-    return {"entry": "sc_causal_conv_fixed_f32_ws", "frac_bits": [FIXED_FRAC, FIXED_FRAC],
+    return {"entry": "sc_causal_conv_fixed_f32", "frac_bits": [FIXED_FRAC, FIXED_FRAC],
             "ms_per_call": round(ms, 5), "value": round(w.outputs / (ms * 1e-3), 1),
             "unit": "outputs/s", "hbm": {"algorithmic_bytes_per_call": 12 * w.outputs,
                                          "achieved_GBps": round(gbps, 1),

@@ -443,9 +443,6 @@ sc_status resolve_path(sc_kind kind, int64_t L, int32_t requested, sc_path* out)
     }
 }
 
-// scratch of the exact real-valued kind: three int32 residues per output
-size_t fixed_bytes(int64_t n) { return (size_t)n * 3 * sizeof(int32_t); }
-
 // the four-step path's second stream and events of the current device, made on first use
 sc_status fourstep_streams(DeviceState& d)
 {
@@ -521,9 +518,7 @@ sc_status run_jobs(sc_kind kind, const Job* jobs, int njobs, bool rev, int64_t n
     // scratch of this path, checked against a caller workspace before any HIP call
     size_t need = 0;
     int64_t chunk = 0;
-    if (kind == SC_KIND_FIXED_F32) {
-        need = fixed_bytes(n);
-    } else if (path == SC_PATH_FOUR_STEP) {
+    if (path == SC_PATH_FOUR_STEP) {
         if (noalloc &&
             sc::fourstep_bytes_per_channel((int)next_pow2(L)) > (size_t)ws_bytes)
             return SC_ERR_UNSUPPORTED;
@@ -545,18 +540,9 @@ sc_status run_jobs(sc_kind kind, const Job* jobs, int njobs, bool rev, int64_t n
     hipError_t e = hipSuccess;
     if (kind == SC_KIND_FIXED_F32) {
         const int M = (int)std::max<int64_t>(64, next_pow2(L));
-        void* scratch = ws;
-        bool own = false;
-        if (!ws) {
-            if (hipMallocAsync(&scratch, need, stream) != hipSuccess) return SC_ERR_HIP;
-            own = true;
-        }
         for (int k = 0; k < njobs && e == hipSuccess; ++k)
             e = sc::launch_fixed((const float*)jobs[k].a, (const float*)jobs[k].b,
-                                 (float*)jobs[k].o, (int32_t*)scratch, nch, (int)L, M, fv, fg,
-                                 d->ntt, stream);
-        if (own && hipFreeAsync(scratch, stream) != hipSuccess && e == hipSuccess)
-            e = hipErrorUnknown;
+                                 (float*)jobs[k].o, nch, (int)L, M, fv, fg, d->ntt, stream);
         return e == hipSuccess ? SC_OK : SC_ERR_HIP;
     }
     if (kind == SC_KIND_NTT_I32 && path == SC_PATH_NTT_MFMA) {
@@ -701,9 +687,7 @@ sc_status blc_plan(sc_kind kind, int64_t B, int64_t L, int64_t C, const sc_optio
     const sc_status st = resolve_path(kind, L, opt ? opt->path : SC_PATH_AUTO, &path);
     if (st != SC_OK) return st;
     p->inner = 0;
-    if (kind == SC_KIND_FIXED_F32) {
-        p->inner = fixed_bytes(nch * L);
-    } else if (path == SC_PATH_FOUR_STEP) {
+    if (path == SC_PATH_FOUR_STEP) {
         int64_t chunk;
         fourstep_plan(nch, L, &chunk, &p->inner);
     }
@@ -881,7 +865,6 @@ size_t sc_workspace_bytes(sc_kind kind, int64_t B, int64_t C, int64_t L)
         if (check_shape(kind, B, C, L, &n) != SC_OK || n == 0) return 0;
         sc_path path;
         if (resolve_path(kind, L, SC_PATH_AUTO, &path) != SC_OK) return 0;
-        if (kind == SC_KIND_FIXED_F32) return fixed_bytes(n);
         if (path != SC_PATH_FOUR_STEP) return 0;
         int64_t chunk;
         size_t need;

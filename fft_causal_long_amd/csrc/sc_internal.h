@@ -94,9 +94,9 @@ hipError_t launch_ntt_mfma(const int32_t* v, const int32_t* g, int32_t* r, int64
                            int M, bool rev, const NttMfmaTables& tables, hipStream_t stream);
 
 // Exact real-valued causal convolution: V = round(v 2^fv), G = round(g 2^fg), the exact
-// integer sum R through primes A, B, C (tables[0..2]) into scratch (3 * nch * L int32), then
-// r = round_f32(R 2^-(fv+fg)).
-hipError_t launch_fixed(const float* v, const float* g, float* r, int32_t* scratch, int64_t nch,
+// integer sum R from its residues modulo primes A, B, C (tables[0..2]), all in one kernel,
+// then r = round_f32(R 2^-(fv+fg)).  Uses no scratch.
+hipError_t launch_fixed(const float* v, const float* g, float* r, int64_t nch,
                         int L, int M, int fv, int fg, const NttTables* tables, hipStream_t stream);
 
 // ---- four-step path (L > FUSED_MAX_L)

@@ -23,11 +23,17 @@
 //     h = fl(a w);  l = fma(a, w, -h)            (the exact rounding error, an integer)
 //     q = round(a w / p)                         (fma with w/p and the 1.5*2^52 shift)
 //     r = fma(-q, p, h) + l = a w - q p          (exact: |h - q p| < 2^31)
-// giving |r| <= 1.5 p.  LDS holds int32 values (|x| < 2^31) between passes.
+// giving |r| <= 1.5 p.  Between passes values are int32 (|x| < 2^31), in LDS and in
+// registers; an array is widened to float64 only inside its butterflies.
 //
 // Layout as in the float kernel: max(64, M/8) threads, a length-M transform held by TB = M/16
 // threads with 16 values each, Stockham radix-16 passes through LDS (a v and a g array per
 // branch unit), 68 KB of LDS per workgroup at M = 4096.
+//
+// The exact real-valued kind runs the same per-prime steps three times in one kernel
+// (fixed_conv_kernel): the residues modulo A and B of a thread's eight outputs wait in
+// registers while the next prime is computed, and Garner's recombination ends the kernel, so
+// no residue goes through memory.
 
 #include "sc_device.h"
 #include "sc_internal.h"
@@ -206,51 +212,89 @@ __device__ __forceinline__ void dft(double* a)
     }
 }
 
-__device__ __forceinline__ int lds_pad(int a) { return a + (a >> 4); }
+// LDS layout of a unit's arrays.  From M = 1024 on (whole waves per unit) the layout is
+// chosen by the pass that wrote the array, so that both its stores and the reads that follow
+// hit 64 different 4-byte banks in every wave (no linear padding serves all three patterns):
+//   S = 1 stores, logical 16 n1 + k2:             a + a/64
+//   S = 16 stores, logical s + 16 k2 + 256 n1:    a + a/64 + 12 (a/256)
+// reads of 64 consecutive positions are conflict-free in both.  Smaller M keeps one pad word
+// per 16 (several units share a wave there).
+template <int M, int S>
+constexpr int lds_words()
+{
+    if constexpr (M < 1024) return M + M / 16;
+    else return M + M / 64 + (S == 16 ? 12 * (M / 256) : 0);
+}
+template <int M>
+constexpr int lds_region() { return lds_words<M, 16>(); }
 
-template <int TB>
+// position of logical element tau + TB q (a per-thread base plus a constant per q)
+template <int M, int S>
 __device__ __forceinline__ int reg_off(int tau, int q)
 {
-    if constexpr (TB % 16 == 0) return tau + (tau >> 4) + q * (TB + TB / 16);
-    else return lds_pad(tau + TB * q);
+    constexpr int TB = M / 16;
+    if constexpr (M < 1024) {
+        if constexpr (TB % 16 == 0) return tau + (tau >> 4) + q * (TB + TB / 16);
+        else {
+            const int a = tau + TB * q;
+            return a + (a >> 4);
+        }
+    } else {
+        // TB is a multiple of 64, so (tau + TB q) / 64 = tau / 64 + q TB / 64, and likewise
+        // for / 256 (tau < 256 when TB < 256)
+        const int b = tau + (tau >> 6) + (S == 16 ? 12 * (tau >> 8) : 0);
+        return b + q * TB + (q * TB) / 64 + (S == 16 ? 12 * ((q * TB) / 256) : 0);
+    }
 }
 
 // One Stockham DIF pass (index scheme as in the float kernel) over NA arrays sharing the
-// twiddles.  Passes with twiddles are radix 16 with one item per thread; their outputs are
-// reduced below 2^31 (k2 > 0 by the twiddle product, k2 = 0 explicitly) and stored as int32.
-template <int M, int R, int S, int NA, class Pr>
-__device__ __forceinline__ void pass(double (&x)[NA][16], int32_t* __restrict__ buf0,
-                                     int32_t* __restrict__ buf1, int tau, const Tw& tw)
+// twiddles.  Arrays are held as int32 (|x| < 2^31) between passes and widened to float64 one
+// array at a time inside the butterfly, so the array not being worked on takes half the
+// registers.  Passes with twiddles are radix 16 with one item per thread; their outputs are
+// reduced below 2^31 (k2 > 0 by the twiddle product, k2 = 0 explicitly) and stored to LDS.
+// The last pass (no twiddles, in registers) hands each output, below 2^36, to
+// fin(a, q, value) for array a and register q, all of array 0 before array 1.
+template <int M, int R, int S, int NA, class Pr, class Fin>
+__device__ __forceinline__ void pass(int32_t (&x)[NA][16], int32_t* __restrict__ buf0,
+                                     int32_t* __restrict__ buf1, int tau, const Tw& tw, Fin& fin)
 {
     constexpr int NB = 16 / R, Q = M / S, QN = Q / R;
     if constexpr (QN > 1) {
         static_assert(R == 16, "passes with twiddles are radix 16");
+        static_assert(S == 1 || S == 16, "twiddled passes are the first two");
         const int s = tau & (S - 1), n1 = tau / S;
-        constexpr int STEP = S == 1 ? 1 : S + S / 16;
-        const int base = S == 1 ? 17 * n1 : (s + (s >> 4)) + 16 * n1 * STEP;
+        // store position of output k2 = base + off(k2) (see lds_words)
+        int base;
+        if constexpr (M < 1024) base = S == 1 ? 17 * n1 : (s + (s >> 4)) + 17 * S * n1;
+        else base = S == 1 ? 16 * n1 + (n1 >> 2) : s + 272 * n1;
+        auto off = [](int k2) {
+            if constexpr (M < 1024) return S == 1 ? k2 : k2 * (S + S / 16);
+            else return S == 1 ? k2 : 16 * k2 + (k2 >> 2);
+        };
         // the fifteen twiddles (cached) are loaded per array in two groups, each group after
-        // the previous one's last product, so that at most eight are live: all fifteen held
-        // across both arrays had pushed the kernel past 128 registers into scratch spills
+        // the previous one's last product, so that at most eight are live
         Tw t = tw;
         double last = 0.0;
 #pragma unroll
         for (int a = 0; a < NA; ++a) {
-            dft<16, Pr>(x[a]);
+            double d[16];
+#pragma unroll
+            for (int q = 0; q < 16; ++q) d[q] = (double)x[a][q];
+            dft<16, Pr>(d);
             int32_t* buf = a == 0 ? buf0 : buf1;
-            buf[base] = (int32_t)reduce<Pr>(x[a][0]);
+            buf[base] = (int32_t)reduce<Pr>(d[0]);
 #pragma unroll
             for (int g = 0; g < 2; ++g) {
                 if (a || g) t.reseed(last);
-                constexpr int K0 = 1;
-                const int lo = g ? 8 : K0, hi = g ? 16 : 8;
+                const int lo = g ? 8 : 1, hi = g ? 16 : 8;
                 W w[8];
 #pragma unroll
                 for (int k2 = lo; k2 < hi; ++k2)
                     w[k2 - lo] = t.at(n1, NTT_PASS_BASE + (Q - 32) + k2 * (Q / 16));
 #pragma unroll
                 for (int k2 = lo; k2 < hi; ++k2) {
-                    last = mulc<Pr>(x[a][k2], w[k2 - lo]);
-                    buf[base + k2 * STEP] = (int32_t)last;
+                    last = mulc<Pr>(d[k2], w[k2 - lo]);
+                    buf[base + off(k2)] = (int32_t)last;
                 }
             }
         }
@@ -258,35 +302,36 @@ __device__ __forceinline__ void pass(double (&x)[NA][16], int32_t* __restrict__ 
 #pragma unroll
         for (int a = 0; a < NA; ++a) {
 #pragma unroll
-            for (int q = 0; q < NB; ++q) {
+            for (int qb = 0; qb < NB; ++qb) {
                 double b[R];
 #pragma unroll
-                for (int n2 = 0; n2 < R; ++n2) b[n2] = x[a][q + NB * n2];
+                for (int n2 = 0; n2 < R; ++n2) b[n2] = (double)x[a][qb + NB * n2];
                 dft<R, Pr>(b);
 #pragma unroll
-                for (int k2 = 0; k2 < R; ++k2) x[a][q + NB * k2] = b[k2];
+                for (int k2 = 0; k2 < R; ++k2) fin(a, qb + NB * k2, b[k2]);
             }
         }
     }
 }
 
-template <int M, int NA, class Pr, int S = 1>
-__device__ __forceinline__ void passes(double (&x)[NA][16], int32_t* __restrict__ buf0,
-                                       int32_t* __restrict__ buf1, int tau, const Tw& tw)
+template <int M, int NA, class Pr, int S = 1, class Fin>
+__device__ __forceinline__ void passes(int32_t (&x)[NA][16], int32_t* __restrict__ buf0,
+                                       int32_t* __restrict__ buf1, int tau, const Tw& tw,
+                                       Fin& fin)
 {
-    constexpr int TB = M / 16, Q = M / S, R = Q >= 16 ? 16 : Q;
+    constexpr int Q = M / S, R = Q >= 16 ? 16 : Q;
     if constexpr (Q / R > 1) {
-        pass<M, R, S, NA, Pr>(x, buf0, buf1, tau, tw);
+        pass<M, R, S, NA, Pr>(x, buf0, buf1, tau, tw, fin);
         __syncthreads();
 #pragma unroll
         for (int q = 0; q < 16; ++q) {
-            x[0][q] = (double)buf0[reg_off<TB>(tau, q)];
-            if constexpr (NA > 1) x[1][q] = (double)buf1[reg_off<TB>(tau, q)];
+            x[0][q] = buf0[reg_off<M, S>(tau, q)];
+            if constexpr (NA > 1) x[1][q] = buf1[reg_off<M, S>(tau, q)];
         }
         __syncthreads();
-        passes<M, NA, Pr, S * R>(x, buf0, buf1, tau, tw);
+        passes<M, NA, Pr, S * R>(x, buf0, buf1, tau, tw, fin);
     } else {
-        pass<M, R, S, NA, Pr>(x, buf0, buf1, tau, tw);
+        pass<M, R, S, NA, Pr>(x, buf0, buf1, tau, tw, fin);
     }
 }
 
@@ -301,45 +346,36 @@ __device__ __forceinline__ void passes(double (&x)[NA][16], int32_t* __restrict_
 template <int M>
 constexpr int ntt_threads() { return M / 8 > 64 ? M / 8 : 64; }
 
+namespace ntt {
+
+// The balanced residues mod Pr of one channel's causal convolution at the eight positions
+// this thread finishes: out[i] belongs to n = (M - tau - TB q) mod M, q = i + 8 beta (a result
+// only where n < L).  bv, bg: the unit's two LDS arrays; xch: the channel's exchange array
+// (branch 0's bv).  The call begins with a barrier before its first LDS write, so calls for
+// several primes may follow one another in a kernel.  salt is zero, but opaque (see after()):
+// added to tau in the global and twiddle offsets, it keeps a later call's loads from being
+// merged with an earlier call's or hoisted above its end.
 template <int M, bool REV, class Pr, bool FIX>
-__global__ __launch_bounds__(ntt_threads<M>(), 4) void ntt_conv_kernel(const void* __restrict__ v,
-                                                       const void* __restrict__ g,
-                                                       int32_t* __restrict__ r, int64_t nch,
-                                                       int L, const double* __restrict__ bank,
-                                                       double ninv, double ninv_q, double sv,
-                                                       double sg)
+__device__ __forceinline__ void residues(const Span& vs, const Span& gs, int cbase, int L,
+                                         int tau, int beta, int32_t* bv, int32_t* bg,
+                                         int32_t* xch, const Tw& tw, double ninv,
+                                         double ninv_q, double sv, double sg, int salt,
+                                         int32_t (&out)[8])
 {
-    using namespace ntt;
-    static_assert(M >= 64 && M <= 4096, "fused NTT handles 64 <= M <= 4096");
-    constexpr int N = 2 * M, TB = M / 16, UNITS = ntt_threads<M>() / TB, CPW = UNITS / 2;
-    constexpr int REG = M + M / 16;
-    __shared__ int32_t lds[UNITS * 2 * REG];
-
-    const Tw tw{__builtin_amdgcn_make_buffer_rsrc((void*)bank, (short)0, NTT_BANK_ENTRIES * 16,
-                                                  0x00020000)};
-    const int tid = threadIdx.x;
-    const int unit = tid / TB, tau = tid % TB;
-    const int cl = unit >> 1, beta = unit & 1;
-    const int64_t ch0 = (int64_t)blockIdx.x * CPW;
-    const int nvalid = (int)((nch - ch0) < CPW ? (nch - ch0) : CPW);
-    // both input kinds have 4-byte elements
-    const Span vs = make_span((const int32_t*)v, ch0 * L, (int64_t)nvalid * L);
-    const Span gs = make_span((const int32_t*)g, ch0 * L, (int64_t)nvalid * L);
-    const Span rs = make_span(r, ch0 * L, (int64_t)nvalid * L);
-    int32_t* bv = lds + unit * 2 * REG;
-    int32_t* bg = bv + REG;
-    const int cbase = cl * L;
-
-    // 1. inputs as exact doubles (|x| < 2^31), times omega_N^n on branch 1.  Positions past
-    //    L are read at byte offset 2^31, beyond the descriptor's range, so they read 0 (a
-    //    select instead of a branch keeps all the loads in flight together).  All 32 element
-    //    loads are issued first and branch 1's 16 twiddle loads right after them: converting
-    //    and multiplying element by element under the branch made every element wait for
-    //    its own loads, one memory latency per element.
+    constexpr int N = 2 * M, TB = M / 16;
+    // 1. inputs as residues below 2^31 in magnitude, times omega_N^n on branch 1.
+    //    Positions past L are read at byte offset 2^31, beyond the descriptor's range, so they
+    //    read 0 (a select instead of a branch keeps all the loads in flight together).  All
+    //    32 element loads are issued first and branch 1's twiddle loads right after them:
+    //    converting and multiplying element by element under the branch made every element
+    //    wait for its own loads, one memory latency per element.
+    // taus = tau, but opaque: the global and twiddle offsets of one call are not shared
+    // with another's (kept live from the first call to the last, they had been spilled)
+    const int taus = tau + salt;
     uint32_t wa[16], wb[16];
 #pragma unroll
     for (int q = 0; q < 16; ++q) {
-        const int n = tau + TB * q;
+        const int n = taus + TB * q;
         const bool in = L == M || n < L;
         const uint32_t ob = in ? (uint32_t)(cbase + n) * 4u : 0x80000000u;
         const uint32_t oa = in ? (uint32_t)(cbase + (REV ? L - 1 - n : n)) * 4u : 0x80000000u;
@@ -352,73 +388,139 @@ __global__ __launch_bounds__(ntt_threads<M>(), 4) void ntt_conv_kernel(const voi
         else
             return (double)(int32_t)w;
     };
-    double x[2][16];
-    if (beta) {
-        // the twiddles in two batches of 8, which bounds the registers held at once
+    // With ONE_PATH, branch 0 multiplies by omega^0 = 1 (table entry 0) instead of taking
+    // another path: in the three-prime kernel, arrays assigned on two paths had become
+    // vectors merged in one block of registers, and spilled.  Without it (one prime), the
+    // branch saves branch 0 the products.  The twiddles come in two batches of 8, which
+    // bounds the registers held at once.
+    constexpr bool ONE_PATH = FIX;
+    int32_t x[2][16];
+    const int twstep = beta ? NTT_TW_N / N : 0;
+    if (ONE_PATH || beta) {
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
             W wq[8];
 #pragma unroll
-            for (int i = 0; i < 8; ++i)
-                wq[i] = tw.at((tau + TB * (8 * h + i)) * (NTT_TW_N / N), 0);
+            for (int i = 0; i < 8; ++i) wq[i] = tw.at((taus + TB * (8 * h + i)) * twstep, 0);
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
                 const int q = 8 * h + i;
-                x[0][q] = mulc<Pr>(to_residue(wa[q], sv), wq[i]);
-                x[1][q] = mulc<Pr>(to_residue(wb[q], sg), wq[i]);
+                x[0][q] = (int32_t)mulc<Pr>(to_residue(wa[q], sv), wq[i]);
+                x[1][q] = (int32_t)mulc<Pr>(to_residue(wb[q], sg), wq[i]);
             }
         }
     } else {
 #pragma unroll
         for (int q = 0; q < 16; ++q) {
-            x[0][q] = to_residue(wa[q], sv);
-            x[1][q] = to_residue(wb[q], sg);
+            x[0][q] = (int32_t)to_residue(wa[q], sv);
+            x[1][q] = (int32_t)to_residue(wb[q], sg);
         }
     }
 
-    // 2. V, G = NTT_M(.) in natural order (values below 2^36)
-    passes<M, 2, Pr>(x, bv, bg, tau, tw);
+    // the previous call's exchange reads are done before this call's passes write the LDS
+    __syncthreads();
 
-    // 3. X = V * (G N^{-1})
-    double y[1][16];
-#pragma unroll
-    for (int q = 0; q < 16; ++q)
-        y[0][q] = mulv<Pr>(reduce<Pr>(x[0][q]), reduce<Pr>(mulc<Pr>(x[1][q], W{ninv, ninv_q})));
+    // 2, 3. V, G = NTT_M(.) in natural order; the last pass hands out V_k, then G_k (below
+    //    2^36), and X_k = V_k (G_k N^{-1}) is formed as they arrive
+    int32_t y[1][16];
+    auto product = [&](int a, int q, double val) {
+        if (a == 0)
+            x[0][q] = (int32_t)reduce<Pr>(val);
+        else
+            y[0][q] = (int32_t)mulv<Pr>((double)x[0][q],
+                                        reduce<Pr>(mulc<Pr>(val, W{ninv, ninv_q})));
+    };
+    passes<M, 2, Pr>(x, bv, bg, tau, tw, product);
 
-    // 4. f = NTT_M(X): e^beta_n = f_{(M - n) mod M}
-    passes<M, 1, Pr>(y, bv, bv, tau, tw);
+    // 4. f = NTT_M(X): e^beta_n = f_{(M - n) mod M}, reduced as it leaves the last pass
+    int32_t f[16];
+    auto keep = [&](int, int q, double val) { f[q] = (int32_t)reduce<Pr>(val); };
+    passes<M, 1, Pr>(y, bv, bv, tau, tw, keep);
 
     // 5. register q of thread tau holds e^beta at n = (M - tau - TB q) mod M.
     //    x_n = e^0_n + omega_N^{-n} e^1_n: branch 0 finishes q < 8, branch 1 q >= 8, each
-    //    handing the other half to its partner through LDS (branch 0's v region).
-    int32_t* xch = lds + (2 * cl) * 2 * REG;
-    double own[16];
+    //    handing the other half to its partner through LDS.
     if (beta) {
-        // omega_N^{-n} = omega_N^{N - n}; the 16 twiddle loads issued together
-        W wq[16];
+        // omega_N^{-n} = omega_N^{N - n}, loaded in two groups of 8, the second after the
+        // first group's products (one path here spills more than it saves)
+        Tw t = tw;
 #pragma unroll
-        for (int q = 0; q < 16; ++q) {
-            const int n = (M - tau - TB * q) & (M - 1);
-            wq[q] = tw.at(((N - n) & (N - 1)) * (NTT_TW_N / N), 0);
+        for (int h = 0; h < 2; ++h) {
+            if (h) t.reseed((double)f[7]);
+            W wq[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const int n = (M - taus - TB * (8 * h + i)) & (M - 1);
+                wq[i] = t.at(((N - n) & (N - 1)) * (NTT_TW_N / N), 0);
+            }
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+                f[8 * h + i] = (int32_t)mulc<Pr>((double)f[8 * h + i], wq[i]);
         }
-#pragma unroll
-        for (int q = 0; q < 16; ++q) own[q] = mulc<Pr>(y[0][q], wq[q]);
-    } else {
-#pragma unroll
-        for (int q = 0; q < 16; ++q) own[q] = reduce<Pr>(y[0][q]);
     }
 #pragma unroll
     for (int q = 0; q < 16; ++q)
-        if ((q < 8) == (beta == 1)) xch[reg_off<TB>(tau, q)] = (int32_t)own[q];
+        if ((q < 8) == (beta == 1)) xch[reg_off<M, 1>(tau, q)] = f[q];
     __syncthreads();
 #pragma unroll
-    for (int q = 0; q < 16; ++q) {
-        if ((q < 8) != (beta == 0)) continue;
-        const int n = (M - tau - TB * q) & (M - 1);
-        if (n >= L) continue;
-        const double s = balance<Pr>(reduce<Pr>(own[q] + (double)xch[reg_off<TB>(tau, q)]));
-        __builtin_amdgcn_raw_buffer_store_b32((uint32_t)(int32_t)s, rs.rs,
-                                              (cbase + (REV ? L - 1 - n : n)) * 4, 0, 0);
+    for (int i = 0; i < 8; ++i) {
+        // a choice between two values (a conditional between the two array elements would
+        // pick an address and force f into memory or an indexed register block)
+        const int32_t lo = f[i], hi = f[8 + i];
+        const int32_t mine = beta ? hi : lo;
+        const int32_t other = xch[beta ? reg_off<M, 1>(tau, 8 + i) : reg_off<M, 1>(tau, i)];
+        out[i] = (int32_t)balance<Pr>(reduce<Pr>((double)mine + (double)other));
+    }
+}
+
+// zero, produced after x is computed, and not known to the compiler to be zero
+__device__ __forceinline__ int after(int32_t x)
+{
+    int z = 0;
+    asm volatile("" : "+s"(z) : "v"(x));
+    return z;
+}
+
+}  // namespace ntt
+
+// Workgroup geometry shared by the two kernels: TB = M / 16 threads per branch unit, two units
+// (branches 0 and 1) per channel, CPW channels per workgroup, two LDS arrays per unit.
+#define SC_NTT_SETUP(VP, GP, RP)                                                              \
+    constexpr int TB = M / 16, UNITS = ntt_threads<M>() / TB, CPW = UNITS / 2;                \
+    constexpr int REG = lds_region<M>();                                                      \
+    __shared__ int32_t lds[UNITS * 2 * REG];                                                  \
+    const int tid = threadIdx.x;                                                              \
+    const int unit = tid / TB, tau = tid % TB;                                                \
+    const int cl = unit >> 1, beta = unit & 1;                                                \
+    const int64_t ch0 = (int64_t)blockIdx.x * CPW;                                            \
+    const int nvalid = (int)((nch - ch0) < CPW ? (nch - ch0) : CPW);                          \
+    const Span vs = make_span((const int32_t*)(VP), ch0 * L, (int64_t)nvalid * L);            \
+    const Span gs = make_span((const int32_t*)(GP), ch0 * L, (int64_t)nvalid * L);            \
+    const Span rs = make_span((RP), ch0 * L, (int64_t)nvalid * L);                            \
+    int32_t* bv = lds + unit * 2 * REG;                                                       \
+    int32_t* bg = bv + REG;                                                                   \
+    int32_t* xch = lds + (2 * cl) * 2 * REG;                                                  \
+    const int cbase = cl * L
+
+template <int M, bool REV>
+__global__ __launch_bounds__(ntt_threads<M>(), 4) void ntt_conv_kernel(
+    const int32_t* __restrict__ v, const int32_t* __restrict__ g, int32_t* __restrict__ r,
+    int64_t nch, int L, const double* __restrict__ bank, double ninv, double ninv_q)
+{
+    using namespace ntt;
+    static_assert(M >= 64 && M <= 4096, "fused NTT handles 64 <= M <= 4096");
+    SC_NTT_SETUP(v, g, r);
+    const Tw tw{__builtin_amdgcn_make_buffer_rsrc((void*)bank, (short)0, NTT_BANK_ENTRIES * 16,
+                                                  0x00020000)};
+    int32_t out[8];
+    residues<M, REV, PrimeA, false>(vs, gs, cbase, L, tau, beta, bv, bg, xch, tw, ninv, ninv_q,
+                                    0.0, 0.0, 0, out);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const int n = (M - tau - TB * (i + 8 * beta)) & (M - 1);
+        if (n < L)
+            __builtin_amdgcn_raw_buffer_store_b32((uint32_t)out[i], rs.rs,
+                                                  (cbase + (REV ? L - 1 - n : n)) * 4, 0, 0);
     }
 }
 
@@ -492,82 +594,128 @@ __device__ __forceinline__ float crt_to_f32(double a0, double a1, double a2, int
     return (float)ldexp(d, -F);
 }
 
-}  // namespace ntt
-
-// r = round_f32(R 2^-F) where R is the integer with the balanced residues sa, sb, sc modulo
-// the primes A, B, C and |R| <= (A B C - 1) / 2.
-__global__ void crt_decode_kernel(const int32_t* __restrict__ sa, const int32_t* __restrict__ sb,
-                                  const int32_t* __restrict__ sc, float* __restrict__ r,
-                                  int64_t n, int F)
+// Garner's recombination of balanced residues ra, rb, rc modulo A, B, C into
+// R = a0 + a1 A + a2 A B (every digit balanced, so |R| <= (A B C - 1) / 2), rounded once:
+// round_f32(R 2^-F)
+__device__ __forceinline__ float garner_f32(int32_t ra, int32_t rb, int32_t rc, int F)
 {
-    using namespace ntt;
-    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
-         i += (int64_t)gridDim.x * blockDim.x) {
-        const double a0 = (double)sa[i];
-        const double a1 = balance<PrimeB>(mulc<PrimeB>((double)sb[i] - a0, INV_A_MOD_B));
-        const double t2 = (double)sc[i] - a0 - mulc<PrimeC>(a1, A_MOD_C);
-        const double a2 = balance<PrimeC>(mulc<PrimeC>(t2, INV_AB_MOD_C));
-        // R = a0 + a1 A + a2 A B, every digit balanced, so |R| <= (A B C - 1) / 2
-        r[i] = crt_to_f32(a0, a1, a2, F);
-    }
+    const double a0 = (double)ra;
+    const double a1 = balance<PrimeB>(mulc<PrimeB>((double)rb - a0, INV_A_MOD_B));
+    const double t2 = (double)rc - a0 - mulc<PrimeC>(a1, A_MOD_C);
+    const double a2 = balance<PrimeC>(mulc<PrimeC>(t2, INV_AB_MOD_C));
+    return crt_to_f32(a0, a1, a2, F);
 }
 
-template <int M, bool REV, class Pr, bool FIX>
-static hipError_t launch_ntt_m(const void* v, const void* g, int32_t* r, int64_t nch, int L,
-                               const NttTables& tb, double sv, double sg, hipStream_t stream)
+}  // namespace ntt
+
+// The exact real-valued convolution of float32 data, fused: per channel the residues modulo
+// A, B and C in turn (each call re-reads v and g, which the first call brought into the
+// cache), the first two kept in registers, then Garner's recombination and the one rounding
+// to float32 per output, r = round_f32(R 2^-F) with R the integer with those residues and
+// |R| <= (A B C - 1) / 2.
+struct FixedArgs {
+    const double* bank[3];
+    double ninv[3], ninv_q[3];
+    double sv, sg;
+    int F;
+};
+
+template <int M>
+__global__ __launch_bounds__(ntt_threads<M>(), 4) void fixed_conv_kernel(
+    const float* __restrict__ v, const float* __restrict__ g, float* __restrict__ r, int64_t nch,
+    int L, FixedArgs fa)
+{
+    using namespace ntt;
+    static_assert(M >= 64 && M <= 4096, "fused NTT handles 64 <= M <= 4096");
+    SC_NTT_SETUP(v, g, r);
+    auto bank = [&](int i) {
+        return Tw{__builtin_amdgcn_make_buffer_rsrc((void*)fa.bank[i], (short)0,
+                                                    NTT_BANK_ENTRIES * 16, 0x00020000)};
+    };
+    int32_t ra[8], rb[8], rc[8];
+    residues<M, false, PrimeA, true>(vs, gs, cbase, L, tau, beta, bv, bg, xch, bank(0),
+                                     fa.ninv[0], fa.ninv_q[0], fa.sv, fa.sg, 0, ra);
+    residues<M, false, PrimeB, true>(vs, gs, cbase, L, tau, beta, bv, bg, xch, bank(1),
+                                     fa.ninv[1], fa.ninv_q[1], fa.sv, fa.sg, after(ra[7]), rb);
+    residues<M, false, PrimeC, true>(vs, gs, cbase, L, tau, beta, bv, bg, xch, bank(2),
+                                     fa.ninv[2], fa.ninv_q[2], fa.sv, fa.sg, after(rb[7]), rc);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const int n = (M - tau - TB * (i + 8 * beta)) & (M - 1);
+        const float res = garner_f32(ra[i], rb[i], rc[i], fa.F);
+        if (n < L)
+            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(res), rs.rs, (cbase + n) * 4,
+                                                  0, 0);
+    }
+}
+#undef SC_NTT_SETUP
+
+template <int M, bool REV>
+static hipError_t launch_ntt_m(const int32_t* v, const int32_t* g, int32_t* r, int64_t nch,
+                               int L, const NttTables& tb, hipStream_t stream)
 {
     constexpr int CPW = (ntt_threads<M>() / (M / 16)) / 2;
     const int64_t blocks = (nch + CPW - 1) / CPW;
     const int lg = __builtin_ctz((unsigned)(2 * M));
     if (!grid_ok(blocks, ntt_threads<M>())) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((ntt_conv_kernel<M, REV, Pr, FIX>), dim3((unsigned)blocks), dim3(ntt_threads<M>()), 0,
-                       stream, v, g, r, nch, L, tb.bank, tb.ninv[lg], tb.ninv_q[lg], sv, sg);
+    hipLaunchKernelGGL((ntt_conv_kernel<M, REV>), dim3((unsigned)blocks), dim3(ntt_threads<M>()),
+                       0, stream, v, g, r, nch, L, tb.bank, tb.ninv[lg], tb.ninv_q[lg]);
     return hipGetLastError();
 }
 
-template <bool REV, class Pr, bool FIX>
-static hipError_t launch_ntt_any(const void* v, const void* g, int32_t* r, int64_t nch, int L,
-                                 int M, const NttTables& tb, double sv, double sg, hipStream_t s)
+template <int M>
+static hipError_t launch_fixed_m(const float* v, const float* g, float* r, int64_t nch, int L,
+                                 const NttTables* tb, double sv, double sg, int F,
+                                 hipStream_t stream)
 {
-    switch (M) {
-    case 64: return launch_ntt_m<64, REV, Pr, FIX>(v, g, r, nch, L, tb, sv, sg, s);
-    case 128: return launch_ntt_m<128, REV, Pr, FIX>(v, g, r, nch, L, tb, sv, sg, s);
-    case 256: return launch_ntt_m<256, REV, Pr, FIX>(v, g, r, nch, L, tb, sv, sg, s);
-    case 512: return launch_ntt_m<512, REV, Pr, FIX>(v, g, r, nch, L, tb, sv, sg, s);
-    case 1024: return launch_ntt_m<1024, REV, Pr, FIX>(v, g, r, nch, L, tb, sv, sg, s);
-    case 2048: return launch_ntt_m<2048, REV, Pr, FIX>(v, g, r, nch, L, tb, sv, sg, s);
-    case 4096: return launch_ntt_m<4096, REV, Pr, FIX>(v, g, r, nch, L, tb, sv, sg, s);
-    default: return hipErrorInvalidValue;
+    constexpr int CPW = (ntt_threads<M>() / (M / 16)) / 2;
+    const int64_t blocks = (nch + CPW - 1) / CPW;
+    const int lg = __builtin_ctz((unsigned)(2 * M));
+    if (!grid_ok(blocks, ntt_threads<M>())) return hipErrorInvalidValue;
+    FixedArgs fa;
+    for (int i = 0; i < 3; ++i) {
+        fa.bank[i] = tb[i].bank;
+        fa.ninv[i] = tb[i].ninv[lg];
+        fa.ninv_q[i] = tb[i].ninv_q[lg];
     }
+    fa.sv = sv;
+    fa.sg = sg;
+    fa.F = F;
+    hipLaunchKernelGGL((fixed_conv_kernel<M>), dim3((unsigned)blocks), dim3(ntt_threads<M>()), 0,
+                       stream, v, g, r, nch, L, fa);
+    return hipGetLastError();
 }
+
+// F(M) expands to the call for each supported M
+#define SC_NTT_SWITCH(F)                                                                      \
+    switch (M) {                                                                              \
+    case 64: return F(64);                                                                    \
+    case 128: return F(128);                                                                  \
+    case 256: return F(256);                                                                  \
+    case 512: return F(512);                                                                  \
+    case 1024: return F(1024);                                                                \
+    case 2048: return F(2048);                                                                \
+    case 4096: return F(4096);                                                                \
+    default: return hipErrorInvalidValue;                                                     \
+    }
 
 hipError_t launch_ntt(const int32_t* v, const int32_t* g, int32_t* r, int64_t nch, int L, int M,
                       bool rev, const NttTables& tb, hipStream_t s)
 {
-    return rev ? launch_ntt_any<true, ntt::PrimeA, false>(v, g, r, nch, L, M, tb, 0.0, 0.0, s)
-               : launch_ntt_any<false, ntt::PrimeA, false>(v, g, r, nch, L, M, tb, 0.0, 0.0, s);
+#define SC_CALL(m) rev ? launch_ntt_m<m, true>(v, g, r, nch, L, tb, s) \
+                       : launch_ntt_m<m, false>(v, g, r, nch, L, tb, s)
+    SC_NTT_SWITCH(SC_CALL)
+#undef SC_CALL
 }
 
-hipError_t launch_fixed(const float* v, const float* g, float* r, int32_t* scratch, int64_t nch,
-                        int L, int M, int fv, int fg, const NttTables* tb, hipStream_t s)
+hipError_t launch_fixed(const float* v, const float* g, float* r, int64_t nch, int L, int M,
+                        int fv, int fg, const NttTables* tb, hipStream_t s)
 {
-    const int64_t n = nch * (int64_t)L;
     const double sv = ldexp(1.0, fv), sg = ldexp(1.0, fg);
-    hipError_t e = launch_ntt_any<false, ntt::PrimeA, true>(v, g, scratch, nch, L, M, tb[0], sv,
-                                                           sg, s);
-    if (e == hipSuccess)
-        e = launch_ntt_any<false, ntt::PrimeB, true>(v, g, scratch + n, nch, L, M, tb[1], sv, sg,
-                                                     s);
-    if (e == hipSuccess)
-        e = launch_ntt_any<false, ntt::PrimeC, true>(v, g, scratch + 2 * n, nch, L, M, tb[2], sv,
-                                                     sg, s);
-    if (e != hipSuccess) return e;
-    const int threads = 256;
-    int64_t blocks = (n + threads - 1) / threads;
-    if (blocks > 65536) blocks = 65536;
-    hipLaunchKernelGGL(crt_decode_kernel, dim3((unsigned)blocks), dim3(threads), 0, s, scratch,
-                       scratch + n, scratch + 2 * n, r, n, fv + fg);
-    return hipGetLastError();
+#define SC_CALL(m) launch_fixed_m<m>(v, g, r, nch, L, tb, sv, sg, fv + fg, s)
+    SC_NTT_SWITCH(SC_CALL)
+#undef SC_CALL
 }
+#undef SC_NTT_SWITCH
 
 }  // namespace sc

@@ -161,10 +161,11 @@ sc_status sc_causal_conv_ntt_i32(const int32_t* v, const int32_t* g, int32_t* r,
  *   precondition, checked from bounds by sc_fixed_range_ok.  Accuracy against the real sum:
  *   |r_t - sum v_j g_{t-j}| <= 2^-(frac_v+1) sum_j |g_j| + 2^-(frac_g+1) sum_j |v_j| + (one
  *   float32 rounding) -- e.g. frac_v = frac_g = 24 for activations of magnitude below 8.
- *   frac_v, frac_g in [-64, 64].  Largest L: 4096.  Scratch: 12 bytes per output
- *   (sc_workspace_bytes(SC_KIND_FIXED_F32, ...)), allocated stream-ordered by this call;
- *   the _ws variant takes it from the caller.  Gradients are not offered for this kind
- *   (SC_ERR_UNSUPPORTED from sc_causal_conv_bwd_ex).
+ *   frac_v, frac_g in [-64, 64].  Largest L: 4096.  One kernel computes the three residues
+ *   of each output in turn and combines them: no scratch, no allocation
+ *   (sc_workspace_bytes(SC_KIND_FIXED_F32, ...) is 0, so the _ws variant, kept for callers
+ *   written against a workspace, accepts any ws and ws_bytes and uses neither).  Gradients
+ *   are not offered for this kind (SC_ERR_UNSUPPORTED from sc_causal_conv_bwd_ex).
  */
 sc_status sc_causal_conv_fixed_f32(const float* v, const float* g, float* r, int64_t B,
                                    int64_t C, int64_t L, int32_t frac_v, int32_t frac_g,

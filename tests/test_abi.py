@@ -202,11 +202,12 @@ def test_fixed_kind_host_checks(sc):
     assert h.sc_causal_conv_ex(0, A, B_, C_, 1, 1, 64, ctypes.byref(opt), None, 0, None) == INVALID
     # no gradients for the fixed kind
     assert h.sc_causal_conv_bwd_ex(3, A, B_, C_, D_, E_, 1, 1, 64, None, None, 0, None) == UNSUP
-    # scratch: three int32 residues per output; a short caller workspace is refused
-    assert sc.sc_workspace_bytes(sc.KIND_FIXED_F32, 2, 3, 100) == 12 * 600
+    # one kernel keeps the three residues of an output in registers: no scratch
+    assert sc.sc_workspace_bytes(sc.KIND_FIXED_F32, 2, 3, 100) == 0
+    assert sc.sc_workspace_bytes(sc.KIND_FIXED_F32, 8, 1024, 4096) == 0
     assert sc.sc_workspace_bytes(sc.KIND_FIXED_F32, 1, 1, 5000) == 0
-    assert h.sc_causal_conv_fixed_f32_ws(A, B_, C_, 1, 1, 64, 8, 8, D_, 12 * 64 - 4, None) == \
-        sc.SC_ERR_WORKSPACE
+    assert sc.sc_blc_workspace_bytes(sc.KIND_FIXED_F32, 2, 100, 3) == \
+        3 * (((2 * 3 * 100 * 4) + 255) // 256 * 256)
 
 
 def test_fixed_range_helper(sc):
