@@ -14,7 +14,11 @@ and the calls for a filter shared by the batch on the same shape in the `shared`
 pre-activation on MFMA, alone and as the mixing step's prologue) in the `gate` object (skip
 with --no-gate).
 Inputs are resident in HBM before the timed region.  Several copies of the buffers are
-rotated so that the 256 MB last-level cache cannot hold a step's working set.
+rotated so that the 256 MB last-level cache cannot hold a step's working set.  Before the W
+warmup steps, untimed launches of the same step run for --prewarm-ms (default 200 ms; the
+`prewarm` object says how many): from idle the chip's clock ramps for about 30 ms, and W = 5
+steps alone would put the timed steps on that ramp.  Every other timed call gets the same
+pre-warm before its own timing.
 
 Prints ONE JSON line.  `value` is causal-conv outputs (B*C*L) per second.  The
 `roofline` object refers to the dominant kernel, timed with HIP events recorded on the
@@ -44,11 +48,33 @@ FP32_FMA_PEAK_UNPACKED_TFLOPS = 256 * 4 * 16 * 2 * 2.4e9 / 1e12
 CACHE_BYTES = 256 << 20          # MI355X last-level (Infinity) cache
 
 
-def time_rounds(torch, stream, fn, n: int, rounds: int = 5):
+PREWARM_MS = 200.0   # set from --prewarm-ms
+
+
+def prewarm(torch, fn) -> int:
+    """Untimed calls of fn back to back for PREWARM_MS of wall time: from idle the chip's
+    clock ramps for about 30 ms under load (the Medium call measured 0.191 ms at first,
+    0.154 ms steady from about its 200th launch on), so a measurement that starts cold times
+    the ramp.  Returns the number of calls."""
+    calls = 0
+    if PREWARM_MS <= 0:
+        return 0
+    t_end = time.perf_counter() + PREWARM_MS * 1e-3
+    while time.perf_counter() < t_end:
+        for i in range(16):
+            fn(i)
+        torch.cuda.synchronize()
+        calls += 16
+    return calls
+
+
+def time_rounds(torch, stream, fn, n: int, rounds: int = 5, warm: bool = True):
     """Mean milliseconds per call of fn(i), i < n, launched back to back on `stream`, with
     HIP events recorded on that stream only at the boundaries of `rounds` equal rounds (an
-    event between every two launches would add its own gap to each).  Returns (mean over
-    all calls, [mean per call of each round])."""
+    event between every two launches would add its own gap to each), after prewarm() unless
+    warm is False.  Returns (mean over all calls, [mean per call of each round])."""
+    if warm:
+        prewarm(torch, fn)
     rounds = max(1, min(rounds, n))
     bounds = [round(r * n / rounds) for r in range(rounds + 1)]
     evs = [torch.cuda.Event(enable_timing=True) for _ in range(rounds + 1)]
@@ -294,7 +320,7 @@ def fixed_measure(sc, torch, w, dev, steps: int, warmup: int) -> dict:
             "unit": "outputs/s", "hbm": {"algorithmic_bytes_per_call": 12 * w.outputs,
                                          "achieved_GBps": round(gbps, 1),
                                          "frac": round(gbps / HBM_PEAK_GBPS, 4)},
-            "scratch_bytes": need}
+            "scratch_bytes": 0}
 
 
 def oracle_sample_rate(w, v, g, nthreads: int, budget_s: float, start: int = 8):
@@ -745,6 +771,9 @@ def main(argv=None):
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--prewarm-ms", type=float, default=200.0,
+                    help="wall time of untimed hot-path launches before the warmup steps, so "
+                         "that the timed steps see the clock the chip holds under load (0: off)")
     ap.add_argument("--config", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-leakage", action="store_true",
@@ -783,6 +812,8 @@ def main(argv=None):
         print(json.dumps(record_traffic(WORKLOADS[args.config], *args.record_traffic)))
         return 0
 
+    global PREWARM_MS
+    PREWARM_MS = args.prewarm_ms
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the library has no multi-GPU path "
               "(channels shard across GPUs with no communication; run one process per GPU)",
@@ -822,6 +853,9 @@ def main(argv=None):
         if st != 0:
             raise RuntimeError("%s failed: %s" % (fn_name, sc.sc_status_string(st)))
 
+    # untimed launches of the same step for --prewarm-ms (see prewarm()), then the W warmup
+    # steps, then the K timed steps
+    warm = {"ms": PREWARM_MS, "launches": prewarm(torch, step)}
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
@@ -829,7 +863,7 @@ def main(argv=None):
     # the K steps back to back on the launch stream, HIP events at 5 round boundaries (and
     # synchronisation on both sides); one step is one kernel launch, so the mean launch
     # duration is the region's time per step
-    ms_per_step, round_ms = time_rounds(torch, stream, step, args.steps)
+    ms_per_step, round_ms = time_rounds(torch, stream, step, args.steps, warm=False)
     total_ms = ms_per_step * args.steps
     kernel_ms = ms_per_step
     # per-launch statistics over 50 more launches (outside the K timed steps)
@@ -887,6 +921,7 @@ def main(argv=None):
                       "method": "launches back to back, HIP events on the launch stream at "
                                 "round boundaries"},
         "launch_ms": stats,
+        "prewarm": warm,
     }
     if not args.no_bwd:
         del bufs
