@@ -204,4 +204,24 @@ __device__ __forceinline__ void direct_head(const float* __restrict__ hb, int nc
 // reversed, which turns the causal convolution into the correlation of the backward pass:
 // rev(causal(rev(dr), b))_j = sum_{t>=j} dr_t b_{t-j}.
 
+// Bring element range [first, first + count) of v and of g into the cache: thread i touches
+// the 128-byte line i of each (lines past the range read nothing; the caller covers the range
+// with its threads).  The two words come back unused: hand them to keep_touched() after the
+// thread's last barrier and load wait, since using them waits for the loads and vector-memory
+// waits are in order.
+template <class T>
+__device__ __forceinline__ uint2 touch_line(const T* v, const T* g, int64_t first, int64_t count,
+                                            int i)
+{
+    const Span sv = make_span(v, first, count), sg = make_span(g, first, count);
+    return make_uint2(__builtin_amdgcn_raw_buffer_load_b32(sv.rs, i * 128, 0, 0),
+                      __builtin_amdgcn_raw_buffer_load_b32(sg.rs, i * 128, 0, 0));
+}
+// Keeps the touched words alive behind a condition that is false for every pf >= 0 the host
+// passes, so the compiler neither removes the loads nor waits for them earlier.
+__device__ __forceinline__ void keep_touched(uint2 w, int64_t pf, const Span& dst)
+{
+    if (pf < 0) __builtin_amdgcn_raw_buffer_store_b32(w.x ^ w.y, dst.rs, 0, 0, 0);
+}
+
 }  // namespace sc

@@ -48,11 +48,15 @@ constexpr int fused_threads() { return M / 8 > 64 ? M / 8 : 64; }
 // unpack's alternating reads of u0[j] and u1[j] land in different banks
 constexpr int LDS_EXTRA = SC_LDS_EXTRA;
 
+// pf > 0 (M >= 1024): the threads idle during the inverse touch the cache lines of v and g of
+// the channels pf workgroups ahead -- the workgroup that will take this one's place when
+// pf = the workgroups resident at once, on the same XCD (pf a multiple of 8), whose L2 then
+// holds its inputs: without it every generation of workgroups began by waiting on HBM.
 template <int M, class IO, bool REV>
 __global__ __launch_bounds__(fused_threads<M>()) void fused_conv_kernel(
     const typename IO::T* __restrict__ v, const typename IO::T* __restrict__ g,
     typename IO::T* __restrict__ r, int64_t nch, int L, int head, int pair_store,
-    const float2* __restrict__ tw)
+    const float2* __restrict__ tw, int64_t pf)
 {
     static_assert(M >= 64 && M <= 4096, "fused path handles 64 <= M <= 4096");
     constexpr int FT = fused_threads<M>();
@@ -199,9 +203,17 @@ __global__ __launch_bounds__(fused_threads<M>()) void fused_conv_kernel(
         __syncthreads();
         // between this barrier and the first one of the inverse, where the active threads run
         // their first radix-16 pass
-        if (!iact)
+        uint2 touched = make_uint2(0u, 0u);
+        if (!iact) {
             direct_head<FT - CPW * TB>(hbuf, CPW, nvalid, L, head, tid - CPW * TB, put);
+            // one line of v and one of g per idle thread covers the CPW channels ahead
+            static_assert(CPW * M * sizeof(typename IO::T) <= 128 * (FT - CPW * TB),
+                          "the idle threads cover the next workgroup's lines");
+            if (pf > 0 && (int64_t)blockIdx.x + pf < (nch + CPW - 1) / CPW)
+                touched = touch_line(v, g, (ch0 + pf * CPW) * L, (int64_t)CPW * L, tid - CPW * TB);
+        }
         fft_passes<M, true>(x, ybuf, itau, bank, iact);
+        if (!iact) keep_touched(touched, pf, rs);
 
         // 5. store: x[q] = 8 M y_m with m = itau + TB q; r_{2m} = Re y_m, r_{2m+1} = Im y_m
         if (iact) {
@@ -260,9 +272,13 @@ static hipError_t launch_fused_m(const void* v, const void* g, void* r, int64_t 
     constexpr int CPW = (fused_threads<M>() / (M / 16)) / 2;
     const int64_t blocks = (nch + CPW - 1) / CPW;
     if (!grid_ok(blocks, fused_threads<M>())) return hipErrorInvalidValue;
+    static int64_t resident[16];
+    const int64_t pf = M >= 1024 ? resident_workgroups((const void*)fused_conv_kernel<M, IO, REV>,
+                                                        fused_threads<M>(), resident) / 8 * 8
+                                 : 0;
     hipLaunchKernelGGL((fused_conv_kernel<M, IO, REV>), dim3((unsigned)blocks), dim3(fused_threads<M>()), 0,
                        stream, (const typename IO::T*)v, (const typename IO::T*)g,
-                       (typename IO::T*)r, nch, L, head, pair ? 1 : 0, tw);
+                       (typename IO::T*)r, nch, L, head, pair ? 1 : 0, tw, pf);
     return hipGetLastError();
 }
 

@@ -145,7 +145,7 @@ __global__ __launch_bounds__(512) void fused4k_kernel(const typename IO::T* __re
                                                       const typename IO::T* __restrict__ g,
                                                       typename IO::T* __restrict__ r, int L,
                                                       int head, int pair_store,
-                                                      const float2* __restrict__ tab)
+                                                      const float2* __restrict__ tab, int64_t pf)
 {
     using namespace f4k;
     __shared__ float2 lds[2 * REGION];
@@ -302,6 +302,8 @@ __global__ __launch_bounds__(512) void fused4k_kernel(const typename IO::T* __re
     // 4. inverse transform (unit 0) of Y; unit 1 computes the direct head meanwhile
     const Span rs = make_span(r, ch * L, L);
     auto put = [&](int t, float a) { IO::store(rs, REV ? L - 1 - t : t, a); };
+    uint2 touched = make_uint2(0u, 0u);
+    static_assert(M * sizeof(typename IO::T) <= 128 * TB, "unit 1 covers a channel's lines");
     if (unit == 0) {
 #pragma unroll
         for (int n2 = 0; n2 < 16; ++n2) x[n2] = ybuf[ypos(tau + TB * n2)];
@@ -313,6 +315,10 @@ __global__ __launch_bounds__(512) void fused4k_kernel(const typename IO::T* __re
         for (int k2 = 0; k2 < 16; ++k2) run_at(k2) = x[k2];
     } else {
         direct_head<TB>(hbuf, 1, 1, L, head, tau, [&](int, int t, float a) { put(t, a); });
+        // the inputs of the channel pf ahead, which will run in this workgroup's place (same
+        // XCD for pf a multiple of 8): one 128-byte line of v and of g per thread
+        if (pf > 0 && ch + pf < (int64_t)gridDim.x)
+            touched = touch_line(v, g, (ch + pf) * L, (int64_t)L, tau);
     }
     __syncthreads();
     const int j = tau >> 4;
@@ -368,6 +374,7 @@ __global__ __launch_bounds__(512) void fused4k_kernel(const typename IO::T* __re
             }
         }
     }
+    if (unit == 1) keep_touched(touched, pf, rs);
 }
 
 template <class IO, bool REV>
@@ -375,9 +382,17 @@ static hipError_t launch4k(const void* v, const void* g, void* r, int64_t nch, i
                            bool pair, const float2* tab, hipStream_t stream)
 {
     if (!grid_ok(nch, f4k::FT)) return hipErrorInvalidValue;
+    // the next generation's inputs: bf16 only (16 KB per channel).  With fp32 (32 KB) the
+    // touched lines of the 64 workgroups ahead on an XCD (2 MB) crowd the 4 MB L2 that the
+    // running ones use, and the call got 2% slower instead of 4% faster.
+    static int64_t resident[16];
+    const int64_t pf =
+        sizeof(typename IO::T) == 2
+            ? resident_workgroups((const void*)fused4k_kernel<IO, REV>, f4k::FT, resident) / 8 * 8
+            : 0;
     hipLaunchKernelGGL((fused4k_kernel<IO, REV>), dim3((unsigned)nch), dim3(f4k::FT), 0, stream,
                        (const typename IO::T*)v, (const typename IO::T*)g, (typename IO::T*)r, L,
-                       head, pair ? 1 : 0, tab);
+                       head, pair ? 1 : 0, tab, pf);
     return hipGetLastError();
 }
 

@@ -20,6 +20,29 @@ constexpr int DIRECT_MAX_L = 32;
 
 enum class Store { F32, BF16 };
 
+// Workgroups of `kernel` (threads per workgroup, static LDS only) resident at once on the
+// current device: the occupancy calculator's workgroups per CU times the CU count, cached per
+// device in `cache` (0: not known yet).  0 if a query fails (its error is cleared).
+inline int64_t resident_workgroups(const void* kernel, int threads, int64_t (&cache)[16])
+{
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 16) {
+        (void)hipGetLastError();
+        return 0;
+    }
+    const int64_t known = __atomic_load_n(&cache[dev], __ATOMIC_RELAXED);
+    if (known > 0) return known;
+    int cus = 0, per_cu = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, threads, 0) != hipSuccess) {
+        (void)hipGetLastError();
+        return 0;
+    }
+    const int64_t n = (int64_t)cus * per_cu;
+    __atomic_store_n(&cache[dev], n, __ATOMIC_RELAXED);
+    return n;
+}
+
 // Every launcher computes r = causal(v, g) per channel; with rev it computes the gradient
 // form r = rev(causal(rev(v), g)), i.e. r_j = sum_{t>=j} v_t g_{t-j} (v read reversed, r
 // written reversed).
