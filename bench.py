@@ -729,12 +729,16 @@ def other_measure(sc, torch, w, dev, steps: int, warmup: int, oracle_too: bool =
            "hbm": {"algorithmic_bytes_per_call": alg_bytes,
                    "achieved_GBps": round(alg_bytes / (ms * 1e-3) / 1e9, 1),
                    "frac": round(alg_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)}}
-    if w.L > 4096:
-        traffic = measured_traffic(w.name)
-        rec["hbm"]["traffic_bytes_per_call"] = traffic
-        if traffic:
-            rec["hbm"]["traffic_GBps"] = round(traffic / (ms * 1e-3) / 1e9, 1)
-            rec["hbm"]["traffic_frac"] = round(traffic / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)
+    # HBM bytes per call from the committed counter record (null when there is none for the
+    # current kernel sources) and the VALU issue floor where a counter record exists
+    traffic = measured_traffic(w.name)
+    rec["hbm"]["traffic_bytes_per_call"] = traffic
+    if traffic:
+        rec["hbm"]["traffic_GBps"] = round(traffic / (ms * 1e-3) / 1e9, 1)
+        rec["hbm"]["traffic_frac"] = round(traffic / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)
+    issue = alu_issue(w.name, ms)
+    if issue:
+        rec["alu_issue"] = issue
     if w.storage != "i32":
         tf = algorithmic_flops_per_output(w.L) * w.outputs / (ms * 1e-3) / 1e12
         rec["alu"] = {"achieved_TFLOPs": round(tf, 2), "peak": FP32_FMA_PEAK_UNPACKED_TFLOPS,
