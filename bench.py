@@ -148,6 +148,9 @@ def kernel_matches(name: str, storage: str, L: int, rev: bool = False) -> bool:
     M = max(64, 1 << (L - 1).bit_length())
     flag = "true" if rev else "false"
     if storage == "i32":
+        if L > 4096:
+            # the four-step NTT: columns (per direction), rows (shared), inverse columns
+            return "ntt4_rows" in name or ("ntt4_columns" in name and (", %s>" % flag) in name)
         return ("ntt_conv_kernel<%d, %s>" % (M, flag)) in name
     if L > 4096:
         return "fs_rows<" in name or (("fs_columns" in name or "head_kernel" in name)
@@ -175,17 +178,25 @@ def record_traffic(w, fetch_dir: str, write_dir: str) -> dict:
                 copy.append(val)
             elif kernel_matches(r["Kernel_Name"], w.storage, w.L):
                 hot[r["Dispatch_Id"]] = hot.get(r["Dispatch_Id"], 0.0) + val
-                if "head_kernel" in r["Kernel_Name"]:
+                if ("head_kernel" if w.storage != "i32" else "ntt4_columns_inv") in r["Kernel_Name"]:
                     calls.add(r["Dispatch_Id"])
         if not hot or len(copy) != 1:
             raise RuntimeError("%s: expected hot-path dispatches and one calibration copy" % d)
         scale = COPY_BYTES / (copy[0] * 1024.0)
         if w.L > 4096:
             # the four-step call is several kernels (columns, rows, columns per part of the
-            # channels, then the head): bytes per call = all of them / calls (one head each)
+            # channels, then for the float kinds the head): bytes per call = all of them /
+            # calls (one head kernel per float call; the exact kind's inverse-column kernel
+            # runs once per chunk of channels)
             if not calls:
-                raise RuntimeError("%s: no head_kernel dispatch to count four-step calls" % d)
-            return float(sum(hot.values())) / len(calls) * 1024.0 * scale, scale
+                raise RuntimeError("%s: no dispatch to count four-step calls" % d)
+            ncalls = len(calls)
+            if w.storage == "i32":
+                import fft_causal_long_amd as sc
+                M = 1 << (w.L - 1).bit_length()
+                per_chunk = sc.sc_workspace_bytes(sc.KIND_NTT_I32, w.B, w.C, w.L) // (24 * M)
+                ncalls = len(calls) / -(-w.channels // per_chunk)
+            return float(sum(hot.values())) / ncalls * 1024.0 * scale, scale
         return float(np.mean(list(hot.values()))) * 1024.0 * scale, scale
 
     fetch, fs = per_dispatch(fetch_dir, "FETCH_SIZE")
@@ -755,7 +766,10 @@ def other_measure(sc, torch, w, dev, steps: int, warmup: int, oracle_too: bool =
             pick = np.sort(rng.choice(w.B * w.C, size=min(64, w.B * w.C), replace=False))
             vs, gs = v.reshape(-1, w.L)[pick], g.reshape(-1, w.L)[pick]
             t0 = time.perf_counter()
-            oracle.causal_conv_f64(vs, gs, nthreads=nt, with_scale=False)
+            if w.storage == "i32":
+                oracle.causal_conv_i64(vs, gs, nthreads=nt)
+            else:
+                oracle.causal_conv_f64(vs, gs, nthreads=nt, with_scale=False)
             dt = time.perf_counter() - t0
             rec["cpu_oracle"] = {"value": round(len(pick) * w.L / dt, 1), "unit": "outputs/s",
                                  "cores": nt, "kind": "oracle", "extrapolated": True,
@@ -941,10 +955,10 @@ def main(argv=None):
     if not args.no_fixed and w.storage != "i32" and w.L <= 4096:
         rec["fixed"] = fixed_measure(sc, torch, w, dev, max(5, args.steps // 5), 2)
     if not args.no_others and args.config == 3:
-        # Tiny, Small, the Medium shape in fp32, exact, long (four-step)
+        # Tiny, Small, the Medium shape in fp32, exact, long (four-step), long exact
         rec["other_workloads"] = [other_measure(sc, torch, WORKLOADS[c], dev, 20, 3,
                                                 not args.no_cpu_baseline)
-                                  for c in (1, 2, 6, 5, 4)]
+                                  for c in (1, 2, 6, 5, 4, 7)]
     if not args.no_leakage:
         rec["leakage"] = leakage_probe(sc, torch, dev)
     if not args.no_cpu_baseline:

@@ -26,10 +26,11 @@
 // transform); between radix passes the values go through LDS.  A workgroup of
 // max(64, M/8) threads serves CPW channels (two branch units of TB threads per channel):
 // one channel from M = 512 on, as many as fill one wave below.  It uses
-// 2*CPW*(M + M/16) complex values of LDS (68 KB at M = 4096, two workgroups per CU).
-// Small workgroups let workgroups at different phases share a CU: at M = 1024 one channel
-// per workgroup took 44 -> 39 us against four channels per 512-thread workgroup, at M = 256
-// (64 channels) 11 -> 7 us, bit for bit the same.
+// 2*CPW*(M + M/16 + 24) complex values of LDS (35 KB at M = 2048).  Small workgroups let
+// workgroups at different phases share a CU: at M = 1024 one channel per workgroup took
+// 44 -> 39 us against four channels per 512-thread workgroup, at M = 256 (64 channels)
+// 11 -> 7 us, bit for bit the same.  The library sends M = 4096 (2048 < L <= 4096) to the
+// kernel of sc_fused4k.hip; this one serves it only as the reference form.
 // HBM traffic is read v, read g, write r: nothing else leaves the chip.
 
 #include "sc_device.h"

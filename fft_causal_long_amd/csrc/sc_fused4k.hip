@@ -30,7 +30,10 @@
 //    through LDS; each thread then forms 4 of its 8 pairs (its mirror forms the other 4).
 //    Y is stored even bins first (Y_{2i} at i, Y_{2i+1} at 2064 + i), which keeps both its
 //    writes and the inverse's reads free of bank conflicts.
-//  * The inverse's last pass computes only the 8 outputs of each item that are kept.
+//  * The inverse's last pass computes only the 8 outputs of each item that are kept.  Unit 1
+//    computes the direct head meanwhile and then, for bf16 storage, touches the inputs of
+//    the workgroup that will take this one's place (see touch_line), so that it starts
+//    from L2 instead of HBM.
 
 #include "sc_device.h"
 #include "sc_fft_lds.h"

@@ -60,6 +60,7 @@ struct DeviceState {
     sc::NttMfmaTables mfma{};     // the matrix-core NTT kernel's tables (prime A)
     bool mfma_ready = false;
     std::map<int, sc::FsTw> fs;     // four-step tables by M
+    std::map<int, const double*> ntt4;   // four-step NTT tables (w_N^j, j < 2M) by M
     // the four-step path's second stream (default priority, non-blocking) and its fork/join
     // events; fs_mu keeps one call's fork, launches and join together, since the events are
     // shared by every call on the device
@@ -351,6 +352,38 @@ sc_status fourstep_tables(DeviceState& d, int M, sc::FsTw* out, hipStream_t stre
     return SC_OK;
 }
 
+// the four-step NTT's table for transform length M: w_N^j (N = 2M, j < N) modulo prime A as
+// float64 pairs (w, w / p), made on first use; under graph capture (or with may_build false)
+// a missing table is SC_ERR_UNSUPPORTED.  Caller holds g_mu.
+sc_status ntt4_table(DeviceState& d, int M, const double** out, hipStream_t stream,
+                     bool may_build = true)
+{
+    auto it = d.ntt4.find(M);
+    if (it != d.ntt4.end()) {
+        *out = it->second;
+        return SC_OK;
+    }
+    if (!may_build) return SC_ERR_UNSUPPORTED;
+    const sc_status cs = capture_forbids_build(stream);
+    if (cs != SC_OK) return cs;
+    const uint64_t p = sc::NTT_PRIMES[0];
+    const int64_t N = 2 * (int64_t)M;
+    const uint64_t w = powmod(3, (p - 1) / (uint64_t)N, p);
+    std::vector<double> h(2 * (size_t)N);
+    uint64_t x = 1;
+    for (int64_t j = 0; j < N; ++j) {
+        h[2 * j] = (double)x;
+        h[2 * j + 1] = (double)x / (double)p;
+        x = x * w % p;
+    }
+    void* dp = nullptr;
+    const sc_status st = upload(h.data(), h.size() * sizeof(double), &dp);
+    if (st != SC_OK) return st;
+    d.ntt4[M] = (const double*)dp;
+    *out = (const double*)dp;
+    return SC_OK;
+}
+
 size_t elt_size(sc_kind k) { return k == SC_KIND_BF16 ? 2 : 4; }
 
 int64_t next_pow2(int64_t x)
@@ -410,8 +443,9 @@ sc_status resolve_path(sc_kind kind, int64_t L, int32_t requested, sc_path* out)
     switch (requested) {
     case SC_PATH_AUTO:
         if (!fl) {
-            if (L > kMaxLNtt) return SC_ERR_UNSUPPORTED;
-            *out = SC_PATH_FUSED;
+            if (L <= kMaxLNtt) *out = SC_PATH_FUSED;
+            else if (kind == SC_KIND_NTT_I32 && L <= sc::NTT4_MAX_L) *out = SC_PATH_FOUR_STEP;
+            else return SC_ERR_UNSUPPORTED;
         } else if (L <= sc::DIRECT_MAX_L) {
             *out = SC_PATH_DIRECT;
         } else if (L <= kMaxLFused) {
@@ -431,7 +465,14 @@ sc_status resolve_path(sc_kind kind, int64_t L, int32_t requested, sc_path* out)
         *out = SC_PATH_DIRECT;
         return SC_OK;
     case SC_PATH_FOUR_STEP:
-        if (!fl || L < kMinLFourStep || L > sc::FOURSTEP_MAX_L) return SC_ERR_UNSUPPORTED;
+        if (!fl) {
+            // the exact kind's four-step split has rows of 4096: L above the fused range only
+            if (kind != SC_KIND_NTT_I32 || L <= kMaxLNtt || L > sc::NTT4_MAX_L)
+                return SC_ERR_UNSUPPORTED;
+            *out = SC_PATH_FOUR_STEP;
+            return SC_OK;
+        }
+        if (L < kMinLFourStep || L > sc::FOURSTEP_MAX_L) return SC_ERR_UNSUPPORTED;
         *out = SC_PATH_FOUR_STEP;
         return SC_OK;
     case SC_PATH_NTT_MFMA:
@@ -464,11 +505,18 @@ sc_status fourstep_streams(DeviceState& d)
 }
 
 // four-step scratch: channels per chunk and bytes needed
-void fourstep_plan(int64_t nch, int64_t L, int64_t* chunk, size_t* bytes,
-                   int64_t budget = kFourStepChunkBytes)
+// scratch bytes per channel of the four-step path of this kind
+size_t fourstep_per_channel(sc_kind kind, int64_t L)
 {
     const int M = (int)next_pow2(L);
-    const int64_t per = (int64_t)sc::fourstep_bytes_per_channel(M);
+    return kind == SC_KIND_NTT_I32 ? sc::ntt4_bytes_per_channel(M)
+                                   : sc::fourstep_bytes_per_channel(M);
+}
+
+void fourstep_plan(sc_kind kind, int64_t nch, int64_t L, int64_t* chunk, size_t* bytes,
+                   int64_t budget = kFourStepChunkBytes)
+{
+    const int64_t per = (int64_t)fourstep_per_channel(kind, L);
     int64_t c = budget / per;
     if (c < 1) c = 1;
     if (c > nch) c = nch;
@@ -519,10 +567,10 @@ sc_status run_jobs(sc_kind kind, const Job* jobs, int njobs, bool rev, int64_t n
     size_t need = 0;
     int64_t chunk = 0;
     if (path == SC_PATH_FOUR_STEP) {
-        if (noalloc &&
-            sc::fourstep_bytes_per_channel((int)next_pow2(L)) > (size_t)ws_bytes)
+        if (noalloc && fourstep_per_channel(kind, L) > (size_t)ws_bytes)
             return SC_ERR_UNSUPPORTED;
-        fourstep_plan(nch, L, &chunk, &need, noalloc ? (int64_t)ws_bytes : kFourStepChunkBytes);
+        fourstep_plan(kind, nch, L, &chunk, &need,
+                      noalloc ? (int64_t)ws_bytes : kFourStepChunkBytes);
     }
     if (need > 0) {
         if (ws) {
@@ -559,6 +607,28 @@ sc_status run_jobs(sc_kind kind, const Job* jobs, int njobs, bool rev, int64_t n
         for (int k = 0; k < njobs && e == hipSuccess; ++k)
             e = sc::launch_ntt_mfma((const int32_t*)jobs[k].a, (const int32_t*)jobs[k].b,
                                     (int32_t*)jobs[k].o, nch, (int)L, M, rev, d->mfma, stream);
+        return e == hipSuccess ? SC_OK : SC_ERR_HIP;
+    }
+    if (kind == SC_KIND_NTT_I32 && path == SC_PATH_FOUR_STEP) {
+        const int M = (int)next_pow2(L);
+        const double* wtab = nullptr;
+        {
+            std::lock_guard<std::mutex> lk(g_mu);
+            st = ntt4_table(*d, M, &wtab, stream, !noalloc);
+        }
+        if (st != SC_OK) return st;
+        void* scratch = ws;
+        bool own = false;
+        if (!ws) {
+            if (hipMallocAsync(&scratch, need, stream) != hipSuccess) return SC_ERR_HIP;
+            own = true;
+        }
+        for (int k = 0; k < njobs && e == hipSuccess; ++k)
+            e = sc::launch_ntt4((const int32_t*)jobs[k].a, (const int32_t*)jobs[k].b,
+                                (int32_t*)jobs[k].o, nch, (int)L, M, rev, d->ntt[0], wtab,
+                                scratch, need, chunk, stream);
+        if (own && hipFreeAsync(scratch, stream) != hipSuccess && e == hipSuccess)
+            e = hipErrorUnknown;
         return e == hipSuccess ? SC_OK : SC_ERR_HIP;
     }
     if (kind == SC_KIND_NTT_I32) {
@@ -689,7 +759,7 @@ sc_status blc_plan(sc_kind kind, int64_t B, int64_t L, int64_t C, const sc_optio
     p->inner = 0;
     if (path == SC_PATH_FOUR_STEP) {
         int64_t chunk;
-        fourstep_plan(nch, L, &chunk, &p->inner);
+        fourstep_plan(kind, nch, L, &chunk, &p->inner);
     }
     p->total = (size_t)nstage * p->stage + align256(p->inner);
     return SC_OK;
@@ -868,7 +938,7 @@ size_t sc_workspace_bytes(sc_kind kind, int64_t B, int64_t C, int64_t L)
         if (path != SC_PATH_FOUR_STEP) return 0;
         int64_t chunk;
         size_t need;
-        fourstep_plan(B * C, L, &chunk, &need);
+        fourstep_plan(kind, B * C, L, &chunk, &need);
         return need;
     } catch (...) {
         return 0;
@@ -1387,8 +1457,12 @@ sc_status sc_prepare(sc_kind kind, int64_t L)
         DeviceState* d = nullptr;
         st = device_state(&d, exact_kind(kind), nullptr);
         if (st != SC_OK || path != SC_PATH_FOUR_STEP) return st;
-        sc::FsTw tw;
         std::lock_guard<std::mutex> lk(g_mu);
+        if (kind == SC_KIND_NTT_I32) {
+            const double* wtab = nullptr;
+            return ntt4_table(*d, (int)next_pow2(L), &wtab, nullptr);
+        }
+        sc::FsTw tw;
         return fourstep_tables(*d, (int)next_pow2(L), &tw, nullptr);
     });
 }

@@ -116,6 +116,17 @@ struct NttMfmaTables {
 hipError_t launch_ntt_mfma(const int32_t* v, const int32_t* g, int32_t* r, int64_t nch, int L,
                            int M, bool rev, const NttMfmaTables& tables, hipStream_t stream);
 
+// Exact NTT causal convolution for FUSED_MAX_L < L <= NTT4_MAX_L through the four-step split
+// (sc_ntt.hip): M = next power of two >= L, chunks of `chunk` channels, each needing
+// ntt4_bytes_per_channel(M) bytes of ws (ws_bytes >= chunk * that); wtab = the per-M table
+// of w_N^j, j < 2M (float64 pairs w, w/p).  Modulo prime A, output lifted to the balanced
+// range; rev as for launch_ntt.
+constexpr int NTT4_MAX_L = 65536;
+size_t ntt4_bytes_per_channel(int M);
+hipError_t launch_ntt4(const int32_t* v, const int32_t* g, int32_t* r, int64_t nch, int L, int M,
+                       bool rev, const NttTables& tables, const double* wtab, void* ws,
+                       size_t ws_bytes, int64_t chunk, hipStream_t stream);
+
 // Exact real-valued causal convolution: V = round(v 2^fv), G = round(g 2^fg), the exact
 // integer sum R from its residues modulo primes A, B, C (tables[0..2]), all in one kernel,
 // then r = round_f32(R 2^-(fv+fg)).  Uses no scratch.

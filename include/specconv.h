@@ -44,10 +44,10 @@
  *    device that needs it (a blocking host-to-device copy) and kept until the process ends:
  *    the float twiddle bank (every call), the modular tables (the first call of an exact
  *    kind: SC_KIND_NTT_I32 or SC_KIND_FIXED_F32), and the four-step tables (the first
- *    four-step call at each transform length M = next power of two >= L).  A call whose
+ *    four-step call of a kind at each transform length M = next power of two >= L).  A call whose
  *    `stream` is being captured into a graph and that would have to build a table returns
  *    SC_ERR_UNSUPPORTED and enqueues nothing; sc_prepare builds them beforehand.  Also,
- *    for the four-step path (L > 4096), a second stream and two events per
+ *    for the float four-step path (L > 4096), a second stream and two events per
  *    device, made on first use: such a call may run half of its channel chunks on that
  *    stream, which waits for `stream` at the start of the call, and `stream` waits for it
  *    at the end, so the call stays ordered on `stream` as a whole.  While `stream` is being
@@ -100,7 +100,8 @@ typedef enum sc_path {
 /* Optional controls for sc_causal_conv_ex (testing and experiments). */
 typedef struct sc_options {
     int32_t path;      /* sc_path; SC_PATH_AUTO picks: L <= 32 direct, L <= 4096 fused,
-                          larger L four-step (the exact kinds: fused)                 */
+                          larger L four-step (SC_KIND_NTT_I32: fused up to 4096,
+                          four-step up to 65536; SC_KIND_FIXED_F32: fused)             */
     int32_t head;      /* float kinds: outputs t < head are computed by direct fp32
                           summation instead of the transform.  -1 = default (32);
                           0 disables; odd values are rounded up to even; at most 64.  */
@@ -140,7 +141,11 @@ sc_status sc_causal_conv_bf16(const uint16_t* v, const uint16_t* g, uint16_t* r,
  *       r_t = the residue of sum_{j<=t} v_j g_{t-j} mod p, in [-(p-1)/2, (p-1)/2].
  *   It equals the integer sum whenever |sum| <= (p-1)/2 = 499,122,176: a caller
  *   precondition (see sc_ntt_range_ok).  Output t depends on v_0..v_t, g_0..g_t only, bit
- *   for bit.  Largest L: 4096 (the transform is held in LDS); no allocation.
+ *   for bit.  L <= 4096: the transform is held in LDS, no allocation.  4096 < L <= 65536:
+ *   the four-step split (column transforms, rows of 4096 in LDS, inverse columns) through
+ *   scratch of 24 M bytes per channel in chunks (sc_workspace_bytes(SC_KIND_NTT_I32, ...)),
+ *   allocated stream-ordered by this call; the _ws variant takes it from the caller.
+ *   Largest L: 65536.
  */
 sc_status sc_causal_conv_ntt_i32(const int32_t* v, const int32_t* g, int32_t* r, int64_t B,
                                  int64_t C, int64_t L, hipStream_t stream);

@@ -24,7 +24,7 @@ int main(void)
     CHECK(sc_causal_conv_bf16(0, 0, 0, 1, 1, 1, 0) == SC_ERR_INVALID_ARGUMENT);
     /* lengths beyond a kind's path (placeholder pointers, never dereferenced) */
     CHECK(sc_causal_conv_ntt_i32((const int32_t*)0x100000, (const int32_t*)0x200000,
-                                 (int32_t*)0x300000, 1, 1, 8192, 0) == SC_ERR_UNSUPPORTED);
+                                 (int32_t*)0x300000, 1, 1, 65537, 0) == SC_ERR_UNSUPPORTED);
     /* empty calls are no-ops */
     CHECK(sc_causal_conv_f32(0, 0, 0, 0, 4, 64, 0) == SC_OK);
     /* sizes */

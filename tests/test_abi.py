@@ -83,13 +83,18 @@ def test_host_validation(sc, fn):
 def test_unsupported_lengths_rejected_before_launch(sc):
     h = sc.lib()
     UNSUP = sc.SC_ERR_UNSUPPORTED
-    assert h.sc_causal_conv_ntt_i32(A, B_, C_, 1, 1, 5000, None) == UNSUP
+    assert h.sc_causal_conv_ntt_i32(A, B_, C_, 1, 1, 65537, None) == UNSUP   # four-step NTT max
     far = (1 << 32, 2 << 32, 3 << 32)                  # fake, far enough apart not to overlap
     assert h.sc_causal_conv_f32(*far, 1, 1, 2**22 + 1, None) == UNSUP
     opt = sc.sc_options(sc.PATH_FOUR_STEP, -1)         # the split needs L > 2048
     assert h.sc_causal_conv_ex(0, A, B_, C_, 1, 1, 2048, ctypes.byref(opt), None, 0, None) == UNSUP
     opt = sc.sc_options(sc.PATH_FUSED, -1)             # one workgroup holds at most L = 4096
     assert h.sc_causal_conv_ex(0, A, B_, C_, 1, 1, 4097, ctypes.byref(opt), None, 0, None) == UNSUP
+    assert h.sc_causal_conv_ex(2, A, B_, C_, 1, 1, 4097, ctypes.byref(opt), None, 0, None) == UNSUP
+    # the exact four-step split has rows of 4096: forced only above the fused range, int32 only
+    opt = sc.sc_options(sc.PATH_FOUR_STEP, -1)
+    assert h.sc_causal_conv_ex(2, A, B_, C_, 1, 1, 4096, ctypes.byref(opt), None, 0, None) == UNSUP
+    assert h.sc_causal_conv_ex(3, A, B_, C_, 1, 1, 5000, ctypes.byref(opt), None, 0, None) == UNSUP
 
 
 def test_options_validation(sc):
@@ -121,7 +126,8 @@ def test_host_helpers(sc):
     # sc_prepare: argument checks on the host; an empty length needs no table
     assert sc.sc_prepare(7, 64) == sc.SC_ERR_INVALID_ARGUMENT
     assert sc.sc_prepare(sc.KIND_F32, -1) == sc.SC_ERR_INVALID_ARGUMENT
-    assert sc.sc_prepare(sc.KIND_NTT_I32, 5000) == sc.SC_ERR_UNSUPPORTED
+    assert sc.sc_prepare(sc.KIND_NTT_I32, 65537) == sc.SC_ERR_UNSUPPORTED
+    assert sc.sc_prepare(sc.KIND_FIXED_F32, 5000) == sc.SC_ERR_UNSUPPORTED
     assert sc.sc_prepare(sc.KIND_F32, 2**22 + 1) == sc.SC_ERR_UNSUPPORTED
     assert sc.sc_prepare(sc.KIND_BF16, 0) == sc.SC_OK
     assert sc.sc_workspace_bytes(sc.KIND_F32, 8, 1024, 4096) == 0
@@ -129,6 +135,11 @@ def test_host_helpers(sc):
     assert sc.sc_workspace_bytes(sc.KIND_F32, 1, 1536, 65536) > 0
     assert sc.sc_workspace_bytes(sc.KIND_BF16, 1, 1, 5000) > 0
     assert sc.sc_workspace_bytes(sc.KIND_NTT_I32, 1, 1, 4096) == 0
+    # the exact four-step path: 24 M bytes per channel (T: 2 branches x 2 arrays, S: 2 branches
+    # of M int32), chunked
+    assert sc.sc_workspace_bytes(sc.KIND_NTT_I32, 1, 3, 5000) == 3 * 24 * 8192
+    assert sc.sc_workspace_bytes(sc.KIND_NTT_I32, 1, 1, 65536) == 24 * 65536
+    assert sc.sc_workspace_bytes(sc.KIND_NTT_I32, 1, 1, 65537) == 0
     assert sc.sc_workspace_bytes(sc.KIND_F32, -1, 1, 65536) == 0
     assert sc.sc_workspace_bytes(sc.KIND_F32, 1, 1, 2**23) == 0      # above the maximum
 
@@ -174,7 +185,7 @@ def test_bwd_host_validation(sc, fn):
 def test_bwd_unsupported_and_options(sc):
     h = sc.lib()
     UNSUP, INVALID = sc.SC_ERR_UNSUPPORTED, sc.SC_ERR_INVALID_ARGUMENT
-    assert h.sc_causal_conv_bwd_ntt_i32(A, B_, C_, D_, E_, 1, 1, 5000, None) == UNSUP
+    assert h.sc_causal_conv_bwd_ntt_i32(A, B_, C_, D_, E_, 1, 1, 65537, None) == UNSUP
     far = [k << 32 for k in range(1, 6)]
     assert h.sc_causal_conv_bwd_f32(*far, 1, 1, 2**22 + 1, None) == UNSUP
     opt = sc.sc_options(sc.PATH_FUSED, -1)
@@ -305,7 +316,10 @@ def test_token_major_host_checks(sc):
     inner = sc.sc_workspace_bytes(F32, 1, 128, 65536)
     assert inner > 0
     assert sc.sc_blc_workspace_bytes(F32, 1, 65536, 1536) == 3 * 32 * MiB + (inner + 255) // 256 * 256
-    assert sc.sc_blc_workspace_bytes(NTT, 1, 8192, 4) == 0          # beyond the exact path
+    # the exact kind above 4096: three staging buffers plus the four-step NTT's 24 M bytes
+    # per channel
+    assert sc.sc_blc_workspace_bytes(NTT, 1, 8192, 4) == 3 * 4 * 8192 * 4 + 4 * 24 * 8192
+    assert sc.sc_blc_workspace_bytes(NTT, 1, 65537, 4) == 0         # beyond the exact paths
     assert sc.sc_blc_workspace_bytes(F32, 0, 64, 4) == 0
     assert sc.sc_blc_workspace_bytes(7, 1, 64, 4) == 0
 
@@ -322,7 +336,7 @@ def test_token_major_host_checks(sc):
     assert f(F32, A, B_, C_, -1, 64, 4, None, W, need, None) == INVALID
     assert f(F32, A, B_, C_, 2, 64, 4, ctypes.byref(sc.sc_options(9, -1)), W, need,
              None) == INVALID
-    assert f(NTT, A, B_, C_, 2, 8192, 4, None, W, need, None) == UNSUP
+    assert f(NTT, A, B_, C_, 1, 65537, 1, None, None, 0, None) == UNSUP     # beyond the exact paths
     assert f(F32, 1 << 40, 2 << 40, 3 << 40, 1, (1 << 22) + 1, 1, None, None, 0, None) == UNSUP
     assert f(F32, None, None, None, 0, 64, 4, ctypes.byref(opt), None, 0, None) == OK
     for name in ("sc_causal_conv_blc_f32", "sc_causal_conv_blc_bf16"):

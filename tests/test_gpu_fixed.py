@@ -46,7 +46,7 @@ def check(sc, v, g, fv, fg, what, chans=None):
         what, int(diff.sum()), diff.size, np.argwhere(diff)[0], r[diff][0], ref[diff][0])
 
 
-@pytest.mark.parametrize("L", [1, 2, 33, 64, 100, 257, 1000, 2048, 3000, 4095, 4096])
+@pytest.mark.parametrize("L", [1, 2, 33, 64, 100, 128, 200, 256, 257, 513, 1000, 2048, 3000, 4095, 4096])
 def test_lengths_bit_exact(sc, L):
     v, g = make_inputs(WORKLOADS[2], B=1, C=6, L=L, seed_offset=L)
     check(sc, v, g, 24, 24, "L=%d" % L)

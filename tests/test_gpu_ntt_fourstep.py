@@ -1,0 +1,170 @@
+"""GPU parity of the exact NTT path above L = 4096 (the four-step split: column transforms,
+rows of 4096 in LDS, inverse columns) against the int64 oracle: bit for bit.
+
+Lengths up to 16384 are checked at every output against the full oracle; the long-context
+shape (C = 1536, L = 65536) on seeded sampled outputs, which the oracle sums one by one
+(integer sums below 2^31, exact in float64).  The inputs are the exact workload's
+distribution (uniform integers in [-127, 127]), whose sums stay far below (p-1)/2, so the
+lifted residue is the integer itself.  Leakage ("Catastrophic Token Leakage ...", abstract:
+integer transforms cannot leak) is checked as for the fused path: outputs t < s bitwise
+unchanged when v_s changes.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from tests.gpu_util import to_device, to_host
+from workloads import WORKLOADS, make_inputs, make_grad
+
+pytestmark = pytest.mark.gpu
+P = oracle.P_NTT
+W5 = WORKLOADS[5]
+
+
+@pytest.fixture(scope="module")
+def sc():
+    import fft_causal_long_amd as m
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    return m
+
+
+def run(sc, v, g, **kw):
+    out = sc.causal_conv(to_device(v), to_device(g), **kw)
+    torch.cuda.synchronize()
+    return to_host(out)
+
+
+def assert_exact(r, ref, what):
+    ref = oracle.lift_mod_p(ref)
+    mism = np.count_nonzero(r.astype(np.int64) != ref)
+    assert mism == 0, "%s: %d mismatches" % (what, mism)
+
+
+@pytest.mark.parametrize("L", [4097, 5000, 8192, 8193, 12345, 16384])
+def test_lengths_bit_exact(sc, L):
+    v, g = make_inputs(W5, B=1, C=3, L=L, seed_offset=L)
+    r = run(sc, v, g)
+    assert_exact(r, oracle.causal_conv_i64(v, g), "L=%d" % L)
+
+
+def test_forced_path_equals_automatic(sc):
+    v, g = make_inputs(W5, B=2, C=2, L=6000, seed_offset=21)
+    a = run(sc, v, g)
+    b = run(sc, v, g, path=sc.PATH_FOUR_STEP)
+    assert np.array_equal(a, b)
+
+
+def test_full_range_inputs_wrap_mod_p(sc):
+    # int32 inputs of any size are reduced mod p; the result is the lifted residue of the
+    # integer sum, which here exceeds (p-1)/2
+    rng = np.random.default_rng(np.random.SeedSequence([5, 77]))
+    L = 4500
+    v = rng.integers(-2**31, 2**31, size=(1, 2, L), dtype=np.int64).astype(np.int32)
+    g = rng.integers(-2**31, 2**31, size=(1, 2, L), dtype=np.int64).astype(np.int32)
+    r = run(sc, v, g)
+    vm, gm = np.mod(v.astype(np.int64), P), np.mod(g.astype(np.int64), P)
+    for c in range(2):
+        for t in (0, 1, 2047, 4095, 4096, L - 1):
+            s = 0
+            for j in range(t + 1):
+                s = (s + int(vm[0, c, j]) * int(gm[0, c, t - j])) % P
+            want = s - P if s > (P - 1) // 2 else s
+            assert int(r[0, c, t]) == want, (c, t)
+
+
+def test_gradients_bit_exact(sc):
+    L = 5000
+    v, g = make_inputs(W5, B=1, C=2, L=L, seed_offset=31)
+    dr = make_grad(W5, B=1, C=2, L=L, seed_offset=31)
+    dv, dg = sc.causal_conv_bwd(to_device(dr), to_device(v), to_device(g))
+    torch.cuda.synchronize()
+    rdv, rdg = oracle.causal_conv_bwd_i64(dr, v, g)
+    assert_exact(to_host(dv), rdv, "dv")
+    assert_exact(to_host(dg), rdg, "dg")
+
+
+def test_leakage_is_exactly_zero(sc):
+    L = 8192
+    v, g = make_inputs(W5, B=1, C=1, L=L, seed_offset=41)
+    pos = [1, 4096, 4097, 5000, L - 1]
+    rows = [v[0, 0]] + [v[0, 0].copy() for _ in pos]
+    for i, s in enumerate(pos):
+        rows[i + 1][s] += 100
+    vv = np.stack(rows)[None]
+    gg = np.repeat(g, len(rows), axis=1)
+    r = run(sc, vv, gg)[0]
+    for i, s in enumerate(pos):
+        assert np.array_equal(r[i + 1, :s], r[0, :s]), "leak before s=%d" % s
+        assert not np.array_equal(r[i + 1, s:], r[0, s:])
+
+
+def test_long_context_shape_sampled(sc):
+    # the long-context shape, several chunks of channels: 128 seeded outputs on each of
+    # 32 seeded channels against sums computed one by one
+    w = WORKLOADS[4]
+    v, g = make_inputs(W5, B=w.B, C=w.C, L=w.L, seed_offset=51)
+    r = run(sc, v, g).reshape(-1, w.L)
+    rng = np.random.default_rng(np.random.SeedSequence([4, 51]))
+    chans = rng.choice(w.C, size=32, replace=False)
+    ch = np.repeat(np.arange(chans.size), 128)
+    t = rng.integers(0, w.L, size=ch.size)
+    t[:32] = w.L - 1
+    # the sampled channels widened to float64, exactly (integer sums below 2^31)
+    vs = v.reshape(-1, w.L)[chans].astype(np.float64)
+    gs = g.reshape(-1, w.L)[chans].astype(np.float64)
+    want, _ = oracle.causal_conv_f64_at(vs, gs, ch, t)
+    got = r[chans[ch], t].astype(np.int64)
+    assert np.array_equal(got, oracle.lift_mod_p(np.rint(want).astype(np.int64)))
+
+
+def test_workspace_variant_and_token_major(sc):
+    L = 8192
+    v, g = make_inputs(W5, B=2, C=3, L=L, seed_offset=61)
+    a = run(sc, v, g)
+    need = sc.sc_workspace_bytes(sc.KIND_NTT_I32, 2, 3, L)
+    assert need == 6 * 24 * L
+    ws = torch.empty(need, dtype=torch.uint8, device="cuda:0")
+    b = run(sc, v, g, workspace=ws)
+    assert np.array_equal(a, b)
+    vt = to_device(np.ascontiguousarray(v.transpose(0, 2, 1)))
+    gt = to_device(np.ascontiguousarray(g.transpose(0, 2, 1)))
+    rt = sc.causal_conv_blc(vt, gt)
+    torch.cuda.synchronize()
+    assert np.array_equal(to_host(rt).transpose(0, 2, 1), a)
+
+
+def test_allocation_free_call(sc):
+    L = 16384
+    v, g = make_inputs(W5, B=1, C=5, L=L, seed_offset=71)
+    a = run(sc, v, g)
+    assert sc.sc_prepare(sc.KIND_NTT_I32, L) == sc.SC_OK
+    tv, tg = to_device(v), to_device(g)
+    out = torch.empty_like(tv)
+    st = sc.sc_causal_conv_noalloc(sc.KIND_NTT_I32, tv.data_ptr(), tg.data_ptr(), out.data_ptr(),
+                                   1, 5, L, torch.cuda.current_stream().cuda_stream)
+    assert st == sc.SC_OK, sc.sc_status_string(st)
+    torch.cuda.synchronize()
+    assert np.array_equal(to_host(out), a)
+
+
+def test_graph_capture_after_prepare(sc):
+    L = 12288
+    v, g = make_inputs(W5, B=1, C=4, L=L, seed_offset=81)
+    assert sc.sc_prepare(sc.KIND_NTT_I32, L) == sc.SC_OK
+    tv, tg = to_device(v), to_device(g)
+    need = sc.sc_workspace_bytes(sc.KIND_NTT_I32, 1, 4, L)
+    ws = torch.empty(need, dtype=torch.uint8, device="cuda:0")
+    eager = sc.causal_conv(tv, tg, workspace=ws)
+    torch.cuda.synchronize()
+    out = torch.empty_like(tv)
+    s = torch.cuda.Stream()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=s):
+        sc.causal_conv(tv, tg, out, workspace=ws)
+    for _ in range(3):
+        out.fill_(0)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, eager)

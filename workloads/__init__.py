@@ -24,6 +24,8 @@ projection; main and ablation tables give the model sizes and the 4096 context):
  4     1           1536  65536  fp32    sigmoid(N(0,1)) * exp(-t / 16384)
  5     4           768   4096   int32   uniform integers in [-127, 127] (v likewise)
  6     8           1024  4096   fp32    the draws of 3 (same seeds) stored as fp32
+ 7     1           1536  65536  int32   uniform integers in [-127, 127] (v likewise): the
+                                        long-context shape of 4 for the exact kind
 =====  ==========  ====  =====  ======  ====================================================
 
 For 1-4, v ~ N(0,1).  The datasets the pages evaluate on are not used; these synthetic
@@ -64,6 +66,8 @@ WORKLOADS = {
     5: Workload(5, "ntt-i32-B4-C768-L4096", 4, 768, 4096, "i32", "int"),
     # the Medium shape with fp32 storage: same seeds (cid 3) as workload 3
     6: Workload(3, "medium-mhf-f32-B8-C1024-L4096", 8, 1024, 4096, "f32", "conv", 16),
+    # the long-context shape with the exact workload's integers (four-step NTT)
+    7: Workload(7, "long-exact-i32-B1-C1536-L65536", 1, 1536, 65536, "i32", "int"),
 }
 
 
