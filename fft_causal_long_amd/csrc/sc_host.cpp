@@ -352,9 +352,9 @@ sc_status fourstep_tables(DeviceState& d, int M, sc::FsTw* out, hipStream_t stre
     return SC_OK;
 }
 
-// the four-step NTT's table for transform length M: w_N^j (N = 2M, j < N) modulo prime A as
-// float64 pairs (w, w / p), made on first use; under graph capture (or with may_build false)
-// a missing table is SC_ERR_UNSUPPORTED.  Caller holds g_mu.
+// the four-step NTT's tables for transform length M (modulo prime A, as doubles, made on
+// first use): w_N^j (N = 2M, j < N) and the column and row twiddles in lane order; under
+// graph capture (or with may_build false) a missing table is SC_ERR_UNSUPPORTED.  Caller holds g_mu.
 sc_status ntt4_table(DeviceState& d, int M, const double** out, hipStream_t stream,
                      bool may_build = true)
 {
@@ -369,13 +369,23 @@ sc_status ntt4_table(DeviceState& d, int M, const double** out, hipStream_t stre
     const uint64_t p = sc::NTT_PRIMES[0];
     const int64_t N = 2 * (int64_t)M;
     const uint64_t w = powmod(3, (p - 1) / (uint64_t)N, p);
-    std::vector<double> h(2 * (size_t)N);
+    // w_N^j, j < N; then w_N^{n1 (2 k2 + b)} at [b][k2][n1]; then w_M^{-m1 k2} at [k2][m1]
+    const int64_t M2 = 4096, M1 = M / M2;
+    std::vector<uint64_t> pw((size_t)N);
     uint64_t x = 1;
     for (int64_t j = 0; j < N; ++j) {
-        h[2 * j] = (double)x;
-        h[2 * j + 1] = (double)x / (double)p;
+        pw[j] = x;
         x = x * w % p;
     }
+    std::vector<double> h((size_t)N + 2 * (size_t)M + (size_t)M);
+    for (int64_t j = 0; j < N; ++j) h[j] = (double)pw[j];
+    for (int64_t b = 0; b < 2; ++b)
+        for (int64_t k2 = 0; k2 < M1; ++k2)
+            for (int64_t n1 = 0; n1 < M2; ++n1)
+                h[N + (b * M1 + k2) * M2 + n1] = (double)pw[(n1 * (2 * k2 + b)) % N];
+    for (int64_t k2 = 0; k2 < M1; ++k2)
+        for (int64_t m1 = 0; m1 < M2; ++m1)
+            h[2 * N + k2 * M2 + m1] = (double)pw[(2 * (M - (m1 * k2) % M)) % N];
     void* dp = nullptr;
     const sc_status st = upload(h.data(), h.size() * sizeof(double), &dp);
     if (st != SC_OK) return st;

@@ -725,15 +725,16 @@ hipError_t launch_fixed(const float* v, const float* g, float* r, int64_t nch, i
 //   U_{M1 k1 + k2} = sum_{n1 < M2} w_M2^{n1 k1} [ w_M^{n1 k2} sum_{n2 < M1} u_{n1 + M2 n2} w_M1^{n2 k2} ]
 // and its inverse, for m = m1 + M2 m2, as
 //   e_m = sum_{k2 < M1} w_M1^{-m2 k2} [ w_M^{-m1 k2} sum_{k1 < M2} X_{M1 k1 + k2} w_M2^{-m1 k1} ].
-//  kernel A (columns): per (channel, branch b, array v or g, column n1), u^b_n = a_n w_N^{b n},
+//  kernel A (columns): per (channel, branch b, column n1), for v and g, u^b_n = a_n w_N^{b n},
 //     the length-M1 transform over n2 in registers, times w_M^{n1 k2} -> T[b][array][k2][n1];
 //  kernel B (rows): per (channel, branch, row k2), the length-M2 transforms of the v and g
 //     rows in LDS (the passes of the fused kernel), X = V G N^{-1}, the inverse over k1 (the
 //     forward transform read at (M2 - m1) mod M2), times w_M^{-m1 k2} -> S[b][k2][m1];
 //  kernel C (columns): per (channel, column m1), both branches' length-M1 inverses over k2
 //     give e^b at n = m1 + M2 m2; x_n = e^0_n + w_N^{-n} e^1_n, lifted and stored for n < L.
-// Values between kernels are int32 residues (|x| <= 1.5 p).  The table wtab holds w_N^j
-// (j < N = 2M) as W pairs; w_M^j is wtab[2 j].  HBM traffic per channel: read v, g; write
+// Values between kernels are int32 residues (|x| <= 1.5 p).  The per-M table holds, as
+// doubles, wtab[j] = w_N^j (j < N = 2M), then ta[b][k2][n1] = w_N^{n1 (2 k2 + b)}, then
+// tr[k2][m1] = w_M^{-m1 k2}, each laid out so that consecutive lanes read consecutive words.  HBM traffic per channel: read v, g; write
 // and read T (16 M bytes) and S (8 M bytes); write r.
 
 namespace ntt4 {
@@ -741,48 +742,69 @@ constexpr int M2 = 4096;
 constexpr int CT = 256;   // threads of the column kernels (one column each)
 }  // namespace ntt4
 
+// w_N^j from the table of doubles (j < N), as the W pair that mulc takes (w / p computed:
+// its rounding error keeps the quotient within one of the exact one, as for a stored w / p)
+__device__ __forceinline__ ntt::W ntt4_w(__amdgpu_buffer_rsrc_t rs, int j)
+{
+    const double w = __builtin_bit_cast(double, __builtin_amdgcn_raw_buffer_load_b64(rs, j * 8, 0, 0));
+    return ntt::W{w, w * (1.0 / (double)ntt::PrimeA::p)};
+}
+
+// Kernel A: thread (channel, branch b, column n1) transforms the v and the g column with the
+// same twiddles.  Branch 1's input rotation w_N^n, n = n1 + M2 n2, is w_N^{n1} w_2M1^{n2}:
+// the second factor is a constant per n2, and the first is merged into the output twiddle,
+// which becomes w_N^{n1 (2 k2 + b)} (w_M^{n1 k2} for b = 0): one read per output from the
+// table ta[b][k2][n1], consecutive across the lanes, shared by the two arrays.
 template <int M1, bool REV>
 __global__ __launch_bounds__(256) void ntt4_columns_fwd(const int32_t* __restrict__ v,
                                                         const int32_t* __restrict__ g,
                                                         int32_t* __restrict__ T, int64_t c0,
-                                                        int L, const double* __restrict__ wtab)
+                                                        int L, const double* __restrict__ ta)
 {
     using namespace ntt;
-    constexpr int M2 = ntt4::M2, M = M1 * M2, N = 2 * M, BPC = M2 / ntt4::CT;
+    constexpr int M2 = ntt4::M2, M = M1 * M2, BPC = M2 / ntt4::CT;
     static_assert(M1 == 2 || M1 == 4 || M1 == 8 || M1 == 16, "M1 is a power of two <= 16");
-    const int blk = blockIdx.x % BPC, job = blockIdx.x / BPC;   // job = (cl * 2 + b) * 2 + arr
-    const int arr = job & 1, b = (job >> 1) & 1, cl = job >> 2;
+    const int blk = blockIdx.x % BPC, job = blockIdx.x / BPC;   // job = cl * 2 + b
+    const int b = job & 1, cl = job >> 1;
     const int n1 = blk * ntt4::CT + threadIdx.x;
-    const Span as = make_span(arr ? g : v, (c0 + cl) * L, (int64_t)L);
-    const Tw tw{__builtin_amdgcn_make_buffer_rsrc((void*)wtab, (short)0, N * 16, 0x00020000)};
-    // the first input is read reversed for the gradient form (as in the fused kernel)
-    const bool rev = REV && arr == 0;
-    double x[M1];
+    const auto wrs = __builtin_amdgcn_make_buffer_rsrc((void*)ta, (short)0, 2 * M * 8, 0x00020000);
+    int32_t raw[2][M1];
 #pragma unroll
-    for (int n2 = 0; n2 < M1; ++n2) {
-        const int n = n1 + M2 * n2;
-        const uint32_t off = n < L ? (uint32_t)(rev ? L - 1 - n : n) * 4u : 0x80000000u;
-        x[n2] = (double)(int32_t)__builtin_amdgcn_raw_buffer_load_b32(as.rs, (int)off, 0, 0);
+    for (int arr = 0; arr < 2; ++arr) {
+        // the first input is read reversed for the gradient form (as in the fused kernel)
+        const bool rev = REV && arr == 0;
+        const Span as = make_span(arr ? g : v, (c0 + cl) * L, (int64_t)L);
+#pragma unroll
+        for (int n2 = 0; n2 < M1; ++n2) {
+            const int n = n1 + M2 * n2;
+            const uint32_t off = n < L ? (uint32_t)(rev ? L - 1 - n : n) * 4u : 0x80000000u;
+            raw[arr][n2] = (int32_t)__builtin_amdgcn_raw_buffer_load_b32(as.rs, (int)off, 0, 0);
+        }
     }
-    if (b) {
 #pragma unroll
-        for (int n2 = 0; n2 < M1; ++n2) x[n2] = mulc<PrimeA>(x[n2], tw.at(n1 + M2 * n2, 0));
-    }
-    dft<M1, PrimeA>(x);
-    const Span ts = make_span(T, (int64_t)job * M, (int64_t)M);
+    for (int arr = 0; arr < 2; ++arr) {
+        double x[M1];
 #pragma unroll
-    for (int k2 = 0; k2 < M1; ++k2) {
-        const double y = k2 ? mulc<PrimeA>(x[k2], tw.at(2 * ((n1 * k2) & (M - 1)), 0))
-                            : reduce<PrimeA>(x[0]);
-        __builtin_amdgcn_raw_buffer_store_b32((uint32_t)(int32_t)y, ts.rs, (k2 * M2 + n1) * 4, 0,
-                                              0);
+        for (int n2 = 0; n2 < M1; ++n2) {
+            x[n2] = (double)raw[arr][n2];
+            if (b && n2) x[n2] = mulc<PrimeA>(x[n2], root_c<PrimeA>(2 * M1, n2));
+        }
+        dft<M1, PrimeA>(x);
+        const Span ts = make_span(T, (int64_t)(2 * job + arr) * M, (int64_t)M);
+#pragma unroll
+        for (int k2 = 0; k2 < M1; ++k2) {
+            const double y = (b || k2) ? mulc<PrimeA>(x[k2], ntt4_w(wrs, (b * M1 + k2) * M2 + n1))
+                                       : reduce<PrimeA>(x[0]);
+            __builtin_amdgcn_raw_buffer_store_b32((uint32_t)(int32_t)y, ts.rs, (k2 * M2 + n1) * 4,
+                                                  0, 0);
+        }
     }
 }
 
 __global__ __launch_bounds__(256, 4) void ntt4_rows(const int32_t* __restrict__ T,
                                                     int32_t* __restrict__ S, int M1,
                                                     const double* __restrict__ bank,
-                                                    const double* __restrict__ wtab, double ninv,
+                                                    const double* __restrict__ tr, double ninv,
                                                     double ninv_q)
 {
     using namespace ntt;
@@ -793,7 +815,7 @@ __global__ __launch_bounds__(256, 4) void ntt4_rows(const int32_t* __restrict__ 
     const int tau = threadIdx.x;
     const Tw tw{__builtin_amdgcn_make_buffer_rsrc((void*)bank, (short)0, NTT_BANK_ENTRIES * 16,
                                                   0x00020000)};
-    const Tw wt{__builtin_amdgcn_make_buffer_rsrc((void*)wtab, (short)0, 2 * M * 16, 0x00020000)};
+    const auto wrs = __builtin_amdgcn_make_buffer_rsrc((void*)tr, (short)0, M * 8, 0x00020000);
     // rows k2 of this job's v and g column outputs
     const Span vs = make_span(T, (int64_t)(2 * job) * M + (int64_t)k2 * M2, (int64_t)M2);
     const Span gs = make_span(T, (int64_t)(2 * job + 1) * M + (int64_t)k2 * M2, (int64_t)M2);
@@ -818,13 +840,12 @@ __global__ __launch_bounds__(256, 4) void ntt4_rows(const int32_t* __restrict__ 
     auto keep = [&](int, int q, double val) { f[q] = (int32_t)reduce<PrimeA>(val); };
     passes<M2, 1, PrimeA>(y, bv, bv, tau, tw, keep);
     // f[q] = NTT(X)_j, j = tau + TB q: the inverse over k1 at m1 = (M2 - j) mod M2, times
-    // w_M^{-m1 k2} = w_N^{2 (M - m1 k2 mod M)}
+    // w_M^{-m1 k2} = tr[k2][m1]
     const Span ss = make_span(S, (int64_t)job * M + (int64_t)k2 * M2, (int64_t)M2);
 #pragma unroll
     for (int q = 0; q < 16; ++q) {
         const int m1 = (M2 - (tau + TB * q)) & (M2 - 1);
-        const int e = (m1 * k2) & (M - 1);
-        const double s = mulc<PrimeA>((double)f[q], wt.at(2 * ((M - e) & (M - 1)), 0));
+        const double s = mulc<PrimeA>((double)f[q], ntt4_w(wrs, k2 * M2 + m1));
         __builtin_amdgcn_raw_buffer_store_b32((uint32_t)(int32_t)s, ss.rs, m1 * 4, 0, 0);
     }
 }
@@ -838,7 +859,7 @@ __global__ __launch_bounds__(256) void ntt4_columns_inv(const int32_t* __restric
     constexpr int M2 = ntt4::M2, M = M1 * M2, N = 2 * M, BPC = M2 / ntt4::CT;
     const int blk = blockIdx.x % BPC, cl = blockIdx.x / BPC;
     const int m1 = blk * ntt4::CT + threadIdx.x;
-    const Tw tw{__builtin_amdgcn_make_buffer_rsrc((void*)wtab, (short)0, N * 16, 0x00020000)};
+    const auto wrs = __builtin_amdgcn_make_buffer_rsrc((void*)wtab, (short)0, N * 8, 0x00020000);
     double e[2][M1];
 #pragma unroll
     for (int b = 0; b < 2; ++b) {
@@ -857,7 +878,7 @@ __global__ __launch_bounds__(256) void ntt4_columns_inv(const int32_t* __restric
 #pragma unroll
     for (int m2 = 0; m2 < M1; ++m2) {
         const int n = m1 + M2 * m2;
-        const double xn = e[0][m2] + mulc<PrimeA>(e[1][m2], tw.at((N - n) & (N - 1), 0));
+        const double xn = e[0][m2] + mulc<PrimeA>(e[1][m2], ntt4_w(wrs, (N - n) & (N - 1)));
         const double lifted = balance<PrimeA>(reduce<PrimeA>(xn));
         if (n < L)
             __builtin_amdgcn_raw_buffer_store_b32((uint32_t)(int32_t)lifted, rs.rs,
@@ -880,12 +901,12 @@ static hipError_t launch_ntt4_m(const int32_t* v, const int32_t* g, int32_t* r, 
         const int64_t nc = nch - c0 < chunk ? nch - c0 : chunk;
         int32_t* T = ws;
         int32_t* S = ws + nc * 4 * (int64_t)M;
-        if (!grid_ok(nc * 4 * BPC, ntt4::CT) || !grid_ok(nc * 2 * M1, 256))
+        if (!grid_ok(nc * 2 * BPC, ntt4::CT) || !grid_ok(nc * 2 * M1, 256))
             return hipErrorInvalidValue;
-        hipLaunchKernelGGL((ntt4_columns_fwd<M1, REV>), dim3((unsigned)(nc * 4 * BPC)),
-                           dim3(ntt4::CT), 0, s, v, g, T, c0, L, wtab);
+        hipLaunchKernelGGL((ntt4_columns_fwd<M1, REV>), dim3((unsigned)(nc * 2 * BPC)),
+                           dim3(ntt4::CT), 0, s, v, g, T, c0, L, wtab + 2 * M);
         hipLaunchKernelGGL(ntt4_rows, dim3((unsigned)(nc * 2 * M1)), dim3(256), 0, s, T, S, M1,
-                           tb.bank, wtab, tb.ninv[lg], tb.ninv_q[lg]);
+                           tb.bank, wtab + 4 * M, tb.ninv[lg], tb.ninv_q[lg]);
         hipLaunchKernelGGL((ntt4_columns_inv<M1, REV>), dim3((unsigned)(nc * BPC)), dim3(ntt4::CT),
                            0, s, S, r, c0, L, wtab);
         const hipError_t e = hipGetLastError();
