@@ -1,6 +1,6 @@
 """Benchmark of the batched causal long convolution on one MI355X.
 
-    python bench.py [--steps K] [--warmup W] [--config 3] [--no-cpu-baseline]
+    python bench.py [--steps K] [--warmup W] [--workload 3] [--no-cpu-baseline]
 
 One step = one call of the library's hot path over one batch of synthetic input (for the
 default workload, sc_causal_conv_bf16 at B=8, C=1024, L=4096: load v and g, pad-to-2L FFT,
@@ -792,7 +792,7 @@ def main(argv=None):
     ap.add_argument("--prewarm-ms", type=float, default=200.0,
                     help="wall time of untimed hot-path launches before the warmup steps, so "
                          "that the timed steps see the clock the chip holds under load (0: off)")
-    ap.add_argument("--config", type=int, default=3)
+    ap.add_argument("--workload", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-leakage", action="store_true",
                     help="skip the leakage probe (keeps profiler runs to the timed kernel)")
@@ -823,11 +823,11 @@ def main(argv=None):
 
     if args.record_valu:
         from workloads import WORKLOADS
-        print(json.dumps(record_valu(WORKLOADS[args.config], args.record_valu)))
+        print(json.dumps(record_valu(WORKLOADS[args.workload], args.record_valu)))
         return 0
     if args.record_traffic:
         from workloads import WORKLOADS
-        print(json.dumps(record_traffic(WORKLOADS[args.config], *args.record_traffic)))
+        print(json.dumps(record_traffic(WORKLOADS[args.workload], *args.record_traffic)))
         return 0
 
     global PREWARM_MS
@@ -842,7 +842,7 @@ def main(argv=None):
     import fft_causal_long_amd as sc
     from workloads import WORKLOADS, make_inputs
 
-    w = WORKLOADS[args.config]
+    w = WORKLOADS[args.workload]
     if w.storage == "i32":
         fn_name, esz = "sc_causal_conv_ntt_i32", 4
     elif w.storage == "bf16":
@@ -954,7 +954,7 @@ def main(argv=None):
                                    kernel_ms)
     if not args.no_fixed and w.storage != "i32" and w.L <= 4096:
         rec["fixed"] = fixed_measure(sc, torch, w, dev, max(5, args.steps // 5), 2)
-    if not args.no_others and args.config == 3:
+    if not args.no_others and args.workload == 3:
         # Tiny, Small, the Medium shape in fp32, exact, long (four-step), long exact
         rec["other_workloads"] = [other_measure(sc, torch, WORKLOADS[c], dev, 20, 3,
                                                 not args.no_cpu_baseline)

@@ -37,14 +37,14 @@ def check(sc, v, g, what, **kw):
     return r, worst
 
 
-def test_config1_tiny_full(sc):
+def test_tiny_full(sc):
     v, g = make_inputs(WORKLOADS[1])
-    check(sc, v, g, "config1")
+    check(sc, v, g, "tiny")
 
 
-def test_config2_small_full(sc):
+def test_small_full(sc):
     v, g = make_inputs(WORKLOADS[2])
-    check(sc, v, g, "config2")
+    check(sc, v, g, "small")
 
 
 LS = [1, 2, 3, 5, 16, 31, 32, 33, 47, 63, 64, 65, 100, 127, 128, 129, 255, 256, 257, 300,
@@ -70,7 +70,7 @@ def test_fp32_conv_gate_shapes(sc, L):
     check(sc, v, g, "f32 conv-gate L=%d" % L)
 
 
-def test_config3_full_size_sampled(sc):
+def test_medium_full_size_sampled(sc):
     # full Caracal-Medium shape in the launch configuration the benchmark times; the
     # oracle checks 96 whole channels spread over the batch
     w = WORKLOADS[3]
@@ -81,18 +81,18 @@ def test_config3_full_size_sampled(sc):
     vs = v.reshape(nch, w.L)[chans]
     gs = g.reshape(nch, w.L)[chans]
     r_ref, S = oracle.causal_conv_f64(vs, gs)
-    worst = assert_within_bound(r.reshape(nch, w.L)[chans], r_ref, S, True, "config3 sampled")
-    print("config3 sampled: worst err/bound = %.3g" % worst, flush=True)
+    worst = assert_within_bound(r.reshape(nch, w.L)[chans], r_ref, S, True, "medium sampled")
+    print("medium sampled: worst err/bound = %.3g" % worst, flush=True)
 
 
-def test_config3_shape_as_fp32_sampled(sc):
+def test_medium_shape_as_fp32_sampled(sc):
     w = WORKLOADS[3]
     v, g = make_inputs(w, B=2)
     v32, g32 = decode(v).astype(np.float32), decode(g).astype(np.float32)
     r = run(sc, v32, g32)
     chans = np.arange(0, 2 * w.C, 37)
     r_ref, S = oracle.causal_conv_f64(v32.reshape(-1, w.L)[chans], g32.reshape(-1, w.L)[chans])
-    assert_within_bound(r.reshape(-1, w.L)[chans], r_ref, S, False, "config3 fp32 sampled")
+    assert_within_bound(r.reshape(-1, w.L)[chans], r_ref, S, False, "medium fp32 sampled")
 
 
 def test_bitwise_deterministic(sc):

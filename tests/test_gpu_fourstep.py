@@ -100,7 +100,7 @@ def test_four_step_two_streams_same_bits(sc):
         assert torch.equal(dg[:, c0:c0 + h].view(torch.int32), pg.view(torch.int32))
 
 
-def test_config4_full_size_sampled(sc):
+def test_long_full_size_sampled(sc):
     # the whole long workload (B=1, C=1536, L=65536) in one call, the launch configuration
     # the benchmark times; 64 seeded channels (always the first and the last) checked on
     # every output against the full oracle (2.1e9 multiply-adds per channel)
@@ -109,7 +109,7 @@ def test_config4_full_size_sampled(sc):
     rng = np.random.default_rng(np.random.SeedSequence([w.cid, 64]))
     inner = rng.choice(np.arange(1, w.C - 1), size=62, replace=False)
     chans = np.sort(np.concatenate([[0, w.C - 1], inner]))
-    check(sc, v, g, "config4 sampled (64 channels)", chans=chans)
+    check(sc, v, g, "long shape sampled (64 channels)", chans=chans)
 
 
 def test_caller_workspace_and_errors(sc):

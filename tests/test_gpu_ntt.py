@@ -30,7 +30,7 @@ def run(sc, v, g, **kw):
     return to_host(out)
 
 
-def test_config5_full_bit_exact(sc):
+def test_exact_medium_full_bit_exact(sc):
     w = WORKLOADS[5]
     v, g = make_inputs(w)
     assert sc.sc_ntt_range_ok(127, 127, w.L)

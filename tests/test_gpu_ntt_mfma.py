@@ -29,10 +29,10 @@ def run(sc, v, g, path):
     return to_host(out)
 
 
-def test_config5_full_bit_exact(sc):
+def test_exact_medium_full_bit_exact(sc):
     w = WORKLOADS[5]
     v, g = make_inputs(w)
-    print("case ntt-mfma config5 full", flush=True)
+    print("case ntt-mfma exact medium full", flush=True)
     r = run(sc, v, g, sc.PATH_NTT_MFMA)
     ref = oracle.causal_conv_i64(v, g)
     assert np.abs(ref).max() <= (P - 1) // 2
