@@ -60,7 +60,7 @@ struct DeviceState {
     sc::NttMfmaTables mfma{};     // the matrix-core NTT kernel's tables (prime A)
     bool mfma_ready = false;
     std::map<int, sc::FsTw> fs;     // four-step tables by M
-    std::map<int, const double*> ntt4;   // four-step NTT tables (w_N^j, j < 2M) by M
+    std::map<std::pair<int, int>, const double*> ntt4;   // four-step NTT tables by (M, prime)
     // the four-step path's second stream (default priority, non-blocking) and its fork/join
     // events; fs_mu keeps one call's fork, launches and join together, since the events are
     // shared by every call on the device
@@ -352,13 +352,13 @@ sc_status fourstep_tables(DeviceState& d, int M, sc::FsTw* out, hipStream_t stre
     return SC_OK;
 }
 
-// the four-step NTT's tables for transform length M (modulo prime A, as doubles, made on
-// first use): w_N^j (N = 2M, j < N) and the column and row twiddles in lane order; under
-// graph capture (or with may_build false) a missing table is SC_ERR_UNSUPPORTED.  Caller holds g_mu.
-sc_status ntt4_table(DeviceState& d, int M, const double** out, hipStream_t stream,
+// the four-step NTT's tables for transform length M modulo NTT_PRIMES[prime] (as doubles,
+// made on first use): w_N^j (N = 2M, j < N) and the column and row twiddles in lane order;
+// under graph capture (or with may_build false) a missing table is SC_ERR_UNSUPPORTED.  Caller holds g_mu.
+sc_status ntt4_table(DeviceState& d, int M, int prime, const double** out, hipStream_t stream,
                      bool may_build = true)
 {
-    auto it = d.ntt4.find(M);
+    auto it = d.ntt4.find({M, prime});
     if (it != d.ntt4.end()) {
         *out = it->second;
         return SC_OK;
@@ -366,7 +366,7 @@ sc_status ntt4_table(DeviceState& d, int M, const double** out, hipStream_t stre
     if (!may_build) return SC_ERR_UNSUPPORTED;
     const sc_status cs = capture_forbids_build(stream);
     if (cs != SC_OK) return cs;
-    const uint64_t p = sc::NTT_PRIMES[0];
+    const uint64_t p = sc::NTT_PRIMES[prime];
     const int64_t N = 2 * (int64_t)M;
     const uint64_t w = powmod(3, (p - 1) / (uint64_t)N, p);
     // w_N^j, j < N; then w_N^{n1 (2 k2 + b)} at [b][k2][n1]; then w_M^{-m1 k2} at [k2][m1]
@@ -389,7 +389,7 @@ sc_status ntt4_table(DeviceState& d, int M, const double** out, hipStream_t stre
     void* dp = nullptr;
     const sc_status st = upload(h.data(), h.size() * sizeof(double), &dp);
     if (st != SC_OK) return st;
-    d.ntt4[M] = (const double*)dp;
+    d.ntt4[{M, prime}] = (const double*)dp;
     *out = (const double*)dp;
     return SC_OK;
 }
@@ -454,7 +454,7 @@ sc_status resolve_path(sc_kind kind, int64_t L, int32_t requested, sc_path* out)
     case SC_PATH_AUTO:
         if (!fl) {
             if (L <= kMaxLNtt) *out = SC_PATH_FUSED;
-            else if (kind == SC_KIND_NTT_I32 && L <= sc::NTT4_MAX_L) *out = SC_PATH_FOUR_STEP;
+            else if (L <= sc::NTT4_MAX_L) *out = SC_PATH_FOUR_STEP;
             else return SC_ERR_UNSUPPORTED;
         } else if (L <= sc::DIRECT_MAX_L) {
             *out = SC_PATH_DIRECT;
@@ -477,8 +477,7 @@ sc_status resolve_path(sc_kind kind, int64_t L, int32_t requested, sc_path* out)
     case SC_PATH_FOUR_STEP:
         if (!fl) {
             // the exact kind's four-step split has rows of 4096: L above the fused range only
-            if (kind != SC_KIND_NTT_I32 || L <= kMaxLNtt || L > sc::NTT4_MAX_L)
-                return SC_ERR_UNSUPPORTED;
+            if (L <= kMaxLNtt || L > sc::NTT4_MAX_L) return SC_ERR_UNSUPPORTED;
             *out = SC_PATH_FOUR_STEP;
             return SC_OK;
         }
@@ -519,8 +518,9 @@ sc_status fourstep_streams(DeviceState& d)
 size_t fourstep_per_channel(sc_kind kind, int64_t L)
 {
     const int M = (int)next_pow2(L);
-    return kind == SC_KIND_NTT_I32 ? sc::ntt4_bytes_per_channel(M)
-                                   : sc::fourstep_bytes_per_channel(M);
+    return kind == SC_KIND_NTT_I32     ? sc::ntt4_bytes_per_channel(M)
+           : kind == SC_KIND_FIXED_F32 ? sc::fixed4_bytes_per_channel(M)
+                                       : sc::fourstep_bytes_per_channel(M);
 }
 
 void fourstep_plan(sc_kind kind, int64_t nch, int64_t L, int64_t* chunk, size_t* bytes,
@@ -530,6 +530,12 @@ void fourstep_plan(sc_kind kind, int64_t nch, int64_t L, int64_t* chunk, size_t*
     int64_t c = budget / per;
     if (c < 1) c = 1;
     if (c > nch) c = nch;
+    // exact kinds: the fewest chunks the budget allows, of balanced sizes (no short last
+    // chunk); the float kinds' chunks are run as two halves on two streams
+    if (exact_kind(kind) && c > 0) {
+        const int64_t k = (nch + c - 1) / c;
+        c = (nch + k - 1) / k;
+    }
     *chunk = c;
     *bytes = (size_t)(c * per);
 }
@@ -596,6 +602,33 @@ sc_status run_jobs(sc_kind kind, const Job* jobs, int njobs, bool rev, int64_t n
     if (st != SC_OK) return st;
 
     hipError_t e = hipSuccess;
+    if (exact_kind(kind) && path == SC_PATH_FOUR_STEP) {
+        const int M = (int)next_pow2(L);
+        const bool fix = kind == SC_KIND_FIXED_F32;
+        const double* wtab[3] = {nullptr, nullptr, nullptr};
+        {
+            std::lock_guard<std::mutex> lk(g_mu);
+            for (int i = 0; i < (fix ? 3 : 1) && st == SC_OK; ++i)
+                st = ntt4_table(*d, M, i, &wtab[i], stream, !noalloc);
+        }
+        if (st != SC_OK) return st;
+        void* scratch = ws;
+        bool own = false;
+        if (!ws) {
+            if (hipMallocAsync(&scratch, need, stream) != hipSuccess) return SC_ERR_HIP;
+            own = true;
+        }
+        for (int k = 0; k < njobs && e == hipSuccess; ++k)
+            e = fix ? sc::launch_fixed4((const float*)jobs[k].a, (const float*)jobs[k].b,
+                                        (float*)jobs[k].o, nch, (int)L, M, fv, fg, d->ntt, wtab,
+                                        scratch, need, chunk, stream)
+                    : sc::launch_ntt4((const int32_t*)jobs[k].a, (const int32_t*)jobs[k].b,
+                                      (int32_t*)jobs[k].o, nch, (int)L, M, rev, d->ntt[0],
+                                      wtab[0], scratch, need, chunk, stream);
+        if (own && hipFreeAsync(scratch, stream) != hipSuccess && e == hipSuccess)
+            e = hipErrorUnknown;
+        return e == hipSuccess ? SC_OK : SC_ERR_HIP;
+    }
     if (kind == SC_KIND_FIXED_F32) {
         const int M = (int)std::max<int64_t>(64, next_pow2(L));
         for (int k = 0; k < njobs && e == hipSuccess; ++k)
@@ -617,28 +650,6 @@ sc_status run_jobs(sc_kind kind, const Job* jobs, int njobs, bool rev, int64_t n
         for (int k = 0; k < njobs && e == hipSuccess; ++k)
             e = sc::launch_ntt_mfma((const int32_t*)jobs[k].a, (const int32_t*)jobs[k].b,
                                     (int32_t*)jobs[k].o, nch, (int)L, M, rev, d->mfma, stream);
-        return e == hipSuccess ? SC_OK : SC_ERR_HIP;
-    }
-    if (kind == SC_KIND_NTT_I32 && path == SC_PATH_FOUR_STEP) {
-        const int M = (int)next_pow2(L);
-        const double* wtab = nullptr;
-        {
-            std::lock_guard<std::mutex> lk(g_mu);
-            st = ntt4_table(*d, M, &wtab, stream, !noalloc);
-        }
-        if (st != SC_OK) return st;
-        void* scratch = ws;
-        bool own = false;
-        if (!ws) {
-            if (hipMallocAsync(&scratch, need, stream) != hipSuccess) return SC_ERR_HIP;
-            own = true;
-        }
-        for (int k = 0; k < njobs && e == hipSuccess; ++k)
-            e = sc::launch_ntt4((const int32_t*)jobs[k].a, (const int32_t*)jobs[k].b,
-                                (int32_t*)jobs[k].o, nch, (int)L, M, rev, d->ntt[0], wtab,
-                                scratch, need, chunk, stream);
-        if (own && hipFreeAsync(scratch, stream) != hipSuccess && e == hipSuccess)
-            e = hipErrorUnknown;
         return e == hipSuccess ? SC_OK : SC_ERR_HIP;
     }
     if (kind == SC_KIND_NTT_I32) {
@@ -1468,15 +1479,17 @@ sc_status sc_prepare(sc_kind kind, int64_t L)
         st = device_state(&d, exact_kind(kind), nullptr);
         if (st != SC_OK || path != SC_PATH_FOUR_STEP) return st;
         std::lock_guard<std::mutex> lk(g_mu);
-        if (kind == SC_KIND_NTT_I32) {
+        if (exact_kind(kind)) {
             const double* wtab = nullptr;
-            return ntt4_table(*d, (int)next_pow2(L), &wtab, nullptr);
+            for (int i = 0; i < (kind == SC_KIND_FIXED_F32 ? 3 : 1) && st == SC_OK; ++i)
+                st = ntt4_table(*d, (int)next_pow2(L), i, &wtab, nullptr);
+            return st;
         }
         sc::FsTw tw;
         return fourstep_tables(*d, (int)next_pow2(L), &tw, nullptr);
     });
 }
 
-int sc_version(void) { return 800; }
+int sc_version(void) { return 900; }
 
 }  // extern "C"

@@ -100,8 +100,8 @@ typedef enum sc_path {
 /* Optional controls for sc_causal_conv_ex (testing and experiments). */
 typedef struct sc_options {
     int32_t path;      /* sc_path; SC_PATH_AUTO picks: L <= 32 direct, L <= 4096 fused,
-                          larger L four-step (SC_KIND_NTT_I32: fused up to 4096,
-                          four-step up to 65536; SC_KIND_FIXED_F32: fused)             */
+                          larger L four-step (the exact kinds: fused up to 4096,
+                          four-step up to 65536)                                     */
     int32_t head;      /* float kinds: outputs t < head are computed by direct fp32
                           summation instead of the transform.  -1 = default (32);
                           0 disables; odd values are rounded up to even; at most 64.  */
@@ -166,11 +166,15 @@ sc_status sc_causal_conv_ntt_i32(const int32_t* v, const int32_t* g, int32_t* r,
  *   precondition, checked from bounds by sc_fixed_range_ok.  Accuracy against the real sum:
  *   |r_t - sum v_j g_{t-j}| <= 2^-(frac_v+1) sum_j |g_j| + 2^-(frac_g+1) sum_j |v_j| + (one
  *   float32 rounding) -- e.g. frac_v = frac_g = 24 for activations of magnitude below 8.
- *   frac_v, frac_g in [-64, 64].  Largest L: 4096.  One kernel computes the three residues
- *   of each output in turn and combines them: no scratch, no allocation
- *   (sc_workspace_bytes(SC_KIND_FIXED_F32, ...) is 0, so the _ws variant, kept for callers
- *   written against a workspace, accepts any ws and ws_bytes and uses neither).  Gradients
- *   are not offered for this kind (SC_ERR_UNSUPPORTED from sc_causal_conv_bwd_ex).
+ *   frac_v, frac_g in [-64, 64].  Largest L: 65536.  L <= 4096: one kernel computes the
+ *   three residues of each output in turn and combines them: no scratch, no allocation
+ *   (sc_workspace_bytes is 0 there; the _ws variant then accepts any ws and ws_bytes and
+ *   uses neither).  4096 < L <= 65536: the four-step split of sc_causal_conv_ntt_i32, run
+ *   once per prime, then one kernel that recombines the three residues of each output;
+ *   it needs sc_workspace_bytes(SC_KIND_FIXED_F32, B, C, L) bytes of device scratch (40 M
+ *   bytes per channel of a chunk, M = the power of two >= L), allocated stream-ordered on
+ *   `stream` by this call, or supplied through the _ws variant.  Gradients are not offered
+ *   for this kind (SC_ERR_UNSUPPORTED from sc_causal_conv_bwd_ex).
  */
 sc_status sc_causal_conv_fixed_f32(const float* v, const float* g, float* r, int64_t B,
                                    int64_t C, int64_t L, int32_t frac_v, int32_t frac_g,
@@ -443,7 +447,7 @@ sc_status sc_causal_conv_noalloc(sc_kind kind, const void* v, const void* g, voi
  */
 sc_status sc_prepare(sc_kind kind, int64_t L);
 
-/* Library version: major * 10000 + minor * 100 + patch (this header: 800).  Host only. */
+/* Library version: major * 10000 + minor * 100 + patch (this header: 900).  Host only. */
 int sc_version(void);
 
 #ifdef __cplusplus

@@ -32,7 +32,8 @@ blocking or fusion (see ``oracle.c`` for the C side):
   float32 (nearest, ties to even, subnormals included).  The leakage page proposes
   transforms executed on integers only ("Catastrophic Token Leakage ...", abstract); a
   fixed-point encoding with caller-chosen scales carries real activations onto integers
-  without letting any output depend on a later input.
+  without letting any output depend on a later input.  :func:`causal_conv_fixed_f32_at`
+  gives the same result at sampled outputs, each sum formed in Python integers.
 * :func:`gate_f64` -- the gate stream of the multi-head Fourier module ("Caracal", key
   design 1): a causal convolution with kernel 3 over sigma(s), grouped by head (the
   channels of one group mix with each other only), g[co, t] = sum_{i, k} W[co, i, k]
@@ -306,6 +307,29 @@ def causal_conv_fixed_f32(v, g, fv: int, fg: int, nthreads: int | None = None) -
     round_f32(sum_{j<=t} round(v_j 2^fv) round(g_{t-j} 2^fg) * 2^-(fv+fg))."""
     return fixed_decode_f32(causal_conv_i128(fixed_encode(v, fv), fixed_encode(g, fg),
                                              nthreads), fv + fg)
+
+
+def causal_conv_fixed_f32_at(v, g, fv: int, fg: int, ch, t) -> np.ndarray:
+    """causal_conv_fixed_f32 at sampled outputs r[ch[i], t[i]] of (nch, L) inputs: the same
+    definition, each exact sum R_t = sum_{j<=t} V_j G_{t-j} formed in Python integers one
+    output at a time (for lengths where the full 128-bit convolution is too slow)."""
+    V, G = fixed_encode(v, fv), fixed_encode(g, fg)
+    if V.shape != G.shape:
+        raise ValueError("v and g must have the same shape")
+    L = V.shape[-1]
+    V, G = V.reshape(-1, L), G.reshape(-1, L)
+    ch = np.asarray(ch, dtype=np.int64).ravel()
+    t = np.asarray(t, dtype=np.int64).ravel()
+    if ch.shape != t.shape:
+        raise ValueError("ch and t must have the same shape")
+    out = np.empty(ch.shape, dtype=np.float32)
+    for i in range(ch.size):
+        c, tt = int(ch[i]), int(t[i])
+        if not (0 <= c < V.shape[0] and 0 <= tt < L):
+            raise IndexError("sample out of range")
+        R = int(np.dot(V[c, :tt + 1].astype(object), G[c, tt::-1].astype(object)))
+        out[i] = np.float32(_rne_to_f32(R, int(fv) + int(fg)))
+    return out
 
 
 def shared_conv_bwd_f64(dr, v, k, nthreads: int | None = None):

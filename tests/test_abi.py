@@ -91,10 +91,12 @@ def test_unsupported_lengths_rejected_before_launch(sc):
     opt = sc.sc_options(sc.PATH_FUSED, -1)             # one workgroup holds at most L = 4096
     assert h.sc_causal_conv_ex(0, A, B_, C_, 1, 1, 4097, ctypes.byref(opt), None, 0, None) == UNSUP
     assert h.sc_causal_conv_ex(2, A, B_, C_, 1, 1, 4097, ctypes.byref(opt), None, 0, None) == UNSUP
-    # the exact four-step split has rows of 4096: forced only above the fused range, int32 only
+    # the exact four-step split has rows of 4096: forced only above the fused range
     opt = sc.sc_options(sc.PATH_FOUR_STEP, -1)
-    assert h.sc_causal_conv_ex(2, A, B_, C_, 1, 1, 4096, ctypes.byref(opt), None, 0, None) == UNSUP
-    assert h.sc_causal_conv_ex(3, A, B_, C_, 1, 1, 5000, ctypes.byref(opt), None, 0, None) == UNSUP
+    for kind in (2, 3):
+        for L in (4096, 65537):
+            assert h.sc_causal_conv_ex(kind, A, B_, C_, 1, 1, L, ctypes.byref(opt), None, 0,
+                                       None) == UNSUP
 
 
 def test_options_validation(sc):
@@ -122,12 +124,12 @@ def test_host_helpers(sc):
     assert sc.sc_status_string(0) == "SC_OK"
     assert sc.sc_status_string(4) == "SC_ERR_WORKSPACE"
     assert sc.sc_status_string(99) == "SC_STATUS_UNKNOWN"
-    assert sc.sc_version() >= 800
+    assert sc.sc_version() >= 900
     # sc_prepare: argument checks on the host; an empty length needs no table
     assert sc.sc_prepare(7, 64) == sc.SC_ERR_INVALID_ARGUMENT
     assert sc.sc_prepare(sc.KIND_F32, -1) == sc.SC_ERR_INVALID_ARGUMENT
     assert sc.sc_prepare(sc.KIND_NTT_I32, 65537) == sc.SC_ERR_UNSUPPORTED
-    assert sc.sc_prepare(sc.KIND_FIXED_F32, 5000) == sc.SC_ERR_UNSUPPORTED
+    assert sc.sc_prepare(sc.KIND_FIXED_F32, 65537) == sc.SC_ERR_UNSUPPORTED
     assert sc.sc_prepare(sc.KIND_F32, 2**22 + 1) == sc.SC_ERR_UNSUPPORTED
     assert sc.sc_prepare(sc.KIND_BF16, 0) == sc.SC_OK
     assert sc.sc_workspace_bytes(sc.KIND_F32, 8, 1024, 4096) == 0
@@ -205,7 +207,7 @@ def test_fixed_kind_host_checks(sc):
     f = h.sc_causal_conv_fixed_f32
     assert f(A, B_, C_, 1, 1, 64, 65, 0, None) == INVALID            # fraction bits in [-64, 64]
     assert f(A, B_, C_, 1, 1, 64, 0, -65, None) == INVALID
-    assert f(A, B_, C_, 1, 1, 4097, 20, 20, None) == UNSUP            # exact paths: L <= 4096
+    assert f(A, B_, C_, 1, 1, 65537, 20, 20, None) == UNSUP           # exact paths: L <= 65536
     assert f(A, B_, A, 1, 1, 64, 20, 20, None) == INVALID             # r aliases v
     assert f(None, None, None, 0, 1, 64, 20, 20, None) == sc.SC_OK
     # fraction bits are only meaningful for the fixed kind
@@ -213,10 +215,13 @@ def test_fixed_kind_host_checks(sc):
     assert h.sc_causal_conv_ex(0, A, B_, C_, 1, 1, 64, ctypes.byref(opt), None, 0, None) == INVALID
     # no gradients for the fixed kind
     assert h.sc_causal_conv_bwd_ex(3, A, B_, C_, D_, E_, 1, 1, 64, None, None, 0, None) == UNSUP
-    # one kernel keeps the three residues of an output in registers: no scratch
+    # up to L = 4096 one kernel keeps the three residues of an output in registers: no
+    # scratch; beyond, the four-step split per prime: 40 M bytes per channel (M = 2^ceil(lg L))
     assert sc.sc_workspace_bytes(sc.KIND_FIXED_F32, 2, 3, 100) == 0
     assert sc.sc_workspace_bytes(sc.KIND_FIXED_F32, 8, 1024, 4096) == 0
-    assert sc.sc_workspace_bytes(sc.KIND_FIXED_F32, 1, 1, 5000) == 0
+    assert sc.sc_workspace_bytes(sc.KIND_FIXED_F32, 1, 1, 5000) == 40 * 8192
+    assert sc.sc_workspace_bytes(sc.KIND_FIXED_F32, 2, 3, 65536) == 6 * 40 * 65536
+    assert sc.sc_workspace_bytes(sc.KIND_FIXED_F32, 1, 1, 65537) == 0
     assert sc.sc_blc_workspace_bytes(sc.KIND_FIXED_F32, 2, 100, 3) == \
         3 * (((2 * 3 * 100 * 4) + 255) // 256 * 256)
 

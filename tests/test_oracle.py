@@ -464,6 +464,24 @@ def test_fixed_path_exact_on_dyadic_inputs():
     assert np.array_equal(r, ref.astype(np.float32))
 
 
+def test_fixed_sampled_outputs_match_full():
+    # the sampled form against the full 128-bit oracle, with encodings near 2^40 so that the
+    # sums pass 2^64 (a sum kept in int64 would wrap) and both tails of each row sampled
+    rng = np.random.default_rng(45)
+    L, fv, fg = 300, 20, 21
+    v = (rng.uniform(-1, 1, size=(4, L)) * 2.0 ** 20).astype(np.float32)
+    g = (rng.uniform(-1, 1, size=(4, L)) * 2.0 ** 19).astype(np.float32)
+    full = oracle.causal_conv_fixed_f32(v, g, fv, fg)
+    R = oracle.causal_conv_i128(oracle.fixed_encode(v, fv), oracle.fixed_encode(g, fg))
+    assert max(abs(int(x)) for x in R.ravel()) > 2 ** 64
+    ch = np.array([0, 3, 1, 2, 3, 0, 2])
+    t = np.array([0, L - 1, 150, 1, 0, L - 1, 299])
+    got = oracle.causal_conv_fixed_f32_at(v, g, fv, fg, ch, t)
+    assert np.array_equal(got.view(np.uint32), full[ch, t].view(np.uint32))
+    with pytest.raises(IndexError):
+        oracle.causal_conv_fixed_f32_at(v, g, fv, fg, [4], [0])
+
+
 def test_fixed_path_error_bound_and_causality():
     rng = np.random.default_rng(44)
     L, fv, fg = 200, 20, 22
