@@ -7,7 +7,8 @@ default workload, sc_causal_conv_bf16 at B=8, C=1024, L=4096: load v and g, pad-
 spectral product, inverse FFT, truncation, direct head, store r -- a single kernel).
 After the timed region, the gradient call of the same workload (dv, dg from dr, v, g) is
 timed the same way and reported in the `bwd` object (skip with --no-bwd), and the exactly
-causal real-valued call on the same inputs in the `fixed` object (skip with --no-fixed),
+causal real-valued call on the same inputs in the `fixed` object and at the long-context
+shape (B=1, C=1536, L=65536) in `fixed_long` (skip both with --no-fixed),
 and the calls for a filter shared by the batch on the same shape in the `shared` object
 (skip with --no-shared), the token-major (B, L, C) call on the same inputs in the
 `token_major` object (skip with --no-blc), and the gate-stream calls (g from the gate
@@ -299,9 +300,10 @@ def leakage_probe(sc, torch, dev, channels: int = 16) -> dict:
 
 def fixed_measure(sc, torch, w, dev, steps: int, warmup: int) -> dict:
     """Time the exactly causal real-valued call (sc_causal_conv_fixed_f32, fraction bits
-    FIXED_FRAC for v and g; one kernel, no scratch, no allocation) on the workload's inputs
-    widened to float32.  Algorithmic bytes per output: read v, g and write r as float32
-    (12)."""
+    FIXED_FRAC for v and g) on the workload's inputs widened to float32: up to L = 4096 one
+    kernel with no scratch, beyond that the four-step split per prime with a caller
+    workspace (sc_causal_conv_fixed_f32_ws).  Algorithmic bytes per output: read v, g and
+    write r as float32 (12)."""
     from workloads import bf16_bits_to_f32, make_inputs
     v, g = make_inputs(w)
     if w.storage == "bf16":
@@ -311,27 +313,30 @@ def fixed_measure(sc, torch, w, dev, steps: int, warmup: int) -> dict:
         raise RuntimeError("fixed-point range check failed for %s" % w.name)
     tv, tg = torch.from_numpy(v).to(dev), torch.from_numpy(g).to(dev)
     out = torch.empty_like(tv)
-    if sc.sc_workspace_bytes(sc.KIND_FIXED_F32, w.B, w.C, w.L) != 0:
-        raise RuntimeError("the exact real-valued call is expected to need no scratch")
+    need = sc.sc_workspace_bytes(sc.KIND_FIXED_F32, w.B, w.C, w.L)
+    if (need != 0) != (w.L > 4096):
+        raise RuntimeError("unexpected scratch size %d for %s" % (need, w.name))
+    ws = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream(dev)
-    fn = sc.lib().sc_causal_conv_fixed_f32
+    fn = sc.lib().sc_causal_conv_fixed_f32_ws
+    entry = "sc_causal_conv_fixed_f32_ws" if need else "sc_causal_conv_fixed_f32"
 
     def call():
         st = fn(tv.data_ptr(), tg.data_ptr(), out.data_ptr(), w.B, w.C, w.L, FIXED_FRAC,
-                FIXED_FRAC, stream.cuda_stream)
+                FIXED_FRAC, ws.data_ptr() if need else None, need, stream.cuda_stream)
         if st != 0:
-            raise RuntimeError("sc_causal_conv_fixed_f32 failed: %s" % sc.sc_status_string(st))
+            raise RuntimeError("%s failed: %s" % (entry, sc.sc_status_string(st)))
 
     for _ in range(warmup):
         call()
     ms, _ = time_rounds(torch, stream, lambda i: call(), steps)
     gbps = 12 * w.outputs / (ms * 1e-3) / 1e9
-    return {"entry": "sc_causal_conv_fixed_f32", "frac_bits": [FIXED_FRAC, FIXED_FRAC],
+    return {"workload": w.name, "entry": entry, "frac_bits": [FIXED_FRAC, FIXED_FRAC],
             "ms_per_call": round(ms, 5), "value": round(w.outputs / (ms * 1e-3), 1),
             "unit": "outputs/s", "hbm": {"algorithmic_bytes_per_call": 12 * w.outputs,
                                          "achieved_GBps": round(gbps, 1),
                                          "frac": round(gbps / HBM_PEAK_GBPS, 4)},
-            "scratch_bytes": 0}
+            "scratch_bytes": need}
 
 
 def oracle_sample_rate(w, v, g, nthreads: int, budget_s: float, start: int = 8):
@@ -952,8 +957,11 @@ def main(argv=None):
     if not args.no_gate and w.storage != "i32" and w.C % 64 == 0:
         rec["gate"] = gate_measure(sc, torch, w, dev, max(5, args.steps // 2), args.warmup,
                                    kernel_ms)
-    if not args.no_fixed and w.storage != "i32" and w.L <= 4096:
+    if not args.no_fixed and w.storage != "i32":
         rec["fixed"] = fixed_measure(sc, torch, w, dev, max(5, args.steps // 5), 2)
+    if not args.no_fixed and not args.no_others and args.workload == 3:
+        # the exact real-valued call at the long-context shape (four-step split per prime)
+        rec["fixed_long"] = fixed_measure(sc, torch, WORKLOADS[4], dev, 5, 2)
     if not args.no_others and args.workload == 3:
         # Tiny, Small, the Medium shape in fp32, exact, long (four-step), long exact
         rec["other_workloads"] = [other_measure(sc, torch, WORKLOADS[c], dev, 20, 3,
