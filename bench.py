@@ -150,8 +150,12 @@ def kernel_matches(name: str, storage: str, L: int, rev: bool = False) -> bool:
     flag = "true" if rev else "false"
     if storage == "i32":
         if L > 4096:
-            # the four-step NTT: columns (per direction), rows (shared), inverse columns
-            return "ntt4_rows" in name or ("ntt4_columns" in name and (", %s>" % flag) in name)
+            # the four-step NTT modulo prime A: columns and inverse columns (per direction),
+            # rows (shared by both directions)
+            m1 = M // 4096
+            return ("ntt4_rows<sc::ntt::PrimeA>" in name
+                    or ("ntt4_columns_fwd<%d, %s, sc::ntt::PrimeA, false>" % (m1, flag)) in name
+                    or ("ntt4_columns_inv<%d, %s>" % (m1, flag)) in name)
         return ("ntt_conv_kernel<%d, %s>" % (M, flag)) in name
     if L > 4096:
         return "fs_rows<" in name or (("fs_columns" in name or "head_kernel" in name)
