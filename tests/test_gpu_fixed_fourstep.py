@@ -154,3 +154,23 @@ def test_graph_capture_after_prepare(sc):
         graph.replay()
         torch.cuda.synchronize()
         assert torch.equal(out.view(torch.int32), eager.view(torch.int32))
+
+
+def test_token_major(sc):
+    # (B, L, C) inputs through the staged token-major call, whose inner call takes the
+    # four-step split: bitwise the channel-major result
+    B, L, C = 2, 5000, 6
+    v, g = make_inputs(W2, B=B, C=C, L=L, seed_offset=43)
+    a = run(sc, v, g, 24, 24)
+    vt = to_device(np.ascontiguousarray(v.transpose(0, 2, 1)))
+    gt = to_device(np.ascontiguousarray(g.transpose(0, 2, 1)))
+    rt = torch.empty_like(vt)
+    opt = sc.sc_options(sc.PATH_AUTO, -1, 24, 24)
+    print("case fixed token-major L=%d" % L, flush=True)
+    st = sc.sc_causal_conv_blc_ex(sc.KIND_FIXED_F32, vt.data_ptr(), gt.data_ptr(), rt.data_ptr(),
+                                  B, L, C, ctypes.byref(opt), None, 0,
+                                  torch.cuda.current_stream().cuda_stream)
+    assert st == sc.SC_OK, sc.sc_status_string(st)
+    torch.cuda.synchronize()
+    got = np.ascontiguousarray(to_host(rt).transpose(0, 2, 1))
+    assert np.array_equal(got.view(np.uint32), a.view(np.uint32))
