@@ -6,14 +6,15 @@ One step = one call of the library's hot path over one batch of synthetic input 
 default workload, sc_causal_conv_bf16 at B=8, C=1024, L=4096: load v and g, pad-to-2L FFT,
 spectral product, inverse FFT, truncation, direct head, store r -- a single kernel).
 After the timed region, the gradient call of the same workload (dv, dg from dr, v, g) is
-timed the same way and reported in the `bwd` object (skip with --no-bwd), and the exactly
+timed the same way and reported in the `bwd` object (skip with --no-bwd); the exactly
 causal real-valued call on the same inputs in the `fixed` object and at the long-context
-shape (B=1, C=1536, L=65536) in `fixed_long` (skip both with --no-fixed),
-and the calls for a filter shared by the batch on the same shape in the `shared` object
-(skip with --no-shared), the token-major (B, L, C) call on the same inputs in the
-`token_major` object (skip with --no-blc), and the gate-stream calls (g from the gate
-pre-activation on MFMA, alone and as the mixing step's prologue) in the `gate` object (skip
-with --no-gate).
+shape (B=1, C=1536, L=65536) in `fixed_long` (skip both with --no-fixed); the pages' own
+pipeline (torch.fft rfft, product, irfft; context only, not a target) in `pages_approach`
+(skip with --no-pages-approach); the calls for a filter shared by the batch on the same
+shape in the `shared` object (skip with --no-shared); the token-major (B, L, C) call on the
+same inputs in the `token_major` object (skip with --no-blc); and the gate-stream calls (g
+from the gate pre-activation on MFMA, alone and as the mixing step's prologue) in the
+`gate` object (skip with --no-gate).
 Inputs are resident in HBM before the timed region.  Several copies of the buffers are
 rotated so that the 256 MB last-level cache cannot hold a step's working set.  Before the W
 warmup steps, untimed launches of the same step run for --prewarm-ms (default 200 ms; the
@@ -300,6 +301,32 @@ def leakage_probe(sc, torch, dev, channels: int = 16) -> dict:
     n_leak, _ = probe(vi, gi, posi, swap)
     return {"fp32_max_abs": f_leak, "fp32_rel_to_rms": f_leak / f_rms, "ntt_max_abs": n_leak,
             "fixed_max_abs": x_leak, "positions": len(pos), "channels": channels, "L": w3.L}
+
+
+def pages_approach(torch, w, dev, steps: int, kernel_ms: float) -> dict:
+    """For context only, not a target: the pages' own pipeline on this hardware -- standard
+    FFT operators ("Caracal", background), here torch.fft on ROCm: rfft of v and g
+    zero-padded to 2L, the spectral product, irfft, the first L values -- in float32 on the
+    workload's inputs widened to float32 (torch has no bfloat16 FFT)."""
+    from workloads import bf16_bits_to_f32, make_inputs
+    v, g = make_inputs(w)
+    if w.storage == "bf16":
+        v, g = bf16_bits_to_f32(v), bf16_bits_to_f32(g)
+    tv, tg = torch.from_numpy(v).to(dev), torch.from_numpy(g).to(dev)
+    n = 2 * w.L
+    stream = torch.cuda.current_stream(dev)
+
+    def call(i):
+        spec = torch.fft.rfft(tv, n=n) * torch.fft.rfft(tg, n=n)
+        return torch.fft.irfft(spec, n=n)[..., :w.L]
+
+    for _ in range(2):
+        call(0)
+    ms, _ = time_rounds(torch, stream, call, steps)
+    return {"what": "torch.fft rfft(v, 2L) * rfft(g, 2L) -> irfft -> first L, float32; the "
+                    "pages' approach on this hardware, context only",
+            "ms_per_call": round(ms, 5), "value": round(w.outputs / (ms * 1e-3), 1),
+            "unit": "outputs/s", "this_library_speedup": round(ms / kernel_ms, 2)}
 
 
 def fixed_measure(sc, torch, w, dev, steps: int, warmup: int) -> dict:
@@ -803,6 +830,8 @@ def main(argv=None):
                          "that the timed steps see the clock the chip holds under load (0: off)")
     ap.add_argument("--workload", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-pages-approach", action="store_true",
+                    help="skip the context timing of the torch.fft pipeline")
     ap.add_argument("--no-leakage", action="store_true",
                     help="skip the leakage probe (keeps profiler runs to the timed kernel)")
     ap.add_argument("--no-bwd", action="store_true",
@@ -963,6 +992,8 @@ def main(argv=None):
                                    kernel_ms)
     if not args.no_fixed and w.storage != "i32":
         rec["fixed"] = fixed_measure(sc, torch, w, dev, max(5, args.steps // 5), 2)
+    if not args.no_pages_approach and w.storage != "i32":
+        rec["pages_approach"] = pages_approach(torch, w, dev, max(5, args.steps // 5), kernel_ms)
     if not args.no_fixed and not args.no_others and args.workload == 3:
         # the exact real-valued call at the long-context shape (four-step split per prime)
         rec["fixed_long"] = fixed_measure(sc, torch, WORKLOADS[4], dev, 5, 2)
