@@ -1,7 +1,7 @@
 """GPU parity on seeded random shapes: every float kind and path the automatic choice
-takes (direct, fused, four-step), forward and gradients, and the exact kind bit for bit,
-at lengths drawn log-uniformly over 1 .. 9000 and channel counts that leave partial
-workgroups.  The bounds are those of the fixed-shape tests (tests/gpu_util.py)."""
+takes (direct, fused, four-step), forward and gradients, and the exact kinds (int32 NTT
+with its gradients, the real-valued fixed-point kind) bit for bit, at lengths drawn
+log-uniformly over 1 .. 9000 and channel counts that leave partial workgroups.  The bounds are those of the fixed-shape tests (tests/gpu_util.py)."""
 import numpy as np
 import pytest
 import torch
@@ -50,14 +50,19 @@ def test_random_shape_float_forward_and_gradients(sc, i):
 
 @pytest.mark.parametrize("i", range(len(SHAPES)))
 def test_random_shape_exact(sc, i):
+    # fused up to L = 4096, the four-step split beyond; forward and gradients bit for bit
     B, C, L = SHAPES[i]
-    L = min(L, 4096)                              # the exact kind's fused range
     v, g = make_inputs(WORKLOADS[5], B=B, C=C, L=L, seed_offset=500 + i)
+    dr, _ = make_inputs(WORKLOADS[5], B=B, C=C, L=L, seed_offset=700 + i)
     print("case random exact %d: B=%d C=%d L=%d" % (i, B, C, L), flush=True)
-    r = to_host(sc.causal_conv(to_device(v), to_device(g)))
+    tv, tg = to_device(v), to_device(g)
+    r = to_host(sc.causal_conv(tv, tg))
+    dv, dg = sc.causal_conv_bwd(to_device(dr), tv, tg)
     torch.cuda.synchronize()
-    ref = oracle.lift_mod_p(oracle.causal_conv_i64(v, g))
-    assert np.array_equal(r.astype(np.int64), ref)
+    assert np.array_equal(r.astype(np.int64), oracle.lift_mod_p(oracle.causal_conv_i64(v, g)))
+    rdv, rdg = oracle.causal_conv_bwd_i64(dr, v, g)
+    assert np.array_equal(to_host(dv).astype(np.int64), oracle.lift_mod_p(rdv))
+    assert np.array_equal(to_host(dg).astype(np.int64), oracle.lift_mod_p(rdg))
 
 
 @pytest.mark.parametrize("i", range(0, len(SHAPES), 2))
@@ -116,9 +121,10 @@ def test_random_shape_shared_filter(sc, i):
     assert_within_bound(to_host(dk), dk_ref, Sk, bf, what + " dk")
 
 
-@pytest.mark.parametrize("i", [i for i in range(len(SHAPES)) if SHAPES[i][2] <= 4096 and i % 3 == 1])
+@pytest.mark.parametrize("i", [i for i in range(len(SHAPES)) if i % 3 == 1 or SHAPES[i][2] > 4096])
 def test_random_shape_exact_real_valued(sc, i):
-    # fixed-point encoding with 20 + 20 fraction bits, three primes: bit for bit the oracle
+    # fixed-point encoding with 20 + 20 fraction bits, three primes (fused, or the four-step
+    # split beyond L = 4096): bit for bit the oracle
     B, C, L = SHAPES[i]
     v, g = make_inputs(WORKLOADS[4], B=B, C=C, L=L, seed_offset=1000 + i)
     assert sc.sc_fixed_range_ok(float(np.abs(v).max()), float(np.abs(g).max()), 20, 20, L)
