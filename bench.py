@@ -167,6 +167,25 @@ def kernel_matches(name: str, storage: str, L: int, rev: bool = False) -> bool:
     return ("fused_conv_kernel<%d, sc::%s, %s>" % (M, io, flag)) in name
 
 
+def four_step_calls(w, markers: int, where: str) -> float:
+    """Calls of the four-step path in a counter run, from its count of marker dispatches:
+    the call is several kernels (columns, rows, columns per part of the channels, then for
+    the float kinds the head); one head kernel per float call, and the exact kind's
+    inverse-column kernel once per chunk of channels."""
+    if not markers:
+        raise RuntimeError("%s: no dispatch to count four-step calls" % where)
+    if w.storage != "i32":
+        return float(markers)
+    import fft_causal_long_amd as sc
+    M = 1 << (w.L - 1).bit_length()
+    per_chunk = sc.sc_workspace_bytes(sc.KIND_NTT_I32, w.B, w.C, w.L) // (24 * M)
+    return markers / -(-w.channels // per_chunk)
+
+
+def four_step_marker(w) -> str:
+    return "head_kernel" if w.storage != "i32" else "ntt4_columns_inv"
+
+
 def record_traffic(w, fetch_dir: str, write_dir: str) -> dict:
     """Turn two rocprofv3 counter runs (FETCH_SIZE, WRITE_SIZE, KiB per dispatch, both run
     with --calib-copy) into HBM bytes per launch of the hot path.  Each counter is scaled
@@ -184,25 +203,14 @@ def record_traffic(w, fetch_dir: str, write_dir: str) -> dict:
                 copy.append(val)
             elif kernel_matches(r["Kernel_Name"], w.storage, w.L):
                 hot[r["Dispatch_Id"]] = hot.get(r["Dispatch_Id"], 0.0) + val
-                if ("head_kernel" if w.storage != "i32" else "ntt4_columns_inv") in r["Kernel_Name"]:
+                if four_step_marker(w) in r["Kernel_Name"]:
                     calls.add(r["Dispatch_Id"])
         if not hot or len(copy) != 1:
             raise RuntimeError("%s: expected hot-path dispatches and one calibration copy" % d)
         scale = COPY_BYTES / (copy[0] * 1024.0)
         if w.L > 4096:
-            # the four-step call is several kernels (columns, rows, columns per part of the
-            # channels, then for the float kinds the head): bytes per call = all of them /
-            # calls (one head kernel per float call; the exact kind's inverse-column kernel
-            # runs once per chunk of channels)
-            if not calls:
-                raise RuntimeError("%s: no dispatch to count four-step calls" % d)
-            ncalls = len(calls)
-            if w.storage == "i32":
-                import fft_causal_long_amd as sc
-                M = 1 << (w.L - 1).bit_length()
-                per_chunk = sc.sc_workspace_bytes(sc.KIND_NTT_I32, w.B, w.C, w.L) // (24 * M)
-                ncalls = len(calls) / -(-w.channels // per_chunk)
-            return float(sum(hot.values())) / ncalls * 1024.0 * scale, scale
+            return float(sum(hot.values())) / four_step_calls(w, len(calls), d) * 1024.0 * scale, \
+                scale
         return float(np.mean(list(hot.values()))) * 1024.0 * scale, scale
 
     fetch, fs = per_dispatch(fetch_dir, "FETCH_SIZE")
@@ -220,17 +228,23 @@ def record_traffic(w, fetch_dir: str, write_dir: str) -> dict:
 
 def record_valu(w, sq_dir: str) -> dict:
     """From a rocprofv3 counter run with SQ_INSTS_VALU (summed over the chip, per dispatch),
-    the VALU instructions one launch of the hot kernel issues."""
+    the VALU instructions one launch of the hot kernel issues; for the four-step path (several
+    kernels per call), the instructions of one whole call."""
     import csv
-    per = {}
+    per, calls = {}, set()
     for r in csv.DictReader(open(os.path.join(sq_dir, "run_counter_collection.csv"))):
         if r["Counter_Name"] == "SQ_INSTS_VALU" and kernel_matches(r["Kernel_Name"], w.storage, w.L):
             per[r["Dispatch_Id"]] = per.get(r["Dispatch_Id"], 0.0) + float(r["Counter_Value"])
+            if four_step_marker(w) in r["Kernel_Name"]:
+                calls.add(r["Dispatch_Id"])
     if not per:
         raise RuntimeError("%s: no SQ_INSTS_VALU rows for the hot kernel" % sq_dir)
+    if w.L > 4096:
+        valu = float(sum(per.values())) / four_step_calls(w, len(calls), sq_dir)
+    else:
+        valu = float(np.mean(list(per.values())))
     rec = {"workload": w.name, "source_hash": kernel_source_hash(),
-           "valu_instructions_per_launch": round(float(np.mean(list(per.values())))),
-           "dispatches": len(per)}
+           "valu_instructions_per_launch": round(valu), "dispatches": len(per)}
     path = os.path.join(ROOT, "profiles", "valu_%s.json" % w.name)
     with open(path, "w") as f:
         json.dump(rec, f, indent=1)
