@@ -194,3 +194,29 @@ def test_empty_inputs_on_every_call(sc):
         k = torch.zeros((C, L), dtype=torch.float32, device=dev)
         assert sc.causal_conv_shared(f, k).shape == f.shape
     torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("L,cid", [(4096, 3), (3000, 3), (3000, 4), (2056, 4), (3001, 4)])
+def test_m4096_many_channels_same_bits(sc, L, cid):
+    # more channels than workgroups resident at once (several generations of workgroups, the
+    # bf16 kernel touching the next generation's inputs): every channel carries the bits of a
+    # call of 100 channels, in both directions, and a few channels are checked on the oracle
+    C = 1500
+    v, g = make_inputs(WORKLOADS[cid], B=1, C=C, L=L, seed_offset=L + cid)
+    dr, _ = make_inputs(WORKLOADS[cid], B=1, C=C, L=L, seed_offset=L + cid + 7)
+    print("case many channels L=%d %s" % (L, "bf16" if v.dtype == np.uint16 else "f32"), flush=True)
+    tv, tg, td = to_device(v), to_device(g), to_device(dr)
+    r = sc.causal_conv(tv, tg)
+    dv, dg = sc.causal_conv_bwd(td, tv, tg)
+    bits = torch.int16 if v.dtype == np.uint16 else torch.int32
+    for c0 in (0, 511, 1024, 1400):
+        sl = slice(c0, c0 + 100)
+        pv, pg, pd = (x[:, sl].contiguous() for x in (tv, tg, td))
+        assert torch.equal(sc.causal_conv(pv, pg).view(bits), r[:, sl].view(bits)), c0
+        qv, qg = sc.causal_conv_bwd(pd, pv, pg)
+        assert torch.equal(qv.view(bits), dv[:, sl].view(bits)), c0
+        assert torch.equal(qg.view(bits), dg[:, sl].view(bits)), c0
+    torch.cuda.synchronize()
+    chans = np.array([0, 511, 512, 513, 1023, 1024, C - 1])
+    r_ref, S = oracle.causal_conv_f64(v[0, chans], g[0, chans])
+    assert_within_bound(to_host(r)[0, chans], r_ref, S, v.dtype == np.uint16, "many channels")
