@@ -34,6 +34,11 @@ constexpr int64_t kMaxLNtt = 4096;
 #define SC_FUSED4K 1
 #endif
 constexpr bool kFused4k = SC_FUSED4K != 0;
+// M = 1024 float convolutions use the kernel of sc_fused1k.hip (0: the general fused kernel)
+#ifndef SC_FUSED1K
+#define SC_FUSED1K 1
+#endif
+constexpr bool kFused1k = SC_FUSED1K != 0;
 constexpr int64_t kNttP = 998244353;
 constexpr int32_t kMaxFrac = 64;          // |fixed-point fraction bits| of the exact real kind
 // the shared-filter gradients take the one-kernel path when it has at least this many
@@ -55,6 +60,7 @@ sc_status upload(const void* host, size_t bytes, void** dev)
 struct DeviceState {
     float2* fused_tw = nullptr;   // the float twiddle bank (sc_internal.h)
     float2* dit4k = nullptr;      // the M = 4096 fused kernel's (c, t) table (sc_internal.h)
+    float2* dit1k = nullptr;      // the M = 1024 fused kernel's (c, t) table (sc_internal.h)
     sc::NttTables ntt[3]{};       // primes A, B, C (sc::NTT_PRIMES)
     bool ntt_ready = false;
     sc::NttMfmaTables mfma{};     // the matrix-core NTT kernel's tables (prime A)
@@ -240,6 +246,25 @@ std::vector<float2> dit4k_table()
     return h;
 }
 
+// the M = 1024 kernel's table (layout in sc_internal.h)
+std::vector<float2> dit1k_table()
+{
+    std::vector<float2> h(sc::DIT1K_TABLE_FLOAT2, make_float2(0.f, 0.f));
+    h[sc::DIT1K_P1B1] = tan_pair(1, 8, false);
+    h[sc::DIT1K_P1B1 + 1] = tan_pair(2, 8, false);
+    for (int var = 0; var < 3; ++var) {
+        const bool inv = var == 2;
+        for (int j = 0; j < 4; ++j)
+            item_pairs(&h[sc::DIT1K_P2 + (var * 4 + j) * 10], var == 1 ? 2 * j + 1 : j,
+                       var == 1 ? 128 : 64, inv);
+        for (int j = 0; j < 64; ++j)
+            item_pairs(&h[sc::DIT1K_P3 + (var * 64 + j) * 10], var == 1 ? 2 * j + 1 : j,
+                       var == 1 ? 2048 : 1024, inv);
+    }
+    for (int k = 0; k < 1024; ++k) h[sc::DIT1K_UNP + k] = tan_pair(k, 2048, true);
+    return h;
+}
+
 std::mutex g_mu;
 DeviceState g_dev[kMaxDevices];
 
@@ -299,6 +324,14 @@ sc_status device_state(DeviceState** out, bool need_ntt, hipStream_t stream,
             (void)hipFree(p);
             return st;
         }
+        const std::vector<float2> t1 = dit1k_table();
+        void* p1 = nullptr;
+        if ((st = upload(t1.data(), t1.size() * sizeof(float2), &p1)) != SC_OK) {
+            (void)hipFree(p4);
+            (void)hipFree(p);
+            return st;
+        }
+        d.dit1k = (float2*)p1;
         d.dit4k = (float2*)p4;
         d.fused_tw = (float2*)p;
     }
@@ -672,6 +705,9 @@ sc_status run_jobs(sc_kind kind, const Job* jobs, int njobs, bool rev, int64_t n
             e = M == 4096 && kFused4k
                     ? sc::launch_fused4k(s, jobs[k].a, jobs[k].b, jobs[k].o, nch, (int)L, head,
                                          pair, rev, d->dit4k, stream)
+                : M == 1024 && kFused1k
+                    ? sc::launch_fused1k(s, jobs[k].a, jobs[k].b, jobs[k].o, nch, (int)L, head,
+                                         pair, rev, d->dit1k, stream)
                     : sc::launch_fused(s, jobs[k].a, jobs[k].b, jobs[k].o, nch, (int)L, M, head,
                                        pair, rev, d->fused_tw, stream);
     } else {
