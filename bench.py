@@ -164,8 +164,8 @@ def kernel_matches(name: str, storage: str, L: int, rev: bool = False) -> bool:
     io = "bf16_io" if storage == "bf16" else "f32_io"
     if M == 4096:
         return ("fused4k_kernel<sc::%s, %s>" % (io, flag)) in name
-    if M == 1024:
-        return ("fused1k_kernel<sc::%s, %s>" % (io, flag)) in name
+    if M in (1024, 2048):
+        return ("fused_dit_kernel<%d, sc::%s, %s>" % (M, io, flag)) in name
     return ("fused_conv_kernel<%d, sc::%s, %s>" % (M, io, flag)) in name
 
 

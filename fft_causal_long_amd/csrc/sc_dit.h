@@ -1,6 +1,6 @@
 // Decimation-in-time radix-16 and radix-4 butterflies with tangent-merged twiddles
 // (Linzer and Feig's scaled-twiddle FFT), for the fused kernels of sc_fused4k.hip (M = 4096)
-// and sc_fused1k.hip (M = 1024).  A twiddle T = c (1 + i t), t = tan of T's angle, is merged
+// and sc_fused_dit.hip (M = 1024, 2048).  A twiddle T = c (1 + i t), t = tan of T's angle, is merged
 // into the butterfly adds: a +- T y = a +- c (y + i t y), 6 fused multiply-adds for both
 // outputs instead of 4 for the product and 4 for the sums.  Where c is 0 (T = +-i) the tables
 // hold c = 2^-40, t = +-2^40, which keeps c (y + i t y) accurate to fp32 round-off.
@@ -97,6 +97,27 @@ __device__ __forceinline__ void load_tw(__amdgpu_buffer_rsrc_t rs, int entry, TC
     }
 }
 
+
+// Y[q] = sum_m W8^{m q} T^m y_m in place (natural order), from the six pairs
+// tw = {T^2, T^4, U_0, U_1, U_2, U_3}, U_p = T W8^p: the even and the odd inputs through
+// dft4t with T^2, then Y[p] = E[p] + U_p O[p] and Y[p + 4] = E[p] - U_p O[p], each pair of
+// outputs 6 fused multiply-adds.
+template <bool INV>
+__device__ __forceinline__ void dft8t(float2 (&y)[8], const TC (&tw)[6])
+{
+    float2 e0 = y[0], e1 = y[2], e2 = y[4], e3 = y[6];
+    float2 o0 = y[1], o1 = y[3], o2 = y[5], o3 = y[7];
+    dft4t<INV>(e0, e1, e2, e3, tw[0], tw[1]);
+    dft4t<INV>(o0, o1, o2, o3, tw[0], tw[1]);
+    const float2 e[4] = {e0, e1, e2, e3}, o[4] = {o0, o1, o2, o3};
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+        const TC u = tw[2 + p];
+        const float2 r = rot(o[p], u.t);
+        y[p] = make_float2(__builtin_fmaf(u.c, r.x, e[p].x), __builtin_fmaf(u.c, r.y, e[p].y));
+        y[p + 4] = make_float2(__builtin_fmaf(-u.c, r.x, e[p].x), __builtin_fmaf(-u.c, r.y, e[p].y));
+    }
+}
 
 }  // namespace dit
 }  // namespace sc

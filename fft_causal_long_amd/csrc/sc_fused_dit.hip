@@ -1,30 +1,32 @@
-// Fused in-LDS causal convolution for 512 < L <= 1024 (transform length M = 1024), gfx950.
+// Fused in-LDS causal convolution for 512 < L <= 2048 (transform length M = 1024 or 2048),
+// gfx950.
 //
 // The method and data flow of the general fused kernel (sc_fused.hip): z = v + i g, the two
-// branches u^b_n = z_n W_N^{b n} (N = 2M) transformed side by side by 64 threads each (one
-// wave per branch), the unpack of V G into the half-length real-output inverse spectrum Y,
-// one length-M inverse, the first `head` outputs by direct summation ("Caracal: Causal
-// Architecture via Spectral Mixing", key designs 1-2 and the real-FFT improvement its
-// limitations name).  The transforms are organised as in the M = 4096 kernel
-// (sc_fused4k.hip), with passes of radix 4, 16 and 16 in decimation in time:
+// branches u^b_n = z_n W_N^{b n} (N = 2M) transformed side by side by TB = M/16 threads each,
+// the unpack of V G into the half-length real-output inverse spectrum Y, one length-M
+// inverse, the first `head` outputs by direct summation ("Caracal: Causal Architecture via
+// Spectral Mixing", key designs 1-2 and the real-FFT improvement its limitations name).  The
+// transforms are organised as in the M = 4096 kernel (sc_fused4k.hip), with passes of radix
+// R1 = M/256 (4 or 8), 16 and 16 in decimation in time:
 //
-//   n = n'' + 16 n2 + 256 n1,  k = k1 + 4 k2 + 64 k3  (n1, k1 < 4; n2, k2, n'', k3 < 16)
-//   pass 1 (registers): y1[n''+16 n2][k1] = sum_{n1} x[n] W4^{n1 k1}
-//   pass 2: y2[n''][k1+4k2] = sum_{n2} W64^{n2 k1} y1[n''+16 n2][k1] W16^{n2 k2}
-//   pass 3: X[m + 64 k3] = sum_{n''} W1024^{n'' m} y2[n''][m] W16^{n'' k3},  m = k1 + 4 k2
+//   n = n'' + 16 n2 + 256 n1,  k = k1 + R1 k2 + TB k3  (n1, k1 < R1; n2, k2, n'', k3 < 16)
+//   pass 1 (registers): y1[n''+16 n2][k1] = sum_{n1} x[n] W_R1^{n1 k1}
+//   pass 2: y2[n''][k1+R1 k2] = sum_{n2} W_{16 R1}^{n2 k1} y1[n''+16 n2][k1] W16^{n2 k2}
+//   pass 3: X[m + TB k3] = sum_{n''} W_M^{n'' m} y2[n''][m] W16^{n'' k3},  m = k1 + R1 k2
 //
-// Thread tau holds elements tau + 64 q (q < 16) at the input, so the radix-4 groups of pass 1
-// (q, q + 4, q + 8, q + 12) sit in its registers and pass 1 needs no exchange; after pass 3
-// it holds bins tau + 64 q, the order the unpack of the M = 4096 kernel takes.  Branch 1's
-// rotation W_N^n = W_N^{n''} W_128^{n2} W_8^{n1} goes into the twiddles: W_8 is pass 1's
-// constant base, W_128^{2k1+1} and W_2048^{2m+1} are the bases of passes 2 and 3.  All
-// twiddles are merged into the butterflies (sc_dit.h).
+// Thread tau holds elements tau + TB q (q < 16) at the input, so the radix-R1 groups of pass
+// 1 (q0 + (16/R1) n1) sit in its registers and pass 1 needs no exchange; after pass 3 it
+// holds bins tau + TB q, the order the unpack of the M = 4096 kernel takes.  Branch 1's
+// rotation W_N^n = W_N^{n''} W_{32 R1}^{n2} W_{2 R1}^{n1} goes into the twiddles: W_{2 R1}
+// is pass 1's constant base, W_{32 R1}^{2k1+1} and W_{2M}^{2m+1} are the bases of passes 2
+// and 3.  All twiddles are merged into the butterflies (sc_dit.h).
 //
 // LDS (float2 units): pass 1 writes y1[n'][k1] at n' + 272 k1, pass 2 reads it (item
-// (n'', k1) = (tau % 16, tau / 16)) and writes y2[n''][m] at m + 66 n'', pass 3 reads that;
-// Y of the inverse at ypos(k), the mirror exchange of the unpack after Y.  Every access
-// pattern of a wave hits 32 different bank pairs per 32 lanes (8-byte accesses serve 32
-// lanes per cycle).  17.9 KB per workgroup of 128 threads: eight workgroups per CU.
+// (n'', k1) = (tau % 16, tau / 16)) and writes y2[n''][m] at m + (TB + 2) n'', pass 3 reads
+// that; Y of the inverse at ypos(k), the mirror exchange of the unpack after Y.  Each access
+// pattern hits 32 different bank pairs per 32 lanes (8-byte accesses serve 32 lanes per
+// cycle).  M = 1024: 17.7 KB per workgroup of 128 threads, eight workgroups per CU; M = 2048:
+// 35 KB per workgroup of 256 threads, four per CU.
 
 #include "sc_device.h"
 #include "sc_dit.h"
@@ -33,39 +35,50 @@
 
 namespace sc {
 
-namespace f1k {
+namespace fdit {
 
-constexpr int M = 1024, TB = 64, FT = 128;
-constexpr int REGION = 1088;   // one branch unit's pass layouts (positions < 1072)
-constexpr int XCH = 1040;      // mirror exchange [unit][8][64], after Y (positions < 1040)
+template <int M>
+struct Shape {
+    static constexpr int TB = M / 16, FT = 2 * TB, R1 = M / 256, G = 16 / R1;
+    static constexpr int P2S = TB + 2;   // y2[n''][m] at m + P2S n''
+    // one branch unit's pass layouts (positions < 272 R1 - 16 and < M + 30)
+    static constexpr int REGION = 272 * R1 - 16 > M + 32 ? 272 * R1 - 16 : M + 32;
+    static constexpr int XCH = M + 16;   // mirror exchange [unit][8][TB], after Y
+    // the table's parts (sc_internal.h)
+    static constexpr int T_P1B1 = DIT_P1B1, T_P2 = dit_p2(M), T_P3 = dit_p3(M);
+    static constexpr int T_UNP = dit_unp(M), T_SIZE = dit_table_size(M);
+    static_assert(R1 == 4 || R1 == 8, "M = 1024 or 2048");
+    static_assert(XCH + 16 * TB <= 2 * REGION, "the exchange fits the two regions");
+};
 
+template <int M>
 __device__ __forceinline__ int ypos(int k) { return (k >> 1) + (k & 1) * (M / 2 + 16); }
-__device__ __forceinline__ int p1pos(int np, int k1) { return np + 272 * k1; }
-__device__ __forceinline__ int p2pos(int npp, int m) { return m + 66 * npp; }
 
-}  // namespace f1k
+}  // namespace fdit
 
-template <class IO, bool REV>
-__global__ __launch_bounds__(128) void fused1k_kernel(const typename IO::T* __restrict__ v,
-                                                      const typename IO::T* __restrict__ g,
-                                                      typename IO::T* __restrict__ r, int L,
-                                                      int head, int pair_store,
-                                                      const float2* __restrict__ tab, int64_t pf)
+template <int M, class IO, bool REV>
+__global__ __launch_bounds__(M / 8) void fused_dit_kernel(const typename IO::T* __restrict__ v,
+                                                         const typename IO::T* __restrict__ g,
+                                                         typename IO::T* __restrict__ r, int L,
+                                                         int head, int pair_store,
+                                                         const float2* __restrict__ tab,
+                                                         int64_t pf)
 {
-    using namespace f1k;
     using namespace dit;
-    __shared__ float2 lds[2 * REGION];
+    using S = fdit::Shape<M>;
+    constexpr int TB = S::TB, R1 = S::R1, G = S::G;
+    __shared__ float2 lds[2 * S::REGION];
     __shared__ float hbuf[2 * HEAD_MAX];
 
-    const auto trs = __builtin_amdgcn_make_buffer_rsrc((void*)tab, (short)0, DIT1K_TABLE_FLOAT2 * 8,
+    const auto trs = __builtin_amdgcn_make_buffer_rsrc((void*)tab, (short)0, S::T_SIZE * 8,
                                                        0x00020000);
     const int tid = threadIdx.x, tau = tid & (TB - 1);
-    const int unit = __builtin_amdgcn_readfirstlane(tid >> 6);   // one wave per unit
+    const int unit = __builtin_amdgcn_readfirstlane(tid / TB);   // uniform per wave
     const int64_t ch = blockIdx.x;
     const Span vs = make_span(v, ch * L, L);
     const Span gs = make_span(g, ch * L, L);
 
-    // 1. z_n = v_n + i g_n, n = tau + 64 q (0 past L)
+    // 1. z_n = v_n + i g_n, n = tau + TB q (0 past L)
     float2 x[16];
     if (L == M) {
         const int vb = REV ? L - 1 - tau - TB * 15 : tau;
@@ -88,45 +101,53 @@ __global__ __launch_bounds__(128) void fused1k_kernel(const typename IO::T* __re
         hbuf[HEAD_MAX + tau] = x[0].y;
     }
 
-    float2* const reg = lds + unit * REGION;
+    float2* const reg = lds + unit * S::REGION;
     const int npp = tau & 15, k1 = tau >> 4;   // the pass-2 item of this thread
 
-    // pass 1 (forward or inverse): the four radix-4 groups of registers q0, q0 + 4, q0 + 8,
-    // q0 + 12 (n' = tau + 64 q0), branch 1 with its constant twiddle base, written to LDS
+    // pass 1 (forward or inverse): the G radix-R1 groups of registers q0 + G n1
+    // (n' = tau + TB q0), branch 1 with its constant twiddle base, written to LDS
     auto pass1 = [&](float2* dst, bool twiddled, auto inv_tag) {
         constexpr bool INV = decltype(inv_tag)::value;
-        TC t1{1.0f, 0.0f}, t2{1.0f, 0.0f};
+        TC tw[6];
         if (twiddled) {
-            const float4 f = __builtin_bit_cast(
-                float4, __builtin_amdgcn_raw_buffer_load_b128(trs, DIT1K_P1B1 * 8, 0, 0));
-            t1 = TC{f.x, f.y};
-            t2 = TC{f.z, f.w};
+#pragma unroll
+            for (int i = 0; i < (R1 == 4 ? 1 : 3); ++i) {
+                const float4 f = __builtin_bit_cast(
+                    float4, __builtin_amdgcn_raw_buffer_load_b128(trs, S::T_P1B1 * 8 + 16 * i, 0, 0));
+                tw[2 * i] = TC{f.x, f.y};
+                tw[2 * i + 1] = TC{f.z, f.w};
+            }
         }
 #pragma unroll
-        for (int q0 = 0; q0 < 4; ++q0) {
-            float2 a = x[q0], b = x[q0 + 4], c = x[q0 + 8], d = x[q0 + 12];
-            if (twiddled) dft4t<INV>(a, b, c, d, t1, t2);
-            else dft4<INV>(a, b, c, d);
+        for (int q0 = 0; q0 < G; ++q0) {
+            float2 y[R1];
+#pragma unroll
+            for (int n1 = 0; n1 < R1; ++n1) y[n1] = x[q0 + G * n1];
+            if constexpr (R1 == 4) {
+                if (twiddled) dft4t<INV>(y[0], y[1], y[2], y[3], tw[0], tw[1]);
+                else dft4<INV>(y[0], y[1], y[2], y[3]);
+            } else {
+                if (twiddled) dft8t<INV>(y, tw);
+                else dft8<INV>(y);
+            }
             const int np = tau + TB * q0;
-            dst[p1pos(np, 0)] = a;
-            dst[p1pos(np, 1)] = b;
-            dst[p1pos(np, 2)] = c;
-            dst[p1pos(np, 3)] = d;
+#pragma unroll
+            for (int kk = 0; kk < R1; ++kk) dst[np + 272 * kk] = y[kk];
         }
     };
     // pass 2, item (n'', k1): its inputs y1[n'' + 16 n2][k1] (read before a barrier), then the
-    // butterfly and y2[n''][k1 + 4 k2] written
+    // butterfly and y2[n''][k1 + R1 k2] written
     auto pass2_read = [&](const float2* buf) {
 #pragma unroll
-        for (int n2 = 0; n2 < 16; ++n2) x[n2] = buf[p1pos(npp + 16 * n2, k1)];
+        for (int n2 = 0; n2 < 16; ++n2) x[n2] = buf[npp + 16 * n2 + 272 * k1];
     };
     auto pass2_write = [&](float2* buf, int var, auto inv_tag) {
         constexpr bool INV = decltype(inv_tag)::value;
         TC tw[10];
-        load_tw(trs, DIT1K_P2 + (var * 4 + k1) * 10, tw);
+        load_tw(trs, S::T_P2 + (var * R1 + k1) * 10, tw);
         dit16<INV>(x, tw);
 #pragma unroll
-        for (int k2 = 0; k2 < 16; ++k2) buf[p2pos(npp, k1 + 4 * k2)] = x[k2];
+        for (int k2 = 0; k2 < 16; ++k2) buf[k1 + R1 * k2 + S::P2S * npp] = x[k2];
     };
 
     // 2. forward transform of branch `unit`
@@ -138,15 +159,15 @@ __global__ __launch_bounds__(128) void fused1k_kernel(const typename IO::T* __re
     __syncthreads();
     {
         TC tw[10];
-        load_tw(trs, DIT1K_P3 + (unit * TB + tau) * 10, tw);
+        load_tw(trs, S::T_P3 + (unit * TB + tau) * 10, tw);
 #pragma unroll
-        for (int n = 0; n < 16; ++n) x[n] = reg[p2pos(n, tau)];
+        for (int n = 0; n < 16; ++n) x[n] = reg[tau + S::P2S * n];
         __syncthreads();
-        dit16<false>(x, tw);   // x[q] = Z_{2 (tau + 64 q) + unit}
+        dit16<false>(x, tw);   // x[q] = Z_{2 (tau + TB q) + unit}
     }
 
     // 3. unpack.  The mirror thread needs registers 4..7 and 12..15 of this one.
-    float2* xch = lds + XCH + unit * 8 * TB;
+    float2* xch = lds + S::XCH + unit * 8 * TB;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         xch[i * TB + tau] = x[4 + i];
@@ -186,7 +207,7 @@ __global__ __launch_bounds__(128) void fused1k_kernel(const typename IO::T* __re
         const float2 df = make_float2(x1.x - x2.x, x1.y + x2.y);
         // T = W_N^{-k} D = c (D + i t D);  Y_k = S + i T,  Y_{M-k} = conj(S - i T)
         const float2 ct = __builtin_bit_cast(
-            float2, __builtin_amdgcn_raw_buffer_load_b64(trs, k * 8, DIT1K_UNP * 8, 0));
+            float2, __builtin_amdgcn_raw_buffer_load_b64(trs, k * 8, S::T_UNP * 8, 0));
         const float2 u = rot(df, ct.y);
         yk[q] = make_float2(__builtin_fmaf(-ct.x, u.y, sm.x), __builtin_fmaf(ct.x, u.x, sm.y));
         ymk[q] = make_float2(__builtin_fmaf(ct.x, u.y, sm.x), __builtin_fmaf(ct.x, u.x, -sm.y));
@@ -201,7 +222,7 @@ __global__ __launch_bounds__(128) void fused1k_kernel(const typename IO::T* __re
         // Y = S + i (i D) = (2 Re 4X, -2 Im 4X)
         ymk[0] = make_float2(2.f * x1.x, -2.f * x1.y);
     }
-    // ypos(k) = yb + 64 q, ypos(M - k) = ym - 64 q for k = 2 (tau + 64 q) + unit
+    // ypos(k) = yb + TB q, ypos(M - k) = ym - TB q for k = 2 (tau + TB q) + unit
     float2* ybuf = lds;
     const int yb = tau + unit * (M / 2 + 16);
     const int ym = M / 2 - tau - unit + unit * (M / 2 + 16);
@@ -219,7 +240,7 @@ __global__ __launch_bounds__(128) void fused1k_kernel(const typename IO::T* __re
     static_assert(M * sizeof(typename IO::T) <= 128 * TB, "unit 1 covers a channel's lines");
     if (unit == 0) {
 #pragma unroll
-        for (int q = 0; q < 16; ++q) x[q] = ybuf[ypos(tau + TB * q)];
+        for (int q = 0; q < 16; ++q) x[q] = ybuf[fdit::ypos<M>(tau + TB * q)];
     }
     __syncthreads();
     if (unit == 0) {
@@ -238,11 +259,11 @@ __global__ __launch_bounds__(128) void fused1k_kernel(const typename IO::T* __re
     __syncthreads();
     if (unit == 0) {
         TC tw[10];
-        load_tw(trs, DIT1K_P3 + (2 * TB + tau) * 10, tw);
+        load_tw(trs, S::T_P3 + (2 * TB + tau) * 10, tw);
 #pragma unroll
-        for (int n = 0; n < 16; ++n) x[n] = lds[p2pos(n, tau)];
+        for (int n = 0; n < 16; ++n) x[n] = lds[tau + S::P2S * n];
         dit16<true, true>(x, tw);
-        // 5. x[q] = 8 M y_m, m = tau + 64 q (q < 8): r_{2m} = Re, r_{2m+1} = Im
+        // 5. x[q] = 8 M y_m, m = tau + TB q (q < 8): r_{2m} = Re, r_{2m+1} = Im
         const float scale = 1.0f / (8.0f * (float)M);
 #pragma unroll
         for (int q = 0; q < 8; ++q) {
@@ -266,31 +287,39 @@ __global__ __launch_bounds__(128) void fused1k_kernel(const typename IO::T* __re
     if (unit == 1) keep_touched(touched, pf, rs);
 }
 
-template <class IO, bool REV>
-static hipError_t launch1k(const void* v, const void* g, void* r, int64_t nch, int L, int head,
-                           bool pair, const float2* tab, hipStream_t stream)
+template <int M, class IO, bool REV>
+static hipError_t launch_dit(const void* v, const void* g, void* r, int64_t nch, int L, int head,
+                             bool pair, const float2* tab, hipStream_t stream)
 {
-    if (!grid_ok(nch, f1k::FT)) return hipErrorInvalidValue;
+    constexpr int FT = fdit::Shape<M>::FT;
+    if (!grid_ok(nch, FT)) return hipErrorInvalidValue;
     // the next generation's inputs touched into the L2 of the XCD that will run it
     static int64_t resident[16];
     const int64_t pf =
-        resident_workgroups((const void*)fused1k_kernel<IO, REV>, f1k::FT, resident) / 8 * 8;
-    hipLaunchKernelGGL((fused1k_kernel<IO, REV>), dim3((unsigned)nch), dim3(f1k::FT), 0, stream,
+        resident_workgroups((const void*)fused_dit_kernel<M, IO, REV>, FT, resident) / 8 * 8;
+    hipLaunchKernelGGL((fused_dit_kernel<M, IO, REV>), dim3((unsigned)nch), dim3(FT), 0, stream,
                        (const typename IO::T*)v, (const typename IO::T*)g, (typename IO::T*)r, L,
                        head, pair ? 1 : 0, tab, pf);
     return hipGetLastError();
 }
 
-hipError_t launch_fused1k(Store st, const void* v, const void* g, void* r, int64_t nch, int L,
-                          int head, bool pair_store, bool rev, const float2* tab,
-                          hipStream_t stream)
+hipError_t launch_fused_dit(Store st, const void* v, const void* g, void* r, int64_t nch, int L,
+                            int M, int head, bool pair_store, bool rev, const float2* tab,
+                            hipStream_t stream)
 {
-    if (L <= 512 || L > 1024 || head > HEAD_MAX) return hipErrorInvalidValue;
-    if (st == Store::F32)
-        return rev ? launch1k<f32_io, true>(v, g, r, nch, L, head, pair_store, tab, stream)
-                   : launch1k<f32_io, false>(v, g, r, nch, L, head, pair_store, tab, stream);
-    return rev ? launch1k<bf16_io, true>(v, g, r, nch, L, head, pair_store, tab, stream)
-               : launch1k<bf16_io, false>(v, g, r, nch, L, head, pair_store, tab, stream);
+    if (L <= M / 2 || L > M || head > HEAD_MAX) return hipErrorInvalidValue;
+#define SC_CALL(m)                                                                             \
+    st == Store::F32                                                                           \
+        ? (rev ? launch_dit<m, f32_io, true>(v, g, r, nch, L, head, pair_store, tab, stream)    \
+               : launch_dit<m, f32_io, false>(v, g, r, nch, L, head, pair_store, tab, stream))  \
+        : (rev ? launch_dit<m, bf16_io, true>(v, g, r, nch, L, head, pair_store, tab, stream)   \
+               : launch_dit<m, bf16_io, false>(v, g, r, nch, L, head, pair_store, tab, stream))
+    switch (M) {
+    case 1024: return SC_CALL(1024);
+    case 2048: return SC_CALL(2048);
+    default: return hipErrorInvalidValue;
+    }
+#undef SC_CALL
 }
 
 }  // namespace sc

@@ -34,11 +34,12 @@ constexpr int64_t kMaxLNtt = 4096;
 #define SC_FUSED4K 1
 #endif
 constexpr bool kFused4k = SC_FUSED4K != 0;
-// M = 1024 float convolutions use the kernel of sc_fused1k.hip (0: the general fused kernel)
-#ifndef SC_FUSED1K
-#define SC_FUSED1K 1
+// M = 1024 and 2048 float convolutions use the kernels of sc_fused_dit.hip (0: the general
+// fused kernel)
+#ifndef SC_FUSED_DIT
+#define SC_FUSED_DIT 1
 #endif
-constexpr bool kFused1k = SC_FUSED1K != 0;
+constexpr bool kFusedDit = SC_FUSED_DIT != 0;
 constexpr int64_t kNttP = 998244353;
 constexpr int32_t kMaxFrac = 64;          // |fixed-point fraction bits| of the exact real kind
 // the shared-filter gradients take the one-kernel path when it has at least this many
@@ -60,7 +61,7 @@ sc_status upload(const void* host, size_t bytes, void** dev)
 struct DeviceState {
     float2* fused_tw = nullptr;   // the float twiddle bank (sc_internal.h)
     float2* dit4k = nullptr;      // the M = 4096 fused kernel's (c, t) table (sc_internal.h)
-    float2* dit1k = nullptr;      // the M = 1024 fused kernel's (c, t) table (sc_internal.h)
+    float2* dit[2] = {nullptr, nullptr};   // the M = 1024, 2048 kernels' tables (sc_internal.h)
     sc::NttTables ntt[3]{};       // primes A, B, C (sc::NTT_PRIMES)
     bool ntt_ready = false;
     sc::NttMfmaTables mfma{};     // the matrix-core NTT kernel's tables (prime A)
@@ -246,22 +247,30 @@ std::vector<float2> dit4k_table()
     return h;
 }
 
-// the M = 1024 kernel's table (layout in sc_internal.h)
-std::vector<float2> dit1k_table()
+// the table of the M = 1024 or 2048 kernel (layout in sc_internal.h)
+std::vector<float2> dit_table(int M)
 {
-    std::vector<float2> h(sc::DIT1K_TABLE_FLOAT2, make_float2(0.f, 0.f));
-    h[sc::DIT1K_P1B1] = tan_pair(1, 8, false);
-    h[sc::DIT1K_P1B1 + 1] = tan_pair(2, 8, false);
+    const int R1 = M / 256, TB = M / 16;
+    std::vector<float2> h(sc::dit_table_size(M), make_float2(0.f, 0.f));
+    if (R1 == 4) {
+        h[sc::DIT_P1B1] = tan_pair(1, 8, false);
+        h[sc::DIT_P1B1 + 1] = tan_pair(2, 8, false);
+    } else {
+        // T = W_16: T^2, T^4, then U_p = T W_8^p = W_16^{1 + 2p}
+        h[sc::DIT_P1B1] = tan_pair(2, 16, false);
+        h[sc::DIT_P1B1 + 1] = tan_pair(4, 16, false);
+        for (int p = 0; p < 4; ++p) h[sc::DIT_P1B1 + 2 + p] = tan_pair(1 + 2 * p, 16, false);
+    }
     for (int var = 0; var < 3; ++var) {
         const bool inv = var == 2;
-        for (int j = 0; j < 4; ++j)
-            item_pairs(&h[sc::DIT1K_P2 + (var * 4 + j) * 10], var == 1 ? 2 * j + 1 : j,
-                       var == 1 ? 128 : 64, inv);
-        for (int j = 0; j < 64; ++j)
-            item_pairs(&h[sc::DIT1K_P3 + (var * 64 + j) * 10], var == 1 ? 2 * j + 1 : j,
-                       var == 1 ? 2048 : 1024, inv);
+        for (int j = 0; j < R1; ++j)
+            item_pairs(&h[sc::dit_p2(M) + (var * R1 + j) * 10], var == 1 ? 2 * j + 1 : j,
+                       var == 1 ? 32 * R1 : 16 * R1, inv);
+        for (int j = 0; j < TB; ++j)
+            item_pairs(&h[sc::dit_p3(M) + (var * TB + j) * 10], var == 1 ? 2 * j + 1 : j,
+                       var == 1 ? 2 * M : M, inv);
     }
-    for (int k = 0; k < 1024; ++k) h[sc::DIT1K_UNP + k] = tan_pair(k, 2048, true);
+    for (int k = 0; k < M; ++k) h[sc::dit_unp(M) + k] = tan_pair(k, 2 * M, true);
     return h;
 }
 
@@ -324,14 +333,19 @@ sc_status device_state(DeviceState** out, bool need_ntt, hipStream_t stream,
             (void)hipFree(p);
             return st;
         }
-        const std::vector<float2> t1 = dit1k_table();
-        void* p1 = nullptr;
-        if ((st = upload(t1.data(), t1.size() * sizeof(float2), &p1)) != SC_OK) {
+        void* pd[2] = {nullptr, nullptr};
+        for (int i = 0; i < 2 && st == SC_OK; ++i) {
+            const std::vector<float2> t = dit_table(1024 << i);
+            st = upload(t.data(), t.size() * sizeof(float2), &pd[i]);
+        }
+        if (st != SC_OK) {
+            if (pd[0]) (void)hipFree(pd[0]);
             (void)hipFree(p4);
             (void)hipFree(p);
             return st;
         }
-        d.dit1k = (float2*)p1;
+        d.dit[0] = (float2*)pd[0];
+        d.dit[1] = (float2*)pd[1];
         d.dit4k = (float2*)p4;
         d.fused_tw = (float2*)p;
     }
@@ -705,9 +719,9 @@ sc_status run_jobs(sc_kind kind, const Job* jobs, int njobs, bool rev, int64_t n
             e = M == 4096 && kFused4k
                     ? sc::launch_fused4k(s, jobs[k].a, jobs[k].b, jobs[k].o, nch, (int)L, head,
                                          pair, rev, d->dit4k, stream)
-                : M == 1024 && kFused1k
-                    ? sc::launch_fused1k(s, jobs[k].a, jobs[k].b, jobs[k].o, nch, (int)L, head,
-                                         pair, rev, d->dit1k, stream)
+                : (M == 1024 || M == 2048) && kFusedDit
+                    ? sc::launch_fused_dit(s, jobs[k].a, jobs[k].b, jobs[k].o, nch, (int)L, M,
+                                           head, pair, rev, d->dit[M == 2048], stream)
                     : sc::launch_fused(s, jobs[k].a, jobs[k].b, jobs[k].o, nch, (int)L, M, head,
                                        pair, rev, d->fused_tw, stream);
     } else {

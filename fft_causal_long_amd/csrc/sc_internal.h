@@ -71,21 +71,23 @@ hipError_t launch_fused4k(Store st, const void* v, const void* g, void* r, int64
                           int head, bool pair_store, bool rev, const float2* table,
                           hipStream_t stream);
 
-// The M = 1024 fused kernel (sc_fused1k.hip, 512 < L <= 1024): passes of radix 4, 16, 16 in
-// decimation in time; its table of (c, t) pairs as for the M = 4096 kernel:
-//   [DIT1K_P1B1 + i]                  branch 1, pass 1: W_8 and W_8^2 (radix 4)
-//   [DIT1K_P2 + (var 4 + k1) 10 + i]  pass 2, item k1 < 4: base A = W_64^k1 (var 0),
-//                                      W_128^{2k1+1} (var 1), conj W_64^k1 (var 2)
-//   [DIT1K_P3 + (var 64 + m) 10 + i]  pass 3, item m < 64: W_1024^m, W_2048^{2m+1}, conj
-//   [DIT1K_UNP + k]                   W_2048^{-k}, k < 1024 (the unpack)
-constexpr int DIT1K_P1B1 = 0;
-constexpr int DIT1K_P2 = 2;
-constexpr int DIT1K_P3 = DIT1K_P2 + 3 * 4 * 10;
-constexpr int DIT1K_UNP = DIT1K_P3 + 3 * 64 * 10;
-constexpr int DIT1K_TABLE_FLOAT2 = DIT1K_UNP + 1024;
-hipError_t launch_fused1k(Store st, const void* v, const void* g, void* r, int64_t nch, int L,
-                          int head, bool pair_store, bool rev, const float2* table,
-                          hipStream_t stream);
+// The fused kernels of sc_fused_dit.hip for M = 1024 and 2048 (M/2 < L <= M): passes of
+// radix R1 = M/256, 16, 16 in decimation in time with tangent-merged twiddles.  Their table
+// of (c, t) pairs for one M (as for the M = 4096 kernel):
+//   [DIT_P1B1 + i]                     branch 1, pass 1: R1 = 4: W_8, W_8^2; R1 = 8: W_8,
+//                                      W_4 (the squares) and W_16^{1+2p}, p < 4
+//   [dit_p2(M) + (var R1 + k1) 10 + i]  pass 2, item k1 < R1: base W_{16 R1}^k1 (var 0),
+//                                      W_{32 R1}^{2k1+1} (var 1), the conjugate of var 0 (2)
+//   [dit_p3(M) + (var M/16 + m) 10 + i] pass 3, item m < M/16: W_M^m, W_2M^{2m+1}, conj
+//   [dit_unp(M) + k]                   W_2M^{-k}, k < M (the unpack)
+constexpr int DIT_P1B1 = 0;
+constexpr int dit_p2(int) { return 6; }
+constexpr int dit_p3(int M) { return dit_p2(M) + 3 * (M / 256) * 10; }
+constexpr int dit_unp(int M) { return dit_p3(M) + 3 * (M / 16) * 10; }
+constexpr int dit_table_size(int M) { return dit_unp(M) + M; }
+hipError_t launch_fused_dit(Store st, const void* v, const void* g, void* r, int64_t nch, int L,
+                            int M, int head, bool pair_store, bool rev, const float2* table,
+                            hipStream_t stream);
 
 // Constants of the exact path modulo p = 998244353 (omega_n = 3^((p-1)/n)).  The bank
 // holds pairs of doubles {w, w / p}:

@@ -50,12 +50,12 @@ def test_direct_lengths(sc, L):
     check(sc, 1, 2, 5, L, "direct L=%d" % L, seed=L)
 
 
-@pytest.mark.parametrize("L", [33, 64, 100, 256, 1000, 1024, 2049, 3000, 4095, 4096])
+@pytest.mark.parametrize("L", [33, 64, 100, 256, 1000, 1024, 1500, 2048, 2049, 3000, 4095, 4096])
 def test_fused_f32(sc, L):
     check(sc, 2, 1, 16, L, "fused f32 L=%d" % L, seed=L)
 
 
-@pytest.mark.parametrize("L", [64, 1000, 4096])
+@pytest.mark.parametrize("L", [64, 1000, 2000, 4096])
 def test_fused_bf16(sc, L):
     check(sc, 3, 1, 8, L, "fused bf16 L=%d" % L, seed=L)
 

@@ -196,11 +196,13 @@ def test_empty_inputs_on_every_call(sc):
     torch.cuda.synchronize()
 
 
-@pytest.mark.parametrize("L,cid", [(4096, 3), (3000, 3), (3000, 4), (2056, 4), (3001, 4)])
-def test_m4096_many_channels_same_bits(sc, L, cid):
-    # more channels than workgroups resident at once (several generations of workgroups, the
-    # bf16 kernel touching the next generation's inputs): every channel carries the bits of a
-    # call of 100 channels, in both directions, and a few channels are checked on the oracle
+@pytest.mark.parametrize("L,cid", [(4096, 3), (3000, 3), (3000, 4), (2056, 4), (3001, 4),
+                                   (1024, 4), (777, 3), (2048, 3), (1500, 4)])
+def test_many_channels_same_bits(sc, L, cid):
+    # more channels than workgroups resident at once (several generations of workgroups, each
+    # touching the next generation's inputs) through the M = 1024, 2048 and 4096 kernels:
+    # every channel carries the bits of a call of 100 channels, in both directions, and a few
+    # channels are checked on the oracle
     C = 1500
     v, g = make_inputs(WORKLOADS[cid], B=1, C=C, L=L, seed_offset=L + cid)
     dr, _ = make_inputs(WORKLOADS[cid], B=1, C=C, L=L, seed_offset=L + cid + 7)
