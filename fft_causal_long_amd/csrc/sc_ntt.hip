@@ -87,15 +87,20 @@ __device__ __forceinline__ double round_int(double x)
 {
     return (x + SHIFT) - SHIFT;
 }
-// a * w mod p, |a| < 2^36, |result| <= 1.5 p
+// the odd part of n
+constexpr uint64_t odd_part(uint64_t n) { return n % 2 ? n : odd_part(n / 2); }
+
+// a * w mod p, |a| < 2^36, |result| <= 1.5 p.  q = a w / p rounded, within one of the exact
+// quotient.  p - 1 = c 2^k with c < 2^15, so q (p - 1) is exact in float64, and
+// a w - q (p - 1), an integer below 2^38 in magnitude, comes exactly out of one fused
+// multiply-add; less q it is a w - q p.  Five operations.
 template <class Pr>
 __device__ __forceinline__ double mulc(double a, W w)
 {
-    constexpr double P = (double)Pr::p;
-    const double h = a * w.w;
-    const double l = __builtin_fma(a, w.w, -h);
+    static_assert(odd_part(Pr::p - 1) < (1u << 15), "q (p - 1) must be exact");
+    constexpr double PM1 = (double)(Pr::p - 1);
     const double q = __builtin_fma(a, w.q, SHIFT) - SHIFT;
-    return __builtin_fma(-q, P, h) + l;
+    return __builtin_fma(a, w.w, -(q * PM1)) - q;
 }
 // a * b mod p for |a|, |b| <= p, |result| <= p
 template <class Pr>
