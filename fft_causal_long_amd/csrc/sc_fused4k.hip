@@ -224,15 +224,18 @@ __global__ __launch_bounds__(512) void fused4k_kernel(const typename IO::T* __re
     auto put = [&](int t, float a) { IO::store(rs, REV ? L - 1 - t : t, a); };
     uint2 touched = make_uint2(0u, 0u);
     static_assert(M * sizeof(typename IO::T) <= 128 * TB, "unit 1 covers a channel's lines");
+    // The inverse alternates between the two regions, unit 1's being free now (its forward
+    // data and the exchange are read): pass 1 writes region 1 while Y in region 0 may still
+    // be read, pass 2 reads region 1 and writes region 0, so neither needs a barrier between
+    // its reads and its writes.
+    constexpr int R1B = REGION * 8;   // region 1, in bytes from region 0
     if (unit == 0) {
 #pragma unroll
         for (int n2 = 0; n2 < 16; ++n2) x[n2] = ybuf[ypos(tau + TB * n2)];
-    }
-    __syncthreads();
-    if (unit == 0) {
         dft<16, true>(x);
 #pragma unroll
-        for (int k2 = 0; k2 < 16; ++k2) run_at(k2) = x[k2];
+        for (int k2 = 0; k2 < 16; ++k2)
+            at_byte(lds, ((wbb ^ (64 * (k2 & 1))) + 2176 * k2) + R1B) = x[k2];
     } else {
         direct_head<TB>(hbuf, 1, 1, L, head, tau, [&](int, int t, float a) { put(t, a); });
         // the inputs of the channel pf ahead, which will run in this workgroup's place (same
@@ -244,10 +247,8 @@ __global__ __launch_bounds__(512) void fused4k_kernel(const typename IO::T* __re
     const int j = tau >> 4;
     if (unit == 0) {
 #pragma unroll
-        for (int n2 = 0; n2 < 16; ++n2) x[n2] = p2_at(n2);
-    }
-    __syncthreads();
-    if (unit == 0) {
+        for (int n2 = 0; n2 < 16; ++n2)
+            x[n2] = at_byte(lds, ((r2b ^ (8 * (n2 >> 1))) + 128 * n2) + R1B);
         TC tw[10];
         load_tw(trs, DIT4K_P2 + (2 * 16 + j) * 10, tw);
         dit16<true>(x, tw);

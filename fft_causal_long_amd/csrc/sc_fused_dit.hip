@@ -238,13 +238,13 @@ __global__ __launch_bounds__(M / 8) void fused_dit_kernel(const typename IO::T* 
     auto put = [&](int t, float a) { IO::store(rs, REV ? L - 1 - t : t, a); };
     uint2 touched = make_uint2(0u, 0u);
     static_assert(M * sizeof(typename IO::T) <= 128 * TB, "unit 1 covers a channel's lines");
+    // The inverse alternates between the two regions, unit 1's being free now: pass 1 writes
+    // region 1 while Y in region 0 may still be read, pass 2 reads region 1 and writes region
+    // 0, so neither needs a barrier between its reads and its writes.
     if (unit == 0) {
 #pragma unroll
         for (int q = 0; q < 16; ++q) x[q] = ybuf[fdit::ypos<M>(tau + TB * q)];
-    }
-    __syncthreads();
-    if (unit == 0) {
-        pass1(lds, false, std::true_type{});
+        pass1(lds + S::REGION, false, std::true_type{});
     } else {
         direct_head<TB>(hbuf, 1, 1, L, head, tau, [&](int, int t, float a) { put(t, a); });
         // the inputs of the channel pf ahead, which will run in this workgroup's place (same
@@ -253,9 +253,10 @@ __global__ __launch_bounds__(M / 8) void fused_dit_kernel(const typename IO::T* 
             touched = touch_line(v, g, (ch + pf) * L, (int64_t)L, tau);
     }
     __syncthreads();
-    if (unit == 0) pass2_read(lds);
-    __syncthreads();
-    if (unit == 0) pass2_write(lds, 2, std::true_type{});
+    if (unit == 0) {
+        pass2_read(lds + S::REGION);
+        pass2_write(lds, 2, std::true_type{});
+    }
     __syncthreads();
     if (unit == 0) {
         TC tw[10];
