@@ -222,3 +222,58 @@ def test_many_channels_same_bits(sc, L, cid):
     chans = np.array([0, 511, 512, 513, 1023, 1024, C - 1])
     r_ref, S = oracle.causal_conv_f64(v[0, chans], g[0, chans])
     assert_within_bound(to_host(r)[0, chans], r_ref, S, v.dtype == np.uint16, "many channels")
+
+
+def _bf16_rne(x32: np.ndarray) -> np.ndarray:
+    """float32 -> bfloat16 bits, nearest with ties to even (finite values)."""
+    b = x32.astype(np.float32).view(np.uint32).astype(np.uint64)
+    return ((b + 0x7FFF + ((b >> 16) & 1)) >> 16).astype(np.uint16)
+
+
+def _near_ties_only(bf: np.ndarray, x32: np.ndarray, S: np.ndarray, what: str) -> float:
+    """bf (bf16 bits) must be the rounding of x32, or the rounding of another value within
+    1e-5 * S_t of x32: then either x32 lies within that distance of the tie between the two
+    roundings, or (outputs near zero, where a sign may flip) both lie within it of x32.
+    Returns the fraction of outputs that differ from the rounding of x32."""
+    rn = _bf16_rne(x32)
+    diff = bf != rn
+    if diff.any():
+        a, b = decode(bf[diff]), decode(rn[diff])
+        x, tol = x32[diff].astype(np.float64), 1e-5 * S[diff]
+        tie = np.abs(x - 0.5 * (a + b)) <= tol
+        near = np.maximum(np.abs(a - x), np.abs(b - x)) <= tol
+        ok = tie | near
+        if not ok.all():
+            i = int(np.argmin(ok))
+            raise AssertionError("%s: %d outputs are no rounding of a value within 1e-5 S_t "
+                                 "(bf16 %r, fp32 call %r, S %r)" % (
+                                     what, int((~ok).sum()), float(a[i]), float(x[i]),
+                                     float(S[diff][i])))
+    return float(diff.mean())
+
+
+@pytest.mark.parametrize("L", [4096, 3001, 2049])
+def test_bf16_storage_matches_fp32_arithmetic(sc, L):
+    # the bf16 call computes in fp32 and rounds once at the store: each of its outputs (and
+    # gradients) is the bf16 rounding of the fp32-storage call's value on the same inputs, or
+    # of a value within 1e-5 S_t of it (10x inside the fp32 bound), which a change to the
+    # bf16 path's arithmetic alone may not exceed
+    v, g = make_inputs(WORKLOADS[3], B=2, C=24, L=L, seed_offset=101 + L)
+    print("case bf16 vs fp32 arithmetic L=%d" % L, flush=True)
+    tv, tg = to_device(v), to_device(g)
+    r_bf = to_host(sc.causal_conv(tv, tg))
+    r_32 = to_host(sc.causal_conv(tv.float(), tg.float()))
+    _, S = oracle.causal_conv_f64(v, g)
+    frac = _near_ties_only(r_bf, r_32, S, "forward L=%d" % L)
+    dr, _ = make_inputs(WORKLOADS[3], B=2, C=24, L=L, seed_offset=202 + L)
+    td = to_device(dr)
+    dv_bf, dg_bf = (to_host(x) for x in sc.causal_conv_bwd(td, tv, tg))
+    dv_32, dg_32 = (to_host(x) for x in sc.causal_conv_bwd(td.float(), tv.float(), tg.float()))
+    # bound scales of the gradients: the correlation sums of |dr| with |g| and with |v|
+    rev = lambda a: np.ascontiguousarray(a[..., ::-1])
+    _, Sv = oracle.causal_conv_f64(rev(dr), g)
+    _, Sg = oracle.causal_conv_f64(rev(dr), v)
+    fv = _near_ties_only(dv_bf, dv_32, rev(Sv), "dv L=%d" % L)
+    fg = _near_ties_only(dg_bf, dg_32, rev(Sg), "dg L=%d" % L)
+    print("bf16 vs fp32 L=%d: neighbour taken at %.2e %.2e %.2e of outputs" % (L, frac, fv, fg),
+          flush=True)
