@@ -587,6 +587,22 @@ void fourstep_plan(sc_kind kind, int64_t nch, int64_t L, int64_t* chunk, size_t*
     *bytes = (size_t)(c * per);
 }
 
+// Whether a four-step call runs its parts on two streams (then made here, once per device):
+// not when there is a single part, when the caller's stream is being captured into a graph,
+// or when the call may not create the second stream (allocation-free entry point).
+sc_status use_second_stream(DeviceState& d, hipStream_t stream, bool noalloc, int64_t nch,
+                            int64_t chunk, bool* two)
+{
+    *two = false;
+    if (noalloc || chunk < 2 || nch <= chunk / 2) return SC_OK;
+    hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(stream, &cap) != hipSuccess) return SC_ERR_HIP;
+    if (cap != hipStreamCaptureStatusNone) return SC_OK;
+    const sc_status st = fourstep_streams(d);
+    if (st == SC_OK) *two = true;
+    return st;
+}
+
 // One convolution of a call: o = causal(a, b) per channel, or with rev the gradient form
 // o = rev(causal(rev(a), b)).
 struct Job {
@@ -659,19 +675,27 @@ sc_status run_jobs(sc_kind kind, const Job* jobs, int njobs, bool rev, int64_t n
                 st = ntt4_table(*d, M, i, &wtab[i], stream, !noalloc);
         }
         if (st != SC_OK) return st;
+        // two streams take alternate halves of the chunks, as on the float path (one part's
+        // column kernels overlap the other's row kernel), under the same conditions
+        bool two = false;
+        if ((st = use_second_stream(*d, stream, noalloc, nch, chunk, &two)) != SC_OK) return st;
+        std::unique_lock<std::mutex> order(d->fs_mu, std::defer_lock);
+        if (two) order.lock();
         void* scratch = ws;
         bool own = false;
         if (!ws) {
             if (hipMallocAsync(&scratch, need, stream) != hipSuccess) return SC_ERR_HIP;
             own = true;
         }
+        hipStream_t side = two ? d->fs_side : nullptr;
+        hipEvent_t fork = two ? d->fs_fork : nullptr, join = two ? d->fs_join : nullptr;
         for (int k = 0; k < njobs && e == hipSuccess; ++k)
             e = fix ? sc::launch_fixed4((const float*)jobs[k].a, (const float*)jobs[k].b,
                                         (float*)jobs[k].o, nch, (int)L, M, fv, fg, d->ntt, wtab,
-                                        scratch, need, chunk, stream)
+                                        scratch, need, chunk, stream, side, fork, join)
                     : sc::launch_ntt4((const int32_t*)jobs[k].a, (const int32_t*)jobs[k].b,
                                       (int32_t*)jobs[k].o, nch, (int)L, M, rev, d->ntt[0],
-                                      wtab[0], scratch, need, chunk, stream);
+                                      wtab[0], scratch, need, chunk, stream, side, fork, join);
         if (own && hipFreeAsync(scratch, stream) != hipSuccess && e == hipSuccess)
             e = hipErrorUnknown;
         return e == hipSuccess ? SC_OK : SC_ERR_HIP;
@@ -733,14 +757,9 @@ sc_status run_jobs(sc_kind kind, const Job* jobs, int njobs, bool rev, int64_t n
         }
         if (st != SC_OK) return st;
         // two streams take alternate halves of the chunks (measured 1.54 -> 1.34 ms on the
-        // long workload: one part's memory-bound column kernels overlap the other's rows),
-        // unless there is a single part, the caller's stream is being captured into a graph,
-        // or the call may not create the second stream (allocation-free entry point)
-        hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
-        if (hipStreamIsCapturing(stream, &cap) != hipSuccess) return SC_ERR_HIP;
-        const bool two = !noalloc && cap == hipStreamCaptureStatusNone && chunk >= 2 &&
-                         nch > chunk / 2;
-        if (two && (st = fourstep_streams(*d)) != SC_OK) return st;
+        // long workload: one part's memory-bound column kernels overlap the other's rows)
+        bool two = false;
+        if ((st = use_second_stream(*d, stream, noalloc, nch, chunk, &two)) != SC_OK) return st;
         std::unique_lock<std::mutex> order(d->fs_mu, std::defer_lock);
         if (two) order.lock();
         void* scratch = ws;
@@ -1540,6 +1559,6 @@ sc_status sc_prepare(sc_kind kind, int64_t L)
     });
 }
 
-int sc_version(void) { return 900; }
+int sc_version(void) { return 901; }
 
 }  // extern "C"

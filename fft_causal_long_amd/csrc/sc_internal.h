@@ -138,19 +138,25 @@ hipError_t launch_ntt_mfma(const int32_t* v, const int32_t* g, int32_t* r, int64
 // (sc_ntt.hip): M = next power of two >= L, chunks of `chunk` channels, each needing
 // ntt4_bytes_per_channel(M) bytes of ws (ws_bytes >= chunk * that); wtab = the per-M tables
 // of prime A (5M doubles: w_N^j for j < 2M, then the column and the row twiddles).  Modulo
-// prime A, output lifted to the balanced range; rev as for launch_ntt.
+// prime A, output lifted to the balanced range; rev as for launch_ntt.  Streams as for
+// launch_fourstep: side null, the parts of `chunk` channels run one after the other on
+// `stream` at the start of ws; with side (and fork, join), parts of chunk/2 channels
+// alternate between the two streams, each with its own half of ws.
 constexpr int NTT4_MAX_L = 65536;
 size_t ntt4_bytes_per_channel(int M);
 hipError_t launch_ntt4(const int32_t* v, const int32_t* g, int32_t* r, int64_t nch, int L, int M,
                        bool rev, const NttTables& tables, const double* wtab, void* ws,
-                       size_t ws_bytes, int64_t chunk, hipStream_t stream);
+                       size_t ws_bytes, int64_t chunk, hipStream_t stream, hipStream_t side,
+                       hipEvent_t fork, hipEvent_t join);
 // The exact real-valued convolution (as launch_fixed) for FUSED_MAX_L < L <= NTT4_MAX_L
 // through the same split, once per prime: tables[3] and wtab[3] (the per-M tables of primes
-// A, B, C), fixed4_bytes_per_channel(M) bytes of ws per channel of a chunk.
+// A, B, C), fixed4_bytes_per_channel(M) bytes of ws per channel of a chunk; streams as for
+// launch_ntt4.
 size_t fixed4_bytes_per_channel(int M);
 hipError_t launch_fixed4(const float* v, const float* g, float* r, int64_t nch, int L, int M,
                          int fv, int fg, const NttTables* tables, const double* const* wtab,
-                         void* ws, size_t ws_bytes, int64_t chunk, hipStream_t stream);
+                         void* ws, size_t ws_bytes, int64_t chunk, hipStream_t stream,
+                         hipStream_t side, hipEvent_t fork, hipEvent_t join);
 
 // Exact real-valued causal convolution: V = round(v 2^fv), G = round(g 2^fg), the exact
 // integer sum R from its residues modulo primes A, B, C (tables[0..2]), all in one kernel,

@@ -963,19 +963,57 @@ __global__ __launch_bounds__(256) void ntt4_columns_inv_fixed(const int32_t* __r
 size_t ntt4_bytes_per_channel(int M) { return (size_t)M * 24; }
 size_t fixed4_bytes_per_channel(int M) { return (size_t)M * 40; }
 
+// The channels of a four-step call in parts: part(c0, nc, scratch, s) enqueues the kernels of
+// channels c0 .. c0 + nc - 1 on stream s with its scratch.  Without a second stream (side
+// null) the parts are `chunk` channels, one after the other on `stream`, each reusing the
+// start of ws.  With one, the parts are chunk/2 channels and alternate between `stream` (even
+// parts) and `side` (odd parts), each stream with its own half of ws, so that one part's
+// column kernels overlap the other's row kernel; `side` waits for `stream` at the start
+// (fork) and `stream` for `side` at the end (join), so the call is ordered on `stream` as a
+// whole.  A part whose scratch would end past ws_bytes is refused before its launch.
+template <class Part>
+static hipError_t run_parts(int64_t nch, int64_t chunk, size_t per_channel, void* ws,
+                            size_t ws_bytes, hipStream_t stream, hipStream_t side,
+                            hipEvent_t fork, hipEvent_t join, Part&& part)
+{
+    if (chunk <= 0 || (size_t)chunk * per_channel > ws_bytes) return hipErrorInvalidValue;
+    const int64_t pc = side ? (chunk / 2 > 0 ? chunk / 2 : 1) : chunk;
+    hipError_t e = hipSuccess;
+    if (side) {
+        e = hipEventRecord(fork, stream);
+        if (e == hipSuccess) e = hipStreamWaitEvent(side, fork, 0);
+        if (e != hipSuccess) return e;
+    }
+    int64_t i = 0;
+    for (int64_t c0 = 0; c0 < nch && e == hipSuccess; c0 += pc, ++i) {
+        const int64_t nc = nch - c0 < pc ? nch - c0 : pc;
+        const int half = side ? (int)(i & 1) : 0;
+        const size_t off = (size_t)half * (size_t)pc * per_channel;
+        if (off + (size_t)nc * per_channel > ws_bytes) {
+            e = hipErrorInvalidValue;
+            break;
+        }
+        e = part(c0, nc, (int32_t*)((char*)ws + off), half ? side : stream);
+    }
+    if (side) {
+        // join even after a failed launch, so that nothing of this call is left unordered
+        hipError_t ej = hipEventRecord(join, side);
+        if (ej == hipSuccess) ej = hipStreamWaitEvent(stream, join, 0);
+        if (e == hipSuccess) e = ej;
+    }
+    return e;
+}
+
 template <int M1, bool REV>
 static hipError_t launch_ntt4_m(const int32_t* v, const int32_t* g, int32_t* r, int64_t nch,
-                                int L, const NttTables& tb, const double* wtab, int32_t* ws,
-                                size_t ws_bytes, int64_t chunk, hipStream_t s)
+                                int L, const NttTables& tb, const double* wtab, void* ws,
+                                size_t ws_bytes, int64_t chunk, hipStream_t stream,
+                                hipStream_t side, hipEvent_t fork, hipEvent_t join)
 {
     constexpr int M = M1 * ntt4::M2, BPC = ntt4::M2 / ntt4::CT;
     const int lg = __builtin_ctz((unsigned)(2 * M));
-    if (chunk <= 0 || (size_t)chunk * ntt4_bytes_per_channel(M) > ws_bytes)
-        return hipErrorInvalidValue;
-    for (int64_t c0 = 0; c0 < nch; c0 += chunk) {
-        const int64_t nc = nch - c0 < chunk ? nch - c0 : chunk;
-        int32_t* T = ws;
-        int32_t* S = ws + nc * 4 * (int64_t)M;
+    auto part = [&](int64_t c0, int64_t nc, int32_t* T, hipStream_t s) -> hipError_t {
+        int32_t* S = T + nc * 4 * (int64_t)M;
         if (!grid_ok(nc * BPC, ntt4::CT) || !grid_ok(nc * 2 * M1, 256))
             return hipErrorInvalidValue;
         hipLaunchKernelGGL((ntt4_columns_fwd<M1, REV, ntt::PrimeA, false>),
@@ -985,28 +1023,25 @@ static hipError_t launch_ntt4_m(const int32_t* v, const int32_t* g, int32_t* r, 
                            T, S, M1, tb.bank, wtab + 4 * M, tb.ninv[lg], tb.ninv_q[lg]);
         hipLaunchKernelGGL((ntt4_columns_inv<M1, REV>), dim3((unsigned)(nc * BPC)), dim3(ntt4::CT),
                            0, s, S, r, c0, L, wtab);
-        const hipError_t e = hipGetLastError();
-        if (e != hipSuccess) return e;
-    }
-    return hipSuccess;
+        return hipGetLastError();
+    };
+    return run_parts(nch, chunk, ntt4_bytes_per_channel(M), ws, ws_bytes, stream, side, fork,
+                     join, part);
 }
 
-// per chunk: for each prime, kernels A and B (T reused, S per prime), then the fixed kernel C
+// per part: for each prime, kernels A and B (T reused, S per prime), then the fixed kernel C
 template <int M1>
 static hipError_t launch_fixed4_m(const float* v, const float* g, float* r, int64_t nch, int L,
                                   const NttTables* tb, const double* const* wtab, double sv,
-                                  double sg, int F, int32_t* ws, size_t ws_bytes, int64_t chunk,
-                                  hipStream_t s)
+                                  double sg, int F, void* ws, size_t ws_bytes, int64_t chunk,
+                                  hipStream_t stream, hipStream_t side, hipEvent_t fork,
+                                  hipEvent_t join)
 {
     constexpr int M = M1 * ntt4::M2, BPC = ntt4::M2 / ntt4::CT;
     const int lg = __builtin_ctz((unsigned)(2 * M));
-    if (chunk <= 0 || (size_t)chunk * fixed4_bytes_per_channel(M) > ws_bytes)
-        return hipErrorInvalidValue;
-    for (int64_t c0 = 0; c0 < nch; c0 += chunk) {
-        const int64_t nc = nch - c0 < chunk ? nch - c0 : chunk;
+    auto part = [&](int64_t c0, int64_t nc, int32_t* T, hipStream_t s) -> hipError_t {
         const int64_t sp = nc * 2 * (int64_t)M;   // one prime's S
-        int32_t* T = ws;
-        int32_t* S = ws + nc * 4 * (int64_t)M;
+        int32_t* S = T + nc * 4 * (int64_t)M;
         if (!grid_ok(nc * BPC, ntt4::CT) || !grid_ok(nc * 2 * M1, 256))
             return hipErrorInvalidValue;
 #define SC_PRIME(i, Pr)                                                                        \
@@ -1022,10 +1057,10 @@ static hipError_t launch_fixed4_m(const float* v, const float* g, float* r, int6
 #undef SC_PRIME
         hipLaunchKernelGGL((ntt4_columns_inv_fixed<M1>), dim3((unsigned)(nc * BPC)),
                            dim3(ntt4::CT), 0, s, S, r, c0, L, sp, wtab[0], wtab[1], wtab[2], F);
-        const hipError_t e = hipGetLastError();
-        if (e != hipSuccess) return e;
-    }
-    return hipSuccess;
+        return hipGetLastError();
+    };
+    return run_parts(nch, chunk, fixed4_bytes_per_channel(M), ws, ws_bytes, stream, side, fork,
+                     join, part);
 }
 
 #define SC_NTT4_SWITCH(F)                                                                     \
@@ -1039,23 +1074,26 @@ static hipError_t launch_fixed4_m(const float* v, const float* g, float* r, int6
 
 hipError_t launch_ntt4(const int32_t* v, const int32_t* g, int32_t* r, int64_t nch, int L, int M,
                        bool rev, const NttTables& tb, const double* wtab, void* ws,
-                       size_t ws_bytes, int64_t chunk, hipStream_t s)
+                       size_t ws_bytes, int64_t chunk, hipStream_t s, hipStream_t side,
+                       hipEvent_t fork, hipEvent_t join)
 {
-    int32_t* w = (int32_t*)ws;
-#define SC_CALL(m1) rev ? launch_ntt4_m<m1, true>(v, g, r, nch, L, tb, wtab, w, ws_bytes, chunk, s) \
-                        : launch_ntt4_m<m1, false>(v, g, r, nch, L, tb, wtab, w, ws_bytes, chunk, s)
+#define SC_CALL(m1)                                                                            \
+    rev ? launch_ntt4_m<m1, true>(v, g, r, nch, L, tb, wtab, ws, ws_bytes, chunk, s, side, fork, \
+                                  join)                                                        \
+        : launch_ntt4_m<m1, false>(v, g, r, nch, L, tb, wtab, ws, ws_bytes, chunk, s, side,     \
+                                   fork, join)
     SC_NTT4_SWITCH(SC_CALL)
 #undef SC_CALL
 }
 
 hipError_t launch_fixed4(const float* v, const float* g, float* r, int64_t nch, int L, int M,
                          int fv, int fg, const NttTables* tb, const double* const* wtab,
-                         void* ws, size_t ws_bytes, int64_t chunk, hipStream_t s)
+                         void* ws, size_t ws_bytes, int64_t chunk, hipStream_t s,
+                         hipStream_t side, hipEvent_t fork, hipEvent_t join)
 {
     const double sv = ldexp(1.0, fv), sg = ldexp(1.0, fg);
-    int32_t* w = (int32_t*)ws;
-#define SC_CALL(m1) launch_fixed4_m<m1>(v, g, r, nch, L, tb, wtab, sv, sg, fv + fg, w, ws_bytes, \
-                                        chunk, s)
+#define SC_CALL(m1) launch_fixed4_m<m1>(v, g, r, nch, L, tb, wtab, sv, sg, fv + fg, ws, ws_bytes, \
+                                        chunk, s, side, fork, join)
     SC_NTT4_SWITCH(SC_CALL)
 #undef SC_CALL
 }

@@ -47,7 +47,7 @@
  *    four-step call of a kind at each transform length M = next power of two >= L).  A call whose
  *    `stream` is being captured into a graph and that would have to build a table returns
  *    SC_ERR_UNSUPPORTED and enqueues nothing; sc_prepare builds them beforehand.  Also,
- *    for the float four-step path (L > 4096), a second stream and two events per
+ *    for the four-step paths (L > 4096, every kind), a second stream and two events per
  *    device, made on first use: such a call may run half of its channel chunks on that
  *    stream, which waits for `stream` at the start of the call, and `stream` waits for it
  *    at the end, so the call stays ordered on `stream` as a whole.  While `stream` is being
@@ -447,7 +447,7 @@ sc_status sc_causal_conv_noalloc(sc_kind kind, const void* v, const void* g, voi
  */
 sc_status sc_prepare(sc_kind kind, int64_t L);
 
-/* Library version: major * 10000 + minor * 100 + patch (this header: 900).  Host only. */
+/* Library version: major * 10000 + minor * 100 + patch (this header: 901).  Host only. */
 int sc_version(void);
 
 #ifdef __cplusplus
