@@ -134,6 +134,22 @@ def test_long_context_shape_sampled(sc):
     assert_bits(r[ch, t], want, "long shape sampled")
 
 
+def test_parts_agree_across_partitions(sc):
+    # The long-context shape in one call (chunks run as halves on two streams) and as three
+    # calls on slices of its channels, whose chunks and halves fall elsewhere: every output
+    # must agree bit for bit.
+    w = WORKLOADS[4]
+    v, g = make_inputs(w, seed_offset=47)
+    assert sc.sc_fixed_range_ok(float(np.abs(v).max()), float(np.abs(g).max()), 24, 24, w.L)
+    print("case fixed long shape partitions: %s" % (v.shape,), flush=True)
+    tv, tg = to_device(v), to_device(g)
+    whole = sc.causal_conv_fixed(tv, tg, 24, 24)
+    for c0, c1 in [(0, 100), (100, 433), (433, w.C)]:
+        part = sc.causal_conv_fixed(tv[:, c0:c1].contiguous(), tg[:, c0:c1].contiguous(), 24, 24)
+        torch.cuda.synchronize()
+        assert torch.equal(part.view(torch.int32), whole[:, c0:c1].view(torch.int32)), (c0, c1)
+
+
 def test_graph_capture_after_prepare(sc):
     L = 12288
     v, g = make_inputs(W2, B=1, C=3, L=L, seed_offset=41)

@@ -118,6 +118,25 @@ def test_long_context_shape_sampled(sc):
     assert np.array_equal(got, oracle.lift_mod_p(np.rint(want).astype(np.int64)))
 
 
+def test_two_stream_parts_equal_one_stream(sc):
+    # At the long-context shape a call runs each chunk as two halves that alternate between
+    # the caller's stream and a second stream, each half with its own part of the scratch.
+    # The allocation-free call runs the same kernels on one stream, in chunks sized to its
+    # static scratch, so every channel falls into a different part: all outputs must agree.
+    w = WORKLOADS[4]
+    v, g = make_inputs(W5, B=w.B, C=w.C, L=w.L, seed_offset=53)
+    print("case ntt4 two streams vs one: %s" % (v.shape,), flush=True)
+    tv, tg = to_device(v), to_device(g)
+    two = sc.causal_conv(tv, tg)
+    assert sc.sc_prepare(sc.KIND_NTT_I32, w.L) == sc.SC_OK
+    one = torch.empty_like(tv)
+    st = sc.sc_causal_conv_noalloc(sc.KIND_NTT_I32, tv.data_ptr(), tg.data_ptr(), one.data_ptr(),
+                                   w.B, w.C, w.L, torch.cuda.current_stream().cuda_stream)
+    assert st == sc.SC_OK, sc.sc_status_string(st)
+    torch.cuda.synchronize()
+    assert torch.equal(one, two)
+
+
 def test_workspace_variant_and_token_major(sc):
     L = 8192
     v, g = make_inputs(W5, B=2, C=3, L=L, seed_offset=61)
