@@ -173,15 +173,18 @@ def four_step_calls(w, markers: int, where: str) -> float:
     """Calls of the four-step path in a counter run, from its count of marker dispatches:
     the call is several kernels (columns, rows, columns per part of the channels, then for
     the float kinds the head); one head kernel per float call, and the exact kind's
-    inverse-column kernel once per chunk of channels."""
+    inverse-column kernel once per part of channels (half a chunk when the call runs its
+    chunks as halves on two streams: at least two channels per chunk and more than half a
+    chunk of channels)."""
     if not markers:
         raise RuntimeError("%s: no dispatch to count four-step calls" % where)
     if w.storage != "i32":
         return float(markers)
     import fft_causal_long_amd as sc
     M = 1 << (w.L - 1).bit_length()
-    per_chunk = sc.sc_workspace_bytes(sc.KIND_NTT_I32, w.B, w.C, w.L) // (24 * M)
-    return markers / -(-w.channels // per_chunk)
+    chunk = sc.sc_workspace_bytes(sc.KIND_NTT_I32, w.B, w.C, w.L) // (24 * M)
+    part = chunk // 2 if chunk >= 2 and w.channels > chunk // 2 else chunk
+    return markers / -(-w.channels // part)
 
 
 def four_step_marker(w) -> str:
