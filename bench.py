@@ -163,7 +163,8 @@ def kernel_matches(name: str, storage: str, L: int, rev: bool = False) -> bool:
                                       and (", %s>" % flag) in name)
     io = "bf16_io" if storage == "bf16" else "f32_io"
     if M == 4096:
-        return ("fused4k_kernel<sc::%s, %s>" % (io, flag)) in name
+        # the default form (the last template argument selects the matrix-core first pass)
+        return ("fused4k_kernel<sc::%s, %s, false>" % (io, flag)) in name
     if M in (1024, 2048):
         return ("fused_dit_kernel<%d, sc::%s, %s>" % (M, io, flag)) in name
     return ("fused_conv_kernel<%d, sc::%s, %s>" % (M, io, flag)) in name
@@ -320,6 +321,37 @@ def leakage_probe(sc, torch, dev, channels: int = 16) -> dict:
     n_leak, _ = probe(vi, gi, posi, swap)
     return {"fp32_max_abs": f_leak, "fp32_rel_to_rms": f_leak / f_rms, "ntt_max_abs": n_leak,
             "fixed_max_abs": x_leak, "positions": len(pos), "channels": channels, "L": w3.L}
+
+
+def fused_mfma_measure(sc, torch, stream, step, bufs, w, steps: int) -> dict:
+    """The same call with SC_PATH_FUSED_MFMA (the first pass of both branch transforms as bf16
+    matrix products), timed in three rounds alternating with rounds of the default call on
+    the same buffers, so that both see the same clock."""
+    import ctypes
+    fn = sc.lib().sc_causal_conv_ex
+    opt = sc.sc_options(sc.PATH_FUSED_MFMA, -1)
+    sptr = stream.cuda_stream
+    nsets = len(bufs)
+
+    def call(i):
+        a, b, c = bufs[i % nsets]
+        st = fn(sc.KIND_BF16, a.data_ptr(), b.data_ptr(), c.data_ptr(), w.B, w.C, w.L,
+                ctypes.byref(opt), None, 0, sptr)
+        if st != 0:
+            raise RuntimeError("sc_causal_conv_ex (fused mfma) failed: %s" % sc.sc_status_string(st))
+
+    prewarm(torch, call)
+    mf, base = [], []
+    for _ in range(3):
+        mf.append(time_rounds(torch, stream, call, steps, rounds=1, warm=False)[0])
+        base.append(time_rounds(torch, stream, step, steps, rounds=1, warm=False)[0])
+    return {"entry": "sc_causal_conv_ex, path SC_PATH_FUSED_MFMA",
+            "what": "first radix-16 pass of both branch transforms as bf16 matrix products "
+                    "(v_mfma_f32_32x32x16_bf16, three-part bf16 DFT matrix); not the default",
+            "ms_per_call": round(min(mf), 5), "fused_ms": round(min(base), 5),
+            "ratio_to_fused": round(min(mf) / min(base), 4),
+            "rounds_ms": {"mfma": [round(x, 5) for x in mf], "fused": [round(x, 5) for x in base]},
+            "method": "best of three rounds of K calls each, alternating with the default call"}
 
 
 def pages_approach(torch, w, dev, steps: int, kernel_ms: float) -> dict:
@@ -944,6 +976,10 @@ def main(argv=None):
     # per-launch statistics over 50 more launches (outside the K timed steps)
     stats = None if args.no_stats else launch_stats(torch, stream, step, 50, args.steps)
 
+    mfma = None
+    if not args.no_others and w.storage == "bf16" and 2048 < w.L <= 4096:
+        mfma = fused_mfma_measure(sc, torch, stream, step, bufs, w, args.steps)
+
     if args.calib_copy:
         # 1 GiB device-to-device copy: a known-size reference for the profiler's byte counters
         src = torch.empty(1 << 28, dtype=torch.float32, device=dev)
@@ -998,6 +1034,8 @@ def main(argv=None):
         "launch_ms": stats,
         "prewarm": warm,
     }
+    if mfma is not None:
+        rec["fused_mfma"] = mfma
     if not args.no_bwd:
         del bufs
         rec["bwd"] = bwd_measure(sc, torch, w, dev, max(5, args.steps // 2), args.warmup)

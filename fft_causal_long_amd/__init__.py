@@ -47,14 +47,14 @@ __all__ = [
     "sc_causal_conv_blc_ex", "gate", "gate_conv", "gate_conv_blc", "sc_gate_f32", "sc_gate_bf16",
     "sc_gate_conv_workspace_bytes", "sc_gate_conv_blc_workspace_bytes", "sc_gate_conv_ex",
     "sc_gate_conv_blc_ex", "sc_gate_conv_blc_f32", "sc_gate_conv_blc_bf16", "KIND_F32", "KIND_BF16", "KIND_NTT_I32", "KIND_FIXED_F32", "PATH_AUTO", "PATH_FUSED", "PATH_FOUR_STEP",
-    "PATH_DIRECT", "PATH_NTT_MFMA", "LIB_PATH",
+    "PATH_DIRECT", "PATH_NTT_MFMA", "PATH_FUSED_MFMA", "LIB_PATH",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libspecconv.so")
 
 SC_OK, SC_ERR_INVALID_ARGUMENT, SC_ERR_UNSUPPORTED, SC_ERR_HIP, SC_ERR_WORKSPACE = range(5)
 KIND_F32, KIND_BF16, KIND_NTT_I32, KIND_FIXED_F32 = 0, 1, 2, 3
-PATH_AUTO, PATH_FUSED, PATH_FOUR_STEP, PATH_DIRECT, PATH_NTT_MFMA = 0, 1, 2, 3, 4
+PATH_AUTO, PATH_FUSED, PATH_FOUR_STEP, PATH_DIRECT, PATH_NTT_MFMA, PATH_FUSED_MFMA = 0, 1, 2, 3, 4, 5
 
 
 class SpecConvError(RuntimeError):

@@ -56,11 +56,15 @@ __device__ __forceinline__ float2& at_byte(float2* base, int byte)
 }
 __device__ __forceinline__ int ypos(int k) { return (k >> 1) + (k & 1) * (M / 2 + 16); }
 
+// operand types of the matrix-core first pass
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+
 using namespace dit;
 
 }  // namespace f4k
 
-template <class IO, bool REV>
+template <class IO, bool REV, bool MF>
 __global__ __launch_bounds__(512) void fused4k_kernel(const typename IO::T* __restrict__ v,
                                                       const typename IO::T* __restrict__ g,
                                                       typename IO::T* __restrict__ r, int L,
@@ -79,31 +83,6 @@ __global__ __launch_bounds__(512) void fused4k_kernel(const typename IO::T* __re
     const Span vs = make_span(v, ch * L, L);
     const Span gs = make_span(g, ch * L, L);
 
-    // 1. z_n = v_n + i g_n, n = tau + 256 q (0 past L): pass 1's inputs as loaded.  For
-    //    L = M the per-element offsets are scalar constants (no vector address arithmetic);
-    //    reversed v runs from element L - 1 - tau - 3840 upwards.
-    float2 x[16];
-    if (L == M) {
-        const int vb = REV ? L - 1 - tau - TB * 15 : tau;
-#pragma unroll
-        for (int q = 0; q < 16; ++q)
-            x[q] = make_float2(IO::load_at(vs, vb, TB * (REV ? 15 - q : q)),
-                               IO::load_at(gs, tau, TB * q));
-    } else {
-#pragma unroll
-        for (int q = 0; q < 16; ++q) {
-            const int n = tau + TB * q;
-            const bool in = n < L;
-            const int e = in ? n : IO::OOB;
-            const int ev = in ? (REV ? L - 1 - n : n) : IO::OOB;
-            x[q] = make_float2(IO::load(vs, ev), IO::load(gs, e));
-        }
-    }
-    if (unit == 0 && tau < head) {
-        hbuf[tau] = x[0].x;
-        hbuf[HEAD_MAX + tau] = x[0].y;
-    }
-
     // LDS positions fpos(a) of the access patterns, as per-thread bases plus constants:
     //  runs tau + 256 k2:        wb ^ (8 (k2 & 1)) + 272 k2
     //  pass 2 reads 256 j + k + 16 n2 (j = tau / 16, k = tau % 16):  r2 ^ (n2 / 2) + 16 n2
@@ -119,16 +98,148 @@ __global__ __launch_bounds__(512) void fused4k_kernel(const typename IO::T* __re
     auto p2_at = [&](int n2) -> float2& { return at_byte(lds, (r2b ^ (8 * (n2 >> 1))) + 128 * n2); };
     auto p3_at = [&](int n2) -> float2& { return at_byte(lds, r3b ^ (8 * n2)); };
 
-    // 2. forward transform of branch `unit`
-    if (unit == 0) {
-        dft<16, false>(x);
-    } else {
-        TC tw[10];
-        load_tw(trs, DIT4K_P1B1, tw);
-        dit16<false>(x, tw);
-    }
+    float2 x[16];
+    if constexpr (MF) {
+        // 1-2. Pass 1 of branch `unit` on the matrix cores (bf16 storage).  Per item it is a
+        //    fixed 32 x 32 real matrix (the 16-point DFT; on branch 1 times the rotation
+        //    W_32^q of input q) applied to the item's 16 complex inputs as 32 reals.  The
+        //    inputs are bf16 and the matrix is held as three bf16 parts (24 significant
+        //    bits), so every product is exact and the fp32 sums give the pass to fp32
+        //    round-off.  32 x 32 x 16 bf16 products: a wave's 64 items are two 32-column
+        //    blocks, K = 32 reals in two halves h; lane l holds column l % 32 and, of half
+        //    h, the reals of inputs q = 8 h + 4 (l / 32) + e (e < 4) as (v, g) bit pairs.
+        const int lane = tid & 63, col = lane & 31, half = lane >> 5;
+        const int wbase = tau & ~63;   // the wave's first item
+        uint4 af[3][2];
 #pragma unroll
-    for (int k2 = 0; k2 < 16; ++k2) run_at(k2) = x[k2];
+        for (int t = 0; t < 3; ++t)
+#pragma unroll
+            for (int h = 0; h < 2; ++h)
+                af[t][h] = __builtin_bit_cast(
+                    uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                               trs, (DIT4K_MF + ((unit * 3 + t) * 2 + h) * 128 + 2 * lane) * 8,
+                               0, 0));
+        // the (v, g) bits of each input, all 32 loads issued before any is used; for L = M
+        // every offset is a per-lane base plus a constant (reversed v: from element
+        // L - 1 - n), past L the loads read 0
+        uint32_t rv[2][2][4], rg[2][2][4];
+        if (L == M) {
+#pragma unroll
+            for (int b = 0; b < 2; ++b)
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    const int it = wbase + 32 * b + col, q0 = 8 * h + 4 * half;
+                    const int vb = REV ? L - 1 - it - TB * (q0 + 3) : it + TB * q0;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        rv[b][h][e] = __builtin_amdgcn_raw_buffer_load_b16(
+                            vs.rs, vb * 2, TB * 2 * (REV ? 3 - e : e), 0);
+                        rg[b][h][e] = __builtin_amdgcn_raw_buffer_load_b16(
+                            gs.rs, (it + TB * q0) * 2, TB * 2 * e, 0);
+                    }
+                }
+        } else {
+#pragma unroll
+            for (int b = 0; b < 2; ++b)
+#pragma unroll
+                for (int h = 0; h < 2; ++h)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int n = wbase + 32 * b + col + TB * (8 * h + 4 * half + e);
+                        const bool in = n < L;
+                        const int ev = in ? (REV ? L - 1 - n : n) : IO::OOB;
+                        const int eg = in ? n : IO::OOB;
+                        rv[b][h][e] = __builtin_amdgcn_raw_buffer_load_b16(
+                            vs.rs, (int)((uint32_t)ev * 2u), 0, 0);
+                        rg[b][h][e] = __builtin_amdgcn_raw_buffer_load_b16(
+                            gs.rs, (int)((uint32_t)eg * 2u), 0, 0);
+                    }
+        }
+        uint4 bfr[2][2];
+#pragma unroll
+        for (int b = 0; b < 2; ++b)
+#pragma unroll
+            for (int h = 0; h < 2; ++h)
+                bfr[b][h] = make_uint4(rv[b][h][0] | (rg[b][h][0] << 16),
+                                       rv[b][h][1] | (rg[b][h][1] << 16),
+                                       rv[b][h][2] | (rg[b][h][2] << 16),
+                                       rv[b][h][3] | (rg[b][h][3] << 16));
+        // input q = 0 of items 0..63 (wave 0 of unit 0, lanes l < 32) for the direct head
+        if (unit == 0 && wbase == 0 && half == 0) {
+#pragma unroll
+            for (int b = 0; b < 2; ++b) {
+                const int t = 32 * b + col;
+                if (t < head) {
+                    hbuf[t] = __uint_as_float(bfr[b][0].x << 16);
+                    hbuf[HEAD_MAX + t] = __uint_as_float(bfr[b][0].x & 0xffff0000u);
+                }
+            }
+        }
+        f4k::f32x16 acc[2];
+#pragma unroll
+        for (int b = 0; b < 2; ++b)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[b][r] = 0.f;
+        // the small parts first
+#pragma unroll
+        for (int b = 0; b < 2; ++b)
+#pragma unroll
+            for (int h = 0; h < 2; ++h)
+#pragma unroll
+                for (int t = 2; t >= 0; --t)
+                    acc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                        __builtin_bit_cast(f4k::bf16x8, af[t][h]),
+                        __builtin_bit_cast(f4k::bf16x8, bfr[b][h]), acc[b], 0, 0, 0);
+        // accumulator r of column c is real row i = 8 (r / 4) + 4 (l / 32) + r % 4 = 2 k2 + re/im
+        // of item wbase + 32 b + c: registers 2 s, 2 s + 1 are output k2 = 4 (s / 2) +
+        // 2 (l / 32) + s % 2, written where pass 2 reads the run of that item
+#pragma unroll
+        for (int b = 0; b < 2; ++b) {
+            const int it = wbase + 32 * b + col;
+            const int wbi = (ro + (it & ~15) + ((it & 15) ^ (it >> 5))) << 3;
+#pragma unroll
+            for (int s2 = 0; s2 < 8; ++s2) {
+                const int k2 = 4 * (s2 >> 1) + 2 * half + (s2 & 1);
+                at_byte(lds, (wbi ^ (64 * (k2 & 1))) + 2176 * k2) =
+                    make_float2(acc[b][2 * s2], acc[b][2 * s2 + 1]);
+            }
+        }
+    } else {
+        // 1. z_n = v_n + i g_n, n = tau + 256 q (0 past L): pass 1's inputs as loaded.  For
+        //    L = M the per-element offsets are scalar constants (no vector address arithmetic);
+        //    reversed v runs from element L - 1 - tau - 3840 upwards.
+        if (L == M) {
+            const int vb = REV ? L - 1 - tau - TB * 15 : tau;
+    #pragma unroll
+            for (int q = 0; q < 16; ++q)
+                x[q] = make_float2(IO::load_at(vs, vb, TB * (REV ? 15 - q : q)),
+                                   IO::load_at(gs, tau, TB * q));
+        } else {
+    #pragma unroll
+            for (int q = 0; q < 16; ++q) {
+                const int n = tau + TB * q;
+                const bool in = n < L;
+                const int e = in ? n : IO::OOB;
+                const int ev = in ? (REV ? L - 1 - n : n) : IO::OOB;
+                x[q] = make_float2(IO::load(vs, ev), IO::load(gs, e));
+            }
+        }
+        if (unit == 0 && tau < head) {
+            hbuf[tau] = x[0].x;
+            hbuf[HEAD_MAX + tau] = x[0].y;
+        }
+
+        // 2. forward transform of branch `unit`
+        if (unit == 0) {
+            dft<16, false>(x);
+        } else {
+            TC tw[10];
+            load_tw(trs, DIT4K_P1B1, tw);
+            dit16<false>(x, tw);
+        }
+    #pragma unroll
+        for (int k2 = 0; k2 < 16; ++k2) run_at(k2) = x[k2];
+    }
     __syncthreads();
     {
         const int j = tau >> 4;
@@ -298,10 +409,11 @@ __global__ __launch_bounds__(512) void fused4k_kernel(const typename IO::T* __re
     if (unit == 1) keep_touched(touched, pf, rs);
 }
 
-template <class IO, bool REV>
+template <class IO, bool REV, bool MF = false>
 static hipError_t launch4k(const void* v, const void* g, void* r, int64_t nch, int L, int head,
                            bool pair, const float2* tab, hipStream_t stream)
 {
+    static_assert(!MF || sizeof(typename IO::T) == 2, "the matrix-core first pass takes bf16");
     if (!grid_ok(nch, f4k::FT)) return hipErrorInvalidValue;
     // the next generation's inputs: bf16 only (16 KB per channel).  With fp32 (32 KB) the
     // touched lines of the 64 workgroups ahead on an XCD (2 MB) crowd the 4 MB L2 that the
@@ -309,19 +421,24 @@ static hipError_t launch4k(const void* v, const void* g, void* r, int64_t nch, i
     static int64_t resident[16];
     const int64_t pf =
         sizeof(typename IO::T) == 2
-            ? resident_workgroups((const void*)fused4k_kernel<IO, REV>, f4k::FT, resident) / 8 * 8
+            ? resident_workgroups((const void*)fused4k_kernel<IO, REV, MF>, f4k::FT, resident) / 8 * 8
             : 0;
-    hipLaunchKernelGGL((fused4k_kernel<IO, REV>), dim3((unsigned)nch), dim3(f4k::FT), 0, stream,
+    hipLaunchKernelGGL((fused4k_kernel<IO, REV, MF>), dim3((unsigned)nch), dim3(f4k::FT), 0, stream,
                        (const typename IO::T*)v, (const typename IO::T*)g, (typename IO::T*)r, L,
                        head, pair ? 1 : 0, tab, pf);
     return hipGetLastError();
 }
 
 hipError_t launch_fused4k(Store st, const void* v, const void* g, void* r, int64_t nch, int L,
-                          int head, bool pair_store, bool rev, const float2* tab,
+                          int head, bool pair_store, bool rev, bool mf, const float2* tab,
                           hipStream_t stream)
 {
     if (L <= 2048 || L > 4096 || head > HEAD_MAX) return hipErrorInvalidValue;
+    if (mf) {
+        if (st != Store::BF16) return hipErrorInvalidValue;
+        return rev ? launch4k<bf16_io, true, true>(v, g, r, nch, L, head, pair_store, tab, stream)
+                   : launch4k<bf16_io, false, true>(v, g, r, nch, L, head, pair_store, tab, stream);
+    }
     if (st == Store::F32)
         return rev ? launch4k<f32_io, true>(v, g, r, nch, L, head, pair_store, tab, stream)
                    : launch4k<f32_io, false>(v, g, r, nch, L, head, pair_store, tab, stream);

@@ -4,6 +4,7 @@
 
 #include <climits>
 #include <cmath>
+#include <cstring>
 #include <map>
 #include <mutex>
 #include <new>
@@ -244,6 +245,56 @@ std::vector<float2> dit4k_table()
                        var == 1 ? 8192 : 4096, inv);
     }
     for (int k = 0; k < 4096; ++k) h[sc::DIT4K_UNP + k] = tan_pair(k, 8192, true);
+    // The matrix-core first pass (bf16 storage): branch u's pass 1 is
+    //   X[k2] = sum_q x[q] F(q, k2),  F = W_16^{q k2} (u = 0),  W_32^{q (2 k2 + 1)} (u = 1)
+    // (branch 1's input rotation W_32^q merged), as a real 32 x 32 matrix: row 2 k2 + c
+    // (c = 0 real, 1 imaginary part of X[k2]), column 2 q + d (d = 0 the real part v of
+    // x[q], 1 the imaginary part g).  Each entry m is the sum of three bf16 parts
+    // (hi = bf16(m), mid = bf16(m - hi), lo = bf16(m - hi - mid): within 2^-26 |m|).  A
+    // 32 x 32 x 16 bf16 product's A fragment: lane l holds row l % 32 and the 8 columns
+    // 16 h + 8 (l / 32) + e, e < 8, of K half h, column e in the low half of 32-bit word e/2.
+    auto bf16_rne = [](double x) -> uint16_t {
+        const float f = (float)x;
+        uint32_t b;
+        std::memcpy(&b, &f, 4);
+        b += 0x7fffu + ((b >> 16) & 1u);
+        return (uint16_t)(b >> 16);
+    };
+    auto bf16_val = [](uint16_t hb) -> double {
+        const uint32_t b = (uint32_t)hb << 16;
+        float f;
+        std::memcpy(&f, &b, 4);
+        return f;
+    };
+    for (int u = 0; u < 2; ++u)
+        for (int kh = 0; kh < 2; ++kh)
+            for (int lane = 0; lane < 64; ++lane) {
+                uint16_t parts[3][8];
+                for (int e = 0; e < 8; ++e) {
+                    const int i = lane % 32, kk = 16 * kh + 8 * (lane / 32) + e;
+                    const int k2 = i / 2, c = i % 2, q = kk / 2, dd = kk % 2;
+                    // F = exp(-2 pi i a / 32): a = 2 q k2 (u = 0) or q (2 k2 + 1) (u = 1)
+                    const double a = u == 0 ? 2.0 * q * k2 : (double)q * (2 * k2 + 1);
+                    const double ang = 6.283185307179586476925286766559 * a / 32.0;
+                    const double fr = std::cos(ang), fi = -std::sin(ang);
+                    // out.re = fr x.re - fi x.im, out.im = fi x.re + fr x.im
+                    const double m = c == 0 ? (dd == 0 ? fr : -fi) : (dd == 0 ? fi : fr);
+                    const uint16_t p0 = bf16_rne(m);
+                    const double r1 = m - bf16_val(p0);
+                    const uint16_t p1 = bf16_rne(r1);
+                    const uint16_t p2 = bf16_rne(r1 - bf16_val(p1));
+                    parts[0][e] = p0;
+                    parts[1][e] = p1;
+                    parts[2][e] = p2;
+                }
+                for (int t = 0; t < 3; ++t) {
+                    uint32_t w[4];
+                    for (int j = 0; j < 4; ++j)
+                        w[j] = (uint32_t)parts[t][2 * j] | ((uint32_t)parts[t][2 * j + 1] << 16);
+                    float2* dst = &h[sc::DIT4K_MF + ((u * 3 + t) * 2 + kh) * 128 + 2 * lane];
+                    std::memcpy(dst, w, 16);
+                }
+            }
     return h;
 }
 
@@ -535,6 +586,12 @@ sc_status resolve_path(sc_kind kind, int64_t L, int32_t requested, sc_path* out)
         if (kind != SC_KIND_NTT_I32 || L > kMaxLNtt) return SC_ERR_UNSUPPORTED;
         *out = SC_PATH_NTT_MFMA;
         return SC_OK;
+    case SC_PATH_FUSED_MFMA:
+        // the M = 4096 kernel's matrix-core first pass (bf16 storage)
+        if (kind != SC_KIND_BF16 || L <= 2048 || L > 4096 || !kFused4k)
+            return SC_ERR_UNSUPPORTED;
+        *out = SC_PATH_FUSED_MFMA;
+        return SC_OK;
     default:
         return SC_ERR_INVALID_ARGUMENT;
     }
@@ -737,12 +794,16 @@ sc_status run_jobs(sc_kind kind, const Job* jobs, int njobs, bool rev, int64_t n
     if (path == SC_PATH_DIRECT) {
         for (int k = 0; k < njobs && e == hipSuccess; ++k)
             e = sc::launch_direct(s, jobs[k].a, jobs[k].b, jobs[k].o, nch, (int)L, rev, stream);
+    } else if (path == SC_PATH_FUSED_MFMA) {
+        for (int k = 0; k < njobs && e == hipSuccess; ++k)
+            e = sc::launch_fused4k(s, jobs[k].a, jobs[k].b, jobs[k].o, nch, (int)L, head, pair,
+                                   rev, true, d->dit4k, stream);
     } else if (path == SC_PATH_FUSED) {
         const int M = (int)std::max<int64_t>(64, next_pow2(L));
         for (int k = 0; k < njobs && e == hipSuccess; ++k)
             e = M == 4096 && kFused4k
                     ? sc::launch_fused4k(s, jobs[k].a, jobs[k].b, jobs[k].o, nch, (int)L, head,
-                                         pair, rev, d->dit4k, stream)
+                                         pair, rev, false, d->dit4k, stream)
                 : (M == 1024 || M == 2048) && kFusedDit
                     ? sc::launch_fused_dit(s, jobs[k].a, jobs[k].b, jobs[k].o, nch, (int)L, M,
                                            head, pair, rev, d->dit[M == 2048], stream)
@@ -1559,6 +1620,6 @@ sc_status sc_prepare(sc_kind kind, int64_t L)
     });
 }
 
-int sc_version(void) { return 901; }
+int sc_version(void) { return 902; }
 
 }  // extern "C"

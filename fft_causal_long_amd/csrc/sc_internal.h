@@ -59,6 +59,10 @@ hipError_t launch_fused(Store st, const void* v, const void* g, void* r, int64_t
 //   [DIT4K_P2 + (var 16 + j) 10 + i]  pass 2, item j < 16
 //   [DIT4K_P3 + (var 256 + j) 10 + i] pass 3, item j < 256
 //   [DIT4K_UNP + k]                  W_8192^{-k}, k < 4096 (the unpack)
+//   [DIT4K_MF + ((u 3 + t) 2 + h) 128 + 2 l], 16 bytes: the matrix-core first pass (bf16
+//                                    storage, mf): lane l's A fragment of part t (three
+//                                    bf16 parts) of branch u's 32 x 32 real pass-1 matrix,
+//                                    K half h (layout at dit4k_table in sc_host.cpp)
 // where var 0 is branch 0 (A = W_256^j, W_4096^j), var 1 branch 1 (A = W_512^{2j+1},
 // W_8192^{2j+1}), var 2 the inverse (conjugates of var 0), and an item's pairs i < 10 are
 // B, B^2, F_0, F_0^2, .., F_3, F_3^2 with B = A^4, F_p = A W16^p (W16^-p for the inverse).
@@ -66,9 +70,11 @@ constexpr int DIT4K_P1B1 = 0;
 constexpr int DIT4K_P2 = 16;
 constexpr int DIT4K_P3 = DIT4K_P2 + 3 * 16 * 10;
 constexpr int DIT4K_UNP = DIT4K_P3 + 3 * 256 * 10;
-constexpr int DIT4K_TABLE_FLOAT2 = DIT4K_UNP + 4096;
+constexpr int DIT4K_MF = DIT4K_UNP + 4096;
+constexpr int DIT4K_TABLE_FLOAT2 = DIT4K_MF + 2 * 3 * 2 * 64 * 2;
+// mf (bf16 storage only): the first pass of both branch transforms as bf16 matrix products
 hipError_t launch_fused4k(Store st, const void* v, const void* g, void* r, int64_t nch, int L,
-                          int head, bool pair_store, bool rev, const float2* table,
+                          int head, bool pair_store, bool rev, bool mf, const float2* table,
                           hipStream_t stream);
 
 // The fused kernels of sc_fused_dit.hip for M = 1024 and 2048 (M/2 < L <= M): passes of

@@ -91,10 +91,17 @@ typedef enum sc_path {
     SC_PATH_FUSED = 1,     /* one workgroup per channel, transform held in LDS     */
     SC_PATH_FOUR_STEP = 2, /* column / twiddle / row transforms staged through HBM  */
     SC_PATH_DIRECT = 3,    /* direct fp32 summation (float kinds, small L only)     */
-    SC_PATH_NTT_MFMA = 4   /* SC_KIND_NTT_I32, L <= 4096: the transform stages as int8
+    SC_PATH_NTT_MFMA = 4,  /* SC_KIND_NTT_I32, L <= 4096: the transform stages as int8
                               matrix products on the matrix cores (the integer-matrix
                               formulation of "Catastrophic Token Leakage ...", abstract);
                               the same result bits as SC_PATH_FUSED                  */
+    SC_PATH_FUSED_MFMA = 5 /* SC_KIND_BF16, 2048 < L <= 4096: SC_PATH_FUSED with the first
+                              radix-16 pass of each branch transform (the pad-2L FFT of
+                              the Caracal notes, key designs 1-2) as bf16 matrix products
+                              on the matrix cores, exact products of the bf16 inputs and
+                              a three-part bf16 DFT matrix summed in fp32; the same
+                              accuracy bound, not the same bits.  Slower than
+                              SC_PATH_FUSED on MI355X (kept for measurement)          */
 } sc_path;
 
 /* Optional controls for sc_causal_conv_ex (testing and experiments). */
@@ -447,7 +454,7 @@ sc_status sc_causal_conv_noalloc(sc_kind kind, const void* v, const void* g, voi
  */
 sc_status sc_prepare(sc_kind kind, int64_t L);
 
-/* Library version: major * 10000 + minor * 100 + patch (this header: 901).  Host only. */
+/* Library version: major * 10000 + minor * 100 + patch (this header: 902).  Host only. */
 int sc_version(void);
 
 #ifdef __cplusplus

@@ -91,6 +91,11 @@ def test_unsupported_lengths_rejected_before_launch(sc):
     opt = sc.sc_options(sc.PATH_FUSED, -1)             # one workgroup holds at most L = 4096
     assert h.sc_causal_conv_ex(0, A, B_, C_, 1, 1, 4097, ctypes.byref(opt), None, 0, None) == UNSUP
     assert h.sc_causal_conv_ex(2, A, B_, C_, 1, 1, 4097, ctypes.byref(opt), None, 0, None) == UNSUP
+    # the matrix-core first pass: the M = 4096 kernel with bf16 storage only
+    opt = sc.sc_options(sc.PATH_FUSED_MFMA, -1)
+    for kind, L in ((0, 4096), (2, 4096), (3, 4096), (1, 2048), (1, 4097), (1, 64)):
+        assert h.sc_causal_conv_ex(kind, A, B_, C_, 1, 1, L, ctypes.byref(opt), None, 0,
+                                   None) == UNSUP
     # the exact four-step split has rows of 4096: forced only above the fused range
     opt = sc.sc_options(sc.PATH_FOUR_STEP, -1)
     for kind in (2, 3):
@@ -124,7 +129,7 @@ def test_host_helpers(sc):
     assert sc.sc_status_string(0) == "SC_OK"
     assert sc.sc_status_string(4) == "SC_ERR_WORKSPACE"
     assert sc.sc_status_string(99) == "SC_STATUS_UNKNOWN"
-    assert sc.sc_version() >= 900
+    assert sc.sc_version() >= 902
     # sc_prepare: argument checks on the host; an empty length needs no table
     assert sc.sc_prepare(7, 64) == sc.SC_ERR_INVALID_ARGUMENT
     assert sc.sc_prepare(sc.KIND_F32, -1) == sc.SC_ERR_INVALID_ARGUMENT

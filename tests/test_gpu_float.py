@@ -230,24 +230,25 @@ def _bf16_rne(x32: np.ndarray) -> np.ndarray:
     return ((b + 0x7FFF + ((b >> 16) & 1)) >> 16).astype(np.uint16)
 
 
-def _near_ties_only(bf: np.ndarray, x32: np.ndarray, S: np.ndarray, what: str) -> float:
+def _near_ties_only(bf: np.ndarray, x32: np.ndarray, S: np.ndarray, what: str,
+                    rel: float = 1e-5) -> float:
     """bf (bf16 bits) must be the rounding of x32, or the rounding of another value within
-    1e-5 * S_t of x32: then either x32 lies within that distance of the tie between the two
+    rel * S_t of x32: then either x32 lies within that distance of the tie between the two
     roundings, or (outputs near zero, where a sign may flip) both lie within it of x32.
     Returns the fraction of outputs that differ from the rounding of x32."""
     rn = _bf16_rne(x32)
     diff = bf != rn
     if diff.any():
         a, b = decode(bf[diff]), decode(rn[diff])
-        x, tol = x32[diff].astype(np.float64), 1e-5 * S[diff]
+        x, tol = x32[diff].astype(np.float64), rel * S[diff]
         tie = np.abs(x - 0.5 * (a + b)) <= tol
         near = np.maximum(np.abs(a - x), np.abs(b - x)) <= tol
         ok = tie | near
         if not ok.all():
             i = int(np.argmin(ok))
-            raise AssertionError("%s: %d outputs are no rounding of a value within 1e-5 S_t "
+            raise AssertionError("%s: %d outputs are no rounding of a value within %g S_t "
                                  "(bf16 %r, fp32 call %r, S %r)" % (
-                                     what, int((~ok).sum()), float(a[i]), float(x[i]),
+                                     what, int((~ok).sum()), rel, float(a[i]), float(x[i]),
                                      float(S[diff][i])))
     return float(diff.mean())
 
