@@ -896,6 +896,8 @@ def main(argv=None):
                     help="skip the timing of the gate-stream calls")
     ap.add_argument("--no-fixed", action="store_true",
                     help="skip the timing of the exactly causal real-valued call")
+    ap.add_argument("--no-mfma", action="store_true",
+                    help="skip timing the SC_PATH_FUSED_MFMA form of the bf16 call")
     ap.add_argument("--no-others", action="store_true",
                     help="skip the plain call on the other workloads (Small, exact, long)")
     ap.add_argument("--no-stats", action="store_true",
@@ -977,7 +979,7 @@ def main(argv=None):
     stats = None if args.no_stats else launch_stats(torch, stream, step, 50, args.steps)
 
     mfma = None
-    if not args.no_others and w.storage == "bf16" and 2048 < w.L <= 4096:
+    if not args.no_mfma and w.storage == "bf16" and 2048 < w.L <= 4096:
         mfma = fused_mfma_measure(sc, torch, stream, step, bufs, w, args.steps)
 
     if args.calib_copy:
