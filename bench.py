@@ -119,8 +119,11 @@ def algorithmic_flops_per_output(L: int) -> float:
 
 
 def kernel_source_hash() -> str:
+    """Hash of the kernel sources and of the build script (its per-file compiler options
+    change the code a counter record describes)."""
     h = hashlib.sha256()
-    for p in sorted(glob.glob(os.path.join(ROOT, "fft_causal_long_amd", "csrc", "*"))):
+    for p in sorted(glob.glob(os.path.join(ROOT, "fft_causal_long_amd", "csrc", "*"))) + \
+            [os.path.join(ROOT, "fft_causal_long_amd", "build.py")]:
         with open(p, "rb") as f:
             h.update(os.path.basename(p).encode())
             h.update(f.read())

@@ -33,33 +33,73 @@ def sources() -> list[str]:
     return sorted(glob.glob(os.path.join(CSRC, "*.hip")) + glob.glob(os.path.join(CSRC, "*.cpp")))
 
 
-def command(out: str) -> list[str]:
+# Per-source device-code options.  The M = 4096 fused kernel is scheduled to group its
+# memory instructions into clauses: measured in alternating processes on one box, with
+# bit-identical outputs, the Medium bf16 call took 0.1427-0.1446 ms against 0.1446-0.1455
+# (median of five rounds of 50 calls, four repetitions) and the fp32 one 0.1574 against
+# 0.1630.  The same schedule for the whole library made the four-step calls 2-5% slower, so
+# it applies to this file alone.
+EXTRA = {"sc_fused4k.hip": ["-mllvm", "-amdgpu-sched-strategy=max-memory-clause"]}
+
+
+def compile_command(src: str, obj: str) -> list[str]:
     return [
-        hipcc(), "-O3", "-std=c++17", "-fPIC", "-shared",
+        hipcc(), "-O3", "-std=c++17", "-fPIC", "-c",
         "--offload-arch=" + ARCH,
         # keep the compiler from forming packed fp32 instructions
         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
         "-Wall", "-Wno-unused-function",
         "-I", INCLUDE, "-I", CSRC,
-        *sources(), "-o", out,
+        *EXTRA.get(os.path.basename(src), []),
+        src, "-o", obj,
     ]
 
 
+def link_command(objs: list[str], out: str) -> list[str]:
+    return [hipcc(), "-shared", "-fPIC", "--offload-arch=" + ARCH, *objs, "-o", out]
+
+
+def _quiet(stderr: str) -> list[str]:
+    # the host pass does not know the packed-fp32 feature flag; drop that noise
+    return [l for l in stderr.splitlines()
+            if l.strip() and "packed-fp32-ops" not in l and not l.startswith("1 warning")]
+
+
 def build(verbose: bool = False) -> str:
-    tmp = LIB + ".tmp%d" % os.getpid()
-    cmd = command(tmp)
-    if verbose:
-        print(" ".join(cmd), flush=True)
-    res = subprocess.run(cmd, capture_output=True, text=True)
-    if res.returncode != 0:
-        sys.stderr.write(res.stdout + res.stderr)
-        raise RuntimeError("hipcc failed building libspecconv.so")
-    if verbose and res.stderr.strip():
-        # the host pass does not know the packed-fp32 feature flag; drop that noise
-        lines = [l for l in res.stderr.splitlines() if "packed-fp32-ops" not in l]
-        if lines:
-            sys.stderr.write("\n".join(lines) + "\n")
-    os.replace(tmp, LIB)
+    """Compile each source to an object (in parallel), then link the shared library."""
+    import tempfile
+    from concurrent.futures import ThreadPoolExecutor
+
+    tmpdir = tempfile.mkdtemp(prefix="specconv_build_")
+    try:
+        srcs = sources()
+        objs = [os.path.join(tmpdir, os.path.basename(s) + ".o") for s in srcs]
+        cmds = [compile_command(s, o) for s, o in zip(srcs, objs)]
+        if verbose:
+            for c in cmds:
+                print(" ".join(c), flush=True)
+        jobs = max(1, min(len(cmds), os.cpu_count() or 1, 16))
+        with ThreadPoolExecutor(jobs) as ex:
+            results = list(ex.map(lambda c: subprocess.run(c, capture_output=True, text=True),
+                                  cmds))
+        for c, res in zip(cmds, results):
+            if res.returncode != 0:
+                sys.stderr.write(res.stdout + res.stderr)
+                raise RuntimeError("hipcc failed on %s" % c[-3])
+            lines = _quiet(res.stderr)
+            if verbose and lines:
+                sys.stderr.write("\n".join(lines) + "\n")
+        tmp = LIB + ".tmp%d" % os.getpid()
+        cmd = link_command(objs, tmp)
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        res = subprocess.run(cmd, capture_output=True, text=True)
+        if res.returncode != 0:
+            sys.stderr.write(res.stdout + res.stderr)
+            raise RuntimeError("linking libspecconv.so failed")
+        os.replace(tmp, LIB)
+    finally:
+        shutil.rmtree(tmpdir, ignore_errors=True)
     return LIB
 
 
