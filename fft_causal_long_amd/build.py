@@ -38,8 +38,11 @@ def sources() -> list[str]:
 # bit-identical outputs, the Medium bf16 call took 0.1427-0.1446 ms against 0.1446-0.1455
 # (median of five rounds of 50 calls, four repetitions) and the fp32 one 0.1574 against
 # 0.1630.  The same schedule for the whole library made the four-step calls 2-5% slower, so
-# it applies to this file alone.
-EXTRA = {"sc_fused4k.hip": ["-mllvm", "-amdgpu-sched-strategy=max-memory-clause"]}
+# it applies to the files that gain from it: the M = 4096 kernel's and the fused NTT
+# kernel's (the exact workload's call 0.1531-0.1540 against 0.1551-0.1558 ms).  The fused
+# exact real-valued kernel, in a file of its own, was 0.7% slower with it.
+_CLAUSES = ["-mllvm", "-amdgpu-sched-strategy=max-memory-clause"]
+EXTRA = {"sc_fused4k.hip": _CLAUSES, "sc_ntt.hip": _CLAUSES}
 
 
 def compile_command(src: str, obj: str) -> list[str]:

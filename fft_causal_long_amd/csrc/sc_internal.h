@@ -141,7 +141,7 @@ hipError_t launch_ntt_mfma(const int32_t* v, const int32_t* g, int32_t* r, int64
                            int M, bool rev, const NttMfmaTables& tables, hipStream_t stream);
 
 // Exact NTT causal convolution for FUSED_MAX_L < L <= NTT4_MAX_L through the four-step split
-// (sc_ntt.hip): M = next power of two >= L, chunks of `chunk` channels, each needing
+// (sc_ntt4.hip): M = next power of two >= L, chunks of `chunk` channels, each needing
 // ntt4_bytes_per_channel(M) bytes of ws (ws_bytes >= chunk * that); wtab = the per-M tables
 // of prime A (5M doubles: w_N^j for j < 2M, then the column and the row twiddles).  Modulo
 // prime A, output lifted to the balanced range; rev as for launch_ntt.  Streams as for
