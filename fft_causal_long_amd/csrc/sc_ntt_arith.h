@@ -1,7 +1,7 @@
 // Exact modular arithmetic and the LDS transform passes shared by the number-theoretic
-// transform kernels: the fused NTT kernel (sc_ntt.hip), the exact real-valued kernel (sc_fixed.hip) and the
-// four-step NTT kernels (sc_ntt4.hip).  The method, the primes and the arithmetic are
-// described at the top of sc_ntt.hip.
+// transform kernels: the fused NTT kernel (sc_ntt.hip), the exact real-valued kernel
+// (sc_fixed.hip) and the four-step NTT kernels (sc_ntt4.hip).  The method, the primes and
+// the arithmetic are described at the top of sc_ntt.hip.
 #pragma once
 
 #include "sc_device.h"
