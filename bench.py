@@ -326,6 +326,29 @@ def leakage_probe(sc, torch, dev, channels: int = 16) -> dict:
             "fixed_max_abs": x_leak, "positions": len(pos), "channels": channels, "L": w3.L}
 
 
+def copy_reference(torch, dev) -> dict:
+    """The achievable HBM rate of a plain read-2 / write-1 stream on this machine: torch's
+    elementwise c = a + b on 256 MiB float32 tensors (3 x 256 MiB per call, past the
+    last-level cache with two rotating sets), best of five rounds of 10 calls."""
+    n = 1 << 26
+    sets = [[torch.empty(n, dtype=torch.float32, device=dev).fill_(1.0) for _ in range(3)]
+            for _ in range(2)]
+    stream = torch.cuda.current_stream(dev)
+
+    def call(i):
+        a, b, c = sets[i % 2]
+        torch.add(a, b, out=c)
+
+    for i in range(10):
+        call(i)
+    best = min(time_rounds(torch, stream, call, 10, rounds=1, warm=False)[0] for _ in range(5))
+    gbps = 3 * n * 4 / (best * 1e-3) / 1e9
+    del sets
+    return {"what": "torch.add(a, b, out=c), float32, 256 MiB each (read 2, write 1)",
+            "ms_per_call": round(best, 5), "achieved_GBps": round(gbps, 1),
+            "frac_of_peak": round(gbps / HBM_PEAK_GBPS, 4)}
+
+
 def fused_mfma_measure(sc, torch, stream, step, bufs, w, steps: int) -> dict:
     """The same call with SC_PATH_FUSED_MFMA (the first pass of both branch transforms as bf16
     matrix products), timed in three rounds alternating with rounds of the default call on
@@ -1041,6 +1064,10 @@ def main(argv=None):
     }
     if mfma is not None:
         rec["fused_mfma"] = mfma
+    if not args.no_others:
+        ref = copy_reference(torch, dev)
+        rec["hbm"]["copy_reference"] = ref
+        rec["hbm"]["frac_of_copy"] = round(hbm_gbps / ref["achieved_GBps"], 4)
     if not args.no_bwd:
         del bufs
         rec["bwd"] = bwd_measure(sc, torch, w, dev, max(5, args.steps // 2), args.warmup)
