@@ -100,8 +100,9 @@ typedef enum sc_path {
                               the Caracal notes, key designs 1-2) as bf16 matrix products
                               on the matrix cores, exact products of the bf16 inputs and
                               a three-part bf16 DFT matrix summed in fp32; the same
-                              accuracy bound, not the same bits.  Slower than
-                              SC_PATH_FUSED on MI355X (kept for measurement)          */
+                              accuracy bound, not the same bits.  No faster than
+                              SC_PATH_FUSED on MI355X (within a few percent either
+                              way; kept for measurement)                              */
 } sc_path;
 
 /* Optional controls for sc_causal_conv_ex (testing and experiments). */
