@@ -180,7 +180,7 @@ __global__ __launch_bounds__(512) void fused4k_kernel(const typename IO::T* __re
         for (int b = 0; b < 2; ++b)
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[b][r] = 0.f;
-        // the small parts first
+        // within each K half, the small parts first
 #pragma unroll
         for (int b = 0; b < 2; ++b)
 #pragma unroll
